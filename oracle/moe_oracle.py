@@ -1,0 +1,383 @@
+"""Plain CPU oracle of the forward pass of a top-k routed MoE FFN layer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import or call
+this module: only the test-suite, the package smoke check and the CPU-baseline
+leg of the benchmark use it.  It shares no code with the HIP library (own
+bf16 decoding, own loops, own reductions) and imports nothing from it.
+
+Everything is computed in float64 from the stored input values (float32, or
+bfloat16 bit patterns decoded exactly), with no intermediate rounding.  The
+structure deliberately follows the pages' reference loops (one expert at a
+time, gather, run the FFN, weight, add back) rather than anything fast.
+
+Sources (web pages; sections as printed on each page):
+  [P1] "Naive-N0.5-Flash" open-source MoE blog, wzjinhao.cn/news/74695
+  [P2] "The quietly activated expert group" MoE explainer, mqxn.cn/news/15586
+  [P3] "Small MoE language model from scratch" tutorial, lshu.cn/news/325687
+  [P4] "OpenMythos" re-implementation blog, lpnh.cn/news/1735864
+  [P5] FLAME-MoE research-platform summary,
+       lsdiaocha.cn/2025/0530/3166997.shtml
+
+Readings taken where the pages are silent or disagree (each is also listed in
+the design notes):
+  * top-k ties: lower expert index first; outputs sorted by descending
+    probability (torch.topk order in [P2 §4.1], [P3 §3.1]).
+  * capacity C = ceil(cf * T * k / E) evaluated exactly on the binary64 value
+    of cf ([P4 §3.1] gives cf * tokens / E, i.e. the k = 1 case).
+  * overflow: within an expert, assignments are kept first-come in ascending
+    token order; a dropped assignment contributes exactly zero and the kept
+    weights are not renormalised ([P1 §2.2], [P4 §3.1]).
+  * f_i of the load-balance loss is the pre-capacity share of the T*k
+    assignments; P_i is the mean over all tokens of the full softmax
+    ([P4 §3.1]).  z-loss = mean over tokens of logsumexp(logits)^2 ([P5 §2]
+    names the loss; the squared-lse form is the standard router z-loss).
+  * SwiGLU: h = silu(x W_gate^T) * (x W_up^T), then W_down; GELU is the exact
+    erf form; dropout is the identity at inference ([P2 §3.1], [P3 §3.1]).
+  * shared experts have weight 1 and sit outside the router ([P4 §2.1],
+    [P5 §2]).  The residual x is added only when asked ([P2 §4.1] adds it
+    inside the layer, [P3 §3.2] outside).
+
+Parity pins: every function below is exercised by the CPU tests against
+closed forms, brute force or an independently written dense computation; the
+one convention with no external pin (the f_i normalisation) is marked
+"parity unpinned beyond the convention" at `aux_losses`.
+"""
+
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+
+__all__ = [
+    "decode",
+    "router_logits",
+    "softmax_lse",
+    "topk_select",
+    "renormalise",
+    "expert_counts",
+    "capacity",
+    "dispatch",
+    "expert_ffn",
+    "shared_ffn",
+    "combine",
+    "aux_losses",
+    "router_gap_ok",
+    "forward",
+]
+
+
+# ---------------------------------------------------------------------------
+# input decoding
+
+
+def decode(a, dtype: str) -> np.ndarray:
+    """Stored tensor -> float64.
+
+    dtype "bf16": `a` holds bfloat16 bit patterns as uint16; the value is the
+    float32 whose upper 16 bits are those bits (exact).  dtype "f32": `a` is
+    float32.  Either way the result is exact in float64.
+    """
+    a = np.asarray(a)
+    if dtype == "bf16":
+        if a.dtype != np.uint16:
+            raise TypeError("bf16 tensors are passed as uint16 bit patterns")
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if dtype == "f32":
+        if a.dtype != np.float32:
+            raise TypeError("f32 tensors are passed as float32")
+        return a.astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+# ---------------------------------------------------------------------------
+# routing: [P2 §3.2] (router is one linear layer), [P3 §3.1] steps 1-2,
+# [P4 §3.1] "routing and top-k selection"
+
+
+def router_logits(x: np.ndarray, w_router: np.ndarray, bias=None) -> np.ndarray:
+    """l[t, e] = sum_c x[t, c] * W_r[e, c] (+ b[e]).
+
+    W_r uses the nn.Linear [out, in] layout, [E, d] ([P3 §3.1], bias-free
+    router).  The optional per-expert bias is added to the logits before the
+    softmax.
+    """
+    logits = x @ w_router.T
+    if bias is not None:
+        logits = logits + np.asarray(bias, dtype=np.float64)[None, :]
+    return logits
+
+
+def softmax_lse(logits: np.ndarray):
+    """Softmax over experts and the per-token log-sum-exp.
+
+    m = max_e l, Z = sum_e exp(l - m), p = exp(l - m) / Z, lse = m + ln Z.
+    """
+    m = logits.max(axis=1, keepdims=True)
+    ex = np.exp(logits - m)
+    z = ex.sum(axis=1, keepdims=True)
+    p = ex / z
+    lse = (m + np.log(z))[:, 0]
+    return p, lse
+
+
+def topk_select(p: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest probabilities per token.
+
+    Ordered by descending probability; equal probabilities keep ascending
+    expert index (stable sort of -p).  [P3 §3.1] / [P4 §3.1] take torch.topk
+    of the softmax output.
+    """
+    order = np.argsort(-p, axis=1, kind="stable")
+    return order[:, :k].astype(np.int64)
+
+
+def renormalise(p: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """w[t, j] = p[t, idx[t, j]] / sum_j' p[t, idx[t, j']] ([P3 §3.1] step 2)."""
+    sel = np.take_along_axis(p, idx, axis=1)
+    return sel / sel.sum(axis=1, keepdims=True)
+
+
+def router_gap_ok(x, w_router, bias, k: int, dtype: str, gap: float = 1e-4) -> np.ndarray:
+    """Input acceptance rule: p_(k) - p_(k+1) >= gap for every token.
+
+    Evaluated in float64 on the stored (rounded) values.  With k == E there is
+    no (k+1)-th expert and every token is accepted.  Used by the input
+    generator through a callback, so that routing is unambiguous.
+    """
+    xd = decode(x, dtype)
+    wr = decode(w_router, dtype)
+    p, _ = softmax_lse(router_logits(xd, wr, bias))
+    E = p.shape[1]
+    if k >= E:
+        return np.ones(p.shape[0], dtype=bool)
+    srt = -np.sort(-p, axis=1)
+    return (srt[:, k - 1] - srt[:, k]) >= gap
+
+
+# ---------------------------------------------------------------------------
+# counts, capacity, dispatch: [P2 §4.1] (expert_counts buffer),
+# [P4 §3.1] "capacity factor and overflow handling" and the flatten/reorder
+# description that follows its pseudo-code, [P1 §2.2] (expert capacity)
+
+
+def expert_counts(idx: np.ndarray, n_experts: int) -> np.ndarray:
+    """counts[e] = number of (t, j) with idx[t, j] == e (before capacity)."""
+    counts = np.zeros(n_experts, dtype=np.int64)
+    for e in idx.reshape(-1):
+        counts[e] += 1
+    return counts
+
+
+def capacity(capacity_factor: float, n_tokens: int, top_k: int, n_experts: int):
+    """C = ceil(cf * T * k / E) in exact rational arithmetic, None = no limit.
+
+    cf <= 0 means no limit.  cf is taken at its exact binary64 value.
+    """
+    if capacity_factor is None or not (capacity_factor > 0):
+        if capacity_factor is not None and math.isnan(capacity_factor):
+            raise ValueError("capacity factor is NaN")
+        return None
+    c = Fraction(float(capacity_factor)) * n_tokens * top_k / n_experts
+    return int(math.ceil(c))
+
+
+def dispatch(idx: np.ndarray, n_experts: int, cap):
+    """Stable expert-contiguous permutation with capacity drops.
+
+    For each expert e, the tokens routed to it in ascending token order; the
+    first min(count, C) are kept.  Kept rows are ordered by (e, t).
+    Returns (offsets[E+1], perm_token[R], perm_slot[R], inv_row[T, k] with -1
+    for dropped assignments, n_dropped).
+    """
+    T, k = idx.shape
+    lists = [[] for _ in range(n_experts)]
+    for t in range(T):
+        for j in range(k):
+            lists[int(idx[t, j])].append((t, j))
+    offsets = np.zeros(n_experts + 1, dtype=np.int64)
+    perm_token, perm_slot = [], []
+    inv_row = np.full((T, k), -1, dtype=np.int64)
+    n_dropped = 0
+    row = 0
+    for e in range(n_experts):
+        assigned = lists[e]  # already in ascending t (outer loop over t)
+        kept = assigned if cap is None else assigned[:cap]
+        n_dropped += len(assigned) - len(kept)
+        for (t, j) in kept:
+            perm_token.append(t)
+            perm_slot.append(j)
+            inv_row[t, j] = row
+            row += 1
+        offsets[e + 1] = row
+    return (offsets, np.array(perm_token, dtype=np.int64),
+            np.array(perm_slot, dtype=np.int64), inv_row, n_dropped)
+
+
+# ---------------------------------------------------------------------------
+# expert FFNs: [P2 §3.1] (two linear maps and a SwiGLU-type non-linearity),
+# [P3 §3.1] (Linear + GELU + Dropout + Linear with biases)
+
+
+def _gelu(z):
+    """Exact GELU: z/2 * (1 + erf(z / sqrt 2)), elementwise via math.erf."""
+    erf = np.vectorize(math.erf, otypes=[np.float64])
+    return 0.5 * z * (1.0 + erf(z / math.sqrt(2.0)))
+
+
+def _silu(z):
+    """SiLU: z / (1 + exp(-z))."""
+    return z / (1.0 + np.exp(-z))
+
+
+def expert_ffn(x_rows: np.ndarray, w1: np.ndarray, b1, w2: np.ndarray, b2, act: str) -> np.ndarray:
+    """One expert on a block of rows (all float64).
+
+    GELU:   h = gelu(x W1^T + b1);          out = h W2^T + b2
+            W1 [f, d], W2 [d, f].
+    SwiGLU: g = x W1[:f]^T, u = x W1[f:]^T;  h = silu(g) * u;  out = h W2^T
+            W1 [2f, d] holds the gate rows then the up rows; optional biases
+            b1 [2f] and b2 [d] are added the same way.
+    """
+    if act == "gelu":
+        z = x_rows @ w1.T
+        if b1 is not None:
+            z = z + b1[None, :]
+        h = _gelu(z)
+    elif act == "swiglu":
+        f = w1.shape[0] // 2
+        g = x_rows @ w1[:f].T
+        u = x_rows @ w1[f:].T
+        if b1 is not None:
+            g = g + b1[None, :f]
+            u = u + b1[None, f:]
+        h = _silu(g) * u
+    else:
+        raise ValueError(f"unknown activation {act!r}")
+    out = h @ w2.T
+    if b2 is not None:
+        out = out + b2[None, :]
+    return out
+
+
+def shared_ffn(x: np.ndarray, ws1, sb1, ws2, sb2, n_shared: int, act: str, dtype: str) -> np.ndarray:
+    """Sum of the always-active shared experts, each with weight 1 ([P4 §2.1],
+    [P5 §2])."""
+    out = np.zeros_like(x)
+    for s in range(n_shared):
+        out += expert_ffn(
+            x, decode(ws1[s], dtype), None if sb1 is None else decode(sb1[s], dtype),
+            decode(ws2[s], dtype), None if sb2 is None else decode(sb2[s], dtype), act)
+    return out
+
+
+def combine(routed: np.ndarray, shared, residual) -> np.ndarray:
+    """y = shared + sum of weighted routed outputs (+ x when asked).
+
+    `routed` already holds sum_j w[t, j] * o(t, idx[t, j]) over kept
+    assignments ([P1 §2.1] weighted sum; [P5 §2] weights are the normalised
+    routing scores; [P2 §4.1] optional residual).
+    """
+    y = routed.copy()
+    if shared is not None:
+        y = y + shared
+    if residual is not None:
+        y = y + residual
+    return y
+
+
+# ---------------------------------------------------------------------------
+# auxiliary statistics: [P4 §3.1] load-balance loss alpha * E * sum f_i P_i,
+# [P5 §2] router z-loss and the 0.01 / 0.001 coefficients
+
+
+def aux_losses(p: np.ndarray, lse: np.ndarray, counts: np.ndarray, top_k: int):
+    """lb = E * sum_e f_e P_e, z = mean_t lse_t^2, weighted = 0.01 lb + 0.001 z.
+
+    f_e = counts_e / (T k) with pre-capacity counts, so sum f = 1 and lb = 1
+    under uniform routing; P_e = mean_t p[t, e] over the full softmax.
+    The f_e normalisation is a convention: parity unpinned beyond the
+    convention.
+    """
+    T, E = p.shape
+    f = counts.astype(np.float64) / float(T * top_k)
+    P = p.mean(axis=0)
+    lb = float(E * np.sum(f * P))
+    z = float(np.mean(lse * lse))
+    return {"lb": lb, "z": z, "weighted": 0.01 * lb + 0.001 * z, "f": f, "P": P}
+
+
+# ---------------------------------------------------------------------------
+# the whole layer
+
+
+def forward(cfg, t, rows=None, want_routed_rows=False):
+    """Full forward of the layer on CPU.
+
+    cfg: object with T, d, E, k, f, S, dtype ("bf16"/"f32"), act
+         ("swiglu"/"gelu"), capacity_factor (<= 0: none), add_residual.
+    t:   dict with x [T, d], w_router [E, d], router_bias [E] float32 or None,
+         w1 / b1 / w2 / b2 (indexable by expert), ws1 / sb1 / ws2 / sb2
+         (indexable by shared expert, may be None when S == 0).
+    rows: optional iterable of token indices; the expert FFNs and y are then
+         evaluated for those tokens only (routing, dispatch and aux always
+         cover all T tokens).
+    want_routed_rows: also return the raw (unweighted) expert output for
+         every kept row in permuted order (needs rows is None).
+
+    Returns a dict of float64 / int64 arrays and scalars.
+    """
+    dt = cfg.dtype
+    x = decode(t["x"], dt)
+    T, d = x.shape
+    E, k = cfg.E, cfg.k
+    wr = decode(t["w_router"], dt)
+    rb = t.get("router_bias")
+    rb = None if rb is None else np.asarray(rb, dtype=np.float32).astype(np.float64)
+
+    logits = router_logits(x, wr, rb)
+    p, lse = softmax_lse(logits)
+    idx = topk_select(p, k)
+    w = renormalise(p, idx)
+    counts = expert_counts(idx, E)
+    cap = capacity(cfg.capacity_factor, T, k, E)
+    offsets, perm_token, perm_slot, inv_row, n_dropped = dispatch(idx, E, cap)
+    aux = aux_losses(p, lse, counts, k)
+
+    tok = np.arange(T) if rows is None else np.asarray(sorted(set(int(r) for r in rows)), dtype=np.int64)
+    pos = {int(tt): i for i, tt in enumerate(tok)}
+    routed = np.zeros((len(tok), d))
+    routed_rows = np.zeros((len(perm_token), d)) if (want_routed_rows and rows is None) else None
+
+    b1s, b2s = t.get("b1"), t.get("b2")
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        sel = [r for r in range(r0, r1) if int(perm_token[r]) in pos]
+        if not sel:
+            continue
+        toks = perm_token[sel]
+        out = expert_ffn(
+            x[toks], decode(t["w1"][e], dt), None if b1s is None else decode(b1s[e], dt),
+            decode(t["w2"][e], dt), None if b2s is None else decode(b2s[e], dt), cfg.act)
+        for i, r in enumerate(sel):
+            tt, j = int(perm_token[r]), int(perm_slot[r])
+            routed[pos[tt]] += w[tt, j] * out[i]
+            if routed_rows is not None:
+                routed_rows[r] = out[i]
+
+    shared = None
+    if cfg.S > 0:
+        shared = shared_ffn(x[tok], t["ws1"], t.get("sb1"), t["ws2"], t.get("sb2"), cfg.S, cfg.act, dt)
+    y = combine(routed, shared, x[tok] if cfg.add_residual else None)
+
+    return {
+        "logits": logits, "p": p, "lse": lse,
+        "topk_idx": idx, "topk_w": w,
+        "counts": counts, "capacity": cap, "offsets": offsets,
+        "perm_token": perm_token, "perm_slot": perm_slot,
+        "perm_w": w[perm_token, perm_slot] if len(perm_token) else np.zeros(0),
+        "inv_row": inv_row, "n_dropped": int(n_dropped),
+        "lb": aux["lb"], "z": aux["z"], "weighted": aux["weighted"],
+        "rows": tok, "y": y, "shared_y": shared, "routed_rows": routed_rows,
+    }

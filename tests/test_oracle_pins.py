@@ -1,0 +1,418 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself:
+closed forms, brute force on tiny inputs, library routines (torch float64 on
+the CPU, scipy) for special cases, invariants, and the parameter arithmetic a
+page prints.  CPU only.
+
+Page keys as in the oracle header: [P1] Naive-N0.5-Flash blog, [P2] MoE
+explainer (mqxn.cn), [P3] small-MoE tutorial (lshu.cn), [P4] OpenMythos blog,
+[P5] FLAME-MoE summary.
+"""
+
+import itertools
+import json
+import math
+import os
+from dataclasses import dataclass
+
+import numpy as np
+import pytest
+import scipy.special
+import scipy.stats
+import torch
+import torch.nn.functional as F
+
+import oracle
+from moe_inputs import LayerConfig, f32_to_bf16_bits, get_config, make_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@dataclass
+class Cfg:
+    T: int
+    d: int
+    E: int
+    k: int
+    f: int
+    S: int = 0
+    dtype: str = "f32"
+    act: str = "swiglu"
+    capacity_factor: float = 0.0
+    add_residual: bool = False
+
+
+def f32(a):
+    return np.asarray(a, dtype=np.float32)
+
+
+def rand_tensors(cfg, seed, bias=False, router_bias=None):
+    """Small float32 tensors for oracle-only pins."""
+    r = np.random.default_rng(seed)
+    rows = 2 * cfg.f if cfg.act == "swiglu" else cfg.f
+    t = {
+        "x": f32(r.standard_normal((cfg.T, cfg.d))),
+        "w_router": f32(r.standard_normal((cfg.E, cfg.d)) * 0.5),
+        "router_bias": None if router_bias is None else f32(router_bias),
+        "w1": f32(r.standard_normal((cfg.E, rows, cfg.d)) * 0.3),
+        "w2": f32(r.standard_normal((cfg.E, cfg.d, cfg.f)) * 0.3),
+        "b1": f32(r.standard_normal((cfg.E, rows)) * 0.1) if bias else None,
+        "b2": f32(r.standard_normal((cfg.E, cfg.d)) * 0.1) if bias else None,
+        "ws1": f32(r.standard_normal((cfg.S, rows, cfg.d)) * 0.3) if cfg.S else None,
+        "ws2": f32(r.standard_normal((cfg.S, cfg.d, cfg.f)) * 0.3) if cfg.S else None,
+        "sb1": None, "sb2": None,
+    }
+    return t
+
+
+def torch_ffn(x, w1, b1, w2, b2, act):
+    """Expert FFN through torch's float64 CPU library routines."""
+    x = torch.as_tensor(x, dtype=torch.float64)
+    w1 = torch.as_tensor(np.asarray(w1, dtype=np.float64))
+    w2 = torch.as_tensor(np.asarray(w2, dtype=np.float64))
+    b1 = None if b1 is None else torch.as_tensor(np.asarray(b1, dtype=np.float64))
+    b2 = None if b2 is None else torch.as_tensor(np.asarray(b2, dtype=np.float64))
+    if act == "gelu":
+        h = F.gelu(F.linear(x, w1, b1), approximate="none")
+    else:
+        gu = F.linear(x, w1, b1)
+        g, u = gu.chunk(2, dim=-1)
+        h = F.silu(g) * u
+    return F.linear(h, w2, b2).numpy()
+
+
+# ---------------------------------------------------------------------------
+# worked example with closed-form values (hand-derived)
+
+
+def test_worked_example_closed_form():
+    """x = [1, 0]; router rows give logits [0, ln 2, ln 3].
+
+    p = [1/6, 1/3, 1/2], lse = ln 6, top-2 = [2, 1], w = [3/5, 2/5];
+    f = [0, 1/2, 1/2], P = p -> lb = 3 * (1/2 * 1/3 + 1/2 * 1/2) = 5/4,
+    z = (ln 6)^2.  SwiGLU expert 2 with one hidden unit: gate weight 2, up
+    weight 3 on x[0] -> h = 3 * silu(2) = 6 / (1 + e^-2); W2 column [1, -1].
+    Expert 1: gate 1, up 1 -> h = 1 / (1 + e^-1); W2 column [2, 0].
+    """
+    cfg = Cfg(T=1, d=2, E=3, k=2, f=1)
+    ln2, ln3 = math.log(2.0), math.log(3.0)
+    t = {
+        "x": f32([[1.0, 0.0]]),
+        "w_router": f32([[0.0, 5.0], [ln2, -1.0], [ln3, 7.0]]),
+        "router_bias": None,
+        "w1": f32([[[9.0, 0.0], [9.0, 0.0]],      # expert 0 (not selected)
+                   [[1.0, 0.0], [1.0, 0.0]],      # expert 1: gate 1, up 1
+                   [[2.0, 0.0], [3.0, 0.0]]]),    # expert 2: gate 2, up 3
+        "w2": f32([[[5.0], [5.0]], [[2.0], [0.0]], [[1.0], [-1.0]]]),
+        "b1": None, "b2": None, "ws1": None, "ws2": None,
+    }
+    o = oracle.forward(cfg, t)
+    tol = 1e-6  # float32 storage of ln 2, ln 3
+    assert np.allclose(o["p"][0], [1 / 6, 1 / 3, 1 / 2], atol=tol)
+    assert abs(o["lse"][0] - math.log(6.0)) < tol
+    assert o["topk_idx"].tolist() == [[2, 1]]
+    assert np.allclose(o["topk_w"][0], [3 / 5, 2 / 5], atol=tol)
+    assert o["counts"].tolist() == [0, 1, 1]
+    assert abs(o["lb"] - 5 / 4) < tol
+    assert abs(o["z"] - math.log(6.0) ** 2) < 1e-5
+    assert abs(o["weighted"] - (0.01 * 5 / 4 + 0.001 * math.log(6.0) ** 2)) < 1e-6
+    h2 = 6.0 / (1.0 + math.exp(-2.0))
+    h1 = 1.0 / (1.0 + math.exp(-1.0))
+    y = 3 / 5 * np.array([h2, -h2]) + 2 / 5 * np.array([2 * h1, 0.0])
+    assert np.allclose(o["y"][0], y, atol=1e-6)
+    # dispatch of the single token: expert 1 row 0, expert 2 row 1
+    assert o["offsets"].tolist() == [0, 0, 1, 2]
+    assert o["perm_token"].tolist() == [0, 0]
+    assert o["inv_row"].tolist() == [[1, 0]]
+
+
+# ---------------------------------------------------------------------------
+# activations against library routines and exact identities
+
+
+def test_gelu_is_exact_erf_form():
+    z = np.linspace(-6, 6, 241)
+    g = oracle.moe_oracle._gelu(z)
+    assert np.allclose(g, z * scipy.stats.norm.cdf(z), rtol=1e-13, atol=1e-15)
+    assert np.allclose(g - oracle.moe_oracle._gelu(-z), z, atol=1e-13)   # gelu(z) - gelu(-z) = z
+    assert oracle.moe_oracle._gelu(np.array([0.0]))[0] == 0.0
+    # not the tanh approximation
+    tanh_form = 0.5 * z * (1 + np.tanh(math.sqrt(2 / math.pi) * (z + 0.044715 * z ** 3)))
+    assert np.max(np.abs(g - tanh_form)) > 1e-5
+
+
+def test_silu_identities():
+    z = np.linspace(-20, 20, 401)
+    s = oracle.moe_oracle._silu(z)
+    assert np.allclose(s, z * scipy.special.expit(z), rtol=1e-13, atol=1e-15)
+    assert np.allclose(s - oracle.moe_oracle._silu(-z), z, atol=1e-12)
+    assert oracle.moe_oracle._silu(np.array([0.0]))[0] == 0.0
+
+
+# ---------------------------------------------------------------------------
+# routing: brute force, logit-form identity, special cases
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_topk_brute_force_tiny(seed):
+    """Top-k set = unique maximiser of the sum of logits over k-subsets, in
+    descending-probability order; weights = softmax over the selected logits
+    ([P2 §4.1] takes top-k on logits then a softmax over the k)."""
+    r = np.random.default_rng(seed)
+    T, E = 8, 2 + seed % 5
+    k = 1 + seed % min(3, E)
+    cfg = Cfg(T=T, d=5, E=E, k=k, f=3)
+    t = rand_tensors(cfg, seed)
+    o = oracle.forward(cfg, t)
+    logits = t["x"].astype(np.float64) @ t["w_router"].astype(np.float64).T
+    for tok in range(T):
+        best = max(itertools.combinations(range(E), k), key=lambda S: sum(logits[tok, i] for i in S))
+        chosen = sorted(best, key=lambda i: -logits[tok, i])
+        assert o["topk_idx"][tok].tolist() == chosen
+        den = sum(math.exp(logits[tok, i]) for i in chosen)
+        w = [math.exp(logits[tok, i]) / den for i in chosen]
+        assert np.allclose(o["topk_w"][tok], w, rtol=1e-12)
+        # full softmax and lse against torch
+        lt = torch.as_tensor(logits[tok])
+        assert np.allclose(o["p"][tok], torch.softmax(lt, 0).numpy(), rtol=1e-12)
+        assert abs(o["lse"][tok] - torch.logsumexp(lt, 0).item()) < 1e-12
+
+
+def test_zero_router_uniform():
+    """W_r = 0: p = 1/E, lse = ln E, idx = 0..k-1, w = 1/k, lb = 1,
+    z = (ln E)^2."""
+    cfg = Cfg(T=16, d=4, E=6, k=3, f=2)
+    t = rand_tensors(cfg, 3)
+    t["w_router"] = np.zeros_like(t["w_router"])
+    o = oracle.forward(cfg, t)
+    assert np.allclose(o["p"], 1 / 6, rtol=1e-15)
+    assert np.allclose(o["lse"], math.log(6), rtol=1e-15)
+    assert (o["topk_idx"] == np.arange(3)[None, :]).all()
+    assert np.allclose(o["topk_w"], 1 / 3, rtol=1e-15)
+    assert abs(o["lb"] - 1.0) < 1e-14
+    assert abs(o["z"] - math.log(6) ** 2) < 1e-13
+
+
+def test_k1_weight_is_one_and_dominant_expert_lb_tends_to_E():
+    cfg = Cfg(T=32, d=4, E=5, k=1, f=2)
+    bias = np.array([60.0, 0, 0, 0, 0])
+    t = rand_tensors(cfg, 4, router_bias=bias)
+    o = oracle.forward(cfg, t)
+    assert (o["topk_w"] == 1.0).all()
+    assert (o["topk_idx"][:, 0] == 0).all()
+    assert abs(o["lb"] - 5.0) < 1e-9          # f_0 = 1, P_0 -> 1
+
+
+def test_k_equals_E_weights_are_full_softmax():
+    cfg = Cfg(T=10, d=4, E=4, k=4, f=2)
+    t = rand_tensors(cfg, 5)
+    o = oracle.forward(cfg, t)
+    p_sorted = np.take_along_axis(o["p"], o["topk_idx"], axis=1)
+    assert np.allclose(o["topk_w"], p_sorted, rtol=1e-13)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_weight_invariants(seed):
+    cfg = Cfg(T=64, d=8, E=7, k=3, f=4)
+    o = oracle.forward(cfg, rand_tensors(cfg, seed))
+    assert np.allclose(o["topk_w"].sum(axis=1), 1.0, atol=1e-12)
+    assert (np.diff(o["topk_w"], axis=1) <= 0).all()
+    assert o["counts"].sum() == cfg.T * cfg.k
+    for row in o["topk_idx"]:
+        assert len(set(row.tolist())) == cfg.k
+
+
+# ---------------------------------------------------------------------------
+# FFN closed forms and dense-mixture equivalence
+
+
+@pytest.mark.parametrize("act", ["swiglu", "gelu"])
+def test_single_expert_closed_form(act):
+    """E = 1, k = 1: y = FFN(x) exactly (weight 1), via torch float64."""
+    cfg = Cfg(T=9, d=6, E=1, k=1, f=5, act=act)
+    t = rand_tensors(cfg, 7, bias=True)
+    o = oracle.forward(cfg, t)
+    ref = torch_ffn(t["x"], t["w1"][0], t["b1"][0], t["w2"][0], t["b2"][0], act)
+    assert np.allclose(o["y"], ref, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("act", ["swiglu", "gelu"])
+def test_dense_mixture_k_equals_E(act):
+    """k = E: y = sum_e p_e FFN_e(x), computed densely with torch."""
+    cfg = Cfg(T=12, d=5, E=4, k=4, f=3, act=act)
+    t = rand_tensors(cfg, 8, bias=True)
+    o = oracle.forward(cfg, t)
+    x = torch.as_tensor(t["x"], dtype=torch.float64)
+    p = torch.softmax(x @ torch.as_tensor(t["w_router"], dtype=torch.float64).T, dim=1).numpy()
+    ref = sum(p[:, e:e + 1] * torch_ffn(t["x"], t["w1"][e], t["b1"][e], t["w2"][e], t["b2"][e], act)
+              for e in range(cfg.E))
+    assert np.allclose(o["y"], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_shared_experts_equal_one_wide_ffn():
+    """S SwiGLU experts of width f (weight 1 each) = one SwiGLU FFN of width
+    S*f with stacked gate rows, stacked up rows and concatenated down columns."""
+    cfg = Cfg(T=7, d=6, E=3, k=1, f=4, S=3)
+    t = rand_tensors(cfg, 9)
+    o = oracle.forward(cfg, t)
+    f = cfg.f
+    gate = np.concatenate([t["ws1"][s][:f] for s in range(cfg.S)])
+    up = np.concatenate([t["ws1"][s][f:] for s in range(cfg.S)])
+    down = np.concatenate([t["ws2"][s] for s in range(cfg.S)], axis=1)
+    ref = torch_ffn(t["x"], np.concatenate([gate, up]), None, down, None, "swiglu")
+    assert np.allclose(o["shared_y"], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_linearity_in_w2():
+    cfg = Cfg(T=20, d=6, E=4, k=2, f=5)
+    t = rand_tensors(cfg, 10)
+    o1 = oracle.forward(cfg, t)
+    t2 = dict(t, w2=t["w2"] * np.float32(2.0))
+    o2 = oracle.forward(cfg, t2)
+    assert np.array_equal(o2["y"], 2.0 * o1["y"])
+
+
+def test_residual_matches_explainer_assert():
+    """[P2 §4.1]: output == expert outputs + x."""
+    cfg = Cfg(T=11, d=6, E=4, k=2, f=5)
+    t = rand_tensors(cfg, 11)
+    o = oracle.forward(cfg, t)
+    o_res = oracle.forward(Cfg(**{**cfg.__dict__, "add_residual": True}), t)
+    assert np.allclose(o_res["y"], o["y"] + t["x"].astype(np.float64), atol=1e-5)
+
+
+# ---------------------------------------------------------------------------
+# counts, capacity, permutation
+
+
+def test_capacity_exact_values():
+    assert oracle.capacity(1.25, 4096, 2, 16) == 640
+    assert oracle.capacity(1.0, 65536, 6, 64) == 6144
+    assert oracle.capacity(0.0, 100, 2, 4) is None
+    assert oracle.capacity(-1.0, 100, 2, 4) is None
+    assert oracle.capacity(0.5, 6, 1, 3) == 1          # exactly integral: no round-up
+    # binary64 reading: 0.1 is slightly above 1/10, so 0.1 * 30 / 3 > 1
+    assert oracle.capacity(0.1, 30, 1, 3) == 2
+    with pytest.raises(ValueError):
+        oracle.capacity(float("nan"), 10, 1, 2)
+
+
+def _check_perm_structure(o, T, k, E):
+    off, pt, inv = o["offsets"], o["perm_token"], o["inv_row"]
+    R = int(off[-1])
+    assert R + o["n_dropped"] == T * k
+    assert len(pt) == R
+    rows = inv[inv >= 0]
+    assert sorted(rows.tolist()) == list(range(R))       # bijection onto kept rows
+    for e in range(E):
+        seg = pt[off[e]:off[e + 1]]
+        assert (np.diff(seg) > 0).all()                   # strictly increasing tokens
+        for r in range(off[e], off[e + 1]):
+            tt = pt[r]
+            j = int(np.nonzero(o["topk_idx"][tt] == e)[0][0])
+            assert inv[tt, j] == r
+
+
+def test_capacity_one_keeps_lowest_token():
+    cfg = Cfg(T=8, d=4, E=4, k=2, f=2, capacity_factor=0.25)   # C = ceil(0.25*16/4) = 1
+    t = rand_tensors(cfg, 12)
+    o = oracle.forward(cfg, t)
+    assert o["capacity"] == 1
+    _check_perm_structure(o, cfg.T, cfg.k, cfg.E)
+    for e in range(cfg.E):
+        toks = np.nonzero((o["topk_idx"] == e).any(axis=1))[0]
+        seg = o["perm_token"][o["offsets"][e]:o["offsets"][e + 1]].tolist()
+        assert seg == ([int(toks.min())] if len(toks) else [])
+
+
+def test_huge_capacity_equals_no_capacity():
+    cfg = Cfg(T=40, d=6, E=5, k=2, f=3)
+    t = rand_tensors(cfg, 13)
+    a = oracle.forward(cfg, t)
+    b = oracle.forward(Cfg(**{**cfg.__dict__, "capacity_factor": 1e6}), t)
+    for key in ("offsets", "perm_token", "inv_row"):
+        assert np.array_equal(a[key], b[key])
+    assert b["n_dropped"] == 0
+    assert np.array_equal(a["y"], b["y"])
+
+
+def test_drop_heavy_against_sorted_lists():
+    """Flash-config shape at capacity factor 0.5 (C = 256): per-expert kept
+    tokens are the C smallest token indices routed to it."""
+    cfg = get_config("c2", capacity_factor=0.5)
+    t = make_inputs(cfg, accept=lambda x, w, b: oracle.router_gap_ok(x, w, b, cfg.k, cfg.dtype))
+    xd = oracle.decode(t["x"], "bf16")
+    wr = oracle.decode(t["w_router"], "bf16")
+    p, _ = oracle.softmax_lse(oracle.router_logits(xd, wr))
+    idx = oracle.topk_select(p, cfg.k)
+    C = oracle.capacity(cfg.capacity_factor, cfg.T, cfg.k, cfg.E)
+    assert C == 256
+    offsets, pt, ps, inv, nd = oracle.dispatch(idx, cfg.E, C)
+    dropped = 0
+    for e in range(cfg.E):
+        toks = np.nonzero((idx == e).any(axis=1))[0]         # ascending
+        kept = toks[:C]
+        dropped += len(toks) - len(kept)
+        assert pt[offsets[e]:offsets[e + 1]].tolist() == kept.tolist()
+        for tt in toks[C:]:
+            j = int(np.nonzero(idx[tt] == e)[0][0])
+            assert inv[tt, j] == -1
+    assert nd == dropped > 0
+
+
+def test_all_dropped_token_outputs_shared_only():
+    cfg = Cfg(T=6, d=4, E=4, k=2, f=3, S=1, capacity_factor=1 / 3)  # C = ceil(6*2/4/3) = 1
+    bias = np.array([40.0, 30.0, 0.0, 0.0])   # every token picks experts 0 and 1
+    t = rand_tensors(cfg, 14, router_bias=bias)
+    o = oracle.forward(cfg, t)
+    assert o["capacity"] == 1
+    assert (o["inv_row"][1:] == -1).all()
+    assert np.array_equal(o["y"][1:], o["shared_y"][1:])
+
+
+def test_token_permutation_invariance():
+    cfg = Cfg(T=30, d=6, E=5, k=2, f=4, S=1)
+    t = rand_tensors(cfg, 15)
+    o = oracle.forward(cfg, t)
+    perm = np.random.default_rng(0).permutation(cfg.T)
+    o2 = oracle.forward(cfg, dict(t, x=t["x"][perm]))
+    assert np.allclose(o2["y"], o["y"][perm], rtol=1e-12, atol=1e-14)
+    assert np.array_equal(o2["counts"], o["counts"])
+    assert np.array_equal(o2["topk_idx"], o["topk_idx"][perm])
+    assert abs(o2["lb"] - o["lb"]) < 1e-12 and abs(o2["z"] - o["z"]) < 1e-12
+
+
+def test_sampled_rows_match_full():
+    cfg = Cfg(T=25, d=6, E=5, k=2, f=4, S=2, capacity_factor=1.0)
+    t = rand_tensors(cfg, 16)
+    full = oracle.forward(cfg, t)
+    rows = [0, 3, 24, 7]
+    part = oracle.forward(cfg, t, rows=rows)
+    assert np.array_equal(part["rows"], sorted(rows))
+    assert np.allclose(part["y"], full["y"][sorted(rows)], rtol=1e-13, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# input decoding and the parameter arithmetic printed by a page
+
+
+def test_bf16_decode_known_bits():
+    bits = np.array([0x3F80, 0xC000, 0x0000, 0x3E80, 0x7F7F], dtype=np.uint16)
+    v = oracle.decode(bits, "bf16")
+    assert v[:4].tolist() == [1.0, -2.0, 0.0, 0.25]
+    assert v[4] == (2 - 2 ** -7) * 2.0 ** 127
+    with pytest.raises(TypeError):
+        oracle.decode(np.zeros(2, np.float32), "bf16")
+
+
+def test_param_arithmetic_fixture():
+    """[P1 §3.3]: d_model 1024, 8 experts, top-2, d_ff 1024 -> 2M per expert,
+    16M total, dense 4*d FFN 8M, 4M active; two-matrix experts as in
+    [P3 §3.1] (num_experts * hidden * ffn * 2)."""
+    with open(os.path.join(GOLDEN, "p1_param_arithmetic.json")) as fh:
+        g = json.load(fh)
+    d, E, k, dff = g["d_model"], g["n_expert"], g["top_k"], g["d_ff"]
+    per_expert = 2 * d * dff
+    assert round(per_expert / 2 ** 20) == g["per_expert_M"]
+    assert round(E * per_expert / 2 ** 20) == g["total_M"]
+    assert round(2 * d * 4 * d / 2 ** 20) == g["dense_M"]
+    assert round(k * per_expert / 2 ** 20) == g["active_M"]
