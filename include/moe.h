@@ -1,0 +1,214 @@
+/*
+ * moe.h - C ABI of an MI355X (gfx950) library for the forward pass of a
+ * top-k routed Mixture-of-Experts FFN layer.
+ *
+ * Page keys used in the citations below (web pages; sections as printed):
+ *   [P1] "Naive-N0.5-Flash" open-source MoE blog, wzjinhao.cn/news/74695
+ *   [P2] "The quietly activated expert group" MoE explainer, mqxn.cn/news/15586
+ *   [P3] "Small MoE language model from scratch" tutorial, lshu.cn/news/325687
+ *   [P4] "OpenMythos" re-implementation blog, lpnh.cn/news/1735864
+ *   [P5] FLAME-MoE research-platform summary, lsdiaocha.cn/2025/0530/3166997.shtml
+ *
+ * Conventions shared by every call
+ *   - All tensor arguments are device pointers owned by the caller; the
+ *     library never allocates, frees or synchronises.  Work is enqueued on
+ *     `stream` and results are valid once the caller has synchronised it.
+ *   - Matrices are row-major.  Weights use the nn.Linear [out, in] layout, so
+ *     both operands of every product are contiguous along the reduction.
+ *   - "act-dtype" tensors (x, expert weights and biases, intermediate and
+ *     output activations) are float32 when cfg->dtype == MOE_DTYPE_F32 and
+ *     bfloat16 when cfg->dtype == MOE_DTYPE_BF16.  Router bias, routing
+ *     weights and log-sum-exp values are always float32; indices int32.
+ *   - Pointers to act-dtype and int32 data must be 16-byte aligned and
+ *     d_model and d_ffn must be multiples of 8 (rows are read with 16-byte
+ *     vector loads).
+ *   - Workspace: calls that need scratch memory take (ws, ws_bytes).  With
+ *     ws == NULL the call only writes the required size to *ws_bytes and
+ *     returns MOE_OK (query mode, nothing is launched).  Otherwise *ws_bytes
+ *     must hold the size of ws; if it is too small the required size is
+ *     written back and MOE_ERR_WORKSPACE is returned.
+ *   - Errors are reported before anything is enqueued; on error nothing is
+ *     written.  A failed launch returns MOE_ERR_HIP.  No C++ exception
+ *     crosses this interface.
+ *   - Results are deterministic: there are no floating-point atomics, and
+ *     every reduction runs in a fixed order.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null required pointer, bad size or option */
+  MOE_ERR_UNSUPPORTED = 2, /* valid but not built (e.g. n_experts > 512) */
+  MOE_ERR_WORKSPACE = 3,   /* workspace too small; *ws_bytes = required */
+  MOE_ERR_HIP = 4          /* a HIP launch failed */
+} moe_status;
+
+typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype;
+
+/* Expert FFN form.  GELU: out = W2 gelu(W1 x + b1) + b2 with the exact erf
+ * GELU ([P3 §3.1]).  SWIGLU: out = W2 (silu(W1g x) * (W1u x)) with W1 the
+ * gate rows followed by the up rows ([P2 §3.1] names SwiGLU experts). */
+typedef enum { MOE_ACT_GELU = 0, MOE_ACT_SWIGLU = 1 } moe_act;
+
+typedef struct {
+  int64_t n_tokens;       /* T >= 1: tokens (batch * seq), [P3 §3.1] flattening */
+  int32_t d_model;        /* d: hidden size */
+  int32_t n_experts;      /* E: routed experts, 1 <= E <= 512 */
+  int32_t top_k;          /* k: 1 <= k <= E ([P4 §2.1]: configurable k) */
+  int32_t d_ffn;          /* f: expert intermediate size */
+  int32_t n_shared;       /* S >= 0: always-active shared experts ([P4 §2.1]) */
+  int32_t dtype;          /* moe_dtype */
+  int32_t act;            /* moe_act */
+  double capacity_factor; /* <= 0: no limit; else C = ceil(cf*T*k/E), exact on
+                             the binary64 value of cf ([P4 §3.1]); NaN rejected */
+  int32_t add_residual;   /* 1: y += x ([P2 §4.1] adds the input inside the layer) */
+  int32_t reserved;       /* must be 0 */
+} moe_config;
+
+/* Device pointers to one layer's parameters (host struct, read during the call). */
+typedef struct {
+  const void* w_router;     /* [E, d] act-dtype, required */
+  const float* router_bias; /* [E] float32 logit bias added before the softmax, or NULL */
+  const void* w1;           /* [E, 2f, d] (SWIGLU: gate rows then up rows) or [E, f, d] (GELU) */
+  const void* b1;           /* [E, 2f] / [E, f] act-dtype, or NULL */
+  const void* w2;           /* [E, d, f] */
+  const void* b2;           /* [E, d] act-dtype, or NULL */
+  const void* shared_w1;    /* [S, 2f, d] / [S, f, d]; required iff S > 0 */
+  const void* shared_b1;    /* [S, 2f] / [S, f] or NULL */
+  const void* shared_w2;    /* [S, d, f]; required iff S > 0 */
+  const void* shared_b2;    /* [S, d] or NULL */
+} moe_weights;
+
+/* Auxiliary statistics, written to device memory.
+ * f_e = counts_e / (T*k) with the counts taken before capacity, P_e = mean
+ * over all tokens of the full softmax ([P4 §3.1] load-balance loss
+ * E * sum f_e P_e); z = mean over tokens of logsumexp(logits)^2 (router
+ * z-loss named in [P5 §2]); weighted = 0.01 lb + 0.001 z, the coefficients
+ * [P5 §2] reports. */
+typedef struct {
+  double load_balance;
+  double z_loss;
+  double weighted;
+  int64_t n_dropped; /* assignments over capacity */
+  int64_t capacity;  /* C, or -1 when there is no limit */
+  int64_t n_kept;    /* R = T*k - n_dropped */
+} moe_aux;
+
+/* Static description of a status code. */
+const char* moe_status_string(moe_status s);
+
+/*
+ * moe_route - router GEMM, softmax, top-k and renormalisation
+ * ([P2 §3.2] a single linear layer; [P3 §3.1] steps 1-2; [P4 §3.1]
+ * routing and top-k selection).
+ *   logits[t,e] = sum_c x[t,c] W_r[e,c] + router_bias[e]   (float32 accumulate)
+ *   p = softmax_e(logits), lse[t] = logsumexp_e(logits[t,:])
+ *   topk_idx[t,:] = the k experts of largest logit (= largest p), sorted by
+ *                   descending logit, lower index first on exact ties
+ *   topk_w[t,j]   = p[t,idx] / sum_j' p[t,idx']
+ * x [T,d], w_router [E,d] act-dtype; router_bias [E] float32 or NULL;
+ * topk_idx [T,k] int32, topk_w [T,k] float32, token_lse [T] float32 (may be
+ * NULL).  The call also leaves per-block routing statistics (expert counts,
+ * probability sums, sum of lse^2) in ws; moe_aux_stats reads them from the
+ * same ws, which must not be reused in between.
+ */
+moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
+                     const float* router_bias, int32_t* topk_idx, float* topk_w,
+                     float* token_lse, void* ws, size_t* ws_bytes, hipStream_t stream);
+
+/*
+ * moe_permute - per-expert counts, capacity and a stable expert-contiguous
+ * permutation ([P4 §3.1] capacity/overflow and its flatten-and-reorder
+ * dispatch; [P1 §2.2] expert capacity).
+ *   expert_counts[e] = #{(t,j): topk_idx[t,j] == e}          (before capacity)
+ *   within expert e the assignments are ranked by ascending token index; the
+ *   first C are kept (all without a limit); kept rows are ordered by
+ *   (expert, token): expert_offsets[E+1] is the exclusive scan of the kept
+ *   counts, perm_token[row] = t, perm_w[row] = topk_w[t,j],
+ *   inv_row[t,j] = row or -1 if dropped, *n_dropped = dropped assignments.
+ * topk_idx [T,k] int32 with values in [0,E) (checked on device: an invalid
+ * index is counted as dropped and reported through n_dropped = -1);
+ * topk_w [T,k] float32 (required iff perm_w != NULL); x [T,d] act-dtype
+ * (required iff x_perm != NULL); outputs: expert_counts [E],
+ * expert_offsets [E+1], perm_token [T*k] (first R entries valid),
+ * perm_w [T*k] or NULL, inv_row [T*k], x_perm [T*k, d] or NULL (row r =
+ * x[perm_token[r]]), n_dropped [1] int32.
+ */
+moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, const float* topk_w,
+                       const void* x, int32_t* expert_counts, int32_t* expert_offsets,
+                       int32_t* perm_token, float* perm_w, int32_t* inv_row, void* x_perm,
+                       int32_t* n_dropped, void* ws, size_t* ws_bytes, hipStream_t stream);
+
+/*
+ * moe_expert_ffn - grouped expert FFN over expert-contiguous rows
+ * ([P4 §3.1] run every expert on its gathered rows; [P1 §4.2] group tokens
+ * by expert and run one large product per expert).
+ * Group g covers rows [group_offsets[g], group_offsets[g+1]) (device array,
+ * non-decreasing, last entry <= rows_max).  Row r reads A row
+ * a_rows ? a_rows[r] : r of `a` [*, d].  Each group is the sum of n_seg
+ * FFNs of width f with weight 1 (n_seg = 1 for routed experts; the S shared
+ * experts form one group with n_seg = S):
+ *   out[r,:] = sum_{s<n_seg} FFN_{g*n_seg+s}(a[row(r),:])
+ * w1 [n_groups*n_seg, 2f or f, d], b1 [.., 2f or f] or NULL,
+ * w2 [n_groups*n_seg, d, f], b2 [.., d] or NULL, out [rows_max, d]; rows of
+ * out outside every group are not written.  ws holds the intermediate
+ * activations (rows_max x n_seg*f) and tile tables.
+ */
+moe_status moe_expert_ffn(const moe_config* cfg, int32_t n_groups, int32_t n_seg,
+                          int64_t rows_max, const void* a, const int32_t* a_rows,
+                          const int32_t* group_offsets, const void* w1, const void* b1,
+                          const void* w2, const void* b2, void* out, void* ws,
+                          size_t* ws_bytes, hipStream_t stream);
+
+/*
+ * moe_combine - weighted gather back to token order, atomic-free
+ * ([P1 §2.1] weighted sum of the selected experts; [P5 §2] weights are the
+ * normalised routing scores; [P2 §4.1] optional residual).
+ *   y[t,:] = shared_y[t,:] + sum_{j: inv_row[t,j] >= 0} topk_w[t,j] * y_perm[inv_row[t,j],:]
+ *            (+ residual[t,:])
+ * summed in float32 in the order shared, j = 0..k-1, residual.
+ * y_perm [R,d], shared_y [T,d] or NULL, residual [T,d] or NULL, y [T,d]
+ * act-dtype; inv_row [T,k] int32; topk_w [T,k] float32.
+ */
+moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* inv_row,
+                       const float* topk_w, const void* shared_y, const void* residual,
+                       void* y, hipStream_t stream);
+
+/*
+ * moe_aux_stats - load-balance and z-loss statistics ([P4 §3.1]
+ * load-balance loss; [P5 §2] router z-loss and coefficients) from the
+ * routing statistics moe_route left in route_ws, the pre-capacity
+ * expert_counts [E] and n_dropped [1] of moe_permute.  Writes one moe_aux
+ * to device memory `aux`.  route_ws / route_ws_bytes are the workspace
+ * given to moe_route.
+ */
+moe_status moe_aux_stats(const moe_config* cfg, const int32_t* expert_counts,
+                         const int32_t* n_dropped, const void* route_ws, size_t route_ws_bytes,
+                         moe_aux* aux, hipStream_t stream);
+
+/*
+ * moe_forward - the whole layer: route, permute, routed and shared expert
+ * FFNs, combine and aux statistics ([P3 §3.1] forward returns the output
+ * and the auxiliary loss).  x, y [T,d] act-dtype.  Optional outputs (NULL
+ * to skip): topk_idx [T,k], topk_w [T,k], expert_counts [E], aux (device).
+ * ws: query with ws == NULL.
+ */
+moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* x, void* y,
+                       int32_t* topk_idx, float* topk_w, int32_t* expert_counts, moe_aux* aux,
+                       void* ws, size_t* ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,480 @@
+// Grouped expert GEMMs with fused activation epilogues.
+//
+// [P4 §3.1] (and [P1 §4.2]): gather every expert's tokens into one tensor and
+// run each expert once over all of its rows instead of looping token by token;
+// [P2 §3.1]: an expert is two linear maps around a SwiGLU-type non-linearity;
+// [P3 §3.1]: Linear + GELU + Linear with biases.
+//
+// Up GEMM   H[r, s*f + n] = act(A[row(r)] . W1[g*S+s]^T)        K = d
+//           SwiGLU: one tile owns 64 H columns and loads the 64 matching
+//           gate rows and the 64 matching up rows of W1, so silu(g)*u is
+//           formed in registers; GELU: 128 columns + bias.
+// Down GEMM Y[r, n] = sum_s H[r, s*f:(s+1)*f] . W2[g*S+s][n]^T   K = S*f
+//           (S shared experts summed inside the K loop).
+//
+// Rows are grouped by expert (group g = rows [off[g], off[g+1])); the tile
+// list is flattened on the device from the offsets, so the host never reads
+// the per-expert counts.  The grid is sized for the worst case
+// ceil(rows_max / BM) + n_groups row tiles; surplus workgroups exit at once.
+//
+// bf16 kernel: 128x128 tile, BK = 64, 4 waves (2x2), each wave a 64x64
+// sub-tile of v_mfma_f32_32x32x16_bf16 (fp32 accumulation), A and B tiles
+// double-buffered through LDS with register prefetch of the next K tile.
+// f32 kernel: 64x64 tile, FMA on the vector ALUs (no reduced precision).
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+// ---------------------------------------------------------------------------
+// tile lookup: flattened row-tile index -> (group, first row, rows)
+
+struct TileInfo {
+  int group;   // -1: no such tile
+  int64_t row0;
+  int rows;
+};
+
+// Executed by the first wave; result broadcast through LDS by the caller.
+// off == nullptr: a single group covering rows [0, rows_max).
+__device__ TileInfo find_row_tile(const int32_t* __restrict__ off, int n_groups, int64_t rows_max,
+                                  int BM, int mt) {
+  const int lane = threadIdx.x % kWave;
+  if (off == nullptr) {
+    TileInfo t;
+    const int64_t r0 = (int64_t)mt * BM;
+    t.group = r0 < rows_max ? 0 : -1;
+    t.row0 = r0;
+    t.rows = (int)min((int64_t)BM, rows_max - r0);
+    return t;
+  }
+  int64_t before = 0;  // tiles in groups already passed
+  for (int g0 = 0; g0 < n_groups; g0 += kWave) {
+    const int g = g0 + lane;
+    int tiles = 0;
+    int64_t start = 0;
+    int rows = 0;
+    if (g < n_groups) {
+      start = off[g];
+      rows = off[g + 1] - (int)start;
+      tiles = (rows + BM - 1) / BM;
+    }
+    // inclusive prefix of tiles across the wave
+    int inc = tiles;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int v = __shfl_up(inc, o, kWave);
+      if (lane >= o) inc += v;
+    }
+    const int64_t hi = before + inc;
+    const int64_t lo = hi - tiles;
+    const unsigned long long hit = __ballot(g < n_groups && mt >= lo && mt < hi);
+    if (hit) {
+      const int src = __ffsll((long long)hit) - 1;
+      const int64_t lo_s = __shfl(lo, src, kWave);
+      const int64_t start_s = __shfl(start, src, kWave);
+      const int rows_s = __shfl(rows, src, kWave);
+      const int local = mt - (int)lo_s;
+      TileInfo t;
+      t.group = g0 + src;
+      t.row0 = start_s + (int64_t)local * BM;
+      t.rows = min(BM, rows_s - local * BM);
+      // never touch rows past rows_max, whatever the offsets say
+      if (t.row0 + t.rows > rows_max) t.rows = (int)max((int64_t)0, rows_max - t.row0);
+      if (t.rows <= 0) t.group = -1;
+      return t;
+    }
+    before += __shfl(inc, kWave - 1, kWave);
+  }
+  TileInfo t;
+  t.group = -1;
+  t.row0 = 0;
+  t.rows = 0;
+  return t;
+}
+
+__device__ __forceinline__ float silu_f(float g) { return g / (1.f + __expf(-g)); }
+__device__ __forceinline__ float gelu_f(float z) { return 0.5f * z * (1.f + erff(z * 0.70710678118654752f)); }
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA kernel
+
+constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int kPitch = BK + 8;  // bf16 per LDS row (pad spreads rows over banks)
+constexpr int kGemmThreads = 256;
+
+template <int KIND, int ACT, bool BIAS>
+__global__ void __launch_bounds__(kGemmThreads)
+gemm_bf16_kernel(GemmDesc p, int tiles_n) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * kPitch];
+  __shared__ TileInfo s_tile;
+
+  const int mt = blockIdx.x / tiles_n;
+  const int nt = blockIdx.x % tiles_n;
+  if (threadIdx.x < kWave) {
+    TileInfo t = find_row_tile(p.group_off, p.n_groups, p.rows_max, BM, mt);
+    if (threadIdx.x == 0) s_tile = t;
+  }
+  __syncthreads();
+  const TileInfo tile = s_tile;
+  if (tile.group < 0) return;
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave;
+  const int wm = wave / 2, wn = wave % 2;
+  const int S = p.n_seg, d = p.d, f = p.f;
+  constexpr bool kSwiglu = (KIND == kGemmUp && ACT == MOE_ACT_SWIGLU);
+  const int bnh = kSwiglu ? BN / 2 : BN;  // output columns per tile
+
+  // --- which output columns / weight rows this tile covers
+  int seg = 0, n0;
+  const uint16_t* wbase;
+  int K, n_valid;  // reduction length per segment, output columns valid in this tile
+  if (KIND == kGemmUp) {
+    const int tpn = (f + bnh - 1) / bnh;
+    seg = nt / tpn;
+    n0 = (nt % tpn) * bnh;
+    const int rows1 = kSwiglu ? 2 * f : f;
+    wbase = static_cast<const uint16_t*>(p.w) + ((int64_t)tile.group * S + seg) * rows1 * (int64_t)d;
+    K = d;
+    n_valid = min(bnh, f - n0);
+  } else {
+    n0 = nt * BN;
+    wbase = static_cast<const uint16_t*>(p.w) + (int64_t)tile.group * S * (int64_t)d * f;
+    K = f;
+    n_valid = min(BN, d - n0);
+  }
+  const int nk_seg = (K + BK - 1) / BK;
+  const int nk = (KIND == kGemmUp) ? nk_seg : S * nk_seg;
+
+  // --- per-thread load slots: 4 x 16 B of A and of B per K tile
+  const int lrow = tid / 8;          // 0..31 (+32 i)
+  const int lk = (tid % 8) * 8;      // bf16 offset in the K tile
+  const uint16_t* arow[4];
+  const uint16_t* brow[4];
+  bool bok[4];
+  const uint16_t* A = static_cast<const uint16_t*>(p.a);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = lrow + 32 * i;
+    const int64_t gr = tile.row0 + (r < tile.rows ? r : 0);
+    const int64_t src = p.a_rows ? (int64_t)p.a_rows[gr] : gr;
+    arow[i] = A + src * p.lda;
+    int wr;  // weight row in the (segment's) matrix
+    if (kSwiglu) {
+      const int c = (r < 64) ? r : r - 64;
+      bok[i] = c < n_valid;
+      wr = (r < 64 ? 0 : f) + n0 + (bok[i] ? c : 0);
+      brow[i] = wbase + (int64_t)wr * d;
+    } else if (KIND == kGemmUp) {
+      bok[i] = r < n_valid;
+      wr = n0 + (bok[i] ? r : 0);
+      brow[i] = wbase + (int64_t)wr * d;
+    } else {
+      bok[i] = r < n_valid;
+      wr = n0 + (bok[i] ? r : 0);
+      brow[i] = wbase + (int64_t)wr * f;
+    }
+  }
+
+  uint4 ra[4], rb[4];
+  auto load_tile = [&](int kt) {
+    int s = 0, kk = kt * BK;
+    if (KIND == kGemmDown) {
+      s = kt / nk_seg;
+      kk = (kt % nk_seg) * BK;
+    }
+    const bool kok = kk + lk < K;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ra[i] = make_uint4(0, 0, 0, 0);
+      rb[i] = make_uint4(0, 0, 0, 0);
+      if (kok) {
+        const int64_t acol = (KIND == kGemmDown) ? (int64_t)s * f + kk + lk : kk + lk;
+        ra[i] = *reinterpret_cast<const uint4*>(arow[i] + acol);
+        if (bok[i]) {
+          const int64_t boff = (KIND == kGemmDown) ? (int64_t)s * d * f + kk + lk : kk + lk;
+          rb[i] = *reinterpret_cast<const uint4*>(brow[i] + boff);
+        }
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = lrow + 32 * i;
+      *reinterpret_cast<uint4*>(&As[buf][r * kPitch + lk]) = ra[i];
+      *reinterpret_cast<uint4*>(&Bs[buf][r * kPitch + lk]) = rb[i];
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  // B rows of this wave's two 32-column MFMA blocks
+  int bsub[2];
+  if (kSwiglu) {
+    bsub[0] = wn * 32;        // gate
+    bsub[1] = 64 + wn * 32;   // up (same output columns)
+  } else {
+    bsub[0] = wn * 64;
+    bsub[1] = wn * 64 + 32;
+  }
+  const int fr = lane % 32;        // fragment row
+  const int fk = 32 * (lane / 32); // this lane's 32-element K half of the tile
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load_tile(kt + 1);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8 fa[2], fb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        fa[i] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4*>(&As[cur][(wm * 64 + i * 32 + fr) * kPitch + fk + 8 * ks]));
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        fb[j] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4*>(&Bs[cur][(bsub[j] + fr) * kPitch + fk + 8 * ks]));
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) store_tile(cur ^ 1);
+    __syncthreads();
+  }
+
+  // --- epilogue.  32x32 C layout: lane holds column lane%32 and rows
+  // 8*(q/4) + 4*(lane/32) + q%4, q = 0..15.
+  uint16_t* out = static_cast<uint16_t*>(p.out);
+  const uint16_t* bias = static_cast<const uint16_t*>(p.bias);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int r = wm * 64 + i * 32 + 8 * (q / 4) + 4 * (lane / 32) + (q % 4);
+      if (r >= tile.rows) continue;
+      const int64_t grow = tile.row0 + r;
+      if (kSwiglu) {
+        const int c = wn * 32 + fr;
+        if (c < n_valid) {
+          float g = acc[i][0][q], u = acc[i][1][q];
+          if (BIAS) {
+            const uint16_t* b = bias + ((int64_t)tile.group * S + seg) * 2 * f;
+            g += bf16_to_f32(b[n0 + c]);
+            u += bf16_to_f32(b[f + n0 + c]);
+          }
+          out[grow * p.ldo + (int64_t)seg * f + n0 + c] = f32_to_bf16(silu_f(g) * u);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int c = wn * 64 + j * 32 + fr;
+          if (c >= n_valid) continue;
+          float v = acc[i][j][q];
+          if (KIND == kGemmUp) {
+            if (BIAS) v += bf16_to_f32(bias[((int64_t)tile.group * S + seg) * f + n0 + c]);
+            v = gelu_f(v);
+            out[grow * p.ldo + (int64_t)seg * f + n0 + c] = f32_to_bf16(v);
+          } else {
+            if (BIAS)
+              for (int s = 0; s < S; ++s)
+                v += bf16_to_f32(bias[((int64_t)tile.group * S + s) * d + n0 + c]);
+            out[grow * p.ldo + n0 + c] = f32_to_bf16(v);
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// float32 kernel (vector ALU FMA)
+
+constexpr int FBM = 64, FBN = 64, FBK = 16;
+
+template <int KIND, int ACT, bool BIAS>
+__global__ void __launch_bounds__(256)
+gemm_f32_kernel(GemmDesc p, int tiles_n) {
+  __shared__ float As[FBK][FBM + 4];
+  __shared__ float Bs[FBK][FBN + 4];
+  __shared__ TileInfo s_tile;
+  const int mt = blockIdx.x / tiles_n;
+  const int nt = blockIdx.x % tiles_n;
+  if (threadIdx.x < kWave) {
+    TileInfo t = find_row_tile(p.group_off, p.n_groups, p.rows_max, FBM, mt);
+    if (threadIdx.x == 0) s_tile = t;
+  }
+  __syncthreads();
+  const TileInfo tile = s_tile;
+  if (tile.group < 0) return;
+
+  const int tid = threadIdx.x;
+  const int S = p.n_seg, d = p.d, f = p.f;
+  constexpr bool kSwiglu = (KIND == kGemmUp && ACT == MOE_ACT_SWIGLU);
+  const int bnh = kSwiglu ? FBN / 2 : FBN;
+  int seg = 0, n0, K, n_valid;
+  const float* wbase;
+  if (KIND == kGemmUp) {
+    const int tpn = (f + bnh - 1) / bnh;
+    seg = nt / tpn;
+    n0 = (nt % tpn) * bnh;
+    const int rows1 = kSwiglu ? 2 * f : f;
+    wbase = static_cast<const float*>(p.w) + ((int64_t)tile.group * S + seg) * rows1 * (int64_t)d;
+    K = d;
+    n_valid = min(bnh, f - n0);
+  } else {
+    n0 = nt * FBN;
+    wbase = static_cast<const float*>(p.w) + (int64_t)tile.group * S * (int64_t)d * f;
+    K = f;
+    n_valid = min(FBN, d - n0);
+  }
+  const int nk_seg = (K + FBK - 1) / FBK;
+  const int nk = (KIND == kGemmUp) ? nk_seg : S * nk_seg;
+
+  // load slot: row tid/4 (0..63), 4 consecutive k at (tid%4)*4
+  const int lr = tid / 4, lk = (tid % 4) * 4;
+  const float* A = static_cast<const float*>(p.a);
+  const int64_t gr = tile.row0 + (lr < tile.rows ? lr : 0);
+  const float* arow = A + (p.a_rows ? (int64_t)p.a_rows[gr] : gr) * p.lda;
+  bool bok;
+  const float* brow;
+  if (kSwiglu) {
+    const int c = lr < 32 ? lr : lr - 32;
+    bok = c < n_valid;
+    brow = wbase + (int64_t)((lr < 32 ? 0 : f) + n0 + (bok ? c : 0)) * d;
+  } else if (KIND == kGemmUp) {
+    bok = lr < n_valid;
+    brow = wbase + (int64_t)(n0 + (bok ? lr : 0)) * d;
+  } else {
+    bok = lr < n_valid;
+    brow = wbase + (int64_t)(n0 + (bok ? lr : 0)) * f;
+  }
+
+  // compute slot: rows ty*4..+4; columns: SwiGLU {2tx, 2tx+1} of gate and up
+  const int tx = tid % 16, ty = tid / 16;
+  int cols[4];
+  if (kSwiglu) {
+    cols[0] = 2 * tx; cols[1] = 2 * tx + 1; cols[2] = 32 + 2 * tx; cols[3] = 33 + 2 * tx;
+  } else {
+    for (int j = 0; j < 4; ++j) cols[j] = 4 * tx + j;
+  }
+  float acc[4][4] = {};
+  for (int kt = 0; kt < nk; ++kt) {
+    int s = 0, kk = kt * FBK;
+    if (KIND == kGemmDown) {
+      s = kt / nk_seg;
+      kk = (kt % nk_seg) * FBK;
+    }
+    float4 va = make_float4(0.f, 0.f, 0.f, 0.f), vb = va;
+    if (kk + lk < K) {
+      const int64_t acol = (KIND == kGemmDown) ? (int64_t)s * f + kk + lk : kk + lk;
+      va = *reinterpret_cast<const float4*>(arow + acol);
+      if (bok) {
+        const int64_t boff = (KIND == kGemmDown) ? (int64_t)s * d * f + kk + lk : kk + lk;
+        vb = *reinterpret_cast<const float4*>(brow + boff);
+      }
+    }
+    As[lk + 0][lr] = va.x; As[lk + 1][lr] = va.y; As[lk + 2][lr] = va.z; As[lk + 3][lr] = va.w;
+    Bs[lk + 0][lr] = vb.x; Bs[lk + 1][lr] = vb.y; Bs[lk + 2][lr] = vb.z; Bs[lk + 3][lr] = vb.w;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < FBK; ++q) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[q][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Bs[q][cols[j]];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+
+  float* out = static_cast<float*>(p.out);
+  const float* bias = static_cast<const float*>(p.bias);
+  for (int i = 0; i < 4; ++i) {
+    const int r = ty * 4 + i;
+    if (r >= tile.rows) continue;
+    const int64_t grow = tile.row0 + r;
+    if (kSwiglu) {
+      for (int j = 0; j < 2; ++j) {
+        const int c = 2 * tx + j;
+        if (c >= n_valid) continue;
+        float g = acc[i][j], u = acc[i][j + 2];
+        if (BIAS) {
+          const float* b = bias + ((int64_t)tile.group * S + seg) * 2 * f;
+          g += b[n0 + c];
+          u += b[f + n0 + c];
+        }
+        out[grow * p.ldo + (int64_t)seg * f + n0 + c] = silu_f(g) * u;
+      }
+    } else {
+      for (int j = 0; j < 4; ++j) {
+        const int c = cols[j];
+        if (c >= n_valid) continue;
+        float v = acc[i][j];
+        if (KIND == kGemmUp) {
+          if (BIAS) v += bias[((int64_t)tile.group * S + seg) * f + n0 + c];
+          out[grow * p.ldo + (int64_t)seg * f + n0 + c] = gelu_f(v);
+        } else {
+          if (BIAS)
+            for (int s2 = 0; s2 < S; ++s2) v += bias[((int64_t)tile.group * S + s2) * d + n0 + c];
+          out[grow * p.ldo + n0 + c] = v;
+        }
+      }
+    }
+  }
+}
+
+template <int KIND, int ACT, bool BIAS>
+hipError_t launch_t(const moe_config& c, const GemmDesc& g, hipStream_t s) {
+  const bool bf = c.dtype == MOE_DTYPE_BF16;
+  const int bm = bf ? BM : FBM;
+  const int bn = bf ? BN : FBN;
+  int tiles_n;
+  if (KIND == kGemmUp) {
+    const int bnh = (ACT == MOE_ACT_SWIGLU) ? bn / 2 : bn;
+    tiles_n = g.n_seg * ((g.f + bnh - 1) / bnh);
+  } else {
+    tiles_n = (g.d + bn - 1) / bn;
+  }
+  const int64_t tiles_m = (g.rows_max + bm - 1) / bm + g.n_groups;
+  const int64_t grid = tiles_m * tiles_n;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  if (bf)
+    gemm_bf16_kernel<KIND, ACT, BIAS><<<dim3((unsigned)grid), dim3(kGemmThreads), 0, s>>>(g, tiles_n);
+  else
+    gemm_f32_kernel<KIND, ACT, BIAS><<<dim3((unsigned)grid), dim3(256), 0, s>>>(g, tiles_n);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const moe_config& c, GemmKind kind, const GemmDesc& g, hipStream_t s) {
+  const bool bias = g.bias != nullptr;
+  if (kind == kGemmDown)
+    return bias ? launch_t<kGemmDown, 0, true>(c, g, s) : launch_t<kGemmDown, 0, false>(c, g, s);
+  if (g.act == MOE_ACT_SWIGLU)
+    return bias ? launch_t<kGemmUp, MOE_ACT_SWIGLU, true>(c, g, s)
+                : launch_t<kGemmUp, MOE_ACT_SWIGLU, false>(c, g, s);
+  return bias ? launch_t<kGemmUp, MOE_ACT_GELU, true>(c, g, s)
+              : launch_t<kGemmUp, MOE_ACT_GELU, false>(c, g, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,383 @@
+// C ABI of the MoE layer library: argument validation, exact capacity,
+// workspace planning and the launch sequences of the six entry points.
+// Nothing here allocates device memory or synchronises; every launch goes to
+// the caller's stream.
+#include <cmath>
+#include <cstring>
+
+#include "moe_internal.h"
+
+namespace moe {
+size_t router_smem_bytes(const moe_config& c);
+}
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+// Carves aligned regions out of a workspace; with base == nullptr it only
+// measures.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <class T>
+  T* take(size_t n) {
+    off = (off + kAlign - 1) / kAlign * kAlign;
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += n * sizeof(T);
+    return p;
+  }
+};
+
+size_t act_bytes(const moe_config& c) { return c.dtype == MOE_DTYPE_BF16 ? 2 : 4; }
+int64_t route_blocks(const moe_config& c) {
+  const int BT = route_block_tokens(c.n_experts);
+  return (c.n_tokens + BT - 1) / BT;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+moe_status check_config(const moe_config* c) {
+  if (c == nullptr) return MOE_ERR_INVALID_ARG;
+  if (c->n_tokens < 1 || c->d_model < 8 || c->d_ffn < 8 || c->n_experts < 1 || c->top_k < 1 ||
+      c->top_k > c->n_experts || c->n_shared < 0 || c->reserved != 0)
+    return MOE_ERR_INVALID_ARG;
+  if (c->dtype != MOE_DTYPE_F32 && c->dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
+  if (c->act != MOE_ACT_GELU && c->act != MOE_ACT_SWIGLU) return MOE_ERR_INVALID_ARG;
+  if (c->add_residual != 0 && c->add_residual != 1) return MOE_ERR_INVALID_ARG;
+  if (std::isnan(c->capacity_factor) || std::isinf(c->capacity_factor) ||
+      c->capacity_factor > 1073741824.0)
+    return MOE_ERR_INVALID_ARG;
+  if (c->d_model % 8 != 0 || c->d_ffn % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (c->n_experts > kMaxExperts || c->n_shared > 64) return MOE_ERR_UNSUPPORTED;
+  // row indices are int32
+  if (c->n_tokens * (int64_t)c->top_k >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)c->d_ffn * (c->n_shared > 1 ? c->n_shared : 1) >= (int64_t)1 << 30)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// C = ceil(cf * T * k / E) on the exact binary64 value of cf; -1 = no limit.
+int64_t exact_capacity(const moe_config& c) {
+  const double cf = c.capacity_factor;
+  if (!(cf > 0.0)) return -1;
+  int e2 = 0;
+  const double m = std::frexp(cf, &e2);                      // cf = m * 2^e2, m in [0.5, 1)
+  const unsigned __int128 M = (unsigned __int128)std::ldexp(m, 53);  // exact 53-bit integer
+  const unsigned __int128 N = (unsigned __int128)(c.n_tokens * (int64_t)c.top_k);
+  const int shift = e2 - 53;                                 // cf = M * 2^shift
+  unsigned __int128 num = M * N;
+  unsigned __int128 den = (unsigned __int128)c.n_experts;
+  if (shift >= 0) {
+    num <<= shift;  // cf <= 2^30 keeps this below 2^115
+  } else {
+    if (-shift >= 100) return 1;  // cf*T*k/E < 1 and > 0
+    den <<= -shift;
+  }
+  return (int64_t)((num + den - 1) / den);
+}
+
+struct RouteWs {
+  RouteStats st;
+  size_t bytes;
+};
+
+RouteWs plan_route(const moe_config& c, void* ws) {
+  Carver cv(ws);
+  const int64_t nb = route_blocks(c);
+  RouteWs r;
+  r.st.cnt = cv.take<int32_t>(nb * c.n_experts);
+  r.st.psum = cv.take<float>(nb * c.n_experts);
+  r.st.zsum = cv.take<float>(nb);
+  r.st.bad = cv.take<int32_t>(nb);
+  r.bytes = cv.off;
+  return r;
+}
+
+moe_status ws_check(void* ws, size_t* ws_bytes, size_t need) {
+  if (ws_bytes == nullptr) return MOE_ERR_INVALID_ARG;
+  if (ws == nullptr) {
+    *ws_bytes = need;
+    return MOE_OK;
+  }
+  if (!aligned16(ws)) return MOE_ERR_INVALID_ARG;
+  if (*ws_bytes < need) {
+    *ws_bytes = need;
+    return MOE_ERR_WORKSPACE;
+  }
+  return MOE_OK;
+}
+
+#define MOE_HIP_TRY(expr)                          \
+  do {                                             \
+    if ((expr) != hipSuccess) return MOE_ERR_HIP;  \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
+                     const float* router_bias, int32_t* topk_idx, float* topk_w,
+                     float* token_lse, void* ws, size_t* ws_bytes, hipStream_t stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  const RouteWs plan = plan_route(*cfg, nullptr);
+  if (ws != nullptr) {
+    if (!x || !w_router || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w_router)) return MOE_ERR_INVALID_ARG;
+  }
+  st = ws_check(ws, ws_bytes, plan.bytes);
+  if (st != MOE_OK || ws == nullptr) return st;
+  const RouteWs r = plan_route(*cfg, ws);
+  MOE_HIP_TRY(launch_router(*cfg, x, w_router, router_bias, topk_idx, topk_w, token_lse, r.st, stream));
+  return MOE_OK;
+}
+
+moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, const float* topk_w,
+                       const void* x, int32_t* expert_counts, int32_t* expert_offsets,
+                       int32_t* perm_token, float* perm_w, int32_t* inv_row, void* x_perm,
+                       int32_t* n_dropped, void* ws, size_t* ws_bytes, hipStream_t stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  const int64_t nb = route_blocks(*cfg);
+  auto plan = [&](void* base, RouteStats& rs, int32_t*& bases) {
+    Carver cv(base);
+    rs.cnt = cv.take<int32_t>(nb * cfg->n_experts);
+    rs.bad = cv.take<int32_t>(nb);
+    rs.psum = nullptr;
+    rs.zsum = nullptr;
+    bases = cv.take<int32_t>(nb * cfg->n_experts);
+    return cv.off;
+  };
+  RouteStats rs{};
+  int32_t* bases = nullptr;
+  const size_t need = plan(nullptr, rs, bases);
+  if (ws != nullptr) {
+    if (!topk_idx || !expert_counts || !expert_offsets || !perm_token || !inv_row || !n_dropped)
+      return MOE_ERR_INVALID_ARG;
+    if (perm_w && !topk_w) return MOE_ERR_INVALID_ARG;
+    if (x_perm && (!x || !aligned16(x) || !aligned16(x_perm))) return MOE_ERR_INVALID_ARG;
+  }
+  st = ws_check(ws, ws_bytes, need);
+  if (st != MOE_OK || ws == nullptr) return st;
+  plan(ws, rs, bases);
+  const int64_t cap = exact_capacity(*cfg);
+  PermuteMeta pm{bases, expert_counts, expert_offsets, n_dropped};
+  MOE_HIP_TRY(launch_histogram(*cfg, topk_idx, rs, stream));
+  MOE_HIP_TRY(launch_scan(*cfg, rs, pm, cap, nullptr, stream));
+  MOE_HIP_TRY(launch_scatter(*cfg, topk_idx, topk_w, pm, cap, perm_token, perm_w, inv_row, x,
+                             x_perm, stream));
+  return MOE_OK;
+}
+
+moe_status moe_expert_ffn(const moe_config* cfg, int32_t n_groups, int32_t n_seg,
+                          int64_t rows_max, const void* a, const int32_t* a_rows,
+                          const int32_t* group_offsets, const void* w1, const void* b1,
+                          const void* w2, const void* b2, void* out, void* ws,
+                          size_t* ws_bytes, hipStream_t stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (n_groups < 1 || n_seg < 1 || n_seg > 64 || rows_max < 0) return MOE_ERR_INVALID_ARG;
+  if (group_offsets == nullptr && n_groups != 1) return MOE_ERR_INVALID_ARG;
+  if (rows_max >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  const int64_t hw = (int64_t)n_seg * cfg->d_ffn;  // intermediate width
+  Carver cv(nullptr);
+  cv.take<char>((size_t)rows_max * hw * act_bytes(*cfg));
+  const size_t need = cv.off;
+  if (ws != nullptr) {
+    if (!a || !w1 || !w2 || !out) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(a) || !aligned16(w1) || !aligned16(w2) || !aligned16(out))
+      return MOE_ERR_INVALID_ARG;
+  }
+  st = ws_check(ws, ws_bytes, need);
+  if (st != MOE_OK || ws == nullptr) return st;
+  if (rows_max == 0) return MOE_OK;
+  Carver c2(ws);
+  void* H = c2.take<char>((size_t)rows_max * hw * act_bytes(*cfg));
+
+  GemmDesc up{};
+  up.a = a;
+  up.a_rows = a_rows;
+  up.lda = cfg->d_model;
+  up.group_off = group_offsets;
+  up.n_groups = n_groups;
+  up.n_seg = n_seg;
+  up.rows_max = rows_max;
+  up.w = w1;
+  up.bias = b1;
+  up.d = cfg->d_model;
+  up.f = cfg->d_ffn;
+  up.act = cfg->act;
+  up.out = H;
+  up.ldo = hw;
+  MOE_HIP_TRY(launch_gemm(*cfg, kGemmUp, up, stream));
+  GemmDesc dn = up;
+  dn.a = H;
+  dn.a_rows = nullptr;
+  dn.lda = hw;
+  dn.w = w2;
+  dn.bias = b2;
+  dn.out = out;
+  dn.ldo = cfg->d_model;
+  MOE_HIP_TRY(launch_gemm(*cfg, kGemmDown, dn, stream));
+  return MOE_OK;
+}
+
+moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* inv_row,
+                       const float* topk_w, const void* shared_y, const void* residual,
+                       void* y, hipStream_t stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!inv_row || !topk_w || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(y) || (y_perm && !aligned16(y_perm)) || (shared_y && !aligned16(shared_y)) ||
+      (residual && !aligned16(residual)))
+    return MOE_ERR_INVALID_ARG;
+  MOE_HIP_TRY(launch_combine(*cfg, y_perm, inv_row, topk_w, shared_y, residual, y, stream));
+  return MOE_OK;
+}
+
+moe_status moe_aux_stats(const moe_config* cfg, const int32_t* expert_counts,
+                         const int32_t* n_dropped, const void* route_ws, size_t route_ws_bytes,
+                         moe_aux* aux, hipStream_t stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!expert_counts || !n_dropped || !route_ws || !aux) return MOE_ERR_INVALID_ARG;
+  const RouteWs plan = plan_route(*cfg, nullptr);
+  if (route_ws_bytes < plan.bytes) return MOE_ERR_WORKSPACE;
+  const RouteWs r = plan_route(*cfg, const_cast<void*>(route_ws));
+  MOE_HIP_TRY(launch_aux(*cfg, r.st, expert_counts, n_dropped, exact_capacity(*cfg), aux, stream));
+  return MOE_OK;
+}
+
+moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* x, void* y,
+                       int32_t* topk_idx, float* topk_w, int32_t* expert_counts, moe_aux* aux,
+                       void* ws, size_t* ws_bytes, hipStream_t stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  const moe_config& c = *cfg;
+  const int64_t T = c.n_tokens, R = T * c.top_k, nb = route_blocks(c);
+  const int E = c.n_experts, S = c.n_shared, d = c.d_model, f = c.d_ffn;
+  const size_t ab = act_bytes(c);
+
+  struct Plan {
+    RouteStats rs;
+    PermuteMeta pm;
+    int32_t *idx, *perm_token, *inv_row;
+    float* wts;
+    void *H, *y_perm, *Hs, *shared_y;
+  };
+  auto plan = [&](void* base, Plan& p) {
+    Carver cv(base);
+    p.rs.cnt = cv.take<int32_t>(nb * E);
+    p.rs.psum = cv.take<float>(nb * E);
+    p.rs.zsum = cv.take<float>(nb);
+    p.rs.bad = nullptr;
+    p.pm.base = cv.take<int32_t>(nb * E);
+    p.pm.counts = cv.take<int32_t>(E);
+    p.pm.offsets = cv.take<int32_t>(E + 1);
+    p.pm.n_dropped = cv.take<int32_t>(1);
+    p.idx = cv.take<int32_t>(R);
+    p.wts = cv.take<float>(R);
+    p.perm_token = cv.take<int32_t>(R);
+    p.inv_row = cv.take<int32_t>(R);
+    p.H = cv.take<char>((size_t)R * f * ab);
+    p.y_perm = cv.take<char>((size_t)R * d * ab);
+    p.Hs = S ? cv.take<char>((size_t)T * S * f * ab) : nullptr;
+    p.shared_y = S ? cv.take<char>((size_t)T * d * ab) : nullptr;
+    return cv.off;
+  };
+  Plan p{};
+  const size_t need = plan(nullptr, p);
+  if (ws != nullptr) {
+    if (!w || !x || !y || !w->w_router || !w->w1 || !w->w2) return MOE_ERR_INVALID_ARG;
+    if (S > 0 && (!w->shared_w1 || !w->shared_w2)) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(y) || !aligned16(w->w_router) || !aligned16(w->w1) ||
+        !aligned16(w->w2) || (S > 0 && (!aligned16(w->shared_w1) || !aligned16(w->shared_w2))))
+      return MOE_ERR_INVALID_ARG;
+  }
+  st = ws_check(ws, ws_bytes, need);
+  if (st != MOE_OK || ws == nullptr) return st;
+  plan(ws, p);
+  if (topk_idx) p.idx = topk_idx;
+  if (topk_w) p.wts = topk_w;
+  if (expert_counts) p.pm.counts = expert_counts;
+  const int64_t cap = exact_capacity(c);
+
+  MOE_HIP_TRY(launch_router(c, x, w->w_router, w->router_bias, p.idx, p.wts, nullptr, p.rs, stream));
+  MOE_HIP_TRY(launch_scan(c, p.rs, p.pm, cap, aux, stream));
+  MOE_HIP_TRY(launch_scatter(c, p.idx, nullptr, p.pm, cap, p.perm_token, nullptr, p.inv_row,
+                             nullptr, nullptr, stream));
+
+  GemmDesc up{};
+  up.a = x;
+  up.a_rows = p.perm_token;
+  up.lda = d;
+  up.group_off = p.pm.offsets;
+  up.n_groups = E;
+  up.n_seg = 1;
+  up.rows_max = R;
+  up.w = w->w1;
+  up.bias = w->b1;
+  up.d = d;
+  up.f = f;
+  up.act = c.act;
+  up.out = p.H;
+  up.ldo = f;
+  MOE_HIP_TRY(launch_gemm(c, kGemmUp, up, stream));
+  GemmDesc dn = up;
+  dn.a = p.H;
+  dn.a_rows = nullptr;
+  dn.lda = f;
+  dn.w = w->w2;
+  dn.bias = w->b2;
+  dn.out = p.y_perm;
+  dn.ldo = d;
+  MOE_HIP_TRY(launch_gemm(c, kGemmDown, dn, stream));
+
+  if (S > 0) {
+    GemmDesc su{};
+    su.a = x;
+    su.a_rows = nullptr;
+    su.lda = d;
+    su.group_off = nullptr;  // one dense group of T rows
+    su.n_groups = 1;
+    su.n_seg = S;
+    su.rows_max = T;
+    su.w = w->shared_w1;
+    su.bias = w->shared_b1;
+    su.d = d;
+    su.f = f;
+    su.act = c.act;
+    su.out = p.Hs;
+    su.ldo = (int64_t)S * f;
+    MOE_HIP_TRY(launch_gemm(c, kGemmUp, su, stream));
+    GemmDesc sd = su;
+    sd.a = p.Hs;
+    sd.lda = (int64_t)S * f;
+    sd.w = w->shared_w2;
+    sd.bias = w->shared_b2;
+    sd.out = p.shared_y;
+    sd.ldo = d;
+    MOE_HIP_TRY(launch_gemm(c, kGemmDown, sd, stream));
+  }
+  MOE_HIP_TRY(launch_combine(c, p.y_perm, p.inv_row, p.wts, p.shared_y,
+                             c.add_residual ? x : nullptr, y, stream));
+  return MOE_OK;
+}
+
+}  // extern "C"

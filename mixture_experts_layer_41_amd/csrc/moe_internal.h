@@ -1,0 +1,111 @@
+// Internal declarations shared by the HIP translation units of the MoE
+// library: device helpers, launch descriptors and launcher prototypes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// constants
+
+constexpr int kMaxExperts = 512;
+constexpr int kWave = 64;
+
+// Tokens per routing block: every routing-side kernel (router, histogram,
+// scatter) splits the tokens into blocks of this many consecutive tokens, and
+// the per-block expert counts feed the stable ranking.
+inline int route_block_tokens(int n_experts) { return n_experts > 128 ? 32 : 64; }
+
+// ---------------------------------------------------------------------------
+// device helpers
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float32 -> bfloat16, round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// ---------------------------------------------------------------------------
+// workspace of the routing side (one region per routing block)
+
+struct RouteStats {
+  int32_t* cnt;    // [nb, E] tokens of block b that picked expert e
+  float* psum;     // [nb, E] sum over the block's tokens of p[t,e]
+  float* zsum;     // [nb]    sum over the block's tokens of lse^2
+  int32_t* bad;    // [nb]    invalid expert indices seen by the block (permute input check)
+};
+
+struct PermuteMeta {
+  int32_t* base;     // [nb, E] exclusive prefix over blocks of cnt (pre-capacity rank base)
+  int32_t* counts;   // [E] pre-capacity counts
+  int32_t* offsets;  // [E+1] exclusive scan of kept counts
+  int32_t* n_dropped;  // [1]
+};
+
+// ---------------------------------------------------------------------------
+// grouped GEMM descriptor
+
+enum GemmKind : int { kGemmUp = 0, kGemmDown = 1 };
+
+struct GemmDesc {
+  // A: row r of the grouped problem reads a + (a_rows ? a_rows[r] : r) * lda
+  const void* a;
+  const int32_t* a_rows;
+  int64_t lda;
+  const int32_t* group_off;  // [n_groups + 1], device
+  int n_groups;
+  int n_seg;                 // FFN segments summed per group
+  int64_t rows_max;          // host upper bound of group_off[n_groups]
+  // up GEMM (N-segmented): out[r, s*f + n] = act(A[r] . W1[g*S+s] rows), K = d
+  // down GEMM (K-segmented): out[r, n] = sum_s H[r, s*f:(s+1)*f] . W2[g*S+s][n], K = S*f
+  const void* w;
+  const void* bias;
+  int d;                     // d_model
+  int f;                     // d_ffn
+  int act;                   // moe_act (up GEMM only)
+  void* out;
+  int64_t ldo;
+};
+
+// ---------------------------------------------------------------------------
+// launchers (each returns hipGetLastError() of its launch)
+
+hipError_t launch_router(const moe_config& c, const void* x, const void* w_router,
+                         const float* router_bias, int32_t* topk_idx, float* topk_w,
+                         float* token_lse, const RouteStats& st, hipStream_t s);
+
+hipError_t launch_histogram(const moe_config& c, const int32_t* topk_idx, const RouteStats& st,
+                            hipStream_t s);
+
+// capacity < 0: no limit.  aux may be null (then psum/zsum are not read).
+hipError_t launch_scan(const moe_config& c, const RouteStats& st, const PermuteMeta& pm,
+                       int64_t capacity, moe_aux* aux, hipStream_t s);
+
+hipError_t launch_scatter(const moe_config& c, const int32_t* topk_idx, const float* topk_w,
+                          const PermuteMeta& pm, int64_t capacity, int32_t* perm_token,
+                          float* perm_w, int32_t* inv_row, const void* x, void* x_perm,
+                          hipStream_t s);
+
+hipError_t launch_aux(const moe_config& c, const RouteStats& st, const int32_t* counts,
+                      const int32_t* n_dropped, int64_t capacity, moe_aux* aux, hipStream_t s);
+
+hipError_t launch_gemm(const moe_config& c, GemmKind kind, const GemmDesc& g, hipStream_t s);
+
+hipError_t launch_combine(const moe_config& c, const void* y_perm, const int32_t* inv_row,
+                          const float* topk_w, const void* shared_y, const void* residual,
+                          void* y, hipStream_t s);
+
+}  // namespace moe
