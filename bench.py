@@ -1,0 +1,227 @@
+"""Throughput of the MoE layer forward on one MI355X.
+
+One step = one moe_forward call (router, permutation, routed and shared
+expert FFNs, combine, aux statistics) over one batch of synthetic tokens
+already resident in HBM.  Workload: the small "Flash" layer (T = 4096 tokens
+as 2 x 2048, d_model 512, 16 experts, top-2, SwiGLU d_ffn 1024, capacity
+factor 1.25), bf16 with float32 accumulation.
+
+Prints ONE JSON line (rank 0).  Extra legs:
+  roofline      the grouped expert GEMMs (moe_expert_ffn on the routed rows:
+                gate/up GEMM + down GEMM) timed with HIP events on the stream
+                they run on, against the bf16 dense MFMA peak;
+  cpu_baseline  the float64 CPU oracle on the same inputs, timed on the host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+WORKLOAD = "c2"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_gemm_flash_T4096_traffic.json")
+GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_41_amd", "csrc", "gemm.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=WORKLOAD, help="named layer config (default: c2)")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def traffic_entry():
+    """HBM traffic of the grouped GEMMs from the committed counter runs, if
+    they were taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+        with open(GEMM_SRC, "rb") as fh:
+            h = hashlib.sha256(fh.read()).hexdigest()[:16]
+        if rec.get("kernel_sha256_16") != h:
+            return None
+        return rec["bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build runs on a single MI355X); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from moe_inputs import get_config, make_inputs
+    from mixture_experts_layer_41_amd import binding as B
+
+    torch.cuda.set_device(0)
+    cfg = get_config(args.workload)
+    log(f"[bench] workload {cfg.name}")
+    t = make_inputs(cfg)   # raw seeded draws (no tie rejection: timing only)
+
+    def dev(a):
+        if a is None:
+            return None
+        if cfg.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+    rb = t["router_bias"]
+    W = B.LayerWeights(
+        w_router=dev(t["w_router"]), w1=dev(t["w1"]), w2=dev(t["w2"]), b1=dev(t["b1"]),
+        b2=dev(t["b2"]), shared_w1=dev(t["ws1"]), shared_w2=dev(t["ws2"]),
+        shared_b1=dev(t["sb1"]), shared_b2=dev(t["sb2"]),
+        router_bias=None if rb is None else torch.from_numpy(rb).cuda())
+    x = dev(t["x"])
+    c = B.config_of(cfg)
+    fwd = B.Forward(c, W)
+    stream = torch.cuda.current_stream()
+
+    # ---- eager warm-up and (optionally) a captured graph of one step
+    for _ in range(max(args.warmup, 1)):
+        fwd(x)
+    torch.cuda.synchronize()
+    graph = None
+    if not args.no_graph:
+        try:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fwd(x)
+            torch.cuda.synchronize()
+            for _ in range(3):
+                g.replay()
+            torch.cuda.synchronize()
+            graph = g
+        except Exception as e:  # capture not possible: time eager launches
+            log(f"[bench] graph capture failed ({e}); timing eager launches")
+            graph = None
+
+    def timed(step_fn, steps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step_fn()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    eager_s = timed(lambda: fwd(x), args.steps)
+    graph_s = timed(graph.replay, args.steps) if graph is not None else None
+    best_s = min(s for s in (eager_s, graph_s) if s is not None)
+    mode = "hip_graph" if (graph_s is not None and graph_s <= eager_s) else "eager"
+    log(f"[bench] eager {eager_s / args.steps * 1e6:.1f} us/step"
+        + (f", graph {graph_s / args.steps * 1e6:.1f} us/step" if graph_s else ""))
+
+    # ---- routing statistics of this batch (for the algorithmic work counts)
+    torch.cuda.synchronize()
+    aux = B.aux_to_dict(fwd.aux)
+    R = int(aux["n_kept"])
+    T, d, f, S, k = cfg.T, cfg.d, cfg.f, cfg.S, cfg.k
+    per_row = (6 if cfg.act == "swiglu" else 4) * d * f        # flops per kept row (one expert)
+    routed_flops = R * per_row
+    shared_flops = T * S * per_row
+    router_flops = 2 * T * d * cfg.E
+    layer_flops = routed_flops + shared_flops + router_flops
+
+    # ---- roofline leg: the routed grouped GEMMs alone, HIP events on this stream
+    pr = B.moe_permute(c, fwd.topk_idx)
+    torch.cuda.synchronize()
+    y_perm = torch.empty(T * k, d, dtype=B.torch_dtype(c), device="cuda")
+    ffn_args = (c, cfg.E, 1, T * k, x, pr["perm_token"], pr["expert_offsets"], W.w1, W.b1, W.w2,
+                W.b2, y_perm)
+    for _ in range(10):
+        B.moe_expert_ffn(*ffn_args)
+    n_ffn = max(50, args.steps // 2)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(n_ffn):
+        B.moe_expert_ffn(*ffn_args)
+    ev1.record(stream)
+    ev1.synchronize()
+    ffn_s = ev0.elapsed_time(ev1) / 1e3 / n_ffn
+    gemm_tflops = routed_flops / ffn_s / 1e12
+    roofline = {
+        "kernel": "grouped expert GEMMs (gate/up + SwiGLU epilogue, down) over the routed rows",
+        "bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+        "unit": "TFLOP/s", "frac": round(gemm_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "traffic": traffic_entry(), "launch_us": round(ffn_s * 1e6, 2),
+        "flops_per_launch": routed_flops,
+    }
+    log(f"[bench] grouped GEMMs {ffn_s * 1e6:.1f} us -> {gemm_tflops:.1f} TFLOP/s")
+
+    # ---- CPU oracle leg (rank 0, N = 1 only)
+    cpu = None
+    parity = None
+    if not args.no_cpu:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        except Exception:
+            cores = os.cpu_count()
+        runs, t_cpu = 0, 0.0
+        ref = None
+        while t_cpu < args.cpu_seconds or runs == 0:
+            t0 = time.perf_counter()
+            ref = oracle.forward(cfg, t)
+            t_cpu += time.perf_counter() - t0
+            runs += 1
+        cpu = {"value": round(T * runs / t_cpu, 1), "unit": "tokens/s", "cores": int(cores),
+               "kind": "oracle",
+               "sample": f"full layer forward of this workload ({T} tokens), {runs} run(s), "
+                         f"{t_cpu:.1f} s, float64 numpy"}
+        y = fwd(x)
+        torch.cuda.synchronize()
+        yg = y.float().cpu().numpy().astype(np.float64)
+        err = float(np.max(np.abs(yg - ref["y"])) / np.max(np.abs(ref["y"])))
+        idx_mismatch = int((fwd.topk_idx.cpu().numpy() != ref["topk_idx"]).any(1).sum())
+        parity = {"y_normwise_err": err, "tokens_with_other_topk": idx_mismatch,
+                  "lb_rel_err": abs(aux["load_balance"] - ref["lb"]) / abs(ref["lb"])}
+        log(f"[bench] oracle {t_cpu / runs:.2f} s/forward on {cores} threads; parity {parity}")
+
+    value = T * args.steps / best_s
+    out = {
+        "metric": "MoE-layer fwd tokens/s + grouped-GEMM % MFMA peak (1 MI355X)",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(best_s / args.steps * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16"
+        if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": T, "d_model": d, "experts": cfg.E,
+                   "top_k": k, "d_ffn": f, "shared_experts": S,
+                   "capacity_factor": cfg.capacity_factor, "launch": mode,
+                   "eager_us_per_step": round(eager_s / args.steps * 1e6, 2),
+                   "graph_us_per_step": None if graph_s is None else round(graph_s / args.steps * 1e6, 2),
+                   "layer_tflops": round(layer_flops / (best_s / args.steps) / 1e12, 2),
+                   "kept_rows": R, "dropped": int(aux["n_dropped"])},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
