@@ -1,0 +1,347 @@
+// Large-tile grouped GEMM for bf16 on gfx950 (the path taken whenever the
+// reduction length is a multiple of the K tile and the output width fills
+// whole tiles; everything else goes to the generic kernel in gemm.hip).
+//
+// Same math as the generic kernel (expert FFN up GEMM with the SwiGLU / GELU
+// epilogue, down GEMM summing shared-expert segments); differences:
+//   * BM x BN workgroup tiles (up to 256 x 256) over 4 or 8 waves; each wave owns
+//     (BM/WM) x (BN/WN) of v_mfma_f32_32x32x16_bf16 blocks, so every 16-byte
+//     LDS fragment feeds several MFMAs;
+//   * global loads of K tile t+1 go to registers while tile t feeds the
+//     MFMAs from LDS, then land in the other LDS stage (one barrier per K
+//     tile);
+//   * LDS rows are XOR-swizzled in 16-byte chunks.  gfx950 serves a 16-byte
+//     LDS read 16 lanes at a time over 64 four-byte banks (a 256-byte
+//     window); the 16 lanes of a fragment read 16 consecutive rows at one
+//     chunk, and chunk' = chunk ^ ((row / rows_per_window) % chunks_per_row)
+//     puts them in 16 distinct 16-byte bank groups;
+//   * workgroups are remapped so each XCD (blockIdx % 8) takes a contiguous
+//     run of tiles: the tiles of one expert, which share its weights, then
+//     hit the same L2.
+#include <cmath>
+
+#include "moe_internal.h"
+#include "gemm_common.h"
+
+namespace moe {
+namespace tiled {
+
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte chunk
+
+template <int BM, int BN, int BK, int WM, int WN, int KIND, int ACT, bool BIAS>
+__global__ void __launch_bounds__(64 * WM * WN)
+gemm_tile_kernel(GemmDesc p, int tiles_n, int tiles_total) {
+  constexpr int NW = WM * WN;
+  constexpr int kTileThreads = 64 * NW;
+  constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
+  constexpr int MI = TM / 32, NI = TN / 32;  // 32x32 MFMA blocks per wave
+  constexpr bool kSwiglu = (KIND == kGemmUp && ACT == MOE_ACT_SWIGLU);
+  constexpr int CPR = BK / 8;                // 16-byte chunks per tile row
+  constexpr int RPW = 256 / (BK * 2);        // tile rows per 256-byte bank window
+  constexpr int A_LD = BM * CPR / kTileThreads;  // 16-byte loads per thread per K tile
+  constexpr int B_LD = BN * CPR / kTileThreads;
+  constexpr int KS = BK / 16;                // MFMA K steps per K tile
+  static_assert(BK == 32 || BK == 64, "K tile");
+  static_assert(MI >= 1 && NI >= 1 && A_LD >= 1 && B_LD >= 1, "tile shape");
+  static_assert(!kSwiglu || (NI % 2 == 0), "SwiGLU pairs gate and up blocks");
+
+  __shared__ __attribute__((aligned(16))) u32x4 sA[2][BM * CPR];
+  __shared__ __attribute__((aligned(16))) u32x4 sB[2][BN * CPR];
+  __shared__ TileInfo s_tile;
+
+  // XCD-aware order: blocks b, b+8, b+16, ... run on one XCD and take
+  // consecutive tiles
+  const int nblk = gridDim.x;  // a multiple of 8
+  const int L = (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8;
+  if (L >= tiles_total) return;
+  const int mt = L / tiles_n, nt = L % tiles_n;
+  if (threadIdx.x < kWave) {
+    TileInfo t = find_row_tile(p.group_off, p.n_groups, p.rows_max, BM, mt);
+    if (threadIdx.x == 0) s_tile = t;
+  }
+  __syncthreads();
+  const TileInfo tile = s_tile;
+  if (tile.group < 0) return;
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave;
+  const int wm = wave / WN, wn = wave % WN;
+  const int S = p.n_seg, d = p.d, f = p.f;
+
+  int seg = 0, n0;
+  const uint16_t* wbase;
+  int K;
+  if (KIND == kGemmUp) {
+    constexpr int bnh = kSwiglu ? BN / 2 : BN;
+    const int tpn = f / bnh;
+    seg = nt / tpn;
+    n0 = (nt % tpn) * bnh;
+    const int rows1 = kSwiglu ? 2 * f : f;
+    wbase = static_cast<const uint16_t*>(p.w) + ((int64_t)tile.group * S + seg) * rows1 * (int64_t)d;
+    K = d;
+  } else {
+    n0 = nt * BN;
+    wbase = static_cast<const uint16_t*>(p.w) + (int64_t)tile.group * S * (int64_t)d * f;
+    K = f;
+  }
+  const int nk_seg = K / BK;
+  const int nk = (KIND == kGemmUp) ? nk_seg : S * nk_seg;
+
+  // --- load slots: chunk c = tid + 256 i -> row c / CPR, chunk c % CPR
+  const uint16_t* A = static_cast<const uint16_t*>(p.a);
+  const uint16_t* aptr[A_LD];
+  const uint16_t* bptr[B_LD];
+  int aoff[A_LD], boff[B_LD];  // swizzled LDS slot (uint4 units)
+#pragma unroll
+  for (int i = 0; i < A_LD; ++i) {
+    const int c = tid + kTileThreads * i;
+    const int r = c / CPR, ch = c % CPR;
+    const int64_t gr = tile.row0 + (r < tile.rows ? r : tile.rows - 1);
+    const int64_t src = p.a_rows ? (int64_t)p.a_rows[gr] : gr;
+    aptr[i] = A + src * p.lda + ch * 8;
+    aoff[i] = r * CPR + (ch ^ ((r / RPW) % CPR));
+  }
+#pragma unroll
+  for (int i = 0; i < B_LD; ++i) {
+    const int c = tid + kTileThreads * i;
+    const int r = c / CPR, ch = c % CPR;
+    int wr;
+    if (kSwiglu)
+      wr = (r < BN / 2) ? n0 + r : f + n0 + (r - BN / 2);
+    else
+      wr = n0 + r;
+    bptr[i] = wbase + (int64_t)wr * (KIND == kGemmUp ? d : f) + ch * 8;
+    boff[i] = r * CPR + (ch ^ ((r / RPW) % CPR));
+  }
+
+  u32x4 ra[A_LD], rb[B_LD];  // staging registers of the next K tile
+#define MOE_TILE_LOAD(kt_)                                                                  \
+  do {                                                                                      \
+    int64_t ao_, bo_;                                                                       \
+    if (KIND == kGemmUp) {                                                                  \
+      ao_ = (int64_t)(kt_) * BK;                                                            \
+      bo_ = ao_;                                                                            \
+    } else {                                                                                \
+      const int s_ = (kt_) / nk_seg, kk_ = ((kt_) % nk_seg) * BK;                           \
+      ao_ = (int64_t)s_ * f + kk_;                                                          \
+      bo_ = (int64_t)s_ * d * f + kk_;                                                      \
+    }                                                                                       \
+    _Pragma("unroll") for (int i_ = 0; i_ < A_LD; ++i_)                                    \
+        ra[i_] = *reinterpret_cast<const u32x4*>(aptr[i_] + ao_);                           \
+    _Pragma("unroll") for (int i_ = 0; i_ < B_LD; ++i_)                                    \
+        rb[i_] = *reinterpret_cast<const u32x4*>(bptr[i_] + bo_);                           \
+  } while (0)
+#define MOE_TILE_STORE(st_)                                                                 \
+  do {                                                                                      \
+    _Pragma("unroll") for (int i_ = 0; i_ < A_LD; ++i_) sA[st_][aoff[i_]] = ra[i_];         \
+    _Pragma("unroll") for (int i_ = 0; i_ < B_LD; ++i_) sB[st_][boff[i_]] = rb[i_];         \
+  } while (0)
+
+  f32x16 acc[MI][NI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  // LDS rows of this wave's fragments (row bases are multiples of 32, so the
+  // swizzle key depends on the fragment row only)
+  const int fr = lane % 32, half = lane / 32;
+  int arow[MI], brow[NI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) arow[i] = (wm * TM + i * 32 + fr) * CPR;
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    int r;
+    if (kSwiglu)
+      r = (j < NI / 2) ? wn * (TN / 2) + j * 32 + fr : BN / 2 + wn * (TN / 2) + (j - NI / 2) * 32 + fr;
+    else
+      r = wn * TN + j * 32 + fr;
+    brow[j] = r * CPR;
+  }
+  const int sw = (fr / RPW) % CPR;
+
+  MOE_TILE_LOAD(0);
+  MOE_TILE_STORE(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & 1;
+    if (kt + 1 < nk) MOE_TILE_LOAD(kt + 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      // lanes of half h take the K elements [h*BK/2, (h+1)*BK/2) of the tile,
+      // one chunk per K step; A and B use the same order
+      const int c = (half * KS + ks) ^ sw;
+      bf16x8 fa[MI], fb[NI];
+#pragma unroll
+      for (int i = 0; i < MI; ++i) fa[i] = __builtin_bit_cast(bf16x8, sA[st][arow[i] + c]);
+#pragma unroll
+      for (int j = 0; j < NI; ++j) fb[j] = __builtin_bit_cast(bf16x8, sB[st][brow[j] + c]);
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) MOE_TILE_STORE(st ^ 1);
+    __syncthreads();
+  }
+#undef MOE_TILE_LOAD
+#undef MOE_TILE_STORE
+
+  // epilogue (32x32 C layout: column lane%32, rows 8*(q/4) + 4*(lane/32) + q%4)
+  uint16_t* out = static_cast<uint16_t*>(p.out);
+  const uint16_t* bias = static_cast<const uint16_t*>(p.bias);
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int r = wm * TM + i * 32 + 8 * (q / 4) + 4 * half + (q % 4);
+      if (r >= tile.rows) continue;
+      const int64_t grow = tile.row0 + r;
+      if (kSwiglu) {
+#pragma unroll
+        for (int j = 0; j < NI / 2; ++j) {
+          const int cidx = wn * (TN / 2) + j * 32 + fr;
+          float g = acc[i][j][q], u = acc[i][j + NI / 2][q];
+          if (BIAS) {
+            const uint16_t* b = bias + ((int64_t)tile.group * S + seg) * 2 * f;
+            g += bf16_to_f32(b[n0 + cidx]);
+            u += bf16_to_f32(b[f + n0 + cidx]);
+          }
+          out[grow * p.ldo + (int64_t)seg * f + n0 + cidx] = f32_to_bf16(silu_f(g) * u);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+          const int cidx = wn * TN + j * 32 + fr;
+          float v = acc[i][j][q];
+          if (KIND == kGemmUp) {
+            if (BIAS) v += bf16_to_f32(bias[((int64_t)tile.group * S + seg) * f + n0 + cidx]);
+            out[grow * p.ldo + (int64_t)seg * f + n0 + cidx] = f32_to_bf16(gelu_f(v));
+          } else {
+            if (BIAS)
+              for (int s = 0; s < S; ++s)
+                v += bf16_to_f32(bias[((int64_t)tile.group * S + s) * d + n0 + cidx]);
+            out[grow * p.ldo + n0 + cidx] = f32_to_bf16(v);
+          }
+        }
+      }
+    }
+  }
+}
+
+}  // namespace tiled
+
+namespace {
+using namespace tiled;
+
+struct TileCfg {
+  int bm, bn, bk, occ;  // occ: workgroups resident per CU
+  double eff;           // relative MFMA efficiency of the shape
+};
+
+constexpr int kVariants = 4;
+constexpr TileCfg kTiles[kVariants] = {
+    {256, 256, 64, 1, 1.0},   // 8 waves, wave tile 128 x 64
+    {256, 128, 64, 1, 0.85},  // 8 waves, wave tile 64 x 64
+    {128, 128, 64, 2, 0.9},   // wave tile 64 x 64
+    {32, 256, 64, 2, 0.6},    // decode-shaped: few rows per expert
+};
+
+template <int BM, int BN, int BK, int WM, int WN, int KIND, int ACT, bool BIAS>
+hipError_t run(const GemmDesc& g, hipStream_t s) {
+  constexpr int kTileThreads = 64 * WM * WN;
+  constexpr bool kSwiglu = (KIND == kGemmUp && ACT == MOE_ACT_SWIGLU);
+  int tiles_n;
+  if (KIND == kGemmUp)
+    tiles_n = g.n_seg * (g.f / (kSwiglu ? BN / 2 : BN));
+  else
+    tiles_n = g.d / BN;
+  const int64_t tiles_m = (g.rows_max + BM - 1) / BM + (g.group_off ? g.n_groups : 0);
+  const int64_t total = tiles_m * tiles_n;
+  if (total <= 0) return hipSuccess;
+  const int64_t grid = (total + 7) / 8 * 8;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  gemm_tile_kernel<BM, BN, BK, WM, WN, KIND, ACT, BIAS>
+      <<<dim3((unsigned)grid), dim3(kTileThreads), 0, s>>>(g, tiles_n, (int)total);
+  return hipGetLastError();
+}
+
+template <int KIND, int ACT, bool BIAS>
+hipError_t dispatch(const GemmDesc& g, int variant, hipStream_t s) {
+  switch (variant) {
+    case 0: return run<256, 256, 64, 2, 4, KIND, ACT, BIAS>(g, s);
+    case 1: return run<256, 128, 64, 4, 2, KIND, ACT, BIAS>(g, s);
+    case 2: return run<128, 128, 64, 2, 2, KIND, ACT, BIAS>(g, s);
+    default: return run<32, 256, 64, 1, 4, KIND, ACT, BIAS>(g, s);
+  }
+}
+
+int cu_count() {
+  static int n = [] {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    return v;
+  }();
+  return n;
+}
+
+}  // namespace
+
+// Picks a tile shape from the expected rows per group (host-side estimate:
+// rows_max spread evenly over the groups, plus half a tile of padding per
+// group), or -1 if no shape covers the problem.  Predicted time ~ rounds of
+// resident workgroups x tile work / shape efficiency (efficiencies fitted to
+// measurements on MI355X).
+// force >= 0 selects that shape if it covers the problem.
+int pick_tile_variant(const moe_config& c, GemmKind kind, const GemmDesc& g, int force) {
+  if (c.dtype != MOE_DTYPE_BF16) return -1;
+  const bool swiglu = kind == kGemmUp && g.act == MOE_ACT_SWIGLU;
+  const int K = kind == kGemmUp ? g.d : g.f;
+  const double groups = g.group_off ? g.n_groups : 1;
+  const double rows_per_group = (double)g.rows_max / groups;
+  const int cus = cu_count();
+  int best = -1;
+  double best_t = 0;
+  for (int v = 0; v < kVariants; ++v) {
+    const TileCfg& tc = kTiles[v];
+    if (K % tc.bk != 0) continue;
+    const int ncol = kind == kGemmUp ? (swiglu ? tc.bn / 2 : tc.bn) : tc.bn;
+    const int nwidth = kind == kGemmUp ? g.f : g.d;
+    if (nwidth % ncol != 0) continue;
+    if (force >= 0) {
+      if (v == force) return v;
+      continue;
+    }
+    const double tiles_n = (double)(kind == kGemmUp ? g.n_seg : 1) * (nwidth / ncol);
+    const double tiles = groups * (g.group_off ? rows_per_group / tc.bm + 0.5
+                                               : std::ceil(rows_per_group / tc.bm)) * tiles_n;
+    const double rounds = std::ceil(tiles / ((double)cus * tc.occ));
+    const double t = rounds * tc.occ * (double)tc.bm * tc.bn / tc.eff;
+    if (best < 0 || t < best_t) {
+      best = v;
+      best_t = t;
+    }
+  }
+  return best;
+}
+
+hipError_t launch_gemm_tiled(const moe_config& c, GemmKind kind, const GemmDesc& g, int variant,
+                             hipStream_t s) {
+  const bool bias = g.bias != nullptr;
+  if (kind == kGemmDown)
+    return bias ? dispatch<kGemmDown, 0, true>(g, variant, s)
+                : dispatch<kGemmDown, 0, false>(g, variant, s);
+  if (g.act == MOE_ACT_SWIGLU)
+    return bias ? dispatch<kGemmUp, MOE_ACT_SWIGLU, true>(g, variant, s)
+                : dispatch<kGemmUp, MOE_ACT_SWIGLU, false>(g, variant, s);
+  return bias ? dispatch<kGemmUp, MOE_ACT_GELU, true>(g, variant, s)
+              : dispatch<kGemmUp, MOE_ACT_GELU, false>(g, variant, s);
+}
+
+}  // namespace moe
