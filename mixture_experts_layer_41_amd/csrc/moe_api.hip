@@ -7,10 +7,6 @@
 
 #include "moe_internal.h"
 
-namespace moe {
-size_t router_smem_bytes(const moe_config& c);
-}
-
 using namespace moe;
 
 namespace {
@@ -34,7 +30,7 @@ struct Carver {
 
 size_t act_bytes(const moe_config& c) { return c.dtype == MOE_DTYPE_BF16 ? 2 : 4; }
 int64_t route_blocks(const moe_config& c) {
-  const int BT = route_block_tokens(c.n_experts);
+  const int BT = route_block_tokens(c.n_tokens, c.n_experts);
   return (c.n_tokens + BT - 1) / BT;
 }
 

@@ -17,8 +17,14 @@ constexpr int kWave = 64;
 
 // Tokens per routing block: every routing-side kernel (router, histogram,
 // scatter) splits the tokens into blocks of this many consecutive tokens, and
-// the per-block expert counts feed the stable ranking.
-inline int route_block_tokens(int n_experts) { return n_experts > 128 ? 32 : 64; }
+// the per-block expert counts feed the stable ranking.  The largest of 64,
+// 32, 16 that still gives >= 512 blocks (two per CU), 16 for E > 256.
+__host__ __device__ inline int route_block_tokens(int64_t n_tokens, int n_experts) {
+  if (n_experts > 256) return 16;
+  if (n_tokens >= 64 * 512) return 64;
+  if (n_tokens >= 32 * 512) return 32;
+  return 16;
+}
 
 // ---------------------------------------------------------------------------
 // device helpers

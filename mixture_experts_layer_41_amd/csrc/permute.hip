@@ -258,7 +258,7 @@ scatter_kernel(const int32_t* __restrict__ idx, const float* __restrict__ topk_w
 
 hipError_t launch_histogram(const moe_config& c, const int32_t* topk_idx, const RouteStats& st,
                             hipStream_t s) {
-  const int BT = route_block_tokens(c.n_experts);
+  const int BT = route_block_tokens(c.n_tokens, c.n_experts);
   const int64_t nb = (c.n_tokens + BT - 1) / BT;
   histogram_kernel<<<dim3((unsigned)nb), dim3(64), 0, s>>>(topk_idx, c.n_tokens, c.top_k,
                                                            c.n_experts, BT, st.cnt, st.bad);
@@ -267,7 +267,7 @@ hipError_t launch_histogram(const moe_config& c, const int32_t* topk_idx, const 
 
 hipError_t launch_scan(const moe_config& c, const RouteStats& st, const PermuteMeta& pm,
                        int64_t capacity, moe_aux* aux, hipStream_t s) {
-  const int BT = route_block_tokens(c.n_experts);
+  const int BT = route_block_tokens(c.n_tokens, c.n_experts);
   const int64_t nb = (c.n_tokens + BT - 1) / BT;
   scan_kernel<<<dim3(1), dim3(kScanThreads), 0, s>>>(
       1, aux != nullptr, c.n_tokens, c.top_k, c.n_experts, nb, capacity, st.cnt, st.psum,
@@ -277,7 +277,7 @@ hipError_t launch_scan(const moe_config& c, const RouteStats& st, const PermuteM
 
 hipError_t launch_aux(const moe_config& c, const RouteStats& st, const int32_t* counts,
                       const int32_t* n_dropped, int64_t capacity, moe_aux* aux, hipStream_t s) {
-  const int BT = route_block_tokens(c.n_experts);
+  const int BT = route_block_tokens(c.n_tokens, c.n_experts);
   const int64_t nb = (c.n_tokens + BT - 1) / BT;
   scan_kernel<<<dim3(1), dim3(kScanThreads), 0, s>>>(
       0, 1, c.n_tokens, c.top_k, c.n_experts, nb, capacity, nullptr, st.psum, st.zsum, nullptr,
@@ -289,7 +289,7 @@ hipError_t launch_scatter(const moe_config& c, const int32_t* topk_idx, const fl
                           const PermuteMeta& pm, int64_t capacity, int32_t* perm_token,
                           float* perm_w, int32_t* inv_row, const void* x, void* x_perm,
                           hipStream_t s) {
-  const int BT = route_block_tokens(c.n_experts);
+  const int BT = route_block_tokens(c.n_tokens, c.n_experts);
   const int64_t nb = (c.n_tokens + BT - 1) / BT;
   const int64_t row_bytes = (int64_t)c.d_model * (c.dtype == MOE_DTYPE_BF16 ? 2 : 4);
   scatter_kernel<<<dim3((unsigned)nb), dim3(64), 0, s>>>(

@@ -7,126 +7,114 @@
 // softmax is monotone), in the total order (logit descending, index
 // ascending), so equal logits pick the lower expert index.
 //
-// One workgroup (4 waves) owns BT consecutive tokens and all E experts.
-// bf16: the logits tile comes from v_mfma_f32_16x16x32_bf16, A = x rows read
-// straight from HBM into registers, B = a 64-wide K-chunk of W_r staged in
-// LDS and shared by the 4 waves.  f32: plain FMA dot products.
+// One workgroup (4 waves) owns BT consecutive tokens (BT = 16, 32 or 64,
+// chosen so that there are enough workgroups to cover the chip) and all E
+// experts.
+//  * bf16 logits: v_mfma_f32_16x16x32_bf16 on 16-token x 16-expert tiles; A
+//    (x rows) and B (W_r rows) are read straight from memory, 32 contiguous
+//    bytes per lane per 64-wide K chunk (both operands use the same K order,
+//    so the dot products are unchanged).  When a workgroup has fewer than 4
+//    tiles, the waves split K and their partial tiles are added in LDS in a
+//    fixed order.
+//  * float32 logits: plain FMA dot products.
+//  * selection: 256 / BT lanes per token; max, sum of exponentials and each
+//    of the k picks are wave-shuffle reductions inside that lane group.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kKC = 64;            // K chunk of the bf16 router
-constexpr int kWrPitch = kKC + 8;  // bf16 elements per LDS row of the W_r chunk (pad: bank spread)
-
-struct RouterSmem {
-  // offsets in bytes into dynamic LDS
-  int wr;      // bf16 [E_pad][kWrPitch]
-  int logits;  // f32 [BT][E_pad + 1]
-  int cnt;     // i32 [E_pad]
-  int lse2;    // f32 [BT]
-  int total;
-};
 
 __host__ __device__ inline int round_up(int a, int b) { return (a + b - 1) / b * b; }
 
-__host__ __device__ inline RouterSmem router_smem(int E, int BT, bool bf16) {
-  const int ep = round_up(E, 16);
-  RouterSmem s;
-  int off = 0;
-  s.wr = off;
-  off += bf16 ? ep * kWrPitch * 2 : 0;
-  off = round_up(off, 16);
-  s.logits = off;
-  off += BT * (ep + 1) * 4;
-  s.cnt = off;
-  off += ep * 4;
-  s.lse2 = off;
-  off += BT * 4;
-  s.total = round_up(off, 16);
+struct RouterShape {
+  int BT, ep, n_tb, n_eb, n_tiles, nks, tiles_per_wave;
+};
+
+// bf16 = false: FMA logits, no K split
+__host__ __device__ inline RouterShape router_shape(int64_t T, int E, bool bf16) {
+  RouterShape s;
+  s.BT = route_block_tokens(T, E);
+  s.ep = round_up(E, 16);
+  s.n_tb = s.BT / 16;
+  s.n_eb = s.ep / 16;
+  s.n_tiles = s.n_tb * s.n_eb;
+  s.nks = (!bf16 || s.n_tiles >= 4) ? 1 : 4 / s.n_tiles;  // waves per tile (K split)
+  const int groups = 4 / s.nks;                 // waves with distinct tiles
+  s.tiles_per_wave = (s.n_tiles + groups - 1) / groups;
   return s;
 }
 
-// Logits of the block's tokens into LDS (bf16, MFMA).  EBW = expert blocks
-// of 16 handled by one wave (compile-time so the accumulators stay in registers).
-template <int EBW>
+// LDS: partial logits [nks][BT][ep + 1] f32, counts [ep] i32, lse^2 [BT] f32
+__host__ __device__ inline int router_smem_bytes_for(const RouterShape& s) {
+  return s.nks * s.BT * (s.ep + 1) * 4 + s.ep * 4 + s.BT * 4;
+}
+
+// Logits of the block's tokens into LDS (bf16, MFMA).  TPW = compile-time
+// bound on the tiles a wave owns, so the accumulators stay in registers.
+template <int TPW>
 __device__ void logits_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
-                            const float* __restrict__ rbias, int64_t T, int d, int E, int BT,
-                            int64_t t0, char* smem, const RouterSmem& L) {
-  const int ep = round_up(E, 16);
-  const int n_eb = ep / 16;
-  const int n_tb = BT / 16;         // token sub-blocks of 16
-  const int n_eg = 4 / n_tb;        // expert groups sharing a token sub-block
-  const int wave = threadIdx.x / kWave;
-  const int lane = threadIdx.x % kWave;
-  const int tb = wave % n_tb;
-  const int eg = wave / n_tb;
-  uint16_t* wr_s = reinterpret_cast<uint16_t*>(smem + L.wr);
-  float* lg = reinterpret_cast<float*>(smem + L.logits);
+                            int64_t T, int d, int E, int64_t t0, const RouterShape& s,
+                            float* __restrict__ part) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int ks = wave % s.nks;          // K slice of this wave
+  const int grp = wave / s.nks;         // tile group
+  const int ngrp = 4 / s.nks;
+  const int nch = (d + 63) / 64;        // 64-wide K chunks
+  const int c0 = ks * nch / s.nks, c1 = (ks + 1) * nch / s.nks;
+  const int kq = 16 * (lane / 16);      // this lane's 16 K elements of a chunk
 
-  // this lane's A row (token), clamped into range for the tail block
-  int64_t tok = t0 + tb * 16 + (lane % 16);
-  if (tok >= T) tok = T - 1;
-  const uint16_t* xrow = x + tok * (int64_t)d;
-  const int kq = 16 * (lane / 16);  // this lane's 16-element slice of a 64-wide chunk
-
-  f32x4 acc[EBW];
+  f32x4 acc[TPW];
+  const uint16_t* arow[TPW];
+  const uint16_t* brow[TPW];
+  bool bok[TPW];
 #pragma unroll
-  for (int i = 0; i < EBW; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int k0 = 0; k0 < d; k0 += kKC) {
-    // stage W_r[:, k0:k0+64] (zero-filled past d and past E)
-    for (int c = threadIdx.x; c < ep * (kKC / 8); c += kThreads) {
-      const int e = c / (kKC / 8);
-      const int kk = (c % (kKC / 8)) * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (e < E && k0 + kk < d) v = *reinterpret_cast<const uint4*>(wr + (int64_t)e * d + k0 + kk);
-      *reinterpret_cast<uint4*>(wr_s + e * kWrPitch + kk) = v;
-    }
-    // A fragments: 16 consecutive K elements of this lane's token
-    uint4 a0 = make_uint4(0, 0, 0, 0), a1 = make_uint4(0, 0, 0, 0);
-    if (k0 + kq < d) a0 = *reinterpret_cast<const uint4*>(xrow + k0 + kq);
-    if (k0 + kq + 8 < d) a1 = *reinterpret_cast<const uint4*>(xrow + k0 + kq + 8);
-    __syncthreads();
-    const bf16x8 fa0 = __builtin_bit_cast(bf16x8, a0);
-    const bf16x8 fa1 = __builtin_bit_cast(bf16x8, a1);
-#pragma unroll
-    for (int i = 0; i < EBW; ++i) {
-      const int eb = eg + i * n_eg;
-      if (eb < n_eb) {
-        const uint16_t* brow = wr_s + (eb * 16 + (lane % 16)) * kWrPitch + kq;
-        const bf16x8 fb0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(brow));
-        const bf16x8 fb1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(brow + 8));
-        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa0, fb0, acc[i], 0, 0, 0);
-        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa1, fb1, acc[i], 0, 0, 0);
-      }
-    }
-    __syncthreads();
+  for (int i = 0; i < TPW; ++i) {
+    acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int t = grp + i * ngrp;
+    const int tb = t < s.n_tiles ? t % s.n_tb : 0, eb = t < s.n_tiles ? t / s.n_tb : 0;
+    int64_t tok = t0 + tb * 16 + (lane % 16);
+    if (tok >= T) tok = T - 1;
+    arow[i] = x + tok * (int64_t)d + kq;
+    const int e = eb * 16 + (lane % 16);
+    bok[i] = t < s.n_tiles && e < E;
+    brow[i] = wr + (int64_t)(bok[i] ? e : 0) * d + kq;
   }
-  // C layout of the 16x16 product: lane holds rows 4*(lane/16)+i, column lane%16
+  for (int c = c0; c < c1; ++c) {
+    const int k0 = c * 64;
+    const bool ok0 = k0 + kq < d, ok1 = k0 + kq + 8 < d;
 #pragma unroll
-  for (int i = 0; i < EBW; ++i) {
-    const int eb = eg + i * n_eg;
-    if (eb < n_eb) {
-      const int e = eb * 16 + (lane % 16);
-      const float b = (rbias != nullptr && e < E) ? rbias[e] : 0.f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = tb * 16 + 4 * (lane / 16) + r;
-        lg[row * (ep + 1) + e] = acc[i][r] + b;
-      }
+    for (int i = 0; i < TPW; ++i) {
+      if (grp + i * ngrp >= s.n_tiles) continue;
+      uint4 a0 = make_uint4(0, 0, 0, 0), a1 = a0, b0 = a0, b1 = a0;
+      if (ok0) a0 = *reinterpret_cast<const uint4*>(arow[i] + k0);
+      if (ok1) a1 = *reinterpret_cast<const uint4*>(arow[i] + k0 + 8);
+      if (bok[i] && ok0) b0 = *reinterpret_cast<const uint4*>(brow[i] + k0);
+      if (bok[i] && ok1) b1 = *reinterpret_cast<const uint4*>(brow[i] + k0 + 8);
+      acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0),
+                                                       __builtin_bit_cast(bf16x8, b0), acc[i], 0, 0, 0);
+      acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1),
+                                                       __builtin_bit_cast(bf16x8, b1), acc[i], 0, 0, 0);
     }
+  }
+  // 16x16 C layout: lane holds rows 4*(lane/16) + r, column lane%16
+  float* pk = part + ks * s.BT * (s.ep + 1);
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int t = grp + i * ngrp;
+    if (t >= s.n_tiles) continue;
+    const int tb = t % s.n_tb, eb = t / s.n_tb;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      pk[(tb * 16 + 4 * (lane / 16) + r) * (s.ep + 1) + eb * 16 + (lane % 16)] = acc[i][r];
   }
 }
 
 // Logits of the block's tokens into LDS (float32, FMA).
-__device__ void logits_f32(const float* __restrict__ x, const float* __restrict__ wr,
-                           const float* __restrict__ rbias, int64_t T, int d, int E, int BT,
-                           int64_t t0, char* smem, const RouterSmem& L) {
-  const int ep = round_up(E, 16);
-  float* lg = reinterpret_cast<float*>(smem + L.logits);
-  for (int o = threadIdx.x; o < BT * E; o += kThreads) {
+__device__ void logits_f32(const float* __restrict__ x, const float* __restrict__ wr, int64_t T,
+                           int d, int E, int64_t t0, const RouterShape& s, float* __restrict__ part) {
+  for (int o = threadIdx.x; o < s.BT * E; o += kThreads) {
     const int r = o / E, e = o % E;
     int64_t tok = t0 + r;
     if (tok >= T) tok = T - 1;
@@ -134,128 +122,138 @@ __device__ void logits_f32(const float* __restrict__ x, const float* __restrict_
     const float* wrow = wr + (int64_t)e * d;
     float acc = 0.f;
     for (int c = 0; c < d; ++c) acc = fmaf(xr[c], wrow[c], acc);
-    lg[r * (ep + 1) + e] = acc + (rbias ? rbias[e] : 0.f);
+    part[r * (s.ep + 1) + e] = acc;
   }
 }
 
-template <int DT, int EBW>
+template <int DT, int TPW>
 __global__ void __launch_bounds__(kThreads)
 router_kernel(const void* __restrict__ x, const void* __restrict__ wr,
-              const float* __restrict__ rbias, int64_t T, int d, int E, int k, int BT,
+              const float* __restrict__ rbias, int64_t T, int d, int E, int k,
               int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
               float* __restrict__ token_lse, int32_t* __restrict__ st_cnt,
               float* __restrict__ st_psum, float* __restrict__ st_zsum) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const RouterSmem L = router_smem(E, BT, DT == MOE_DTYPE_BF16);
-  const int ep = round_up(E, 16);
+  const RouterShape s = router_shape(T, E, DT == MOE_DTYPE_BF16);
+  const int BT = s.BT, ep = s.ep;
   const int64_t blk = blockIdx.x;
   const int64_t t0 = blk * BT;
   const int nvalid = (int)((T - t0) < BT ? (T - t0) : BT);
-  float* lg = reinterpret_cast<float*>(smem + L.logits);
-  int32_t* cnt = reinterpret_cast<int32_t*>(smem + L.cnt);
-  float* lse2 = reinterpret_cast<float*>(smem + L.lse2);
+  float* part = reinterpret_cast<float*>(smem);
+  float* lg = part;  // K-slice 0 holds the summed logits
+  int32_t* cnt = reinterpret_cast<int32_t*>(smem + s.nks * BT * (ep + 1) * 4);
+  float* lse2 = reinterpret_cast<float*>(cnt + ep);
 
   for (int e = threadIdx.x; e < ep; e += kThreads) cnt[e] = 0;
   if (DT == MOE_DTYPE_BF16)
-    logits_bf16<EBW>(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wr), rbias, T, d, E,
-                BT, t0, smem, L);
+    logits_bf16<TPW>(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wr), T, d, E, t0,
+                     s, part);
   else
-    logits_f32(static_cast<const float*>(x), static_cast<const float*>(wr), rbias, T, d, E, BT,
-               t0, smem, L);
+    logits_f32(static_cast<const float*>(x), static_cast<const float*>(wr), T, d, E, t0, s, part);
+  __syncthreads();
+  // sum the K slices in a fixed order and add the bias
+  for (int o = threadIdx.x; o < BT * E; o += kThreads) {
+    const int r = o / E, e = o % E;
+    float v = lg[r * (ep + 1) + e];
+    for (int q = 1; q < s.nks; ++q) v += part[(q * BT + r) * (ep + 1) + e];
+    lg[r * (ep + 1) + e] = v + (rbias ? rbias[e] : 0.f);
+  }
   __syncthreads();
 
-  // one thread per token: softmax statistics, top-k, weights
-  if (threadIdx.x < nvalid) {
-    const int r = threadIdx.x;
-    const int64_t tok = t0 + r;
-    float* row = lg + r * (ep + 1);
-    float m = -INFINITY;
-    for (int e = 0; e < E; ++e) m = fmaxf(m, row[e]);
-    float z = 0.f;
-    for (int e = 0; e < E; ++e) z += expf(row[e] - m);
-    const float lse = m + logf(z);
+  // selection: G = 256 / BT consecutive lanes per token
+  const int G = kThreads / BT;
+  const int r = threadIdx.x / G, sub = threadIdx.x % G;
+  const bool valid = r < nvalid;
+  const int64_t tok = t0 + r;
+  float* row = lg + r * (ep + 1);
+  float m = -INFINITY;
+  for (int e = sub; e < E; e += G) m = fmaxf(m, row[e]);
+  for (int o = G / 2; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, G));
+  float z = 0.f;
+  for (int e = sub; e < E; e += G) z += expf(row[e] - m);
+  for (int o = G / 2; o > 0; o >>= 1) z += __shfl_xor(z, o, G);
+  const float lse = m + logf(z);
+  if (valid && sub == 0) {
     if (token_lse) token_lse[tok] = lse;
     lse2[r] = lse * lse;
-
-    // k passes in the order (logit desc, index asc): each pass takes the best
-    // element strictly after the previous pick in that order.
-    float prev_l = INFINITY;
-    int prev_e = -1;
-    float wsum = 0.f;
-    int32_t* out_i = topk_idx + tok * k;
-    float* out_w = topk_w + tok * k;
-    for (int j = 0; j < k; ++j) {
-      float best_l = -INFINITY;
-      int best_e = -1;
-      for (int e = 0; e < E; ++e) {
-        const float l = row[e];
-        const bool after = (l < prev_l) || (l == prev_l && e > prev_e);
-        if (after && (best_e < 0 || l > best_l)) {
-          best_l = l;
-          best_e = e;
-        }
-      }
-      if (best_e < 0) best_e = j % E;  // only reachable with NaN logits: keep indices in range
-      const float ex = expf(best_l - m);
-      out_i[j] = best_e;
-      out_w[j] = ex;
-      wsum += ex;
-      atomicAdd(&cnt[best_e], 1);
-      prev_l = best_l;
-      prev_e = best_e;
-    }
-    const float inv = 1.f / wsum;
-    for (int j = 0; j < k; ++j) out_w[j] = out_w[j] * inv;
-    // probabilities for the per-expert sums
-    const float iz = 1.f / z;
-    for (int e = 0; e < E; ++e) row[e] = expf(row[e] - m) * iz;
   }
+  // k picks; each takes the best element strictly after the previous pick in
+  // the order (logit desc, index asc)
+  float prev_l = INFINITY, wsum = 0.f;
+  int prev_e = -1;
+  for (int j = 0; j < k; ++j) {
+    float bl = -INFINITY;
+    int be = 0x7FFFFFFF;
+    for (int e = sub; e < E; e += G) {
+      const float l = row[e];
+      const bool after = (l < prev_l) || (l == prev_l && e > prev_e);
+      if (after && (be == 0x7FFFFFFF || l > bl || (l == bl && e < be))) {
+        bl = l;
+        be = e;
+      }
+    }
+    for (int o = G / 2; o > 0; o >>= 1) {
+      const float ol = __shfl_xor(bl, o, G);
+      const int oe = __shfl_xor(be, o, G);
+      if (oe != 0x7FFFFFFF && (be == 0x7FFFFFFF || ol > bl || (ol == bl && oe < be))) {
+        bl = ol;
+        be = oe;
+      }
+    }
+    if (be == 0x7FFFFFFF) be = j % E;  // only reachable with NaN logits: keep indices in range
+    const float ex = expf(bl - m);
+    wsum += ex;
+    if (valid && sub == 0) {
+      topk_idx[tok * k + j] = be;
+      topk_w[tok * k + j] = ex;
+      atomicAdd(&cnt[be], 1);
+    }
+    prev_l = bl;
+    prev_e = be;
+  }
+  if (valid && sub == 0) {
+    const float inv = 1.f / wsum;
+    for (int j = 0; j < k; ++j) topk_w[tok * k + j] *= inv;
+  }
+  // probabilities for the per-expert sums
+  const float iz = 1.f / z;
+  if (valid)
+    for (int e = sub; e < E; e += G) row[e] = expf(row[e] - m) * iz;
   __syncthreads();
 
   for (int e = threadIdx.x; e < E; e += kThreads) {
-    float s = 0.f;
-    for (int r = 0; r < nvalid; ++r) s += lg[r * (ep + 1) + e];
-    st_psum[blk * E + e] = s;
+    float acc = 0.f;
+    for (int q = 0; q < nvalid; ++q) acc += lg[q * (ep + 1) + e];
+    st_psum[blk * E + e] = acc;
     st_cnt[blk * E + e] = cnt[e];
   }
   if (threadIdx.x == 0) {
-    float s = 0.f;
-    for (int r = 0; r < nvalid; ++r) s += lse2[r];
-    st_zsum[blk] = s;
+    float acc = 0.f;
+    for (int q = 0; q < nvalid; ++q) acc += lse2[q];
+    st_zsum[blk] = acc;
   }
+}
+
+template <int DT, int TPW>
+hipError_t router_launch_t(const moe_config& c, const void* x, const void* w_router,
+                           const float* router_bias, int32_t* topk_idx, float* topk_w,
+                           float* token_lse, const RouteStats& st, hipStream_t s) {
+  const RouterShape sh = router_shape(c.n_tokens, c.n_experts, DT == MOE_DTYPE_BF16);
+  const int64_t nb = (c.n_tokens + sh.BT - 1) / sh.BT;
+  const int smem = router_smem_bytes_for(sh);
+  auto fn = router_kernel<DT, TPW>;
+  if (smem > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    if (e != hipSuccess) return e;
+  }
+  fn<<<dim3((unsigned)nb), dim3(kThreads), smem, s>>>(
+      x, w_router, router_bias, c.n_tokens, c.d_model, c.n_experts, c.top_k, topk_idx, topk_w,
+      token_lse, st.cnt, st.psum, st.zsum);
+  return hipGetLastError();
 }
 
 }  // namespace
-
-// expert blocks of 16 per wave for this E (see logits_bf16)
-static int router_ebw(int E) {
-  const int BT = route_block_tokens(E);
-  const int n_eb = (E + 15) / 16;
-  const int n_eg = 4 / (BT / 16);
-  const int need = (n_eb + n_eg - 1) / n_eg;
-  int ebw = 1;
-  while (ebw < need) ebw *= 2;
-  return ebw;
-}
-
-template <int DT, int EBW>
-static hipError_t router_launch_t(const moe_config& c, const void* x, const void* w_router,
-                                  const float* router_bias, int32_t* topk_idx, float* topk_w,
-                                  float* token_lse, const RouteStats& st, hipStream_t s) {
-  const int BT = route_block_tokens(c.n_experts);
-  const int64_t nb = (c.n_tokens + BT - 1) / BT;
-  const RouterSmem L = router_smem(c.n_experts, BT, DT == MOE_DTYPE_BF16);
-  auto fn = router_kernel<DT, EBW>;
-  if (L.total > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, L.total);
-    if (e != hipSuccess) return e;
-  }
-  fn<<<dim3((unsigned)nb), dim3(kThreads), L.total, s>>>(
-      x, w_router, router_bias, c.n_tokens, c.d_model, c.n_experts, c.top_k, BT, topk_idx,
-      topk_w, token_lse, st.cnt, st.psum, st.zsum);
-  return hipGetLastError();
-}
 
 hipError_t launch_router(const moe_config& c, const void* x, const void* w_router,
                          const float* router_bias, int32_t* topk_idx, float* topk_w,
@@ -263,18 +261,17 @@ hipError_t launch_router(const moe_config& c, const void* x, const void* w_route
   if (c.dtype == MOE_DTYPE_F32)
     return router_launch_t<MOE_DTYPE_F32, 1>(c, x, w_router, router_bias, topk_idx, topk_w,
                                              token_lse, st, s);
-  switch (router_ebw(c.n_experts)) {
-    case 1: return router_launch_t<MOE_DTYPE_BF16, 1>(c, x, w_router, router_bias, topk_idx, topk_w, token_lse, st, s);
-    case 2: return router_launch_t<MOE_DTYPE_BF16, 2>(c, x, w_router, router_bias, topk_idx, topk_w, token_lse, st, s);
-    case 4: return router_launch_t<MOE_DTYPE_BF16, 4>(c, x, w_router, router_bias, topk_idx, topk_w, token_lse, st, s);
-    case 8: return router_launch_t<MOE_DTYPE_BF16, 8>(c, x, w_router, router_bias, topk_idx, topk_w, token_lse, st, s);
-    default: return router_launch_t<MOE_DTYPE_BF16, 16>(c, x, w_router, router_bias, topk_idx, topk_w, token_lse, st, s);
-  }
-}
-
-size_t router_smem_bytes(const moe_config& c) {
-  const int BT = route_block_tokens(c.n_experts);
-  return (size_t)router_smem(c.n_experts, BT, c.dtype == MOE_DTYPE_BF16).total;
+  const int tpw = router_shape(c.n_tokens, c.n_experts, true).tiles_per_wave;
+#define MOE_ROUTER_CASE(N) \
+  if (tpw <= N)            \
+    return router_launch_t<MOE_DTYPE_BF16, N>(c, x, w_router, router_bias, topk_idx, topk_w, token_lse, st, s);
+  MOE_ROUTER_CASE(1)
+  MOE_ROUTER_CASE(2)
+  MOE_ROUTER_CASE(4)
+  MOE_ROUTER_CASE(8)
+  MOE_ROUTER_CASE(16)
+#undef MOE_ROUTER_CASE
+  return hipErrorInvalidConfiguration;
 }
 
 }  // namespace moe
