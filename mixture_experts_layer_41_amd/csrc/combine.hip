@@ -69,6 +69,7 @@ combine_kernel(const void* __restrict__ y_perm, const int32_t* __restrict__ inv_
 #pragma unroll
       for (int q = 0; q < 8; ++q) acc[q] = v[q];
     }
+#pragma unroll 4
     for (int j = 0; j < k; ++j) {
       const int32_t row = inv_row[t * k + j];
       if (row < 0) continue;

@@ -18,6 +18,7 @@
 //   * workgroups are remapped so each XCD (blockIdx % 8) takes a contiguous
 //     run of tiles: the tiles of one expert, which share its weights, then
 //     hit the same L2.
+#include <algorithm>
 #include <cmath>
 
 #include "moe_internal.h"
@@ -29,9 +30,12 @@ namespace tiled {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte chunk
 
+// One output tile: K loop over the group's rows and the tile's weight rows,
+// then the epilogue.  sA / sB are the two LDS stages.
 template <int BM, int BN, int BK, int WM, int WN, int KIND, int ACT, bool BIAS>
-__global__ void __launch_bounds__(64 * WM * WN)
-gemm_tile_kernel(GemmDesc p, int tiles_n, int tiles_total) {
+__device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo& tile, int nt,
+                                               u32x4 (*sA)[BM * (BK / 8)],
+                                               u32x4 (*sB)[BN * (BK / 8)]) {
   constexpr int NW = WM * WN;
   constexpr int kTileThreads = 64 * NW;
   constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
@@ -45,25 +49,6 @@ gemm_tile_kernel(GemmDesc p, int tiles_n, int tiles_total) {
   static_assert(BK == 32 || BK == 64, "K tile");
   static_assert(MI >= 1 && NI >= 1 && A_LD >= 1 && B_LD >= 1, "tile shape");
   static_assert(!kSwiglu || (NI % 2 == 0), "SwiGLU pairs gate and up blocks");
-
-  __shared__ __attribute__((aligned(16))) u32x4 sA[2][BM * CPR];
-  __shared__ __attribute__((aligned(16))) u32x4 sB[2][BN * CPR];
-  __shared__ TileInfo s_tile;
-
-  // XCD-aware order: blocks b, b+8, b+16, ... run on one XCD and take
-  // consecutive tiles
-  const int nblk = gridDim.x;  // a multiple of 8
-  const int L = (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8;
-  if (L >= tiles_total) return;
-  const int mt = L / tiles_n, nt = L % tiles_n;
-  if (threadIdx.x < kWave) {
-    TileInfo t = find_row_tile(p.group_off, p.n_groups, p.rows_max, BM, mt);
-    if (threadIdx.x == 0) s_tile = t;
-  }
-  __syncthreads();
-  const TileInfo tile = s_tile;
-  if (tile.group < 0) return;
-
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
   const int wm = wave / WN, wn = wave % WN;
@@ -233,6 +218,83 @@ gemm_tile_kernel(GemmDesc p, int tiles_n, int tiles_total) {
   }
 }
 
+// One workgroup per tile slot; the row tile is looked up from the group
+// offsets.  Blocks are remapped so that each XCD (blockIdx % 8) takes a
+// contiguous run of tiles: the tiles of one expert share its weights in that
+// XCD's L2.
+template <int BM, int BN, int BK, int WM, int WN, int KIND, int ACT, bool BIAS>
+__global__ void __launch_bounds__(64 * WM * WN)
+gemm_tile_kernel(GemmDesc p, int tiles_n, int tiles_total) {
+  __shared__ __attribute__((aligned(16))) u32x4 sA[2][BM * (BK / 8)];
+  __shared__ __attribute__((aligned(16))) u32x4 sB[2][BN * (BK / 8)];
+  __shared__ TileInfo s_tile;
+  const int nblk = gridDim.x;  // a multiple of 8
+  const int L = (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8;
+  if (L >= tiles_total) return;
+  const int mt = L / tiles_n, nt = L % tiles_n;
+  if (threadIdx.x < kWave) {
+    TileInfo t = find_row_tile(p.group_off, p.n_groups, p.rows_max, BM, mt);
+    if (threadIdx.x == 0) s_tile = t;
+  }
+  __syncthreads();
+  const TileInfo tile = s_tile;
+  if (tile.group < 0) return;
+  gemm_tile_body<BM, BN, BK, WM, WN, KIND, ACT, BIAS>(p, tile, nt, sA, sB);
+}
+
+// Persistent variant: the grid holds only the resident workgroups; the
+// row-tile table of the groups is built once per workgroup in LDS, and XCD
+// x = blockIdx % 8 walks a contiguous run of the (exact) tile list.
+template <int BM, int BN, int BK, int WM, int WN, int KIND, int ACT, bool BIAS>
+__global__ void __launch_bounds__(64 * WM * WN)
+gemm_tile_persistent(GemmDesc p, int tiles_n) {
+  constexpr int kTileThreads = 64 * WM * WN;
+  __shared__ __attribute__((aligned(16))) u32x4 sA[2][BM * (BK / 8)];
+  __shared__ __attribute__((aligned(16))) u32x4 sB[2][BN * (BK / 8)];
+  __shared__ int s_off[kMaxExperts + 1];     // group row offsets
+  __shared__ int s_tstart[kMaxExperts + 1];  // first row tile of each group
+  __shared__ int s_scan[kMaxExperts + 1];
+
+  const int G = p.group_off ? p.n_groups : 1;
+  for (int g = threadIdx.x; g <= G; g += kTileThreads)
+    s_off[g] = p.group_off ? p.group_off[g] : (g == 0 ? 0 : (int)p.rows_max);
+  __syncthreads();
+  for (int g = threadIdx.x; g <= G; g += kTileThreads) {
+    const int rows = g < G ? min(s_off[g + 1], (int)p.rows_max) - min(s_off[g], (int)p.rows_max) : 0;
+    s_tstart[g] = rows > 0 ? (rows + BM - 1) / BM : 0;  // tiles of group g, scanned below
+  }
+  __syncthreads();
+  for (int o = 1; o <= G; o <<= 1) {  // inclusive scan over g = 0..G
+    for (int g = threadIdx.x; g <= G; g += kTileThreads) s_scan[g] = g >= o ? s_tstart[g - o] : 0;
+    __syncthreads();
+    for (int g = threadIdx.x; g <= G; g += kTileThreads) s_tstart[g] += s_scan[g];
+    __syncthreads();
+  }
+  const int m_tiles = s_tstart[G - 1];
+  for (int g = threadIdx.x; g <= G; g += kTileThreads) s_scan[g] = g == 0 ? 0 : s_tstart[g - 1];
+  __syncthreads();
+  for (int g = threadIdx.x; g <= G; g += kTileThreads) s_tstart[g] = s_scan[g];
+  __syncthreads();
+
+  const int total = m_tiles * tiles_n;
+  const int xcd = blockIdx.x % 8, per_xcd = gridDim.x / 8;
+  const int lo = (int)((int64_t)total * xcd / 8), hi = (int)((int64_t)total * (xcd + 1) / 8);
+  for (int L = lo + (int)(blockIdx.x / 8); L < hi; L += per_xcd) {
+    const int mt = L / tiles_n, nt = L % tiles_n;
+    // group of row tile mt: last g with s_tstart[g] <= mt (binary search)
+    int glo = 0, ghi = G - 1;
+    while (glo < ghi) {
+      const int mid = (glo + ghi + 1) / 2;
+      if (s_tstart[mid] <= mt) glo = mid; else ghi = mid - 1;
+    }
+    TileInfo tile;
+    tile.group = glo;
+    tile.row0 = (int64_t)s_off[glo] + (int64_t)(mt - s_tstart[glo]) * BM;
+    tile.rows = min(BM, min(s_off[glo + 1], (int)p.rows_max) - (int)tile.row0);
+    gemm_tile_body<BM, BN, BK, WM, WN, KIND, ACT, BIAS>(p, tile, nt, sA, sB);
+  }
+}
+
 }  // namespace tiled
 
 namespace {
@@ -251,8 +313,10 @@ constexpr TileCfg kTiles[kVariants] = {
     {32, 256, 64, 2, 0.6},    // decode-shaped: few rows per expert
 };
 
-template <int BM, int BN, int BK, int WM, int WN, int KIND, int ACT, bool BIAS>
-hipError_t run(const GemmDesc& g, hipStream_t s) {
+int cu_count();
+
+template <int BM, int BN, int BK, int WM, int WN, bool PERSIST, int KIND, int ACT, bool BIAS>
+hipError_t run(const GemmDesc& g, int occ, hipStream_t s) {
   constexpr int kTileThreads = 64 * WM * WN;
   constexpr bool kSwiglu = (KIND == kGemmUp && ACT == MOE_ACT_SWIGLU);
   int tiles_n;
@@ -260,23 +324,29 @@ hipError_t run(const GemmDesc& g, hipStream_t s) {
     tiles_n = g.n_seg * (g.f / (kSwiglu ? BN / 2 : BN));
   else
     tiles_n = g.d / BN;
+  // upper bound of the row tiles (the exact count is known on the device)
   const int64_t tiles_m = (g.rows_max + BM - 1) / BM + (g.group_off ? g.n_groups : 0);
-  const int64_t total = tiles_m * tiles_n;
-  if (total <= 0) return hipSuccess;
-  const int64_t grid = (total + 7) / 8 * 8;
+  const int64_t upper = tiles_m * tiles_n;
+  if (upper <= 0 || g.rows_max <= 0) return hipSuccess;
+  int64_t grid = PERSIST ? std::min<int64_t>(upper, (int64_t)cu_count() * occ) : upper;
+  grid = (grid + 7) / 8 * 8;  // a multiple of 8 (XCDs)
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  gemm_tile_kernel<BM, BN, BK, WM, WN, KIND, ACT, BIAS>
-      <<<dim3((unsigned)grid), dim3(kTileThreads), 0, s>>>(g, tiles_n, (int)total);
+  if constexpr (PERSIST)
+    gemm_tile_persistent<BM, BN, BK, WM, WN, KIND, ACT, BIAS>
+        <<<dim3((unsigned)grid), dim3(kTileThreads), 0, s>>>(g, tiles_n);
+  else
+    gemm_tile_kernel<BM, BN, BK, WM, WN, KIND, ACT, BIAS>
+        <<<dim3((unsigned)grid), dim3(kTileThreads), 0, s>>>(g, tiles_n, (int)upper);
   return hipGetLastError();
 }
 
 template <int KIND, int ACT, bool BIAS>
 hipError_t dispatch(const GemmDesc& g, int variant, hipStream_t s) {
   switch (variant) {
-    case 0: return run<256, 256, 64, 2, 4, KIND, ACT, BIAS>(g, s);
-    case 1: return run<256, 128, 64, 4, 2, KIND, ACT, BIAS>(g, s);
-    case 2: return run<128, 128, 64, 2, 2, KIND, ACT, BIAS>(g, s);
-    default: return run<32, 256, 64, 1, 4, KIND, ACT, BIAS>(g, s);
+    case 0: return run<256, 256, 64, 2, 4, false, KIND, ACT, BIAS>(g, kTiles[0].occ, s);
+    case 1: return run<256, 128, 64, 4, 2, true, KIND, ACT, BIAS>(g, kTiles[1].occ, s);
+    case 2: return run<128, 128, 64, 2, 2, true, KIND, ACT, BIAS>(g, kTiles[2].occ, s);
+    default: return run<32, 256, 64, 1, 4, true, KIND, ACT, BIAS>(g, kTiles[3].occ, s);
   }
 }
 

@@ -151,18 +151,18 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, const flo
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
   const int64_t nb = route_blocks(*cfg);
-  auto plan = [&](void* base, RouteStats& rs, int32_t*& bases) {
+  auto plan = [&](void* base, RouteStats& rs, void*& scratch) {
     Carver cv(base);
     rs.cnt = cv.take<int32_t>(nb * cfg->n_experts);
     rs.bad = cv.take<int32_t>(nb);
     rs.psum = nullptr;
     rs.zsum = nullptr;
-    bases = cv.take<int32_t>(nb * cfg->n_experts);
+    scratch = cv.take<char>(permute_scratch_bytes(*cfg));
     return cv.off;
   };
   RouteStats rs{};
-  int32_t* bases = nullptr;
-  const size_t need = plan(nullptr, rs, bases);
+  void* scratch = nullptr;
+  const size_t need = plan(nullptr, rs, scratch);
   if (ws != nullptr) {
     if (!topk_idx || !expert_counts || !expert_offsets || !perm_token || !inv_row || !n_dropped)
       return MOE_ERR_INVALID_ARG;
@@ -171,13 +171,12 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, const flo
   }
   st = ws_check(ws, ws_bytes, need);
   if (st != MOE_OK || ws == nullptr) return st;
-  plan(ws, rs, bases);
+  plan(ws, rs, scratch);
   const int64_t cap = exact_capacity(*cfg);
-  PermuteMeta pm{bases, expert_counts, expert_offsets, n_dropped};
+  PermuteOut po{expert_counts, expert_offsets, n_dropped, perm_token, perm_w, inv_row};
   MOE_HIP_TRY(launch_histogram(*cfg, topk_idx, rs, stream));
-  MOE_HIP_TRY(launch_scan(*cfg, rs, pm, cap, nullptr, stream));
-  MOE_HIP_TRY(launch_scatter(*cfg, topk_idx, topk_w, pm, cap, perm_token, perm_w, inv_row, x,
-                             x_perm, stream));
+  MOE_HIP_TRY(launch_permute(*cfg, rs, po, cap, topk_idx, topk_w, x, x_perm, nullptr, scratch,
+                             stream));
   return MOE_OK;
 }
 
@@ -272,8 +271,9 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
 
   struct Plan {
     RouteStats rs;
-    PermuteMeta pm;
-    int32_t *idx, *perm_token, *inv_row;
+    PermuteOut po;
+    void* scratch;
+    int32_t* idx;
     float* wts;
     void *H, *y_perm, *Hs, *shared_y;
   };
@@ -283,14 +283,15 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
     p.rs.psum = cv.take<float>(nb * E);
     p.rs.zsum = cv.take<float>(nb);
     p.rs.bad = nullptr;
-    p.pm.base = cv.take<int32_t>(nb * E);
-    p.pm.counts = cv.take<int32_t>(E);
-    p.pm.offsets = cv.take<int32_t>(E + 1);
-    p.pm.n_dropped = cv.take<int32_t>(1);
+    p.scratch = cv.take<char>(permute_scratch_bytes(c));
+    p.po.counts = cv.take<int32_t>(E);
+    p.po.offsets = cv.take<int32_t>(E + 1);
+    p.po.n_dropped = cv.take<int32_t>(1);
+    p.po.perm_w = nullptr;
     p.idx = cv.take<int32_t>(R);
     p.wts = cv.take<float>(R);
-    p.perm_token = cv.take<int32_t>(R);
-    p.inv_row = cv.take<int32_t>(R);
+    p.po.perm_token = cv.take<int32_t>(R);
+    p.po.inv_row = cv.take<int32_t>(R);
     p.H = cv.take<char>((size_t)R * f * ab);
     p.y_perm = cv.take<char>((size_t)R * d * ab);
     p.Hs = S ? cv.take<char>((size_t)T * S * f * ab) : nullptr;
@@ -311,19 +312,18 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
   plan(ws, p);
   if (topk_idx) p.idx = topk_idx;
   if (topk_w) p.wts = topk_w;
-  if (expert_counts) p.pm.counts = expert_counts;
+  if (expert_counts) p.po.counts = expert_counts;
   const int64_t cap = exact_capacity(c);
 
   MOE_HIP_TRY(launch_router(c, x, w->w_router, w->router_bias, p.idx, p.wts, nullptr, p.rs, stream));
-  MOE_HIP_TRY(launch_scan(c, p.rs, p.pm, cap, aux, stream));
-  MOE_HIP_TRY(launch_scatter(c, p.idx, nullptr, p.pm, cap, p.perm_token, nullptr, p.inv_row,
-                             nullptr, nullptr, stream));
+  MOE_HIP_TRY(launch_permute(c, p.rs, p.po, cap, p.idx, nullptr, nullptr, nullptr, aux, p.scratch,
+                             stream));
 
   GemmDesc up{};
   up.a = x;
-  up.a_rows = p.perm_token;
+  up.a_rows = p.po.perm_token;
   up.lda = d;
-  up.group_off = p.pm.offsets;
+  up.group_off = p.po.offsets;
   up.n_groups = E;
   up.n_seg = 1;
   up.rows_max = R;
@@ -371,7 +371,7 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
     sd.ldo = d;
     MOE_HIP_TRY(launch_gemm(c, kGemmDown, sd, stream));
   }
-  MOE_HIP_TRY(launch_combine(c, p.y_perm, p.inv_row, p.wts, p.shared_y,
+  MOE_HIP_TRY(launch_combine(c, p.y_perm, p.po.inv_row, p.wts, p.shared_y,
                              c.add_residual ? x : nullptr, y, stream));
   return MOE_OK;
 }

@@ -54,11 +54,13 @@ struct RouteStats {
   int32_t* bad;    // [nb]    invalid expert indices seen by the block (permute input check)
 };
 
-struct PermuteMeta {
-  int32_t* base;     // [nb, E] exclusive prefix over blocks of cnt (pre-capacity rank base)
-  int32_t* counts;   // [E] pre-capacity counts
-  int32_t* offsets;  // [E+1] exclusive scan of kept counts
-  int32_t* n_dropped;  // [1]
+struct PermuteOut {
+  int32_t* counts;      // [E] pre-capacity counts
+  int32_t* offsets;     // [E+1] exclusive scan of kept counts
+  int32_t* n_dropped;   // [1] (-1: an expert index was out of range)
+  int32_t* perm_token;  // [T*k]
+  float* perm_w;        // [T*k] or null
+  int32_t* inv_row;     // [T*k]
 };
 
 // ---------------------------------------------------------------------------
@@ -96,14 +98,13 @@ hipError_t launch_router(const moe_config& c, const void* x, const void* w_route
 hipError_t launch_histogram(const moe_config& c, const int32_t* topk_idx, const RouteStats& st,
                             hipStream_t s);
 
-// capacity < 0: no limit.  aux may be null (then psum/zsum are not read).
-hipError_t launch_scan(const moe_config& c, const RouteStats& st, const PermuteMeta& pm,
-                       int64_t capacity, moe_aux* aux, hipStream_t s);
-
-hipError_t launch_scatter(const moe_config& c, const int32_t* topk_idx, const float* topk_w,
-                          const PermuteMeta& pm, int64_t capacity, int32_t* perm_token,
-                          float* perm_w, int32_t* inv_row, const void* x, void* x_perm,
-                          hipStream_t s);
+// Counts, offsets and the stable permutation from the per-block histograms
+// in st; capacity < 0: no limit.  aux (may be null) needs st.psum / st.zsum.
+// scratch: permute_scratch_bytes(c) bytes of device memory (may be 0).
+size_t permute_scratch_bytes(const moe_config& c);
+hipError_t launch_permute(const moe_config& c, const RouteStats& st, const PermuteOut& po,
+                          int64_t capacity, const int32_t* topk_idx, const float* topk_w,
+                          const void* x, void* x_perm, moe_aux* aux, void* scratch, hipStream_t s);
 
 hipError_t launch_aux(const moe_config& c, const RouteStats& st, const int32_t* counts,
                       const int32_t* n_dropped, int64_t capacity, moe_aux* aux, hipStream_t s);

@@ -6,26 +6,36 @@
 // experts, flatten the assignments, reorder them by expert, compute, and
 // scatter back by the original positions.  [P2 §4.1] keeps an expert_counts
 // buffer.  [P1 §2.2]: overflow assignments are dropped (they contribute
-// nothing; the caller's residual carries the token).
+// nothing; the caller's residual carries the token).  [P4 §3.1] / [P5 §2]:
+// load-balance and router z-loss statistics.
 //
-// Three kernels, all integer and atomic-free in global memory:
-//   histogram (only when the router did not already count): per routing
-//       block of BT tokens, how many tokens picked each expert;
-//   scan (one workgroup): per expert the exclusive prefix of those counts
-//       over blocks (= the rank base of the block's first token), the
-//       pre-capacity totals, the kept counts min(total, C), their exclusive
-//       scan (expert offsets) and the number of dropped assignments;
-//   scatter (one wave per routing block): the rank of token t among the
-//       block's tokens routed to e comes from a 64-bit LDS mask per expert;
-//       rank = base + that; kept iff rank < C; row = offset[e] + rank.
-// Ranks therefore follow ascending token order inside each expert, which
-// makes the permutation unique and the capacity drop first-come.
+// The tokens are cut into routing blocks of BT consecutive tokens; the router
+// (or the histogram kernel) leaves cnt[b][e], the number of tokens of block b
+// that picked expert e.  The rank of token t inside expert e is
+//   (tokens of earlier blocks that picked e) + (earlier tokens of t's block
+//   that picked e),
+// the second term from a 64-bit LDS mask per expert and a popcount.  Ranks
+// thus follow ascending token order inside each expert, which makes the
+// permutation unique and the capacity drop first-come.  Kept iff rank < C;
+// row = offset[e] + rank with offset the exclusive scan of min(count, C).
+//
+// Kernels (integer work, no floating-point atomics):
+//   histogram   only when the router did not already count;
+//   colscan     large tables only: one workgroup per expert scans cnt[.][e]
+//               over the blocks (rank bases, totals, probability sums);
+//   scatter     4 routing blocks per workgroup (one wave each); small tables
+//               are summed in the workgroup itself, so no scan launch; the
+//               first workgroup also writes counts, offsets, drops and the
+//               aux record.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int kScanThreads = 1024;
+constexpr int kThreads = 256;
+constexpr int kBlocksPerScatter = 4;     // routing blocks per scatter workgroup
+constexpr int64_t kSmallTable = 8192;    // nb * E up to this: no colscan launch
+constexpr int kBatch = 8;                // independent loads issued together
 
 __global__ void __launch_bounds__(64)
 histogram_kernel(const int32_t* __restrict__ idx, int64_t T, int k, int E, int BT,
@@ -50,211 +60,371 @@ histogram_kernel(const int32_t* __restrict__ idx, int64_t T, int k, int E, int B
   if (threadIdx.x == 0) bad[blockIdx.x] = nbad;
 }
 
-// Exclusive scan of v[0..n) in LDS (n <= kScanThreads), Hillis-Steele.
-__device__ void block_exclusive_scan(int64_t* v, int64_t* tmp, int n) {
-  const int i = threadIdx.x;
-  int64_t x = (i < n) ? v[i] : 0;
-  for (int off = 1; off < n; off <<= 1) {
-    if (i < n) tmp[i] = x;
-    __syncthreads();
-    if (i < n && i >= off) x += tmp[i - off];
+// Block-wide sums in a fixed order (tree over the thread index).
+__device__ double block_sum_f64(double v, double* red) {
+  red[threadIdx.x] = v;
+  __syncthreads();
+  for (int o = kThreads / 2; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
     __syncthreads();
   }
-  // x is inclusive; shift
-  if (i < n) tmp[i] = x;
+  const double r = red[0];
   __syncthreads();
-  if (i < n) v[i] = (i == 0) ? 0 : tmp[i - 1];
-  __syncthreads();
+  return r;
 }
 
-// do_scan: compute bases/counts/offsets/drops from st.cnt.
-// do_aux:  compute the moe_aux record; counts come from the scan (do_scan) or
-//          from `counts_in`, drops from the scan or `dropped_in`.
-__global__ void __launch_bounds__(kScanThreads)
-scan_kernel(int do_scan, int do_aux, int64_t T, int k, int E, int64_t nb, int64_t cap,
-            const int32_t* __restrict__ st_cnt, const float* __restrict__ st_psum,
-            const float* __restrict__ st_zsum, const int32_t* __restrict__ st_bad,
-            int32_t* __restrict__ base, int32_t* __restrict__ counts,
-            int32_t* __restrict__ offsets, int32_t* __restrict__ n_dropped,
-            const int32_t* __restrict__ counts_in, const int32_t* __restrict__ dropped_in,
-            moe_aux* __restrict__ aux) {
-  __shared__ int64_t part[kScanThreads];   // [G][E] partial sums of counts
-  __shared__ double ppart[kScanThreads];   // [G][E] partial sums of probabilities
-  __shared__ int64_t total[kMaxExperts + 1];
-  __shared__ int64_t tmp[kScanThreads];
-  __shared__ double red[kScanThreads];
-  __shared__ int64_t ired[kScanThreads];
-  const int tid = threadIdx.x;
-  const int G = kScanThreads / E;  // E <= 512 -> G >= 2
-  const int g = tid / E, e = tid % E;
-  const bool act = tid < G * E;
-  const int64_t b0 = act ? (g * nb) / G : 0;
-  const int64_t b1 = act ? ((g + 1) * nb) / G : 0;
+__device__ int64_t block_sum_i64(int64_t v, int64_t* red) {
+  red[threadIdx.x] = v;
+  __syncthreads();
+  for (int o = kThreads / 2; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  const int64_t r = red[0];
+  __syncthreads();
+  return r;
+}
 
-  // pass 1: per (g, e) partial sums over blocks [b0, b1)
+// One workgroup per expert e: rank bases base[b][e] = sum_{b' < b} cnt[b'][e],
+// total[e], pe[e] = sum_b psum[b][e] (float64, fixed order); workgroup 0 also
+// sums the lse^2 partials and the invalid-index counts.
+__global__ void __launch_bounds__(kThreads)
+colscan_kernel(int64_t nb, int E, const int32_t* __restrict__ cnt, const float* __restrict__ psum,
+               const float* __restrict__ zsum, const int32_t* __restrict__ bad,
+               int32_t* __restrict__ base, int32_t* __restrict__ total, double* __restrict__ pe,
+               double* __restrict__ zs, int32_t* __restrict__ nbad) {
+  __shared__ int64_t sc[kThreads];
+  __shared__ double red[kThreads];
+  __shared__ int64_t ired[kThreads];
+  const int e = blockIdx.x;
+  const int tid = threadIdx.x;
+  // a contiguous range of blocks per thread
+  const int64_t per = (nb + kThreads - 1) / kThreads;
+  const int64_t b0 = min(nb, tid * per), b1 = min(nb, b0 + per);
   int64_t s = 0;
   double ps = 0.0;
-  if (act) {
-    for (int64_t b = b0; b < b1; ++b) {
-      if (do_scan) s += st_cnt[b * E + e];
-      if (do_aux) ps += (double)st_psum[b * E + e];
-    }
-    part[tid] = s;
-    ppart[tid] = ps;
+#pragma unroll 8
+  for (int64_t b = b0; b < b1; ++b) {
+    s += cnt[b * E + e];
+    if (psum) ps += (double)psum[b * E + e];
   }
+  // inclusive scan of the per-thread sums (Hillis-Steele)
+  sc[tid] = s;
   __syncthreads();
-  // per expert: exclusive prefix over g, totals, P_e
-  double P = 0.0;
-  if (tid < E) {
-    int64_t run = 0;
-    for (int gg = 0; gg < G; ++gg) {
-      const int64_t v = part[gg * E + tid];
-      part[gg * E + tid] = run;
-      run += v;
-      P += ppart[gg * E + tid];
-    }
-    total[tid] = do_scan ? run : (int64_t)counts_in[tid];
+  for (int o = 1; o < kThreads; o <<= 1) {
+    const int64_t v = tid >= o ? sc[tid - o] : 0;
+    __syncthreads();
+    sc[tid] += v;
+    __syncthreads();
   }
-  __syncthreads();
-
-  int64_t dropped = 0, kept_sum = 0, bad = 0;
-  if (do_scan) {
-    // pass 2: rank bases of every block
-    if (act) {
-      int64_t run = part[tid];
-      for (int64_t b = b0; b < b1; ++b) {
-        base[b * E + e] = (int32_t)run;
-        run += st_cnt[b * E + e];
-      }
-    }
-    // kept counts and their exclusive scan
-    if (tid < E) {
-      const int64_t tot = total[tid];
-      const int64_t kept = (cap < 0 || tot < cap) ? tot : cap;
-      counts[tid] = (int32_t)tot;
-      tmp[tid] = kept;  // staged for the scan below
-    }
-    __syncthreads();
-    if (tid < E) part[tid] = tmp[tid];
-    __syncthreads();
-    block_exclusive_scan(part, tmp, E);
-    if (tid < E) {
-      const int64_t tot = total[tid];
-      const int64_t kept = (cap < 0 || tot < cap) ? tot : cap;
-      offsets[tid] = (int32_t)part[tid];
-      if (tid == E - 1) offsets[E] = (int32_t)(part[tid] + kept);
-    }
-    // dropped assignments and invalid indices: fixed-order block sums
-    int64_t my_drop = 0, my_bad = 0;
-    if (tid < E) {
-      const int64_t tot = total[tid];
-      my_drop = tot - ((cap < 0 || tot < cap) ? tot : cap);
-    }
-    if (st_bad)
-      for (int64_t b = tid; b < nb; b += kScanThreads) my_bad += st_bad[b];
-    ired[tid] = my_drop;
-    tmp[tid] = my_bad;
-    __syncthreads();
-    for (int off = kScanThreads / 2; off > 0; off >>= 1) {
-      if (tid < off) {
-        ired[tid] += ired[tid + off];
-        tmp[tid] += tmp[tid + off];
-      }
-      __syncthreads();
-    }
-    dropped = ired[0];
-    bad = tmp[0];
-    if (tid == 0) n_dropped[0] = bad ? -1 : (int32_t)dropped;
-  } else if (tid == 0) {
-    dropped = dropped_in[0];
+  int64_t run = sc[tid] - s;
+#pragma unroll 8
+  for (int64_t b = b0; b < b1; ++b) {
+    base[b * E + e] = (int32_t)run;
+    run += cnt[b * E + e];
   }
-
-  if (do_aux) {
-    // f_e P_e terms in LDS, then fixed-order sums
-    if (tid < E) red[tid] = ((double)total[tid] / (double)(T * k)) * (P / (double)T);
-    __syncthreads();
-    double zs = 0.0;
-    for (int64_t b = tid; b < nb; b += kScanThreads) zs += (double)st_zsum[b];
-    __syncthreads();
-    if (tid == 0) {
-      double lb = 0.0;
-      for (int i = 0; i < E; ++i) lb += red[i];
-      red[0] = lb * (double)E;
+  if (tid == kThreads - 1) total[e] = (int32_t)sc[tid];
+  const double P = block_sum_f64(ps, red);
+  if (tid == 0) pe[e] = P;
+  if (e == 0) {
+    double z = 0.0;
+    int64_t nbd = 0;
+    for (int64_t b = tid; b < nb; b += kThreads) {
+      if (zsum) z += (double)zsum[b];
+      if (bad) nbd += bad[b];
     }
-    __syncthreads();
-    const double lb = red[0];
-    __syncthreads();
-    red[tid] = zs;
-    __syncthreads();
-    for (int off = kScanThreads / 2; off > 0; off >>= 1) {
-      if (tid < off) red[tid] += red[tid + off];
-      __syncthreads();
-    }
+    z = block_sum_f64(z, red);
+    nbd = block_sum_i64(nbd, ired);
     if (tid == 0) {
-      for (int i = 0; i < E; ++i) kept_sum += total[i];  // pre-capacity sum = T*k
-      const double z = red[0] / (double)T;
-      aux->load_balance = lb;
-      aux->z_loss = z;
-      aux->weighted = 0.01 * lb + 0.001 * z;
-      aux->n_dropped = dropped;
-      aux->capacity = cap;
-      aux->n_kept = kept_sum - dropped;
+      *zs = z;
+      *nbad = (int32_t)nbd;
     }
   }
 }
 
-__global__ void __launch_bounds__(64)
-scatter_kernel(const int32_t* __restrict__ idx, const float* __restrict__ topk_w, int64_t T,
-               int k, int E, int BT, int64_t cap, const int32_t* __restrict__ base,
-               const int32_t* __restrict__ offsets, int32_t* __restrict__ perm_token,
-               float* __restrict__ perm_w, int32_t* __restrict__ inv_row,
-               const uint8_t* __restrict__ x, uint8_t* __restrict__ x_perm, int64_t row_bytes) {
-  __shared__ unsigned long long mask[kMaxExperts];
-  const int lane = threadIdx.x;
-  const int64_t blk = blockIdx.x;
-  const int64_t t = blk * BT + lane;
-  const bool valid = lane < BT && t < T;
-  for (int e = lane; e < E; e += 64) mask[e] = 0ull;
-  __syncthreads();
-  if (valid) {
-    for (int j = 0; j < k; ++j) {
-      const int e = idx[t * k + j];
-      if (e >= 0 && e < E) atomicOr(&mask[e], 1ull << lane);
+struct ScatterArgs {
+  const int32_t* idx;
+  const float* topk_w;
+  int64_t T;
+  int k, E, BT;
+  int64_t nb, cap;
+  // per-block counts / partials from the router or the histogram
+  const int32_t* cnt;
+  const float* psum;
+  const float* zsum;
+  const int32_t* bad;
+  // large tables: the colscan results
+  const int32_t* base;
+  const int32_t* total;
+  const double* pe;
+  const double* zs;
+  const int32_t* nbad;
+  // outputs
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* n_dropped;
+  moe_aux* aux;
+  int32_t* perm_token;
+  float* perm_w;
+  int32_t* inv_row;
+  const uint8_t* x;
+  uint8_t* x_perm;
+  int64_t row_bytes;
+};
+
+template <bool SMALL>
+__global__ void __launch_bounds__(kThreads)
+scatter_kernel(ScatterArgs a) {
+  __shared__ int32_t tot[kMaxExperts];                      // pre-capacity totals
+  __shared__ int32_t bases[kBlocksPerScatter][kMaxExperts];  // rank base of each wave's block
+  __shared__ int32_t offs[kMaxExperts + 1];
+  __shared__ unsigned long long mask[kBlocksPerScatter][kMaxExperts];
+  __shared__ double red[kThreads];
+  __shared__ int64_t ired[kThreads];
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int E = a.E;
+  const int64_t rb0 = (int64_t)blockIdx.x * kBlocksPerScatter;  // first routing block
+
+  // ---- totals and rank bases
+  if (SMALL) {
+    // G = 256 / E threads per expert (one when E > 256) sum interleaved
+    // blocks in registers: the total and, for each of this workgroup's
+    // blocks, the tokens of the blocks before it; partials meet in LDS in a
+    // fixed order (integer sums, exact)
+    const int G = E <= kThreads ? kThreads / E : 1;
+    int32_t* pt = reinterpret_cast<int32_t*>(red);  // [G][E] partial totals
+    for (int e0 = 0; e0 < E; e0 += kThreads) {
+      const int e = e0 + (E <= kThreads ? tid % E : tid);
+      const int g = E <= kThreads ? tid / E : 0;
+      int32_t s_tot = 0, s_pre[kBlocksPerScatter] = {0, 0, 0, 0};
+      if (g < G && e < E) {
+        // batches of independent loads keep several requests in flight
+        for (int64_t b = g; b < a.nb; b += (int64_t)G * kBatch) {
+          int32_t v[kBatch];
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) {
+            const int64_t bb = b + (int64_t)u * G;
+            v[u] = bb < a.nb ? a.cnt[bb * E + e] : 0;
+          }
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) {
+            const int64_t bb = b + (int64_t)u * G;
+            s_tot += v[u];
+#pragma unroll
+            for (int w = 0; w < kBlocksPerScatter; ++w) s_pre[w] += (bb < rb0 + w) ? v[u] : 0;
+          }
+        }
+      }
+      const bool act = g < G && e < E;
+      // totals
+      if (act) pt[g * (E <= kThreads ? E : kThreads) + (e - e0)] = s_tot;
+      __syncthreads();
+      if (tid < (E <= kThreads ? E : min(kThreads, E - e0))) {
+        int32_t sum = 0;
+        for (int q = 0; q < G; ++q) sum += pt[q * (E <= kThreads ? E : kThreads) + tid];
+        tot[e0 + tid] = sum;
+      }
+      __syncthreads();
+      for (int w = 0; w < kBlocksPerScatter; ++w) {
+        if (act) pt[g * (E <= kThreads ? E : kThreads) + (e - e0)] = s_pre[w];
+        __syncthreads();
+        if (tid < (E <= kThreads ? E : min(kThreads, E - e0))) {
+          int32_t sum = 0;
+          for (int q = 0; q < G; ++q) sum += pt[q * (E <= kThreads ? E : kThreads) + tid];
+          bases[w][e0 + tid] = sum;
+        }
+        __syncthreads();
+      }
+      if (E <= kThreads) break;
+    }
+  } else {
+    for (int e = tid; e < E; e += kThreads) {
+      tot[e] = a.total[e];
+      for (int w = 0; w < kBlocksPerScatter; ++w) {
+        const int64_t b = rb0 + w;
+        bases[w][e] = b < a.nb ? a.base[b * E + e] : 0;
+      }
     }
   }
+  for (int w = 0; w < kBlocksPerScatter; ++w)
+    for (int e = tid; e < E; e += kThreads) mask[w][e] = 0ull;
+  __syncthreads();
+
+  // ---- kept counts and their exclusive scan (offsets), Hillis-Steele in LDS
+  for (int e = tid; e < E; e += kThreads) {
+    const int64_t t = tot[e];
+    offs[e + 1] = (int32_t)((a.cap < 0 || t < a.cap) ? t : a.cap);
+  }
+  if (tid == 0) offs[0] = 0;
+  __syncthreads();
+  for (int o = 1; o <= E; o <<= 1) {
+    int32_t v[2] = {0, 0};
+    for (int q = 0; q < 2; ++q) {
+      const int e = tid + q * kThreads + 1;
+      if (e <= E && e - o >= 1) v[q] = offs[e - o];
+    }
+    __syncthreads();
+    for (int q = 0; q < 2; ++q) {
+      const int e = tid + q * kThreads + 1;
+      if (e <= E) offs[e] += v[q];
+    }
+    __syncthreads();
+  }
+
+  // ---- workgroup 0: counts, offsets, drops, aux
+  if (blockIdx.x == 0) {
+    int64_t my_drop = 0;
+    for (int e = tid; e < E; e += kThreads) {
+      a.counts[e] = tot[e];
+      a.offsets[e] = offs[e];
+      my_drop += tot[e] - (offs[e + 1] - offs[e]);
+    }
+    if (tid == 0) a.offsets[E] = offs[E];
+    const int64_t dropped = block_sum_i64(my_drop, ired);
+    int64_t nbd;
+    if (SMALL) {
+      int64_t v = 0;
+      if (a.bad)
+        for (int64_t b = tid; b < a.nb; b += kThreads) v += a.bad[b];
+      nbd = block_sum_i64(v, ired);
+    } else {
+      nbd = *a.nbad;
+    }
+    if (tid == 0) a.n_dropped[0] = nbd ? -1 : (int32_t)dropped;
+    if (a.aux) {
+      // lb = E * sum_e f_e P_e with f_e = total_e / (T k), P_e = sum_t p / T
+      double lbp = 0.0, zp = 0.0;
+      if (SMALL) {
+        // P_e: G = 256 / E threads per expert sum interleaved blocks, then
+        // the G partials are added in order (E > 256: one thread per expert)
+        const int G = E <= kThreads ? kThreads / E : 1;
+        double part = 0.0;
+        if (E <= kThreads) {
+          const int e = tid % E, g = tid / E;
+          if (g < G)
+            for (int64_t b = g; b < a.nb; b += (int64_t)G * kBatch) {
+              float v[kBatch];
+#pragma unroll
+              for (int u = 0; u < kBatch; ++u) {
+                const int64_t bb = b + (int64_t)u * G;
+                v[u] = bb < a.nb ? a.psum[bb * E + e] : 0.f;
+              }
+#pragma unroll
+              for (int u = 0; u < kBatch; ++u) part += (double)v[u];
+            }
+          red[tid] = part;
+          __syncthreads();
+          if (tid < E) {
+            double P = 0.0;
+            for (int q = 0; q < G; ++q) P += red[q * E + tid];
+            lbp = ((double)tot[tid] / (double)(a.T * a.k)) * (P / (double)a.T);
+          }
+          __syncthreads();
+        } else {
+          for (int e = tid; e < E; e += kThreads) {
+            double P = 0.0;
+            for (int64_t b = 0; b < a.nb; ++b) P += (double)a.psum[b * E + e];
+            lbp += ((double)tot[e] / (double)(a.T * a.k)) * (P / (double)a.T);
+          }
+        }
+#pragma unroll 8
+        for (int64_t b = tid; b < a.nb; b += kThreads) zp += (double)a.zsum[b];
+      } else {
+        for (int e = tid; e < E; e += kThreads)
+          lbp += ((double)tot[e] / (double)(a.T * a.k)) * (a.pe[e] / (double)a.T);
+      }
+      const double lb = block_sum_f64(lbp, red) * (double)E;
+      const double zsum_all = SMALL ? block_sum_f64(zp, red) : *a.zs;
+      const double z = zsum_all / (double)a.T;
+      if (tid == 0) {
+        a.aux->load_balance = lb;
+        a.aux->z_loss = z;
+        a.aux->weighted = 0.01 * lb + 0.001 * z;
+        a.aux->n_dropped = dropped;
+        a.aux->capacity = a.cap;
+        a.aux->n_kept = a.T * a.k - dropped;
+      }
+    }
+  }
+
+  // ---- ranks and scatter: wave w owns routing block rb0 + w, lane = token
+  const int64_t rb = rb0 + wave;
+  const int64_t t = rb * a.BT + lane;
+  const bool valid = rb < a.nb && lane < a.BT && t < a.T;
+  if (valid)
+    for (int j = 0; j < a.k; ++j) {
+      const int e = a.idx[t * a.k + j];
+      if (e >= 0 && e < E) atomicOr(&mask[wave][e], 1ull << lane);
+    }
   __syncthreads();
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   if (valid) {
-    for (int j = 0; j < k; ++j) {
-      const int e = idx[t * k + j];
+    for (int j = 0; j < a.k; ++j) {
+      const int e = a.idx[t * a.k + j];
       int32_t row = -1;
       if (e >= 0 && e < E) {
-        const int64_t rank = (int64_t)base[blk * E + e] + __popcll(mask[e] & below);
-        if (cap < 0 || rank < cap) {
-          row = offsets[e] + (int32_t)rank;
-          perm_token[row] = (int32_t)t;
-          if (perm_w) perm_w[row] = topk_w[t * k + j];
+        const int64_t rank = (int64_t)bases[wave][e] + __popcll(mask[wave][e] & below);
+        if (a.cap < 0 || rank < a.cap) {
+          row = offs[e] + (int32_t)rank;
+          a.perm_token[row] = (int32_t)t;
+          if (a.perm_w) a.perm_w[row] = a.topk_w[t * a.k + j];
         }
       }
-      inv_row[t * k + j] = row;
+      a.inv_row[t * a.k + j] = row;
     }
   }
-  if (x_perm == nullptr) return;
+  if (a.x_perm == nullptr) return;
   __syncthreads();  // inv_row of every lane is visible below
-  // optional gather x_perm[row] = x[t]: the wave copies one row at a time
-  for (int i = 0; i < BT * k; ++i) {
-    const int r = i / k;
-    const int64_t tt = blk * BT + r;
-    if (r >= BT || tt >= T) break;
-    const int32_t row = inv_row[tt * k + (i % k)];
-    if (row < 0) continue;
-    const uint4* src = reinterpret_cast<const uint4*>(x + tt * row_bytes);
-    uint4* dst = reinterpret_cast<uint4*>(x_perm + (int64_t)row * row_bytes);
-    for (int64_t c = lane; c < row_bytes / 16; c += 64) dst[c] = src[c];
+  // optional gather x_perm[row] = x[t]: each wave copies its block's rows
+  for (int r = 0; r < a.BT; ++r) {
+    const int64_t tt = rb * a.BT + r;
+    if (rb >= a.nb || tt >= a.T) break;
+    for (int j = 0; j < a.k; ++j) {
+      const int32_t row = a.inv_row[tt * a.k + j];
+      if (row < 0) continue;
+      const uint4* src = reinterpret_cast<const uint4*>(a.x + tt * a.row_bytes);
+      uint4* dst = reinterpret_cast<uint4*>(a.x_perm + (int64_t)row * a.row_bytes);
+      for (int64_t c = lane; c < a.row_bytes / 16; c += kWave) dst[c] = src[c];
+    }
+  }
+}
+
+// moe_aux_stats on its own: counts and drops given, partials from the router.
+__global__ void __launch_bounds__(kThreads)
+aux_kernel(int64_t T, int k, int E, int64_t nb, int64_t cap, const float* __restrict__ psum,
+           const float* __restrict__ zsum, const int32_t* __restrict__ counts,
+           const int32_t* __restrict__ n_dropped, moe_aux* __restrict__ aux) {
+  __shared__ double red[kThreads];
+  double lbp = 0.0, zp = 0.0;
+  for (int e = threadIdx.x; e < E; e += kThreads) {
+    double P = 0.0;
+    for (int64_t b = 0; b < nb; ++b) P += (double)psum[b * E + e];
+    lbp += ((double)counts[e] / (double)(T * k)) * (P / (double)T);
+  }
+  for (int64_t b = threadIdx.x; b < nb; b += kThreads) zp += (double)zsum[b];
+  const double lb = block_sum_f64(lbp, red) * (double)E;
+  const double z = block_sum_f64(zp, red) / (double)T;
+  if (threadIdx.x == 0) {
+    const int64_t dropped = n_dropped[0];
+    aux->load_balance = lb;
+    aux->z_loss = z;
+    aux->weighted = 0.01 * lb + 0.001 * z;
+    aux->n_dropped = dropped;
+    aux->capacity = cap;
+    aux->n_kept = T * k - dropped;
   }
 }
 
 }  // namespace
+
+size_t permute_scratch_bytes(const moe_config& c) {
+  const int BT = route_block_tokens(c.n_tokens, c.n_experts);
+  const int64_t nb = (c.n_tokens + BT - 1) / BT;
+  if (nb * c.n_experts <= kSmallTable) return 0;
+  // base [nb*E] i32, total [E] i32, pe [E] f64, zs f64 + nbad i32, each 256-aligned
+  return ((size_t)nb * c.n_experts * 4 + 255) / 256 * 256 + ((size_t)c.n_experts * 4 + 255) / 256 * 256 +
+         ((size_t)c.n_experts * 8 + 255) / 256 * 256 + 256;
+}
 
 hipError_t launch_histogram(const moe_config& c, const int32_t* topk_idx, const RouteStats& st,
                             hipStream_t s) {
@@ -265,13 +435,61 @@ hipError_t launch_histogram(const moe_config& c, const int32_t* topk_idx, const 
   return hipGetLastError();
 }
 
-hipError_t launch_scan(const moe_config& c, const RouteStats& st, const PermuteMeta& pm,
-                       int64_t capacity, moe_aux* aux, hipStream_t s) {
+hipError_t launch_permute(const moe_config& c, const RouteStats& st, const PermuteOut& po,
+                          int64_t capacity, const int32_t* topk_idx, const float* topk_w,
+                          const void* x, void* x_perm, moe_aux* aux, void* scratch, hipStream_t s) {
   const int BT = route_block_tokens(c.n_tokens, c.n_experts);
   const int64_t nb = (c.n_tokens + BT - 1) / BT;
-  scan_kernel<<<dim3(1), dim3(kScanThreads), 0, s>>>(
-      1, aux != nullptr, c.n_tokens, c.top_k, c.n_experts, nb, capacity, st.cnt, st.psum,
-      st.zsum, st.bad, pm.base, pm.counts, pm.offsets, pm.n_dropped, nullptr, nullptr, aux);
+  const int E = c.n_experts;
+  ScatterArgs a{};
+  a.idx = topk_idx;
+  a.topk_w = topk_w;
+  a.T = c.n_tokens;
+  a.k = c.top_k;
+  a.E = E;
+  a.BT = BT;
+  a.nb = nb;
+  a.cap = capacity;
+  a.cnt = st.cnt;
+  a.psum = st.psum;
+  a.zsum = st.zsum;
+  a.bad = st.bad;
+  a.counts = po.counts;
+  a.offsets = po.offsets;
+  a.n_dropped = po.n_dropped;
+  a.aux = aux;
+  a.perm_token = po.perm_token;
+  a.perm_w = po.perm_w;
+  a.inv_row = po.inv_row;
+  a.x = static_cast<const uint8_t*>(x);
+  a.x_perm = static_cast<uint8_t*>(x_perm);
+  a.row_bytes = (int64_t)c.d_model * (c.dtype == MOE_DTYPE_BF16 ? 2 : 4);
+  const int64_t grid = (nb + kBlocksPerScatter - 1) / kBlocksPerScatter;
+  if (nb * E <= kSmallTable) {
+    scatter_kernel<true><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(a);
+    return hipGetLastError();
+  }
+  // large tables: carve the colscan results out of the scratch area
+  char* p = static_cast<char*>(scratch);
+  int32_t* base = reinterpret_cast<int32_t*>(p);
+  p += ((size_t)nb * E * 4 + 255) / 256 * 256;
+  int32_t* total = reinterpret_cast<int32_t*>(p);
+  p += ((size_t)E * 4 + 255) / 256 * 256;
+  double* pe = reinterpret_cast<double*>(p);
+  p += ((size_t)E * 8 + 255) / 256 * 256;
+  double* zs = reinterpret_cast<double*>(p);
+  int32_t* nbad = reinterpret_cast<int32_t*>(p + 8);
+  colscan_kernel<<<dim3(E), dim3(kThreads), 0, s>>>(nb, E, st.cnt, aux ? st.psum : nullptr,
+                                                   aux ? st.zsum : nullptr, st.bad, base, total,
+                                                   pe, zs, nbad);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  a.base = base;
+  a.total = total;
+  a.pe = pe;
+  a.zs = zs;
+  a.nbad = nbad;
+  scatter_kernel<false><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -279,23 +497,8 @@ hipError_t launch_aux(const moe_config& c, const RouteStats& st, const int32_t* 
                       const int32_t* n_dropped, int64_t capacity, moe_aux* aux, hipStream_t s) {
   const int BT = route_block_tokens(c.n_tokens, c.n_experts);
   const int64_t nb = (c.n_tokens + BT - 1) / BT;
-  scan_kernel<<<dim3(1), dim3(kScanThreads), 0, s>>>(
-      0, 1, c.n_tokens, c.top_k, c.n_experts, nb, capacity, nullptr, st.psum, st.zsum, nullptr,
-      nullptr, nullptr, nullptr, nullptr, counts, n_dropped, aux);
-  return hipGetLastError();
-}
-
-hipError_t launch_scatter(const moe_config& c, const int32_t* topk_idx, const float* topk_w,
-                          const PermuteMeta& pm, int64_t capacity, int32_t* perm_token,
-                          float* perm_w, int32_t* inv_row, const void* x, void* x_perm,
-                          hipStream_t s) {
-  const int BT = route_block_tokens(c.n_tokens, c.n_experts);
-  const int64_t nb = (c.n_tokens + BT - 1) / BT;
-  const int64_t row_bytes = (int64_t)c.d_model * (c.dtype == MOE_DTYPE_BF16 ? 2 : 4);
-  scatter_kernel<<<dim3((unsigned)nb), dim3(64), 0, s>>>(
-      topk_idx, topk_w, c.n_tokens, c.top_k, c.n_experts, BT, capacity, pm.base, pm.offsets,
-      perm_token, perm_w, inv_row, static_cast<const uint8_t*>(x), static_cast<uint8_t*>(x_perm),
-      row_bytes);
+  aux_kernel<<<dim3(1), dim3(kThreads), 0, s>>>(c.n_tokens, c.top_k, c.n_experts, nb, capacity,
+                                               st.psum, st.zsum, counts, n_dropped, aux);
   return hipGetLastError();
 }
 

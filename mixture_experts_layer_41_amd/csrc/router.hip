@@ -52,11 +52,16 @@ __host__ __device__ inline int router_smem_bytes_for(const RouterShape& s) {
 }
 
 // Logits of the block's tokens into LDS (bf16, MFMA).  TPW = compile-time
-// bound on the tiles a wave owns, so the accumulators stay in registers.
+// bound on the tiles a wave owns, so the accumulators stay in registers.  All
+// of a wave's tiles share one 16-token row block (tile t = grp + 4 i with the
+// row block t mod n_tb, n_tb in {1, 2, 4}), so A is loaded once per chunk.
+// U chunks are loaded before their MFMAs are issued, to keep several memory
+// requests in flight per wave.
 template <int TPW>
 __device__ void logits_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
                             int64_t T, int d, int E, int64_t t0, const RouterShape& s,
                             float* __restrict__ part) {
+  constexpr int U = TPW <= 2 ? 4 : (TPW <= 4 ? 2 : 1);
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int ks = wave % s.nks;          // K slice of this wave
   const int grp = wave / s.nks;         // tile group
@@ -66,36 +71,47 @@ __device__ void logits_bf16(const uint16_t* __restrict__ x, const uint16_t* __re
   const int kq = 16 * (lane / 16);      // this lane's 16 K elements of a chunk
 
   f32x4 acc[TPW];
-  const uint16_t* arow[TPW];
   const uint16_t* brow[TPW];
-  bool bok[TPW];
+  bool tok_ok[TPW], bok[TPW];
+  const int tb = (grp < s.n_tiles ? grp : 0) % s.n_tb;
+  int64_t tok = t0 + tb * 16 + (lane % 16);
+  if (tok >= T) tok = T - 1;
+  const uint16_t* arow = x + tok * (int64_t)d + kq;
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
     acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int t = grp + i * ngrp;
-    const int tb = t < s.n_tiles ? t % s.n_tb : 0, eb = t < s.n_tiles ? t / s.n_tb : 0;
-    int64_t tok = t0 + tb * 16 + (lane % 16);
-    if (tok >= T) tok = T - 1;
-    arow[i] = x + tok * (int64_t)d + kq;
+    tok_ok[i] = t < s.n_tiles;
+    const int eb = tok_ok[i] ? t / s.n_tb : 0;
     const int e = eb * 16 + (lane % 16);
-    bok[i] = t < s.n_tiles && e < E;
+    bok[i] = tok_ok[i] && e < E;
     brow[i] = wr + (int64_t)(bok[i] ? e : 0) * d + kq;
   }
-  for (int c = c0; c < c1; ++c) {
-    const int k0 = c * 64;
-    const bool ok0 = k0 + kq < d, ok1 = k0 + kq + 8 < d;
+  for (int c = c0; c < c1; c += U) {
+    uint4 A[U][2], B[U][TPW][2];
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      if (grp + i * ngrp >= s.n_tiles) continue;
-      uint4 a0 = make_uint4(0, 0, 0, 0), a1 = a0, b0 = a0, b1 = a0;
-      if (ok0) a0 = *reinterpret_cast<const uint4*>(arow[i] + k0);
-      if (ok1) a1 = *reinterpret_cast<const uint4*>(arow[i] + k0 + 8);
-      if (bok[i] && ok0) b0 = *reinterpret_cast<const uint4*>(brow[i] + k0);
-      if (bok[i] && ok1) b1 = *reinterpret_cast<const uint4*>(brow[i] + k0 + 8);
-      acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0),
-                                                       __builtin_bit_cast(bf16x8, b0), acc[i], 0, 0, 0);
-      acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1),
-                                                       __builtin_bit_cast(bf16x8, b1), acc[i], 0, 0, 0);
+    for (int u = 0; u < U; ++u) {
+      const int k0 = (c + u) * 64;
+      const bool in = c + u < c1;
+      const bool ok0 = in && k0 + kq < d, ok1 = in && k0 + kq + 8 < d;
+      A[u][0] = ok0 ? *reinterpret_cast<const uint4*>(arow + k0) : make_uint4(0, 0, 0, 0);
+      A[u][1] = ok1 ? *reinterpret_cast<const uint4*>(arow + k0 + 8) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        B[u][i][0] = (bok[i] && ok0) ? *reinterpret_cast<const uint4*>(brow[i] + k0) : make_uint4(0, 0, 0, 0);
+        B[u][i][1] = (bok[i] && ok1) ? *reinterpret_cast<const uint4*>(brow[i] + k0 + 8) : make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        if (!tok_ok[i]) continue;
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[u][0]),
+                                                         __builtin_bit_cast(bf16x8, B[u][i][0]), acc[i], 0, 0, 0);
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[u][1]),
+                                                         __builtin_bit_cast(bf16x8, B[u][i][1]), acc[i], 0, 0, 0);
+      }
     }
   }
   // 16x16 C layout: lane holds rows 4*(lane/16) + r, column lane%16
@@ -104,7 +120,7 @@ __device__ void logits_bf16(const uint16_t* __restrict__ x, const uint16_t* __re
   for (int i = 0; i < TPW; ++i) {
     const int t = grp + i * ngrp;
     if (t >= s.n_tiles) continue;
-    const int tb = t % s.n_tb, eb = t / s.n_tb;
+    const int eb = t / s.n_tb;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       pk[(tb * 16 + 4 * (lane / 16) + r) * (s.ep + 1) + eb * 16 + (lane % 16)] = acc[i][r];
@@ -167,9 +183,11 @@ router_kernel(const void* __restrict__ x, const void* __restrict__ wr,
   const int64_t tok = t0 + r;
   float* row = lg + r * (ep + 1);
   float m = -INFINITY;
+#pragma unroll 4
   for (int e = sub; e < E; e += G) m = fmaxf(m, row[e]);
   for (int o = G / 2; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, G));
   float z = 0.f;
+#pragma unroll 4
   for (int e = sub; e < E; e += G) z += expf(row[e] - m);
   for (int o = G / 2; o > 0; o >>= 1) z += __shfl_xor(z, o, G);
   const float lse = m + logf(z);
@@ -223,12 +241,14 @@ router_kernel(const void* __restrict__ x, const void* __restrict__ wr,
 
   for (int e = threadIdx.x; e < E; e += kThreads) {
     float acc = 0.f;
+#pragma unroll 8
     for (int q = 0; q < nvalid; ++q) acc += lg[q * (ep + 1) + e];
     st_psum[blk * E + e] = acc;
     st_cnt[blk * E + e] = cnt[e];
   }
   if (threadIdx.x == 0) {
     float acc = 0.f;
+#pragma unroll 8
     for (int q = 0; q < nvalid; ++q) acc += lse2[q];
     st_zsum[blk] = acc;
   }
