@@ -154,7 +154,8 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, const flo
  * ([P4 §3.1] run every expert on its gathered rows; [P1 §4.2] group tokens
  * by expert and run one large product per expert).
  * Group g covers rows [group_offsets[g], group_offsets[g+1]) (device array,
- * non-decreasing, last entry <= rows_max).  Row r reads A row
+ * non-decreasing, last entry <= rows_max); group_offsets may be NULL only
+ * with n_groups == 1, meaning one dense group of rows_max rows.  Row r reads A row
  * a_rows ? a_rows[r] : r of `a` [*, d].  Each group is the sum of n_seg
  * FFNs of width f with weight 1 (n_seg = 1 for routed experts; the S shared
  * experts form one group with n_seg = S):
@@ -162,7 +163,10 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, const flo
  * w1 [n_groups*n_seg, 2f or f, d], b1 [.., 2f or f] or NULL,
  * w2 [n_groups*n_seg, d, f], b2 [.., d] or NULL, out [rows_max, d]; rows of
  * out outside every group are not written.  ws holds the intermediate
- * activations (rows_max x n_seg*f) and tile tables.
+ * activations (rows_max x n_seg*f, act dtype).  Errors: INVALID_ARG for
+ * n_groups < 1, n_seg outside [1, 64], rows_max < 0, NULL offsets with
+ * n_groups > 1, NULL or misaligned a / w1 / w2 / out; UNSUPPORTED for
+ * rows_max >= 2^31.  rows_max == 0 launches nothing.
  */
 moe_status moe_expert_ffn(const moe_config* cfg, int32_t n_groups, int32_t n_seg,
                           int64_t rows_max, const void* a, const int32_t* a_rows,
