@@ -29,7 +29,10 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 WORKLOAD = "c2"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_gemm_flash_T4096_traffic.json")
-GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_41_amd", "csrc", "gemm.hip")
+# sources of the grouped GEMM kernels: the committed counter figures hold only
+# while these are unchanged
+GEMM_SRCS = [os.path.join(ROOT, "mixture_experts_layer_41_amd", "csrc", n)
+             for n in ("gemm.hip", "gemm_mfma.hip", "gemm_common.h")]
 
 
 def log(*a):
@@ -45,7 +48,35 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (for scaling HBM byte counters)")
     return ap.parse_args()
+
+
+def gemm_source_hash():
+    h = hashlib.sha256()
+    for p in GEMM_SRCS:
+        with open(p, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def copy_calibration(n_bytes=1 << 30, reps=5):
+    """A plain device-to-device copy of n_bytes, run reps times: the reference
+    workload against which the HBM byte counters are scaled."""
+    import torch
+    torch.cuda.set_device(0)
+    src = torch.ones(n_bytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    print(json.dumps({"copy_bytes_read": n_bytes, "copy_bytes_written": n_bytes, "reps": reps,
+                      "GB_per_s": round(2 * n_bytes / dt / 1e9, 1),
+                      "gemm_source_sha256_16": gemm_source_hash()}), flush=True)
 
 
 def traffic_entry():
@@ -54,9 +85,7 @@ def traffic_entry():
     try:
         with open(TRAFFIC_FILE) as fh:
             rec = json.load(fh)
-        with open(GEMM_SRC, "rb") as fh:
-            h = hashlib.sha256(fh.read()).hexdigest()[:16]
-        if rec.get("kernel_sha256_16") != h:
+        if rec.get("kernel_sha256_16") != gemm_source_hash():
             return None
         return rec["bytes_per_launch"]
     except (OSError, KeyError, ValueError):
@@ -69,6 +98,9 @@ def main():
         print(f"bench.py measures one GPU only (this build runs on a single MI355X); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import numpy as np
     import torch
