@@ -209,12 +209,16 @@ def main():
     ffn_s = ev0.elapsed_time(ev1) / 1e3 / n_ffn
     gemm_tflops = routed_flops / ffn_s / 1e12
     # algorithmic bytes of the same call: the weights of every expert that
-    # keeps a row, the gathered input rows, H written and read back, the output
+    # keeps a row (W1 [w1_rows, d] and W2 [d, f]), the gathered input rows,
+    # H written and read back, the output rows
     counts = pr["expert_offsets"].cpu().numpy()
     touched = int((counts[1:] - counts[:-1] > 0).sum())
     ab = 2 if cfg.dtype == "bf16" else 4
-    routed_bytes = ab * (touched * (cfg.w1_rows + d) * f + R * d + 2 * R * f + R * d)
-    if routed_flops / routed_bytes >= MFMA_BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3:
+    weight_bytes = ab * touched * (cfg.w1_rows + f) * d
+    routed_bytes = weight_bytes + ab * (R * d + 2 * R * f + R * d)
+    # MFMA-bound unless the weights alone give fewer flops per byte than the
+    # MFMA / HBM ridge (the weight-streaming decode shape)
+    if routed_flops / weight_bytes >= MFMA_BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3:
         roofline = {
             "kernel": "grouped expert GEMMs (gate/up + activation epilogue, down) over the routed rows",
             "bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,

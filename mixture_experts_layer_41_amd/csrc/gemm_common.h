@@ -73,6 +73,27 @@ __device__ inline TileInfo find_row_tile(const int32_t* __restrict__ off, int n_
   return t;
 }
 
+// Number of row tiles over all groups (executed by one full wave; every lane
+// gets the total).
+__device__ inline int count_row_tiles(const int32_t* __restrict__ off, int n_groups, int64_t rows_max,
+                                      int BM) {
+  if (off == nullptr) return (int)((rows_max + BM - 1) / BM);
+  const int lane = threadIdx.x % kWave;
+  int total = 0;
+  for (int g0 = 0; g0 < n_groups; g0 += kWave) {
+    const int g = g0 + lane;
+    int tiles = 0;
+    if (g < n_groups) {
+      const int64_t lo = min((int64_t)off[g], rows_max), hi = min((int64_t)off[g + 1], rows_max);
+      tiles = hi > lo ? (int)((hi - lo + BM - 1) / BM) : 0;
+    }
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) tiles += __shfl_xor(tiles, o, kWave);
+    total += tiles;
+  }
+  return total;
+}
+
 __device__ __forceinline__ float silu_f(float g) { return g / (1.f + __expf(-g)); }
 __device__ __forceinline__ float gelu_f(float z) { return 0.5f * z * (1.f + erff(z * 0.70710678118654752f)); }
 

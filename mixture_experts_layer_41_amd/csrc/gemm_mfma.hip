@@ -224,20 +224,31 @@ __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo
 // XCD's L2.
 template <int BM, int BN, int BK, int WM, int WN, int KIND, int ACT, bool BIAS>
 __global__ void __launch_bounds__(64 * WM * WN)
-gemm_tile_kernel(GemmDesc p, int tiles_n, int tiles_total) {
+gemm_tile_kernel(GemmDesc p, int tiles_n) {
   __shared__ __attribute__((aligned(16))) u32x4 sA[2][BM * (BK / 8)];
   __shared__ __attribute__((aligned(16))) u32x4 sB[2][BN * (BK / 8)];
   __shared__ TileInfo s_tile;
-  const int nblk = gridDim.x;  // a multiple of 8
-  const int L = (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8;
-  if (L >= tiles_total) return;
-  const int mt = L / tiles_n, nt = L % tiles_n;
+  __shared__ int s_nt;
+  // XCD x = blockIdx % 8 takes the x-th eighth of the exact tile list (the
+  // grid is sized for an upper bound; surplus blocks leave at once)
   if (threadIdx.x < kWave) {
-    TileInfo t = find_row_tile(p.group_off, p.n_groups, p.rows_max, BM, mt);
-    if (threadIdx.x == 0) s_tile = t;
+    const int64_t total = (int64_t)count_row_tiles(p.group_off, p.n_groups, p.rows_max, BM) * tiles_n;
+    const int xcd = blockIdx.x % 8;
+    const int64_t lo = total * xcd / 8, hi = total * (xcd + 1) / 8;
+    const int64_t L = lo + blockIdx.x / 8;
+    TileInfo t;
+    t.group = -1;
+    t.row0 = 0;
+    t.rows = 0;
+    if (L < hi) t = find_row_tile(p.group_off, p.n_groups, p.rows_max, BM, (int)(L / tiles_n));
+    if (threadIdx.x == 0) {
+      s_tile = t;
+      s_nt = (int)(L % tiles_n);
+    }
   }
   __syncthreads();
   const TileInfo tile = s_tile;
+  const int nt = s_nt;
   if (tile.group < 0) return;
   gemm_tile_body<BM, BN, BK, WM, WN, KIND, ACT, BIAS>(p, tile, nt, sA, sB);
 }
@@ -297,6 +308,9 @@ gemm_tile_persistent(GemmDesc p, int tiles_n) {
 
 }  // namespace tiled
 
+bool pipe_shape_fits(GemmKind kind, const GemmDesc& g, int bm, int bn);
+hipError_t launch_gemm_pipe(GemmKind kind, const GemmDesc& g, int shape, int occ, hipStream_t s);
+
 namespace {
 using namespace tiled;
 
@@ -305,12 +319,16 @@ struct TileCfg {
   double eff;           // relative MFMA efficiency of the shape
 };
 
-constexpr int kVariants = 4;
+constexpr int kVariants = 7;
+constexpr int kFirstPipe = 4;  // variants from here on are the pipelined kernel (gemm_pipe.hip)
 constexpr TileCfg kTiles[kVariants] = {
     {256, 256, 64, 1, 1.0},   // 8 waves, wave tile 128 x 64
     {256, 128, 64, 1, 0.85},  // 8 waves, wave tile 64 x 64
     {128, 128, 64, 2, 0.9},   // wave tile 64 x 64
     {32, 256, 64, 2, 0.6},    // decode-shaped: few rows per expert
+    {256, 256, 32, 1, 1.3},   // pipelined, 4 waves, wave tile 128 x 128
+    {256, 128, 32, 1, 1.1},   // pipelined, 4 waves, wave tile 128 x 64
+    {128, 128, 32, 2, 1.1},   // pipelined, 4 waves, wave tile 64 x 64
 };
 
 int cu_count();
@@ -336,7 +354,7 @@ hipError_t run(const GemmDesc& g, int occ, hipStream_t s) {
         <<<dim3((unsigned)grid), dim3(kTileThreads), 0, s>>>(g, tiles_n);
   else
     gemm_tile_kernel<BM, BN, BK, WM, WN, KIND, ACT, BIAS>
-        <<<dim3((unsigned)grid), dim3(kTileThreads), 0, s>>>(g, tiles_n, (int)upper);
+        <<<dim3((unsigned)grid), dim3(kTileThreads), 0, s>>>(g, tiles_n);
   return hipGetLastError();
 }
 
@@ -363,11 +381,26 @@ int cu_count() {
 
 }  // namespace
 
-// Picks a tile shape from the expected rows per group (host-side estimate:
-// rows_max spread evenly over the groups, plus half a tile of padding per
-// group), or -1 if no shape covers the problem.  Predicted time ~ rounds of
-// resident workgroups x tile work / shape efficiency (efficiencies fitted to
-// measurements on MI355X).
+// Shape preference by expected rows per group, from kernel-time sweeps of
+// every shape on MI355X: weight streaming (few rows per group) is fastest
+// with the 32-row decode tile on the up GEMM and the pipelined 128x128 tile
+// on the down GEMM; a few hundred rows per group with the pipelined 128x128
+// (up) and the 128x128 persistent tile (down); thousands of rows with the
+// pipelined 256x128 (up) and the 8-wave 256x256 (down).
+const int* preferred_variants(GemmKind kind, double rows_per_group) {
+  static const int up_decode[] = {3, 6, 2, -1}, dn_decode[] = {6, 3, 2, -1};
+  static const int up_small[] = {6, 2, 5, -1}, dn_small[] = {2, 1, 6, -1};
+  static const int up_large[] = {5, 0, 4, -1}, dn_large[] = {0, 2, 5, -1};
+  if (rows_per_group < 64) return kind == kGemmUp ? up_decode : dn_decode;
+  if (rows_per_group < 1024) return kind == kGemmUp ? up_small : dn_small;
+  return kind == kGemmUp ? up_large : dn_large;
+}
+
+// Picks a tile shape, or -1 if no shape covers the problem: the first
+// preferred shape that covers it, else the cost model below.  Expected rows
+// per group = rows_max spread evenly over the groups (plus half a tile of
+// padding per group in the model).  Predicted time ~ rounds of resident
+// workgroups x tile work / shape efficiency.
 // force >= 0 selects that shape if it covers the problem.
 int pick_tile_variant(const moe_config& c, GemmKind kind, const GemmDesc& g, int force) {
   if (c.dtype != MOE_DTYPE_BF16) return -1;
@@ -376,18 +409,25 @@ int pick_tile_variant(const moe_config& c, GemmKind kind, const GemmDesc& g, int
   const double groups = g.group_off ? g.n_groups : 1;
   const double rows_per_group = (double)g.rows_max / groups;
   const int cus = cu_count();
+  auto fits = [&](int v) {
+    const TileCfg& tc = kTiles[v];
+    if (K % tc.bk != 0) return false;
+    const int ncol = kind == kGemmUp ? (swiglu ? tc.bn / 2 : tc.bn) : tc.bn;
+    const int nwidth = kind == kGemmUp ? g.f : g.d;
+    if (nwidth % ncol != 0) return false;
+    if (v >= kFirstPipe && !pipe_shape_fits(kind, g, tc.bm, tc.bn)) return false;
+    return true;
+  };
+  if (force >= 0) return force < kVariants && fits(force) ? force : -1;
+  for (const int* v = preferred_variants(kind, rows_per_group); *v >= 0; ++v)
+    if (fits(*v)) return *v;
   int best = -1;
   double best_t = 0;
   for (int v = 0; v < kVariants; ++v) {
     const TileCfg& tc = kTiles[v];
-    if (K % tc.bk != 0) continue;
+    if (!fits(v)) continue;
     const int ncol = kind == kGemmUp ? (swiglu ? tc.bn / 2 : tc.bn) : tc.bn;
     const int nwidth = kind == kGemmUp ? g.f : g.d;
-    if (nwidth % ncol != 0) continue;
-    if (force >= 0) {
-      if (v == force) return v;
-      continue;
-    }
     const double tiles_n = (double)(kind == kGemmUp ? g.n_seg : 1) * (nwidth / ncol);
     const double tiles = groups * (g.group_off ? rows_per_group / tc.bm + 0.5
                                                : std::ceil(rows_per_group / tc.bm)) * tiles_n;
@@ -403,6 +443,8 @@ int pick_tile_variant(const moe_config& c, GemmKind kind, const GemmDesc& g, int
 
 hipError_t launch_gemm_tiled(const moe_config& c, GemmKind kind, const GemmDesc& g, int variant,
                              hipStream_t s) {
+  if (variant >= kFirstPipe)
+    return launch_gemm_pipe(kind, g, variant - kFirstPipe, kTiles[variant].occ, s);
   const bool bias = g.bias != nullptr;
   if (kind == kGemmDown)
     return bias ? dispatch<kGemmDown, 0, true>(g, variant, s)
