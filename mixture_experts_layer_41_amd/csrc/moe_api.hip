@@ -89,6 +89,7 @@ RouteWs plan_route(const moe_config& c, void* ws) {
   r.st.psum = cv.take<float>(nb * c.n_experts);
   r.st.zsum = cv.take<float>(nb);
   r.st.bad = cv.take<int32_t>(nb);
+  r.st.logit_part = cv.take<float>(router_scratch_bytes(c) / sizeof(float));
   r.bytes = cv.off;
   return r;
 }
@@ -283,6 +284,7 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
     p.rs.psum = cv.take<float>(nb * E);
     p.rs.zsum = cv.take<float>(nb);
     p.rs.bad = nullptr;
+    p.rs.logit_part = cv.take<float>(router_scratch_bytes(c) / sizeof(float));
     p.scratch = cv.take<char>(permute_scratch_bytes(c));
     p.po.counts = cv.take<int32_t>(E);
     p.po.offsets = cv.take<int32_t>(E + 1);

@@ -52,6 +52,7 @@ struct RouteStats {
   float* psum;     // [nb, E] sum over the block's tokens of p[t,e]
   float* zsum;     // [nb]    sum over the block's tokens of lse^2
   int32_t* bad;    // [nb]    invalid expert indices seen by the block (permute input check)
+  float* logit_part;  // router K-split partial logits [splits][T][E] (router_scratch_bytes)
 };
 
 struct PermuteOut {
@@ -91,6 +92,8 @@ struct GemmDesc {
 // ---------------------------------------------------------------------------
 // launchers (each returns hipGetLastError() of its launch)
 
+// Bytes of RouteStats::logit_part the router needs (0: no K split).
+size_t router_scratch_bytes(const moe_config& c);
 hipError_t launch_router(const moe_config& c, const void* x, const void* w_router,
                          const float* router_bias, int32_t* topk_idx, float* topk_w,
                          float* token_lse, const RouteStats& st, hipStream_t s);

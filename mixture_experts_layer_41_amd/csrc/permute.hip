@@ -24,9 +24,9 @@
 //   colscan     large tables only: one workgroup per expert scans cnt[.][e]
 //               over the blocks (rank bases, totals, probability sums);
 //   scatter     4 routing blocks per workgroup (one wave each); small tables
-//               are summed in the workgroup itself, so no scan launch; the
-//               first workgroup also writes counts, offsets, drops and the
-//               aux record.
+//               are summed in the workgroup itself, so no scan launch; one
+//               extra workgroup writes counts, offsets, drops and the aux
+//               record while the others scatter.
 #include "moe_internal.h"
 
 namespace moe {
@@ -35,7 +35,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBlocksPerScatter = 4;     // routing blocks per scatter workgroup
 constexpr int64_t kSmallTable = 8192;    // nb * E up to this: no colscan launch
-constexpr int kBatch = 8;                // independent loads issued together
+constexpr int kBatch = 16;               // independent loads issued together
+constexpr int kMaxKReg = 8;              // top-k indices of a token kept in registers
 
 __global__ void __launch_bounds__(64)
 histogram_kernel(const int32_t* __restrict__ idx, int64_t T, int k, int E, int BT,
@@ -183,7 +184,18 @@ scatter_kernel(ScatterArgs a) {
   __shared__ int64_t ired[kThreads];
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int E = a.E;
+  // the last workgroup only writes counts, offsets, drops and the aux record;
+  // the others scatter (nobody waits for the summary)
+  const bool summary = blockIdx.x == gridDim.x - 1;
   const int64_t rb0 = (int64_t)blockIdx.x * kBlocksPerScatter;  // first routing block
+
+  // this lane's token and its expert indices, loaded before anything else
+  const int64_t rb = rb0 + wave;
+  const int64_t t = rb * a.BT + lane;
+  const bool valid = !summary && rb < a.nb && lane < a.BT && t < a.T;
+  int32_t ev[kMaxKReg];
+#pragma unroll
+  for (int j = 0; j < kMaxKReg; ++j) ev[j] = (valid && j < a.k) ? a.idx[t * a.k + j] : -1;
 
   // ---- totals and rank bases
   if (SMALL) {
@@ -271,8 +283,8 @@ scatter_kernel(ScatterArgs a) {
     __syncthreads();
   }
 
-  // ---- workgroup 0: counts, offsets, drops, aux
-  if (blockIdx.x == 0) {
+  // ---- summary workgroup: counts, offsets, drops, aux
+  if (summary) {
     int64_t my_drop = 0;
     for (int e = tid; e < E; e += kThreads) {
       a.counts[e] = tot[e];
@@ -347,19 +359,38 @@ scatter_kernel(ScatterArgs a) {
     }
   }
 
+  if (summary) return;
+
   // ---- ranks and scatter: wave w owns routing block rb0 + w, lane = token
-  const int64_t rb = rb0 + wave;
-  const int64_t t = rb * a.BT + lane;
-  const bool valid = rb < a.nb && lane < a.BT && t < a.T;
-  if (valid)
-    for (int j = 0; j < a.k; ++j) {
+  // (the first kMaxKReg indices come from registers: constant indices only)
+  if (valid) {
+#pragma unroll
+    for (int j = 0; j < kMaxKReg; ++j)
+      if (j < a.k && ev[j] >= 0 && ev[j] < E) atomicOr(&mask[wave][ev[j]], 1ull << lane);
+    for (int j = kMaxKReg; j < a.k; ++j) {
       const int e = a.idx[t * a.k + j];
       if (e >= 0 && e < E) atomicOr(&mask[wave][e], 1ull << lane);
     }
+  }
   __syncthreads();
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   if (valid) {
-    for (int j = 0; j < a.k; ++j) {
+#pragma unroll
+    for (int j = 0; j < kMaxKReg; ++j) {
+      if (j >= a.k) break;
+      const int e = ev[j];
+      int32_t row = -1;
+      if (e >= 0 && e < E) {
+        const int64_t rank = (int64_t)bases[wave][e] + __popcll(mask[wave][e] & below);
+        if (a.cap < 0 || rank < a.cap) {
+          row = offs[e] + (int32_t)rank;
+          a.perm_token[row] = (int32_t)t;
+          if (a.perm_w) a.perm_w[row] = a.topk_w[t * a.k + j];
+        }
+      }
+      a.inv_row[t * a.k + j] = row;
+    }
+    for (int j = kMaxKReg; j < a.k; ++j) {
       const int e = a.idx[t * a.k + j];
       int32_t row = -1;
       if (e >= 0 && e < E) {
@@ -464,7 +495,8 @@ hipError_t launch_permute(const moe_config& c, const RouteStats& st, const Permu
   a.x = static_cast<const uint8_t*>(x);
   a.x_perm = static_cast<uint8_t*>(x_perm);
   a.row_bytes = (int64_t)c.d_model * (c.dtype == MOE_DTYPE_BF16 ? 2 : 4);
-  const int64_t grid = (nb + kBlocksPerScatter - 1) / kBlocksPerScatter;
+  // scatter workgroups plus one summary workgroup
+  const int64_t grid = (nb + kBlocksPerScatter - 1) / kBlocksPerScatter + 1;
   if (nb * E <= kSmallTable) {
     scatter_kernel<true><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(a);
     return hipGetLastError();

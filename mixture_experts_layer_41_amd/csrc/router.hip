@@ -142,41 +142,15 @@ __device__ void logits_f32(const float* __restrict__ x, const float* __restrict_
   }
 }
 
-template <int DT, int TPW>
-__global__ void __launch_bounds__(kThreads)
-router_kernel(const void* __restrict__ x, const void* __restrict__ wr,
-              const float* __restrict__ rbias, int64_t T, int d, int E, int k,
-              int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-              float* __restrict__ token_lse, int32_t* __restrict__ st_cnt,
-              float* __restrict__ st_psum, float* __restrict__ st_zsum) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  const RouterShape s = router_shape(T, E, DT == MOE_DTYPE_BF16);
-  const int BT = s.BT, ep = s.ep;
-  const int64_t blk = blockIdx.x;
-  const int64_t t0 = blk * BT;
-  const int nvalid = (int)((T - t0) < BT ? (T - t0) : BT);
-  float* part = reinterpret_cast<float*>(smem);
-  float* lg = part;  // K-slice 0 holds the summed logits
-  int32_t* cnt = reinterpret_cast<int32_t*>(smem + s.nks * BT * (ep + 1) * 4);
-  float* lse2 = reinterpret_cast<float*>(cnt + ep);
-
-  for (int e = threadIdx.x; e < ep; e += kThreads) cnt[e] = 0;
-  if (DT == MOE_DTYPE_BF16)
-    logits_bf16<TPW>(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wr), T, d, E, t0,
-                     s, part);
-  else
-    logits_f32(static_cast<const float*>(x), static_cast<const float*>(wr), T, d, E, t0, s, part);
-  __syncthreads();
-  // sum the K slices in a fixed order and add the bias
-  for (int o = threadIdx.x; o < BT * E; o += kThreads) {
-    const int r = o / E, e = o % E;
-    float v = lg[r * (ep + 1) + e];
-    for (int q = 1; q < s.nks; ++q) v += part[(q * BT + r) * (ep + 1) + e];
-    lg[r * (ep + 1) + e] = v + (rbias ? rbias[e] : 0.f);
-  }
-  __syncthreads();
-
-  // selection: G = 256 / BT consecutive lanes per token
+// Softmax statistics, top-k selection and per-block routing statistics of
+// BT tokens whose logits (bias included) are in lg [BT][ep + 1] (LDS).  cnt
+// [ep] (zeroed by the caller) and lse2 [BT] are LDS scratch.  256 threads;
+// G = 256 / BT consecutive lanes per token.
+__device__ void select_and_stats(float* lg, int ep, int BT, int nvalid, int E, int k, int64_t t0,
+                                 int64_t blk, int32_t* __restrict__ topk_idx,
+                                 float* __restrict__ topk_w, float* __restrict__ token_lse,
+                                 int32_t* __restrict__ st_cnt, float* __restrict__ st_psum,
+                                 float* __restrict__ st_zsum, int32_t* cnt, float* lse2) {
   const int G = kThreads / BT;
   const int r = threadIdx.x / G, sub = threadIdx.x % G;
   const bool valid = r < nvalid;
@@ -255,6 +229,286 @@ router_kernel(const void* __restrict__ x, const void* __restrict__ wr,
 }
 
 template <int DT, int TPW>
+__global__ void __launch_bounds__(kThreads)
+router_kernel(const void* __restrict__ x, const void* __restrict__ wr,
+              const float* __restrict__ rbias, int64_t T, int d, int E, int k,
+              int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+              float* __restrict__ token_lse, int32_t* __restrict__ st_cnt,
+              float* __restrict__ st_psum, float* __restrict__ st_zsum) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const RouterShape s = router_shape(T, E, DT == MOE_DTYPE_BF16);
+  const int BT = s.BT, ep = s.ep;
+  const int64_t blk = blockIdx.x;
+  const int64_t t0 = blk * BT;
+  const int nvalid = (int)((T - t0) < BT ? (T - t0) : BT);
+  float* part = reinterpret_cast<float*>(smem);
+  float* lg = part;  // K-slice 0 holds the summed logits
+  int32_t* cnt = reinterpret_cast<int32_t*>(smem + s.nks * BT * (ep + 1) * 4);
+  float* lse2 = reinterpret_cast<float*>(cnt + ep);
+
+  for (int e = threadIdx.x; e < ep; e += kThreads) cnt[e] = 0;
+  if (DT == MOE_DTYPE_BF16)
+    logits_bf16<TPW>(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wr), T, d, E, t0,
+                     s, part);
+  else
+    logits_f32(static_cast<const float*>(x), static_cast<const float*>(wr), T, d, E, t0, s, part);
+  __syncthreads();
+  // sum the K slices in a fixed order and add the bias
+  for (int o = threadIdx.x; o < BT * E; o += kThreads) {
+    const int r = o / E, e = o % E;
+    float v = lg[r * (ep + 1) + e];
+    for (int q = 1; q < s.nks; ++q) v += part[(q * BT + r) * (ep + 1) + e];
+    lg[r * (ep + 1) + e] = v + (rbias ? rbias[e] : 0.f);
+  }
+  __syncthreads();
+
+  select_and_stats(lg, ep, BT, nvalid, E, k, t0, blk, topk_idx, topk_w, token_lse, st_cnt, st_psum,
+                   st_zsum, cnt, lse2);
+}
+
+// ---------------------------------------------------------------------------
+// bfloat16 router: logits GEMM with x and W_r staged through LDS
+//
+// Workgroup (blk, ks): tokens [blk*BT, +BT), all experts, K chunks
+// [c0, c1) of the ks-th split (one split unless the token blocks alone are
+// too few to fill the chip).  Per chunk of CH K elements the workgroup copies
+// the BT x rows and the ep W_r rows (16 bytes per lane, registers, the next
+// chunk loaded while the current one feeds the MFMAs) into an LDS stage,
+// rows XOR-swizzled in 16-byte pieces (piece' = piece ^ ((row / rpw) % ppr)
+// with ppr pieces per row and rpw rows per 256-byte bank window).
+// Waves own 16x16 tiles (v_mfma_f32_16x16x32_bf16); with fewer than four
+// tiles, the waves split each chunk's K steps and their partial tiles are
+// added in LDS in wave order.
+struct Router2Shape {
+  int BT, ep, n_tb, n_tiles, nks, tpw, ch, nch, ks, cps;  // cps: chunks per split
+};
+
+__host__ __device__ inline Router2Shape router2_shape(int64_t T, int E, int d) {
+  Router2Shape s;
+  s.BT = route_block_tokens(T, E);
+  s.ep = round_up(E, 16);
+  s.n_tb = s.BT / 16;
+  s.n_tiles = s.n_tb * (s.ep / 16);
+  s.nks = s.n_tiles >= 4 ? 1 : 4 / s.n_tiles;
+  s.tpw = (s.n_tiles + (4 / s.nks) - 1) / (4 / s.nks);
+  // K per chunk: one 32-wide K step per wave when the waves split K four
+  // ways; narrower chunks keep two stages of 512 expert rows within LDS
+  s.ch = s.nks == 4 ? 128 : (s.ep > 256 ? 32 : 64);
+  s.nch = (d + s.ch - 1) / s.ch;
+  const int64_t nb = (T + s.BT - 1) / s.BT;
+  int ks = 1;
+  if (nb < 128) ks = (int)((256 + nb - 1) / nb);
+  if (ks > s.nch) ks = s.nch;
+  s.cps = (s.nch + ks - 1) / ks;
+  s.ks = (s.nch + s.cps - 1) / s.cps;  // no empty split
+  return s;
+}
+
+// LDS of the logits kernel: 2 stages of (BT + ep) rows x ch bf16, then the
+// partial logits [nks][BT][ep + 1] f32, counts [ep], lse^2 [BT]
+__host__ __device__ inline int router2_stage_bytes(const Router2Shape& s) {
+  return (s.BT + s.ep) * s.ch * 2;
+}
+__host__ __device__ inline int router2_smem_bytes(const Router2Shape& s) {
+  return 2 * router2_stage_bytes(s) + s.nks * s.BT * (s.ep + 1) * 4 + s.ep * 4 + s.BT * 4;
+}
+
+template <int TPW>
+__global__ void __launch_bounds__(kThreads)
+router_bf16_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+                   const float* __restrict__ rbias, int64_t T, int d, int E, int k,
+                   int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+                   float* __restrict__ token_lse, int32_t* __restrict__ st_cnt,
+                   float* __restrict__ st_psum, float* __restrict__ st_zsum,
+                   float* __restrict__ part_out) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const Router2Shape s = router2_shape(T, E, d);
+  const int BT = s.BT, ep = s.ep, CH = s.ch;
+  const int PPR = CH / 8;                    // 16-byte pieces per row
+  const int rows = BT + ep;                  // rows per stage: tokens then experts
+  const int64_t blk = blockIdx.x;
+  const int ks = blockIdx.y;
+  const int64_t t0 = blk * BT;
+  const int nvalid = (int)((T - t0) < BT ? (T - t0) : BT);
+  u32x4* stage0 = reinterpret_cast<u32x4*>(smem);
+  u32x4* stage1 = stage0 + rows * PPR;
+  float* part = reinterpret_cast<float*>(smem + 2 * router2_stage_bytes(s));
+  int32_t* cnt = reinterpret_cast<int32_t*>(part + s.nks * BT * (ep + 1));
+  float* lse2 = reinterpret_cast<float*>(cnt + ep);
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int c0 = ks * s.cps, c1 = min(s.nch, c0 + s.cps);
+
+  // copy slots: piece q = tid + 256 i -> row q / PPR, piece q % PPR
+  const int RPW = 128 / CH;                  // rows per 256-byte bank window
+  const int nload = (rows * PPR + kThreads - 1) / kThreads;
+  constexpr int kMaxLoads = 18;  // (16 + 512) rows x 8 pieces / 256 lanes, rounded up
+  const uint16_t* src[kMaxLoads];
+  int dst[kMaxLoads];
+#pragma unroll
+  for (int i = 0; i < kMaxLoads; ++i) {
+    src[i] = nullptr;
+    dst[i] = -1;
+    if (i >= nload) continue;
+    const int q = tid + kThreads * i;
+    if (q >= rows * PPR) continue;
+    const int r = q / PPR, pc = q % PPR;
+    const uint16_t* rowp;
+    if (r < BT) {
+      int64_t tok = t0 + r;
+      if (tok >= T) tok = T - 1;
+      rowp = x + tok * (int64_t)d;
+    } else {
+      const int e = r - BT;
+      rowp = e < E ? wr + (int64_t)e * d : nullptr;  // padding experts: zeros
+    }
+    src[i] = rowp ? rowp + pc * 8 : nullptr;
+    dst[i] = r * PPR + (pc ^ ((r / RPW) % PPR));
+  }
+  u32x4 reg[kMaxLoads];
+#define MOE_ROUTER_LOAD(c_)                                                                  \
+  do {                                                                                      \
+    const int k0_ = (c_) * CH;                                                              \
+    _Pragma("unroll") for (int i_ = 0; i_ < kMaxLoads; ++i_) {                             \
+      const int kk_ = k0_ + ((tid + kThreads * i_) % PPR) * 8;                              \
+      reg[i_] = (i_ < nload && src[i_] && kk_ < d)                                          \
+                    ? *reinterpret_cast<const u32x4*>(src[i_] + k0_)                        \
+                    : u32x4{0u, 0u, 0u, 0u};                                                \
+    }                                                                                       \
+  } while (0)
+#define MOE_ROUTER_STORE(st_)                                                                \
+  do {                                                                                      \
+    _Pragma("unroll") for (int i_ = 0; i_ < kMaxLoads; ++i_)                               \
+      if (i_ < nload && dst[i_] >= 0) (st_)[dst[i_]] = reg[i_];                              \
+  } while (0)
+
+  // tiles of this wave: t = grp + (4 / nks) * i, token block t % n_tb,
+  // expert block t / n_tb; K steps of a chunk: ksub = wave % nks, + nks ...
+  const int ngrp = 4 / s.nks, grp = wave / s.nks, ksub = wave % s.nks;
+  const int ksteps = CH / 32;
+  f32x4 acc[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (c0 < c1) {
+    MOE_ROUTER_LOAD(c0);
+    MOE_ROUTER_STORE(stage0);
+  }
+  __syncthreads();
+  for (int c = c0; c < c1; ++c) {
+    u32x4* cur = ((c - c0) & 1) ? stage1 : stage0;
+    u32x4* nxt = ((c - c0) & 1) ? stage0 : stage1;
+    if (c + 1 < c1) MOE_ROUTER_LOAD(c + 1);
+    for (int kq = ksub; kq < ksteps; kq += s.nks) {
+      // lane: row lane % 16 of its tile, pieces 4 * kq + lane / 16
+      const int pc = 4 * kq + lane / 16;
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        const int t = grp + ngrp * i;
+        if (t >= s.n_tiles) break;
+        const int ra = (t % s.n_tb) * 16 + lane % 16;
+        const int rb = BT + (t / s.n_tb) * 16 + lane % 16;
+        const u32x4 a = cur[ra * PPR + (pc ^ ((ra / RPW) % PPR))];
+        const u32x4 b = cur[rb * PPR + (pc ^ ((rb / RPW) % PPR))];
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                         __builtin_bit_cast(bf16x8, b), acc[i], 0, 0, 0);
+      }
+    }
+    if (c + 1 < c1) MOE_ROUTER_STORE(nxt);
+    __syncthreads();
+  }
+
+#undef MOE_ROUTER_LOAD
+#undef MOE_ROUTER_STORE
+  // 16x16 C layout: lane holds token rows 4*(lane/16) + r, expert column lane%16
+  float* pk = part + ksub * BT * (ep + 1);
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int t = grp + ngrp * i;
+    if (t >= s.n_tiles) break;
+    const int tb = t % s.n_tb, eb = t / s.n_tb;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      pk[(tb * 16 + 4 * (lane / 16) + r) * (ep + 1) + eb * 16 + (lane % 16)] = acc[i][r];
+  }
+  for (int e = tid; e < ep; e += kThreads) cnt[e] = 0;
+  __syncthreads();
+  float* lg = part;  // wave-split slice 0 receives the sum
+  if (s.ks > 1) {
+    // K split over workgroups: this split's partial logits go out, in
+    // [ks][T][E] order; the selection kernel adds the splits in order
+    for (int o = tid; o < nvalid * E; o += kThreads) {
+      const int r = o / E, e = o % E;
+      float v = lg[r * (ep + 1) + e];
+      for (int q = 1; q < s.nks; ++q) v += part[(q * BT + r) * (ep + 1) + e];
+      part_out[((int64_t)ks * T + t0 + r) * E + e] = v;
+    }
+    return;
+  }
+  for (int o = tid; o < BT * E; o += kThreads) {
+    const int r = o / E, e = o % E;
+    float v = lg[r * (ep + 1) + e];
+    for (int q = 1; q < s.nks; ++q) v += part[(q * BT + r) * (ep + 1) + e];
+    lg[r * (ep + 1) + e] = v + (rbias ? rbias[e] : 0.f);
+  }
+  __syncthreads();
+  select_and_stats(lg, ep, BT, nvalid, E, k, t0, blk, topk_idx, topk_w, token_lse, st_cnt, st_psum,
+                   st_zsum, cnt, lse2);
+}
+
+// Selection after a K-split logits pass: the splits are added in split order.
+__global__ void __launch_bounds__(kThreads)
+router_select_kernel(const float* __restrict__ part_in, int nsplit, const float* __restrict__ rbias,
+                     int64_t T, int E, int k, int32_t* __restrict__ topk_idx,
+                     float* __restrict__ topk_w, float* __restrict__ token_lse,
+                     int32_t* __restrict__ st_cnt, float* __restrict__ st_psum,
+                     float* __restrict__ st_zsum) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int BT = route_block_tokens(T, E), ep = round_up(E, 16);
+  const int64_t blk = blockIdx.x;
+  const int64_t t0 = blk * BT;
+  const int nvalid = (int)((T - t0) < BT ? (T - t0) : BT);
+  float* lg = reinterpret_cast<float*>(smem);
+  int32_t* cnt = reinterpret_cast<int32_t*>(lg + BT * (ep + 1));
+  float* lse2 = reinterpret_cast<float*>(cnt + ep);
+  for (int e = threadIdx.x; e < ep; e += kThreads) cnt[e] = 0;
+  // each thread adds up to kPer elements' splits in split order; the loads
+  // of four splits are in flight together
+  constexpr int kPer = 32;
+  const int n = nvalid * E;
+  for (int o0 = 0; o0 < n; o0 += kThreads * kPer) {
+    float v[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) v[i] = 0.f;
+    for (int q0 = 0; q0 < nsplit; q0 += 4) {
+      float w[4][kPer];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+          const int o = o0 + threadIdx.x + i * kThreads;
+          w[u][i] = (q0 + u < nsplit && o < n) ? part_in[((int64_t)(q0 + u) * T + t0) * E + o] : 0.f;
+        }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) v[i] += w[u][i];
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int o = o0 + threadIdx.x + i * kThreads;
+      if (o < n) {
+        const int r = o / E, e = o % E;
+        lg[r * (ep + 1) + e] = v[i] + (rbias ? rbias[e] : 0.f);
+      }
+    }
+  }
+  __syncthreads();
+  select_and_stats(lg, ep, BT, nvalid, E, k, t0, blk, topk_idx, topk_w, token_lse, st_cnt, st_psum,
+                   st_zsum, cnt, lse2);
+}
+
+template <int DT, int TPW>
 hipError_t router_launch_t(const moe_config& c, const void* x, const void* w_router,
                            const float* router_bias, int32_t* topk_idx, float* topk_w,
                            float* token_lse, const RouteStats& st, hipStream_t s) {
@@ -273,7 +527,39 @@ hipError_t router_launch_t(const moe_config& c, const void* x, const void* w_rou
   return hipGetLastError();
 }
 
+template <int TPW>
+hipError_t router_bf16_launch(const moe_config& c, const void* x, const void* w_router,
+                              const float* router_bias, int32_t* topk_idx, float* topk_w,
+                              float* token_lse, const RouteStats& st, hipStream_t s) {
+  const Router2Shape sh = router2_shape(c.n_tokens, c.n_experts, c.d_model);
+  const int64_t nb = (c.n_tokens + sh.BT - 1) / sh.BT;
+  const int smem = router2_smem_bytes(sh);
+  auto fn = router_bf16_kernel<TPW>;
+  if (smem > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    if (e != hipSuccess) return e;
+  }
+  fn<<<dim3((unsigned)nb, (unsigned)sh.ks), dim3(kThreads), smem, s>>>(
+      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router), router_bias,
+      c.n_tokens, c.d_model, c.n_experts, c.top_k, topk_idx, topk_w, token_lse, st.cnt, st.psum,
+      st.zsum, st.logit_part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || sh.ks == 1) return e;
+  const int ssmem = sh.BT * (sh.ep + 1) * 4 + sh.ep * 4 + sh.BT * 4;
+  router_select_kernel<<<dim3((unsigned)nb), dim3(kThreads), ssmem, s>>>(
+      st.logit_part, sh.ks, router_bias, c.n_tokens, c.n_experts, c.top_k, topk_idx, topk_w,
+      token_lse, st.cnt, st.psum, st.zsum);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+size_t router_scratch_bytes(const moe_config& c) {
+  if (c.dtype != MOE_DTYPE_BF16) return 0;
+  const Router2Shape sh = router2_shape(c.n_tokens, c.n_experts, c.d_model);
+  return sh.ks > 1 ? (size_t)sh.ks * c.n_tokens * c.n_experts * sizeof(float) : 0;
+}
 
 hipError_t launch_router(const moe_config& c, const void* x, const void* w_router,
                          const float* router_bias, int32_t* topk_idx, float* topk_w,
@@ -281,6 +567,21 @@ hipError_t launch_router(const moe_config& c, const void* x, const void* w_route
   if (c.dtype == MOE_DTYPE_F32)
     return router_launch_t<MOE_DTYPE_F32, 1>(c, x, w_router, router_bias, topk_idx, topk_w,
                                              token_lse, st, s);
+  const Router2Shape sh2 = router2_shape(c.n_tokens, c.n_experts, c.d_model);
+  if (sh2.ks > 1) {
+    // decode-sized batch: K split over workgroups, then the selection
+#define MOE_ROUTER2_CASE(N) \
+    if (sh2.tpw <= N)       \
+      return router_bf16_launch<N>(c, x, w_router, router_bias, topk_idx, topk_w, token_lse, st, s);
+    MOE_ROUTER2_CASE(1)
+    MOE_ROUTER2_CASE(2)
+    MOE_ROUTER2_CASE(4)
+    MOE_ROUTER2_CASE(8)
+    MOE_ROUTER2_CASE(16)
+    MOE_ROUTER2_CASE(32)
+#undef MOE_ROUTER2_CASE
+    return hipErrorInvalidConfiguration;
+  }
   const int tpw = router_shape(c.n_tokens, c.n_experts, true).tiles_per_wave;
 #define MOE_ROUTER_CASE(N) \
   if (tpw <= N)            \
