@@ -308,7 +308,7 @@ gemm_tile_persistent(GemmDesc p, int tiles_n) {
 
 }  // namespace tiled
 
-bool pipe_shape_fits(GemmKind kind, const GemmDesc& g, int bm, int bn);
+bool pipe_shape_fits(GemmKind kind, const GemmDesc& g, int bm, int bn, int stages);
 hipError_t launch_gemm_pipe(GemmKind kind, const GemmDesc& g, int shape, int occ, hipStream_t s);
 
 namespace {
@@ -319,7 +319,7 @@ struct TileCfg {
   double eff;           // relative MFMA efficiency of the shape
 };
 
-constexpr int kVariants = 7;
+constexpr int kVariants = 8;
 constexpr int kFirstPipe = 4;  // variants from here on are the pipelined kernel (gemm_pipe.hip)
 constexpr TileCfg kTiles[kVariants] = {
     {256, 256, 64, 1, 1.0},   // 8 waves, wave tile 128 x 64
@@ -329,6 +329,7 @@ constexpr TileCfg kTiles[kVariants] = {
     {256, 256, 32, 1, 1.3},   // pipelined, 4 waves, wave tile 128 x 128
     {256, 128, 32, 1, 1.1},   // pipelined, 4 waves, wave tile 128 x 64
     {128, 128, 32, 2, 1.1},   // pipelined, 4 waves, wave tile 64 x 64
+    {128, 128, 32, 1, 1.0},   // pipelined, 8 stages (long K, few tiles)
 };
 
 int cu_count();
@@ -415,7 +416,7 @@ int pick_tile_variant(const moe_config& c, GemmKind kind, const GemmDesc& g, int
     const int ncol = kind == kGemmUp ? (swiglu ? tc.bn / 2 : tc.bn) : tc.bn;
     const int nwidth = kind == kGemmUp ? g.f : g.d;
     if (nwidth % ncol != 0) return false;
-    if (v >= kFirstPipe && !pipe_shape_fits(kind, g, tc.bm, tc.bn)) return false;
+    if (v >= kFirstPipe && !pipe_shape_fits(kind, g, tc.bm, tc.bn, v == 7 ? 8 : 4)) return false;
     return true;
   };
   if (force >= 0) return force < kVariants && fits(force) ? force : -1;

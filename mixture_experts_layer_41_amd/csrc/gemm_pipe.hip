@@ -3,7 +3,8 @@
 // Same operation as the other grouped GEMM kernels (expert FFN up GEMM with
 // the SwiGLU / GELU epilogue; down GEMM summing the shared-expert segments
 // along K), built for long runs of tiles:
-//   * K advances 32 elements per stage; NS = 4 LDS stages are in flight.  The
+//   * K advances 32 elements per stage; NS = 4 LDS stages rotate (8 in the
+//     deep variant, for few tiles with long K).  The
 //     global -> LDS copies use the direct-to-LDS load (global_load_lds,
 //     16 bytes per lane), so no registers stage the data, and each stage
 //     lives in its own __shared__ array, which lets the compiler see that
@@ -32,7 +33,7 @@ namespace pipe {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte chunk
 
 constexpr int BK = 32;              // K elements per stage
-constexpr int NS = 4;               // LDS stages
+constexpr int NS = 4;               // LDS stages (default; the deep variant uses 8)
 constexpr int CPR = BK / 8;         // 16-byte chunks per tile row
 constexpr int KS = BK / 16;         // MFMA K steps per stage
 static_assert(CPR == 4, "the swizzle below assumes 64-byte rows");
@@ -96,7 +97,6 @@ struct Shape {
   static constexpr int LPS = A_IW + B_IW;           // copies per lane per stage
   static_assert(MI >= 1 && NI >= 1 && A_IW >= 1 && B_IW >= 1, "tile shape");
   static_assert(BM % (16 * NW) == 0 && BN % (16 * NW) == 0, "tile shape");
-  static_assert(2 * LPS < 64, "vmcnt range");
 };
 
 // Per-lane source rows of one tile's copies, at K = 0 (the swizzled chunk
@@ -107,9 +107,11 @@ struct TileSrc {
   const uint16_t* b[B_IW];
 };
 
-template <int BM, int BN, int WM, int WN, int KIND, int ACT, bool BIAS>
+template <int BM, int BN, int WM, int WN, int KIND, int ACT, bool BIAS, int NSt>
 __global__ void __launch_bounds__(64 * WM * WN)
 gemm_pipe_kernel(GemmDesc p, int tiles_n) {
+  constexpr int NS = NSt;  // LDS stages: 4, or 8 for the deep variant
+  static_assert(NS == 4 || NS == 8, "stages");
   using Sh = Shape<BM, BN, WM, WN>;
   constexpr int NT = Sh::NT, TM = Sh::TM, TN = Sh::TN, MI = Sh::MI, NI = Sh::NI;
   constexpr int A_IW = Sh::A_IW, B_IW = Sh::B_IW, LPS = Sh::LPS;
@@ -117,6 +119,8 @@ gemm_pipe_kernel(GemmDesc p, int tiles_n) {
   static_assert(RW <= kWave, "one gather-index copy per wave");
   constexpr bool kSwiglu = (KIND == kGemmUp && ACT == MOE_ACT_SWIGLU);
   static_assert(!kSwiglu || (NI % 2 == 0), "SwiGLU pairs gate and up blocks");
+  static_assert((NS - 3) * LPS < 64, "vmcnt range");
+  constexpr int XS = NS > 4 ? 1 : 0;  // the deep variant's extra stages
 
   __shared__ __attribute__((aligned(16))) u32x4 sA0[BM * CPR];
   __shared__ __attribute__((aligned(16))) u32x4 sA1[BM * CPR];
@@ -126,6 +130,10 @@ gemm_pipe_kernel(GemmDesc p, int tiles_n) {
   __shared__ __attribute__((aligned(16))) u32x4 sB1[BN * CPR];
   __shared__ __attribute__((aligned(16))) u32x4 sB2[BN * CPR];
   __shared__ __attribute__((aligned(16))) u32x4 sB3[BN * CPR];
+  __shared__ __attribute__((aligned(16))) u32x4 sA4[XS * BM * CPR + 1], sA5[XS * BM * CPR + 1];
+  __shared__ __attribute__((aligned(16))) u32x4 sA6[XS * BM * CPR + 1], sA7[XS * BM * CPR + 1];
+  __shared__ __attribute__((aligned(16))) u32x4 sB4[XS * BN * CPR + 1], sB5[XS * BN * CPR + 1];
+  __shared__ __attribute__((aligned(16))) u32x4 sB6[XS * BN * CPR + 1], sB7[XS * BN * CPR + 1];
   __shared__ int s_idx[3][BM];               // gather indices of three consecutive tiles
   __shared__ int s_off[kMaxExperts + 1];     // group row offsets
   __shared__ int s_tstart[kMaxExperts + 1];  // first row tile of each group
@@ -297,7 +305,13 @@ gemm_pipe_kernel(GemmDesc p, int tiles_n) {
   MOE_PIPE_LOAD(cur, 0, sA0, sB0);
   MOE_PIPE_LOAD(cur, 1, sA1, sB1);
   MOE_PIPE_LOAD(cur, 2, sA2, sB2);
-  wait_vmcnt<LPS>();  // stages 0 and 1 landed (this lane's copies)
+  if constexpr (NS == 8) {
+    MOE_PIPE_LOAD(cur, 3, sA3, sB3);
+    MOE_PIPE_LOAD(cur, 4, sA4, sB4);
+    MOE_PIPE_LOAD(cur, 5, sA5, sB5);
+    MOE_PIPE_LOAD(cur, 6, sA6, sB6);
+  }
+  wait_vmcnt<(NS - 3) * LPS>();  // stages 0 and 1 landed (this lane's copies)
   wg_barrier();
 
   // MFMA operands: the first K step of a stage (R0 / R1, alternating between
@@ -360,15 +374,28 @@ gemm_pipe_kernel(GemmDesc p, int tiles_n) {
     MOE_PIPE_FRAGS(Rna, Rnb, na_, nb_, 0);                                                  \
     __builtin_amdgcn_sched_barrier(0); /* next operands in flight under these MFMAs */     \
     MOE_PIPE_MFMA(RKa, RKb);                                                                \
-    wait_vmcnt_lds<LPS>();                                                                  \
+    wait_vmcnt_lds<(NS - 3) * LPS>();                                                       \
     wg_barrier();                                                                           \
   } while (0)
 
-    for (int kk = 0; kk < nk; kk += NS) {
-      MOE_PIPE_STEP(kk + 0, sA0, sB0, sA1, sB1, sA3, sB3, R0a, R0b, R1a, R1b);
-      MOE_PIPE_STEP(kk + 1, sA1, sB1, sA2, sB2, sA0, sB0, R1a, R1b, R0a, R0b);
-      MOE_PIPE_STEP(kk + 2, sA2, sB2, sA3, sB3, sA1, sB1, R0a, R0b, R1a, R1b);
-      MOE_PIPE_STEP(kk + 3, sA3, sB3, sA0, sB0, sA2, sB2, R1a, R1b, R0a, R0b);
+    if constexpr (NS == 4) {
+      for (int kk = 0; kk < nk; kk += NS) {
+        MOE_PIPE_STEP(kk + 0, sA0, sB0, sA1, sB1, sA3, sB3, R0a, R0b, R1a, R1b);
+        MOE_PIPE_STEP(kk + 1, sA1, sB1, sA2, sB2, sA0, sB0, R1a, R1b, R0a, R0b);
+        MOE_PIPE_STEP(kk + 2, sA2, sB2, sA3, sB3, sA1, sB1, R0a, R0b, R1a, R1b);
+        MOE_PIPE_STEP(kk + 3, sA3, sB3, sA0, sB0, sA2, sB2, R1a, R1b, R0a, R0b);
+      }
+    } else {
+      for (int kk = 0; kk < nk; kk += NS) {
+        MOE_PIPE_STEP(kk + 0, sA0, sB0, sA1, sB1, sA7, sB7, R0a, R0b, R1a, R1b);
+        MOE_PIPE_STEP(kk + 1, sA1, sB1, sA2, sB2, sA0, sB0, R1a, R1b, R0a, R0b);
+        MOE_PIPE_STEP(kk + 2, sA2, sB2, sA3, sB3, sA1, sB1, R0a, R0b, R1a, R1b);
+        MOE_PIPE_STEP(kk + 3, sA3, sB3, sA4, sB4, sA2, sB2, R1a, R1b, R0a, R0b);
+        MOE_PIPE_STEP(kk + 4, sA4, sB4, sA5, sB5, sA3, sB3, R0a, R0b, R1a, R1b);
+        MOE_PIPE_STEP(kk + 5, sA5, sB5, sA6, sB6, sA4, sB4, R1a, R1b, R0a, R0b);
+        MOE_PIPE_STEP(kk + 6, sA6, sB6, sA7, sB7, sA5, sB5, R0a, R0b, R1a, R1b);
+        MOE_PIPE_STEP(kk + 7, sA7, sB7, sA0, sB0, sA6, sB6, R1a, R1b, R0a, R0b);
+      }
     }
 #undef MOE_PIPE_STEP
 
@@ -477,7 +504,7 @@ int device_cus() {
   return n;
 }
 
-template <int BM, int BN, int WM, int WN, int KIND, int ACT, bool BIAS>
+template <int BM, int BN, int WM, int WN, int KIND, int ACT, bool BIAS, int NSt>
 hipError_t run_pipe(const GemmDesc& g, int occ, hipStream_t s) {
   constexpr int NT = 64 * WM * WN;
   constexpr bool kSwiglu = (KIND == kGemmUp && ACT == MOE_ACT_SWIGLU);
@@ -487,7 +514,7 @@ hipError_t run_pipe(const GemmDesc& g, int occ, hipStream_t s) {
   if (upper <= 0 || g.rows_max <= 0) return hipSuccess;
   int64_t grid = std::min<int64_t>(upper, (int64_t)device_cus() * occ);
   grid = (grid + 7) / 8 * 8;  // a multiple of 8 (XCDs)
-  pipe::gemm_pipe_kernel<BM, BN, WM, WN, KIND, ACT, BIAS>
+  pipe::gemm_pipe_kernel<BM, BN, WM, WN, KIND, ACT, BIAS, NSt>
       <<<dim3((unsigned)grid), dim3(NT), 0, s>>>(g, tiles_n);
   return hipGetLastError();
 }
@@ -495,22 +522,24 @@ hipError_t run_pipe(const GemmDesc& g, int occ, hipStream_t s) {
 template <int KIND, int ACT, bool BIAS>
 hipError_t dispatch_pipe(const GemmDesc& g, int shape, int occ, hipStream_t s) {
   switch (shape) {
-    case 0: return run_pipe<256, 256, 2, 2, KIND, ACT, BIAS>(g, occ, s);
-    case 1: return run_pipe<256, 128, 2, 2, KIND, ACT, BIAS>(g, occ, s);
-    default: return run_pipe<128, 128, 2, 2, KIND, ACT, BIAS>(g, occ, s);
+    case 0: return run_pipe<256, 256, 2, 2, KIND, ACT, BIAS, 4>(g, occ, s);
+    case 1: return run_pipe<256, 128, 2, 2, KIND, ACT, BIAS, 4>(g, occ, s);
+    case 2: return run_pipe<128, 128, 2, 2, KIND, ACT, BIAS, 4>(g, occ, s);
+    default: return run_pipe<128, 128, 2, 2, KIND, ACT, BIAS, 8>(g, occ, s);
   }
 }
 
 }  // namespace
 
-// Shape index 0: 256x256, 1: 256x128, 2: 128x128 (all 4 waves, 2 x 2).
-bool pipe_shape_fits(GemmKind kind, const GemmDesc& g, int bm, int bn) {
+// Shape index 0: 256x256, 1: 256x128, 2: 128x128 (4 stages), 3: 128x128 with
+// 8 stages (all 4 waves, 2 x 2).
+bool pipe_shape_fits(GemmKind kind, const GemmDesc& g, int bm, int bn, int stages) {
   (void)bm;
   const bool swiglu = kind == kGemmUp && g.act == MOE_ACT_SWIGLU;
   const int K = kind == kGemmUp ? g.d : g.f;
   if (K % pipe::BK != 0) return false;
   const int nk = (kind == kGemmUp ? 1 : g.n_seg) * (K / pipe::BK);
-  if (nk % pipe::NS != 0) return false;
+  if (nk % stages != 0) return false;
   const int ncol = kind == kGemmUp ? (swiglu ? bn / 2 : bn) : bn;
   const int width = kind == kGemmUp ? g.f : g.d;
   return width % ncol == 0;
