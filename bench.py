@@ -32,7 +32,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_gemm_flash_T4096_traffic.
 # sources of the grouped GEMM kernels: the committed counter figures hold only
 # while these are unchanged
 GEMM_SRCS = [os.path.join(ROOT, "mixture_experts_layer_41_amd", "csrc", n)
-             for n in ("gemm.hip", "gemm_mfma.hip", "gemm_common.h")]
+             for n in ("gemm.hip", "gemm_mfma.hip", "gemm_pipe.hip", "gemm_common.h")]
 
 
 def log(*a):
