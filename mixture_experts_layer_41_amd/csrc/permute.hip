@@ -86,6 +86,39 @@ __device__ int64_t block_sum_i64(int64_t v, int64_t* red) {
   return r;
 }
 
+// Four block-wide sums at once (two integer, two float64): a butterfly over
+// each wave (every lane ends with the same value), then the four wave
+// partials added in wave order.  One barrier pair instead of a tree of
+// barriers per sum.
+__device__ void block_sum4(int64_t& i0, int64_t& i1, double& f0, double& f1, int64_t* ired,
+                           double* red) {
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    i0 += __shfl_xor(i0, o);
+    i1 += __shfl_xor(i1, o);
+    f0 += __shfl_xor(f0, o);
+    f1 += __shfl_xor(f1, o);
+  }
+  const int wave = threadIdx.x / kWave, nw = kThreads / kWave;
+  if (threadIdx.x % kWave == 0) {
+    ired[wave] = i0;
+    ired[nw + wave] = i1;
+    red[wave] = f0;
+    red[nw + wave] = f1;
+  }
+  __syncthreads();
+  i0 = ired[0];
+  i1 = ired[nw];
+  f0 = red[0];
+  f1 = red[nw];
+  for (int w = 1; w < nw; ++w) {
+    i0 += ired[w];
+    i1 += ired[nw + w];
+    f0 += red[w];
+    f1 += red[nw + w];
+  }
+  __syncthreads();
+}
+
 // One workgroup per expert e: rank bases base[b][e] = sum_{b' < b} cnt[b'][e],
 // total[e], pe[e] = sum_b psum[b][e] (float64, fixed order); workgroup 0 also
 // sums the lse^2 partials and the invalid-index counts.
@@ -173,6 +206,39 @@ struct ScatterArgs {
   int64_t row_bytes;
 };
 
+// Column sums of the count table (and of the probability sums when P) over
+// the blocks g, g + G, ... for expert e: the total, the tokens of the blocks
+// before each of the workgroup's blocks, and P_e's share.  Batches of
+// kBatch unconditional loads (clamped rows, then a select) keep the requests
+// in flight together.
+template <bool P>
+__device__ __forceinline__ void sum_blocks(const ScatterArgs& a, int e, int g, int G, int64_t rb0,
+                                           int32_t& s_tot, int32_t (&s_pre)[kBlocksPerScatter],
+                                           double& s_p) {
+  const int E = a.E;
+  for (int64_t b = g; b < a.nb; b += (int64_t)G * kBatch) {
+    int32_t v[kBatch];
+    float pv[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t bb = b + (int64_t)u * G;
+      const int64_t bc = bb < a.nb ? bb : a.nb - 1;
+      v[u] = a.cnt[bc * E + e];
+      if (P) pv[u] = a.psum[bc * E + e];
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t bb = b + (int64_t)u * G;
+      const bool in = bb < a.nb;
+      const int32_t c = in ? v[u] : 0;
+      s_tot += c;
+      if (P) s_p += in ? (double)pv[u] : 0.0;
+#pragma unroll
+      for (int w = 0; w < kBlocksPerScatter; ++w) s_pre[w] += (bb < rb0 + w) ? c : 0;
+    }
+  }
+}
+
 template <bool SMALL>
 __global__ void __launch_bounds__(kThreads)
 scatter_kernel(ScatterArgs a) {
@@ -182,6 +248,8 @@ scatter_kernel(ScatterArgs a) {
   __shared__ unsigned long long mask[kBlocksPerScatter][kMaxExperts];
   __shared__ double red[kThreads];
   __shared__ int64_t ired[kThreads];
+  __shared__ double Pe[kMaxExperts];  // summary: P_e numerators (sum of block prob. sums)
+  __shared__ int32_t part[1 + kBlocksPerScatter][kThreads];  // [total, bases][G][E] partials
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int E = a.E;
   // the last workgroup only writes counts, offsets, drops and the aux record;
@@ -196,6 +264,29 @@ scatter_kernel(ScatterArgs a) {
   int32_t ev[kMaxKReg];
 #pragma unroll
   for (int j = 0; j < kMaxKReg; ++j) ev[j] = (valid && j < a.k) ? a.idx[t * a.k + j] : -1;
+  // the summary workgroup issues its other loads (per-block z sums and
+  // invalid-logit flags, probability sums below) in the same round as the
+  // count loads: one memory round trip instead of four
+  // (unconditional loads from clamped addresses, masked where they are
+  // used: a load under a per-lane condition is followed by a wait for it)
+  constexpr int kSumReg = 4;
+  const bool want_aux = summary && a.aux != nullptr;
+  float zv[kSumReg] = {0.f, 0.f, 0.f, 0.f};
+  int32_t bv[kSumReg] = {0, 0, 0, 0};
+  if (SMALL && want_aux) {
+#pragma unroll
+    for (int u = 0; u < kSumReg; ++u) {
+      const int64_t b = tid + (int64_t)u * kThreads;
+      zv[u] = a.zsum[b < a.nb ? b : a.nb - 1];
+    }
+  }
+  if (SMALL && summary && a.bad) {
+#pragma unroll
+    for (int u = 0; u < kSumReg; ++u) {
+      const int64_t b = tid + (int64_t)u * kThreads;
+      bv[u] = a.bad[b < a.nb ? b : a.nb - 1];
+    }
+  }
 
   // ---- totals and rank bases
   if (SMALL) {
@@ -204,49 +295,50 @@ scatter_kernel(ScatterArgs a) {
     // blocks, the tokens of the blocks before it; partials meet in LDS in a
     // fixed order (integer sums, exact)
     const int G = E <= kThreads ? kThreads / E : 1;
-    int32_t* pt = reinterpret_cast<int32_t*>(red);  // [G][E] partial totals
+    const int EW = E <= kThreads ? E : kThreads;  // experts per pass
     for (int e0 = 0; e0 < E; e0 += kThreads) {
       const int e = e0 + (E <= kThreads ? tid % E : tid);
       const int g = E <= kThreads ? tid / E : 0;
       int32_t s_tot = 0, s_pre[kBlocksPerScatter] = {0, 0, 0, 0};
+      double s_p = 0.0;  // summary: this thread's share of P_e (interleaved blocks, in order)
       if (g < G && e < E) {
-        // batches of independent loads keep several requests in flight
-        for (int64_t b = g; b < a.nb; b += (int64_t)G * kBatch) {
-          int32_t v[kBatch];
+        if (want_aux)
+          sum_blocks<true>(a, e, g, G, rb0, s_tot, s_pre, s_p);
+        else
+          sum_blocks<false>(a, e, g, G, rb0, s_tot, s_pre, s_p);
+      }
+      // all partials meet in LDS in one round: the total, this workgroup's
+      // rank bases (not needed by the summary) and P_e (summary only)
+      if (g < G && e < E) {
+        const int slot = g * EW + (e - e0);
+        part[0][slot] = s_tot;
+        if (!summary) {
 #pragma unroll
-          for (int u = 0; u < kBatch; ++u) {
-            const int64_t bb = b + (int64_t)u * G;
-            v[u] = bb < a.nb ? a.cnt[bb * E + e] : 0;
-          }
-#pragma unroll
-          for (int u = 0; u < kBatch; ++u) {
-            const int64_t bb = b + (int64_t)u * G;
-            s_tot += v[u];
-#pragma unroll
-            for (int w = 0; w < kBlocksPerScatter; ++w) s_pre[w] += (bb < rb0 + w) ? v[u] : 0;
-          }
+          for (int w = 0; w < kBlocksPerScatter; ++w) part[1 + w][slot] = s_pre[w];
         }
-      }
-      const bool act = g < G && e < E;
-      // totals
-      if (act) pt[g * (E <= kThreads ? E : kThreads) + (e - e0)] = s_tot;
-      __syncthreads();
-      if (tid < (E <= kThreads ? E : min(kThreads, E - e0))) {
-        int32_t sum = 0;
-        for (int q = 0; q < G; ++q) sum += pt[q * (E <= kThreads ? E : kThreads) + tid];
-        tot[e0 + tid] = sum;
+        if (want_aux) red[slot] = s_p;
       }
       __syncthreads();
-      for (int w = 0; w < kBlocksPerScatter; ++w) {
-        if (act) pt[g * (E <= kThreads ? E : kThreads) + (e - e0)] = s_pre[w];
-        __syncthreads();
-        if (tid < (E <= kThreads ? E : min(kThreads, E - e0))) {
+      const int ne = min(EW, E - e0);
+      const int rows = summary ? 1 : 1 + kBlocksPerScatter;
+      for (int o = tid; o < (rows + (want_aux ? 1 : 0)) * ne; o += kThreads) {
+        const int row = o / ne, c = o % ne;
+        if (row < rows) {  // the G partials added in order (integers: exact anyway)
           int32_t sum = 0;
-          for (int q = 0; q < G; ++q) sum += pt[q * (E <= kThreads ? E : kThreads) + tid];
-          bases[w][e0 + tid] = sum;
+#pragma unroll 8
+          for (int q = 0; q < G; ++q) sum += part[row][q * EW + c];
+          if (row == 0)
+            tot[e0 + c] = sum;
+          else
+            bases[row - 1][e0 + c] = sum;
+        } else {  // P_e: the G partials added in order
+          double P = 0.0;
+#pragma unroll 8
+          for (int q = 0; q < G; ++q) P += red[q * EW + c];
+          Pe[e0 + c] = P;
         }
-        __syncthreads();
       }
+      __syncthreads();
       if (E <= kThreads) break;
     }
   } else {
@@ -262,100 +354,75 @@ scatter_kernel(ScatterArgs a) {
     for (int e = tid; e < E; e += kThreads) mask[w][e] = 0ull;
   __syncthreads();
 
-  // ---- kept counts and their exclusive scan (offsets), Hillis-Steele in LDS
-  for (int e = tid; e < E; e += kThreads) {
-    const int64_t t = tot[e];
-    offs[e + 1] = (int32_t)((a.cap < 0 || t < a.cap) ? t : a.cap);
+  // ---- kept counts and their exclusive scan (offsets): wave 0 scans 64
+  // experts at a time with lane shuffles and carries the running total
+  if (wave == 0) {
+    int32_t carry = 0;
+    for (int c0 = 0; c0 < E; c0 += kWave) {
+      const int e = c0 + lane;
+      int32_t v = 0;
+      if (e < E) {
+        const int64_t te = tot[e];
+        v = (int32_t)((a.cap < 0 || te < a.cap) ? te : a.cap);
+      }
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int32_t n = __shfl_up(v, o);
+        if (lane >= o) v += n;
+      }
+      if (e < E) offs[e + 1] = carry + v;
+      carry += __shfl(v, kWave - 1);
+    }
+    if (lane == 0) offs[0] = 0;
   }
-  if (tid == 0) offs[0] = 0;
   __syncthreads();
-  for (int o = 1; o <= E; o <<= 1) {
-    int32_t v[2] = {0, 0};
-    for (int q = 0; q < 2; ++q) {
-      const int e = tid + q * kThreads + 1;
-      if (e <= E && e - o >= 1) v[q] = offs[e - o];
-    }
-    __syncthreads();
-    for (int q = 0; q < 2; ++q) {
-      const int e = tid + q * kThreads + 1;
-      if (e <= E) offs[e] += v[q];
-    }
-    __syncthreads();
-  }
 
   // ---- summary workgroup: counts, offsets, drops, aux
   if (summary) {
-    int64_t my_drop = 0;
+    int64_t my_drop = 0, my_bad = 0;
     for (int e = tid; e < E; e += kThreads) {
       a.counts[e] = tot[e];
       a.offsets[e] = offs[e];
       my_drop += tot[e] - (offs[e + 1] - offs[e]);
     }
     if (tid == 0) a.offsets[E] = offs[E];
-    const int64_t dropped = block_sum_i64(my_drop, ired);
-    int64_t nbd;
     if (SMALL) {
-      int64_t v = 0;
+#pragma unroll
+      for (int u = 0; u < kSumReg; ++u) my_bad += tid + (int64_t)u * kThreads < a.nb ? bv[u] : 0;
       if (a.bad)
-        for (int64_t b = tid; b < a.nb; b += kThreads) v += a.bad[b];
-      nbd = block_sum_i64(v, ired);
-    } else {
-      nbd = *a.nbad;
+        for (int64_t b = tid + (int64_t)kSumReg * kThreads; b < a.nb; b += kThreads) my_bad += a.bad[b];
     }
-    if (tid == 0) a.n_dropped[0] = nbd ? -1 : (int32_t)dropped;
+    // lb = E * sum_e f_e P_e with f_e = total_e / (T k), P_e = sum_t p / T
+    double lbp = 0.0, zp = 0.0;
     if (a.aux) {
-      // lb = E * sum_e f_e P_e with f_e = total_e / (T k), P_e = sum_t p / T
-      double lbp = 0.0, zp = 0.0;
       if (SMALL) {
-        // P_e: G = 256 / E threads per expert sum interleaved blocks, then
-        // the G partials are added in order (E > 256: one thread per expert)
-        const int G = E <= kThreads ? kThreads / E : 1;
-        double part = 0.0;
-        if (E <= kThreads) {
-          const int e = tid % E, g = tid / E;
-          if (g < G)
-            for (int64_t b = g; b < a.nb; b += (int64_t)G * kBatch) {
-              float v[kBatch];
+        // P_e was summed with the counts: G = 256 / E threads per expert
+        // over interleaved blocks, the G partials added in order (E > 256:
+        // one thread per expert, blocks in order)
+        for (int e = tid; e < E; e += kThreads)
+          lbp += ((double)tot[e] / (double)(a.T * a.k)) * (Pe[e] / (double)a.T);
 #pragma unroll
-              for (int u = 0; u < kBatch; ++u) {
-                const int64_t bb = b + (int64_t)u * G;
-                v[u] = bb < a.nb ? a.psum[bb * E + e] : 0.f;
-              }
-#pragma unroll
-              for (int u = 0; u < kBatch; ++u) part += (double)v[u];
-            }
-          red[tid] = part;
-          __syncthreads();
-          if (tid < E) {
-            double P = 0.0;
-            for (int q = 0; q < G; ++q) P += red[q * E + tid];
-            lbp = ((double)tot[tid] / (double)(a.T * a.k)) * (P / (double)a.T);
-          }
-          __syncthreads();
-        } else {
-          for (int e = tid; e < E; e += kThreads) {
-            double P = 0.0;
-            for (int64_t b = 0; b < a.nb; ++b) P += (double)a.psum[b * E + e];
-            lbp += ((double)tot[e] / (double)(a.T * a.k)) * (P / (double)a.T);
-          }
-        }
-#pragma unroll 8
-        for (int64_t b = tid; b < a.nb; b += kThreads) zp += (double)a.zsum[b];
+        for (int u = 0; u < kSumReg; ++u)
+          zp += tid + (int64_t)u * kThreads < a.nb ? (double)zv[u] : 0.0;
+        for (int64_t b = tid + (int64_t)kSumReg * kThreads; b < a.nb; b += kThreads)
+          zp += (double)a.zsum[b];
       } else {
         for (int e = tid; e < E; e += kThreads)
           lbp += ((double)tot[e] / (double)(a.T * a.k)) * (a.pe[e] / (double)a.T);
       }
-      const double lb = block_sum_f64(lbp, red) * (double)E;
-      const double zsum_all = SMALL ? block_sum_f64(zp, red) : *a.zs;
-      const double z = zsum_all / (double)a.T;
-      if (tid == 0) {
-        a.aux->load_balance = lb;
-        a.aux->z_loss = z;
-        a.aux->weighted = 0.01 * lb + 0.001 * z;
-        a.aux->n_dropped = dropped;
-        a.aux->capacity = a.cap;
-        a.aux->n_kept = a.T * a.k - dropped;
-      }
+    }
+    block_sum4(my_drop, my_bad, lbp, zp, ired, red);
+    const int64_t dropped = my_drop;
+    const int64_t nbd = SMALL ? my_bad : (int64_t)*a.nbad;
+    if (tid == 0) a.n_dropped[0] = nbd ? -1 : (int32_t)dropped;
+    if (a.aux && tid == 0) {
+      const double lb = lbp * (double)E;
+      const double z = (SMALL ? zp : *a.zs) / (double)a.T;
+      a.aux->load_balance = lb;
+      a.aux->z_loss = z;
+      a.aux->weighted = 0.01 * lb + 0.001 * z;
+      a.aux->n_dropped = dropped;
+      a.aux->capacity = a.cap;
+      a.aux->n_kept = a.T * a.k - dropped;
     }
   }
 

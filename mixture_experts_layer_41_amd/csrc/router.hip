@@ -11,14 +11,16 @@
 // chosen so that there are enough workgroups to cover the chip) and all E
 // experts.
 //  * bf16 logits: v_mfma_f32_16x16x32_bf16 on 16-token x 16-expert tiles; A
-//    (x rows) and B (W_r rows) are read straight from memory, 32 contiguous
-//    bytes per lane per 64-wide K chunk (both operands use the same K order,
-//    so the dot products are unchanged).  When a workgroup has fewer than 4
+//    (x rows) and B (W_r rows) are read straight from memory, two 16-byte
+//    loads per lane per 64-wide K chunk, the four lanes of a row covering 64
+//    contiguous bytes per load (both operands use the same K order, so the
+//    dot products are unchanged).  When a workgroup has fewer than 4
 //    tiles, the waves split K and their partial tiles are added in LDS in a
 //    fixed order.
 //  * float32 logits: plain FMA dot products.
-//  * selection: 256 / BT lanes per token; max, sum of exponentials and each
-//    of the k picks are wave-shuffle reductions inside that lane group.
+//  * selection: 256 / BT lanes per token, each holding its share of the
+//    token's logits as order keys in registers; max, sum of exponentials
+//    and each of the k picks end in DPP reductions inside that lane group.
 #include "moe_internal.h"
 
 namespace moe {
@@ -68,7 +70,10 @@ __device__ void logits_bf16(const uint16_t* __restrict__ x, const uint16_t* __re
   const int ngrp = 4 / s.nks;
   const int nch = (d + 63) / 64;        // 64-wide K chunks
   const int c0 = ks * nch / s.nks, c1 = (ks + 1) * nch / s.nks;
-  const int kq = 16 * (lane / 16);      // this lane's 16 K elements of a chunk
+  // this lane's K elements of a 64-wide chunk: [kq, kq + 8) for the first
+  // MFMA and [kq + 32, kq + 40) for the second, so the four lanes of a row
+  // read 64 contiguous bytes per load
+  const int kq = 8 * (lane / 16);
 
   f32x4 acc[TPW];
   const uint16_t* brow[TPW];
@@ -93,13 +98,13 @@ __device__ void logits_bf16(const uint16_t* __restrict__ x, const uint16_t* __re
     for (int u = 0; u < U; ++u) {
       const int k0 = (c + u) * 64;
       const bool in = c + u < c1;
-      const bool ok0 = in && k0 + kq < d, ok1 = in && k0 + kq + 8 < d;
+      const bool ok0 = in && k0 + kq < d, ok1 = in && k0 + kq + 32 < d;
       A[u][0] = ok0 ? *reinterpret_cast<const uint4*>(arow + k0) : make_uint4(0, 0, 0, 0);
-      A[u][1] = ok1 ? *reinterpret_cast<const uint4*>(arow + k0 + 8) : make_uint4(0, 0, 0, 0);
+      A[u][1] = ok1 ? *reinterpret_cast<const uint4*>(arow + k0 + 32) : make_uint4(0, 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < TPW; ++i) {
         B[u][i][0] = (bok[i] && ok0) ? *reinterpret_cast<const uint4*>(brow[i] + k0) : make_uint4(0, 0, 0, 0);
-        B[u][i][1] = (bok[i] && ok1) ? *reinterpret_cast<const uint4*>(brow[i] + k0 + 8) : make_uint4(0, 0, 0, 0);
+        B[u][i][1] = (bok[i] && ok1) ? *reinterpret_cast<const uint4*>(brow[i] + k0 + 32) : make_uint4(0, 0, 0, 0);
       }
     }
 #pragma unroll
@@ -142,70 +147,139 @@ __device__ void logits_f32(const float* __restrict__ x, const float* __restrict_
   }
 }
 
+// Order key of a logit: a larger logit has a larger key and -0 and +0 share
+// one; NaN gets 0, below every number (-inf has 0x007FFFFF).  No number has
+// key 0, so 0 also marks an expert that is absent or already picked.
+__device__ inline uint32_t order_key(float l) {
+  const uint32_t u = l == 0.f ? 0u : __float_as_uint(l);
+  const uint32_t key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return l != l ? 0u : key;
+}
+__device__ inline float key_logit(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+// Lane exchanges inside aligned groups of 4, 8 or 16 lanes (DPP, no LDS
+// traffic): xor 1 and xor 2 inside a quad, then the half-row mirror (lane i
+// <-> 7 - i) and the row mirror (i <-> 15 - i).  Once every lane of a quad
+// holds the quad's result, a mirror pairs each lane with a lane of the other
+// half, so every lane of the group ends with the group's result; sums are
+// the same in every lane (commutative pairs).
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+template <int CTRL>
+__device__ inline uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ inline void argmax_step(uint32_t& bk, int& be) {
+  const uint32_t ok = dpp_u32<CTRL>(bk);
+  const int oe = (int)dpp_u32<CTRL>((uint32_t)be);
+  const bool take = ok > bk || (ok == bk && oe < be);
+  bk = take ? ok : bk;
+  be = take ? oe : be;
+}
+template <int CTRL>
+__device__ inline void max_step(uint32_t& k) {
+  const uint32_t o = dpp_u32<CTRL>(k);
+  k = o > k ? o : k;
+}
+template <int CTRL>
+__device__ inline void sum_step(float& z) {
+  z += __uint_as_float(dpp_u32<CTRL>(__float_as_uint(z)));
+}
+
 // Softmax statistics, top-k selection and per-block routing statistics of
 // BT tokens whose logits (bias included) are in lg [BT][ep + 1] (LDS).  cnt
 // [ep] (zeroed by the caller) and lse2 [BT] are LDS scratch.  256 threads;
-// G = 256 / BT consecutive lanes per token.
-__device__ void select_and_stats(float* lg, int ep, int BT, int nvalid, int E, int k, int64_t t0,
-                                 int64_t blk, int32_t* __restrict__ topk_idx,
-                                 float* __restrict__ topk_w, float* __restrict__ token_lse,
-                                 int32_t* __restrict__ st_cnt, float* __restrict__ st_psum,
-                                 float* __restrict__ st_zsum, int32_t* cnt, float* lse2) {
+// G = 256 / BT consecutive lanes per token (4, 8 or 16), lane sub of a token
+// owns experts e = sub + G i, i < NPL (NPL >= E / G), as order keys in
+// registers.  Each of the k picks is a branch-free scan of the lane's keys,
+// then a group arg-max in the order (logit descending, index ascending); the
+// winner's key is then cleared in its owner lane.
+template <int NPL>
+__device__ void select_and_stats_t(float* lg, int ep, int BT, int nvalid, int E, int k, int64_t t0,
+                                   int64_t blk, int32_t* __restrict__ topk_idx,
+                                   float* __restrict__ topk_w, float* __restrict__ token_lse,
+                                   int32_t* __restrict__ st_cnt, float* __restrict__ st_psum,
+                                   float* __restrict__ st_zsum, int32_t* cnt, float* lse2) {
   const int G = kThreads / BT;
   const int r = threadIdx.x / G, sub = threadIdx.x % G;
   const bool valid = r < nvalid;
   const int64_t tok = t0 + r;
   float* row = lg + r * (ep + 1);
-  float m = -INFINITY;
-#pragma unroll 4
-  for (int e = sub; e < E; e += G) m = fmaxf(m, row[e]);
-  for (int o = G / 2; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, G));
+  constexpr int kNone = 0x7FFFFFFF;
+  uint32_t key[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int e = sub + G * i;
+    key[i] = e < E ? order_key(row[e]) : 0u;
+  }
+  // max over the numbers of the row (NaN ignored)
+  uint32_t mk = 0;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) mk = key[i] > mk ? key[i] : mk;
+  max_step<kDppXor1>(mk);
+  max_step<kDppXor2>(mk);
+  if (G >= 8) max_step<kDppHalfMirror>(mk);
+  if (G >= 16) max_step<kDppMirror>(mk);
+  const float m = key_logit(mk);
   float z = 0.f;
 #pragma unroll 4
   for (int e = sub; e < E; e += G) z += expf(row[e] - m);
-  for (int o = G / 2; o > 0; o >>= 1) z += __shfl_xor(z, o, G);
+  sum_step<kDppXor1>(z);
+  sum_step<kDppXor2>(z);
+  if (G >= 8) sum_step<kDppHalfMirror>(z);
+  if (G >= 16) sum_step<kDppMirror>(z);
   const float lse = m + logf(z);
   if (valid && sub == 0) {
     if (token_lse) token_lse[tok] = lse;
     lse2[r] = lse * lse;
   }
-  // k picks; each takes the best element strictly after the previous pick in
-  // the order (logit desc, index asc)
-  float prev_l = INFINITY, wsum = 0.f;
-  int prev_e = -1;
+  // the first kRegPicks weights stay in registers until they are
+  // renormalised (no read-back of global memory); later ones (k > kRegPicks)
+  // are stored and rescaled in place
+  constexpr int kRegPicks = 8;
+  float exv[kRegPicks];
+  float wsum = 0.f;
   for (int j = 0; j < k; ++j) {
-    float bl = -INFINITY;
-    int be = 0x7FFFFFFF;
-    for (int e = sub; e < E; e += G) {
-      const float l = row[e];
-      const bool after = (l < prev_l) || (l == prev_l && e > prev_e);
-      if (after && (be == 0x7FFFFFFF || l > bl || (l == bl && e < be))) {
-        bl = l;
-        be = e;
-      }
-    }
-    for (int o = G / 2; o > 0; o >>= 1) {
-      const float ol = __shfl_xor(bl, o, G);
-      const int oe = __shfl_xor(be, o, G);
-      if (oe != 0x7FFFFFFF && (be == 0x7FFFFFFF || ol > bl || (ol == bl && oe < be))) {
-        bl = ol;
-        be = oe;
-      }
-    }
-    if (be == 0x7FFFFFFF) be = j % E;  // only reachable with NaN logits: keep indices in range
-    const float ex = expf(bl - m);
+    // the lane's largest key, then its lowest index holding it
+    uint32_t bk = key[0];
+#pragma unroll
+    for (int i = 1; i < NPL; ++i) bk = key[i] > bk ? key[i] : bk;
+    int bi = -1;
+#pragma unroll
+    for (int i = NPL - 1; i >= 0; --i) bi = key[i] == bk ? i : bi;
+    if (bk == 0u) bi = -1;
+    const int my_e = bi >= 0 ? sub + G * bi : kNone;
+    int be = my_e;
+    argmax_step<kDppXor1>(bk, be);
+    argmax_step<kDppXor2>(bk, be);
+    if (G >= 8) argmax_step<kDppHalfMirror>(bk, be);
+    if (G >= 16) argmax_step<kDppMirror>(bk, be);
+    // the owner lane clears the winner's key
+    const bool mine = be == my_e && bi >= 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) key[i] = (mine && i == bi) ? 0u : key[i];
+    // no number left (NaN logits, k above the count of numbers): keep the
+    // index in range, weight 0
+    if (be == kNone) be = j % E;
+    const float ex = bk != 0u ? expf(key_logit(bk) - m) : 0.f;
     wsum += ex;
     if (valid && sub == 0) {
       topk_idx[tok * k + j] = be;
-      topk_w[tok * k + j] = ex;
+      if (j >= kRegPicks) topk_w[tok * k + j] = ex;
       atomicAdd(&cnt[be], 1);
     }
-    prev_l = bl;
-    prev_e = be;
+#pragma unroll
+    for (int q = 0; q < kRegPicks; ++q)
+      if (q == j) exv[q] = ex;
   }
   if (valid && sub == 0) {
     const float inv = 1.f / wsum;
-    for (int j = 0; j < k; ++j) topk_w[tok * k + j] *= inv;
+#pragma unroll
+    for (int q = 0; q < kRegPicks; ++q)
+      if (q < k) topk_w[tok * k + q] = exv[q] * inv;
+    for (int j = kRegPicks; j < k; ++j) topk_w[tok * k + j] *= inv;
   }
   // probabilities for the per-expert sums
   const float iz = 1.f / z;
@@ -226,6 +300,27 @@ __device__ void select_and_stats(float* lg, int ep, int BT, int nvalid, int E, i
     for (int q = 0; q < nvalid; ++q) acc += lse2[q];
     st_zsum[blk] = acc;
   }
+}
+
+// Register budget chosen at run time (float32 router, split-K selection
+// kernel).  The bfloat16 logits kernels instantiate select_and_stats_t with
+// NPL = 4 TPW directly: a wave's TPW 16x16 tiles cover (BT / 16) * (ep / 16)
+// <= 4 TPW tiles, and E / G <= BT * ep / 256 is that tile count.
+__device__ void select_and_stats_any(float* lg, int ep, int BT, int nvalid, int E, int k, int64_t t0,
+                                     int64_t blk, int32_t* __restrict__ topk_idx,
+                                     float* __restrict__ topk_w, float* __restrict__ token_lse,
+                                     int32_t* __restrict__ st_cnt, float* __restrict__ st_psum,
+                                     float* __restrict__ st_zsum, int32_t* cnt, float* lse2) {
+  const int npl = (E + kThreads / BT - 1) / (kThreads / BT);
+#define MOE_SELECT(N)                                                                           \
+  select_and_stats_t<N>(lg, ep, BT, nvalid, E, k, t0, blk, topk_idx, topk_w, token_lse, st_cnt, \
+                        st_psum, st_zsum, cnt, lse2)
+  if (npl <= 4) MOE_SELECT(4);
+  else if (npl <= 8) MOE_SELECT(8);
+  else if (npl <= 16) MOE_SELECT(16);
+  else if (npl <= 32) MOE_SELECT(32);
+  else MOE_SELECT(64);
+#undef MOE_SELECT
 }
 
 template <int DT, int TPW>
@@ -262,8 +357,13 @@ router_kernel(const void* __restrict__ x, const void* __restrict__ wr,
   }
   __syncthreads();
 
-  select_and_stats(lg, ep, BT, nvalid, E, k, t0, blk, topk_idx, topk_w, token_lse, st_cnt, st_psum,
-                   st_zsum, cnt, lse2);
+  if (DT == MOE_DTYPE_BF16)
+    select_and_stats_t<(4 * TPW < 64 ? 4 * TPW : 64)>(lg, ep, BT, nvalid, E, k, t0, blk, topk_idx,
+                                                      topk_w, token_lse, st_cnt, st_psum, st_zsum,
+                                                      cnt, lse2);
+  else
+    select_and_stats_any(lg, ep, BT, nvalid, E, k, t0, blk, topk_idx, topk_w, token_lse, st_cnt,
+                         st_psum, st_zsum, cnt, lse2);
 }
 
 // ---------------------------------------------------------------------------
@@ -452,8 +552,9 @@ router_bf16_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
     lg[r * (ep + 1) + e] = v + (rbias ? rbias[e] : 0.f);
   }
   __syncthreads();
-  select_and_stats(lg, ep, BT, nvalid, E, k, t0, blk, topk_idx, topk_w, token_lse, st_cnt, st_psum,
-                   st_zsum, cnt, lse2);
+  select_and_stats_t<(4 * TPW < 64 ? 4 * TPW : 64)>(lg, ep, BT, nvalid, E, k, t0, blk, topk_idx,
+                                                    topk_w, token_lse, st_cnt, st_psum, st_zsum,
+                                                    cnt, lse2);
 }
 
 // Selection after a K-split logits pass: the splits are added in split order.
@@ -504,8 +605,8 @@ router_select_kernel(const float* __restrict__ part_in, int nsplit, const float*
     }
   }
   __syncthreads();
-  select_and_stats(lg, ep, BT, nvalid, E, k, t0, blk, topk_idx, topk_w, token_lse, st_cnt, st_psum,
-                   st_zsum, cnt, lse2);
+  select_and_stats_any(lg, ep, BT, nvalid, E, k, t0, blk, topk_idx, topk_w, token_lse, st_cnt,
+                       st_psum, st_zsum, cnt, lse2);
 }
 
 template <int DT, int TPW>
