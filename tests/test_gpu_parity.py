@@ -102,6 +102,9 @@ SMALL = [
     ("bf16_E512", 96, 2048, 512, 8, 32, 0, "bf16", "swiglu", 0.0, "none", "none", False),
     ("f32_k1", 90, 16, 3, 1, 16, 0, "f32", "gelu", 0.0, "random", "none", False),
     ("bf16_cap1", 40, 32, 4, 2, 32, 0, "bf16", "swiglu", 0.25, "none", "none", False),
+    # k above 8: picks past the register-held ones, generic combine and scatter paths
+    ("bf16_k12_cap", 300, 64, 16, 12, 64, 1, "bf16", "swiglu", 1.0, "none", "none", True),
+    ("f32_k10", 100, 32, 12, 10, 32, 0, "f32", "gelu", 0.0, "random", "none", False),
 ]
 
 
