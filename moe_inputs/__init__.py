@@ -13,7 +13,12 @@ whole stack (the decode-shaped layer holds 22.6 GB of expert weights).
 
 Storage: "f32" tensors are float32 arrays; "bf16" tensors are uint16 arrays
 holding bfloat16 bit patterns, rounded from float32 draws with
-round-to-nearest-even.
+round-to-nearest-even.  Layers with 8-bit expert weights get int8 code
+arrays (a standard normal draw times 127/4, rounded and clipped to
+[-127, 127]) and one float32 scale per weight row (0.02 * 4 / 127 times a
+factor drawn uniformly from [0.75, 1.25]), so that scale * code has about
+the 0.02 standard deviation of the other layers' weights.  These are drawn
+as given, already-quantized weights.
 """
 
 from __future__ import annotations
@@ -31,6 +36,7 @@ __all__ = ["LayerConfig", "CONFIGS", "get_config", "f32_to_bf16_bits", "Bank",
 TAGS = {
     "x": 1, "w_router": 2, "w1": 3, "b1": 4, "w2": 5, "b2": 6,
     "ws1": 7, "sb1": 8, "ws2": 9, "sb2": 10, "x_redraw": 11,
+    "w1_scale": 12, "w2_scale": 13, "ws1_scale": 14, "ws2_scale": 15,
 }
 X_ROW_BLOCK = 4096          # rows of x per sub-stream
 WEIGHT_STD = 0.02
@@ -53,6 +59,7 @@ class LayerConfig:
     expert_bias: str = "none"      # "none", "zero" or "random"
     add_residual: bool = False
     seed: int = 0
+    weights: str = "act"      # expert weights: "act" (activation dtype) or "int8" (codes + row scales)
 
     @property
     def w1_rows(self) -> int:
@@ -79,6 +86,9 @@ CONFIGS = {
     # decode-shaped, weight-streaming layer
     "c5": LayerConfig("decode_bf16_T128_d7168_E256_k8_S1_f2048", T=128, d=7168, E=256,
                       k=8, f=2048, S=1, seed=1005),
+    # the same layer with 8-bit expert weights (row-scaled INT8 codes)
+    "c5q": LayerConfig("decode_int8w_T128_d7168_E256_k8_S1_f2048", T=128, d=7168, E=256,
+                       k=8, f=2048, S=1, weights="int8", seed=1006),
 }
 
 
@@ -109,7 +119,9 @@ class Bank:
     """Lazily generated stack of per-expert tensors, [n, *shape].
 
     bank[e] draws expert e's tensor from its own stream; array() builds the
-    whole stack.  Values: N(0, std^2) rounded to the storage dtype, or zeros.
+    whole stack.  Values: N(0, std^2) rounded to the storage dtype, or zeros;
+    dtype "int8": codes rint(N(0, 1) * 127 / 4) clipped to [-127, 127];
+    dtype "scale": float32 std * 4 / 127 * U(0.75, 1.25) (one per row).
     """
 
     def __init__(self, seed: int, tag: str, n: int, shape, dtype: str, std: float, zero=False):
@@ -119,7 +131,7 @@ class Bank:
 
     @property
     def np_dtype(self):
-        return np.uint16 if self.dtype == "bf16" else np.float32
+        return {"bf16": np.uint16, "int8": np.int8}.get(self.dtype, np.float32)
 
     @property
     def full_shape(self):
@@ -127,7 +139,7 @@ class Bank:
 
     @property
     def nbytes(self) -> int:
-        return self.n * int(np.prod(self.shape)) * (2 if self.dtype == "bf16" else 4)
+        return self.n * int(np.prod(self.shape)) * np.dtype(self.np_dtype).itemsize
 
     def __len__(self) -> int:
         return self.n
@@ -137,7 +149,12 @@ class Bank:
             raise IndexError(e)
         if self.zero:
             return np.zeros(self.shape, dtype=self.np_dtype)
+        if self.dtype == "scale":
+            u = _rng(self.seed, self.tag, e).uniform(0.75, 1.25, self.shape).astype(np.float32)
+            return u * np.float32(self.std * 4.0 / 127.0)
         z = _rng(self.seed, self.tag, e).standard_normal(self.shape, dtype=np.float32)
+        if self.dtype == "int8":
+            return np.clip(np.rint(z * np.float32(127.0 / 4.0)), -127, 127).astype(np.int8)
         z *= np.float32(self.std)
         return _store(z, self.dtype)
 
@@ -219,16 +236,25 @@ def make_inputs(cfg: LayerConfig, accept=None, max_redraws: int = 64, materializ
     bias_zero = cfg.expert_bias == "zero"
     has_bias = cfg.expert_bias in ("zero", "random")
     E, S, d, f = cfg.E, cfg.S, cfg.d, cfg.f
+    q8 = cfg.weights == "int8"
+    wdt = "int8" if q8 else dt
     banks = {
-        "w1": Bank(cfg.seed, "w1", E, (cfg.w1_rows, d), dt, WEIGHT_STD),
-        "w2": Bank(cfg.seed, "w2", E, (d, f), dt, WEIGHT_STD),
+        "w1": Bank(cfg.seed, "w1", E, (cfg.w1_rows, d), wdt, WEIGHT_STD),
+        "w2": Bank(cfg.seed, "w2", E, (d, f), wdt, WEIGHT_STD),
         "b1": Bank(cfg.seed, "b1", E, (cfg.w1_rows,), dt, WEIGHT_STD, zero=bias_zero) if has_bias else None,
         "b2": Bank(cfg.seed, "b2", E, (d,), dt, WEIGHT_STD, zero=bias_zero) if has_bias else None,
-        "ws1": Bank(cfg.seed, "ws1", S, (cfg.w1_rows, d), dt, WEIGHT_STD) if S else None,
-        "ws2": Bank(cfg.seed, "ws2", S, (d, f), dt, WEIGHT_STD) if S else None,
+        "ws1": Bank(cfg.seed, "ws1", S, (cfg.w1_rows, d), wdt, WEIGHT_STD) if S else None,
+        "ws2": Bank(cfg.seed, "ws2", S, (d, f), wdt, WEIGHT_STD) if S else None,
         "sb1": Bank(cfg.seed, "sb1", S, (cfg.w1_rows,), dt, WEIGHT_STD, zero=bias_zero) if (S and has_bias) else None,
         "sb2": Bank(cfg.seed, "sb2", S, (d,), dt, WEIGHT_STD, zero=bias_zero) if (S and has_bias) else None,
     }
+    if cfg.weights not in ("act", "int8"):
+        raise ValueError(cfg.weights)
+    if q8:  # one float32 scale per weight row
+        banks["w1_scale"] = Bank(cfg.seed, "w1_scale", E, (cfg.w1_rows,), "scale", WEIGHT_STD)
+        banks["w2_scale"] = Bank(cfg.seed, "w2_scale", E, (d,), "scale", WEIGHT_STD)
+        banks["ws1_scale"] = Bank(cfg.seed, "ws1_scale", S, (cfg.w1_rows,), "scale", WEIGHT_STD) if S else None
+        banks["ws2_scale"] = Bank(cfg.seed, "ws2_scale", S, (d,), "scale", WEIGHT_STD) if S else None
     out = {"x": x, "w_router": w_router, "router_bias": rbias, "n_redrawn": len(redrawn)}
     for key, bank in banks.items():
         out[key] = None if bank is None else (bank.array() if materialize else bank)

@@ -36,6 +36,10 @@ the design notes):
   * shared experts have weight 1 and sit outside the router ([P4 §2.1],
     [P5 §2]).  The residual x is added only when asked ([P2 §4.1] adds it
     inside the layer, [P3 §3.2] outside).
+  * 8-bit expert weights ([P3 §6] suggests compressing each expert's
+    weights to INT8 for deployment, with no scheme given): symmetric INT8
+    codes q with one float32 scale per weight row, W[n, :] = scale[n] *
+    q[n, :] (the row is an output channel of W1 and of W2).
 
 Parity pins: every function below is exercised by the CPU tests against
 closed forms, brute force or an independently written dense computation; the
@@ -52,6 +56,8 @@ import numpy as np
 
 __all__ = [
     "decode",
+    "dequantize_int8",
+    "expert_weight",
     "router_logits",
     "softmax_lse",
     "topk_select",
@@ -89,6 +95,35 @@ def decode(a, dtype: str) -> np.ndarray:
             raise TypeError("f32 tensors are passed as float32")
         return a.astype(np.float64)
     raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def dequantize_int8(q, scale) -> np.ndarray:
+    """INT8 weight codes with one scale per row -> float64 ([P3 §6]: expert
+    weights compressed to INT8).
+
+    q: int8 [rows, cols]; scale: float32 [rows].  W[n, c] = scale[n] * q[n, c],
+    exact in float64 (an 8-bit integer times a float32).
+    """
+    q = np.asarray(q)
+    scale = np.asarray(scale)
+    if q.dtype != np.int8:
+        raise TypeError("INT8 weight codes are passed as int8")
+    if scale.dtype != np.float32:
+        raise TypeError("INT8 weight scales are passed as float32")
+    if q.ndim != 2 or scale.shape != (q.shape[0],):
+        raise ValueError("one scale per row of the code matrix")
+    return scale.astype(np.float64)[:, None] * q.astype(np.float64)
+
+
+def expert_weight(t, name: str, i: int, dtype: str, weights: str = "act") -> np.ndarray:
+    """Weight matrix `name` ("w1", "w2", "ws1", "ws2") of expert i as float64:
+    decoded from the activation dtype, or dequantized from INT8 codes with
+    the row scales t[name + "_scale"][i]."""
+    if weights == "int8":
+        return dequantize_int8(t[name][i], t[name + "_scale"][i])
+    if weights != "act":
+        raise ValueError(f"unknown weight format {weights!r}")
+    return decode(t[name][i], dtype)
 
 
 # ---------------------------------------------------------------------------
@@ -261,14 +296,16 @@ def expert_ffn(x_rows: np.ndarray, w1: np.ndarray, b1, w2: np.ndarray, b2, act: 
     return out
 
 
-def shared_ffn(x: np.ndarray, ws1, sb1, ws2, sb2, n_shared: int, act: str, dtype: str) -> np.ndarray:
+def shared_ffn(x: np.ndarray, ws1, sb1, ws2, sb2, n_shared: int, act: str, dtype: str,
+               weights: str = "act", ws1_scale=None, ws2_scale=None) -> np.ndarray:
     """Sum of the always-active shared experts, each with weight 1 ([P4 §2.1],
-    [P5 §2])."""
+    [P5 §2]).  weights "int8": ws1 / ws2 hold INT8 codes with row scales."""
+    t = {"ws1": ws1, "ws2": ws2, "ws1_scale": ws1_scale, "ws2_scale": ws2_scale}
     out = np.zeros_like(x)
     for s in range(n_shared):
         out += expert_ffn(
-            x, decode(ws1[s], dtype), None if sb1 is None else decode(sb1[s], dtype),
-            decode(ws2[s], dtype), None if sb2 is None else decode(sb2[s], dtype), act)
+            x, expert_weight(t, "ws1", s, dtype, weights), None if sb1 is None else decode(sb1[s], dtype),
+            expert_weight(t, "ws2", s, dtype, weights), None if sb2 is None else decode(sb2[s], dtype), act)
     return out
 
 
@@ -316,7 +353,10 @@ def forward(cfg, t, rows=None, want_routed_rows=False):
     """Full forward of the layer on CPU.
 
     cfg: object with T, d, E, k, f, S, dtype ("bf16"/"f32"), act
-         ("swiglu"/"gelu"), capacity_factor (<= 0: none), add_residual.
+         ("swiglu"/"gelu"), capacity_factor (<= 0: none), add_residual, and
+         optionally weights ("act", or "int8": expert weights are INT8
+         codes with float32 row scales w1_scale / w2_scale / ws1_scale /
+         ws2_scale in t).
     t:   dict with x [T, d], w_router [E, d], router_bias [E] float32 or None,
          w1 / b1 / w2 / b2 (indexable by expert), ws1 / sb1 / ws2 / sb2
          (indexable by shared expert, may be None when S == 0).
@@ -329,6 +369,7 @@ def forward(cfg, t, rows=None, want_routed_rows=False):
     Returns a dict of float64 / int64 arrays and scalars.
     """
     dt = cfg.dtype
+    wf = getattr(cfg, "weights", "act")
     x = decode(t["x"], dt)
     T, d = x.shape
     E, k = cfg.E, cfg.k
@@ -358,8 +399,8 @@ def forward(cfg, t, rows=None, want_routed_rows=False):
             continue
         toks = perm_token[sel]
         out = expert_ffn(
-            x[toks], decode(t["w1"][e], dt), None if b1s is None else decode(b1s[e], dt),
-            decode(t["w2"][e], dt), None if b2s is None else decode(b2s[e], dt), cfg.act)
+            x[toks], expert_weight(t, "w1", e, dt, wf), None if b1s is None else decode(b1s[e], dt),
+            expert_weight(t, "w2", e, dt, wf), None if b2s is None else decode(b2s[e], dt), cfg.act)
         for i, r in enumerate(sel):
             tt, j = int(perm_token[r]), int(perm_slot[r])
             routed[pos[tt]] += w[tt, j] * out[i]
@@ -368,7 +409,8 @@ def forward(cfg, t, rows=None, want_routed_rows=False):
 
     shared = None
     if cfg.S > 0:
-        shared = shared_ffn(x[tok], t["ws1"], t.get("sb1"), t["ws2"], t.get("sb2"), cfg.S, cfg.act, dt)
+        shared = shared_ffn(x[tok], t["ws1"], t.get("sb1"), t["ws2"], t.get("sb2"), cfg.S, cfg.act, dt,
+                            wf, t.get("ws1_scale"), t.get("ws2_scale"))
     y = combine(routed, shared, x[tok] if cfg.add_residual else None)
 
     return {

@@ -416,3 +416,128 @@ def test_param_arithmetic_fixture():
     assert round(E * per_expert / 2 ** 20) == g["total_M"]
     assert round(2 * d * 4 * d / 2 ** 20) == g["dense_M"]
     assert round(k * per_expert / 2 ** 20) == g["active_M"]
+
+
+# ---------------------------------------------------------------------------
+# 8-bit expert weights ([P3 §6]: compress each expert's weights to INT8;
+# read as symmetric codes with one float32 scale per weight row)
+
+
+def int8_tensors(cfg, seed):
+    """Small INT8 codes with row scales (shared experts too), float32 x."""
+    r = np.random.default_rng(seed)
+    rows = 2 * cfg.f if cfg.act == "swiglu" else cfg.f
+
+    def codes(*shape):
+        return r.integers(-127, 128, size=shape).astype(np.int8)
+
+    def scales(*shape):
+        return f32(r.uniform(0.002, 0.004, size=shape))
+
+    t = {
+        "x": f32(r.standard_normal((cfg.T, cfg.d))),
+        "w_router": f32(r.standard_normal((cfg.E, cfg.d)) * 0.5),
+        "router_bias": None,
+        "w1": codes(cfg.E, rows, cfg.d), "w1_scale": scales(cfg.E, rows),
+        "w2": codes(cfg.E, cfg.d, cfg.f), "w2_scale": scales(cfg.E, cfg.d),
+        "b1": None, "b2": None,
+        "ws1": codes(cfg.S, rows, cfg.d) if cfg.S else None,
+        "ws1_scale": scales(cfg.S, rows) if cfg.S else None,
+        "ws2": codes(cfg.S, cfg.d, cfg.f) if cfg.S else None,
+        "ws2_scale": scales(cfg.S, cfg.d) if cfg.S else None,
+        "sb1": None, "sb2": None,
+    }
+    return t
+
+
+@dataclass
+class QCfg(Cfg):
+    weights: str = "int8"
+
+
+def test_dequantize_int8_worked_values():
+    """Row n is scaled by scale[n]: hand-computed values (binary fractions,
+    exact)."""
+    q = np.array([[1, -2, 0], [127, -127, 64]], dtype=np.int8)
+    s = f32([0.5, 2.0])
+    w = oracle.dequantize_int8(q, s)
+    assert np.array_equal(w, np.array([[0.5, -1.0, 0.0], [254.0, -254.0, 128.0]]))
+    with pytest.raises(TypeError):
+        oracle.dequantize_int8(q.astype(np.int16), s)
+    with pytest.raises(ValueError):  # a scale per column is not the format
+        oracle.dequantize_int8(q, f32([1.0, 1.0, 1.0]))
+
+
+@pytest.mark.parametrize("act", ["swiglu", "gelu"])
+def test_int8_unit_scales_equal_the_float_layer(act):
+    """Scales of 1: the INT8 layer is the float layer on the codes."""
+    cfg = QCfg(T=40, d=16, E=4, k=2, f=8, S=1, act=act)
+    t = int8_tensors(cfg, 11)
+    for key in ("w1_scale", "w2_scale", "ws1_scale", "ws2_scale"):
+        t[key] = np.ones_like(t[key])
+    for key in ("w1", "w2", "ws1", "ws2"):  # small codes keep the activations moderate
+        t[key] = (t[key] // 43).astype(np.int8)
+    fl = dict(t)
+    for key in ("w1", "w2", "ws1", "ws2"):
+        fl[key] = t[key].astype(np.float32)
+    a = oracle.forward(cfg, t)
+    b = oracle.forward(Cfg(T=40, d=16, E=4, k=2, f=8, S=1, act=act), fl)
+    assert np.array_equal(a["y"], b["y"])
+
+
+def test_int8_down_scale_is_per_output_row():
+    """A zero scale on output row m of every W2 (routed and shared) zeroes
+    column m of the layer output; a per-column reading would not."""
+    cfg = QCfg(T=30, d=12, E=3, k=2, f=8, S=1)
+    t = int8_tensors(cfg, 12)
+    m = 5
+    t["w2_scale"][:, m] = 0
+    t["ws2_scale"][:, m] = 0
+    y = oracle.forward(cfg, t)["y"]
+    assert np.all(y[:, m] == 0.0)
+    assert np.all(np.abs(np.delete(y, m, axis=1)).max(axis=0) > 0)
+
+
+def test_int8_gate_scale_is_per_row_of_w1():
+    """A zero scale on gate row n of every W1 (SwiGLU) silences hidden unit
+    n: the same output as the float layer with column n of every W2 cleared."""
+    cfg = QCfg(T=30, d=12, E=3, k=2, f=8, S=1)
+    t = int8_tensors(cfg, 13)
+    n = 3
+    t["w1_scale"][:, n] = 0
+    t["ws1_scale"][:, n] = 0
+    a = oracle.forward(cfg, t)["y"]
+    fl = dict(t)
+    for key, sk in (("w1", "w1_scale"), ("w2", "w2_scale"), ("ws1", "ws1_scale"), ("ws2", "ws2_scale")):
+        fl[key] = f32(t[key].astype(np.float64) * t[sk][..., None])
+    fl["w2"][:, :, n] = 0
+    fl["ws2"][:, :, n] = 0
+    b = oracle.forward(Cfg(T=30, d=12, E=3, k=2, f=8, S=1), fl)["y"]
+    # the float layer holds scale * code rounded to float32 (relative 6e-8
+    # per weight); a scale on the wrong axis would differ at order one
+    np.testing.assert_allclose(a, b, rtol=1e-4, atol=1e-7)
+
+
+def test_int8_output_linear_in_down_scales():
+    """Doubling every W2 scale doubles the output (no residual, no b2)."""
+    cfg = QCfg(T=30, d=12, E=3, k=2, f=8, S=1)
+    t = int8_tensors(cfg, 14)
+    a = oracle.forward(cfg, t)["y"]
+    t2 = dict(t)
+    t2["w2_scale"] = t["w2_scale"] * np.float32(2)
+    t2["ws2_scale"] = t["ws2_scale"] * np.float32(2)
+    b = oracle.forward(cfg, t2)["y"]
+    np.testing.assert_allclose(b, 2.0 * a, rtol=1e-12, atol=1e-15)
+
+
+def test_int8_generator_codes_and_scales():
+    """The INT8 workload's inputs: codes in [-127, 127], positive row scales,
+    scale * code with about the 0.02 standard deviation of the bf16 layers."""
+    cfg = get_config("c5q", T=8, d=256, E=4, f=64)
+    t = make_inputs(cfg)
+    for key in ("w1", "w2", "ws1", "ws2"):
+        assert t[key].dtype == np.int8 and t[key].min() >= -127 and t[key].max() <= 127
+        s = t[key + "_scale"]
+        assert s.dtype == np.float32 and s.shape == t[key].shape[:2] and (s > 0).all()
+    w = t["w1"].astype(np.float64) * t["w1_scale"][..., None]
+    assert 0.018 < w.std() < 0.022
