@@ -124,14 +124,17 @@ def main():
             return None
         if isinstance(a, Bank):
             from concurrent.futures import ThreadPoolExecutor
-            out = torch.empty(a.full_shape, dtype=torch.bfloat16 if cfg.dtype == "bf16"
-                              else torch.float32, device="cuda")
+            tdt = {np.uint16: torch.bfloat16, np.int8: torch.int8}.get(a.np_dtype, torch.float32)
+            out = torch.empty(a.full_shape, dtype=tdt, device="cuda")
             with ThreadPoolExecutor(max_workers=16) as ex:
                 for e, arr in ex.map(lambda e: (e, a[e]), range(a.n)):
                     out[e].copy_(dev(arr))
             return out
-        if cfg.dtype == "bf16":
-            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.int8:          # 8-bit weight codes
+            return torch.from_numpy(a).cuda()
+        if a.dtype == np.uint16:        # bf16 bit patterns
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
 
     rb = t["router_bias"]
@@ -139,7 +142,10 @@ def main():
         w_router=dev(t["w_router"]), w1=dev(t["w1"]), w2=dev(t["w2"]), b1=dev(t["b1"]),
         b2=dev(t["b2"]), shared_w1=dev(t["ws1"]), shared_w2=dev(t["ws2"]),
         shared_b1=dev(t["sb1"]), shared_b2=dev(t["sb2"]),
+        w1_scale=dev(t.get("w1_scale")), w2_scale=dev(t.get("w2_scale")),
+        shared_w1_scale=dev(t.get("ws1_scale")), shared_w2_scale=dev(t.get("ws2_scale")),
         router_bias=None if rb is None else torch.from_numpy(rb).cuda())
+    q8 = cfg.weights == "int8"
     x = dev(t["x"])
     c = B.config_of(cfg)
     fwd = B.Forward(c, W)
@@ -194,27 +200,37 @@ def main():
     pr = B.moe_permute(c, fwd.topk_idx)
     torch.cuda.synchronize()
     y_perm = torch.empty(T * k, d, dtype=B.torch_dtype(c), device="cuda")
-    ffn_args = (c, cfg.E, 1, T * k, x, pr["perm_token"], pr["expert_offsets"], W.w1, W.b1, W.w2,
-                W.b2, y_perm)
+    if q8:
+        ffn_call = B.moe_expert_ffn_int8
+        ffn_args = (c, cfg.E, 1, T * k, x, pr["perm_token"], pr["expert_offsets"], W.w1,
+                    W.w1_scale, W.b1, W.w2, W.w2_scale, W.b2, y_perm)
+    else:
+        ffn_call = B.moe_expert_ffn
+        ffn_args = (c, cfg.E, 1, T * k, x, pr["perm_token"], pr["expert_offsets"], W.w1, W.b1,
+                    W.w2, W.b2, y_perm)
     for _ in range(10):
-        B.moe_expert_ffn(*ffn_args)
+        ffn_call(*ffn_args)
     n_ffn = max(50, args.steps // 2)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record(stream)
     for _ in range(n_ffn):
-        B.moe_expert_ffn(*ffn_args)
+        ffn_call(*ffn_args)
     ev1.record(stream)
     ev1.synchronize()
     ffn_s = ev0.elapsed_time(ev1) / 1e3 / n_ffn
     gemm_tflops = routed_flops / ffn_s / 1e12
     # algorithmic bytes of the same call: the weights of every expert that
-    # keeps a row (W1 [w1_rows, d] and W2 [d, f]), the gathered input rows,
-    # H written and read back, the output rows
+    # keeps a row (W1 [w1_rows, d] and W2 [d, f]; with 8-bit weights one byte
+    # per code plus a float32 scale per row), the gathered input rows, H
+    # written and read back, the output rows
     counts = pr["expert_offsets"].cpu().numpy()
     touched = int((counts[1:] - counts[:-1] > 0).sum())
     ab = 2 if cfg.dtype == "bf16" else 4
-    weight_bytes = ab * touched * (cfg.w1_rows + f) * d
+    if q8:
+        weight_bytes = touched * ((cfg.w1_rows + f) * d + 4 * (cfg.w1_rows + d))
+    else:
+        weight_bytes = ab * touched * (cfg.w1_rows + f) * d
     routed_bytes = weight_bytes + ab * (R * d + 2 * R * f + R * d)
     # MFMA-bound unless the weights alone give fewer flops per byte than the
     # MFMA / HBM ridge (the weight-streaming decode shape)
@@ -278,7 +294,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "tokens": T, "d_model": d, "experts": cfg.E,
                    "top_k": k, "d_ffn": f, "shared_experts": S,
-                   "capacity_factor": cfg.capacity_factor, "launch": mode,
+                   "capacity_factor": cfg.capacity_factor, "expert_weights": "int8 codes + "
+                   "f32 row scales" if q8 else ("bf16" if cfg.dtype == "bf16" else "f32"),
+                   "launch": mode,
                    "eager_us_per_step": round(eager_s / args.steps * 1e6, 2),
                    "graph_us_per_step": None if graph_s is None else round(graph_s / args.steps * 1e6, 2),
                    "layer_tflops": round(layer_flops / (best_s / args.steps) / 1e12, 2),

@@ -19,6 +19,8 @@
  *     output activations) are float32 when cfg->dtype == MOE_DTYPE_F32 and
  *     bfloat16 when cfg->dtype == MOE_DTYPE_BF16.  Router bias, routing
  *     weights and log-sum-exp values are always float32; indices int32.
+ *     Expert weights may instead be INT8 codes with float32 row scales
+ *     (cfg->weight_format, moe_weight_format).
  *   - Pointers to act-dtype and int32 data must be 16-byte aligned and
  *     d_model and d_ffn must be multiples of 8 (rows are read with 16-byte
  *     vector loads).
@@ -60,6 +62,17 @@ typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype;
  * gate rows followed by the up rows ([P2 §3.1] names SwiGLU experts). */
 typedef enum { MOE_ACT_GELU = 0, MOE_ACT_SWIGLU = 1 } moe_act;
 
+/* Storage of the expert weights (W1, W2 of the routed and the shared
+ * experts; router weights and biases always use the activation dtype).
+ * ACT: the activation dtype.  INT8: 8-bit codes q with one float32 scale per
+ * weight row, W[n, :] = scale[n] * q[n, :] ([P3 §6]: compress each expert's
+ * weights to INT8 for deployment; the per-row symmetric scheme is this
+ * library's reading).  INT8 needs BF16 activations and d_model, d_ffn
+ * multiples of 128 (else MOE_ERR_UNSUPPORTED).  The kernels multiply each
+ * code by its scale and round the product to bfloat16 (to nearest even)
+ * before the matrix products; accumulation is float32 as for bf16 weights. */
+typedef enum { MOE_WEIGHTS_ACT = 0, MOE_WEIGHTS_INT8 = 1 } moe_weight_format;
+
 typedef struct {
   int64_t n_tokens;       /* T >= 1: tokens (batch * seq), [P3 §3.1] flattening */
   int32_t d_model;        /* d: hidden size */
@@ -72,7 +85,7 @@ typedef struct {
   double capacity_factor; /* <= 0: no limit; else C = ceil(cf*T*k/E), exact on
                              the binary64 value of cf ([P4 §3.1]); NaN rejected */
   int32_t add_residual;   /* 1: y += x ([P2 §4.1] adds the input inside the layer) */
-  int32_t reserved;       /* must be 0 */
+  int32_t weight_format;  /* moe_weight_format of the expert weights */
 } moe_config;
 
 /* Device pointers to one layer's parameters (host struct, read during the call). */
@@ -87,6 +100,13 @@ typedef struct {
   const void* shared_b1;    /* [S, 2f] / [S, f] or NULL */
   const void* shared_w2;    /* [S, d, f]; required iff S > 0 */
   const void* shared_b2;    /* [S, d] or NULL */
+  /* weight_format INT8: w1 / w2 / shared_w1 / shared_w2 hold int8 codes and
+   * these hold one float32 scale per weight row (required with them);
+   * ignored otherwise */
+  const float* w1_scale;        /* [E, 2f] / [E, f] */
+  const float* w2_scale;        /* [E, d] */
+  const float* shared_w1_scale; /* [S, 2f] / [S, f] */
+  const float* shared_w2_scale; /* [S, d] */
 } moe_weights;
 
 /* Auxiliary statistics, written to device memory.
@@ -165,7 +185,8 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, const flo
  * out outside every group are not written.  ws holds the intermediate
  * activations (rows_max x n_seg*f, act dtype).  Errors: INVALID_ARG for
  * n_groups < 1, n_seg outside [1, 64], rows_max < 0, NULL offsets with
- * n_groups > 1, NULL or misaligned a / w1 / w2 / out; UNSUPPORTED for
+ * n_groups > 1, NULL or misaligned a / w1 / w2 / out, weight_format other
+ * than ACT (INT8 weights go through moe_expert_ffn_int8); UNSUPPORTED for
  * rows_max >= 2^31.  rows_max == 0 launches nothing.
  */
 moe_status moe_expert_ffn(const moe_config* cfg, int32_t n_groups, int32_t n_seg,
@@ -173,6 +194,24 @@ moe_status moe_expert_ffn(const moe_config* cfg, int32_t n_groups, int32_t n_seg
                           const int32_t* group_offsets, const void* w1, const void* b1,
                           const void* w2, const void* b2, void* out, void* ws,
                           size_t* ws_bytes, hipStream_t stream);
+
+/*
+ * moe_expert_ffn_int8 - moe_expert_ffn with 8-bit expert weights ([P3 §6]:
+ * experts compressed to INT8 for deployment).  cfg->weight_format must be
+ * MOE_WEIGHTS_INT8.  w1 [n_groups*n_seg, 2f or f, d] and w2
+ * [n_groups*n_seg, d, f] hold int8 codes; w1_scale [n_groups*n_seg, 2f or f]
+ * and w2_scale [n_groups*n_seg, d] one float32 scale per weight row
+ * (W[n, :] = scale[n] * q[n, :]); everything else as in moe_expert_ffn.
+ * Errors as moe_expert_ffn, plus INVALID_ARG for NULL or misaligned
+ * (4-byte) scales and UNSUPPORTED for shapes INT8 weights do not cover
+ * (see moe_weight_format).
+ */
+moe_status moe_expert_ffn_int8(const moe_config* cfg, int32_t n_groups, int32_t n_seg,
+                               int64_t rows_max, const void* a, const int32_t* a_rows,
+                               const int32_t* group_offsets, const int8_t* w1,
+                               const float* w1_scale, const void* b1, const int8_t* w2,
+                               const float* w2_scale, const void* b2, void* out, void* ws,
+                               size_t* ws_bytes, hipStream_t stream);
 
 /*
  * moe_combine - weighted gather back to token order, atomic-free
@@ -205,7 +244,9 @@ moe_status moe_aux_stats(const moe_config* cfg, const int32_t* expert_counts,
  * FFNs, combine and aux statistics ([P3 §3.1] forward returns the output
  * and the auxiliary loss).  x, y [T,d] act-dtype.  Optional outputs (NULL
  * to skip): topk_idx [T,k], topk_w [T,k], expert_counts [E], aux (device).
- * ws: query with ws == NULL.
+ * Expert weights per cfg->weight_format (INT8: the scale pointers of `w`
+ * for the routed experts, and for the shared ones when S > 0, are
+ * required).  ws: query with ws == NULL.
  */
 moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* x, void* y,
                        int32_t* topk_idx, float* topk_w, int32_t* expert_counts, moe_aux* aux,

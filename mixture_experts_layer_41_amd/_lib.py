@@ -15,10 +15,11 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 MOE_ACT_GELU, MOE_ACT_SWIGLU = 0, 1
+MOE_WEIGHTS_ACT, MOE_WEIGHTS_INT8 = 0, 1
 
 # every symbol include/moe.h declares
-EXPORTS = ("moe_status_string", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
-           "moe_aux_stats", "moe_forward")
+EXPORTS = ("moe_status_string", "moe_route", "moe_permute", "moe_expert_ffn",
+           "moe_expert_ffn_int8", "moe_combine", "moe_aux_stats", "moe_forward")
 
 
 class MoeConfig(ctypes.Structure):
@@ -33,14 +34,15 @@ class MoeConfig(ctypes.Structure):
         ("act", ctypes.c_int32),
         ("capacity_factor", ctypes.c_double),
         ("add_residual", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("weight_format", ctypes.c_int32),
     ]
 
 
 class MoeWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "w_router", "router_bias", "w1", "b1", "w2", "b2",
-        "shared_w1", "shared_b1", "shared_w2", "shared_b2")]
+        "shared_w1", "shared_b1", "shared_w2", "shared_b2",
+        "w1_scale", "w2_scale", "shared_w1_scale", "shared_w2_scale")]
 
 
 class MoeAux(ctypes.Structure):
@@ -80,6 +82,7 @@ def lib():
         "moe_route": [cfgp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_permute": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_expert_ffn": [cfgp, i32, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "moe_expert_ffn_int8": [cfgp, i32, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_combine": [cfgp, vp, vp, vp, vp, vp, vp, vp],
         "moe_aux_stats": [cfgp, vp, vp, vp, ctypes.c_size_t, vp, vp],
         "moe_forward": [cfgp, ctypes.POINTER(MoeWeights), vp, vp, vp, vp, vp, vp, vp, sz, vp],

@@ -3,7 +3,8 @@
 Argument marshalling only: tensors are allocated with torch on the current
 CUDA (HIP) device, their data pointers and torch's current stream are passed
 to the library, and every step of the layer runs in the library's kernels.
-bf16 tensors are torch.bfloat16; float32 ones torch.float32; indices int32.
+bf16 tensors are torch.bfloat16; float32 ones torch.float32; indices int32;
+INT8 weight codes torch.int8 with float32 row scales.
 """
 
 from __future__ import annotations
@@ -20,20 +21,23 @@ _TORCH_DT = {_lib.MOE_DTYPE_F32: torch.float32, _lib.MOE_DTYPE_BF16: torch.bfloa
 
 
 def make_config(T, d, E, k, f, S=0, dtype="bf16", act="swiglu", capacity_factor=0.0,
-                add_residual=False) -> MoeConfig:
+                add_residual=False, weights="act") -> MoeConfig:
     return MoeConfig(
         n_tokens=int(T), d_model=int(d), n_experts=int(E), top_k=int(k), d_ffn=int(f),
         n_shared=int(S),
         dtype=_lib.MOE_DTYPE_BF16 if dtype == "bf16" else _lib.MOE_DTYPE_F32,
         act=_lib.MOE_ACT_SWIGLU if act == "swiglu" else _lib.MOE_ACT_GELU,
-        capacity_factor=float(capacity_factor), add_residual=int(bool(add_residual)), reserved=0)
+        capacity_factor=float(capacity_factor), add_residual=int(bool(add_residual)),
+        weight_format=_lib.MOE_WEIGHTS_INT8 if weights == "int8" else _lib.MOE_WEIGHTS_ACT)
 
 
 def config_of(layer) -> MoeConfig:
     """MoeConfig from any object with T, d, E, k, f, S, dtype, act,
-    capacity_factor and add_residual attributes."""
+    capacity_factor and add_residual attributes (and optionally weights:
+    "act" or "int8")."""
     return make_config(layer.T, layer.d, layer.E, layer.k, layer.f, layer.S, layer.dtype,
-                       layer.act, layer.capacity_factor, layer.add_residual)
+                       layer.act, layer.capacity_factor, layer.add_residual,
+                       getattr(layer, "weights", "act"))
 
 
 def torch_dtype(cfg: MoeConfig) -> torch.dtype:
@@ -125,6 +129,26 @@ def moe_expert_ffn(cfg: MoeConfig, n_groups, n_seg, rows_max, a, a_rows, group_o
     return out
 
 
+def moe_expert_ffn_int8(cfg: MoeConfig, n_groups, n_seg, rows_max, a, a_rows, group_offsets, w1,
+                        w1_scale, b1, w2, w2_scale, b2, out=None):
+    """moe_expert_ffn with INT8 weight codes (torch.int8) and float32 row
+    scales."""
+    L = lib()
+    if out is None:
+        out = torch.zeros(max(int(rows_max), 1), cfg.d_model, dtype=torch_dtype(cfg), device=_dev())
+
+    def call(ws, nb):
+        return L.moe_expert_ffn_int8(ctypes.byref(cfg), int(n_groups), int(n_seg), int(rows_max),
+                                     _p(a), _p(a_rows), _p(group_offsets), _p(w1), _p(w1_scale),
+                                     _p(b1), _p(w2), _p(w2_scale), _p(b2), _p(out), ws, nb,
+                                     _stream())
+    n = ctypes.c_size_t(0)
+    check("moe_expert_ffn_int8", call(None, ctypes.byref(n)))
+    ws = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=_dev())
+    check("moe_expert_ffn_int8", call(_p(ws), ctypes.byref(n)))
+    return out
+
+
 def moe_combine(cfg: MoeConfig, y_perm, inv_row, topk_w, shared_y=None, residual=None, y=None):
     L = lib()
     if y is None:
@@ -166,6 +190,11 @@ class LayerWeights:
     shared_b1: torch.Tensor | None = None
     shared_w2: torch.Tensor | None = None
     shared_b2: torch.Tensor | None = None
+    # INT8 expert weights: float32 row scales of w1 / w2 / shared_w1 / shared_w2
+    w1_scale: torch.Tensor | None = None
+    w2_scale: torch.Tensor | None = None
+    shared_w1_scale: torch.Tensor | None = None
+    shared_w2_scale: torch.Tensor | None = None
 
     def c_struct(self) -> MoeWeights:
         return MoeWeights(**{n: (None if getattr(self, n) is None else getattr(self, n).data_ptr())

@@ -412,8 +412,12 @@ static int forced_tile(GemmKind kind) {
 }
 
 hipError_t launch_gemm(const moe_config& c, GemmKind kind, const GemmDesc& g, hipStream_t s) {
-  const int variant = pick_tile_variant(c, kind, g, forced_tile(kind));
+  int variant = pick_tile_variant(c, kind, g, forced_tile(kind));
+  // INT8 weights run on the register-staged tiles only (a forced shape that
+  // cannot take them falls back to the model's choice)
+  if (variant < 0 && g.w_scale) variant = pick_tile_variant(c, kind, g, -1);
   if (variant >= 0) return launch_gemm_tiled(c, kind, g, variant, s);
+  if (g.w_scale) return hipErrorInvalidValue;  // shapes checked by the API never get here
   const bool bias = g.bias != nullptr;
   if (kind == kGemmDown)
     return bias ? launch_t<kGemmDown, 0, true>(c, g, s) : launch_t<kGemmDown, 0, false>(c, g, s);

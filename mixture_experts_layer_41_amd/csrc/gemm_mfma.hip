@@ -17,7 +17,12 @@
 //     puts them in 16 distinct 16-byte bank groups;
 //   * workgroups are remapped so each XCD (blockIdx % 8) takes a contiguous
 //     run of tiles: the tiles of one expert, which share its weights, then
-//     hit the same L2.
+//     hit the same L2;
+//   * INT8 weights (Q8): the weight tile is loaded as codes (half the bytes),
+//     and each code is multiplied by its row scale and rounded to bf16 on
+//     the way from the staging registers to LDS; the MFMA loop and the
+//     epilogues are the bf16 ones.  The down GEMM's K segments (shared
+//     experts) each bring their own row scales.
 #include <algorithm>
 #include <cmath>
 
@@ -32,7 +37,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte chun
 
 // One output tile: K loop over the group's rows and the tile's weight rows,
 // then the epilogue.  sA / sB are the two LDS stages.
-template <int BM, int BN, int BK, int WM, int WN, int KIND, int ACT, bool BIAS>
+template <int BM, int BN, int BK, int WM, int WN, int KIND, int ACT, bool BIAS, bool Q8>
 __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo& tile, int nt,
                                                u32x4 (*sA)[BM * (BK / 8)],
                                                u32x4 (*sB)[BN * (BK / 8)]) {
@@ -44,10 +49,13 @@ __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo
   constexpr int CPR = BK / 8;                // 16-byte chunks per tile row
   constexpr int RPW = 256 / (BK * 2);        // tile rows per 256-byte bank window
   constexpr int A_LD = BM * CPR / kTileThreads;  // 16-byte loads per thread per K tile
-  constexpr int B_LD = BN * CPR / kTileThreads;
+  constexpr int B_LD = Q8 ? 1 : BN * CPR / kTileThreads;  // (unused with Q8)
+  constexpr int CPR8 = BK / 16;                  // 16-byte chunks of codes per tile row (Q8)
+  constexpr int B8_LD = BN * CPR8 / kTileThreads;  // 16-byte code loads per thread (Q8)
   constexpr int KS = BK / 16;                // MFMA K steps per K tile
   static_assert(BK == 32 || BK == 64, "K tile");
   static_assert(MI >= 1 && NI >= 1 && A_LD >= 1 && B_LD >= 1, "tile shape");
+  static_assert(!Q8 || (B8_LD >= 1 && BN * CPR8 % kTileThreads == 0), "tile shape");
   static_assert(!kSwiglu || (NI % 2 == 0), "SwiGLU pairs gate and up blocks");
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
@@ -55,19 +63,19 @@ __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo
   const int S = p.n_seg, d = p.d, f = p.f;
 
   int seg = 0, n0;
-  const uint16_t* wbase;
+  int64_t wbase;  // element offset of the tile's weight slab
   int K;
+  const int rows1 = (KIND == kGemmUp) ? (kSwiglu ? 2 * f : f) : d;  // weight rows per segment
   if (KIND == kGemmUp) {
     constexpr int bnh = kSwiglu ? BN / 2 : BN;
     const int tpn = f / bnh;
     seg = nt / tpn;
     n0 = (nt % tpn) * bnh;
-    const int rows1 = kSwiglu ? 2 * f : f;
-    wbase = static_cast<const uint16_t*>(p.w) + ((int64_t)tile.group * S + seg) * rows1 * (int64_t)d;
+    wbase = ((int64_t)tile.group * S + seg) * rows1 * (int64_t)d;
     K = d;
   } else {
     n0 = nt * BN;
-    wbase = static_cast<const uint16_t*>(p.w) + (int64_t)tile.group * S * (int64_t)d * f;
+    wbase = (int64_t)tile.group * S * (int64_t)d * f;
     K = f;
   }
   const int nk_seg = K / BK;
@@ -78,6 +86,10 @@ __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo
   const uint16_t* aptr[A_LD];
   const uint16_t* bptr[B_LD];
   int aoff[A_LD], boff[B_LD];  // swizzled LDS slot (uint4 units)
+  const int8_t* bptr8[B8_LD];
+  int boff8[B8_LD][2];   // LDS slots of the two bf16 chunks a code chunk becomes
+  int brow8[B8_LD];      // weight row (within the segment) of each code load
+  float bscale[B8_LD];   // its scale
 #pragma unroll
   for (int i = 0; i < A_LD; ++i) {
     const int c = tid + kTileThreads * i;
@@ -87,20 +99,41 @@ __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo
     aptr[i] = A + src * p.lda + ch * 8;
     aoff[i] = r * CPR + (ch ^ ((r / RPW) % CPR));
   }
+  if constexpr (!Q8) {
 #pragma unroll
-  for (int i = 0; i < B_LD; ++i) {
-    const int c = tid + kTileThreads * i;
-    const int r = c / CPR, ch = c % CPR;
-    int wr;
-    if (kSwiglu)
-      wr = (r < BN / 2) ? n0 + r : f + n0 + (r - BN / 2);
-    else
-      wr = n0 + r;
-    bptr[i] = wbase + (int64_t)wr * (KIND == kGemmUp ? d : f) + ch * 8;
-    boff[i] = r * CPR + (ch ^ ((r / RPW) % CPR));
+    for (int i = 0; i < B_LD; ++i) {
+      const int c = tid + kTileThreads * i;
+      const int r = c / CPR, ch = c % CPR;
+      int wr;
+      if (kSwiglu)
+        wr = (r < BN / 2) ? n0 + r : f + n0 + (r - BN / 2);
+      else
+        wr = n0 + r;
+      bptr[i] = static_cast<const uint16_t*>(p.w) + wbase + (int64_t)wr * K + ch * 8;
+      boff[i] = r * CPR + (ch ^ ((r / RPW) % CPR));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < B8_LD; ++i) {
+      const int c = tid + kTileThreads * i;
+      const int r = c / CPR8, c8 = c % CPR8;  // 16 codes = K [16 c8, 16 c8 + 16)
+      int wr;
+      if (kSwiglu)
+        wr = (r < BN / 2) ? n0 + r : f + n0 + (r - BN / 2);
+      else
+        wr = n0 + r;
+      brow8[i] = wr;
+      bptr8[i] = static_cast<const int8_t*>(p.w) + wbase + (int64_t)wr * K + c8 * 16;
+      boff8[i][0] = r * CPR + ((2 * c8) ^ ((r / RPW) % CPR));
+      boff8[i][1] = r * CPR + ((2 * c8 + 1) ^ ((r / RPW) % CPR));
+      // up: one segment per tile; down: reloaded per K tile below
+      if (KIND == kGemmUp) bscale[i] = p.w_scale[((int64_t)tile.group * S + seg) * rows1 + wr];
+    }
   }
 
   u32x4 ra[A_LD], rb[B_LD];  // staging registers of the next K tile
+  u32x4 rb8[B8_LD];          // (Q8) codes of the next K tile
+  float sc8[B8_LD];          // (Q8, down) their row scales
 #define MOE_TILE_LOAD(kt_)                                                                  \
   do {                                                                                      \
     int64_t ao_, bo_;                                                                       \
@@ -114,13 +147,32 @@ __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo
     }                                                                                       \
     _Pragma("unroll") for (int i_ = 0; i_ < A_LD; ++i_)                                    \
         ra[i_] = *reinterpret_cast<const u32x4*>(aptr[i_] + ao_);                           \
-    _Pragma("unroll") for (int i_ = 0; i_ < B_LD; ++i_)                                    \
-        rb[i_] = *reinterpret_cast<const u32x4*>(bptr[i_] + bo_);                           \
+    if constexpr (!Q8) {                                                                    \
+      _Pragma("unroll") for (int i_ = 0; i_ < B_LD; ++i_)                                  \
+          rb[i_] = *reinterpret_cast<const u32x4*>(bptr[i_] + bo_);                         \
+    } else {                                                                                \
+      _Pragma("unroll") for (int i_ = 0; i_ < B8_LD; ++i_)                                 \
+          rb8[i_] = *reinterpret_cast<const u32x4*>(bptr8[i_] + bo_);                       \
+      if (KIND == kGemmDown) {                                                              \
+        const int s_ = (kt_) / nk_seg;                                                      \
+        _Pragma("unroll") for (int i_ = 0; i_ < B8_LD; ++i_)                               \
+            sc8[i_] = p.w_scale[((int64_t)tile.group * S + s_) * rows1 + brow8[i_]];        \
+      }                                                                                     \
+    }                                                                                       \
   } while (0)
 #define MOE_TILE_STORE(st_)                                                                 \
   do {                                                                                      \
     _Pragma("unroll") for (int i_ = 0; i_ < A_LD; ++i_) sA[st_][aoff[i_]] = ra[i_];         \
-    _Pragma("unroll") for (int i_ = 0; i_ < B_LD; ++i_) sB[st_][boff[i_]] = rb[i_];         \
+    if constexpr (!Q8) {                                                                    \
+      _Pragma("unroll") for (int i_ = 0; i_ < B_LD; ++i_) sB[st_][boff[i_]] = rb[i_];       \
+    } else {                                                                                \
+      _Pragma("unroll") for (int i_ = 0; i_ < B8_LD; ++i_) {                               \
+        u32x4 lo_, hi_;                                                                     \
+        dequant16(rb8[i_], KIND == kGemmDown ? sc8[i_] : bscale[i_], lo_, hi_);             \
+        sB[st_][boff8[i_][0]] = lo_;                                                        \
+        sB[st_][boff8[i_][1]] = hi_;                                                        \
+      }                                                                                     \
+    }                                                                                       \
   } while (0)
 
   f32x16 acc[MI][NI];
@@ -222,7 +274,7 @@ __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo
 // offsets.  Blocks are remapped so that each XCD (blockIdx % 8) takes a
 // contiguous run of tiles: the tiles of one expert share its weights in that
 // XCD's L2.
-template <int BM, int BN, int BK, int WM, int WN, int KIND, int ACT, bool BIAS>
+template <int BM, int BN, int BK, int WM, int WN, int KIND, int ACT, bool BIAS, bool Q8>
 __global__ void __launch_bounds__(64 * WM * WN)
 gemm_tile_kernel(GemmDesc p, int tiles_n) {
   __shared__ __attribute__((aligned(16))) u32x4 sA[2][BM * (BK / 8)];
@@ -250,13 +302,13 @@ gemm_tile_kernel(GemmDesc p, int tiles_n) {
   const TileInfo tile = s_tile;
   const int nt = s_nt;
   if (tile.group < 0) return;
-  gemm_tile_body<BM, BN, BK, WM, WN, KIND, ACT, BIAS>(p, tile, nt, sA, sB);
+  gemm_tile_body<BM, BN, BK, WM, WN, KIND, ACT, BIAS, Q8>(p, tile, nt, sA, sB);
 }
 
 // Persistent variant: the grid holds only the resident workgroups; the
 // row-tile table of the groups is built once per workgroup in LDS, and XCD
 // x = blockIdx % 8 walks a contiguous run of the (exact) tile list.
-template <int BM, int BN, int BK, int WM, int WN, int KIND, int ACT, bool BIAS>
+template <int BM, int BN, int BK, int WM, int WN, int KIND, int ACT, bool BIAS, bool Q8>
 __global__ void __launch_bounds__(64 * WM * WN)
 gemm_tile_persistent(GemmDesc p, int tiles_n) {
   constexpr int kTileThreads = 64 * WM * WN;
@@ -302,7 +354,7 @@ gemm_tile_persistent(GemmDesc p, int tiles_n) {
     tile.group = glo;
     tile.row0 = (int64_t)s_off[glo] + (int64_t)(mt - s_tstart[glo]) * BM;
     tile.rows = min(BM, min(s_off[glo + 1], (int)p.rows_max) - (int)tile.row0);
-    gemm_tile_body<BM, BN, BK, WM, WN, KIND, ACT, BIAS>(p, tile, nt, sA, sB);
+    gemm_tile_body<BM, BN, BK, WM, WN, KIND, ACT, BIAS, Q8>(p, tile, nt, sA, sB);
   }
 }
 
@@ -334,7 +386,7 @@ constexpr TileCfg kTiles[kVariants] = {
 
 int cu_count();
 
-template <int BM, int BN, int BK, int WM, int WN, bool PERSIST, int KIND, int ACT, bool BIAS>
+template <int BM, int BN, int BK, int WM, int WN, bool PERSIST, int KIND, int ACT, bool BIAS, bool Q8>
 hipError_t run(const GemmDesc& g, int occ, hipStream_t s) {
   constexpr int kTileThreads = 64 * WM * WN;
   constexpr bool kSwiglu = (KIND == kGemmUp && ACT == MOE_ACT_SWIGLU);
@@ -351,22 +403,28 @@ hipError_t run(const GemmDesc& g, int occ, hipStream_t s) {
   grid = (grid + 7) / 8 * 8;  // a multiple of 8 (XCDs)
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   if constexpr (PERSIST)
-    gemm_tile_persistent<BM, BN, BK, WM, WN, KIND, ACT, BIAS>
+    gemm_tile_persistent<BM, BN, BK, WM, WN, KIND, ACT, BIAS, Q8>
         <<<dim3((unsigned)grid), dim3(kTileThreads), 0, s>>>(g, tiles_n);
   else
-    gemm_tile_kernel<BM, BN, BK, WM, WN, KIND, ACT, BIAS>
+    gemm_tile_kernel<BM, BN, BK, WM, WN, KIND, ACT, BIAS, Q8>
         <<<dim3((unsigned)grid), dim3(kTileThreads), 0, s>>>(g, tiles_n);
   return hipGetLastError();
 }
 
-template <int KIND, int ACT, bool BIAS>
+template <int KIND, int ACT, bool BIAS, bool Q8>
 hipError_t dispatch(const GemmDesc& g, int variant, hipStream_t s) {
   switch (variant) {
-    case 0: return run<256, 256, 64, 2, 4, false, KIND, ACT, BIAS>(g, kTiles[0].occ, s);
-    case 1: return run<256, 128, 64, 4, 2, true, KIND, ACT, BIAS>(g, kTiles[1].occ, s);
-    case 2: return run<128, 128, 64, 2, 2, true, KIND, ACT, BIAS>(g, kTiles[2].occ, s);
-    default: return run<32, 256, 64, 1, 4, true, KIND, ACT, BIAS>(g, kTiles[3].occ, s);
+    case 0: return run<256, 256, 64, 2, 4, false, KIND, ACT, BIAS, Q8>(g, kTiles[0].occ, s);
+    case 1: return run<256, 128, 64, 4, 2, true, KIND, ACT, BIAS, Q8>(g, kTiles[1].occ, s);
+    case 2: return run<128, 128, 64, 2, 2, true, KIND, ACT, BIAS, Q8>(g, kTiles[2].occ, s);
+    default: return run<32, 256, 64, 1, 4, true, KIND, ACT, BIAS, Q8>(g, kTiles[3].occ, s);
   }
+}
+
+template <int KIND, int ACT, bool BIAS>
+hipError_t dispatch_w(const GemmDesc& g, int variant, hipStream_t s) {
+  return g.w_scale ? dispatch<KIND, ACT, BIAS, true>(g, variant, s)
+                   : dispatch<KIND, ACT, BIAS, false>(g, variant, s);
 }
 
 int cu_count() {
@@ -412,6 +470,7 @@ int pick_tile_variant(const moe_config& c, GemmKind kind, const GemmDesc& g, int
   const int cus = cu_count();
   auto fits = [&](int v) {
     const TileCfg& tc = kTiles[v];
+    if (g.w_scale && v >= kFirstPipe) return false;  // INT8 weights: register-staged tiles only
     if (K % tc.bk != 0) return false;
     const int ncol = kind == kGemmUp ? (swiglu ? tc.bn / 2 : tc.bn) : tc.bn;
     const int nwidth = kind == kGemmUp ? g.f : g.d;
@@ -448,13 +507,13 @@ hipError_t launch_gemm_tiled(const moe_config& c, GemmKind kind, const GemmDesc&
     return launch_gemm_pipe(kind, g, variant - kFirstPipe, kTiles[variant].occ, s);
   const bool bias = g.bias != nullptr;
   if (kind == kGemmDown)
-    return bias ? dispatch<kGemmDown, 0, true>(g, variant, s)
-                : dispatch<kGemmDown, 0, false>(g, variant, s);
+    return bias ? dispatch_w<kGemmDown, 0, true>(g, variant, s)
+                : dispatch_w<kGemmDown, 0, false>(g, variant, s);
   if (g.act == MOE_ACT_SWIGLU)
-    return bias ? dispatch<kGemmUp, MOE_ACT_SWIGLU, true>(g, variant, s)
-                : dispatch<kGemmUp, MOE_ACT_SWIGLU, false>(g, variant, s);
-  return bias ? dispatch<kGemmUp, MOE_ACT_GELU, true>(g, variant, s)
-              : dispatch<kGemmUp, MOE_ACT_GELU, false>(g, variant, s);
+    return bias ? dispatch_w<kGemmUp, MOE_ACT_SWIGLU, true>(g, variant, s)
+                : dispatch_w<kGemmUp, MOE_ACT_SWIGLU, false>(g, variant, s);
+  return bias ? dispatch_w<kGemmUp, MOE_ACT_GELU, true>(g, variant, s)
+              : dispatch_w<kGemmUp, MOE_ACT_GELU, false>(g, variant, s);
 }
 
 }  // namespace moe

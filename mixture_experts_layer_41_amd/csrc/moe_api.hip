@@ -1,5 +1,5 @@
 // C ABI of the MoE layer library: argument validation, exact capacity,
-// workspace planning and the launch sequences of the six entry points.
+// workspace planning and the launch sequences of the entry points.
 // Nothing here allocates device memory or synchronises; every launch goes to
 // the caller's stream.
 #include <cmath>
@@ -35,11 +35,14 @@ int64_t route_blocks(const moe_config& c) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 moe_status check_config(const moe_config* c) {
   if (c == nullptr) return MOE_ERR_INVALID_ARG;
   if (c->n_tokens < 1 || c->d_model < 8 || c->d_ffn < 8 || c->n_experts < 1 || c->top_k < 1 ||
-      c->top_k > c->n_experts || c->n_shared < 0 || c->reserved != 0)
+      c->top_k > c->n_experts || c->n_shared < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (c->weight_format != MOE_WEIGHTS_ACT && c->weight_format != MOE_WEIGHTS_INT8)
     return MOE_ERR_INVALID_ARG;
   if (c->dtype != MOE_DTYPE_F32 && c->dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
   if (c->act != MOE_ACT_GELU && c->act != MOE_ACT_SWIGLU) return MOE_ERR_INVALID_ARG;
@@ -49,6 +52,11 @@ moe_status check_config(const moe_config* c) {
     return MOE_ERR_INVALID_ARG;
   if (c->d_model % 8 != 0 || c->d_ffn % 8 != 0) return MOE_ERR_UNSUPPORTED;
   if (c->n_experts > kMaxExperts || c->n_shared > 64) return MOE_ERR_UNSUPPORTED;
+  // INT8 expert weights: bf16 activations; shapes the dequantizing tiled
+  // GEMM covers for every activation (K tile 64, output tiles of 128)
+  if (c->weight_format == MOE_WEIGHTS_INT8 &&
+      (c->dtype != MOE_DTYPE_BF16 || c->d_model % 128 != 0 || c->d_ffn % 128 != 0))
+    return MOE_ERR_UNSUPPORTED;
   // row indices are int32
   if (c->n_tokens * (int64_t)c->top_k >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)c->d_ffn * (c->n_shared > 1 ? c->n_shared : 1) >= (int64_t)1 << 30)
@@ -181,13 +189,18 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, const flo
   return MOE_OK;
 }
 
-moe_status moe_expert_ffn(const moe_config* cfg, int32_t n_groups, int32_t n_seg,
-                          int64_t rows_max, const void* a, const int32_t* a_rows,
-                          const int32_t* group_offsets, const void* w1, const void* b1,
-                          const void* w2, const void* b2, void* out, void* ws,
-                          size_t* ws_bytes, hipStream_t stream) {
-  moe_status st = check_config(cfg);
-  if (st != MOE_OK) return st;
+}  // extern "C"
+
+namespace {
+
+// moe_expert_ffn and moe_expert_ffn_int8 (w1_scale / w2_scale non-null with
+// INT8 codes in w1 / w2).
+moe_status expert_ffn(const moe_config* cfg, int32_t n_groups, int32_t n_seg, int64_t rows_max,
+                      const void* a, const int32_t* a_rows, const int32_t* group_offsets,
+                      const void* w1, const float* w1_scale, const void* b1, const void* w2,
+                      const float* w2_scale, const void* b2, void* out, void* ws,
+                      size_t* ws_bytes, hipStream_t stream) {
+  const bool q8 = cfg->weight_format == MOE_WEIGHTS_INT8;
   if (n_groups < 1 || n_seg < 1 || n_seg > 64 || rows_max < 0) return MOE_ERR_INVALID_ARG;
   if (group_offsets == nullptr && n_groups != 1) return MOE_ERR_INVALID_ARG;
   if (rows_max >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
@@ -199,8 +212,10 @@ moe_status moe_expert_ffn(const moe_config* cfg, int32_t n_groups, int32_t n_seg
     if (!a || !w1 || !w2 || !out) return MOE_ERR_INVALID_ARG;
     if (!aligned16(a) || !aligned16(w1) || !aligned16(w2) || !aligned16(out))
       return MOE_ERR_INVALID_ARG;
+    if (q8 && (!w1_scale || !w2_scale || !aligned4(w1_scale) || !aligned4(w2_scale)))
+      return MOE_ERR_INVALID_ARG;
   }
-  st = ws_check(ws, ws_bytes, need);
+  moe_status st = ws_check(ws, ws_bytes, need);
   if (st != MOE_OK || ws == nullptr) return st;
   if (rows_max == 0) return MOE_OK;
   Carver c2(ws);
@@ -215,6 +230,7 @@ moe_status moe_expert_ffn(const moe_config* cfg, int32_t n_groups, int32_t n_seg
   up.n_seg = n_seg;
   up.rows_max = rows_max;
   up.w = w1;
+  up.w_scale = q8 ? w1_scale : nullptr;
   up.bias = b1;
   up.d = cfg->d_model;
   up.f = cfg->d_ffn;
@@ -227,11 +243,41 @@ moe_status moe_expert_ffn(const moe_config* cfg, int32_t n_groups, int32_t n_seg
   dn.a_rows = nullptr;
   dn.lda = hw;
   dn.w = w2;
+  dn.w_scale = q8 ? w2_scale : nullptr;
   dn.bias = b2;
   dn.out = out;
   dn.ldo = cfg->d_model;
   MOE_HIP_TRY(launch_gemm(*cfg, kGemmDown, dn, stream));
   return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_expert_ffn(const moe_config* cfg, int32_t n_groups, int32_t n_seg,
+                          int64_t rows_max, const void* a, const int32_t* a_rows,
+                          const int32_t* group_offsets, const void* w1, const void* b1,
+                          const void* w2, const void* b2, void* out, void* ws,
+                          size_t* ws_bytes, hipStream_t stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->weight_format != MOE_WEIGHTS_ACT) return MOE_ERR_INVALID_ARG;
+  return expert_ffn(cfg, n_groups, n_seg, rows_max, a, a_rows, group_offsets, w1, nullptr, b1, w2,
+                    nullptr, b2, out, ws, ws_bytes, stream);
+}
+
+moe_status moe_expert_ffn_int8(const moe_config* cfg, int32_t n_groups, int32_t n_seg,
+                               int64_t rows_max, const void* a, const int32_t* a_rows,
+                               const int32_t* group_offsets, const int8_t* w1,
+                               const float* w1_scale, const void* b1, const int8_t* w2,
+                               const float* w2_scale, const void* b2, void* out, void* ws,
+                               size_t* ws_bytes, hipStream_t stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->weight_format != MOE_WEIGHTS_INT8) return MOE_ERR_INVALID_ARG;
+  return expert_ffn(cfg, n_groups, n_seg, rows_max, a, a_rows, group_offsets, w1, w1_scale, b1,
+                    w2, w2_scale, b2, out, ws, ws_bytes, stream);
 }
 
 moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* inv_row,
@@ -308,6 +354,13 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
     if (!aligned16(x) || !aligned16(y) || !aligned16(w->w_router) || !aligned16(w->w1) ||
         !aligned16(w->w2) || (S > 0 && (!aligned16(w->shared_w1) || !aligned16(w->shared_w2))))
       return MOE_ERR_INVALID_ARG;
+    if (c.weight_format == MOE_WEIGHTS_INT8) {
+      if (!w->w1_scale || !w->w2_scale || !aligned4(w->w1_scale) || !aligned4(w->w2_scale))
+        return MOE_ERR_INVALID_ARG;
+      if (S > 0 && (!w->shared_w1_scale || !w->shared_w2_scale || !aligned4(w->shared_w1_scale) ||
+                    !aligned4(w->shared_w2_scale)))
+        return MOE_ERR_INVALID_ARG;
+    }
   }
   st = ws_check(ws, ws_bytes, need);
   if (st != MOE_OK || ws == nullptr) return st;
@@ -316,6 +369,7 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
   if (topk_w) p.wts = topk_w;
   if (expert_counts) p.po.counts = expert_counts;
   const int64_t cap = exact_capacity(c);
+  const bool q8 = c.weight_format == MOE_WEIGHTS_INT8;
 
   MOE_HIP_TRY(launch_router(c, x, w->w_router, w->router_bias, p.idx, p.wts, nullptr, p.rs, stream));
   MOE_HIP_TRY(launch_permute(c, p.rs, p.po, cap, p.idx, nullptr, nullptr, nullptr, aux, p.scratch,
@@ -330,6 +384,7 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
   up.n_seg = 1;
   up.rows_max = R;
   up.w = w->w1;
+  up.w_scale = q8 ? w->w1_scale : nullptr;
   up.bias = w->b1;
   up.d = d;
   up.f = f;
@@ -342,6 +397,7 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
   dn.a_rows = nullptr;
   dn.lda = f;
   dn.w = w->w2;
+  dn.w_scale = q8 ? w->w2_scale : nullptr;
   dn.bias = w->b2;
   dn.out = p.y_perm;
   dn.ldo = d;
@@ -357,6 +413,7 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
     su.n_seg = S;
     su.rows_max = T;
     su.w = w->shared_w1;
+    su.w_scale = q8 ? w->shared_w1_scale : nullptr;
     su.bias = w->shared_b1;
     su.d = d;
     su.f = f;
@@ -368,6 +425,7 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
     sd.a = p.Hs;
     sd.lda = (int64_t)S * f;
     sd.w = w->shared_w2;
+    sd.w_scale = q8 ? w->shared_w2_scale : nullptr;
     sd.bias = w->shared_b2;
     sd.out = p.shared_y;
     sd.ldo = d;

@@ -81,6 +81,7 @@ struct GemmDesc {
   // up GEMM (N-segmented): out[r, s*f + n] = act(A[r] . W1[g*S+s] rows), K = d
   // down GEMM (K-segmented): out[r, n] = sum_s H[r, s*f:(s+1)*f] . W2[g*S+s][n], K = S*f
   const void* w;
+  const float* w_scale;      // non-null: w holds int8 codes, one scale per weight row
   const void* bias;
   int d;                     // d_model
   int f;                     // d_ffn

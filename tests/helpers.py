@@ -24,12 +24,15 @@ def normwise(a, ref) -> float:
 
 
 def to_dev(arr, dtype: str):
-    """numpy (uint16 bf16 bits or float32) -> cuda tensor."""
+    """numpy (uint16 bf16 bits, int8 weight codes or float32) -> cuda tensor."""
     if arr is None:
         return None
-    if dtype == "bf16":
-        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).cuda().view(torch.bfloat16)
-    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).cuda()
+    a = np.ascontiguousarray(arr)
+    if a.dtype == np.int8:
+        return torch.from_numpy(a).cuda()
+    if dtype == "bf16" and a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
 
 
 def bank_to_dev(bank, dtype: str, threads: int = 16, keep=None):
@@ -40,7 +43,7 @@ def bank_to_dev(bank, dtype: str, threads: int = 16, keep=None):
         return None
     if isinstance(bank, np.ndarray):
         return to_dev(bank, dtype)
-    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    tdt = {np.uint16: torch.bfloat16, np.int8: torch.int8}.get(bank.np_dtype, torch.float32)
     out = torch.empty(bank.full_shape, dtype=tdt, device="cuda")
     from concurrent.futures import ThreadPoolExecutor
 
@@ -77,8 +80,9 @@ def weights_to_dev(cfg, t, keep_experts=None) -> B.LayerWeights:
     rb = t.get("router_bias")
     kept = {}
     banks = {}
-    for key in ("w1", "w2", "b1", "b2", "ws1", "ws2", "sb1", "sb2"):
-        ids = keep_experts if key in ("w1", "w2", "b1", "b2") else set(range(cfg.S))
+    routed_keys = ("w1", "w2", "b1", "b2", "w1_scale", "w2_scale")
+    for key in routed_keys + ("ws1", "ws2", "sb1", "sb2", "ws1_scale", "ws2_scale"):
+        ids = keep_experts if key in routed_keys else set(range(cfg.S))
         kept[key] = {"ids": ids or set()}
         banks[key] = bank_to_dev(t.get(key), dt, keep=kept[key])
     if keep_experts is not None:
@@ -90,6 +94,8 @@ def weights_to_dev(cfg, t, keep_experts=None) -> B.LayerWeights:
         router_bias=None if rb is None else torch.from_numpy(np.asarray(rb, np.float32)).cuda(),
         w1=banks["w1"], w2=banks["w2"], b1=banks["b1"], b2=banks["b2"],
         shared_w1=banks["ws1"], shared_w2=banks["ws2"], shared_b1=banks["sb1"], shared_b2=banks["sb2"],
+        w1_scale=banks["w1_scale"], w2_scale=banks["w2_scale"],
+        shared_w1_scale=banks["ws1_scale"], shared_w2_scale=banks["ws2_scale"],
     )
 
 

@@ -33,7 +33,7 @@ def cfg(**kw):
     c = _lib.MoeConfig()
     base = dict(n_tokens=256, d_model=64, n_experts=8, top_k=2, d_ffn=128, n_shared=0,
                 dtype=_lib.MOE_DTYPE_BF16, act=_lib.MOE_ACT_SWIGLU, capacity_factor=1.25,
-                add_residual=0, reserved=0)
+                add_residual=0, weight_format=0)
     base.update(kw)
     for k, v in base.items():
         setattr(c, k, v)
@@ -101,7 +101,7 @@ def test_forward_workspace_covers_its_buffers(L):
 @pytest.mark.parametrize("bad", [
     dict(n_tokens=0), dict(n_tokens=-5), dict(top_k=0), dict(top_k=9), dict(n_experts=0),
     dict(n_shared=-1), dict(dtype=7), dict(act=4), dict(capacity_factor=math.nan),
-    dict(capacity_factor=math.inf), dict(capacity_factor=2.0 ** 31), dict(reserved=1),
+    dict(capacity_factor=math.inf), dict(capacity_factor=2.0 ** 31), dict(weight_format=2),
     dict(add_residual=2), dict(d_model=4),
 ])
 def test_invalid_config(L, bad):
@@ -112,7 +112,11 @@ def test_invalid_config(L, bad):
 
 
 @pytest.mark.parametrize("bad", [dict(d_model=68), dict(d_ffn=100), dict(n_experts=513, top_k=2),
-                                 dict(n_shared=65), dict(n_tokens=1 << 30, top_k=2)])
+                                 dict(n_shared=65), dict(n_tokens=1 << 30, top_k=2),
+                                 # INT8 expert weights: bf16 activations, d and f multiples of 128
+                                 dict(weight_format=1, dtype=_lib.MOE_DTYPE_F32),
+                                 dict(weight_format=1, d_model=64, d_ffn=128),
+                                 dict(weight_format=1, d_model=128, d_ffn=192)])
 def test_unsupported_config(L, bad):
     for fn in ("route", "permute", "forward"):
         assert query(L, fn, cfg(**bad))[0] == UNSUPPORTED, (fn, bad)
@@ -175,3 +179,54 @@ def test_aux_stats_argument_checks(L):
     assert L.moe_aux_stats(ctypes.byref(c), P, P, P, 0, ctypes.byref(aux), None) == WORKSPACE
     assert L.moe_aux_stats(ctypes.byref(c), None, P, P, 1 << 20, ctypes.byref(aux), None) == INVALID
     assert L.moe_aux_stats(ctypes.byref(c), P, P, P, 1 << 20, None, None) == INVALID
+
+
+def q8cfg(**kw):
+    base = dict(d_model=128, d_ffn=256, weight_format=_lib.MOE_WEIGHTS_INT8)
+    base.update(kw)
+    return cfg(**base)
+
+
+def test_int8_entry_points_and_format_checks(L):
+    n = ctypes.c_size_t(0)
+    null6 = [None] * 6
+    c8 = q8cfg()
+    # the INT8 call takes only INT8 configs; the plain one only ACT ones
+    assert L.moe_expert_ffn(ctypes.byref(c8), 1, 1, 16, None, None, None, *null6,
+                            ctypes.byref(n), None) == INVALID
+    c = cfg(d_model=128, d_ffn=256)
+    assert L.moe_expert_ffn_int8(ctypes.byref(c), 1, 1, 16, None, None, None, *null6, None, None,
+                                 ctypes.byref(n), None) == INVALID
+    # query mode works without pointers
+    assert L.moe_expert_ffn_int8(ctypes.byref(c8), 1, 1, 16, None, None, None, *null6, None, None,
+                                 ctypes.byref(n), None) == OK
+    need = n.value
+    assert need >= 16 * 256 * 2
+    # with a workspace: weights, scales and buffers are required and aligned
+    # with a workspace, missing or misaligned scales are rejected before any
+    # launch (a call with every argument valid would launch: not done here)
+    m = ctypes.c_size_t(need)
+    args = [P, None, None, P, P, None, P, P, None, P]  # a, a_rows, offs, w1, s1, b1, w2, s2, b2, out
+    bad = list(args)
+    bad[4] = None  # w1_scale
+    assert L.moe_expert_ffn_int8(ctypes.byref(c8), 1, 1, 16, *bad, P, ctypes.byref(m), None) == INVALID
+    bad = list(args)
+    bad[7] = P + 2  # w2_scale not 4-byte aligned
+    assert L.moe_expert_ffn_int8(ctypes.byref(c8), 1, 1, 16, *bad, P, ctypes.byref(m), None) == INVALID
+
+
+def test_int8_forward_needs_scales(L):
+    c8 = q8cfg(n_shared=1)
+    n = ctypes.c_size_t(0)
+    w = _lib.MoeWeights(w_router=P, w1=P, w2=P, shared_w1=P, shared_w2=P, w1_scale=P, w2_scale=P,
+                        shared_w1_scale=P, shared_w2_scale=P)
+    st = L.moe_forward(ctypes.byref(c8), ctypes.byref(w), None, None, None, None, None, None, None,
+                       ctypes.byref(n), None)
+    assert st == OK and n.value > 0
+    m = ctypes.c_size_t(n.value)
+    for missing in ("w1_scale", "w2_scale", "shared_w1_scale", "shared_w2_scale"):
+        w2 = _lib.MoeWeights(w_router=P, w1=P, w2=P, shared_w1=P, shared_w2=P, w1_scale=P,
+                             w2_scale=P, shared_w1_scale=P, shared_w2_scale=P)
+        setattr(w2, missing, None)
+        assert L.moe_forward(ctypes.byref(c8), ctypes.byref(w2), P, P, None, None, None, None, P,
+                             ctypes.byref(m), None) == INVALID, missing

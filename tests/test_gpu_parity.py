@@ -189,7 +189,8 @@ def test_small_shapes_all_steps(row):
 # the named workloads at full size: routing, permutation and aux in full;
 # the output on all tokens (small layers) or on sampled tokens (large ones)
 
-FULL = {"c1": None, "c2": None, "c3": 512, "c4": 96, "c4cap": 96, "c5": 6}
+FULL = {"c1": None, "c2": None, "c3": 512, "c4": 96, "c4cap": 96, "c5": 6, "c5q": 6}
+LAZY = ("c5", "c5q")  # expert weights generated one expert at a time
 
 
 @pytest.mark.parametrize("name", list(FULL))
@@ -197,14 +198,14 @@ def test_named_workload_full_size(name):
     cfg = get_config(name)
     n_rows = FULL[name]
     say(f"[case] {name}: {cfg.name}")
-    t = inputs(cfg, materialize=(name != "c5"))
+    t = inputs(cfg, materialize=(name not in LAZY))
     rows = None
     if n_rows is not None:
         rng = np.random.default_rng(7)
         rows = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, n_rows, replace=False)]))
     c = B.config_of(cfg)
     say(f"[upload] {name}")
-    keep = routed_experts(cfg, t, rows) if name == "c5" else None
+    keep = routed_experts(cfg, t, rows) if name in LAZY else None
     W = weights_to_dev(cfg, t, keep_experts=keep)
     say(f"[oracle] {name}")
     o = run_oracle(cfg, t, rows=rows)
@@ -226,3 +227,60 @@ def test_named_workload_full_size(name):
     check_permutation(o, pr, cfg.T, cfg.k, F.topk_idx)
     say(f"[ok] {name} y_err={err:.2e} lb={aux['load_balance']:.6f} z={aux['z_loss']:.6f} "
         f"dropped={aux['n_dropped']}")
+
+
+# ---------------------------------------------------------------------------
+# 8-bit expert weights: INT8 codes with float32 row scales (bf16 activations)
+
+SMALL_Q8 = [
+    # name, T, d, E, k, f, S, act, cf, expert_bias, router_bias, residual
+    ("q8_swiglu", 200, 128, 8, 2, 128, 0, "swiglu", 0.0, "none", "none", False),
+    ("q8_gelu_bias_shared2", 150, 256, 6, 3, 128, 2, "gelu", 0.0, "random", "none", True),
+    ("q8_cap_drop_shared", 300, 128, 16, 2, 256, 1, "swiglu", 1.0, "none", "zipf", False),
+    ("q8_k10", 64, 128, 12, 10, 128, 0, "swiglu", 0.0, "none", "none", False),
+]
+
+
+@pytest.mark.parametrize("row", SMALL_Q8, ids=[r[0] for r in SMALL_Q8])
+def test_int8_weights_small(row):
+    (name, T, d, E, k, f, S, act, cf, eb, rb, res) = row
+    cfg = LayerConfig(name, T=T, d=d, E=E, k=k, f=f, S=S, dtype="bf16", act=act,
+                      capacity_factor=cf, router_bias=rb, expert_bias=eb, add_residual=res,
+                      weights="int8", seed=700 + SMALL_Q8.index(row))
+    say(f"[case] {name} T={T} d={d} E={E} k={k} f={f} S={S} int8 weights")
+    t = inputs(cfg)
+    o = run_oracle(cfg, t, want_routed_rows=True)
+    c = B.config_of(cfg)
+    W = weights_to_dev(cfg, t)
+    x = to_dev(t["x"], cfg.dtype)
+
+    # the expert FFN entry point with INT8 weights, routed and shared
+    idx, w, _, _ = B.moe_route(c, x, W.w_router, W.router_bias)
+    pr = B.moe_permute(c, idx, w, x)
+    torch.cuda.synchronize()
+    check_permutation(o, pr, T, k, idx)
+    R = int(o["offsets"][-1])
+    y_perm = B.moe_expert_ffn_int8(c, E, 1, T * k, x, pr["perm_token"], pr["expert_offsets"],
+                                   W.w1, W.w1_scale, W.b1, W.w2, W.w2_scale, W.b2)
+    torch.cuda.synchronize()
+    if R:
+        err = normwise(from_dev(y_perm[:R]), o["routed_rows"])
+        assert err <= tol_for(cfg), f"expert rows normwise err {err:.3e}"
+    if S:
+        sy = B.moe_expert_ffn_int8(c, 1, S, T, x, None, None, W.shared_w1, W.shared_w1_scale,
+                                   W.shared_b1, W.shared_w2, W.shared_w2_scale, W.shared_b2)
+        torch.cuda.synchronize()
+        err = normwise(from_dev(sy), o["shared_y"])
+        assert err <= tol_for(cfg), f"shared normwise err {err:.3e}"
+
+    # the whole layer, twice (deterministic)
+    F = B.Forward(c, W)
+    y1 = F(x).clone()
+    y2 = F(x).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    err = normwise(from_dev(y1), o["y"])
+    assert err <= tol_for(cfg), f"forward normwise err {err:.3e}"
+    check_routing(cfg, o, F.topk_idx, F.topk_w)
+    check_aux(B.aux_to_dict(F.aux), o)
+    say(f"[ok] {name} y_err={err:.2e}")
