@@ -36,8 +36,10 @@ namespace tiled {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte chunk
 
 // One output tile: K loop over the group's rows and the tile's weight rows,
-// then the epilogue.  sA / sB are the two LDS stages.
-template <int BM, int BN, int BK, int WM, int WN, int KIND, int ACT, bool BIAS, bool Q8>
+// then the epilogue.  sA / sB are the two LDS stages.  PD = K tiles whose
+// global loads are in flight at once (1, or 2 with two register sets; PD = 2
+// needs an even number of K tiles).
+template <int BM, int BN, int BK, int WM, int WN, int KIND, int ACT, bool BIAS, bool Q8, int PD>
 __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo& tile, int nt,
                                                u32x4 (*sA)[BM * (BK / 8)],
                                                u32x4 (*sB)[BN * (BK / 8)]) {
@@ -57,6 +59,7 @@ __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo
   static_assert(MI >= 1 && NI >= 1 && A_LD >= 1 && B_LD >= 1, "tile shape");
   static_assert(!Q8 || (B8_LD >= 1 && BN * CPR8 % kTileThreads == 0), "tile shape");
   static_assert(!kSwiglu || (NI % 2 == 0), "SwiGLU pairs gate and up blocks");
+  static_assert(PD == 1 || PD == 2, "prefetch depth");
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
   const int wm = wave / WN, wn = wave % WN;
@@ -131,10 +134,11 @@ __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo
     }
   }
 
-  u32x4 ra[A_LD], rb[B_LD];  // staging registers of the next K tile
-  u32x4 rb8[B8_LD];          // (Q8) codes of the next K tile
-  float sc8[B8_LD];          // (Q8, down) their row scales
-#define MOE_TILE_LOAD(kt_)                                                                  \
+  u32x4 ra[PD][A_LD], rb[PD][B_LD];  // staging registers of the next K tile(s)
+  u32x4 rb8[PD][B8_LD];              // (Q8) codes of the next K tile(s)
+  float sc8[PD][B8_LD];              // (Q8, down) their row scales
+  // load K tile kt_ into register set r_ (a compile-time constant)
+#define MOE_TILE_LOAD(kt_, r_)                                                              \
   do {                                                                                      \
     int64_t ao_, bo_;                                                                       \
     if (KIND == kGemmUp) {                                                                  \
@@ -146,29 +150,32 @@ __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo
       bo_ = (int64_t)s_ * d * f + kk_;                                                      \
     }                                                                                       \
     _Pragma("unroll") for (int i_ = 0; i_ < A_LD; ++i_)                                    \
-        ra[i_] = *reinterpret_cast<const u32x4*>(aptr[i_] + ao_);                           \
+        ra[r_][i_] = *reinterpret_cast<const u32x4*>(aptr[i_] + ao_);                       \
     if constexpr (!Q8) {                                                                    \
       _Pragma("unroll") for (int i_ = 0; i_ < B_LD; ++i_)                                  \
-          rb[i_] = *reinterpret_cast<const u32x4*>(bptr[i_] + bo_);                         \
+          rb[r_][i_] = *reinterpret_cast<const u32x4*>(bptr[i_] + bo_);                     \
     } else {                                                                                \
       _Pragma("unroll") for (int i_ = 0; i_ < B8_LD; ++i_)                                 \
-          rb8[i_] = *reinterpret_cast<const u32x4*>(bptr8[i_] + bo_);                       \
+          rb8[r_][i_] = *reinterpret_cast<const u32x4*>(bptr8[i_] + bo_);                   \
       if (KIND == kGemmDown) {                                                              \
         const int s_ = (kt_) / nk_seg;                                                      \
         _Pragma("unroll") for (int i_ = 0; i_ < B8_LD; ++i_)                               \
-            sc8[i_] = p.w_scale[((int64_t)tile.group * S + s_) * rows1 + brow8[i_]];        \
+            sc8[r_][i_] = p.w_scale[((int64_t)tile.group * S + s_) * rows1 + brow8[i_]];    \
       }                                                                                     \
     }                                                                                       \
   } while (0)
-#define MOE_TILE_STORE(st_)                                                                 \
+  // store register set r_ into LDS stage st_
+#define MOE_TILE_STORE(st_, r_)                                                             \
   do {                                                                                      \
-    _Pragma("unroll") for (int i_ = 0; i_ < A_LD; ++i_) sA[st_][aoff[i_]] = ra[i_];         \
+    _Pragma("unroll") for (int i_ = 0; i_ < A_LD; ++i_) sA[st_][aoff[i_]] = ra[r_][i_];     \
     if constexpr (!Q8) {                                                                    \
-      _Pragma("unroll") for (int i_ = 0; i_ < B_LD; ++i_) sB[st_][boff[i_]] = rb[i_];       \
+      _Pragma("unroll") for (int i_ = 0; i_ < B_LD; ++i_) sB[st_][boff[i_]] = rb[r_][i_];   \
     } else {                                                                                \
       _Pragma("unroll") for (int i_ = 0; i_ < B8_LD; ++i_) {                               \
+        /* codes stay packed until here: no unpacking next to the load */                   \
+        if constexpr (PD == 2) asm volatile("" : "+v"(rb8[r_][i_]));                       \
         u32x4 lo_, hi_;                                                                     \
-        dequant16(rb8[i_], KIND == kGemmDown ? sc8[i_] : bscale[i_], lo_, hi_);             \
+        dequant16(rb8[r_][i_], KIND == kGemmDown ? sc8[r_][i_] : bscale[i_], lo_, hi_);     \
         sB[st_][boff8[i_][0]] = lo_;                                                        \
         sB[st_][boff8[i_][1]] = hi_;                                                        \
       }                                                                                     \
@@ -200,33 +207,66 @@ __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo
   }
   const int sw = (fr / RPW) % CPR;
 
-  MOE_TILE_LOAD(0);
-  MOE_TILE_STORE(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < nk) MOE_TILE_LOAD(kt + 1);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      // lanes of half h take the K elements [h*BK/2, (h+1)*BK/2) of the tile,
-      // one chunk per K step; A and B use the same order
-      const int c = (half * KS + ks) ^ sw;
-      bf16x8 fa[MI], fb[NI];
-#pragma unroll
-      for (int i = 0; i < MI; ++i) fa[i] = __builtin_bit_cast(bf16x8, sA[st][arow[i] + c]);
-#pragma unroll
-      for (int j = 0; j < NI; ++j) fb[j] = __builtin_bit_cast(bf16x8, sB[st][brow[j] + c]);
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NI; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) MOE_TILE_STORE(st ^ 1);
+  // MFMAs over the K tile in LDS stage st_
+#define MOE_TILE_COMPUTE(st_)                                                               \
+  do {                                                                                      \
+    _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) {                                    \
+      /* lanes of half h take the K elements [h*BK/2, (h+1)*BK/2) of the tile, */           \
+      /* one chunk per K step; A and B use the same order */                                \
+      const int c = (half * KS + ks) ^ sw;                                                  \
+      bf16x8 fa[MI], fb[NI];                                                                \
+      _Pragma("unroll") for (int i = 0; i < MI; ++i)                                       \
+          fa[i] = __builtin_bit_cast(bf16x8, sA[st_][arow[i] + c]);                         \
+      _Pragma("unroll") for (int j = 0; j < NI; ++j)                                       \
+          fb[j] = __builtin_bit_cast(bf16x8, sB[st_][brow[j] + c]);                         \
+      _Pragma("unroll") for (int i = 0; i < MI; ++i)                                       \
+          _Pragma("unroll") for (int j = 0; j < NI; ++j)                                   \
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j],  \
+                                                                  0, 0, 0);                 \
+    }                                                                                       \
+  } while (0)
+
+  if constexpr (PD == 1) {
+    MOE_TILE_LOAD(0, 0);
+    MOE_TILE_STORE(0, 0);
     __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int st = kt & 1;
+      if (kt + 1 < nk) MOE_TILE_LOAD(kt + 1, 0);
+      MOE_TILE_COMPUTE(st);
+      if (kt + 1 < nk) MOE_TILE_STORE(st ^ 1, 0);
+      __syncthreads();
+    }
+  } else {
+    // two K tiles in flight: register set r holds the tile bound for LDS
+    // stage r, loaded one step before the step that stores it.  nk is even;
+    // the loads past the end re-read the last tile (clamped, so no branch
+    // splits the loads from the MFMAs) and the stores after the last tile go
+    // to a stage nobody reads again.  The scheduling barriers keep each
+    // step's loads ahead of its MFMAs and the dequantizing stores behind
+    // them, so a load has two steps to land.
+    MOE_TILE_LOAD(0, 0);
+    MOE_TILE_LOAD(1, 1);
+    MOE_TILE_STORE(0, 0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt += 2) {
+      MOE_TILE_LOAD(min(kt + 2, nk - 1), 0);
+      __builtin_amdgcn_sched_barrier(0);
+      MOE_TILE_COMPUTE(0);
+      __builtin_amdgcn_sched_barrier(0);
+      MOE_TILE_STORE(1, 1);
+      __syncthreads();
+      MOE_TILE_LOAD(min(kt + 3, nk - 1), 1);
+      __builtin_amdgcn_sched_barrier(0);
+      MOE_TILE_COMPUTE(1);
+      __builtin_amdgcn_sched_barrier(0);
+      MOE_TILE_STORE(0, 0);
+      __syncthreads();
+    }
   }
 #undef MOE_TILE_LOAD
 #undef MOE_TILE_STORE
+#undef MOE_TILE_COMPUTE
 
   // epilogue (32x32 C layout: column lane%32, rows 8*(q/4) + 4*(lane/32) + q%4)
   uint16_t* out = static_cast<uint16_t*>(p.out);
@@ -274,8 +314,8 @@ __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo
 // offsets.  Blocks are remapped so that each XCD (blockIdx % 8) takes a
 // contiguous run of tiles: the tiles of one expert share its weights in that
 // XCD's L2.
-template <int BM, int BN, int BK, int WM, int WN, int KIND, int ACT, bool BIAS, bool Q8>
-__global__ void __launch_bounds__(64 * WM * WN)
+template <int BM, int BN, int BK, int WM, int WN, int KIND, int ACT, bool BIAS, bool Q8, int PD>
+__global__ void __launch_bounds__(64 * WM * WN, PD == 2 ? 2 : 1)
 gemm_tile_kernel(GemmDesc p, int tiles_n) {
   __shared__ __attribute__((aligned(16))) u32x4 sA[2][BM * (BK / 8)];
   __shared__ __attribute__((aligned(16))) u32x4 sB[2][BN * (BK / 8)];
@@ -302,14 +342,18 @@ gemm_tile_kernel(GemmDesc p, int tiles_n) {
   const TileInfo tile = s_tile;
   const int nt = s_nt;
   if (tile.group < 0) return;
-  gemm_tile_body<BM, BN, BK, WM, WN, KIND, ACT, BIAS, Q8>(p, tile, nt, sA, sB);
+  gemm_tile_body<BM, BN, BK, WM, WN, KIND, ACT, BIAS, Q8, PD>(p, tile, nt, sA, sB);
 }
 
+// (With two tiles in flight the extra staging registers would otherwise push
+// the kernel past 256 VGPRs, i.e. to one wave per SIMD; every shape here runs
+// two waves per SIMD, which the second bound asks for.)
+//
 // Persistent variant: the grid holds only the resident workgroups; the
 // row-tile table of the groups is built once per workgroup in LDS, and XCD
 // x = blockIdx % 8 walks a contiguous run of the (exact) tile list.
-template <int BM, int BN, int BK, int WM, int WN, int KIND, int ACT, bool BIAS, bool Q8>
-__global__ void __launch_bounds__(64 * WM * WN)
+template <int BM, int BN, int BK, int WM, int WN, int KIND, int ACT, bool BIAS, bool Q8, int PD>
+__global__ void __launch_bounds__(64 * WM * WN, PD == 2 ? 2 : 1)
 gemm_tile_persistent(GemmDesc p, int tiles_n) {
   constexpr int kTileThreads = 64 * WM * WN;
   __shared__ __attribute__((aligned(16))) u32x4 sA[2][BM * (BK / 8)];
@@ -354,7 +398,7 @@ gemm_tile_persistent(GemmDesc p, int tiles_n) {
     tile.group = glo;
     tile.row0 = (int64_t)s_off[glo] + (int64_t)(mt - s_tstart[glo]) * BM;
     tile.rows = min(BM, min(s_off[glo + 1], (int)p.rows_max) - (int)tile.row0);
-    gemm_tile_body<BM, BN, BK, WM, WN, KIND, ACT, BIAS, Q8>(p, tile, nt, sA, sB);
+    gemm_tile_body<BM, BN, BK, WM, WN, KIND, ACT, BIAS, Q8, PD>(p, tile, nt, sA, sB);
   }
 }
 
@@ -386,7 +430,8 @@ constexpr TileCfg kTiles[kVariants] = {
 
 int cu_count();
 
-template <int BM, int BN, int BK, int WM, int WN, bool PERSIST, int KIND, int ACT, bool BIAS, bool Q8>
+template <int BM, int BN, int BK, int WM, int WN, bool PERSIST, int KIND, int ACT, bool BIAS, bool Q8,
+          int PD>
 hipError_t run(const GemmDesc& g, int occ, hipStream_t s) {
   constexpr int kTileThreads = 64 * WM * WN;
   constexpr bool kSwiglu = (KIND == kGemmUp && ACT == MOE_ACT_SWIGLU);
@@ -403,21 +448,29 @@ hipError_t run(const GemmDesc& g, int occ, hipStream_t s) {
   grid = (grid + 7) / 8 * 8;  // a multiple of 8 (XCDs)
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   if constexpr (PERSIST)
-    gemm_tile_persistent<BM, BN, BK, WM, WN, KIND, ACT, BIAS, Q8>
+    gemm_tile_persistent<BM, BN, BK, WM, WN, KIND, ACT, BIAS, Q8, PD>
         <<<dim3((unsigned)grid), dim3(kTileThreads), 0, s>>>(g, tiles_n);
   else
-    gemm_tile_kernel<BM, BN, BK, WM, WN, KIND, ACT, BIAS, Q8>
+    gemm_tile_kernel<BM, BN, BK, WM, WN, KIND, ACT, BIAS, Q8, PD>
         <<<dim3((unsigned)grid), dim3(kTileThreads), 0, s>>>(g, tiles_n);
   return hipGetLastError();
 }
 
+// INT8 weights keep two K tiles in flight (their K is a multiple of 128, so
+// the K tile count is even): a tile of codes is half the bytes of a bf16 one.
+// The decode-shaped tile (weight streaming) does so for bf16 too when the K
+// tile count is even.
 template <int KIND, int ACT, bool BIAS, bool Q8>
 hipError_t dispatch(const GemmDesc& g, int variant, hipStream_t s) {
+  constexpr int PD = Q8 ? 2 : 1;
+  const bool even_k_tiles = (KIND == kGemmUp ? g.d : g.f) % 128 == 0;
   switch (variant) {
-    case 0: return run<256, 256, 64, 2, 4, false, KIND, ACT, BIAS, Q8>(g, kTiles[0].occ, s);
-    case 1: return run<256, 128, 64, 4, 2, true, KIND, ACT, BIAS, Q8>(g, kTiles[1].occ, s);
-    case 2: return run<128, 128, 64, 2, 2, true, KIND, ACT, BIAS, Q8>(g, kTiles[2].occ, s);
-    default: return run<32, 256, 64, 1, 4, true, KIND, ACT, BIAS, Q8>(g, kTiles[3].occ, s);
+    case 0: return run<256, 256, 64, 2, 4, false, KIND, ACT, BIAS, Q8, PD>(g, kTiles[0].occ, s);
+    case 1: return run<256, 128, 64, 4, 2, true, KIND, ACT, BIAS, Q8, PD>(g, kTiles[1].occ, s);
+    case 2: return run<128, 128, 64, 2, 2, true, KIND, ACT, BIAS, Q8, PD>(g, kTiles[2].occ, s);
+    default:
+      if (even_k_tiles) return run<32, 256, 64, 1, 4, true, KIND, ACT, BIAS, Q8, 2>(g, kTiles[3].occ, s);
+      return run<32, 256, 64, 1, 4, true, KIND, ACT, BIAS, Q8, PD>(g, kTiles[3].occ, s);
   }
 }
 
