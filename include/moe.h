@@ -68,9 +68,13 @@ typedef enum { MOE_ACT_GELU = 0, MOE_ACT_SWIGLU = 1 } moe_act;
  * weight row, W[n, :] = scale[n] * q[n, :] ([P3 §6]: compress each expert's
  * weights to INT8 for deployment; the per-row symmetric scheme is this
  * library's reading).  INT8 needs BF16 activations and d_model, d_ffn
- * multiples of 128 (else MOE_ERR_UNSUPPORTED).  The kernels multiply each
- * code by its scale and round the product to bfloat16 (to nearest even)
- * before the matrix products; accumulation is float32 as for bf16 weights. */
+ * multiples of 128 (else MOE_ERR_UNSUPPORTED).  Accumulation is float32 as
+ * for bf16 weights.  Where a product's reduction runs over one weight matrix
+ * (every gate/up product, and the down product of routed experts or of a
+ * single shared expert) the codes enter the matrix cores exactly and the
+ * float32 sum of each output column is multiplied by its row scale.  The
+ * down product that sums n_seg > 1 shared experts multiplies each code by
+ * its scale and rounds the product to bfloat16 (to nearest even) first. */
 typedef enum { MOE_WEIGHTS_ACT = 0, MOE_WEIGHTS_INT8 = 1 } moe_weight_format;
 
 typedef struct {

@@ -98,7 +98,8 @@ __device__ __forceinline__ float silu_f(float g) { return g / (1.f + __expf(-g))
 
 // INT8 weight codes: 16 codes (one 16-byte load, code i in byte i) times the
 // row scale s, each product rounded to bfloat16 (nearest even), as two
-// 16-byte chunks of 8 bf16 (codes 0..7 and 8..15).
+// 16-byte chunks of 8 bf16 (codes 0..7 and 8..15).  codes16_to_bf16 below
+// widens the codes alone (no scale) in the same layout.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -113,6 +114,21 @@ __device__ __forceinline__ void dequant16(const u32x4_t q, float s, u32x4_t& lo,
     float v[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) v[b] = (float)(int8_t)(w[i] >> (8 * b)) * s;
+    o[2 * i] = pack_bf16x2(v[0], v[1]);
+    o[2 * i + 1] = pack_bf16x2(v[2], v[3]);
+  }
+  lo = u32x4_t{o[0], o[1], o[2], o[3]};
+  hi = u32x4_t{o[4], o[5], o[6], o[7]};
+}
+// 16 INT8 codes -> 16 bf16 of the same integer values (exact: |code| <= 128)
+__device__ __forceinline__ void codes16_to_bf16(const u32x4_t q, u32x4_t& lo, u32x4_t& hi) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  uint32_t o[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float v[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) v[b] = (float)(int8_t)(w[i] >> (8 * b));
     o[2 * i] = pack_bf16x2(v[0], v[1]);
     o[2 * i + 1] = pack_bf16x2(v[2], v[3]);
   }

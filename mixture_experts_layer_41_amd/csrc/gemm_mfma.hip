@@ -18,11 +18,15 @@
 //   * workgroups are remapped so each XCD (blockIdx % 8) takes a contiguous
 //     run of tiles: the tiles of one expert, which share its weights, then
 //     hit the same L2;
-//   * INT8 weights (Q8): the weight tile is loaded as codes (half the bytes),
-//     and each code is multiplied by its row scale and rounded to bf16 on
-//     the way from the staging registers to LDS; the MFMA loop and the
-//     epilogues are the bf16 ones.  The down GEMM's K segments (shared
-//     experts) each bring their own row scales.
+//   * INT8 weights (Q8 != 0): the weight tile is loaded as codes (half the
+//     bytes) and widened to bf16 on the way from the staging registers to
+//     LDS; the MFMA loop is the bf16 one.  Q8 = 1: the codes enter the MFMAs
+//     as they are (small integers are exact in bf16) and the epilogue
+//     multiplies each output column by its weight row's scale; this covers
+//     every GEMM whose K range is one weight matrix.  Q8 = 2 (the down GEMM
+//     summing several shared experts, whose K segments each bring their own
+//     row scales): each code is multiplied by its row scale and rounded to
+//     bf16 while staging.
 #include <algorithm>
 #include <cmath>
 
@@ -39,7 +43,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte chun
 // then the epilogue.  sA / sB are the two LDS stages.  PD = K tiles whose
 // global loads are in flight at once (1, or 2 with two register sets; PD = 2
 // needs an even number of K tiles).
-template <int BM, int BN, int BK, int WM, int WN, int KIND, int ACT, bool BIAS, bool Q8, int PD>
+template <int BM, int BN, int BK, int WM, int WN, int KIND, int ACT, bool BIAS, int Q8, int PD>
 __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo& tile, int nt,
                                                u32x4 (*sA)[BM * (BK / 8)],
                                                u32x4 (*sB)[BN * (BK / 8)]) {
@@ -58,6 +62,7 @@ __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo
   static_assert(BK == 32 || BK == 64, "K tile");
   static_assert(MI >= 1 && NI >= 1 && A_LD >= 1 && B_LD >= 1, "tile shape");
   static_assert(!Q8 || (B8_LD >= 1 && BN * CPR8 % kTileThreads == 0), "tile shape");
+  static_assert(Q8 != 2 || KIND == kGemmDown, "row scales while staging: the shared down GEMM only");
   static_assert(!kSwiglu || (NI % 2 == 0), "SwiGLU pairs gate and up blocks");
   static_assert(PD == 1 || PD == 2, "prefetch depth");
   const int tid = threadIdx.x;
@@ -92,7 +97,6 @@ __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo
   const int8_t* bptr8[B8_LD];
   int boff8[B8_LD][2];   // LDS slots of the two bf16 chunks a code chunk becomes
   int brow8[B8_LD];      // weight row (within the segment) of each code load
-  float bscale[B8_LD];   // its scale
 #pragma unroll
   for (int i = 0; i < A_LD; ++i) {
     const int c = tid + kTileThreads * i;
@@ -129,14 +133,12 @@ __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo
       bptr8[i] = static_cast<const int8_t*>(p.w) + wbase + (int64_t)wr * K + c8 * 16;
       boff8[i][0] = r * CPR + ((2 * c8) ^ ((r / RPW) % CPR));
       boff8[i][1] = r * CPR + ((2 * c8 + 1) ^ ((r / RPW) % CPR));
-      // up: one segment per tile; down: reloaded per K tile below
-      if (KIND == kGemmUp) bscale[i] = p.w_scale[((int64_t)tile.group * S + seg) * rows1 + wr];
     }
   }
 
   u32x4 ra[PD][A_LD], rb[PD][B_LD];  // staging registers of the next K tile(s)
   u32x4 rb8[PD][B8_LD];              // (Q8) codes of the next K tile(s)
-  float sc8[PD][B8_LD];              // (Q8, down) their row scales
+  float sc8[PD][B8_LD];              // (Q8 = 2) their row scales
   // load K tile kt_ into register set r_ (a compile-time constant)
 #define MOE_TILE_LOAD(kt_, r_)                                                              \
   do {                                                                                      \
@@ -157,7 +159,7 @@ __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo
     } else {                                                                                \
       _Pragma("unroll") for (int i_ = 0; i_ < B8_LD; ++i_)                                 \
           rb8[r_][i_] = *reinterpret_cast<const u32x4*>(bptr8[i_] + bo_);                   \
-      if (KIND == kGemmDown) {                                                              \
+      if constexpr (Q8 == 2) {                                                              \
         const int s_ = (kt_) / nk_seg;                                                      \
         _Pragma("unroll") for (int i_ = 0; i_ < B8_LD; ++i_)                               \
             sc8[r_][i_] = p.w_scale[((int64_t)tile.group * S + s_) * rows1 + brow8[i_]];    \
@@ -175,7 +177,10 @@ __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo
         /* codes stay packed until here: no unpacking next to the load */                   \
         if constexpr (PD == 2) asm volatile("" : "+v"(rb8[r_][i_]));                       \
         u32x4 lo_, hi_;                                                                     \
-        dequant16(rb8[r_][i_], KIND == kGemmDown ? sc8[r_][i_] : bscale[i_], lo_, hi_);     \
+        if constexpr (Q8 == 2)                                                              \
+          dequant16(rb8[r_][i_], sc8[r_][i_], lo_, hi_);                                    \
+        else                                                                                \
+          codes16_to_bf16(rb8[r_][i_], lo_, hi_);                                           \
         sB[st_][boff8[i_][0]] = lo_;                                                        \
         sB[st_][boff8[i_][1]] = hi_;                                                        \
       }                                                                                     \
@@ -206,6 +211,23 @@ __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo
     brow[j] = r * CPR;
   }
   const int sw = (fr / RPW) % CPR;
+
+  // (Q8 = 1) row scale of each output column this lane holds: fragment j's
+  // column fr is weight row brow[j] / CPR of the tile
+  float esc[Q8 == 1 ? NI : 1];
+  if constexpr (Q8 == 1) {
+    const int64_t sbase = ((int64_t)tile.group * S + seg) * rows1;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int r = brow[j] / CPR;
+      int wr;
+      if (kSwiglu)
+        wr = (r < BN / 2) ? n0 + r : f + n0 + (r - BN / 2);
+      else
+        wr = n0 + r;
+      esc[j] = p.w_scale[sbase + wr];
+    }
+  }
 
   // MFMAs over the K tile in LDS stage st_
 #define MOE_TILE_COMPUTE(st_)                                                               \
@@ -283,6 +305,10 @@ __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo
         for (int j = 0; j < NI / 2; ++j) {
           const int cidx = wn * (TN / 2) + j * 32 + fr;
           float g = acc[i][j][q], u = acc[i][j + NI / 2][q];
+          if constexpr (Q8 == 1) {
+            g *= esc[j];
+            u *= esc[j + NI / 2];
+          }
           if (BIAS) {
             const uint16_t* b = bias + ((int64_t)tile.group * S + seg) * 2 * f;
             g += bf16_to_f32(b[n0 + cidx]);
@@ -295,6 +321,7 @@ __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo
         for (int j = 0; j < NI; ++j) {
           const int cidx = wn * TN + j * 32 + fr;
           float v = acc[i][j][q];
+          if constexpr (Q8 == 1) v *= esc[j];
           if (KIND == kGemmUp) {
             if (BIAS) v += bf16_to_f32(bias[((int64_t)tile.group * S + seg) * f + n0 + cidx]);
             out[grow * p.ldo + (int64_t)seg * f + n0 + cidx] = f32_to_bf16(gelu_f(v));
@@ -314,7 +341,7 @@ __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo
 // offsets.  Blocks are remapped so that each XCD (blockIdx % 8) takes a
 // contiguous run of tiles: the tiles of one expert share its weights in that
 // XCD's L2.
-template <int BM, int BN, int BK, int WM, int WN, int KIND, int ACT, bool BIAS, bool Q8, int PD>
+template <int BM, int BN, int BK, int WM, int WN, int KIND, int ACT, bool BIAS, int Q8, int PD>
 __global__ void __launch_bounds__(64 * WM * WN, PD == 2 ? 2 : 1)
 gemm_tile_kernel(GemmDesc p, int tiles_n) {
   __shared__ __attribute__((aligned(16))) u32x4 sA[2][BM * (BK / 8)];
@@ -352,7 +379,7 @@ gemm_tile_kernel(GemmDesc p, int tiles_n) {
 // Persistent variant: the grid holds only the resident workgroups; the
 // row-tile table of the groups is built once per workgroup in LDS, and XCD
 // x = blockIdx % 8 walks a contiguous run of the (exact) tile list.
-template <int BM, int BN, int BK, int WM, int WN, int KIND, int ACT, bool BIAS, bool Q8, int PD>
+template <int BM, int BN, int BK, int WM, int WN, int KIND, int ACT, bool BIAS, int Q8, int PD>
 __global__ void __launch_bounds__(64 * WM * WN, PD == 2 ? 2 : 1)
 gemm_tile_persistent(GemmDesc p, int tiles_n) {
   constexpr int kTileThreads = 64 * WM * WN;
@@ -430,7 +457,7 @@ constexpr TileCfg kTiles[kVariants] = {
 
 int cu_count();
 
-template <int BM, int BN, int BK, int WM, int WN, bool PERSIST, int KIND, int ACT, bool BIAS, bool Q8,
+template <int BM, int BN, int BK, int WM, int WN, bool PERSIST, int KIND, int ACT, bool BIAS, int Q8,
           int PD>
 hipError_t run(const GemmDesc& g, int occ, hipStream_t s) {
   constexpr int kTileThreads = 64 * WM * WN;
@@ -460,7 +487,7 @@ hipError_t run(const GemmDesc& g, int occ, hipStream_t s) {
 // the K tile count is even): a tile of codes is half the bytes of a bf16 one.
 // The decode-shaped tile (weight streaming) does so for bf16 too when the K
 // tile count is even.
-template <int KIND, int ACT, bool BIAS, bool Q8>
+template <int KIND, int ACT, bool BIAS, int Q8>
 hipError_t dispatch(const GemmDesc& g, int variant, hipStream_t s) {
   constexpr int PD = Q8 ? 2 : 1;
   const bool even_k_tiles = (KIND == kGemmUp ? g.d : g.f) % 128 == 0;
@@ -476,8 +503,10 @@ hipError_t dispatch(const GemmDesc& g, int variant, hipStream_t s) {
 
 template <int KIND, int ACT, bool BIAS>
 hipError_t dispatch_w(const GemmDesc& g, int variant, hipStream_t s) {
-  return g.w_scale ? dispatch<KIND, ACT, BIAS, true>(g, variant, s)
-                   : dispatch<KIND, ACT, BIAS, false>(g, variant, s);
+  if (!g.w_scale) return dispatch<KIND, ACT, BIAS, 0>(g, variant, s);
+  if constexpr (KIND == kGemmDown)
+    if (g.n_seg > 1) return dispatch<KIND, ACT, BIAS, 2>(g, variant, s);
+  return dispatch<KIND, ACT, BIAS, 1>(g, variant, s);
 }
 
 int cu_count() {
