@@ -36,7 +36,7 @@ __all__ = ["LayerConfig", "CONFIGS", "get_config", "f32_to_bf16_bits", "Bank",
 TAGS = {
     "x": 1, "w_router": 2, "w1": 3, "b1": 4, "w2": 5, "b2": 6,
     "ws1": 7, "sb1": 8, "ws2": 9, "sb2": 10, "x_redraw": 11,
-    "w1_scale": 12, "w2_scale": 13, "ws1_scale": 14, "ws2_scale": 15,
+    "w1_scale": 12, "w2_scale": 13, "ws1_scale": 14, "ws2_scale": 15, "router_noise": 16,
 }
 X_ROW_BLOCK = 4096          # rows of x per sub-stream
 WEIGHT_STD = 0.02
@@ -60,6 +60,8 @@ class LayerConfig:
     add_residual: bool = False
     seed: int = 0
     weights: str = "act"      # expert weights: "act" (activation dtype) or "int8" (codes + row scales)
+    router_temperature: float = 1.0   # tau of the router scores
+    router_noise_std: float = 0.0     # > 0: Gaussian noise [T, E] of this std added to the scores
 
     @property
     def w1_rows(self) -> int:
@@ -208,18 +210,26 @@ def router_bias_values(cfg: LayerConfig):
 def make_inputs(cfg: LayerConfig, accept=None, max_redraws: int = 64, materialize: bool = True):
     """All inputs of one layer workload.
 
-    accept(x, w_router, router_bias) -> bool[T] marks acceptable token rows;
-    each rejected row t is redrawn from stream (seed, "x_redraw", t, attempt)
-    until accepted.  Returns a dict; expert weight stacks are numpy arrays if
-    `materialize`, else lazy `Bank`s.
+    accept(x, w_router, router_bias, noise) -> bool[T] marks acceptable token
+    rows (noise: the router noise rows of the same tokens, or None); each
+    rejected row t is redrawn from stream (seed, "x_redraw", t, attempt)
+    until accepted (its noise row stays).  Returns a dict; expert weight
+    stacks are numpy arrays if `materialize`, else lazy `Bank`s.
+
+    Router noise (router_noise_std > 0): float32 std * N(0, 1) [T, E] from
+    stream (seed, "router_noise", 0).
     """
     dt = cfg.dtype
     x = _draw_x_rows(cfg)
     w_router = Bank(cfg.seed, "w_router", 1, (cfg.E, cfg.d), dt, WEIGHT_STD)[0]
     rbias = router_bias_values(cfg)
+    noise = None
+    if cfg.router_noise_std > 0:
+        z = _rng(cfg.seed, "router_noise", 0).standard_normal((cfg.T, cfg.E), dtype=np.float32)
+        noise = (z * np.float32(cfg.router_noise_std)).astype(np.float32)
     redrawn = set()
     if accept is not None:
-        ok = np.asarray(accept(x, w_router, rbias), dtype=bool)
+        ok = np.asarray(accept(x, w_router, rbias, noise), dtype=bool)
         attempt = 0
         while not ok.all():
             if attempt >= max_redraws:
@@ -230,7 +240,8 @@ def make_inputs(cfg: LayerConfig, accept=None, max_redraws: int = 64, materializ
                 z = _rng(cfg.seed, "x_redraw", int(t), attempt).standard_normal(cfg.d, dtype=np.float32)
                 x[t] = _store(z, dt)
             redrawn.update(int(t) for t in bad)
-            ok[bad] = np.asarray(accept(x[bad], w_router, rbias), dtype=bool)
+            ok[bad] = np.asarray(accept(x[bad], w_router, rbias, None if noise is None else noise[bad]),
+                                 dtype=bool)
             attempt += 1
 
     bias_zero = cfg.expert_bias == "zero"
@@ -255,7 +266,8 @@ def make_inputs(cfg: LayerConfig, accept=None, max_redraws: int = 64, materializ
         banks["w2_scale"] = Bank(cfg.seed, "w2_scale", E, (d,), "scale", WEIGHT_STD)
         banks["ws1_scale"] = Bank(cfg.seed, "ws1_scale", S, (cfg.w1_rows,), "scale", WEIGHT_STD) if S else None
         banks["ws2_scale"] = Bank(cfg.seed, "ws2_scale", S, (d,), "scale", WEIGHT_STD) if S else None
-    out = {"x": x, "w_router": w_router, "router_bias": rbias, "n_redrawn": len(redrawn)}
+    out = {"x": x, "w_router": w_router, "router_bias": rbias, "router_noise": noise,
+           "n_redrawn": len(redrawn)}
     for key, bank in banks.items():
         out[key] = None if bank is None else (bank.array() if materialize else bank)
     return out

@@ -40,6 +40,13 @@ the design notes):
     weights to INT8 for deployment, with no scheme given): symmetric INT8
     codes q with one float32 scale per weight row, W[n, :] = scale[n] *
     q[n, :] (the row is an output channel of W1 and of W2).
+  * router temperature and noise ([P2 §5.1], [P2 §2.2]): the scores are
+    logits / tau + noise, tau dividing the router output with its bias and
+    the caller's noise added after; everything downstream uses the scores.
+  * the other load-balance forms ([P3 §3.1] E * sum P^2; [P2 §4.2] KL of
+    the uniform distribution from P, with 1e-8 in the logarithm, plus the
+    squared distance of the hard frequencies from 1/E) use the same P and f
+    as the main one and are reported unweighted.
 
 Parity pins: every function below is exercised by the CPU tests against
 closed forms, brute force or an independently written dense computation; the
@@ -59,6 +66,7 @@ __all__ = [
     "dequantize_int8",
     "expert_weight",
     "router_logits",
+    "router_scores",
     "softmax_lse",
     "topk_select",
     "renormalise",
@@ -144,6 +152,25 @@ def router_logits(x: np.ndarray, w_router: np.ndarray, bias=None) -> np.ndarray:
     return logits
 
 
+def router_scores(logits: np.ndarray, temperature: float = 1.0, noise=None) -> np.ndarray:
+    """The scores the softmax and the top-k see: s[t, e] = l[t, e] / tau + n[t, e].
+
+    [P2 §5.1] (troubleshooting table) scales the router logits by a
+    temperature, l / tau with tau = 1 by default, to soften a router whose
+    top-1 share is too high; [P2 §2.2] (and the routing noise of [P3 §6])
+    adds a controllable random perturbation to the scores before the top-k.
+    Reading: tau divides the router's output, bias included, the noise is
+    added after it, and the probabilities, weights, lse and the statistics
+    all use s.  The noise n [T, E] is an input drawn by the caller.
+    """
+    s = np.asarray(logits, dtype=np.float64)
+    if temperature != 1.0:
+        s = s / float(temperature)
+    if noise is not None:
+        s = s + np.asarray(noise, dtype=np.float32).astype(np.float64)
+    return s
+
+
 def softmax_lse(logits: np.ndarray):
     """Softmax over experts and the per-token log-sum-exp.
 
@@ -174,16 +201,18 @@ def renormalise(p: np.ndarray, idx: np.ndarray) -> np.ndarray:
     return sel / sel.sum(axis=1, keepdims=True)
 
 
-def router_gap_ok(x, w_router, bias, k: int, dtype: str, gap: float = 1e-4) -> np.ndarray:
+def router_gap_ok(x, w_router, bias, k: int, dtype: str, gap: float = 1e-4,
+                  temperature: float = 1.0, noise=None) -> np.ndarray:
     """Input acceptance rule: p_(k) - p_(k+1) >= gap for every token.
 
-    Evaluated in float64 on the stored (rounded) values.  With k == E there is
-    no (k+1)-th expert and every token is accepted.  Used by the input
-    generator through a callback, so that routing is unambiguous.
+    Evaluated in float64 on the stored (rounded) values, with the router's
+    temperature and noise rows (of the same tokens) applied.  With k == E
+    there is no (k+1)-th expert and every token is accepted.  Used by the
+    input generator through a callback, so that routing is unambiguous.
     """
     xd = decode(x, dtype)
     wr = decode(w_router, dtype)
-    p, _ = softmax_lse(router_logits(xd, wr, bias))
+    p, _ = softmax_lse(router_scores(router_logits(xd, wr, bias), temperature, noise))
     E = p.shape[1]
     if k >= E:
         return np.ones(p.shape[0], dtype=bool)
@@ -326,7 +355,9 @@ def combine(routed: np.ndarray, shared, residual) -> np.ndarray:
 
 # ---------------------------------------------------------------------------
 # auxiliary statistics: [P4 §3.1] load-balance loss alpha * E * sum f_i P_i,
-# [P5 §2] router z-loss and the 0.01 / 0.001 coefficients
+# [P5 §2] router z-loss and the 0.01 / 0.001 coefficients; the two other
+# load-balance forms the pages give: [P3 §3.1] E * sum P_i^2 and [P2 §4.2]
+# KL(uniform || P) plus a penalty on the hard frequencies
 
 
 def aux_losses(p: np.ndarray, lse: np.ndarray, counts: np.ndarray, top_k: int):
@@ -336,13 +367,25 @@ def aux_losses(p: np.ndarray, lse: np.ndarray, counts: np.ndarray, top_k: int):
     under uniform routing; P_e = mean_t p[t, e] over the full softmax.
     The f_e normalisation is a convention: parity unpinned beyond the
     convention.
+
+    Also, unweighted (the pages' coefficients are the caller's):
+      lb_squares   = E * sum_e P_e^2                          ([P3 §3.1] code)
+      kl_uniform   = sum_e (1/E) (ln(1/E) - ln(P_e + 1e-8))   ([P2 §4.2]: the KL
+                     divergence of the uniform distribution from P, with the
+                     page's 1e-8 inside the logarithm)
+      freq_penalty = sum_e (f_e - 1/E)^2                      ([P2 §4.2]: f_e is
+                     the expert's share of all top-k selections)
     """
     T, E = p.shape
     f = counts.astype(np.float64) / float(T * top_k)
     P = p.mean(axis=0)
     lb = float(E * np.sum(f * P))
     z = float(np.mean(lse * lse))
-    return {"lb": lb, "z": z, "weighted": 0.01 * lb + 0.001 * z, "f": f, "P": P}
+    u = 1.0 / E
+    return {"lb": lb, "z": z, "weighted": 0.01 * lb + 0.001 * z, "f": f, "P": P,
+            "lb_squares": float(E * np.sum(P * P)),
+            "kl_uniform": float(np.sum(u * (np.log(u) - np.log(P + 1e-8)))),
+            "freq_penalty": float(np.sum((f - u) ** 2))}
 
 
 # ---------------------------------------------------------------------------
@@ -356,8 +399,9 @@ def forward(cfg, t, rows=None, want_routed_rows=False):
          ("swiglu"/"gelu"), capacity_factor (<= 0: none), add_residual, and
          optionally weights ("act", or "int8": expert weights are INT8
          codes with float32 row scales w1_scale / w2_scale / ws1_scale /
-         ws2_scale in t).
+         ws2_scale in t) and router_temperature (tau, default 1).
     t:   dict with x [T, d], w_router [E, d], router_bias [E] float32 or None,
+         optionally router_noise [T, E] float32 (added to the scores),
          w1 / b1 / w2 / b2 (indexable by expert), ws1 / sb1 / ws2 / sb2
          (indexable by shared expert, may be None when S == 0).
     rows: optional iterable of token indices; the expert FFNs and y are then
@@ -377,7 +421,8 @@ def forward(cfg, t, rows=None, want_routed_rows=False):
     rb = t.get("router_bias")
     rb = None if rb is None else np.asarray(rb, dtype=np.float32).astype(np.float64)
 
-    logits = router_logits(x, wr, rb)
+    tau = float(getattr(cfg, "router_temperature", 1.0))
+    logits = router_scores(router_logits(x, wr, rb), tau, t.get("router_noise"))
     p, lse = softmax_lse(logits)
     idx = topk_select(p, k)
     w = renormalise(p, idx)
@@ -421,5 +466,7 @@ def forward(cfg, t, rows=None, want_routed_rows=False):
         "perm_w": w[perm_token, perm_slot] if len(perm_token) else np.zeros(0),
         "inv_row": inv_row, "n_dropped": int(n_dropped),
         "lb": aux["lb"], "z": aux["z"], "weighted": aux["weighted"],
+        "lb_squares": aux["lb_squares"], "kl_uniform": aux["kl_uniform"],
+        "freq_penalty": aux["freq_penalty"],
         "rows": tok, "y": y, "shared_y": shared, "routed_rows": routed_rows,
     }

@@ -65,7 +65,8 @@ def from_dev(t) -> np.ndarray:
 
 
 def gap_accept(cfg):
-    return lambda x, w, b: oracle.router_gap_ok(x, w, b, cfg.k, cfg.dtype)
+    return lambda x, w, b, n: oracle.router_gap_ok(x, w, b, cfg.k, cfg.dtype,
+                                                   temperature=cfg.router_temperature, noise=n)
 
 
 def inputs(cfg, materialize=True):

@@ -41,9 +41,9 @@ def test_gap_rule_holds_after_redraw(name):
     cfg = CONFIGS[name]
     if cfg.T > 4096:
         cfg = get_config(name, T=4096)
-    acc = lambda x, w, b: oracle.router_gap_ok(x, w, b, cfg.k, cfg.dtype)
+    acc = lambda x, w, b, n: oracle.router_gap_ok(x, w, b, cfg.k, cfg.dtype, noise=n)
     t = make_inputs(cfg, accept=acc)
-    assert acc(t["x"], t["w_router"], t["router_bias"]).all()
+    assert acc(t["x"], t["w_router"], t["router_bias"], t["router_noise"]).all()
     assert t["n_redrawn"] > 0          # the rule is active on these shapes
 
 

@@ -339,7 +339,7 @@ def test_drop_heavy_against_sorted_lists():
     """Flash-config shape at capacity factor 0.5 (C = 256): per-expert kept
     tokens are the C smallest token indices routed to it."""
     cfg = get_config("c2", capacity_factor=0.5)
-    t = make_inputs(cfg, accept=lambda x, w, b: oracle.router_gap_ok(x, w, b, cfg.k, cfg.dtype))
+    t = make_inputs(cfg, accept=lambda x, w, b, n: oracle.router_gap_ok(x, w, b, cfg.k, cfg.dtype, noise=n))
     xd = oracle.decode(t["x"], "bf16")
     wr = oracle.decode(t["w_router"], "bf16")
     p, _ = oracle.softmax_lse(oracle.router_logits(xd, wr))
@@ -541,3 +541,163 @@ def test_int8_generator_codes_and_scales():
         assert s.dtype == np.float32 and s.shape == t[key].shape[:2] and (s > 0).all()
     w = t["w1"].astype(np.float64) * t["w1_scale"][..., None]
     assert 0.018 < w.std() < 0.022
+
+
+# ---------------------------------------------------------------------------
+# router temperature and noise ([P2 §5.1], [P2 §2.2]); the other
+# load-balance forms ([P3 §3.1], [P2 §4.2])
+
+
+@dataclass
+class TCfg(Cfg):
+    router_temperature: float = 1.0
+
+
+def test_temperature_divides_logits_and_bias():
+    """Scores (x W^T + b) / tau: with tau = 2 the layer equals the tau = 1
+    layer with W_r / 2 and b / 2 (exact halvings of float32 values)."""
+    bias = 2.0 * np.log(1.0 / (np.arange(6) + 1.0))
+    c2 = TCfg(T=24, d=8, E=6, k=2, f=4, router_temperature=2.0)
+    t = rand_tensors(c2, 41, router_bias=bias)
+    o2 = oracle.forward(c2, t)
+    t1 = dict(t)
+    t1["w_router"] = f32(t["w_router"] / 2)
+    t1["router_bias"] = f32(t["router_bias"] / 2)
+    o1 = oracle.forward(TCfg(T=24, d=8, E=6, k=2, f=4), t1)
+    assert np.array_equal(o1["topk_idx"], o2["topk_idx"])
+    for key in ("p", "lse", "topk_w", "y"):
+        assert np.allclose(o1[key], o2[key], rtol=1e-13, atol=1e-15), key
+    for key in ("lb", "z", "lb_squares", "kl_uniform", "freq_penalty"):
+        assert abs(o1[key] - o2[key]) < 1e-12, key
+
+
+def test_large_temperature_flattens_the_softmax():
+    """tau -> infinity: p -> 1/E, lse -> ln E, lb_squares -> 1."""
+    cfg = TCfg(T=16, d=4, E=5, k=2, f=2, router_temperature=1e9)
+    o = oracle.forward(cfg, rand_tensors(cfg, 42))
+    assert np.allclose(o["p"], 0.2, atol=1e-8)
+    assert np.allclose(o["lse"], math.log(5), atol=1e-8)
+    assert abs(o["lb_squares"] - 1.0) < 1e-8
+
+
+def test_noise_is_added_after_the_temperature():
+    """Noise n[t, e] = c_e for every token acts like a router bias of tau*c
+    (the bias is divided by tau, the noise is not)."""
+    c = np.array([0.5, -0.25, 1.0, 0.0, -1.5], dtype=np.float32)
+    cfg = TCfg(T=20, d=6, E=5, k=2, f=3, router_temperature=2.0)
+    t = rand_tensors(cfg, 43)
+    tn = dict(t)
+    tn["router_noise"] = np.tile(c, (cfg.T, 1))
+    tb = dict(t)
+    tb["router_bias"] = f32(2.0 * c)
+    on, ob = oracle.forward(cfg, tn), oracle.forward(cfg, tb)
+    assert np.array_equal(on["topk_idx"], ob["topk_idx"])
+    for key in ("p", "lse", "topk_w", "y"):
+        assert np.allclose(on[key], ob[key], rtol=1e-13, atol=1e-15), key
+
+
+def test_noise_changes_the_selection_worked_example():
+    """One token, logits [0, ln 2, ln 3] (the worked example above); noise
+    [ln 4, 0, 0] lifts expert 0: scores [ln 4, ln 2, ln 3], p = [4, 2, 3]/9,
+    top-2 = [0, 2], w = [4/7, 3/7], lse = ln 9."""
+    cfg = TCfg(T=1, d=2, E=3, k=2, f=1)
+    ln2, ln3 = math.log(2.0), math.log(3.0)
+    t = {
+        "x": f32([[1.0, 0.0]]),
+        "w_router": f32([[0.0, 5.0], [ln2, -1.0], [ln3, 7.0]]),
+        "router_bias": None,
+        "router_noise": f32([[math.log(4.0), 0.0, 0.0]]),
+        "w1": f32(np.ones((3, 2, 2))), "w2": f32(np.ones((3, 2, 1))),
+        "b1": None, "b2": None, "ws1": None, "ws2": None,
+    }
+    o = oracle.forward(cfg, t)
+    tol = 1e-6
+    assert o["topk_idx"].tolist() == [[0, 2]]
+    assert np.allclose(o["p"][0], [4 / 9, 2 / 9, 3 / 9], atol=tol)
+    assert np.allclose(o["topk_w"][0], [4 / 7, 3 / 7], atol=tol)
+    assert abs(o["lse"][0] - math.log(9.0)) < tol
+    assert o["counts"].tolist() == [1, 0, 1]
+
+
+def test_lb_squares_uniform_and_dominant():
+    """E * sum P^2 is 1 for a zero router and tends to E when one expert
+    takes all the probability."""
+    cfg = TCfg(T=16, d=4, E=6, k=2, f=2)
+    t = rand_tensors(cfg, 44)
+    t["w_router"] = np.zeros_like(t["w_router"])
+    assert abs(oracle.forward(cfg, t)["lb_squares"] - 1.0) < 1e-14
+    t = rand_tensors(cfg, 44, router_bias=np.array([80.0, 0, 0, 0, 0, 0]))
+    assert abs(oracle.forward(cfg, t)["lb_squares"] - 6.0) < 1e-9
+
+
+def test_kl_and_frequency_penalty_closed_forms():
+    """Two experts, k = 1, four tokens.  Router logits [ln 3, 0] for three
+    tokens and [0, ln 3] for one: P = ((3 * 3/4 + 1/4) / 4, ...) = (5/8, 3/8);
+    f = (3/4, 1/4).
+      kl_uniform = 1/2 ln((1/2) / (5/8)) + 1/2 ln((1/2) / (3/8))
+                 = 1/2 ln(16/15)                  (up to the 1e-8 in the log)
+      freq_penalty = (1/4)^2 + (1/4)^2 = 1/8."""
+    cfg = TCfg(T=4, d=2, E=2, k=1, f=1)
+    ln3 = math.log(3.0)
+    t = {
+        "x": f32([[1.0, 0.0], [1.0, 0.0], [1.0, 0.0], [0.0, 1.0]]),
+        "w_router": f32([[ln3, 0.0], [0.0, ln3]]),
+        "router_bias": None,
+        "w1": f32(np.ones((2, 2, 2))), "w2": f32(np.ones((2, 2, 1))),
+        "b1": None, "b2": None, "ws1": None, "ws2": None,
+    }
+    o = oracle.forward(cfg, t)
+    assert o["counts"].tolist() == [3, 1]
+    assert abs(o["kl_uniform"] - 0.5 * math.log(16 / 15)) < 1e-7
+    assert abs(o["freq_penalty"] - 0.125) < 1e-15
+    assert abs(o["lb_squares"] - 2 * ((5 / 8) ** 2 + (3 / 8) ** 2)) < 1e-7
+
+
+def test_kl_uniform_special_values_and_sign():
+    """Uniform P: kl = -ln(1 + E * 1e-8) (only the page's 1e-8 remains);
+    otherwise kl >= that value (Gibbs' inequality), and it grows as one
+    expert takes more of the probability."""
+    cfg = TCfg(T=16, d=4, E=8, k=2, f=2)
+    t = rand_tensors(cfg, 45)
+    t["w_router"] = np.zeros_like(t["w_router"])
+    o = oracle.forward(cfg, t)
+    assert abs(o["kl_uniform"] - (-math.log(1 + 8e-8))) < 1e-15
+    prev = o["kl_uniform"]
+    for b0 in (1.0, 3.0, 6.0):
+        t = rand_tensors(cfg, 45, router_bias=np.array([b0] + [0.0] * 7))
+        t["w_router"] = np.zeros_like(t["w_router"])
+        kl = oracle.forward(cfg, t)["kl_uniform"]
+        assert kl > prev
+        prev = kl
+    for seed in range(3):
+        o = oracle.forward(cfg, rand_tensors(cfg, 46 + seed))
+        assert o["kl_uniform"] >= -math.log(1 + 8e-8) - 1e-15
+        assert o["freq_penalty"] >= 0.0
+
+
+def test_noise_generator_draws():
+    """Router noise: float32 [T, E], std as asked, fixed by the seed."""
+    cfg = get_config("c2", T=512, router_noise_std=0.5)
+    a = make_inputs(cfg)["router_noise"]
+    b = make_inputs(cfg)["router_noise"]
+    assert a.dtype == np.float32 and a.shape == (512, cfg.E)
+    assert np.array_equal(a, b)
+    assert abs(float(a.std()) - 0.5) < 0.02
+    assert make_inputs(get_config("c2", T=64))["router_noise"] is None
+
+
+def test_frequency_penalty_with_top2():
+    """f is the share of all T*k selections: two tokens choosing {0, 1} and
+    {0, 2} give f = (1/2, 1/4, 1/4, 0), so the penalty is
+    (1/4)^2 + 0 + 0 + (1/4)^2 = 1/8."""
+    cfg = TCfg(T=2, d=2, E=4, k=2, f=1)
+    t = {
+        "x": f32([[1.0, 0.0], [0.0, 1.0]]),
+        "w_router": f32([[3.0, 3.0], [2.0, 0.0], [0.0, 2.0], [-5.0, -5.0]]),
+        "router_bias": None,
+        "w1": f32(np.ones((4, 2, 2))), "w2": f32(np.ones((4, 2, 1))),
+        "b1": None, "b2": None, "ws1": None, "ws2": None,
+    }
+    o = oracle.forward(cfg, t)
+    assert o["counts"].tolist() == [2, 1, 1, 0]
+    assert abs(o["freq_penalty"] - 0.125) < 1e-15
