@@ -147,20 +147,21 @@ def main():
         router_bias=None if rb is None else torch.from_numpy(rb).cuda())
     q8 = cfg.weights == "int8"
     x = dev(t["x"])
+    noise = dev(t.get("router_noise"))   # [T, E] float32 or None
     c = B.config_of(cfg)
     fwd = B.Forward(c, W)
     stream = torch.cuda.current_stream()
 
     # ---- eager warm-up and (optionally) a captured graph of one step
     for _ in range(max(args.warmup, 1)):
-        fwd(x)
+        fwd(x, noise)
     torch.cuda.synchronize()
     graph = None
     if not args.no_graph:
         try:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                fwd(x)
+                fwd(x, noise)
             torch.cuda.synchronize()
             for _ in range(3):
                 g.replay()
@@ -178,7 +179,7 @@ def main():
         torch.cuda.synchronize()
         return time.perf_counter() - t0
 
-    eager_s = timed(lambda: fwd(x), args.steps)
+    eager_s = timed(lambda: fwd(x, noise), args.steps)
     graph_s = timed(graph.replay, args.steps) if graph is not None else None
     best_s = min(s for s in (eager_s, graph_s) if s is not None)
     mode = "hip_graph" if (graph_s is not None and graph_s <= eager_s) else "eager"
@@ -275,7 +276,7 @@ def main():
                "kind": "oracle",
                "sample": f"full layer forward of this workload ({T} tokens), {runs} run(s), "
                          f"{t_cpu:.1f} s, float64 numpy"}
-        y = fwd(x)
+        y = fwd(x, noise)
         torch.cuda.synchronize()
         yg = y.float().cpu().numpy().astype(np.float64)
         err = float(np.max(np.abs(yg - ref["y"])) / np.max(np.abs(ref["y"])))
@@ -294,7 +295,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "tokens": T, "d_model": d, "experts": cfg.E,
                    "top_k": k, "d_ffn": f, "shared_experts": S,
-                   "capacity_factor": cfg.capacity_factor, "expert_weights": "int8 codes + "
+                   "capacity_factor": cfg.capacity_factor,
+                   "router_temperature": cfg.router_temperature,
+                   "router_noise_std": cfg.router_noise_std, "expert_weights": "int8 codes + "
                    "f32 row scales" if q8 else ("bf16" if cfg.dtype == "bf16" else "f32"),
                    "launch": mode,
                    "eager_us_per_step": round(eager_s / args.steps * 1e6, 2),

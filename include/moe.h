@@ -90,6 +90,11 @@ typedef struct {
                              the binary64 value of cf ([P4 §3.1]); NaN rejected */
   int32_t add_residual;   /* 1: y += x ([P2 §4.1] adds the input inside the layer) */
   int32_t weight_format;  /* moe_weight_format of the expert weights */
+  float router_temperature; /* tau: the router's scores are logits / tau
+                               ([P2 §5.1] temperature scaling to soften an
+                               over-confident router); 0 means 1; otherwise
+                               finite, > 0 and with 1/tau finite, else
+                               INVALID_ARG */
 } moe_config;
 
 /* Device pointers to one layer's parameters (host struct, read during the call). */
@@ -116,9 +121,13 @@ typedef struct {
 /* Auxiliary statistics, written to device memory.
  * f_e = counts_e / (T*k) with the counts taken before capacity, P_e = mean
  * over all tokens of the full softmax ([P4 §3.1] load-balance loss
- * E * sum f_e P_e); z = mean over tokens of logsumexp(logits)^2 (router
+ * E * sum f_e P_e); z = mean over tokens of logsumexp(scores)^2 (router
  * z-loss named in [P5 §2]); weighted = 0.01 lb + 0.001 z, the coefficients
- * [P5 §2] reports. */
+ * [P5 §2] reports.  The other load-balance forms the pages give, unweighted:
+ * lb_squares = E * sum_e P_e^2 ([P3 §3.1]); kl_uniform = sum_e (1/E)
+ * (ln(1/E) - ln(P_e + 1e-8)), the KL divergence of the uniform distribution
+ * from P with the page's 1e-8, and freq_penalty = sum_e (f_e - 1/E)^2
+ * ([P2 §4.2]; its alpha of 0.001-0.01 is the caller's). */
 typedef struct {
   double load_balance;
   double z_loss;
@@ -126,6 +135,9 @@ typedef struct {
   int64_t n_dropped; /* assignments over capacity */
   int64_t capacity;  /* C, or -1 when there is no limit */
   int64_t n_kept;    /* R = T*k - n_dropped */
+  double lb_squares;
+  double kl_uniform;
+  double freq_penalty;
 } moe_aux;
 
 /* Static description of a status code. */
@@ -136,19 +148,25 @@ const char* moe_status_string(moe_status s);
  * ([P2 §3.2] a single linear layer; [P3 §3.1] steps 1-2; [P4 §3.1]
  * routing and top-k selection).
  *   logits[t,e] = sum_c x[t,c] W_r[e,c] + router_bias[e]   (float32 accumulate)
- *   p = softmax_e(logits), lse[t] = logsumexp_e(logits[t,:])
- *   topk_idx[t,:] = the k experts of largest logit (= largest p), sorted by
- *                   descending logit, lower index first on exact ties
+ *   s[t,e] = logits[t,e] / tau + router_noise[t,e]
+ *   p = softmax_e(s), lse[t] = logsumexp_e(s[t,:])
+ *   topk_idx[t,:] = the k experts of largest score (= largest p), sorted by
+ *                   descending score, lower index first on exact ties
  *   topk_w[t,j]   = p[t,idx] / sum_j' p[t,idx']
+ * tau = cfg->router_temperature ([P2 §5.1]); router_noise [T,E] float32 or
+ * NULL: a perturbation the caller draws, added before the top-k ([P2 §2.2]
+ * noisy top-k; [P3 §6] routing noise for exploration).
  * x [T,d], w_router [E,d] act-dtype; router_bias [E] float32 or NULL;
  * topk_idx [T,k] int32, topk_w [T,k] float32, token_lse [T] float32 (may be
  * NULL).  The call also leaves per-block routing statistics (expert counts,
  * probability sums, sum of lse^2) in ws; moe_aux_stats reads them from the
- * same ws, which must not be reused in between.
+ * same ws, which must not be reused in between.  INVALID_ARG for a
+ * misaligned (4-byte) router_noise.
  */
 moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
-                     const float* router_bias, int32_t* topk_idx, float* topk_w,
-                     float* token_lse, void* ws, size_t* ws_bytes, hipStream_t stream);
+                     const float* router_bias, const float* router_noise, int32_t* topk_idx,
+                     float* topk_w, float* token_lse, void* ws, size_t* ws_bytes,
+                     hipStream_t stream);
 
 /*
  * moe_permute - per-expert counts, capacity and a stable expert-contiguous
@@ -246,15 +264,17 @@ moe_status moe_aux_stats(const moe_config* cfg, const int32_t* expert_counts,
 /*
  * moe_forward - the whole layer: route, permute, routed and shared expert
  * FFNs, combine and aux statistics ([P3 §3.1] forward returns the output
- * and the auxiliary loss).  x, y [T,d] act-dtype.  Optional outputs (NULL
- * to skip): topk_idx [T,k], topk_w [T,k], expert_counts [E], aux (device).
+ * and the auxiliary loss).  x, y [T,d] act-dtype.  router_noise [T,E]
+ * float32 or NULL as in moe_route.  Optional outputs (NULL to skip):
+ * topk_idx [T,k], topk_w [T,k], expert_counts [E], aux (device).
  * Expert weights per cfg->weight_format (INT8: the scale pointers of `w`
  * for the routed experts, and for the shared ones when S > 0, are
  * required).  ws: query with ws == NULL.
  */
-moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* x, void* y,
-                       int32_t* topk_idx, float* topk_w, int32_t* expert_counts, moe_aux* aux,
-                       void* ws, size_t* ws_bytes, hipStream_t stream);
+moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* x,
+                       const float* router_noise, void* y, int32_t* topk_idx, float* topk_w,
+                       int32_t* expert_counts, moe_aux* aux, void* ws, size_t* ws_bytes,
+                       hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -35,6 +35,7 @@ class MoeConfig(ctypes.Structure):
         ("capacity_factor", ctypes.c_double),
         ("add_residual", ctypes.c_int32),
         ("weight_format", ctypes.c_int32),
+        ("router_temperature", ctypes.c_float),
     ]
 
 
@@ -53,6 +54,9 @@ class MoeAux(ctypes.Structure):
         ("n_dropped", ctypes.c_int64),
         ("capacity", ctypes.c_int64),
         ("n_kept", ctypes.c_int64),
+        ("lb_squares", ctypes.c_double),
+        ("kl_uniform", ctypes.c_double),
+        ("freq_penalty", ctypes.c_double),
     ]
 
 
@@ -79,13 +83,13 @@ def lib():
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_status_string.argtypes = [ctypes.c_int]
     sigs = {
-        "moe_route": [cfgp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "moe_route": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_permute": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_expert_ffn": [cfgp, i32, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_expert_ffn_int8": [cfgp, i32, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_combine": [cfgp, vp, vp, vp, vp, vp, vp, vp],
         "moe_aux_stats": [cfgp, vp, vp, vp, ctypes.c_size_t, vp, vp],
-        "moe_forward": [cfgp, ctypes.POINTER(MoeWeights), vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "moe_forward": [cfgp, ctypes.POINTER(MoeWeights), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)

@@ -21,23 +21,24 @@ _TORCH_DT = {_lib.MOE_DTYPE_F32: torch.float32, _lib.MOE_DTYPE_BF16: torch.bfloa
 
 
 def make_config(T, d, E, k, f, S=0, dtype="bf16", act="swiglu", capacity_factor=0.0,
-                add_residual=False, weights="act") -> MoeConfig:
+                add_residual=False, weights="act", temperature=1.0) -> MoeConfig:
     return MoeConfig(
         n_tokens=int(T), d_model=int(d), n_experts=int(E), top_k=int(k), d_ffn=int(f),
         n_shared=int(S),
         dtype=_lib.MOE_DTYPE_BF16 if dtype == "bf16" else _lib.MOE_DTYPE_F32,
         act=_lib.MOE_ACT_SWIGLU if act == "swiglu" else _lib.MOE_ACT_GELU,
         capacity_factor=float(capacity_factor), add_residual=int(bool(add_residual)),
-        weight_format=_lib.MOE_WEIGHTS_INT8 if weights == "int8" else _lib.MOE_WEIGHTS_ACT)
+        weight_format=_lib.MOE_WEIGHTS_INT8 if weights == "int8" else _lib.MOE_WEIGHTS_ACT,
+        router_temperature=float(temperature))
 
 
 def config_of(layer) -> MoeConfig:
     """MoeConfig from any object with T, d, E, k, f, S, dtype, act,
     capacity_factor and add_residual attributes (and optionally weights:
-    "act" or "int8")."""
+    "act" or "int8", and router_temperature)."""
     return make_config(layer.T, layer.d, layer.E, layer.k, layer.f, layer.S, layer.dtype,
                        layer.act, layer.capacity_factor, layer.add_residual,
-                       getattr(layer, "weights", "act"))
+                       getattr(layer, "weights", "act"), getattr(layer, "router_temperature", 1.0))
 
 
 def torch_dtype(cfg: MoeConfig) -> torch.dtype:
@@ -67,15 +68,15 @@ def _f32(*shape):
 # ---------------------------------------------------------------------------
 
 
-def moe_route(cfg: MoeConfig, x, w_router, router_bias=None):
+def moe_route(cfg: MoeConfig, x, w_router, router_bias=None, router_noise=None):
     """Returns (topk_idx [T,k] i32, topk_w [T,k] f32, token_lse [T] f32, route_ws)."""
     L = lib()
     T, k = cfg.n_tokens, cfg.top_k
     idx, w, lse = _i32(T, k), _f32(T, k), _f32(T)
 
     def q(ws, nb):
-        return L.moe_route(ctypes.byref(cfg), _p(x), _p(w_router), _p(router_bias), _p(idx), _p(w),
-                           _p(lse), ws, nb, _stream())
+        return L.moe_route(ctypes.byref(cfg), _p(x), _p(w_router), _p(router_bias),
+                           _p(router_noise), _p(idx), _p(w), _p(lse), ws, nb, _stream())
     q.__name__ = "moe_route"
     n = ctypes.c_size_t(0)
     check("moe_route", q(None, ctypes.byref(n)))
@@ -217,24 +218,26 @@ class Forward:
         self.aux = new_aux() if want_aux else None
         n = ctypes.c_size_t(0)
         check("moe_forward", lib().moe_forward(ctypes.byref(cfg), ctypes.byref(self._w), None, None,
-                                               None, None, None, None, None, ctypes.byref(n), None))
+                                               None, None, None, None, None, None, ctypes.byref(n),
+                                               None))
         self.ws_bytes = int(n.value)
         self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=_dev())
 
-    def __call__(self, x):
+    def __call__(self, x, router_noise=None):
         n = ctypes.c_size_t(self.ws.numel())
         check("moe_forward", lib().moe_forward(
-            ctypes.byref(self.cfg), ctypes.byref(self._w), _p(x), _p(self.y), _p(self.topk_idx),
+            ctypes.byref(self.cfg), ctypes.byref(self._w), _p(x), _p(router_noise), _p(self.y),
+            _p(self.topk_idx),
             _p(self.topk_w), _p(self.expert_counts), _p(self.aux), _p(self.ws), ctypes.byref(n),
             _stream()))
         return self.y
 
 
-def moe_forward(cfg: MoeConfig, weights: LayerWeights, x):
+def moe_forward(cfg: MoeConfig, weights: LayerWeights, x, router_noise=None):
     """One-shot forward: returns (y, extras dict with topk_idx, topk_w,
     expert_counts, aux (decoded after a synchronise))."""
     f = Forward(cfg, weights)
-    y = f(x)
+    y = f(x, router_noise)
     torch.cuda.synchronize()
     return y, {"topk_idx": f.topk_idx, "topk_w": f.topk_w, "expert_counts": f.expert_counts,
                "aux": aux_to_dict(f.aux)}

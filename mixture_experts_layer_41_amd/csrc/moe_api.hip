@@ -37,6 +37,15 @@ int64_t route_blocks(const moe_config& c) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
+// The router's score modifiers; temperature 0 means 1.
+RouterMod router_mod(const moe_config& c, const float* bias, const float* noise) {
+  RouterMod m;
+  m.bias = bias;
+  m.noise = noise;
+  m.inv_tau = c.router_temperature == 0.f ? 1.f : 1.f / c.router_temperature;
+  return m;
+}
+
 moe_status check_config(const moe_config* c) {
   if (c == nullptr) return MOE_ERR_INVALID_ARG;
   if (c->n_tokens < 1 || c->d_model < 8 || c->d_ffn < 8 || c->n_experts < 1 || c->top_k < 1 ||
@@ -49,6 +58,10 @@ moe_status check_config(const moe_config* c) {
   if (c->add_residual != 0 && c->add_residual != 1) return MOE_ERR_INVALID_ARG;
   if (std::isnan(c->capacity_factor) || std::isinf(c->capacity_factor) ||
       c->capacity_factor > 1073741824.0)
+    return MOE_ERR_INVALID_ARG;
+  if (c->router_temperature != 0.f &&
+      !(c->router_temperature > 0.f && std::isfinite(c->router_temperature) &&
+        std::isfinite(1.f / c->router_temperature)))
     return MOE_ERR_INVALID_ARG;
   if (c->d_model % 8 != 0 || c->d_ffn % 8 != 0) return MOE_ERR_UNSUPPORTED;
   if (c->n_experts > kMaxExperts || c->n_shared > 64) return MOE_ERR_UNSUPPORTED;
@@ -137,19 +150,21 @@ const char* moe_status_string(moe_status s) {
 }
 
 moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
-                     const float* router_bias, int32_t* topk_idx, float* topk_w,
-                     float* token_lse, void* ws, size_t* ws_bytes, hipStream_t stream) {
+                     const float* router_bias, const float* router_noise, int32_t* topk_idx,
+                     float* topk_w, float* token_lse, void* ws, size_t* ws_bytes,
+                     hipStream_t stream) {
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
   const RouteWs plan = plan_route(*cfg, nullptr);
   if (ws != nullptr) {
     if (!x || !w_router || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
-    if (!aligned16(x) || !aligned16(w_router)) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w_router) || !aligned4(router_noise)) return MOE_ERR_INVALID_ARG;
   }
   st = ws_check(ws, ws_bytes, plan.bytes);
   if (st != MOE_OK || ws == nullptr) return st;
   const RouteWs r = plan_route(*cfg, ws);
-  MOE_HIP_TRY(launch_router(*cfg, x, w_router, router_bias, topk_idx, topk_w, token_lse, r.st, stream));
+  MOE_HIP_TRY(launch_router(*cfg, x, w_router, router_mod(*cfg, router_bias, router_noise), topk_idx,
+                            topk_w, token_lse, r.st, stream));
   return MOE_OK;
 }
 
@@ -306,9 +321,10 @@ moe_status moe_aux_stats(const moe_config* cfg, const int32_t* expert_counts,
   return MOE_OK;
 }
 
-moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* x, void* y,
-                       int32_t* topk_idx, float* topk_w, int32_t* expert_counts, moe_aux* aux,
-                       void* ws, size_t* ws_bytes, hipStream_t stream) {
+moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* x,
+                       const float* router_noise, void* y, int32_t* topk_idx, float* topk_w,
+                       int32_t* expert_counts, moe_aux* aux, void* ws, size_t* ws_bytes,
+                       hipStream_t stream) {
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
   const moe_config& c = *cfg;
@@ -351,6 +367,7 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
   if (ws != nullptr) {
     if (!w || !x || !y || !w->w_router || !w->w1 || !w->w2) return MOE_ERR_INVALID_ARG;
     if (S > 0 && (!w->shared_w1 || !w->shared_w2)) return MOE_ERR_INVALID_ARG;
+    if (!aligned4(router_noise)) return MOE_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(y) || !aligned16(w->w_router) || !aligned16(w->w1) ||
         !aligned16(w->w2) || (S > 0 && (!aligned16(w->shared_w1) || !aligned16(w->shared_w2))))
       return MOE_ERR_INVALID_ARG;
@@ -371,7 +388,8 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
   const int64_t cap = exact_capacity(c);
   const bool q8 = c.weight_format == MOE_WEIGHTS_INT8;
 
-  MOE_HIP_TRY(launch_router(c, x, w->w_router, w->router_bias, p.idx, p.wts, nullptr, p.rs, stream));
+  MOE_HIP_TRY(launch_router(c, x, w->w_router, router_mod(c, w->router_bias, router_noise), p.idx,
+                            p.wts, nullptr, p.rs, stream));
   MOE_HIP_TRY(launch_permute(c, p.rs, p.po, cap, p.idx, nullptr, nullptr, nullptr, aux, p.scratch,
                              stream));
 

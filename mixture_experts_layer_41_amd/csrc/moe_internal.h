@@ -93,10 +93,18 @@ struct GemmDesc {
 // ---------------------------------------------------------------------------
 // launchers (each returns hipGetLastError() of its launch)
 
+// What turns the router's logits into its scores:
+//   s[t, e] = (logit[t, e] + bias[e]) * inv_tau + noise[t, e]
+struct RouterMod {
+  const float* bias;   // [E] or null
+  const float* noise;  // [T, E] or null
+  float inv_tau;       // 1 / temperature
+};
+
 // Bytes of RouteStats::logit_part the router needs (0: no K split).
 size_t router_scratch_bytes(const moe_config& c);
 hipError_t launch_router(const moe_config& c, const void* x, const void* w_router,
-                         const float* router_bias, int32_t* topk_idx, float* topk_w,
+                         const RouterMod& mod, int32_t* topk_idx, float* topk_w,
                          float* token_lse, const RouteStats& st, hipStream_t s);
 
 hipError_t launch_histogram(const moe_config& c, const int32_t* topk_idx, const RouteStats& st,

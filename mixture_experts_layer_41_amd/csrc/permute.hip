@@ -119,6 +119,56 @@ __device__ void block_sum4(int64_t& i0, int64_t& i1, double& f0, double& f1, int
   __syncthreads();
 }
 
+// Three float64 block-wide sums at once, in the same fixed order as
+// block_sum4.
+__device__ void block_sum3(double& f0, double& f1, double& f2, double* red) {
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    f0 += __shfl_xor(f0, o);
+    f1 += __shfl_xor(f1, o);
+    f2 += __shfl_xor(f2, o);
+  }
+  const int wave = threadIdx.x / kWave, nw = kThreads / kWave;
+  if (threadIdx.x % kWave == 0) {
+    red[wave] = f0;
+    red[nw + wave] = f1;
+    red[2 * nw + wave] = f2;
+  }
+  __syncthreads();
+  f0 = red[0];
+  f1 = red[nw];
+  f2 = red[2 * nw];
+  for (int w = 1; w < nw; ++w) {
+    f0 += red[w];
+    f1 += red[nw + w];
+    f2 += red[2 * nw + w];
+  }
+  __syncthreads();
+}
+
+// Per-expert terms of the other load-balance forms ([P3 §3.1] E sum P^2;
+// [P2 §4.2] KL(uniform || P) with 1e-8 in the logarithm, and the squared
+// distance of the selection shares f from 1/E), added to sq, lg, fq.
+__device__ __forceinline__ void lb_form_terms(double f, double P, int E, double& sq, double& lg,
+                                              double& fq) {
+  sq += P * P;
+  lg += log(P + 1e-8);
+  const double df = f - 1.0 / (double)E;
+  fq += df * df;
+}
+
+// Writes the float64 statistics of the aux record from the block-summed
+// parts (lbp = sum f P, lgp = sum ln(P + 1e-8), ...).
+__device__ __forceinline__ void write_lb_forms(moe_aux* aux, int E, double lbp, double z,
+                                               double sqp, double lgp, double fqp) {
+  const double lb = lbp * (double)E;
+  aux->load_balance = lb;
+  aux->z_loss = z;
+  aux->weighted = 0.01 * lb + 0.001 * z;
+  aux->lb_squares = (double)E * sqp;
+  aux->kl_uniform = log(1.0 / (double)E) - lgp / (double)E;
+  aux->freq_penalty = fqp;
+}
+
 // One workgroup per expert e: rank bases base[b][e] = sum_{b' < b} cnt[b'][e],
 // total[e], pe[e] = sum_b psum[b][e] (float64, fixed order); workgroup 0 also
 // sums the lse^2 partials and the invalid-index counts.
@@ -392,34 +442,38 @@ scatter_kernel(ScatterArgs a) {
         for (int64_t b = tid + (int64_t)kSumReg * kThreads; b < a.nb; b += kThreads) my_bad += a.bad[b];
     }
     // lb = E * sum_e f_e P_e with f_e = total_e / (T k), P_e = sum_t p / T
-    double lbp = 0.0, zp = 0.0;
+    double lbp = 0.0, zp = 0.0, sqp = 0.0, lgp = 0.0, fqp = 0.0;
     if (a.aux) {
       if (SMALL) {
         // P_e was summed with the counts: G = 256 / E threads per expert
         // over interleaved blocks, the G partials added in order (E > 256:
         // one thread per expert, blocks in order)
-        for (int e = tid; e < E; e += kThreads)
-          lbp += ((double)tot[e] / (double)(a.T * a.k)) * (Pe[e] / (double)a.T);
+        for (int e = tid; e < E; e += kThreads) {
+          const double fe = (double)tot[e] / (double)(a.T * a.k), P = Pe[e] / (double)a.T;
+          lbp += fe * P;
+          lb_form_terms(fe, P, E, sqp, lgp, fqp);
+        }
 #pragma unroll
         for (int u = 0; u < kSumReg; ++u)
           zp += tid + (int64_t)u * kThreads < a.nb ? (double)zv[u] : 0.0;
         for (int64_t b = tid + (int64_t)kSumReg * kThreads; b < a.nb; b += kThreads)
           zp += (double)a.zsum[b];
       } else {
-        for (int e = tid; e < E; e += kThreads)
-          lbp += ((double)tot[e] / (double)(a.T * a.k)) * (a.pe[e] / (double)a.T);
+        for (int e = tid; e < E; e += kThreads) {
+          const double fe = (double)tot[e] / (double)(a.T * a.k), P = a.pe[e] / (double)a.T;
+          lbp += fe * P;
+          lb_form_terms(fe, P, E, sqp, lgp, fqp);
+        }
       }
     }
     block_sum4(my_drop, my_bad, lbp, zp, ired, red);
+    if (a.aux) block_sum3(sqp, lgp, fqp, red);
     const int64_t dropped = my_drop;
     const int64_t nbd = SMALL ? my_bad : (int64_t)*a.nbad;
     if (tid == 0) a.n_dropped[0] = nbd ? -1 : (int32_t)dropped;
     if (a.aux && tid == 0) {
-      const double lb = lbp * (double)E;
       const double z = (SMALL ? zp : *a.zs) / (double)a.T;
-      a.aux->load_balance = lb;
-      a.aux->z_loss = z;
-      a.aux->weighted = 0.01 * lb + 0.001 * z;
+      write_lb_forms(a.aux, E, lbp, z, sqp, lgp, fqp);
       a.aux->n_dropped = dropped;
       a.aux->capacity = a.cap;
       a.aux->n_kept = a.T * a.k - dropped;
@@ -493,20 +547,22 @@ aux_kernel(int64_t T, int k, int E, int64_t nb, int64_t cap, const float* __rest
            const float* __restrict__ zsum, const int32_t* __restrict__ counts,
            const int32_t* __restrict__ n_dropped, moe_aux* __restrict__ aux) {
   __shared__ double red[kThreads];
-  double lbp = 0.0, zp = 0.0;
+  double lbp = 0.0, zp = 0.0, sqp = 0.0, lgp = 0.0, fqp = 0.0;
   for (int e = threadIdx.x; e < E; e += kThreads) {
     double P = 0.0;
     for (int64_t b = 0; b < nb; ++b) P += (double)psum[b * E + e];
-    lbp += ((double)counts[e] / (double)(T * k)) * (P / (double)T);
+    const double fe = (double)counts[e] / (double)(T * k);
+    P /= (double)T;
+    lbp += fe * P;
+    lb_form_terms(fe, P, E, sqp, lgp, fqp);
   }
   for (int64_t b = threadIdx.x; b < nb; b += kThreads) zp += (double)zsum[b];
-  const double lb = block_sum_f64(lbp, red) * (double)E;
+  const double lbs = block_sum_f64(lbp, red);
   const double z = block_sum_f64(zp, red) / (double)T;
+  block_sum3(sqp, lgp, fqp, red);
   if (threadIdx.x == 0) {
     const int64_t dropped = n_dropped[0];
-    aux->load_balance = lb;
-    aux->z_loss = z;
-    aux->weighted = 0.01 * lb + 0.001 * z;
+    write_lb_forms(aux, E, lbs, z, sqp, lgp, fqp);
     aux->n_dropped = dropped;
     aux->capacity = cap;
     aux->n_kept = T * k - dropped;

@@ -21,12 +21,26 @@
 //  * selection: 256 / BT lanes per token, each holding its share of the
 //    token's logits as order keys in registers; max, sum of exponentials
 //    and each of the k picks end in DPP reductions inside that lane group.
+//  * scores: everything after the logits GEMM sees
+//    s = (logit + bias) / tau + noise ([P2 §5.1] temperature scaling,
+//    [P2 §2.2] noise added before the top-k); with tau = 1 and no noise these
+//    are the logits plus bias, bit for bit.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
+
+// Score of token t (global index; rows past T only fill tile padding and
+// read no noise) for expert e from its summed logit v.
+__device__ __forceinline__ float router_score(float v, const RouterMod& m, int64_t t, int64_t T,
+                                              int E, int e) {
+  v += m.bias ? m.bias[e] : 0.f;
+  v *= m.inv_tau;
+  if (m.noise && t < T) v += m.noise[t * E + e];
+  return v;
+}
 
 __host__ __device__ inline int round_up(int a, int b) { return (a + b - 1) / b * b; }
 
@@ -326,7 +340,7 @@ __device__ void select_and_stats_any(float* lg, int ep, int BT, int nvalid, int 
 template <int DT, int TPW>
 __global__ void __launch_bounds__(kThreads)
 router_kernel(const void* __restrict__ x, const void* __restrict__ wr,
-              const float* __restrict__ rbias, int64_t T, int d, int E, int k,
+              const RouterMod mod, int64_t T, int d, int E, int k,
               int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
               float* __restrict__ token_lse, int32_t* __restrict__ st_cnt,
               float* __restrict__ st_psum, float* __restrict__ st_zsum) {
@@ -353,7 +367,7 @@ router_kernel(const void* __restrict__ x, const void* __restrict__ wr,
     const int r = o / E, e = o % E;
     float v = lg[r * (ep + 1) + e];
     for (int q = 1; q < s.nks; ++q) v += part[(q * BT + r) * (ep + 1) + e];
-    lg[r * (ep + 1) + e] = v + (rbias ? rbias[e] : 0.f);
+    lg[r * (ep + 1) + e] = router_score(v, mod, t0 + r, T, E, e);
   }
   __syncthreads();
 
@@ -416,7 +430,7 @@ __host__ __device__ inline int router2_smem_bytes(const Router2Shape& s) {
 template <int TPW>
 __global__ void __launch_bounds__(kThreads)
 router_bf16_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
-                   const float* __restrict__ rbias, int64_t T, int d, int E, int k,
+                   const RouterMod mod, int64_t T, int d, int E, int k,
                    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
                    float* __restrict__ token_lse, int32_t* __restrict__ st_cnt,
                    float* __restrict__ st_psum, float* __restrict__ st_zsum,
@@ -549,7 +563,7 @@ router_bf16_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
     const int r = o / E, e = o % E;
     float v = lg[r * (ep + 1) + e];
     for (int q = 1; q < s.nks; ++q) v += part[(q * BT + r) * (ep + 1) + e];
-    lg[r * (ep + 1) + e] = v + (rbias ? rbias[e] : 0.f);
+    lg[r * (ep + 1) + e] = router_score(v, mod, t0 + r, T, E, e);
   }
   __syncthreads();
   select_and_stats_t<(4 * TPW < 64 ? 4 * TPW : 64)>(lg, ep, BT, nvalid, E, k, t0, blk, topk_idx,
@@ -559,7 +573,7 @@ router_bf16_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
 
 // Selection after a K-split logits pass: the splits are added in split order.
 __global__ void __launch_bounds__(kThreads)
-router_select_kernel(const float* __restrict__ part_in, int nsplit, const float* __restrict__ rbias,
+router_select_kernel(const float* __restrict__ part_in, int nsplit, const RouterMod mod,
                      int64_t T, int E, int k, int32_t* __restrict__ topk_idx,
                      float* __restrict__ topk_w, float* __restrict__ token_lse,
                      int32_t* __restrict__ st_cnt, float* __restrict__ st_psum,
@@ -600,7 +614,7 @@ router_select_kernel(const float* __restrict__ part_in, int nsplit, const float*
       const int o = o0 + threadIdx.x + i * kThreads;
       if (o < n) {
         const int r = o / E, e = o % E;
-        lg[r * (ep + 1) + e] = v[i] + (rbias ? rbias[e] : 0.f);
+        lg[r * (ep + 1) + e] = router_score(v[i], mod, t0 + r, T, E, e);
       }
     }
   }
@@ -611,7 +625,7 @@ router_select_kernel(const float* __restrict__ part_in, int nsplit, const float*
 
 template <int DT, int TPW>
 hipError_t router_launch_t(const moe_config& c, const void* x, const void* w_router,
-                           const float* router_bias, int32_t* topk_idx, float* topk_w,
+                           const RouterMod& mod, int32_t* topk_idx, float* topk_w,
                            float* token_lse, const RouteStats& st, hipStream_t s) {
   const RouterShape sh = router_shape(c.n_tokens, c.n_experts, DT == MOE_DTYPE_BF16);
   const int64_t nb = (c.n_tokens + sh.BT - 1) / sh.BT;
@@ -623,14 +637,14 @@ hipError_t router_launch_t(const moe_config& c, const void* x, const void* w_rou
     if (e != hipSuccess) return e;
   }
   fn<<<dim3((unsigned)nb), dim3(kThreads), smem, s>>>(
-      x, w_router, router_bias, c.n_tokens, c.d_model, c.n_experts, c.top_k, topk_idx, topk_w,
+      x, w_router, mod, c.n_tokens, c.d_model, c.n_experts, c.top_k, topk_idx, topk_w,
       token_lse, st.cnt, st.psum, st.zsum);
   return hipGetLastError();
 }
 
 template <int TPW>
 hipError_t router_bf16_launch(const moe_config& c, const void* x, const void* w_router,
-                              const float* router_bias, int32_t* topk_idx, float* topk_w,
+                              const RouterMod& mod, int32_t* topk_idx, float* topk_w,
                               float* token_lse, const RouteStats& st, hipStream_t s) {
   const Router2Shape sh = router2_shape(c.n_tokens, c.n_experts, c.d_model);
   const int64_t nb = (c.n_tokens + sh.BT - 1) / sh.BT;
@@ -642,14 +656,14 @@ hipError_t router_bf16_launch(const moe_config& c, const void* x, const void* w_
     if (e != hipSuccess) return e;
   }
   fn<<<dim3((unsigned)nb, (unsigned)sh.ks), dim3(kThreads), smem, s>>>(
-      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router), router_bias,
+      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router), mod,
       c.n_tokens, c.d_model, c.n_experts, c.top_k, topk_idx, topk_w, token_lse, st.cnt, st.psum,
       st.zsum, st.logit_part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sh.ks == 1) return e;
   const int ssmem = sh.BT * (sh.ep + 1) * 4 + sh.ep * 4 + sh.BT * 4;
   router_select_kernel<<<dim3((unsigned)nb), dim3(kThreads), ssmem, s>>>(
-      st.logit_part, sh.ks, router_bias, c.n_tokens, c.n_experts, c.top_k, topk_idx, topk_w,
+      st.logit_part, sh.ks, mod, c.n_tokens, c.n_experts, c.top_k, topk_idx, topk_w,
       token_lse, st.cnt, st.psum, st.zsum);
   return hipGetLastError();
 }
@@ -663,17 +677,17 @@ size_t router_scratch_bytes(const moe_config& c) {
 }
 
 hipError_t launch_router(const moe_config& c, const void* x, const void* w_router,
-                         const float* router_bias, int32_t* topk_idx, float* topk_w,
+                         const RouterMod& mod, int32_t* topk_idx, float* topk_w,
                          float* token_lse, const RouteStats& st, hipStream_t s) {
   if (c.dtype == MOE_DTYPE_F32)
-    return router_launch_t<MOE_DTYPE_F32, 1>(c, x, w_router, router_bias, topk_idx, topk_w,
+    return router_launch_t<MOE_DTYPE_F32, 1>(c, x, w_router, mod, topk_idx, topk_w,
                                              token_lse, st, s);
   const Router2Shape sh2 = router2_shape(c.n_tokens, c.n_experts, c.d_model);
   if (sh2.ks > 1) {
     // decode-sized batch: K split over workgroups, then the selection
 #define MOE_ROUTER2_CASE(N) \
     if (sh2.tpw <= N)       \
-      return router_bf16_launch<N>(c, x, w_router, router_bias, topk_idx, topk_w, token_lse, st, s);
+      return router_bf16_launch<N>(c, x, w_router, mod, topk_idx, topk_w, token_lse, st, s);
     MOE_ROUTER2_CASE(1)
     MOE_ROUTER2_CASE(2)
     MOE_ROUTER2_CASE(4)
@@ -686,7 +700,7 @@ hipError_t launch_router(const moe_config& c, const void* x, const void* w_route
   const int tpw = router_shape(c.n_tokens, c.n_experts, true).tiles_per_wave;
 #define MOE_ROUTER_CASE(N) \
   if (tpw <= N)            \
-    return router_launch_t<MOE_DTYPE_BF16, N>(c, x, w_router, router_bias, topk_idx, topk_w, token_lse, st, s);
+    return router_launch_t<MOE_DTYPE_BF16, N>(c, x, w_router, mod, topk_idx, topk_w, token_lse, st, s);
   MOE_ROUTER_CASE(1)
   MOE_ROUTER_CASE(2)
   MOE_ROUTER_CASE(4)

@@ -91,6 +91,10 @@ CONFIGS = {
     # the same layer with 8-bit expert weights (row-scaled INT8 codes)
     "c5q": LayerConfig("decode_int8w_T128_d7168_E256_k8_S1_f2048", T=128, d=7168, E=256,
                        k=8, f=2048, S=1, weights="int8", seed=1006),
+    # the "Flash" layer with router temperature 1.5 and Gaussian router noise (std 1)
+    "c2n": LayerConfig("flash_bf16_T4096_d512_E16_k2_f1024_cf1.25_tau1.5_noise1", T=4096, d=512,
+                       E=16, k=2, f=1024, capacity_factor=1.25, router_temperature=1.5,
+                       router_noise_std=1.0, seed=1007),
 }
 
 

@@ -67,12 +67,13 @@ def test_status_strings(L):
 def query(L, fn, c):
     n = ctypes.c_size_t(0)
     if fn == "route":
-        st = L.moe_route(ctypes.byref(c), None, None, None, None, None, None, None, ctypes.byref(n), None)
+        st = L.moe_route(ctypes.byref(c), None, None, None, None, None, None, None, None,
+                         ctypes.byref(n), None)
     elif fn == "permute":
         st = L.moe_permute(ctypes.byref(c), None, None, None, None, None, None, None, None, None,
                            None, None, ctypes.byref(n), None)
     elif fn == "forward":
-        st = L.moe_forward(ctypes.byref(c), None, None, None, None, None, None, None, None,
+        st = L.moe_forward(ctypes.byref(c), None, None, None, None, None, None, None, None, None,
                            ctypes.byref(n), None)
     else:
         st = L.moe_expert_ffn(ctypes.byref(c), c.n_experts, 1, c.n_tokens * c.top_k, None, None,
@@ -103,6 +104,9 @@ def test_forward_workspace_covers_its_buffers(L):
     dict(n_shared=-1), dict(dtype=7), dict(act=4), dict(capacity_factor=math.nan),
     dict(capacity_factor=math.inf), dict(capacity_factor=2.0 ** 31), dict(weight_format=2),
     dict(add_residual=2), dict(d_model=4),
+    # router temperature: 0 means 1; otherwise finite, positive, 1/tau finite
+    dict(router_temperature=-1.0), dict(router_temperature=math.nan),
+    dict(router_temperature=math.inf), dict(router_temperature=1e-45),
 ])
 def test_invalid_config(L, bad):
     for fn in ("route", "permute", "forward", "ffn"):
@@ -122,11 +126,30 @@ def test_unsupported_config(L, bad):
         assert query(L, fn, cfg(**bad))[0] == UNSUPPORTED, (fn, bad)
 
 
+@pytest.mark.parametrize("tau", [0.0, 1.0, 0.25, 1.5, 1e4])
+def test_valid_temperatures(L, tau):
+    for fn in ("route", "permute", "forward", "ffn"):
+        assert query(L, fn, cfg(router_temperature=tau))[0] == OK, (fn, tau)
+
+
+def test_misaligned_router_noise(L):
+    c = cfg()
+    st, need = query(L, "route", c)
+    n = ctypes.c_size_t(need)
+    assert L.moe_route(ctypes.byref(c), P, P, None, P + 2, P, P, None, P, ctypes.byref(n),
+                       None) == INVALID
+    st, need = query(L, "forward", c)
+    m = ctypes.c_size_t(need)
+    w = _lib.MoeWeights(w_router=P, w1=P, w2=P)
+    assert L.moe_forward(ctypes.byref(c), ctypes.byref(w), P, P + 2, P, None, None, None, None, P,
+                         ctypes.byref(m), None) == INVALID
+
+
 def test_null_config_and_null_size(L):
     n = ctypes.c_size_t(0)
-    assert L.moe_route(None, None, None, None, None, None, None, None, ctypes.byref(n), None) == INVALID
+    assert L.moe_route(None, None, None, None, None, None, None, None, None, ctypes.byref(n), None) == INVALID
     c = cfg()
-    assert L.moe_route(ctypes.byref(c), None, None, None, None, None, None, None, None, None) == INVALID
+    assert L.moe_route(ctypes.byref(c), None, None, None, None, None, None, None, None, None, None) == INVALID
 
 
 def test_small_workspace_reports_the_size(L):
@@ -134,7 +157,7 @@ def test_small_workspace_reports_the_size(L):
     st, need = query(L, "route", c)
     assert st == OK
     n = ctypes.c_size_t(need - 1)
-    st = L.moe_route(ctypes.byref(c), P, P, None, P, P, None, P, ctypes.byref(n), None)
+    st = L.moe_route(ctypes.byref(c), P, P, None, None, P, P, None, P, ctypes.byref(n), None)
     assert st == WORKSPACE and n.value == need
 
 
@@ -143,11 +166,11 @@ def test_misaligned_pointers(L):
     st, need = query(L, "route", c)
     n = ctypes.c_size_t(need)
     # x not 16-byte aligned
-    assert L.moe_route(ctypes.byref(c), P + 2, P, None, P, P, None, P, ctypes.byref(n), None) == INVALID
+    assert L.moe_route(ctypes.byref(c), P + 2, P, None, None, P, P, None, P, ctypes.byref(n), None) == INVALID
     # workspace not 16-byte aligned
-    assert L.moe_route(ctypes.byref(c), P, P, None, P, P, None, P + 8, ctypes.byref(n), None) == INVALID
+    assert L.moe_route(ctypes.byref(c), P, P, None, None, P, P, None, P + 8, ctypes.byref(n), None) == INVALID
     # missing outputs
-    assert L.moe_route(ctypes.byref(c), P, P, None, None, P, None, P, ctypes.byref(n), None) == INVALID
+    assert L.moe_route(ctypes.byref(c), P, P, None, None, None, P, None, P, ctypes.byref(n), None) == INVALID
     assert L.moe_combine(ctypes.byref(c), P, P, P, None, None, P + 4, None) == INVALID
     assert L.moe_combine(ctypes.byref(c), P, None, P, None, None, P, None) == INVALID
 
@@ -220,7 +243,7 @@ def test_int8_forward_needs_scales(L):
     n = ctypes.c_size_t(0)
     w = _lib.MoeWeights(w_router=P, w1=P, w2=P, shared_w1=P, shared_w2=P, w1_scale=P, w2_scale=P,
                         shared_w1_scale=P, shared_w2_scale=P)
-    st = L.moe_forward(ctypes.byref(c8), ctypes.byref(w), None, None, None, None, None, None, None,
+    st = L.moe_forward(ctypes.byref(c8), ctypes.byref(w), None, None, None, None, None, None, None, None,
                        ctypes.byref(n), None)
     assert st == OK and n.value > 0
     m = ctypes.c_size_t(n.value)
@@ -228,5 +251,5 @@ def test_int8_forward_needs_scales(L):
         w2 = _lib.MoeWeights(w_router=P, w1=P, w2=P, shared_w1=P, shared_w2=P, w1_scale=P,
                              w2_scale=P, shared_w1_scale=P, shared_w2_scale=P)
         setattr(w2, missing, None)
-        assert L.moe_forward(ctypes.byref(c8), ctypes.byref(w2), P, P, None, None, None, None, P,
+        assert L.moe_forward(ctypes.byref(c8), ctypes.byref(w2), P, None, P, None, None, None, None, P,
                              ctypes.byref(m), None) == INVALID, missing

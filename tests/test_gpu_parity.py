@@ -27,6 +27,12 @@ pytestmark = pytest.mark.gpu
 W_RTOL = 1e-5
 LSE_RTOL = 1e-5
 AUX_RTOL = 1e-5
+# kl_uniform = ln(1/E) - mean_e ln(P_e + 1e-8): P_e carries the float32
+# probabilities' relative error (~1e-6), so the logarithms, and kl, carry
+# about that much absolute error whatever kl's size (it is ~0 for balanced
+# routing).  freq_penalty comes from the integer counts: exact up to the
+# float64 summation order.
+KL_ATOL = 1e-5
 
 
 def say(*a):
@@ -82,6 +88,9 @@ def check_aux(aux, o):
     assert abs(aux["weighted"] - o["weighted"]) <= AUX_RTOL * abs(o["weighted"])
     assert aux["n_dropped"] == o["n_dropped"]
     assert aux["capacity"] == (-1 if o["capacity"] is None else o["capacity"])
+    assert abs(aux["lb_squares"] - o["lb_squares"]) <= AUX_RTOL * abs(o["lb_squares"])
+    assert abs(aux["kl_uniform"] - o["kl_uniform"]) <= KL_ATOL, (aux["kl_uniform"], o["kl_uniform"])
+    assert abs(aux["freq_penalty"] - o["freq_penalty"]) <= 1e-12 + 1e-9 * o["freq_penalty"]
 
 
 # ---------------------------------------------------------------------------
@@ -189,7 +198,8 @@ def test_small_shapes_all_steps(row):
 # the named workloads at full size: routing, permutation and aux in full;
 # the output on all tokens (small layers) or on sampled tokens (large ones)
 
-FULL = {"c1": None, "c2": None, "c3": 512, "c4": 96, "c4cap": 96, "c5": 6, "c5q": 6}
+FULL = {"c1": None, "c2": None, "c2n": None, "c3": 512, "c4": 96, "c4cap": 96, "c5": 6,
+        "c5q": 6}
 LAZY = ("c5", "c5q")  # expert weights generated one expert at a time
 
 
@@ -210,9 +220,10 @@ def test_named_workload_full_size(name):
     say(f"[oracle] {name}")
     o = run_oracle(cfg, t, rows=rows)
     x = to_dev(t["x"], cfg.dtype)
+    noise = to_dev(t.get("router_noise"), "f32")
     F = B.Forward(c, W)
     say(f"[forward] {name}")
-    y = F(x)
+    y = F(x, noise)
     torch.cuda.synchronize()
     check_routing(cfg, o, F.topk_idx, F.topk_w)
     assert np.array_equal(F.expert_counts.cpu().numpy(), o["counts"])
@@ -284,3 +295,49 @@ def test_int8_weights_small(row):
     check_routing(cfg, o, F.topk_idx, F.topk_w)
     check_aux(B.aux_to_dict(F.aux), o)
     say(f"[ok] {name} y_err={err:.2e}")
+
+
+# ---------------------------------------------------------------------------
+# router temperature and noise: the scores are logits / tau + noise
+
+VARIANTS = [
+    # name, T, d, E, k, f, S, dtype, tau, noise std, router bias, cf
+    ("f32_tau_half", 150, 32, 8, 2, 32, 0, "f32", 0.5, 0.0, "none", 0.0),
+    ("f32_tau2_noise", 200, 48, 10, 3, 32, 1, "f32", 2.0, 0.5, "zipf", 0.0),
+    ("bf16_noise_cap", 700, 128, 16, 2, 128, 0, "bf16", 1.0, 1.0, "none", 1.0),
+    ("bf16_tau1.5_noise_E64", 1200, 256, 64, 6, 64, 2, "bf16", 1.5, 1.0, "zipf", 0.0),
+    # decode-sized: the router's K split and separate selection kernel
+    ("bf16_decode_tau_noise", 64, 2048, 128, 8, 128, 1, "bf16", 1.5, 1.0, "none", 0.0),
+]
+
+
+@pytest.mark.parametrize("row", VARIANTS, ids=[r[0] for r in VARIANTS])
+def test_router_temperature_and_noise(row):
+    (name, T, d, E, k, f, S, dt, tau, sd, rb, cf) = row
+    cfg = LayerConfig(name, T=T, d=d, E=E, k=k, f=f, S=S, dtype=dt, act="swiglu",
+                      capacity_factor=cf, router_bias=rb, router_temperature=tau,
+                      router_noise_std=sd, seed=800 + VARIANTS.index(row))
+    say(f"[case] {name} T={T} d={d} E={E} k={k} tau={tau} noise={sd}")
+    t = inputs(cfg)
+    o = run_oracle(cfg, t)
+    c = B.config_of(cfg)
+    W = weights_to_dev(cfg, t)
+    x = to_dev(t["x"], cfg.dtype)
+    noise = to_dev(t["router_noise"], "f32")
+
+    idx, w, lse, route_ws = B.moe_route(c, x, W.w_router, W.router_bias, noise)
+    torch.cuda.synchronize()
+    check_routing(cfg, o, idx, w, lse)
+    pr = B.moe_permute(c, idx, w)
+    aux = B.aux_to_dict(B.moe_aux_stats(c, pr["expert_counts"], pr["n_dropped"], route_ws))
+    check_permutation(o, pr, T, k, idx)
+    check_aux(aux, o)
+
+    F = B.Forward(c, W)
+    y = F(x, noise)
+    torch.cuda.synchronize()
+    check_routing(cfg, o, F.topk_idx, F.topk_w)
+    check_aux(B.aux_to_dict(F.aux), o)
+    err = normwise(from_dev(y), o["y"])
+    assert err <= tol_for(cfg), f"forward normwise err {err:.3e}"
+    say(f"[ok] {name} y_err={err:.2e} kl={aux['kl_uniform']:.3e} freq={aux['freq_penalty']:.3e}")
