@@ -43,6 +43,10 @@ the design notes):
   * router temperature and noise ([P2 §5.1], [P2 §2.2]): the scores are
     logits / tau + noise, tau dividing the router output with its bias and
     the caller's noise added after; everything downstream uses the scores.
+  * backward ([P3 §4.2] trains on loss = task + aux; [P5 §2] coefficients
+    0.01 / 0.001): the gradient of sum(dy * y) + aux_scale * (0.01 lb +
+    0.001 z); top-k selection, capacity drops and the shares f_e carry no
+    gradient (they are piecewise constant).
   * the other load-balance forms ([P3 §3.1] E * sum P^2; [P2 §4.2] KL of
     the uniform distribution from P, with 1e-8 in the logarithm, plus the
     squared distance of the hard frequencies from 1/E) use the same P and f
@@ -79,6 +83,8 @@ __all__ = [
     "aux_losses",
     "router_gap_ok",
     "forward",
+    "expert_ffn_backward",
+    "backward",
 ]
 
 
@@ -470,3 +476,163 @@ def forward(cfg, t, rows=None, want_routed_rows=False):
         "freq_penalty": aux["freq_penalty"],
         "rows": tok, "y": y, "shared_y": shared, "routed_rows": routed_rows,
     }
+
+
+# ---------------------------------------------------------------------------
+# backward pass: the gradient of the training loss the pages use,
+# loss = task + aux ([P3 §4.2] adds the auxiliary loss to the main loss and
+# back-propagates both; [P5 §2] weights load balance 0.01 and z-loss 0.001).
+# The task loss enters through dy = dLoss/dy; the aux part is
+# aux_scale * (0.01 lb + 0.001 z).  Top-k selection, capacity drops and the
+# selection shares f_e are piecewise constant: no gradient flows through them.
+
+
+def _gelu_grad(z):
+    """d/dz gelu(z) = Phi(z) + z phi(z) (exact GELU)."""
+    erf = np.vectorize(math.erf, otypes=[np.float64])
+    Phi = 0.5 * (1.0 + erf(z / math.sqrt(2.0)))
+    phi = np.exp(-0.5 * z * z) / math.sqrt(2.0 * math.pi)
+    return Phi + z * phi
+
+
+def _silu_grad(z):
+    """d/dz silu(z) = s (1 + z (1 - s)), s = 1 / (1 + exp(-z))."""
+    s = 1.0 / (1.0 + np.exp(-z))
+    return s * (1.0 + z * (1.0 - s))
+
+
+def expert_ffn_backward(x_rows, w1, b1, w2, b2, act: str, d_out):
+    """Gradients of one expert on a block of rows, given d_out = dL/d out.
+
+    Recomputes the pre-activations a = x W1^T (+ b1) and h = act(a), then
+      dW2 = d_out^T h, db2 = sum_rows d_out, dh = d_out W2,
+      da = dh * act'(a)   (SwiGLU: dg = dh u silu'(g), du = dh silu(g)),
+      dW1 = da^T x, db1 = sum_rows da, dx = da W1.
+    Returns (dx, dW1, db1, dW2, db2) in float64.
+    """
+    a = x_rows @ w1.T
+    if b1 is not None:
+        a = a + b1[None, :]
+    if act == "gelu":
+        h = _gelu(a)
+    elif act == "swiglu":
+        f = w1.shape[0] // 2
+        g, u = a[:, :f], a[:, f:]
+        h = _silu(g) * u
+    else:
+        raise ValueError(f"unknown activation {act!r}")
+    dW2 = d_out.T @ h
+    db2 = d_out.sum(axis=0)
+    dh = d_out @ w2
+    if act == "gelu":
+        da = dh * _gelu_grad(a)
+    else:
+        da = np.concatenate([dh * u * _silu_grad(g), dh * _silu(g)], axis=1)
+    dW1 = da.T @ x_rows
+    db1 = da.sum(axis=0)
+    dx = da @ w1
+    return dx, dW1, db1, dW2, db2
+
+
+def backward(cfg, t, dy, aux_scale: float = 1.0):
+    """Gradients of  sum(dy * y) + aux_scale * (0.01 lb + 0.001 z)  with
+    respect to x and every parameter (float64), for activation-dtype
+    expert weights.
+
+    dy: [T, d] upstream gradient of the layer output.
+    Returns a dict: dx [T, d], dw_router [E, d], drouter_bias [E],
+    dw1 [E, w1_rows, d], db1 [E, w1_rows], dw2 [E, d, f], db2 [E, d], and for
+    S > 0 dws1 / dsb1 / dws2 / dsb2 of the same shapes per shared expert; plus
+    dtopk_w [T, k] (the gradient reaching the routing weights) and
+    dscores [T, E] (the gradient of the router scores).
+
+    Steps, in the forward's reverse order:
+      combine    y_t = sum_j w_tj o_tj + sum_s FFN_s(x_t) (+ x_t):
+                 d o_tj = w_tj dy_t for kept slots, dw_tj = dy_t . o_tj;
+      experts    expert_ffn_backward on each expert's kept rows, dx of the
+                 rows added back to their tokens; shared experts on all
+                 tokens with d out = dy; the residual passes dy to dx;
+      renorm     w_j = p_j / P with P the sum of the k selected p:
+                 dp_m = (dw_m - sum_j dw_j w_j) / P for selected m, else 0;
+      aux        d lb / d p_te = E f_e / T;  d z / d s_te = 2 lse_t p_te / T;
+      softmax    ds_te = p_te (dp_te - sum_e' p_te' dp_te');
+      scores     s = (x W_r^T + b) / tau + noise:  dl = ds / tau,
+                 dW_r = dl^T x, db = sum_t dl, dx += dl W_r.
+    """
+    dt = cfg.dtype
+    if getattr(cfg, "weights", "act") != "act":
+        raise ValueError("the backward takes activation-dtype expert weights")
+    x = decode(t["x"], dt)
+    T, d = x.shape
+    E, k = cfg.E, cfg.k
+    dy = np.asarray(dy, dtype=np.float64)
+    wr = decode(t["w_router"], dt)
+    rb = t.get("router_bias")
+    rb = None if rb is None else np.asarray(rb, dtype=np.float32).astype(np.float64)
+    tau = float(getattr(cfg, "router_temperature", 1.0))
+    s = router_scores(router_logits(x, wr, rb), tau, t.get("router_noise"))
+    p, lse = softmax_lse(s)
+    idx = topk_select(p, k)
+    w = renormalise(p, idx)
+    counts = expert_counts(idx, E)
+    cap = capacity(cfg.capacity_factor, T, k, E)
+    offsets, perm_token, perm_slot, inv_row, _ = dispatch(idx, E, cap)
+
+    dx = np.zeros((T, d))
+    dw = np.zeros((T, k))
+    g = {}
+    b1s, b2s = t.get("b1"), t.get("b2")
+    w1_0 = decode(t["w1"][0], dt)
+    g["dw1"] = np.zeros((E,) + w1_0.shape)
+    g["db1"] = np.zeros((E, w1_0.shape[0]))
+    g["dw2"] = np.zeros((E, d, cfg.f))
+    g["db2"] = np.zeros((E, d))
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r0 == r1:
+            continue
+        toks, slots = perm_token[r0:r1], perm_slot[r0:r1]
+        w1 = decode(t["w1"][e], dt)
+        w2 = decode(t["w2"][e], dt)
+        b1 = None if b1s is None else decode(b1s[e], dt)
+        b2 = None if b2s is None else decode(b2s[e], dt)
+        out = expert_ffn(x[toks], w1, b1, w2, b2, cfg.act)
+        dw[toks, slots] = np.sum(dy[toks] * out, axis=1)
+        d_out = w[toks, slots][:, None] * dy[toks]
+        dxe, g["dw1"][e], g["db1"][e], g["dw2"][e], g["db2"][e] = expert_ffn_backward(
+            x[toks], w1, b1, w2, b2, cfg.act, d_out)
+        np.add.at(dx, toks, dxe)
+
+    if cfg.S > 0:
+        sb1s, sb2s = t.get("sb1"), t.get("sb2")
+        ws1_0 = decode(t["ws1"][0], dt)
+        g["dws1"] = np.zeros((cfg.S,) + ws1_0.shape)
+        g["dsb1"] = np.zeros((cfg.S, ws1_0.shape[0]))
+        g["dws2"] = np.zeros((cfg.S, d, cfg.f))
+        g["dsb2"] = np.zeros((cfg.S, d))
+        for si in range(cfg.S):
+            dxs, g["dws1"][si], g["dsb1"][si], g["dws2"][si], g["dsb2"][si] = expert_ffn_backward(
+                x, decode(t["ws1"][si], dt), None if sb1s is None else decode(sb1s[si], dt),
+                decode(t["ws2"][si], dt), None if sb2s is None else decode(sb2s[si], dt), cfg.act, dy)
+            dx += dxs
+    if cfg.add_residual:
+        dx += dy
+
+    # routing weights -> probabilities (renormalisation), aux, softmax
+    sel = np.take_along_axis(p, idx, axis=1)
+    P = sel.sum(axis=1, keepdims=True)
+    dp = np.zeros((T, E))
+    dsel = (dw - np.sum(dw * w, axis=1, keepdims=True)) / P
+    np.put_along_axis(dp, idx, dsel, axis=1)
+    f_share = counts.astype(np.float64) / float(T * k)
+    dp += aux_scale * 0.01 * E * f_share[None, :] / T
+    ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+    ds += aux_scale * 0.001 * 2.0 * lse[:, None] * p / T
+    dl = ds / tau
+    g["dw_router"] = dl.T @ x
+    g["drouter_bias"] = dl.sum(axis=0)
+    dx += dl @ wr
+    g["dx"] = dx
+    g["dtopk_w"] = dw
+    g["dscores"] = ds
+    return g

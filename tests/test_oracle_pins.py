@@ -701,3 +701,161 @@ def test_frequency_penalty_with_top2():
     o = oracle.forward(cfg, t)
     assert o["counts"].tolist() == [2, 1, 1, 0]
     assert abs(o["freq_penalty"] - 0.125) < 1e-15
+
+
+# ---------------------------------------------------------------------------
+# backward pass ([P3 §4.2] loss = task + aux; [P5 §2] coefficients)
+
+
+@dataclass
+class BCfg(TCfg):
+    weights: str = "act"
+
+
+def _loss(cfg, t, dy, aux_scale):
+    o = oracle.forward(cfg, t)
+    return float(np.sum(dy * o["y"])) + aux_scale * o["weighted"], o["topk_idx"]
+
+
+def _stable_tensors(cfg, seed, **kw):
+    """Random tensors whose k-th / (k+1)-th probability gap is wide enough
+    that a 2^-10 perturbation cannot change the selection."""
+    for s in range(seed, seed + 200):
+        t = rand_tensors(cfg, s, **kw)
+        ok = oracle.router_gap_ok(t["x"], t["w_router"], t.get("router_bias"), cfg.k, "f32",
+                                  gap=0.03, temperature=cfg.router_temperature,
+                                  noise=t.get("router_noise"))
+        if ok.all():
+            return t
+    raise RuntimeError("no stable draw")
+
+
+FD_CASES = [
+    # act, S, bias, residual, cf, tau, noise
+    ("swiglu", 1, False, True, 0.0, 1.0, False),
+    ("gelu", 1, True, False, 0.0, 1.5, True),
+    ("swiglu", 2, True, False, 0.75, 0.8, True),
+]
+
+
+@pytest.mark.parametrize("case", FD_CASES, ids=["swiglu_shared_res", "gelu_bias_tau_noise",
+                                                "swiglu_cap_shared2"])
+def test_backward_central_differences(case):
+    """Every gradient entry against a central difference of the forward loss
+    sum(dy * y) + 2.5 (0.01 lb + 0.001 z), step 2^-10 (exact on float32)."""
+    act, S, bias, res, cf, tau, noise = case
+    cfg = BCfg(T=6, d=4, E=4, k=2, f=3, S=S, act=act, capacity_factor=cf, add_residual=res,
+               router_temperature=tau)
+    t = _stable_tensors(cfg, 60, bias=bias, router_bias=np.array([0.25, 0, -0.5, 0]))
+    if bias:
+        r = np.random.default_rng(11)
+        t["sb1"] = f32(r.standard_normal(t["ws1"].shape[:2]) * 0.1)
+        t["sb2"] = f32(r.standard_normal((S, cfg.d)) * 0.1)
+    if noise:
+        t["router_noise"] = f32(np.random.default_rng(7).standard_normal((cfg.T, cfg.E)) * 0.5)
+        t = dict(t)
+    dy = np.random.default_rng(8).standard_normal((cfg.T, cfg.d))
+    aux = 2.5
+    g = oracle.backward(cfg, t, dy, aux)
+    _, idx0 = _loss(cfg, t, dy, aux)
+    h = 2.0 ** -10
+    names = [("x", "dx"), ("w_router", "dw_router"), ("router_bias", "drouter_bias"),
+             ("w1", "dw1"), ("w2", "dw2"), ("ws1", "dws1"), ("ws2", "dws2")]
+    if bias:
+        names += [("b1", "db1"), ("b2", "db2"), ("sb1", "dsb1"), ("sb2", "dsb2")]
+    checked = 0
+    for src, key in names:
+        a = t.get(src)
+        if a is None:
+            continue
+        ref = g[key]
+        for i in np.ndindex(a.shape):
+            orig = a[i]
+            a[i] = orig + np.float32(h)
+            lp, ip = _loss(cfg, t, dy, aux)
+            a[i] = orig - np.float32(h)
+            lm, im = _loss(cfg, t, dy, aux)
+            a[i] = orig
+            assert np.array_equal(ip, idx0) and np.array_equal(im, idx0)
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - ref[i]) <= 2e-5 * (1 + abs(ref[i])), (key, i, fd, ref[i])
+            checked += 1
+    assert checked > 150
+
+
+def _torch_layer_loss(cfg, tt, dy, aux_scale):
+    """The layer written with torch float64 ops, in the loop form of the pages
+    (mask / gather / run / weight / add): router, softmax, torch.topk of the
+    probabilities, renormalise, capacity by token order, experts, shared
+    experts, residual, and the aux terms."""
+    x, wr = tt["x"], tt["w_router"]
+    T, E, k = x.shape[0], cfg.E, cfg.k
+    logits = x @ wr.T
+    if tt.get("router_bias") is not None:
+        logits = logits + tt["router_bias"]
+    s = logits / cfg.router_temperature
+    if tt.get("router_noise") is not None:
+        s = s + tt["router_noise"]
+    p = torch.softmax(s, dim=-1)
+    lse = torch.logsumexp(s, dim=-1)
+    topv, topi = torch.topk(p, k, dim=-1)
+    w = topv / topv.sum(-1, keepdim=True)
+
+    def ffn(xr, w1, b1, w2, b2):
+        a = xr @ w1.T + (0 if b1 is None else b1)
+        if cfg.act == "gelu":
+            h = F.gelu(a)
+        else:
+            f = w1.shape[0] // 2
+            h = F.silu(a[:, :f]) * a[:, f:]
+        return h @ w2.T + (0 if b2 is None else b2)
+
+    cap = oracle.capacity(cfg.capacity_factor, T, k, E)
+    seen = [0] * E
+    y = torch.zeros_like(x)
+    for t_ in range(T):
+        for j in range(k):
+            e = int(topi[t_, j])
+            seen[e] += 1
+            if cap is not None and seen[e] > cap:
+                continue
+            b1 = None if tt.get("b1") is None else tt["b1"][e]
+            b2 = None if tt.get("b2") is None else tt["b2"][e]
+            y[t_] = y[t_] + w[t_, j] * ffn(x[t_:t_ + 1], tt["w1"][e], b1, tt["w2"][e], b2)[0]
+    for si in range(cfg.S):
+        sb1 = None if tt.get("sb1") is None else tt["sb1"][si]
+        sb2 = None if tt.get("sb2") is None else tt["sb2"][si]
+        y = y + ffn(x, tt["ws1"][si], sb1, tt["ws2"][si], sb2)
+    if cfg.add_residual:
+        y = y + x
+    counts = torch.zeros(E, dtype=torch.float64)
+    for e in topi.reshape(-1).tolist():
+        counts[e] += 1
+    lb = E * torch.sum(counts / (T * k) * p.mean(0))
+    z = torch.mean(lse * lse)
+    return torch.sum(torch.as_tensor(dy) * y) + aux_scale * (0.01 * lb + 0.001 * z)
+
+
+def test_backward_matches_torch_autograd():
+    cfg = BCfg(T=40, d=8, E=6, k=2, f=5, S=2, act="swiglu", capacity_factor=1.0,
+               add_residual=True, router_temperature=1.5)
+    t = rand_tensors(cfg, 300, bias=True, router_bias=np.linspace(-1, 1, 6))
+    t["router_noise"] = f32(np.random.default_rng(9).standard_normal((cfg.T, cfg.E)) * 0.3)
+    r = np.random.default_rng(11)
+    t["sb1"] = f32(r.standard_normal(t["ws1"].shape[:2]) * 0.1)
+    t["sb2"] = f32(r.standard_normal((cfg.S, cfg.d)) * 0.1)
+    dy = np.random.default_rng(10).standard_normal((cfg.T, cfg.d))
+    g = oracle.backward(cfg, t, dy, 4.0)
+    assert g["dw1"].shape == (6, 10, 8)
+    keys = {"x": "dx", "w_router": "dw_router", "router_bias": "drouter_bias", "w1": "dw1",
+            "b1": "db1", "w2": "dw2", "b2": "db2", "ws1": "dws1", "sb1": "dsb1", "ws2": "dws2",
+            "sb2": "dsb2"}
+    tt = {}
+    for name in list(keys) + ["router_noise"]:
+        if t.get(name) is not None:
+            tt[name] = torch.tensor(np.asarray(t[name], np.float64), requires_grad=name in keys)
+    loss = _torch_layer_loss(cfg, tt, dy, 4.0)
+    loss.backward()
+    for name, key in keys.items():
+        ref = tt[name].grad.numpy()
+        assert np.allclose(g[key], ref, rtol=1e-10, atol=1e-12), key
