@@ -276,6 +276,81 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
                        int32_t* expert_counts, moe_aux* aux, void* ws, size_t* ws_bytes,
                        hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Training: the forward with the state the backward needs, and the backward
+ * ([P3 §4.2] trains on loss = task loss + auxiliary loss and back-propagates
+ * both; [P5 §2] weights load balance 0.01 and z-loss 0.001).
+ */
+
+/* Forward state kept for the backward: device buffers the caller owns, all
+ * required.  scores [T,E] float32 (s of moe_route), token_lse [T] float32,
+ * topk_idx [T,k] int32, topk_w [T,k] float32, expert_counts [E] int32,
+ * expert_offsets [E+1] int32, perm_token [T*k] int32, inv_row [T*k] int32,
+ * y_perm [T*k, d] act dtype (each kept row's expert output). */
+typedef struct {
+  float* scores;
+  float* token_lse;
+  int32_t* topk_idx;
+  float* topk_w;
+  int32_t* expert_counts;
+  int32_t* expert_offsets;
+  int32_t* perm_token;
+  int32_t* inv_row;
+  void* y_perm;
+} moe_saved;
+
+/* Gradients written by moe_backward (device buffers the caller owns; each is
+ * overwritten, not accumulated).  dx [T,d] act dtype and dw_router [E,d]
+ * float32 are required; drouter_bias [E] may be NULL.  Expert weight
+ * gradients are float32 in the weights' layouts: dw1 [E, 2f|f, d],
+ * dw2 [E, d, f] required; db1 [E, 2f|f] and db2 [E, d] required iff the
+ * layer has b1 / b2.  With S > 0: dws1 [S, 2f|f, d] and dws2 [S, d, f]
+ * required, dsb1 / dsb2 iff the shared biases exist. */
+typedef struct {
+  void* dx;
+  float* dw_router;
+  float* drouter_bias;
+  float* dw1;
+  float* db1;
+  float* dw2;
+  float* db2;
+  float* dws1;
+  float* dsb1;
+  float* dws2;
+  float* dsb2;
+} moe_grads;
+
+/*
+ * moe_forward_train - moe_forward that also fills `saved` for moe_backward.
+ * Arguments as moe_forward; saved (host struct of device pointers) is
+ * required.  BF16 activations with activation-dtype expert weights only
+ * (else MOE_ERR_UNSUPPORTED).
+ */
+moe_status moe_forward_train(const moe_config* cfg, const moe_weights* w, const void* x,
+                             const float* router_noise, void* y, const moe_saved* saved,
+                             moe_aux* aux, void* ws, size_t* ws_bytes, hipStream_t stream);
+
+/*
+ * moe_backward - gradients of  L = sum(dy * y) + aux_scale * (0.01 lb +
+ * 0.001 z)  with respect to x and every parameter, for the forward that
+ * filled `saved` (same cfg, weights, x and router noise).  Top-k
+ * selection, capacity drops and the selection shares f_e pass no gradient.
+ *   combine: d o_tj = w_tj dy_t (kept slots), dw_tj = dy_t . o_tj;
+ *   experts: a = x W1^T + b1 recomputed; dW2 = d o^T act(a), dh = d o W2,
+ *            da = dh * act'(a), dW1 = da^T x, dx += da W1 (rows added back
+ *            to their tokens); shared experts with d o = dy; residual: dx += dy;
+ *   router:  renormalisation, aux terms (d lb / d p_te = E f_e / T,
+ *            d z / d s_te = 2 lse_t p_te / T), softmax, then / tau:
+ *            dW_r = dl^T x, d bias = sum_t dl, dx += dl W_r.
+ * x, dy [T,d] act dtype.  Precision: bf16 operands with float32
+ * accumulation; d o, a, dh, da and act(a) are stored as bf16 between the
+ * steps.  BF16 activation-dtype weights only (else UNSUPPORTED); NULL
+ * required buffers: INVALID_ARG.  ws: query with ws == NULL.
+ */
+moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void* x,
+                        const moe_saved* saved, const void* dy, double aux_scale,
+                        const moe_grads* g, void* ws, size_t* ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

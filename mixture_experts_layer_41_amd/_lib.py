@@ -19,7 +19,8 @@ MOE_WEIGHTS_ACT, MOE_WEIGHTS_INT8 = 0, 1
 
 # every symbol include/moe.h declares
 EXPORTS = ("moe_status_string", "moe_route", "moe_permute", "moe_expert_ffn",
-           "moe_expert_ffn_int8", "moe_combine", "moe_aux_stats", "moe_forward")
+           "moe_expert_ffn_int8", "moe_combine", "moe_aux_stats", "moe_forward",
+           "moe_forward_train", "moe_backward")
 
 
 class MoeConfig(ctypes.Structure):
@@ -60,6 +61,18 @@ class MoeAux(ctypes.Structure):
     ]
 
 
+class MoeSaved(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "scores", "token_lse", "topk_idx", "topk_w", "expert_counts", "expert_offsets",
+        "perm_token", "inv_row", "y_perm")]
+
+
+class MoeGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "dx", "dw_router", "drouter_bias", "dw1", "db1", "dw2", "db2", "dws1", "dsb1", "dws2",
+        "dsb2")]
+
+
 class MoeError(RuntimeError):
     def __init__(self, fn: str, status: int, text: str):
         super().__init__(f"{fn}: {text} (status {status})")
@@ -90,6 +103,10 @@ def lib():
         "moe_combine": [cfgp, vp, vp, vp, vp, vp, vp, vp],
         "moe_aux_stats": [cfgp, vp, vp, vp, ctypes.c_size_t, vp, vp],
         "moe_forward": [cfgp, ctypes.POINTER(MoeWeights), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "moe_forward_train": [cfgp, ctypes.POINTER(MoeWeights), vp, vp, vp, ctypes.POINTER(MoeSaved),
+                              vp, vp, sz, vp],
+        "moe_backward": [cfgp, ctypes.POINTER(MoeWeights), vp, ctypes.POINTER(MoeSaved), vp,
+                         ctypes.c_double, ctypes.POINTER(MoeGrads), vp, sz, vp],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)

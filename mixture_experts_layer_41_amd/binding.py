@@ -15,7 +15,7 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from ._lib import MoeAux, MoeConfig, MoeWeights, check, lib
+from ._lib import MoeAux, MoeConfig, MoeGrads, MoeSaved, MoeWeights, check, lib
 
 _TORCH_DT = {_lib.MOE_DTYPE_F32: torch.float32, _lib.MOE_DTYPE_BF16: torch.bfloat16}
 
@@ -241,3 +241,76 @@ def moe_forward(cfg: MoeConfig, weights: LayerWeights, x, router_noise=None):
     torch.cuda.synchronize()
     return y, {"topk_idx": f.topk_idx, "topk_w": f.topk_w, "expert_counts": f.expert_counts,
                "aux": aux_to_dict(f.aux)}
+
+
+# ---------------------------------------------------------------------------
+# training: forward with saved state, then the backward
+
+
+class TrainStep:
+    """moe_forward_train + moe_backward with their buffers allocated once.
+
+    forward(x, router_noise=None) -> y; backward(dy, aux_scale=1.0) -> dict
+    of gradient tensors (dx in the activation dtype, the rest float32), for
+    the x / noise of the last forward."""
+
+    def __init__(self, cfg: MoeConfig, weights: LayerWeights):
+        self.cfg = cfg
+        self.weights = weights
+        self._w = weights.c_struct()
+        T, k, E, d, f, S = cfg.n_tokens, cfg.top_k, cfg.n_experts, cfg.d_model, cfg.d_ffn, cfg.n_shared
+        w1r = 2 * f if cfg.act == _lib.MOE_ACT_SWIGLU else f
+        dt = torch_dtype(cfg)
+        dev = _dev()
+        self.saved = {
+            "scores": _f32(T, E), "token_lse": _f32(T), "topk_idx": _i32(T, k), "topk_w": _f32(T, k),
+            "expert_counts": _i32(E), "expert_offsets": _i32(E + 1), "perm_token": _i32(T * k),
+            "inv_row": _i32(T * k),
+            "y_perm": torch.empty(T * k, d, dtype=dt, device=dev),
+        }
+        self._s = MoeSaved(**{n: v.data_ptr() for n, v in self.saved.items()})
+        self.y = torch.empty(T, d, dtype=dt, device=dev)
+        self.aux = new_aux()
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.grads = {
+            "dx": torch.empty(T, d, dtype=dt, device=dev),
+            "dw_router": torch.empty(E, d, **f32),
+            "drouter_bias": torch.empty(E, **f32),
+            "dw1": torch.empty(E, w1r, d, **f32), "dw2": torch.empty(E, d, f, **f32),
+            "db1": torch.empty(E, w1r, **f32) if weights.b1 is not None else None,
+            "db2": torch.empty(E, d, **f32) if weights.b2 is not None else None,
+        }
+        if S:
+            self.grads.update({
+                "dws1": torch.empty(S, w1r, d, **f32), "dws2": torch.empty(S, d, f, **f32),
+                "dsb1": torch.empty(S, w1r, **f32) if weights.shared_b1 is not None else None,
+                "dsb2": torch.empty(S, d, **f32) if weights.shared_b2 is not None else None,
+            })
+        self._g = MoeGrads(**{n: (None if self.grads.get(n) is None else self.grads[n].data_ptr())
+                              for n, _ in MoeGrads._fields_})
+        L = lib()
+        n = ctypes.c_size_t(0)
+        check("moe_forward_train", L.moe_forward_train(ctypes.byref(cfg), ctypes.byref(self._w), None,
+                                                       None, None, None, None, None, ctypes.byref(n),
+                                                       None))
+        self.fws = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=dev)
+        m = ctypes.c_size_t(0)
+        check("moe_backward", L.moe_backward(ctypes.byref(cfg), ctypes.byref(self._w), None, None, None,
+                                             1.0, None, None, ctypes.byref(m), None))
+        self.bws = torch.empty(max(int(m.value), 1), dtype=torch.uint8, device=dev)
+        self.x = None
+
+    def forward(self, x, router_noise=None):
+        self.x = x
+        n = ctypes.c_size_t(self.fws.numel())
+        check("moe_forward_train", lib().moe_forward_train(
+            ctypes.byref(self.cfg), ctypes.byref(self._w), _p(x), _p(router_noise), _p(self.y),
+            ctypes.byref(self._s), _p(self.aux), _p(self.fws), ctypes.byref(n), _stream()))
+        return self.y
+
+    def backward(self, dy, aux_scale=1.0):
+        n = ctypes.c_size_t(self.bws.numel())
+        check("moe_backward", lib().moe_backward(
+            ctypes.byref(self.cfg), ctypes.byref(self._w), _p(self.x), ctypes.byref(self._s), _p(dy),
+            float(aux_scale), ctypes.byref(self._g), _p(self.bws), ctypes.byref(n), _stream()))
+        return self.grads

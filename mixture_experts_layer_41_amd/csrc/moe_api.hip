@@ -43,6 +43,7 @@ RouterMod router_mod(const moe_config& c, const float* bias, const float* noise)
   m.bias = bias;
   m.noise = noise;
   m.inv_tau = c.router_temperature == 0.f ? 1.f : 1.f / c.router_temperature;
+  m.scores_out = nullptr;
   return m;
 }
 
@@ -321,10 +322,14 @@ moe_status moe_aux_stats(const moe_config* cfg, const int32_t* expert_counts,
   return MOE_OK;
 }
 
-moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* x,
-                       const float* router_noise, void* y, int32_t* topk_idx, float* topk_w,
-                       int32_t* expert_counts, moe_aux* aux, void* ws, size_t* ws_bytes,
-                       hipStream_t stream) {
+// The forward of moe_forward and moe_forward_train (saved != null: the
+// routing results, scores, lse, permutation and expert outputs go to the
+// caller's buffers).
+static moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const void* x,
+                               const float* router_noise, void* y, int32_t* topk_idx,
+                               float* topk_w, int32_t* expert_counts, moe_aux* aux,
+                               const moe_saved* saved, void* ws, size_t* ws_bytes,
+                               hipStream_t stream) {
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
   const moe_config& c = *cfg;
@@ -385,11 +390,23 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
   if (topk_idx) p.idx = topk_idx;
   if (topk_w) p.wts = topk_w;
   if (expert_counts) p.po.counts = expert_counts;
+  RouterMod rm = router_mod(c, w->router_bias, router_noise);
+  float* lse_out = nullptr;
+  if (saved) {
+    p.idx = saved->topk_idx;
+    p.wts = saved->topk_w;
+    p.po.counts = saved->expert_counts;
+    p.po.offsets = saved->expert_offsets;
+    p.po.perm_token = saved->perm_token;
+    p.po.inv_row = saved->inv_row;
+    p.y_perm = saved->y_perm;
+    rm.scores_out = saved->scores;
+    lse_out = saved->token_lse;
+  }
   const int64_t cap = exact_capacity(c);
   const bool q8 = c.weight_format == MOE_WEIGHTS_INT8;
 
-  MOE_HIP_TRY(launch_router(c, x, w->w_router, router_mod(c, w->router_bias, router_noise), p.idx,
-                            p.wts, nullptr, p.rs, stream));
+  MOE_HIP_TRY(launch_router(c, x, w->w_router, rm, p.idx, p.wts, lse_out, p.rs, stream));
   MOE_HIP_TRY(launch_permute(c, p.rs, p.po, cap, p.idx, nullptr, nullptr, nullptr, aux, p.scratch,
                              stream));
 
@@ -451,6 +468,247 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
   }
   MOE_HIP_TRY(launch_combine(c, p.y_perm, p.po.inv_row, p.wts, p.shared_y,
                              c.add_residual ? x : nullptr, y, stream));
+  return MOE_OK;
+}
+
+moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* x,
+                       const float* router_noise, void* y, int32_t* topk_idx, float* topk_w,
+                       int32_t* expert_counts, moe_aux* aux, void* ws, size_t* ws_bytes,
+                       hipStream_t stream) {
+  return forward_impl(cfg, w, x, router_noise, y, topk_idx, topk_w, expert_counts, aux, nullptr, ws,
+                      ws_bytes, stream);
+}
+
+// Training needs bf16 activations and activation-dtype expert weights.
+static moe_status check_train(const moe_config* cfg) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->dtype != MOE_DTYPE_BF16 || cfg->weight_format != MOE_WEIGHTS_ACT)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+static bool saved_ok(const moe_saved* sv) {
+  return sv && sv->scores && sv->token_lse && sv->topk_idx && sv->topk_w && sv->expert_counts &&
+         sv->expert_offsets && sv->perm_token && sv->inv_row && sv->y_perm && aligned4(sv->scores) &&
+         aligned4(sv->token_lse) && aligned4(sv->topk_idx) && aligned4(sv->topk_w) &&
+         aligned4(sv->expert_counts) && aligned4(sv->expert_offsets) && aligned4(sv->perm_token) &&
+         aligned4(sv->inv_row) && aligned16(sv->y_perm);
+}
+
+moe_status moe_forward_train(const moe_config* cfg, const moe_weights* w, const void* x,
+                             const float* router_noise, void* y, const moe_saved* saved,
+                             moe_aux* aux, void* ws, size_t* ws_bytes, hipStream_t stream) {
+  moe_status st = check_train(cfg);
+  if (st != MOE_OK) return st;
+  if (ws != nullptr && !saved_ok(saved)) return MOE_ERR_INVALID_ARG;
+  return forward_impl(cfg, w, x, router_noise, y, nullptr, nullptr, nullptr, aux,
+                      ws != nullptr ? saved : nullptr, ws, ws_bytes, stream);
+}
+
+moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void* x,
+                        const moe_saved* sv, const void* dy, double aux_scale,
+                        const moe_grads* g, void* ws, size_t* ws_bytes, hipStream_t stream) {
+  moe_status st = check_train(cfg);
+  if (st != MOE_OK) return st;
+  if (!std::isfinite(aux_scale)) return MOE_ERR_INVALID_ARG;
+  const moe_config& c = *cfg;
+  const int64_t T = c.n_tokens, R = T * c.top_k;
+  const int E = c.n_experts, S = c.n_shared, d = c.d_model, f = c.d_ffn;
+  const int w1r = c.act == MOE_ACT_SWIGLU ? 2 * f : f;
+  constexpr int kPad = 64;  // K tile of the weight-gradient GEMM
+  const int64_t Rp = (R + (int64_t)kPad * E + kPad - 1) / kPad * kPad;  // padded columns, bound
+  const int64_t Tp = (T + kPad - 1) / kPad * kPad;
+  const int nsplit = simt_splits(E, d, T);
+
+  struct Plan {
+    void *dO, *A, *W2t, *W1t, *dH, *dA, *H, *dXr, *dOt, *Ht, *dAt, *Xt;
+    float *dw, *dl, *dxr, *wr_part;
+    int32_t *poff, *colrow;
+    void *As, *Ws2t, *Ws1t, *dHs, *dAs, *Hs, *dXs, *dyt, *Hst, *dAst, *xt;
+  };
+  auto plan = [&](void* base, Plan& p) {
+    Carver cv(base);
+    p.dO = cv.take<uint16_t>(R * d);
+    p.dw = cv.take<float>(R);
+    p.dl = cv.take<float>(T * E);
+    p.dxr = cv.take<float>(T * d);
+    p.wr_part = cv.take<float>(nsplit > 1 ? (size_t)nsplit * E * d : 0);
+    p.A = cv.take<uint16_t>(R * w1r);
+    p.W2t = cv.take<uint16_t>((size_t)E * f * d);
+    p.W1t = cv.take<uint16_t>((size_t)E * d * w1r);
+    p.dH = cv.take<uint16_t>(R * f);
+    p.dA = cv.take<uint16_t>(R * w1r);
+    p.H = cv.take<uint16_t>(R * f);
+    p.dXr = cv.take<uint16_t>(R * d);
+    p.poff = cv.take<int32_t>(E + 1);
+    p.colrow = cv.take<int32_t>(Rp);
+    p.dOt = cv.take<uint16_t>(d * Rp);
+    p.Ht = cv.take<uint16_t>(f * Rp);
+    p.dAt = cv.take<uint16_t>(w1r * Rp);
+    p.Xt = cv.take<uint16_t>(d * Rp);
+    if (S > 0) {
+      p.As = cv.take<uint16_t>(T * S * w1r);
+      p.Ws2t = cv.take<uint16_t>((size_t)S * f * d);
+      p.Ws1t = cv.take<uint16_t>((size_t)S * d * w1r);
+      p.dHs = cv.take<uint16_t>(T * S * f);
+      p.dAs = cv.take<uint16_t>(T * S * w1r);
+      p.Hs = cv.take<uint16_t>(T * S * f);
+      p.dXs = cv.take<uint16_t>(T * d);
+      p.dyt = cv.take<uint16_t>(d * Tp);
+      p.Hst = cv.take<uint16_t>(S * f * Tp);
+      p.dAst = cv.take<uint16_t>(S * w1r * Tp);
+      p.xt = cv.take<uint16_t>(d * Tp);
+    }
+    return cv.off;
+  };
+  Plan p{};
+  const size_t need = plan(nullptr, p);
+  if (ws != nullptr) {
+    if (!w || !x || !dy || !g || !saved_ok(sv) || !w->w_router || !w->w1 || !w->w2)
+      return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(dy) || !aligned16(w->w_router) || !aligned16(w->w1) ||
+        !aligned16(w->w2))
+      return MOE_ERR_INVALID_ARG;
+    if (!g->dx || !aligned16(g->dx) || !g->dw_router || !g->dw1 || !g->dw2 ||
+        (w->b1 && !g->db1) || (w->b2 && !g->db2))
+      return MOE_ERR_INVALID_ARG;
+    if (S > 0 && (!w->shared_w1 || !w->shared_w2 || !aligned16(w->shared_w1) ||
+                  !aligned16(w->shared_w2) || !g->dws1 || !g->dws2 ||
+                  (w->shared_b1 && !g->dsb1) || (w->shared_b2 && !g->dsb2)))
+      return MOE_ERR_INVALID_ARG;
+  }
+  st = ws_check(ws, ws_bytes, need);
+  if (st != MOE_OK || ws == nullptr) return st;
+  plan(ws, p);
+
+  // combine and router
+  MOE_HIP_TRY(launch_combine_bwd(c, dy, sv->y_perm, sv->inv_row, sv->topk_w, p.dO, p.dw, stream));
+  MOE_HIP_TRY(launch_router_grad(c, sv->scores, sv->token_lse, sv->topk_idx, sv->topk_w, p.dw,
+                                 sv->expert_counts, aux_scale, p.dl, stream));
+  MOE_HIP_TRY(launch_simt_gemm(p.dl, 1, E, x, d, E, d, T, nsplit, g->dw_router, d, p.wr_part,
+                               stream));
+  if (g->drouter_bias) MOE_HIP_TRY(launch_colsum_f32(p.dl, T, E, g->drouter_bias, stream));
+  MOE_HIP_TRY(launch_simt_gemm(p.dl, E, 1, w->w_router, d, (int)T, d, E, 1, p.dxr, d, nullptr,
+                               stream));
+
+  // routed experts: pre-activations, transposed weights, dh, da / h, dx rows
+  GemmDesc gd{};
+  gd.group_off = sv->expert_offsets;
+  gd.n_groups = E;
+  gd.n_seg = 1;
+  gd.rows_max = R;
+  gd.a = x;
+  gd.a_rows = sv->perm_token;
+  gd.lda = d;
+  gd.w = w->w1;
+  gd.bias = w->b1;
+  gd.d = w1r;  // N
+  gd.f = d;    // K
+  gd.out = p.A;
+  gd.ldo = w1r;
+  MOE_HIP_TRY(launch_gemm(c, kGemmDown, gd, stream));
+  MOE_HIP_TRY(launch_transpose(w->w2, f, (int64_t)d * f, nullptr, nullptr, d, d, f, p.W2t, d,
+                               (int64_t)f * d, E, stream));
+  MOE_HIP_TRY(launch_transpose(w->w1, d, (int64_t)w1r * d, nullptr, nullptr, w1r, w1r, d, p.W1t,
+                               w1r, (int64_t)d * w1r, E, stream));
+  gd.a = p.dO;
+  gd.a_rows = nullptr;
+  gd.lda = d;
+  gd.w = p.W2t;
+  gd.bias = nullptr;
+  gd.d = f;
+  gd.f = d;
+  gd.out = p.dH;
+  gd.ldo = f;
+  MOE_HIP_TRY(launch_gemm(c, kGemmDown, gd, stream));
+  MOE_HIP_TRY(launch_act_bwd(p.A, p.dH, sv->expert_offsets + E, R, 1, f, c.act, p.dA, p.H, stream));
+  gd.a = p.dA;
+  gd.lda = w1r;
+  gd.w = p.W1t;
+  gd.d = d;
+  gd.f = w1r;
+  gd.out = p.dXr;
+  gd.ldo = d;
+  MOE_HIP_TRY(launch_gemm(c, kGemmDown, gd, stream));
+
+  // weight gradients from the expert-padded transposes
+  MOE_HIP_TRY(launch_pad_offsets(sv->expert_offsets, E, kPad, Rp, p.poff, p.colrow, stream));
+  MOE_HIP_TRY(launch_transpose(p.dO, d, 0, p.colrow, nullptr, 0, Rp, d, p.dOt, Rp, 0, 1, stream));
+  MOE_HIP_TRY(launch_transpose(p.H, f, 0, p.colrow, nullptr, 0, Rp, f, p.Ht, Rp, 0, 1, stream));
+  MOE_HIP_TRY(launch_transpose(p.dA, w1r, 0, p.colrow, nullptr, 0, Rp, w1r, p.dAt, Rp, 0, 1, stream));
+  MOE_HIP_TRY(launch_transpose(x, d, 0, p.colrow, sv->perm_token, 0, Rp, d, p.Xt, Rp, 0, 1, stream));
+  MOE_HIP_TRY(launch_wgrad(p.dOt, Rp, 0, p.Ht, Rp, 0, p.poff, 0, d, f, E, g->dw2, f,
+                           (int64_t)d * f, stream));
+  MOE_HIP_TRY(launch_wgrad(p.dAt, Rp, 0, p.Xt, Rp, 0, p.poff, 0, w1r, d, E, g->dw1, d,
+                           (int64_t)w1r * d, stream));
+  if (w->b2) MOE_HIP_TRY(launch_seg_rowsum(p.dOt, Rp, d, p.poff, Rp, E, g->db2, d, stream));
+  if (w->b1) MOE_HIP_TRY(launch_seg_rowsum(p.dAt, Rp, w1r, p.poff, Rp, E, g->db1, w1r, stream));
+
+  // shared experts: every token, d o = dy
+  if (S > 0) {
+    GemmDesc sd{};
+    sd.group_off = nullptr;  // one dense group of T rows
+    sd.n_groups = 1;
+    sd.n_seg = 1;
+    sd.rows_max = T;
+    for (int s = 0; s < S; ++s) {
+      sd.a = x;
+      sd.a_rows = nullptr;
+      sd.lda = d;
+      sd.w = static_cast<const uint16_t*>(w->shared_w1) + (int64_t)s * w1r * d;
+      sd.bias = w->shared_b1 ? static_cast<const uint16_t*>(w->shared_b1) + (int64_t)s * w1r : nullptr;
+      sd.d = w1r;
+      sd.f = d;
+      sd.out = static_cast<uint16_t*>(p.As) + (int64_t)s * w1r;
+      sd.ldo = (int64_t)S * w1r;
+      MOE_HIP_TRY(launch_gemm(c, kGemmDown, sd, stream));
+    }
+    MOE_HIP_TRY(launch_transpose(w->shared_w2, f, (int64_t)d * f, nullptr, nullptr, d, d, f, p.Ws2t,
+                                 d, (int64_t)f * d, S, stream));
+    MOE_HIP_TRY(launch_transpose(w->shared_w1, d, (int64_t)w1r * d, nullptr, nullptr, w1r, w1r, d,
+                                 p.Ws1t, w1r, (int64_t)d * w1r, S, stream));
+    for (int s = 0; s < S; ++s) {
+      sd.a = dy;
+      sd.lda = d;
+      sd.w = static_cast<const uint16_t*>(p.Ws2t) + (int64_t)s * f * d;
+      sd.bias = nullptr;
+      sd.d = f;
+      sd.f = d;
+      sd.out = static_cast<uint16_t*>(p.dHs) + (int64_t)s * f;
+      sd.ldo = (int64_t)S * f;
+      MOE_HIP_TRY(launch_gemm(c, kGemmDown, sd, stream));
+    }
+    MOE_HIP_TRY(launch_act_bwd(p.As, p.dHs, nullptr, T, S, f, c.act, p.dAs, p.Hs, stream));
+    sd.a = p.dAs;
+    sd.lda = (int64_t)S * w1r;
+    sd.n_seg = S;
+    sd.w = p.Ws1t;
+    sd.d = d;
+    sd.f = w1r;
+    sd.out = p.dXs;
+    sd.ldo = d;
+    MOE_HIP_TRY(launch_gemm(c, kGemmDown, sd, stream));
+    MOE_HIP_TRY(launch_transpose(dy, d, 0, nullptr, nullptr, T, Tp, d, p.dyt, Tp, 0, 1, stream));
+    MOE_HIP_TRY(launch_transpose(p.Hs, (int64_t)S * f, 0, nullptr, nullptr, T, Tp, S * f, p.Hst, Tp,
+                                 0, 1, stream));
+    MOE_HIP_TRY(launch_transpose(p.dAs, (int64_t)S * w1r, 0, nullptr, nullptr, T, Tp, S * w1r,
+                                 p.dAst, Tp, 0, 1, stream));
+    MOE_HIP_TRY(launch_transpose(x, d, 0, nullptr, nullptr, T, Tp, d, p.xt, Tp, 0, 1, stream));
+    MOE_HIP_TRY(launch_wgrad(p.dyt, Tp, 0, p.Hst, Tp, (int64_t)f * Tp, nullptr, Tp, d, f, S, g->dws2,
+                             f, (int64_t)d * f, stream));
+    MOE_HIP_TRY(launch_wgrad(p.dAst, Tp, (int64_t)w1r * Tp, p.xt, Tp, 0, nullptr, Tp, w1r, d, S,
+                             g->dws1, d, (int64_t)w1r * d, stream));
+    if (w->shared_b2)
+      for (int s = 0; s < S; ++s)
+        MOE_HIP_TRY(launch_seg_rowsum(p.dyt, Tp, d, nullptr, Tp, 1, g->dsb2 + (int64_t)s * d, d,
+                                      stream));
+    if (w->shared_b1)
+      MOE_HIP_TRY(launch_seg_rowsum(p.dAst, Tp, S * w1r, nullptr, Tp, 1, g->dsb1, S * w1r, stream));
+  }
+
+  MOE_HIP_TRY(launch_dx_gather(c, p.dXr, sv->inv_row, S > 0 ? p.dXs : nullptr, p.dxr,
+                               c.add_residual ? dy : nullptr, g->dx, stream));
   return MOE_OK;
 }
 

@@ -99,6 +99,7 @@ struct RouterMod {
   const float* bias;   // [E] or null
   const float* noise;  // [T, E] or null
   float inv_tau;       // 1 / temperature
+  float* scores_out;   // [T, E] or null: the scores are also written here
 };
 
 // Bytes of RouteStats::logit_part the router needs (0: no K split).
@@ -126,5 +127,36 @@ hipError_t launch_gemm(const moe_config& c, GemmKind kind, const GemmDesc& g, hi
 hipError_t launch_combine(const moe_config& c, const void* y_perm, const int32_t* inv_row,
                           const float* topk_w, const void* shared_y, const void* residual,
                           void* y, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// backward pass (backward.hip, gemm_wgrad.hip); bf16 operands
+
+hipError_t launch_combine_bwd(const moe_config& c, const void* dy, const void* y_perm,
+                              const int32_t* inv_row, const float* topk_w, void* d_yperm,
+                              float* d_topk_w, hipStream_t s);
+hipError_t launch_router_grad(const moe_config& c, const float* scores, const float* lse,
+                              const int32_t* topk_idx, const float* topk_w, const float* d_topk_w,
+                              const int32_t* counts, double aux_scale, float* dl, hipStream_t s);
+hipError_t launch_pad_offsets(const int32_t* offsets, int G, int pad, int64_t ncols, int32_t* poff,
+                              int32_t* colrow, hipStream_t s);
+hipError_t launch_transpose(const void* src, int64_t src_ld, int64_t src_batch,
+                            const int32_t* colrow, const int32_t* gather, int64_t nsrc,
+                            int64_t ncols, int C, void* dst, int64_t dst_ld, int64_t dst_batch,
+                            int batches, hipStream_t s);
+hipError_t launch_act_bwd(const void* a, const void* dh, const int32_t* nrows_dev, int64_t nrows_host,
+                          int S, int f, int act, void* da, void* h, hipStream_t s);
+hipError_t launch_seg_rowsum(const void* m, int64_t ld, int C, const int32_t* poff, int64_t ncols,
+                             int G, float* out, int64_t out_ld, hipStream_t s);
+hipError_t launch_colsum_f32(const float* m, int64_t T, int E, float* out, hipStream_t s);
+hipError_t launch_dx_gather(const moe_config& c, const void* dx_rows, const int32_t* inv_row,
+                            const void* shared, const float* dx_router, const void* residual,
+                            void* dx, hipStream_t s);
+int simt_splits(int M, int N, int64_t K);
+hipError_t launch_simt_gemm(const float* a, int64_t sam, int64_t sak, const void* b, int64_t ldb,
+                            int M, int N, int64_t K, int nsplit, float* c, int64_t ldc,
+                            float* partial, hipStream_t s);
+hipError_t launch_wgrad(const void* a, int64_t lda, int64_t a_batch, const void* b, int64_t ldb,
+                        int64_t b_batch, const int32_t* kofs, int64_t K, int M, int N, int batches,
+                        float* c, int64_t ldc, int64_t c_batch, hipStream_t s);
 
 }  // namespace moe

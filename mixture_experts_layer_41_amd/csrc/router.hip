@@ -367,7 +367,9 @@ router_kernel(const void* __restrict__ x, const void* __restrict__ wr,
     const int r = o / E, e = o % E;
     float v = lg[r * (ep + 1) + e];
     for (int q = 1; q < s.nks; ++q) v += part[(q * BT + r) * (ep + 1) + e];
-    lg[r * (ep + 1) + e] = router_score(v, mod, t0 + r, T, E, e);
+    const float sc = router_score(v, mod, t0 + r, T, E, e);
+    lg[r * (ep + 1) + e] = sc;
+    if (mod.scores_out && t0 + r < T) mod.scores_out[(t0 + r) * E + e] = sc;
   }
   __syncthreads();
 
@@ -563,7 +565,9 @@ router_bf16_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
     const int r = o / E, e = o % E;
     float v = lg[r * (ep + 1) + e];
     for (int q = 1; q < s.nks; ++q) v += part[(q * BT + r) * (ep + 1) + e];
-    lg[r * (ep + 1) + e] = router_score(v, mod, t0 + r, T, E, e);
+    const float sc = router_score(v, mod, t0 + r, T, E, e);
+    lg[r * (ep + 1) + e] = sc;
+    if (mod.scores_out && t0 + r < T) mod.scores_out[(t0 + r) * E + e] = sc;
   }
   __syncthreads();
   select_and_stats_t<(4 * TPW < 64 ? 4 * TPW : 64)>(lg, ep, BT, nvalid, E, k, t0, blk, topk_idx,
@@ -614,7 +618,9 @@ router_select_kernel(const float* __restrict__ part_in, int nsplit, const Router
       const int o = o0 + threadIdx.x + i * kThreads;
       if (o < n) {
         const int r = o / E, e = o % E;
-        lg[r * (ep + 1) + e] = router_score(v[i], mod, t0 + r, T, E, e);
+        const float sc = router_score(v[i], mod, t0 + r, T, E, e);
+        lg[r * (ep + 1) + e] = sc;
+        if (mod.scores_out) mod.scores_out[(t0 + r) * E + e] = sc;
       }
     }
   }

@@ -253,3 +253,68 @@ def test_int8_forward_needs_scales(L):
         setattr(w2, missing, None)
         assert L.moe_forward(ctypes.byref(c8), ctypes.byref(w2), P, None, P, None, None, None, None, P,
                              ctypes.byref(m), None) == INVALID, missing
+
+
+# ---------------------------------------------------------------------------
+# training entry points (no launches: size queries and argument checks)
+
+
+def _train_query(L, c, w=None):
+    n = ctypes.c_size_t(0)
+    w = w or _lib.MoeWeights(w_router=P, w1=P, w2=P)
+    st1 = L.moe_forward_train(ctypes.byref(c), ctypes.byref(w), None, None, None, None, None, None,
+                              ctypes.byref(n), None)
+    m = ctypes.c_size_t(0)
+    st2 = L.moe_backward(ctypes.byref(c), ctypes.byref(w), None, None, None, 1.0, None, None,
+                         ctypes.byref(m), None)
+    return st1, n.value, st2, m.value
+
+
+def test_training_workspace_queries(L):
+    st1, n, st2, m = _train_query(L, cfg())
+    assert st1 == OK and st2 == OK and n > 0 and m > 0
+    # the backward holds at least d o, the pre-activations and their transposes
+    c = cfg(n_tokens=1000)
+    _, _, _, m2 = _train_query(L, c)
+    T, k, d, f = 1000, 2, 64, 128
+    assert m2 >= 2 * (T * k * d + T * k * 2 * f + T * k * 2 * f + T * k * d)
+
+
+@pytest.mark.parametrize("bad", [dict(dtype=_lib.MOE_DTYPE_F32),
+                                 dict(weight_format=1, d_model=128, d_ffn=128)])
+def test_training_unsupported(L, bad):
+    st1, _, st2, _ = _train_query(L, cfg(**bad))
+    assert st1 == UNSUPPORTED and st2 == UNSUPPORTED
+
+
+def test_training_argument_checks(L):
+    c = cfg()
+    _, n, _, m = _train_query(L, c)
+    w = _lib.MoeWeights(w_router=P, w1=P, w2=P)
+    nn_ = ctypes.c_size_t(n)
+    # the training forward needs every saved buffer
+    sv = _lib.MoeSaved(scores=P, token_lse=P, topk_idx=P, topk_w=P, expert_counts=P,
+                       expert_offsets=P, perm_token=P, inv_row=P, y_perm=P)
+    for miss in ("scores", "y_perm", "inv_row"):
+        bad = _lib.MoeSaved(**{f: getattr(sv, f) for f, _ in _lib.MoeSaved._fields_})
+        setattr(bad, miss, None)
+        assert L.moe_forward_train(ctypes.byref(c), ctypes.byref(w), P, None, P, ctypes.byref(bad),
+                                   None, P, ctypes.byref(nn_), None) == INVALID, miss
+    assert L.moe_forward_train(ctypes.byref(c), ctypes.byref(w), P, None, P, None, None, P,
+                               ctypes.byref(nn_), None) == INVALID
+    # the backward needs dy, the saved state and the required gradient buffers
+    g = _lib.MoeGrads(dx=P, dw_router=P, dw1=P, dw2=P)
+    mm = ctypes.c_size_t(m)
+    assert L.moe_backward(ctypes.byref(c), ctypes.byref(w), P, ctypes.byref(sv), None, 1.0,
+                          ctypes.byref(g), P, ctypes.byref(mm), None) == INVALID
+    for miss in ("dx", "dw_router", "dw1", "dw2"):
+        bad = _lib.MoeGrads(dx=P, dw_router=P, dw1=P, dw2=P)
+        setattr(bad, miss, None)
+        assert L.moe_backward(ctypes.byref(c), ctypes.byref(w), P, ctypes.byref(sv), P, 1.0,
+                              ctypes.byref(bad), P, ctypes.byref(mm), None) == INVALID, miss
+    # biases present: their gradients are required
+    wb = _lib.MoeWeights(w_router=P, w1=P, w2=P, b1=P)
+    assert L.moe_backward(ctypes.byref(c), ctypes.byref(wb), P, ctypes.byref(sv), P, 1.0,
+                          ctypes.byref(g), P, ctypes.byref(mm), None) == INVALID
+    assert L.moe_backward(ctypes.byref(c), ctypes.byref(w), P, ctypes.byref(sv), P, math.nan,
+                          ctypes.byref(g), P, ctypes.byref(mm), None) == INVALID
