@@ -48,6 +48,7 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-backward", action="store_true", help="skip the training (backward) leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling HBM byte counters)")
     return ap.parse_args()
@@ -255,6 +256,47 @@ def main():
     log(f"[bench] grouped GEMMs {ffn_s * 1e6:.1f} us -> {gemm_tflops:.1f} TFLOP/s, "
         f"{routed_bytes / ffn_s / 1e9:.0f} GB/s")
 
+    # ---- training leg: moe_forward_train + moe_backward on the same batch
+    # (bf16 activations with bf16 expert weights), HIP events on this stream
+    backward = None
+    if not args.no_backward and cfg.dtype == "bf16" and not q8:
+        tr = B.TrainStep(c, W)
+        g_dy = torch.randn(T, d, device="cuda", generator=torch.Generator(device="cuda").manual_seed(5))
+        g_dy = g_dy.to(torch.bfloat16)
+        for _ in range(5):
+            tr.forward(x, noise)
+            tr.backward(g_dy)
+        n_tr = max(20, args.steps // 4)
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        torch.cuda.synchronize()
+        f_ms = b_ms = 0.0
+        for _ in range(n_tr):
+            e0.record(stream)
+            tr.forward(x, noise)
+            e1.record(stream)
+            tr.backward(g_dy)
+            e2.record(stream)
+            e2.synchronize()
+            f_ms += e0.elapsed_time(e1)
+            b_ms += e1.elapsed_time(e2)
+        bwd_s = b_ms / 1e3 / n_tr
+        # algorithmic backward flops: twice the forward's expert products
+        # (d input and d weight of each), routed and shared, plus the router's
+        w1r = 2 * f if cfg.act == "swiglu" else f
+        bflops = 2 * (R + T * S) * (2 * d * w1r + 2 * d * f) + 2 * 2 * T * d * cfg.E
+        bt = bflops / bwd_s / 1e12
+        backward = {
+            "what": "moe_backward (all gradients) after moe_forward_train, same batch",
+            "us_per_step": round(bwd_s * 1e6, 2),
+            "train_forward_us": round(f_ms / n_tr * 1e3, 2),
+            "train_step_us": round((f_ms + b_ms) / n_tr * 1e3, 2),
+            "tokens_per_s_train": round(T / ((f_ms + b_ms) / n_tr / 1e3), 1),
+            "flops_per_step": bflops, "achieved_tflops": round(bt, 2),
+            "frac_of_mfma_peak": round(bt / MFMA_BF16_PEAK_TFLOPS, 4),
+        }
+        log(f"[bench] training step: forward {f_ms / n_tr * 1e3:.1f} us + backward "
+            f"{bwd_s * 1e6:.1f} us ({bt:.0f} TFLOP/s algorithmic)")
+
     # ---- CPU oracle leg (rank 0, N = 1 only)
     cpu = None
     parity = None
@@ -305,6 +347,7 @@ def main():
                    "layer_tflops": round(layer_flops / (best_s / args.steps) / 1e12, 2),
                    "kept_rows": R, "dropped": int(aux["n_dropped"])},
         "roofline": roofline,
+        "backward": backward,
         "cpu_baseline": cpu,
         "parity": parity,
     }

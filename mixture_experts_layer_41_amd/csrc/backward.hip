@@ -176,17 +176,22 @@ pad_offsets_kernel(const int32_t* __restrict__ offsets, int G, int pad, int64_t 
 }
 
 // ---------------------------------------------------------------------------
-// transpose of 2-byte elements through a 64 x 64 LDS tile.
+// transpose of 2-byte elements through a 64 x 64 LDS tile, 16-byte global
+// loads and stores (C, the destination leading dimension and every chunk
+// start are multiples of 8 elements).
 // dst[b][c][j] = src[b][row(j)][c] for c < C and destination columns j < ncols,
 // with row(j) = colrow ? colrow[j] : (j < nsrc ? j : -1), gathered through
-// `gather` when given; row -1 writes 0, row -2 writes nothing.
+// `gather` when given; rows -1 and -2 (past the last group) read as 0.
+// Destination chunks of 8 columns at or past ncols are not written.
+
+constexpr int kTP = 72;  // LDS row pitch (elements): 64 + 8 keeps rows 16-byte aligned
 
 __global__ void __launch_bounds__(kThreads)
 transpose_kernel(const uint16_t* __restrict__ src, int64_t src_ld, int64_t src_batch,
                  const int32_t* __restrict__ colrow, const int32_t* __restrict__ gather,
                  int64_t nsrc, int64_t ncols, int C, uint16_t* __restrict__ dst, int64_t dst_ld,
                  int64_t dst_batch) {
-  __shared__ uint16_t tile[64][66];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * kTP];
   __shared__ int32_t rows[64];
   const int64_t j0 = (int64_t)blockIdx.x * 64;
   const int c0 = blockIdx.y * 64;
@@ -194,7 +199,7 @@ transpose_kernel(const uint16_t* __restrict__ src, int64_t src_ld, int64_t src_b
   uint16_t* D = dst + (int64_t)blockIdx.z * dst_batch;
   if (threadIdx.x < 64) {
     const int64_t j = j0 + threadIdx.x;
-    int32_t r = -2;
+    int32_t r = -1;
     if (j < ncols) {
       r = colrow ? colrow[j] : (j < nsrc ? (int32_t)j : -1);
       if (r >= 0 && gather) r = gather[r];
@@ -202,22 +207,32 @@ transpose_kernel(const uint16_t* __restrict__ src, int64_t src_ld, int64_t src_b
     rows[threadIdx.x] = r;
   }
   __syncthreads();
-  // load: 64 rows x 64 columns, 4 columns (8 bytes) per thread per pass
-  for (int o = threadIdx.x; o < 64 * 16; o += kThreads) {
-    const int jj = o / 16, cc = (o % 16) * 4;
-    const int32_t r = rows[jj];
+  // load: 64 source rows x 8 chunks of 8 columns
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int c = c0 + cc + q;
-      tile[jj][cc + q] = (r >= 0 && c < C) ? S[(int64_t)r * src_ld + c] : (uint16_t)0;
-    }
+  for (int u = 0; u < 2; ++u) {
+    const int o = threadIdx.x + kThreads * u;
+    const int jj = o / 8, ch = o % 8;
+    const int32_t r = rows[jj];
+    const int c = c0 + ch * 8;
+    u32x4v v = {0u, 0u, 0u, 0u};
+    if (r >= 0 && c < C) v = *reinterpret_cast<const u32x4v*>(S + (int64_t)r * src_ld + c);
+    *reinterpret_cast<u32x4v*>(&tile[jj * kTP + ch * 8]) = v;
   }
   __syncthreads();
-  // store: 64 destination rows (c) x 64 columns (j)
-  for (int o = threadIdx.x; o < 64 * 64; o += kThreads) {
-    const int cc = o / 64, jj = o % 64;
+  // store: 64 destination rows (c) x 8 chunks of 8 columns (j)
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int o = threadIdx.x + kThreads * u;
+    const int cc = o / 8, jc = o % 8;
     const int c = c0 + cc;
-    if (c < C && rows[jj] != -2) D[(int64_t)c * dst_ld + j0 + jj] = tile[jj][cc];
+    const int64_t j = j0 + jc * 8;
+    if (c >= C || j >= ncols) continue;
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      w[q] = (uint32_t)tile[(jc * 8 + 2 * q) * kTP + cc] |
+             ((uint32_t)tile[(jc * 8 + 2 * q + 1) * kTP + cc] << 16);
+    *reinterpret_cast<u32x4v*>(D + (int64_t)c * dst_ld + j) = u32x4v{w[0], w[1], w[2], w[3]};
   }
 }
 
@@ -352,7 +367,8 @@ dx_gather_kernel(const uint16_t* __restrict__ dx_rows, const int32_t* __restrict
 // float32 SIMT GEMM for the router's gradients:
 //   C[m, n] = sum_{k in split} A(m, k) B(k, n),
 //   A(m, k) = a[m * sam + k * sak] (float32), B(k, n) = b[k * ldb + n] (bf16),
-// 64 x 64 tiles, K chunks of 16 through LDS, 4 x 4 outputs per thread.
+// 64 x 64 tiles, K chunks of 16 through LDS (the next chunk's loads in
+// registers while the current one is used), 4 x 4 outputs per thread.
 // blockIdx.z = K split s: rows k in [s * kchunk, (s + 1) * kchunk) go to
 // c + s * c_split (partials summed afterwards in split order).
 
@@ -367,14 +383,26 @@ simt_gemm_kernel(const float* __restrict__ a, int64_t sam, int64_t sak,
   const int64_t ke = kb + kchunk < K ? kb + kchunk : K;
   const int tm = threadIdx.x / 16, tn = threadIdx.x % 16;
   float acc[4][4] = {};
-  for (int64_t k0 = kb; k0 < ke; k0 += 16) {
-    for (int o = threadIdx.x; o < 16 * 64; o += kThreads) {
-      const int kk = o / 64, mm = o % 64;
+  float ra[4], rb[4];
+  auto load = [&](int64_t k0) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int o = threadIdx.x + kThreads * u, kk = o / 64, mm = o % 64;
       const int64_t kg = k0 + kk;
-      As[kk][mm] = (kg < ke && m0 + mm < M) ? a[(int64_t)(m0 + mm) * sam + kg * sak] : 0.f;
-      Bs[kk][mm] = (kg < ke && n0 + mm < N) ? bf(b[kg * ldb + n0 + mm]) : 0.f;
+      ra[u] = (kg < ke && m0 + mm < M) ? a[(int64_t)(m0 + mm) * sam + kg * sak] : 0.f;
+      rb[u] = (kg < ke && n0 + mm < N) ? bf(b[kg * ldb + n0 + mm]) : 0.f;
+    }
+  };
+  if (kb < ke) load(kb);
+  for (int64_t k0 = kb; k0 < ke; k0 += 16) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int o = threadIdx.x + kThreads * u, kk = o / 64, mm = o % 64;
+      As[kk][mm] = ra[u];
+      Bs[kk][mm] = rb[u];
     }
     __syncthreads();
+    if (k0 + 16 < ke) load(k0 + 16);
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) {
       float av[4], bv[4];
@@ -488,11 +516,12 @@ hipError_t launch_dx_gather(const moe_config& c, const void* dx_rows, const int3
 }
 
 // Split count of a SIMT GEMM with long K: enough workgroups to cover the
-// chip, each with at least 256 rows of K.
+// chip several times over (each K chunk costs a memory round trip), each
+// with at least 64 rows of K.
 int simt_splits(int M, int N, int64_t K) {
   const int64_t tiles = (int64_t)((M + 63) / 64) * ((N + 63) / 64);
-  int64_t want = (1024 + tiles - 1) / tiles;
-  const int64_t most = (K + 255) / 256;
+  int64_t want = (2048 + tiles - 1) / tiles;
+  const int64_t most = (K + 63) / 64;
   if (want > most) want = most;
   if (want < 1) want = 1;
   if (want > 256) want = 256;
