@@ -13,7 +13,7 @@
 //   pad_offsets     per-group columns padded to multiples of the K tile, and
 //                   for each padded column its source row (-1: zero padding)
 //   transpose       [rows, C] -> [C, padded columns], optional row gather
-//   act_bwd         a, dh -> da and h = act(a)
+//   act_bwd_t       a, dh -> da (row-major) and da^T, h^T (padded columns)
 //   seg_rowsum      bias gradients: sums of each row of a transposed matrix
 //                   over each group's columns
 //   dx_gather       dx_t = sum_j dx_rows[row_tj] + shared + router + residual
@@ -237,51 +237,98 @@ transpose_kernel(const uint16_t* __restrict__ src, int64_t src_ld, int64_t src_b
 }
 
 // ---------------------------------------------------------------------------
-// activation backward over rows x S segments x f columns, 8 columns per
-// thread.  SwiGLU: a holds [gate | up] per segment (2f columns), h =
-// silu(g) u, dg = dh u silu'(g), du = dh silu(g).  GELU: h = gelu(a),
-// da = dh gelu'(a).  Rows past *nrows (device) are left alone.
+// activation backward fused with the transposes the weight gradients need.
+// Tile (64 destination columns j) x (64 columns n of one segment s): column j
+// takes source row r = colrow ? colrow[j] : (j < nsrc ? j : -1) (-1 and -2:
+// zero padding).  SwiGLU: a holds [gate | up] per segment (2f columns),
+// h = silu(g) u, dg = dh u silu'(g), du = dh silu(g); GELU: h = gelu(a),
+// da = dh gelu'(a).  Writes da row-major (rows r >= 0 only, for the dx
+// product) and, through LDS, da^T [S * arow, ldt] and h^T [S * f, ldt] at
+// columns j (zeros for padding).
 
 __global__ void __launch_bounds__(kThreads)
-act_bwd_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict__ dh,
-               const int32_t* __restrict__ nrows_dev, int64_t nrows_host, int S, int f, int act,
-               uint16_t* __restrict__ da, uint16_t* __restrict__ h) {
-  const int64_t nrows = nrows_dev ? (int64_t)*nrows_dev : nrows_host;
-  const int per_row = S * (f / 8);
-  const int64_t o = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (o >= nrows * per_row) return;
-  const int64_t r = o / per_row;
-  const int rem = (int)(o % per_row), s = rem / (f / 8), c = (rem % (f / 8)) * 8;
+act_bwd_t_kernel(const uint16_t* __restrict__ a, int64_t lda, const uint16_t* __restrict__ dh,
+                 int64_t ldh, const int32_t* __restrict__ colrow, int64_t nsrc, int64_t ncols,
+                 int f, int act, uint16_t* __restrict__ da, uint16_t* __restrict__ dat,
+                 uint16_t* __restrict__ ht, int64_t ldt) {
+  __shared__ __attribute__((aligned(16))) uint16_t tg[64 * kTP];
+  __shared__ __attribute__((aligned(16))) uint16_t tu[64 * kTP];
+  __shared__ __attribute__((aligned(16))) uint16_t th[64 * kTP];
+  __shared__ int32_t rows[64];
+  const int64_t j0 = (int64_t)blockIdx.x * 64;
+  const int n0 = blockIdx.y * 64, s = blockIdx.z;
   const bool swiglu = act == MOE_ACT_SWIGLU;
   const int arow = swiglu ? 2 * f : f;
-  const int64_t abase = r * (int64_t)S * arow + (int64_t)s * arow + c;
-  const int64_t hbase = r * (int64_t)S * f + (int64_t)s * f + c;
-  float g[8], up[8], d[8], hv[8], dg[8], du[8];
-  unpack8(*reinterpret_cast<const u32x4v*>(a + abase), g);
-  unpack8(*reinterpret_cast<const u32x4v*>(dh + hbase), d);
-  if (swiglu) {
-    unpack8(*reinterpret_cast<const u32x4v*>(a + abase + f), up);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float sg = 1.f / (1.f + __expf(-g[i]));
-      const float si = g[i] * sg;
-      hv[i] = si * up[i];
-      dg[i] = d[i] * up[i] * sg * (1.f + g[i] * (1.f - sg));
-      du[i] = d[i] * si;
-    }
-    *reinterpret_cast<u32x4v*>(da + abase) = pack8(dg);
-    *reinterpret_cast<u32x4v*>(da + abase + f) = pack8(du);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float Phi = 0.5f * (1.f + erff(g[i] * 0.70710678118654752f));
-      const float phi = 0.39894228040143268f * __expf(-0.5f * g[i] * g[i]);
-      hv[i] = g[i] * Phi;
-      dg[i] = d[i] * (Phi + g[i] * phi);
-    }
-    *reinterpret_cast<u32x4v*>(da + abase) = pack8(dg);
+  if (threadIdx.x < 64) {
+    const int64_t j = j0 + threadIdx.x;
+    int32_t r = -1;
+    if (j < ncols) r = colrow ? colrow[j] : (j < nsrc ? (int32_t)j : -1);
+    rows[threadIdx.x] = r;
   }
-  *reinterpret_cast<u32x4v*>(h + hbase) = pack8(hv);
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int o = threadIdx.x + kThreads * u;
+    const int jj = o / 8, ch = o % 8;
+    const int32_t r = rows[jj];
+    const int n = n0 + ch * 8;
+    float gv[8], uv[8], dv[8], dg[8], du[8], hv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dg[i] = du[i] = hv[i] = 0.f;
+    if (r >= 0 && n < f) {
+      const int64_t ab = (int64_t)r * lda + (int64_t)s * arow + n;
+      unpack8(*reinterpret_cast<const u32x4v*>(a + ab), gv);
+      unpack8(*reinterpret_cast<const u32x4v*>(dh + (int64_t)r * ldh + (int64_t)s * f + n), dv);
+      if (swiglu) {
+        unpack8(*reinterpret_cast<const u32x4v*>(a + ab + f), uv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float sg = 1.f / (1.f + __expf(-gv[i]));
+          const float si = gv[i] * sg;
+          hv[i] = si * uv[i];
+          dg[i] = dv[i] * uv[i] * sg * (1.f + gv[i] * (1.f - sg));
+          du[i] = dv[i] * si;
+        }
+        *reinterpret_cast<u32x4v*>(da + ab) = pack8(dg);
+        *reinterpret_cast<u32x4v*>(da + ab + f) = pack8(du);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float Phi = 0.5f * (1.f + erff(gv[i] * 0.70710678118654752f));
+          const float phi = 0.39894228040143268f * __expf(-0.5f * gv[i] * gv[i]);
+          hv[i] = gv[i] * Phi;
+          dg[i] = dv[i] * (Phi + gv[i] * phi);
+        }
+        *reinterpret_cast<u32x4v*>(da + ab) = pack8(dg);
+      }
+    }
+    // the bf16 values written above, or zeros
+    *reinterpret_cast<u32x4v*>(&tg[jj * kTP + ch * 8]) = pack8(dg);
+    if (swiglu) *reinterpret_cast<u32x4v*>(&tu[jj * kTP + ch * 8]) = pack8(du);
+    *reinterpret_cast<u32x4v*>(&th[jj * kTP + ch * 8]) = pack8(hv);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int o = threadIdx.x + kThreads * u;
+    const int cc = o / 8, jc = o % 8;
+    const int c = n0 + cc;
+    const int64_t j = j0 + jc * 8;
+    if (c >= f || j >= ncols) continue;
+    uint32_t wg[4], wu[4], wh[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r0 = (jc * 8 + 2 * q) * kTP + cc, r1 = r0 + kTP;
+      wg[q] = (uint32_t)tg[r0] | ((uint32_t)tg[r1] << 16);
+      wu[q] = swiglu ? ((uint32_t)tu[r0] | ((uint32_t)tu[r1] << 16)) : 0u;
+      wh[q] = (uint32_t)th[r0] | ((uint32_t)th[r1] << 16);
+    }
+    const int64_t crow = (int64_t)s * arow + c;
+    *reinterpret_cast<u32x4v*>(dat + crow * ldt + j) = u32x4v{wg[0], wg[1], wg[2], wg[3]};
+    if (swiglu)
+      *reinterpret_cast<u32x4v*>(dat + (crow + f) * ldt + j) = u32x4v{wu[0], wu[1], wu[2], wu[3]};
+    *reinterpret_cast<u32x4v*>(ht + ((int64_t)s * f + c) * ldt + j) = u32x4v{wh[0], wh[1], wh[2], wh[3]};
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -481,13 +528,14 @@ hipError_t launch_transpose(const void* src, int64_t src_ld, int64_t src_batch,
   return hipGetLastError();
 }
 
-hipError_t launch_act_bwd(const void* a, const void* dh, const int32_t* nrows_dev, int64_t nrows_host,
-                          int S, int f, int act, void* da, void* h, hipStream_t s) {
-  const int64_t n = nrows_host * S * (f / 8);
-  if (n <= 0) return hipSuccess;
-  act_bwd_kernel<<<blocks_for(n, kThreads), kThreads, 0, s>>>(
-      static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(dh), nrows_dev, nrows_host, S, f,
-      act, static_cast<uint16_t*>(da), static_cast<uint16_t*>(h));
+hipError_t launch_act_bwd_t(const void* a, int64_t lda, const void* dh, int64_t ldh,
+                            const int32_t* colrow, int64_t nsrc, int64_t ncols, int S, int f,
+                            int act, void* da, void* dat, void* ht, int64_t ldt, hipStream_t s) {
+  if (ncols <= 0 || S <= 0) return hipSuccess;
+  act_bwd_t_kernel<<<dim3(blocks_for(ncols, 64), blocks_for(f, 64), S), kThreads, 0, s>>>(
+      static_cast<const uint16_t*>(a), lda, static_cast<const uint16_t*>(dh), ldh, colrow, nsrc,
+      ncols, f, act, static_cast<uint16_t*>(da), static_cast<uint16_t*>(dat),
+      static_cast<uint16_t*>(ht), ldt);
   return hipGetLastError();
 }
 

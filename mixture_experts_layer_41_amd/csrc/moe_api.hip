@@ -522,10 +522,10 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
   const int nsplit = simt_splits(E, d, T);
 
   struct Plan {
-    void *dO, *A, *W2t, *W1t, *dH, *dA, *H, *dXr, *dOt, *Ht, *dAt, *Xt;
+    void *dO, *A, *W2t, *W1t, *dH, *dA, *dXr, *dOt, *Ht, *dAt, *Xt;
     float *dw, *dl, *dxr, *wr_part;
     int32_t *poff, *colrow;
-    void *As, *Ws2t, *Ws1t, *dHs, *dAs, *Hs, *dXs, *dyt, *Hst, *dAst, *xt;
+    void *As, *Ws2t, *Ws1t, *dHs, *dAs, *dXs, *dyt, *Hst, *dAst, *xt;
   };
   auto plan = [&](void* base, Plan& p) {
     Carver cv(base);
@@ -539,7 +539,6 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
     p.W1t = cv.take<uint16_t>((size_t)E * d * w1r);
     p.dH = cv.take<uint16_t>(R * f);
     p.dA = cv.take<uint16_t>(R * w1r);
-    p.H = cv.take<uint16_t>(R * f);
     p.dXr = cv.take<uint16_t>(R * d);
     p.poff = cv.take<int32_t>(E + 1);
     p.colrow = cv.take<int32_t>(Rp);
@@ -553,7 +552,6 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
       p.Ws1t = cv.take<uint16_t>((size_t)S * d * w1r);
       p.dHs = cv.take<uint16_t>(T * S * f);
       p.dAs = cv.take<uint16_t>(T * S * w1r);
-      p.Hs = cv.take<uint16_t>(T * S * f);
       p.dXs = cv.take<uint16_t>(T * d);
       p.dyt = cv.take<uint16_t>(d * Tp);
       p.Hst = cv.take<uint16_t>(S * f * Tp);
@@ -622,7 +620,10 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
   gd.out = p.dH;
   gd.ldo = f;
   MOE_HIP_TRY(launch_gemm(c, kGemmDown, gd, stream));
-  MOE_HIP_TRY(launch_act_bwd(p.A, p.dH, sv->expert_offsets + E, R, 1, f, c.act, p.dA, p.H, stream));
+  // da (row-major) and the expert-padded da^T, h^T in one pass
+  MOE_HIP_TRY(launch_pad_offsets(sv->expert_offsets, E, kPad, Rp, p.poff, p.colrow, stream));
+  MOE_HIP_TRY(launch_act_bwd_t(p.A, w1r, p.dH, f, p.colrow, 0, Rp, 1, f, c.act, p.dA, p.dAt, p.Ht,
+                               Rp, stream));
   gd.a = p.dA;
   gd.lda = w1r;
   gd.w = p.W1t;
@@ -633,10 +634,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
   MOE_HIP_TRY(launch_gemm(c, kGemmDown, gd, stream));
 
   // weight gradients from the expert-padded transposes
-  MOE_HIP_TRY(launch_pad_offsets(sv->expert_offsets, E, kPad, Rp, p.poff, p.colrow, stream));
   MOE_HIP_TRY(launch_transpose(p.dO, d, 0, p.colrow, nullptr, 0, Rp, d, p.dOt, Rp, 0, 1, stream));
-  MOE_HIP_TRY(launch_transpose(p.H, f, 0, p.colrow, nullptr, 0, Rp, f, p.Ht, Rp, 0, 1, stream));
-  MOE_HIP_TRY(launch_transpose(p.dA, w1r, 0, p.colrow, nullptr, 0, Rp, w1r, p.dAt, Rp, 0, 1, stream));
   MOE_HIP_TRY(launch_transpose(x, d, 0, p.colrow, sv->perm_token, 0, Rp, d, p.Xt, Rp, 0, 1, stream));
   MOE_HIP_TRY(launch_wgrad(p.dOt, Rp, 0, p.Ht, Rp, 0, p.poff, 0, d, f, E, g->dw2, f,
                            (int64_t)d * f, stream));
@@ -679,7 +677,8 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
       sd.ldo = (int64_t)S * f;
       MOE_HIP_TRY(launch_gemm(c, kGemmDown, sd, stream));
     }
-    MOE_HIP_TRY(launch_act_bwd(p.As, p.dHs, nullptr, T, S, f, c.act, p.dAs, p.Hs, stream));
+    MOE_HIP_TRY(launch_act_bwd_t(p.As, (int64_t)S * w1r, p.dHs, (int64_t)S * f, nullptr, T, Tp, S, f,
+                                 c.act, p.dAs, p.dAst, p.Hst, Tp, stream));
     sd.a = p.dAs;
     sd.lda = (int64_t)S * w1r;
     sd.n_seg = S;
@@ -690,10 +689,6 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
     sd.ldo = d;
     MOE_HIP_TRY(launch_gemm(c, kGemmDown, sd, stream));
     MOE_HIP_TRY(launch_transpose(dy, d, 0, nullptr, nullptr, T, Tp, d, p.dyt, Tp, 0, 1, stream));
-    MOE_HIP_TRY(launch_transpose(p.Hs, (int64_t)S * f, 0, nullptr, nullptr, T, Tp, S * f, p.Hst, Tp,
-                                 0, 1, stream));
-    MOE_HIP_TRY(launch_transpose(p.dAs, (int64_t)S * w1r, 0, nullptr, nullptr, T, Tp, S * w1r,
-                                 p.dAst, Tp, 0, 1, stream));
     MOE_HIP_TRY(launch_transpose(x, d, 0, nullptr, nullptr, T, Tp, d, p.xt, Tp, 0, 1, stream));
     MOE_HIP_TRY(launch_wgrad(p.dyt, Tp, 0, p.Hst, Tp, (int64_t)f * Tp, nullptr, Tp, d, f, S, g->dws2,
                              f, (int64_t)d * f, stream));

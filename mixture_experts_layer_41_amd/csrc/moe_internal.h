@@ -143,8 +143,9 @@ hipError_t launch_transpose(const void* src, int64_t src_ld, int64_t src_batch,
                             const int32_t* colrow, const int32_t* gather, int64_t nsrc,
                             int64_t ncols, int C, void* dst, int64_t dst_ld, int64_t dst_batch,
                             int batches, hipStream_t s);
-hipError_t launch_act_bwd(const void* a, const void* dh, const int32_t* nrows_dev, int64_t nrows_host,
-                          int S, int f, int act, void* da, void* h, hipStream_t s);
+hipError_t launch_act_bwd_t(const void* a, int64_t lda, const void* dh, int64_t ldh,
+                            const int32_t* colrow, int64_t nsrc, int64_t ncols, int S, int f,
+                            int act, void* da, void* dat, void* ht, int64_t ldt, hipStream_t s);
 hipError_t launch_seg_rowsum(const void* m, int64_t ld, int C, const int32_t* poff, int64_t ncols,
                              int G, float* out, int64_t out_ld, hipStream_t s);
 hipError_t launch_colsum_f32(const float* m, int64_t T, int E, float* out, hipStream_t s);
