@@ -283,10 +283,14 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
  */
 
 /* Forward state kept for the backward: device buffers the caller owns, all
- * required.  scores [T,E] float32 (s of moe_route), token_lse [T] float32,
- * topk_idx [T,k] int32, topk_w [T,k] float32, expert_counts [E] int32,
- * expert_offsets [E+1] int32, perm_token [T*k] int32, inv_row [T*k] int32,
- * y_perm [T*k, d] act dtype (each kept row's expert output). */
+ * required (shared_preact only when S > 0).  scores [T,E] float32 (s of
+ * moe_route), token_lse [T] float32, topk_idx [T,k] int32, topk_w [T,k]
+ * float32, expert_counts [E] int32, expert_offsets [E+1] int32, perm_token
+ * [T*k] int32, inv_row [T*k] int32, y_perm [T*k, d] act dtype (each kept
+ * row's expert output), preact [T*k, 2f|f] act dtype (each kept row's
+ * pre-activations x W1^T + b1, SwiGLU gate then up), shared_preact
+ * [T, S*(2f|f)] act dtype (the shared experts' pre-activations, expert s at
+ * columns s*(2f|f)). */
 typedef struct {
   float* scores;
   float* token_lse;
@@ -297,6 +301,8 @@ typedef struct {
   int32_t* perm_token;
   int32_t* inv_row;
   void* y_perm;
+  void* preact;
+  void* shared_preact;
 } moe_saved;
 
 /* Gradients written by moe_backward (device buffers the caller owns; each is
@@ -336,7 +342,7 @@ moe_status moe_forward_train(const moe_config* cfg, const moe_weights* w, const 
  * filled `saved` (same cfg, weights, x and router noise).  Top-k
  * selection, capacity drops and the selection shares f_e pass no gradient.
  *   combine: d o_tj = w_tj dy_t (kept slots), dw_tj = dy_t . o_tj;
- *   experts: a = x W1^T + b1 recomputed; dW2 = d o^T act(a), dh = d o W2,
+ *   experts: a = x W1^T + b1 (saved); dW2 = d o^T act(a), dh = d o W2,
  *            da = dh * act'(a), dW1 = da^T x, dx += da W1 (rows added back
  *            to their tokens); shared experts with d o = dy; residual: dx += dy;
  *   router:  renormalisation, aux terms (d lb / d p_te = E f_e / T,

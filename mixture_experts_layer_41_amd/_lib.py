@@ -64,7 +64,7 @@ class MoeAux(ctypes.Structure):
 class MoeSaved(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "scores", "token_lse", "topk_idx", "topk_w", "expert_counts", "expert_offsets",
-        "perm_token", "inv_row", "y_perm")]
+        "perm_token", "inv_row", "y_perm", "preact", "shared_preact")]
 
 
 class MoeGrads(ctypes.Structure):

@@ -267,8 +267,10 @@ class TrainStep:
             "expert_counts": _i32(E), "expert_offsets": _i32(E + 1), "perm_token": _i32(T * k),
             "inv_row": _i32(T * k),
             "y_perm": torch.empty(T * k, d, dtype=dt, device=dev),
+            "preact": torch.empty(T * k, w1r, dtype=dt, device=dev),
+            "shared_preact": torch.empty(T, S * w1r, dtype=dt, device=dev) if S else None,
         }
-        self._s = MoeSaved(**{n: v.data_ptr() for n, v in self.saved.items()})
+        self._s = MoeSaved(**{n: (None if v is None else v.data_ptr()) for n, v in self.saved.items()})
         self.y = torch.empty(T, d, dtype=dt, device=dev)
         self.aux = new_aux()
         f32 = dict(dtype=torch.float32, device=dev)

@@ -210,6 +210,11 @@ gemm_bf16_kernel(GemmDesc p, int tiles_n) {
             u += bf16_to_f32(b[f + n0 + c]);
           }
           out[grow * p.ldo + (int64_t)seg * f + n0 + c] = f32_to_bf16(silu_f(g) * u);
+          if (p.preact) {
+            uint16_t* pa = static_cast<uint16_t*>(p.preact) + grow * p.ldp + (int64_t)seg * 2 * f + n0 + c;
+            pa[0] = f32_to_bf16(g);
+            pa[f] = f32_to_bf16(u);
+          }
         }
       } else {
 #pragma unroll
@@ -219,6 +224,8 @@ gemm_bf16_kernel(GemmDesc p, int tiles_n) {
           float v = acc[i][j][q];
           if (KIND == kGemmUp) {
             if (BIAS) v += bf16_to_f32(bias[((int64_t)tile.group * S + seg) * f + n0 + c]);
+            if (p.preact)
+              static_cast<uint16_t*>(p.preact)[grow * p.ldp + (int64_t)seg * f + n0 + c] = f32_to_bf16(v);
             v = gelu_f(v);
             out[grow * p.ldo + (int64_t)seg * f + n0 + c] = f32_to_bf16(v);
           } else {

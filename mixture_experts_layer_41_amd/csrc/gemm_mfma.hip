@@ -315,6 +315,11 @@ __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo
             u += bf16_to_f32(b[f + n0 + cidx]);
           }
           out[grow * p.ldo + (int64_t)seg * f + n0 + cidx] = f32_to_bf16(silu_f(g) * u);
+          if (p.preact) {
+            uint16_t* pa = static_cast<uint16_t*>(p.preact) + grow * p.ldp + (int64_t)seg * 2 * f + n0 + cidx;
+            pa[0] = f32_to_bf16(g);
+            pa[f] = f32_to_bf16(u);
+          }
         }
       } else {
 #pragma unroll
@@ -324,6 +329,8 @@ __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo
           if constexpr (Q8 == 1) v *= esc[j];
           if (KIND == kGemmUp) {
             if (BIAS) v += bf16_to_f32(bias[((int64_t)tile.group * S + seg) * f + n0 + cidx]);
+            if (p.preact)
+              static_cast<uint16_t*>(p.preact)[grow * p.ldp + (int64_t)seg * f + n0 + cidx] = f32_to_bf16(v);
             out[grow * p.ldo + (int64_t)seg * f + n0 + cidx] = f32_to_bf16(gelu_f(v));
           } else {
             if (BIAS)

@@ -412,7 +412,7 @@ gemm_pipe_kernel(GemmDesc p, int tiles_n) {
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
               const int cidx = wn * (TN / 2) + j * 32 + 8 * g4 + 4 * half;
-              uint16_t h[4];
+              uint16_t h[4], pg[4], pu[4];
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 float gv = acc[i][j][4 * g4 + e], uv = acc[i][j + NI / 2][4 * g4 + e];
@@ -422,11 +422,21 @@ gemm_pipe_kernel(GemmDesc p, int tiles_n) {
                   uv += bf16_to_f32(b[f + tc.n0 + cidx + e]);
                 }
                 h[e] = f32_to_bf16(silu_f(gv) * uv);
+                pg[e] = f32_to_bf16(gv);
+                pu[e] = f32_to_bf16(uv);
               }
               uint2 v;
               v.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
               v.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
               *reinterpret_cast<uint2*>(out + grow * p.ldo + (int64_t)tc.seg * f + tc.n0 + cidx) = v;
+              if (p.preact) {
+                uint16_t* pa = static_cast<uint16_t*>(p.preact) + grow * p.ldp +
+                               (int64_t)tc.seg * 2 * f + tc.n0 + cidx;
+                *reinterpret_cast<uint2*>(pa) =
+                    uint2{(uint32_t)pg[0] | ((uint32_t)pg[1] << 16), (uint32_t)pg[2] | ((uint32_t)pg[3] << 16)};
+                *reinterpret_cast<uint2*>(pa + f) =
+                    uint2{(uint32_t)pu[0] | ((uint32_t)pu[1] << 16), (uint32_t)pu[2] | ((uint32_t)pu[3] << 16)};
+              }
             }
           }
         } else {
@@ -435,12 +445,13 @@ gemm_pipe_kernel(GemmDesc p, int tiles_n) {
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
               const int cidx = wn * TN + j * 32 + 8 * g4 + 4 * half;
-              uint16_t h[4];
+              uint16_t h[4], pv[4];
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 float v = acc[i][j][4 * g4 + e];
                 if (KIND == kGemmUp) {
                   if (BIAS) v += bf16_to_f32(bias[((int64_t)tc.group * S + tc.seg) * f + tc.n0 + cidx + e]);
+                  pv[e] = f32_to_bf16(v);
                   h[e] = f32_to_bf16(gelu_f(v));
                 } else {
                   if (BIAS)
@@ -454,6 +465,9 @@ gemm_pipe_kernel(GemmDesc p, int tiles_n) {
               v.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
               const int64_t col = (KIND == kGemmUp) ? (int64_t)tc.seg * f + tc.n0 + cidx : tc.n0 + cidx;
               *reinterpret_cast<uint2*>(out + grow * p.ldo + col) = v;
+              if (KIND == kGemmUp && p.preact)
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.preact) + grow * p.ldp + col) =
+                    uint2{(uint32_t)pv[0] | ((uint32_t)pv[1] << 16), (uint32_t)pv[2] | ((uint32_t)pv[3] << 16)};
             }
           }
         }

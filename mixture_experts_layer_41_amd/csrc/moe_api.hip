@@ -426,6 +426,10 @@ static moe_status forward_impl(const moe_config* cfg, const moe_weights* w, cons
   up.act = c.act;
   up.out = p.H;
   up.ldo = f;
+  if (saved) {
+    up.preact = saved->preact;
+    up.ldp = c.act == MOE_ACT_SWIGLU ? 2 * f : f;
+  }
   MOE_HIP_TRY(launch_gemm(c, kGemmUp, up, stream));
   GemmDesc dn = up;
   dn.a = p.H;
@@ -436,6 +440,7 @@ static moe_status forward_impl(const moe_config* cfg, const moe_weights* w, cons
   dn.bias = w->b2;
   dn.out = p.y_perm;
   dn.ldo = d;
+  dn.preact = nullptr;
   MOE_HIP_TRY(launch_gemm(c, kGemmDown, dn, stream));
 
   if (S > 0) {
@@ -455,6 +460,10 @@ static moe_status forward_impl(const moe_config* cfg, const moe_weights* w, cons
     su.act = c.act;
     su.out = p.Hs;
     su.ldo = (int64_t)S * f;
+    if (saved) {
+      su.preact = saved->shared_preact;
+      su.ldp = (int64_t)S * (c.act == MOE_ACT_SWIGLU ? 2 * f : f);
+    }
     MOE_HIP_TRY(launch_gemm(c, kGemmUp, su, stream));
     GemmDesc sd = su;
     sd.a = p.Hs;
@@ -464,6 +473,7 @@ static moe_status forward_impl(const moe_config* cfg, const moe_weights* w, cons
     sd.bias = w->shared_b2;
     sd.out = p.shared_y;
     sd.ldo = d;
+    sd.preact = nullptr;
     MOE_HIP_TRY(launch_gemm(c, kGemmDown, sd, stream));
   }
   MOE_HIP_TRY(launch_combine(c, p.y_perm, p.po.inv_row, p.wts, p.shared_y,
@@ -488,9 +498,11 @@ static moe_status check_train(const moe_config* cfg) {
   return MOE_OK;
 }
 
-static bool saved_ok(const moe_saved* sv) {
+static bool saved_ok(const moe_saved* sv, int S) {
   return sv && sv->scores && sv->token_lse && sv->topk_idx && sv->topk_w && sv->expert_counts &&
-         sv->expert_offsets && sv->perm_token && sv->inv_row && sv->y_perm && aligned4(sv->scores) &&
+         sv->expert_offsets && sv->perm_token && sv->inv_row && sv->y_perm && sv->preact &&
+         aligned16(sv->preact) &&
+         (S == 0 || (sv->shared_preact && aligned16(sv->shared_preact))) && aligned4(sv->scores) &&
          aligned4(sv->token_lse) && aligned4(sv->topk_idx) && aligned4(sv->topk_w) &&
          aligned4(sv->expert_counts) && aligned4(sv->expert_offsets) && aligned4(sv->perm_token) &&
          aligned4(sv->inv_row) && aligned16(sv->y_perm);
@@ -501,7 +513,7 @@ moe_status moe_forward_train(const moe_config* cfg, const moe_weights* w, const 
                              moe_aux* aux, void* ws, size_t* ws_bytes, hipStream_t stream) {
   moe_status st = check_train(cfg);
   if (st != MOE_OK) return st;
-  if (ws != nullptr && !saved_ok(saved)) return MOE_ERR_INVALID_ARG;
+  if (ws != nullptr && !saved_ok(saved, cfg->n_shared)) return MOE_ERR_INVALID_ARG;
   return forward_impl(cfg, w, x, router_noise, y, nullptr, nullptr, nullptr, aux,
                       ws != nullptr ? saved : nullptr, ws, ws_bytes, stream);
 }
@@ -522,10 +534,10 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
   const int nsplit = simt_splits(E, d, T);
 
   struct Plan {
-    void *dO, *A, *W2t, *W1t, *dH, *dA, *dXr, *dOt, *Ht, *dAt, *Xt;
+    void *dO, *W2t, *W1t, *dH, *dA, *dXr, *dOt, *Ht, *dAt, *Xt;
     float *dw, *dl, *dxr, *wr_part;
     int32_t *poff, *colrow;
-    void *As, *Ws2t, *Ws1t, *dHs, *dAs, *dXs, *dyt, *Hst, *dAst, *xt;
+    void *Ws2t, *Ws1t, *dHs, *dAs, *dXs, *dyt, *Hst, *dAst, *xt;
   };
   auto plan = [&](void* base, Plan& p) {
     Carver cv(base);
@@ -534,7 +546,6 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
     p.dl = cv.take<float>(T * E);
     p.dxr = cv.take<float>(T * d);
     p.wr_part = cv.take<float>(nsplit > 1 ? (size_t)nsplit * E * d : 0);
-    p.A = cv.take<uint16_t>(R * w1r);
     p.W2t = cv.take<uint16_t>((size_t)E * f * d);
     p.W1t = cv.take<uint16_t>((size_t)E * d * w1r);
     p.dH = cv.take<uint16_t>(R * f);
@@ -547,7 +558,6 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
     p.dAt = cv.take<uint16_t>(w1r * Rp);
     p.Xt = cv.take<uint16_t>(d * Rp);
     if (S > 0) {
-      p.As = cv.take<uint16_t>(T * S * w1r);
       p.Ws2t = cv.take<uint16_t>((size_t)S * f * d);
       p.Ws1t = cv.take<uint16_t>((size_t)S * d * w1r);
       p.dHs = cv.take<uint16_t>(T * S * f);
@@ -563,7 +573,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
   Plan p{};
   const size_t need = plan(nullptr, p);
   if (ws != nullptr) {
-    if (!w || !x || !dy || !g || !saved_ok(sv) || !w->w_router || !w->w1 || !w->w2)
+    if (!w || !x || !dy || !g || !saved_ok(sv, S) || !w->w_router || !w->w1 || !w->w2)
       return MOE_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(dy) || !aligned16(w->w_router) || !aligned16(w->w1) ||
         !aligned16(w->w2))
@@ -590,22 +600,13 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
   MOE_HIP_TRY(launch_simt_gemm(p.dl, E, 1, w->w_router, d, (int)T, d, E, 1, p.dxr, d, nullptr,
                                stream));
 
-  // routed experts: pre-activations, transposed weights, dh, da / h, dx rows
+  // routed experts: transposed weights, dh, da / h (from the saved
+  // pre-activations), dx rows
   GemmDesc gd{};
   gd.group_off = sv->expert_offsets;
   gd.n_groups = E;
   gd.n_seg = 1;
   gd.rows_max = R;
-  gd.a = x;
-  gd.a_rows = sv->perm_token;
-  gd.lda = d;
-  gd.w = w->w1;
-  gd.bias = w->b1;
-  gd.d = w1r;  // N
-  gd.f = d;    // K
-  gd.out = p.A;
-  gd.ldo = w1r;
-  MOE_HIP_TRY(launch_gemm(c, kGemmDown, gd, stream));
   MOE_HIP_TRY(launch_transpose(w->w2, f, (int64_t)d * f, nullptr, nullptr, d, d, f, p.W2t, d,
                                (int64_t)f * d, E, stream));
   MOE_HIP_TRY(launch_transpose(w->w1, d, (int64_t)w1r * d, nullptr, nullptr, w1r, w1r, d, p.W1t,
@@ -622,8 +623,8 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
   MOE_HIP_TRY(launch_gemm(c, kGemmDown, gd, stream));
   // da (row-major) and the expert-padded da^T, h^T in one pass
   MOE_HIP_TRY(launch_pad_offsets(sv->expert_offsets, E, kPad, Rp, p.poff, p.colrow, stream));
-  MOE_HIP_TRY(launch_act_bwd_t(p.A, w1r, p.dH, f, p.colrow, 0, Rp, 1, f, c.act, p.dA, p.dAt, p.Ht,
-                               Rp, stream));
+  MOE_HIP_TRY(launch_act_bwd_t(sv->preact, w1r, p.dH, f, p.colrow, 0, Rp, 1, f, c.act, p.dA, p.dAt,
+                               p.Ht, Rp, stream));
   gd.a = p.dA;
   gd.lda = w1r;
   gd.w = p.W1t;
@@ -650,18 +651,6 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
     sd.n_groups = 1;
     sd.n_seg = 1;
     sd.rows_max = T;
-    for (int s = 0; s < S; ++s) {
-      sd.a = x;
-      sd.a_rows = nullptr;
-      sd.lda = d;
-      sd.w = static_cast<const uint16_t*>(w->shared_w1) + (int64_t)s * w1r * d;
-      sd.bias = w->shared_b1 ? static_cast<const uint16_t*>(w->shared_b1) + (int64_t)s * w1r : nullptr;
-      sd.d = w1r;
-      sd.f = d;
-      sd.out = static_cast<uint16_t*>(p.As) + (int64_t)s * w1r;
-      sd.ldo = (int64_t)S * w1r;
-      MOE_HIP_TRY(launch_gemm(c, kGemmDown, sd, stream));
-    }
     MOE_HIP_TRY(launch_transpose(w->shared_w2, f, (int64_t)d * f, nullptr, nullptr, d, d, f, p.Ws2t,
                                  d, (int64_t)f * d, S, stream));
     MOE_HIP_TRY(launch_transpose(w->shared_w1, d, (int64_t)w1r * d, nullptr, nullptr, w1r, w1r, d,
@@ -677,8 +666,8 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
       sd.ldo = (int64_t)S * f;
       MOE_HIP_TRY(launch_gemm(c, kGemmDown, sd, stream));
     }
-    MOE_HIP_TRY(launch_act_bwd_t(p.As, (int64_t)S * w1r, p.dHs, (int64_t)S * f, nullptr, T, Tp, S, f,
-                                 c.act, p.dAs, p.dAst, p.Hst, Tp, stream));
+    MOE_HIP_TRY(launch_act_bwd_t(sv->shared_preact, (int64_t)S * w1r, p.dHs, (int64_t)S * f, nullptr,
+                                 T, Tp, S, f, c.act, p.dAs, p.dAst, p.Hst, Tp, stream));
     sd.a = p.dAs;
     sd.lda = (int64_t)S * w1r;
     sd.n_seg = S;

@@ -88,6 +88,12 @@ struct GemmDesc {
   int act;                   // moe_act (up GEMM only)
   void* out;
   int64_t ldo;
+  // up GEMM, bf16 only, optional: the pre-activations (bias added) are also
+  // stored, at [row, seg * 2f + n] (gate) and [row, seg * 2f + f + n] (up)
+  // for SwiGLU, at [row, seg * f + n] for GELU (the training forward keeps
+  // them for the backward)
+  void* preact;
+  int64_t ldp;
 };
 
 // ---------------------------------------------------------------------------

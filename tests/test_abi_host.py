@@ -294,8 +294,8 @@ def test_training_argument_checks(L):
     nn_ = ctypes.c_size_t(n)
     # the training forward needs every saved buffer
     sv = _lib.MoeSaved(scores=P, token_lse=P, topk_idx=P, topk_w=P, expert_counts=P,
-                       expert_offsets=P, perm_token=P, inv_row=P, y_perm=P)
-    for miss in ("scores", "y_perm", "inv_row"):
+                       expert_offsets=P, perm_token=P, inv_row=P, y_perm=P, preact=P)
+    for miss in ("scores", "y_perm", "inv_row", "preact"):
         bad = _lib.MoeSaved(**{f: getattr(sv, f) for f, _ in _lib.MoeSaved._fields_})
         setattr(bad, miss, None)
         assert L.moe_forward_train(ctypes.byref(c), ctypes.byref(w), P, None, P, ctypes.byref(bad),
