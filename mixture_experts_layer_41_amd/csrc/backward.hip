@@ -474,13 +474,21 @@ simt_gemm_kernel(const float* __restrict__ a, int64_t sam, int64_t sak,
     }
 }
 
-// out[i] = sum_s part[s * n + i], s in order
+// out[i] = sum_s part[s * n + i], s in order (eight loads in flight)
 __global__ void __launch_bounds__(kThreads)
 sum_splits_kernel(const float* __restrict__ part, int nsplit, int64_t n, float* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (i >= n) return;
   float acc = 0.f;
-  for (int s = 0; s < nsplit; ++s) acc += part[(int64_t)s * n + i];
+  int s = 0;
+  for (; s + 8 <= nsplit; s += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = part[(int64_t)(s + u) * n + i];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u];
+  }
+  for (; s < nsplit; ++s) acc += part[(int64_t)s * n + i];
   out[i] = acc;
 }
 
