@@ -2,17 +2,19 @@
 //
 // [P3 §4.2] trains on loss = task loss + auxiliary loss and back-propagates
 // both; [P5 §2] weights load balance 0.01 and z-loss 0.001.  The grouped
-// GEMMs of the backward reuse the forward's kernels (dh = d_o W2, dx_rows =
-// da W1, and the recomputed pre-activations a = x W1^T + b1 are all
-// "row-grouped" products with K-contiguous weights once W1 and W2 are
-// transposed) and the weight-gradient kernel of gemm_wgrad.hip.
+// GEMMs of the backward reuse the forward's kernels (dh = d_o W2 and
+// dx_rows = da W1 are "row-grouped" products with K-contiguous weights once
+// W1 and W2 are transposed; the pre-activations a = x W1^T + b1 come saved
+// from the training forward) and the weight-gradient kernel of
+// gemm_wgrad.hip.
 //
 //   combine_bwd     d o_tj = w_tj dy_t into the kept row, dw_tj = dy_t . o_tj
 //   router_grad     renormalisation, aux terms, softmax and 1/tau:
 //                   scores [T, E] -> dl [T, E] (float32)
 //   pad_offsets     per-group columns padded to multiples of the K tile, and
 //                   for each padded column its source row (-1: zero padding)
-//   transpose       [rows, C] -> [C, padded columns], optional row gather
+//   transpose       [rows, C] -> [C, columns]: the weights, and d_o and the
+//                   gathered x into the padded columns, optional row gather
 //   act_bwd_t       a, dh -> da (row-major) and da^T, h^T (padded columns)
 //   seg_rowsum      bias gradients: sums of each row of a transposed matrix
 //                   over each group's columns
