@@ -534,10 +534,16 @@ def expert_ffn_backward(x_rows, w1, b1, w2, b2, act: str, d_out):
     return dx, dW1, db1, dW2, db2
 
 
-def backward(cfg, t, dy, aux_scale: float = 1.0):
+def backward(cfg, t, dy, aux_scale: float = 1.0, loss_weights=None):
     """Gradients of  sum(dy * y) + aux_scale * (0.01 lb + 0.001 z)  with
     respect to x and every parameter (float64), for activation-dtype
-    expert weights.
+    expert weights.  loss_weights, if given, replaces the aux part with
+    c_lb lb + c_z z + c_sq lb_squares + c_kl kl_uniform for the dict
+    {"lb": c_lb, "z": c_z, "lb_squares": c_sq, "kl_uniform": c_kl}
+    (aux_scale is then ignored): the load-balance forms of [P3 §3.1] and
+    [P2 §4.2] used as the training loss instead of, or beside, the main one.
+    The frequency penalty of [P2 §4.2] depends on the selection only and has
+    no gradient.
 
     dy: [T, d] upstream gradient of the layer output.
     Returns a dict: dx [T, d], dw_router [E, d], drouter_bias [E],
@@ -555,6 +561,8 @@ def backward(cfg, t, dy, aux_scale: float = 1.0):
       renorm     w_j = p_j / P with P the sum of the k selected p:
                  dp_m = (dw_m - sum_j dw_j w_j) / P for selected m, else 0;
       aux        d lb / d p_te = E f_e / T;  d z / d s_te = 2 lse_t p_te / T;
+                 d lb_squares / d p_te = 2 E P_e / T;
+                 d kl_uniform / d p_te = -1 / (E (P_e + 1e-8) T);
       softmax    ds_te = p_te (dp_te - sum_e' p_te' dp_te');
       scores     s = (x W_r^T + b) / tau + noise:  dl = ds / tau,
                  dW_r = dl^T x, db = sum_t dl, dx += dl W_r.
@@ -624,10 +632,18 @@ def backward(cfg, t, dy, aux_scale: float = 1.0):
     dp = np.zeros((T, E))
     dsel = (dw - np.sum(dw * w, axis=1, keepdims=True)) / P
     np.put_along_axis(dp, idx, dsel, axis=1)
+    if loss_weights is None:
+        c_lb, c_z, c_sq, c_kl = 0.01 * aux_scale, 0.001 * aux_scale, 0.0, 0.0
+    else:
+        c_lb, c_z = loss_weights.get("lb", 0.0), loss_weights.get("z", 0.0)
+        c_sq, c_kl = loss_weights.get("lb_squares", 0.0), loss_weights.get("kl_uniform", 0.0)
     f_share = counts.astype(np.float64) / float(T * k)
-    dp += aux_scale * 0.01 * E * f_share[None, :] / T
+    P_mean = p.mean(axis=0)
+    dp += c_lb * E * f_share[None, :] / T
+    dp += c_sq * 2.0 * E * P_mean[None, :] / T
+    dp += c_kl * (-1.0 / (E * (P_mean + 1e-8)))[None, :] / T
     ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
-    ds += aux_scale * 0.001 * 2.0 * lse[:, None] * p / T
+    ds += c_z * 2.0 * lse[:, None] * p / T
     dl = ds / tau
     g["dw_router"] = dl.T @ x
     g["drouter_bias"] = dl.sum(axis=0)
