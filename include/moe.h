@@ -326,6 +326,19 @@ typedef struct {
   float* dsb2;
 } moe_grads;
 
+/* Weights of the auxiliary terms in the training loss (moe_backward):
+ * L_aux = load_balance * lb + z_loss * z + lb_squares * (E sum P^2)
+ *       + kl_uniform * KL(uniform || P), the quantities of moe_aux.  The
+ * pages train with 0.01 lb + 0.001 z ([P5 §2]); [P3 §3.1] uses
+ * 0.01 E sum P^2 and [P2 §4.2] alpha (KL + frequency penalty), whose
+ * frequency part depends on the selection only and has no gradient. */
+typedef struct {
+  double load_balance;
+  double z_loss;
+  double lb_squares;
+  double kl_uniform;
+} moe_loss_weights;
+
 /*
  * moe_forward_train - moe_forward that also fills `saved` for moe_backward.
  * Arguments as moe_forward; saved (host struct of device pointers) is
@@ -337,24 +350,28 @@ moe_status moe_forward_train(const moe_config* cfg, const moe_weights* w, const 
                              moe_aux* aux, void* ws, size_t* ws_bytes, hipStream_t stream);
 
 /*
- * moe_backward - gradients of  L = sum(dy * y) + aux_scale * (0.01 lb +
- * 0.001 z)  with respect to x and every parameter, for the forward that
- * filled `saved` (same cfg, weights, x and router noise).  Top-k
- * selection, capacity drops and the selection shares f_e pass no gradient.
+ * moe_backward - gradients of  L = sum(dy * y) + L_aux  with respect to x
+ * and every parameter, for the forward that filled `saved` (same cfg,
+ * weights, x and router noise).  L_aux per `lw` (moe_loss_weights; NULL:
+ * 0.01 lb + 0.001 z).  Top-k selection, capacity drops and the selection
+ * shares f_e pass no gradient.
  *   combine: d o_tj = w_tj dy_t (kept slots), dw_tj = dy_t . o_tj;
  *   experts: a = x W1^T + b1 (saved); dW2 = d o^T act(a), dh = d o W2,
  *            da = dh * act'(a), dW1 = da^T x, dx += da W1 (rows added back
  *            to their tokens); shared experts with d o = dy; residual: dx += dy;
  *   router:  renormalisation, aux terms (d lb / d p_te = E f_e / T,
- *            d z / d s_te = 2 lse_t p_te / T), softmax, then / tau:
+ *            d z / d s_te = 2 lse_t p_te / T, d (E sum P^2) / d p_te =
+ *            2 E P_e / T, d KL / d p_te = -1 / (E (P_e + 1e-8) T)), softmax,
+ *            then / tau:
  *            dW_r = dl^T x, d bias = sum_t dl, dx += dl W_r.
  * x, dy [T,d] act dtype.  Precision: bf16 operands with float32
  * accumulation; d o, a, dh, da and act(a) are stored as bf16 between the
  * steps.  BF16 activation-dtype weights only (else UNSUPPORTED); NULL
- * required buffers: INVALID_ARG.  ws: query with ws == NULL.
+ * required buffers or a non-finite loss weight: INVALID_ARG.  ws: query
+ * with ws == NULL.
  */
 moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void* x,
-                        const moe_saved* saved, const void* dy, double aux_scale,
+                        const moe_saved* saved, const void* dy, const moe_loss_weights* lw,
                         const moe_grads* g, void* ws, size_t* ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus

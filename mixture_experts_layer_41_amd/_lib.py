@@ -73,6 +73,10 @@ class MoeGrads(ctypes.Structure):
         "dsb2")]
 
 
+class MoeLossWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_double) for n in ("load_balance", "z_loss", "lb_squares", "kl_uniform")]
+
+
 class MoeError(RuntimeError):
     def __init__(self, fn: str, status: int, text: str):
         super().__init__(f"{fn}: {text} (status {status})")
@@ -106,7 +110,7 @@ def lib():
         "moe_forward_train": [cfgp, ctypes.POINTER(MoeWeights), vp, vp, vp, ctypes.POINTER(MoeSaved),
                               vp, vp, sz, vp],
         "moe_backward": [cfgp, ctypes.POINTER(MoeWeights), vp, ctypes.POINTER(MoeSaved), vp,
-                         ctypes.c_double, ctypes.POINTER(MoeGrads), vp, sz, vp],
+                         ctypes.POINTER(MoeLossWeights), ctypes.POINTER(MoeGrads), vp, sz, vp],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)

@@ -15,7 +15,7 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from ._lib import MoeAux, MoeConfig, MoeGrads, MoeSaved, MoeWeights, check, lib
+from ._lib import MoeAux, MoeConfig, MoeGrads, MoeLossWeights, MoeSaved, MoeWeights, check, lib
 
 _TORCH_DT = {_lib.MOE_DTYPE_F32: torch.float32, _lib.MOE_DTYPE_BF16: torch.bfloat16}
 
@@ -250,9 +250,11 @@ def moe_forward(cfg: MoeConfig, weights: LayerWeights, x, router_noise=None):
 class TrainStep:
     """moe_forward_train + moe_backward with their buffers allocated once.
 
-    forward(x, router_noise=None) -> y; backward(dy, aux_scale=1.0) -> dict
-    of gradient tensors (dx in the activation dtype, the rest float32), for
-    the x / noise of the last forward."""
+    forward(x, router_noise=None) -> y; backward(dy, aux_scale=1.0,
+    loss_weights=None) -> dict of gradient tensors (dx in the activation
+    dtype, the rest float32), for the x / noise of the last forward.  The aux
+    part of the loss is aux_scale * (0.01 lb + 0.001 z), or loss_weights
+    (dict with keys load_balance, z_loss, lb_squares, kl_uniform) when given."""
 
     def __init__(self, cfg: MoeConfig, weights: LayerWeights):
         self.cfg = cfg
@@ -298,7 +300,7 @@ class TrainStep:
         self.fws = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=dev)
         m = ctypes.c_size_t(0)
         check("moe_backward", L.moe_backward(ctypes.byref(cfg), ctypes.byref(self._w), None, None, None,
-                                             1.0, None, None, ctypes.byref(m), None))
+                                             None, None, None, ctypes.byref(m), None))
         self.bws = torch.empty(max(int(m.value), 1), dtype=torch.uint8, device=dev)
         self.x = None
 
@@ -310,9 +312,13 @@ class TrainStep:
             ctypes.byref(self._s), _p(self.aux), _p(self.fws), ctypes.byref(n), _stream()))
         return self.y
 
-    def backward(self, dy, aux_scale=1.0):
+    def backward(self, dy, aux_scale=1.0, loss_weights=None):
+        if loss_weights is None:
+            lw = MoeLossWeights(load_balance=0.01 * aux_scale, z_loss=0.001 * aux_scale)
+        else:
+            lw = MoeLossWeights(**{k: float(v) for k, v in loss_weights.items()})
         n = ctypes.c_size_t(self.bws.numel())
         check("moe_backward", lib().moe_backward(
             ctypes.byref(self.cfg), ctypes.byref(self._w), _p(self.x), ctypes.byref(self._s), _p(dy),
-            float(aux_scale), ctypes.byref(self._g), _p(self.bws), ctypes.byref(n), _stream()))
+            ctypes.byref(lw), ctypes.byref(self._g), _p(self.bws), ctypes.byref(n), _stream()))
         return self.grads

@@ -89,12 +89,41 @@ combine_bwd_kernel(const uint16_t* __restrict__ dy, const uint16_t* __restrict__
 
 constexpr int kMaxPerLane = kMaxExperts / kWave;
 
+// Per-expert part of dL/dp from the load-balance terms (one workgroup per
+// expert): c_lb E f_e / T + c_sq 2 E P_e / T - c_kl / (E (P_e + 1e-8) T),
+// with P_e the mean over tokens of p = exp(s - lse) (fixed-order tree sum;
+// only summed when a P term is weighted).
+__global__ void __launch_bounds__(kThreads)
+aux_dp_kernel(const float* __restrict__ scores, const float* __restrict__ lse,
+              const int32_t* __restrict__ counts, int64_t T, int E, int k, double c_lb,
+              double c_sq, double c_kl, float* __restrict__ aux_dp) {
+  __shared__ float red[kThreads];
+  const int e = blockIdx.x;
+  double P = 0.0;
+  if (c_sq != 0.0 || c_kl != 0.0) {
+    float acc = 0.f;
+    for (int64_t t = threadIdx.x; t < T; t += kThreads) acc += __expf(scores[t * E + e] - lse[t]);
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int o = kThreads / 2; o > 0; o >>= 1) {
+      if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+      __syncthreads();
+    }
+    P = (double)red[0] / (double)T;
+  }
+  if (threadIdx.x == 0) {
+    const double f = (double)counts[e] / (double)(T * k);
+    double g = c_lb * E * f + c_sq * 2.0 * E * P;
+    if (c_kl != 0.0) g -= c_kl / ((double)E * (P + 1e-8));
+    aux_dp[e] = (float)(g / (double)T);
+  }
+}
+
 __global__ void __launch_bounds__(kThreads)
 router_grad_kernel(const float* __restrict__ scores, const float* __restrict__ lse,
                    const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_w,
-                   const float* __restrict__ d_topk_w, const int32_t* __restrict__ counts,
-                   int64_t T, int E, int k, float c_lb, float c_z, float inv_tau,
-                   float* __restrict__ dl) {
+                   const float* __restrict__ d_topk_w, const float* __restrict__ aux_dp,
+                   int64_t T, int E, int k, float c_z, float inv_tau, float* __restrict__ dl) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int64_t t = (int64_t)blockIdx.x * (kThreads / kWave) + wave;
   if (t >= T) return;
@@ -107,9 +136,8 @@ router_grad_kernel(const float* __restrict__ scores, const float* __restrict__ l
     S1 += d_topk_w[t * k + j] * topk_w[t * k + j];
   }
   const float invP = 1.f / P;
-  // c_lb = aux_scale * 0.01 * E / T (times f_e), c_z = aux_scale * 0.001 * 2 / T
+  // aux_dp[e]: the load-balance terms; c_z = (z weight) * 2 / T
   float p[kMaxPerLane], dp[kMaxPerLane];
-  const float f_norm = 1.f / (float)(T * k);
   float sp = 0.f;
 #pragma unroll
   for (int i = 0; i < kMaxPerLane; ++i) {
@@ -118,7 +146,7 @@ router_grad_kernel(const float* __restrict__ scores, const float* __restrict__ l
     dp[i] = 0.f;
     if (e < E) {
       p[i] = __expf(scores[t * E + e] - l);
-      dp[i] = c_lb * ((float)counts[e] * f_norm);
+      dp[i] = aux_dp[e];
     }
   }
   for (int j = 0; j < k; ++j) {
@@ -509,13 +537,17 @@ hipError_t launch_combine_bwd(const moe_config& c, const void* dy, const void* y
 
 hipError_t launch_router_grad(const moe_config& c, const float* scores, const float* lse,
                               const int32_t* topk_idx, const float* topk_w, const float* d_topk_w,
-                              const int32_t* counts, double aux_scale, float* dl, hipStream_t s) {
-  const double T = (double)c.n_tokens;
-  const float c_lb = (float)(aux_scale * 0.01 * c.n_experts / T);
-  const float c_z = (float)(aux_scale * 0.001 * 2.0 / T);
+                              const int32_t* counts, const moe_loss_weights& lw, float* aux_dp,
+                              float* dl, hipStream_t s) {
+  aux_dp_kernel<<<c.n_experts, kThreads, 0, s>>>(scores, lse, counts, c.n_tokens, c.n_experts,
+                                                 c.top_k, lw.load_balance, lw.lb_squares,
+                                                 lw.kl_uniform, aux_dp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const float c_z = (float)(lw.z_loss * 2.0 / (double)c.n_tokens);
   const float inv_tau = c.router_temperature == 0.f ? 1.f : 1.f / c.router_temperature;
   router_grad_kernel<<<blocks_for(c.n_tokens, kThreads / kWave), kThreads, 0, s>>>(
-      scores, lse, topk_idx, topk_w, d_topk_w, counts, c.n_tokens, c.n_experts, c.top_k, c_lb, c_z,
+      scores, lse, topk_idx, topk_w, d_topk_w, aux_dp, c.n_tokens, c.n_experts, c.top_k, c_z,
       inv_tau, dl);
   return hipGetLastError();
 }

@@ -519,11 +519,15 @@ moe_status moe_forward_train(const moe_config* cfg, const moe_weights* w, const 
 }
 
 moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void* x,
-                        const moe_saved* sv, const void* dy, double aux_scale,
+                        const moe_saved* sv, const void* dy, const moe_loss_weights* lw_in,
                         const moe_grads* g, void* ws, size_t* ws_bytes, hipStream_t stream) {
   moe_status st = check_train(cfg);
   if (st != MOE_OK) return st;
-  if (!std::isfinite(aux_scale)) return MOE_ERR_INVALID_ARG;
+  moe_loss_weights lw{0.01, 0.001, 0.0, 0.0};  // the pages' training loss
+  if (lw_in) lw = *lw_in;
+  if (!std::isfinite(lw.load_balance) || !std::isfinite(lw.z_loss) ||
+      !std::isfinite(lw.lb_squares) || !std::isfinite(lw.kl_uniform))
+    return MOE_ERR_INVALID_ARG;
   const moe_config& c = *cfg;
   const int64_t T = c.n_tokens, R = T * c.top_k;
   const int E = c.n_experts, S = c.n_shared, d = c.d_model, f = c.d_ffn;
@@ -535,7 +539,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
 
   struct Plan {
     void *dO, *W2t, *W1t, *dH, *dA, *dXr, *dOt, *Ht, *dAt, *Xt;
-    float *dw, *dl, *dxr, *wr_part;
+    float *dw, *dl, *dxr, *wr_part, *aux_dp;
     int32_t *poff, *colrow;
     void *Ws2t, *Ws1t, *dHs, *dAs, *dXs, *dyt, *Hst, *dAst, *xt;
   };
@@ -544,6 +548,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
     p.dO = cv.take<uint16_t>(R * d);
     p.dw = cv.take<float>(R);
     p.dl = cv.take<float>(T * E);
+    p.aux_dp = cv.take<float>(E);
     p.dxr = cv.take<float>(T * d);
     p.wr_part = cv.take<float>(nsplit > 1 ? (size_t)nsplit * E * d : 0);
     p.W2t = cv.take<uint16_t>((size_t)E * f * d);
@@ -593,7 +598,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
   // combine and router
   MOE_HIP_TRY(launch_combine_bwd(c, dy, sv->y_perm, sv->inv_row, sv->topk_w, p.dO, p.dw, stream));
   MOE_HIP_TRY(launch_router_grad(c, sv->scores, sv->token_lse, sv->topk_idx, sv->topk_w, p.dw,
-                                 sv->expert_counts, aux_scale, p.dl, stream));
+                                 sv->expert_counts, lw, p.aux_dp, p.dl, stream));
   MOE_HIP_TRY(launch_simt_gemm(p.dl, 1, E, x, d, E, d, T, nsplit, g->dw_router, d, p.wr_part,
                                stream));
   if (g->drouter_bias) MOE_HIP_TRY(launch_colsum_f32(p.dl, T, E, g->drouter_bias, stream));

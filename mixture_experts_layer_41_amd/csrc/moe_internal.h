@@ -142,7 +142,8 @@ hipError_t launch_combine_bwd(const moe_config& c, const void* dy, const void* y
                               float* d_topk_w, hipStream_t s);
 hipError_t launch_router_grad(const moe_config& c, const float* scores, const float* lse,
                               const int32_t* topk_idx, const float* topk_w, const float* d_topk_w,
-                              const int32_t* counts, double aux_scale, float* dl, hipStream_t s);
+                              const int32_t* counts, const moe_loss_weights& lw, float* aux_dp,
+                              float* dl, hipStream_t s);
 hipError_t launch_pad_offsets(const int32_t* offsets, int G, int pad, int64_t ncols, int32_t* poff,
                               int32_t* colrow, hipStream_t s);
 hipError_t launch_transpose(const void* src, int64_t src_ld, int64_t src_batch,

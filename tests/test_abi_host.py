@@ -265,7 +265,7 @@ def _train_query(L, c, w=None):
     st1 = L.moe_forward_train(ctypes.byref(c), ctypes.byref(w), None, None, None, None, None, None,
                               ctypes.byref(n), None)
     m = ctypes.c_size_t(0)
-    st2 = L.moe_backward(ctypes.byref(c), ctypes.byref(w), None, None, None, 1.0, None, None,
+    st2 = L.moe_backward(ctypes.byref(c), ctypes.byref(w), None, None, None, None, None, None,
                          ctypes.byref(m), None)
     return st1, n.value, st2, m.value
 
@@ -305,16 +305,17 @@ def test_training_argument_checks(L):
     # the backward needs dy, the saved state and the required gradient buffers
     g = _lib.MoeGrads(dx=P, dw_router=P, dw1=P, dw2=P)
     mm = ctypes.c_size_t(m)
-    assert L.moe_backward(ctypes.byref(c), ctypes.byref(w), P, ctypes.byref(sv), None, 1.0,
+    assert L.moe_backward(ctypes.byref(c), ctypes.byref(w), P, ctypes.byref(sv), None, None,
                           ctypes.byref(g), P, ctypes.byref(mm), None) == INVALID
     for miss in ("dx", "dw_router", "dw1", "dw2"):
         bad = _lib.MoeGrads(dx=P, dw_router=P, dw1=P, dw2=P)
         setattr(bad, miss, None)
-        assert L.moe_backward(ctypes.byref(c), ctypes.byref(w), P, ctypes.byref(sv), P, 1.0,
+        assert L.moe_backward(ctypes.byref(c), ctypes.byref(w), P, ctypes.byref(sv), P, None,
                               ctypes.byref(bad), P, ctypes.byref(mm), None) == INVALID, miss
     # biases present: their gradients are required
     wb = _lib.MoeWeights(w_router=P, w1=P, w2=P, b1=P)
-    assert L.moe_backward(ctypes.byref(c), ctypes.byref(wb), P, ctypes.byref(sv), P, 1.0,
+    assert L.moe_backward(ctypes.byref(c), ctypes.byref(wb), P, ctypes.byref(sv), P, None,
                           ctypes.byref(g), P, ctypes.byref(mm), None) == INVALID
-    assert L.moe_backward(ctypes.byref(c), ctypes.byref(w), P, ctypes.byref(sv), P, math.nan,
-                          ctypes.byref(g), P, ctypes.byref(mm), None) == INVALID
+    bad_lw = _lib.MoeLossWeights(load_balance=0.01, z_loss=math.nan)
+    assert L.moe_backward(ctypes.byref(c), ctypes.byref(w), P, ctypes.byref(sv), P,
+                          ctypes.byref(bad_lw), ctypes.byref(g), P, ctypes.byref(mm), None) == INVALID

@@ -38,7 +38,9 @@ def bf16_dy(cfg, seed):
     return f32_to_bf16_bits(z)
 
 
-def run_case(cfg, aux_scale, seed, full_compare=True):
+def run_case(cfg, aux_scale, seed, loss_weights=None):
+    """loss_weights: None (aux_scale * (0.01 lb + 0.001 z)) or a dict with
+    keys load_balance, z_loss, lb_squares, kl_uniform."""
     t = inputs(cfg)
     dy_bits = bf16_dy(cfg, seed)
     dy64 = oracle.decode(dy_bits, "bf16")
@@ -64,9 +66,12 @@ def run_case(cfg, aux_scale, seed, full_compare=True):
     assert err <= 2e-2, f"training forward y err {err:.3e}"
 
     say(f"[backward] {cfg.name}")
-    g = st.backward(dy, aux_scale)
+    g = st.backward(dy, aux_scale, loss_weights)
     torch.cuda.synchronize()
-    ref = oracle.backward(cfg, t, dy64, aux_scale)
+    lw_ref = None if loss_weights is None else {
+        "lb": loss_weights["load_balance"], "z": loss_weights["z_loss"],
+        "lb_squares": loss_weights["lb_squares"], "kl_uniform": loss_weights["kl_uniform"]}
+    ref = oracle.backward(cfg, t, dy64, aux_scale, loss_weights=lw_ref)
     errs = {}
     for key in GRADS:
         if key not in ref or g.get(key) is None:
@@ -78,7 +83,7 @@ def run_case(cfg, aux_scale, seed, full_compare=True):
         assert e <= GRAD_TOL, f"{key} normwise err {e:.3e}"
     # determinism: the same backward again, bit for bit
     snap = {k: v.clone() for k, v in g.items() if v is not None}
-    g2 = st.backward(dy, aux_scale)
+    g2 = st.backward(dy, aux_scale, loss_weights)
     torch.cuda.synchronize()
     for k, v in snap.items():
         a, b = v.view(torch.int16) if v.dtype == torch.bfloat16 else v, g2[k]
@@ -119,3 +124,19 @@ def test_backward_full_size(name):
     cfg = get_config(name)
     say(f"[case] {name}: {cfg.name}")
     run_case(cfg, 1.0, seed=902)
+
+
+# the load-balance forms of both explainers as training-loss terms, with
+# weights large enough that the router gradient is mostly theirs
+LW = {"load_balance": 0.5, "z_loss": 0.05, "lb_squares": 2.0, "kl_uniform": 3.0}
+
+
+@pytest.mark.parametrize("name", ["lb_forms_small", "lb_forms_c2"])
+def test_backward_load_balance_forms(name):
+    if name == "lb_forms_small":
+        cfg = LayerConfig(name, T=300, d=64, E=12, k=3, f=64, S=1, dtype="bf16", act="swiglu",
+                          router_bias="zipf", router_temperature=1.3, router_noise_std=0.5, seed=950)
+    else:
+        cfg = get_config("c2")
+    say(f"[case] {name}")
+    run_case(cfg, 1.0, seed=951, loss_weights=LW)
