@@ -16,6 +16,7 @@ Prints ONE JSON line (rank 0).  Extra legs:
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -49,6 +50,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-backward", action="store_true", help="skip the training (backward) leg")
+    ap.add_argument("--top-k", type=int, default=None,
+                    help="override the workload's k (e.g. top-1 against top-2 inference)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling HBM byte counters)")
     return ap.parse_args()
@@ -111,6 +114,8 @@ def main():
 
     torch.cuda.set_device(0)
     cfg = get_config(args.workload)
+    if args.top_k is not None:
+        cfg = dataclasses.replace(cfg, k=args.top_k, name=f"{cfg.name}_top{args.top_k}")
     log(f"[bench] workload {cfg.name}")
     # raw seeded draws (no tie rejection: timing only); expert weight stacks
     # stay lazy (generated one expert at a time) unless the CPU leg needs them
