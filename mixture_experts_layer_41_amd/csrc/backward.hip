@@ -8,19 +8,26 @@
 // from the training forward) and the weight-gradient kernel of
 // gemm_wgrad.hip.
 //
-//   combine_bwd     d o_tj = w_tj dy_t into the kept row, dw_tj = dy_t . o_tj
-//   router_grad     renormalisation, aux terms, softmax and 1/tau:
-//                   scores [T, E] -> dl [T, E] (float32)
-//   pad_offsets     per-group columns padded to multiples of the K tile, and
-//                   for each padded column its source row (-1: zero padding)
-//   transpose       [rows, C] -> [C, columns]: the weights, and d_o and the
-//                   gathered x into the padded columns, optional row gather
+//   aux_dp          per-expert load-balance part of dL/dp when it needs the
+//                   mean router probability (one workgroup per expert)
+//   combine_router  one wave per token: d o_tj = w_tj dy_t into the kept
+//                   row, dw_tj = dy_t . o_tj, then renormalisation, aux
+//                   terms, softmax and 1/tau: dl [T, E] (float32); extra
+//                   workgroups of the same launch pad the group offsets to
+//                   multiples of the K tile and map every padded column to
+//                   its source row (-1: zero padding)
+//   transpose       [rows, C] -> [C, columns], two problems per launch: the
+//                   weights, and d_o and the gathered x into the padded
+//                   columns
 //   act_bwd_t       a, dh -> da (row-major) and da^T, h^T (padded columns)
 //   seg_rowsum      bias gradients: sums of each row of a transposed matrix
 //                   over each group's columns
-//   dx_gather       dx_t = sum_j dx_rows[row_tj] + shared + router + residual
-//   simt_gemm       router gradients (float32, split K)
+//   router_wgrad    dW_r = dl^T x and db_r = column sums of dl (float32,
+//                   split over tokens), reduce_splits sums the splits
+//   dx_final        dx_t = dl_t W_r + sum_j dx_rows[row_tj] + shared +
+//                   residual
 // Every reduction runs in a fixed order: no atomics.
+#include <algorithm>
 #include <cmath>
 
 #include "moe_internal.h"
@@ -31,7 +38,6 @@ namespace {
 constexpr int kThreads = 256;
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ float bf(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
@@ -50,68 +56,31 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // ---------------------------------------------------------------------------
-// combine backward: one wave per token, 16-byte chunks of the row per lane
-
-__global__ void __launch_bounds__(kThreads)
-combine_bwd_kernel(const uint16_t* __restrict__ dy, const uint16_t* __restrict__ y_perm,
-                   const int32_t* __restrict__ inv_row, const float* __restrict__ topk_w, int64_t T,
-                   int d, int k, uint16_t* __restrict__ d_yperm, float* __restrict__ d_topk_w) {
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int64_t t = (int64_t)blockIdx.x * (kThreads / kWave) + wave;
-  if (t >= T) return;
-  const int nch = d / 8;
-  for (int j = 0; j < k; ++j) {
-    const int32_t row = inv_row[t * k + j];
-    if (row < 0) {  // dropped: no output, no gradient
-      if (lane == 0) d_topk_w[t * k + j] = 0.f;
-      continue;
-    }
-    const float wj = topk_w[t * k + j];
-    float dot = 0.f;
-    for (int c = lane; c < nch; c += kWave) {
-      float g[8], o[8], r[8];
-      unpack8(*reinterpret_cast<const u32x4v*>(dy + t * d + c * 8), g);
-      unpack8(*reinterpret_cast<const u32x4v*>(y_perm + (int64_t)row * d + c * 8), o);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        dot += g[i] * o[i];
-        r[i] = wj * g[i];
-      }
-      *reinterpret_cast<u32x4v*>(d_yperm + (int64_t)row * d + c * 8) = pack8(r);
-    }
-    dot = wave_sum(dot);
-    if (lane == 0) d_topk_w[t * k + j] = dot;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// router gradient: one wave per token, expert e on lane e % 64
+// router gradient
 
 constexpr int kMaxPerLane = kMaxExperts / kWave;
 
 // Per-expert part of dL/dp from the load-balance terms (one workgroup per
 // expert): c_lb E f_e / T + c_sq 2 E P_e / T - c_kl / (E (P_e + 1e-8) T),
-// with P_e the mean over tokens of p = exp(s - lse) (fixed-order tree sum;
-// only summed when a P term is weighted).
+// with P_e the mean over tokens of p = exp(s - lse) (fixed-order tree sum).
+// Launched only when a P term is weighted; otherwise the combine/router
+// kernel takes c_lb E f_e / T from the counts itself.
 __global__ void __launch_bounds__(kThreads)
 aux_dp_kernel(const float* __restrict__ scores, const float* __restrict__ lse,
               const int32_t* __restrict__ counts, int64_t T, int E, int k, double c_lb,
               double c_sq, double c_kl, float* __restrict__ aux_dp) {
   __shared__ float red[kThreads];
   const int e = blockIdx.x;
-  double P = 0.0;
-  if (c_sq != 0.0 || c_kl != 0.0) {
-    float acc = 0.f;
-    for (int64_t t = threadIdx.x; t < T; t += kThreads) acc += __expf(scores[t * E + e] - lse[t]);
-    red[threadIdx.x] = acc;
+  float acc = 0.f;
+  for (int64_t t = threadIdx.x; t < T; t += kThreads) acc += __expf(scores[t * E + e] - lse[t]);
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int o = kThreads / 2; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
     __syncthreads();
-    for (int o = kThreads / 2; o > 0; o >>= 1) {
-      if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
-      __syncthreads();
-    }
-    P = (double)red[0] / (double)T;
   }
   if (threadIdx.x == 0) {
+    const double P = (double)red[0] / (double)T;
     const double f = (double)counts[e] / (double)(T * k);
     double g = c_lb * E * f + c_sq * 2.0 * E * P;
     if (c_kl != 0.0) g -= c_kl / ((double)E * (P + 1e-8));
@@ -119,81 +88,59 @@ aux_dp_kernel(const float* __restrict__ scores, const float* __restrict__ lse,
   }
 }
 
-__global__ void __launch_bounds__(kThreads)
-router_grad_kernel(const float* __restrict__ scores, const float* __restrict__ lse,
-                   const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_w,
-                   const float* __restrict__ d_topk_w, const float* __restrict__ aux_dp,
-                   int64_t T, int E, int k, float c_z, float inv_tau, float* __restrict__ dl) {
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int64_t t = (int64_t)blockIdx.x * (kThreads / kWave) + wave;
-  if (t >= T) return;
-  const float l = lse[t];
-  // P = sum of the selected probabilities, S1 = sum_j dw_j w_j
-  float P = 0.f, S1 = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int e = topk_idx[t * k + j];
-    P += __expf(scores[t * E + e] - l);
-    S1 += d_topk_w[t * k + j] * topk_w[t * k + j];
-  }
-  const float invP = 1.f / P;
-  // aux_dp[e]: the load-balance terms; c_z = (z weight) * 2 / T
-  float p[kMaxPerLane], dp[kMaxPerLane];
-  float sp = 0.f;
-#pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
-    const int e = lane + kWave * i;
-    p[i] = 0.f;
-    dp[i] = 0.f;
-    if (e < E) {
-      p[i] = __expf(scores[t * E + e] - l);
-      dp[i] = aux_dp[e];
-    }
-  }
-  for (int j = 0; j < k; ++j) {
-    const int e = topk_idx[t * k + j];
-    const float g = (d_topk_w[t * k + j] - S1) * invP;
-#pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i)
-      if (e == lane + kWave * i) dp[i] += g;
-  }
-#pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) sp += p[i] * dp[i];
-  sp = wave_sum(sp);
-#pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
-    const int e = lane + kWave * i;
-    if (e < E) dl[t * E + e] = (p[i] * (dp[i] - sp) + c_z * l * p[i]) * inv_tau;
-  }
-}
+struct CombineRouterArgs {
+  // combine backward
+  const uint16_t* dy;
+  const uint16_t* y_perm;
+  const int32_t* inv_row;
+  const float* topk_w;
+  uint16_t* d_yperm;
+  // router backward
+  const float* scores;
+  const float* lse;
+  const int32_t* topk_idx;
+  const int32_t* counts;
+  const float* aux_dp;  // [E], or null: lb_coef * counts[e]
+  double lb_coef;       // load-balance weight * E / (T k T)
+  float c_z;            // z-loss weight * 2 / T
+  float inv_tau;
+  float* dl;
+  int64_t T;
+  int d, E, k;
+  unsigned nb_tok;  // workgroups of the token part; the rest pad the offsets
+  // padded group offsets
+  const int32_t* offsets;
+  int pad;
+  int64_t ncols;
+  int32_t* poff;
+  int32_t* colrow;
+};
 
-// ---------------------------------------------------------------------------
-// padded group offsets: poff[g] = sum_{g' < g} roundup(rows_g', pad); for
-// every padded column j < ncols: colrow[j] = source row, -1 (padding inside
-// a group) or -2 (past the last group).  Every workgroup scans the offsets in
-// LDS; workgroup 0 also writes poff.
-
-__global__ void __launch_bounds__(kThreads)
-pad_offsets_kernel(const int32_t* __restrict__ offsets, int G, int pad, int64_t ncols,
-                   int32_t* __restrict__ poff, int32_t* __restrict__ colrow) {
+// poff[g] = sum_{g' < g} roundup(rows_g', pad); for every padded column
+// j < ncols: colrow[j] = source row, -1 (padding inside a group) or -2 (past
+// the last group).  Every workgroup scans the offsets in LDS; workgroup 0
+// also writes poff.
+__device__ void pad_offsets_part(const CombineRouterArgs& a, unsigned b) {
   __shared__ int32_t s_off[kMaxExperts + 1], s_poff[kMaxExperts + 1];
-  for (int g = threadIdx.x; g <= G; g += kThreads) s_off[g] = offsets[g];
+  const int G = a.E;
+  for (int g = threadIdx.x; g <= G; g += kThreads) s_off[g] = a.offsets[g];
   __syncthreads();
   if (threadIdx.x == 0) {
     int32_t acc = 0;
     for (int g = 0; g < G; ++g) {
       s_poff[g] = acc;
       const int32_t rows = s_off[g + 1] - s_off[g];
-      acc += (rows + pad - 1) / pad * pad;
+      acc += (rows + a.pad - 1) / a.pad * a.pad;
     }
     s_poff[G] = acc;
   }
   __syncthreads();
-  if (blockIdx.x == 0)
-    for (int g = threadIdx.x; g <= G; g += kThreads) poff[g] = s_poff[g];
-  const int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (j >= ncols) return;
+  if (b == 0)
+    for (int g = threadIdx.x; g <= G; g += kThreads) a.poff[g] = s_poff[g];
+  const int64_t j = (int64_t)b * kThreads + threadIdx.x;
+  if (j >= a.ncols) return;
   if (j >= s_poff[G]) {
-    colrow[j] = -2;
+    a.colrow[j] = -2;
     return;
   }
   int lo = 0, hi = G - 1;  // last g with s_poff[g] <= j
@@ -202,33 +149,197 @@ pad_offsets_kernel(const int32_t* __restrict__ offsets, int G, int pad, int64_t 
     if (s_poff[mid] <= j) lo = mid; else hi = mid - 1;
   }
   const int32_t r = s_off[lo] + (int32_t)(j - s_poff[lo]);
-  colrow[j] = r < s_off[lo + 1] ? r : -1;
+  a.colrow[j] = r < s_off[lo + 1] ? r : -1;
+}
+
+// One wave per token.  Combine backward: for each kept assignment j,
+// d o_tj = w_tj dy_t goes to its row of d_yperm and dw_tj = dy_t . o_tj (0
+// for a dropped one); the dw_tj stay in the wave's LDS row.  Router
+// backward, expert e on lane e % 64: with p = softmax(s), P = sum of the
+// selected p and w_j = p_j / P, dL/dp_e = (dw_e - sum_j dw_j w_j) / P for a
+// selected e, plus the load-balance part; dl = (p (dL/dp - p . dL/dp) +
+// c_z lse p) / tau.
+template <int NPL>  // experts per lane: E <= 64 * NPL
+__global__ void __launch_bounds__(kThreads) combine_router_bwd_kernel(CombineRouterArgs a) {
+  __shared__ float s_dw[kThreads / kWave][kMaxExperts];
+  if (blockIdx.x >= a.nb_tok) {
+    pad_offsets_part(a, blockIdx.x - a.nb_tok);
+    return;
+  }
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int64_t t = (int64_t)blockIdx.x * (kThreads / kWave) + wave;
+  if (t >= a.T) return;
+  const int d = a.d, E = a.E, k = a.k;
+  float* dw = s_dw[wave];
+  const int nch = d / 8;
+  // router inputs first, so that they arrive while the combine part runs:
+  // the scores of the lane's experts, and lane j < k holds assignment j
+  const float l = a.lse[t];
+  float sc[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int e = lane + kWave * i;
+    sc[i] = e < E ? a.scores[t * E + e] : 0.f;
+  }
+  int ej = 0;
+  float wl = 0.f, sj = 0.f;
+  if (lane < k) {
+    ej = a.topk_idx[t * k + lane];
+    wl = a.topk_w[t * k + lane];
+    sj = a.scores[t * E + ej];
+  }
+
+  // combine backward, two assignments at a time (row < 0: dropped, no
+  // output and no gradient)
+  for (int j0 = 0; j0 < k; j0 += 2) {
+    int32_t row[2];
+    float wj[2], dot[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const bool in = j0 + q < k;
+      row[q] = in ? a.inv_row[t * k + j0 + q] : -1;
+      wj[q] = in ? a.topk_w[t * k + j0 + q] : 0.f;
+      dot[q] = 0.f;
+    }
+    for (int c = lane; c < nch; c += kWave) {
+      float g[8];
+      unpack8(*reinterpret_cast<const u32x4v*>(a.dy + t * d + c * 8), g);
+      u32x4v raw[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        raw[q] = u32x4v{0u, 0u, 0u, 0u};
+        if (row[q] >= 0)
+          raw[q] = *reinterpret_cast<const u32x4v*>(a.y_perm + (int64_t)row[q] * d + c * 8);
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        if (row[q] < 0) continue;
+        float o[8], r[8];
+        unpack8(raw[q], o);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          dot[q] += g[i] * o[i];
+          r[i] = wj[q] * g[i];
+        }
+        *reinterpret_cast<u32x4v*>(a.d_yperm + (int64_t)row[q] * d + c * 8) = pack8(r);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if (j0 + q >= k) break;
+      const float sum = row[q] >= 0 ? wave_sum(dot[q]) : 0.f;  // row is the same on every lane
+      if (lane == 0) dw[j0 + q] = sum;
+    }
+  }
+  // LDS accesses of one wave complete in order: the reads below see lane 0's
+  // writes; the barrier keeps the compiler from moving them
+  __builtin_amdgcn_wave_barrier();
+
+  // P = sum of the selected probabilities, S1 = sum_j dw_j w_j
+  float P = 0.f, S1 = 0.f;
+  if (lane < k) {
+    P = __expf(sj - l);
+    S1 = dw[lane] * wl;
+  }
+  for (int j = kWave + lane; j < k; j += kWave) {
+    P += __expf(a.scores[t * E + a.topk_idx[t * k + j]] - l);
+    S1 += dw[j] * a.topk_w[t * k + j];
+  }
+  P = wave_sum(P);
+  S1 = wave_sum(S1);
+  const float invP = 1.f / P;
+  float p[NPL], dp[NPL];
+  float sp = 0.f;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int e = lane + kWave * i;
+    p[i] = 0.f;
+    dp[i] = 0.f;
+    if (e < E) {
+      p[i] = __expf(sc[i] - l);
+      dp[i] = a.aux_dp ? a.aux_dp[e] : (float)(a.lb_coef * (double)a.counts[e]);
+    }
+  }
+  // dL/dp of the selected experts: assignment j's (expert, value) from lane j
+  const float gl = lane < k ? (dw[lane] - S1) * invP : 0.f;
+  const int k0 = k < kWave ? k : kWave;
+  for (int j = 0; j < k0; ++j) {
+    const int e = __shfl(ej, j);
+    const float g = __shfl(gl, j);
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      if (e == lane + kWave * i) dp[i] += g;
+  }
+  for (int j = kWave; j < k; ++j) {
+    const int e = a.topk_idx[t * k + j];
+    const float g = (dw[j] - S1) * invP;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      if (e == lane + kWave * i) dp[i] += g;
+  }
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) sp += p[i] * dp[i];
+  sp = wave_sum(sp);
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int e = lane + kWave * i;
+    if (e < E) a.dl[t * E + e] = (p[i] * (dp[i] - sp) + a.c_z * l * p[i]) * a.inv_tau;
+  }
 }
 
 // ---------------------------------------------------------------------------
-// transpose of 2-byte elements through a 64 x 64 LDS tile, 16-byte global
+// transpose of 2-byte elements through a 128 x 128 LDS tile, 16-byte global
 // loads and stores (C, the destination leading dimension and every chunk
-// start are multiples of 8 elements).
+// start are multiples of 8 elements).  One problem:
 // dst[b][c][j] = src[b][row(j)][c] for c < C and destination columns j < ncols,
 // with row(j) = colrow ? colrow[j] : (j < nsrc ? j : -1), gathered through
 // `gather` when given; rows -1 and -2 (past the last group) read as 0.
-// Destination chunks of 8 columns at or past ncols are not written.
+// Destination chunks of 8 columns at or past ncols are not written.  A
+// launch runs two problems, one workgroup per tile: the first problem's
+// tiles, then the second's.
+//
+// LDS: tile row jj (a source row) holds its 16 chunks of 8 columns with
+// chunk ch stored at position ch ^ (jj / 8 % 16).  The read phase takes one
+// column from rows jc * 8 + r of the 16 chunk-columns jc at once; the XOR
+// puts those 16 reads in 16 distinct bank groups.
 
-constexpr int kTP = 72;  // LDS row pitch (elements): 64 + 8 keeps rows 16-byte aligned
+struct TransposeJob {
+  const uint16_t* src;
+  int64_t src_ld, src_batch;
+  const int32_t* colrow;
+  const int32_t* gather;
+  int64_t nsrc, ncols;
+  int C;
+  uint16_t* dst;
+  int64_t dst_ld, dst_batch;
+  unsigned tx, ty;  // tiles along the columns j and along C
+};
+
+constexpr int kTT = 128;
+constexpr int kTC = kTT / 8;  // 16-byte chunks per tile row
 
 __global__ void __launch_bounds__(kThreads)
-transpose_kernel(const uint16_t* __restrict__ src, int64_t src_ld, int64_t src_batch,
-                 const int32_t* __restrict__ colrow, const int32_t* __restrict__ gather,
-                 int64_t nsrc, int64_t ncols, int C, uint16_t* __restrict__ dst, int64_t dst_ld,
-                 int64_t dst_batch) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * kTP];
-  __shared__ int32_t rows[64];
-  const int64_t j0 = (int64_t)blockIdx.x * 64;
-  const int c0 = blockIdx.y * 64;
-  const uint16_t* S = src + (int64_t)blockIdx.z * src_batch;
-  uint16_t* D = dst + (int64_t)blockIdx.z * dst_batch;
-  if (threadIdx.x < 64) {
-    const int64_t j = j0 + threadIdx.x;
+transpose_kernel(TransposeJob j0, TransposeJob j1, unsigned n0) {
+  __shared__ __attribute__((aligned(16))) u32x4v tile[kTT * kTC];
+  __shared__ int32_t rows[kTT];
+  unsigned b = blockIdx.x;
+  const bool second = b >= n0;
+  const TransposeJob& J = second ? j1 : j0;
+  if (second) b -= n0;
+  const unsigned bx = b % J.tx;
+  b /= J.tx;
+  const unsigned by = b % J.ty, bz = b / J.ty;
+  const int64_t jt = (int64_t)bx * kTT;
+  const int c0 = (int)by * kTT;
+  const int64_t ncols = J.ncols, nsrc = J.nsrc;
+  const int C = J.C;
+  const int32_t* colrow = J.colrow;
+  const int32_t* gather = J.gather;
+  const uint16_t* S = J.src + (int64_t)bz * J.src_batch;
+  uint16_t* D = J.dst + (int64_t)bz * J.dst_batch;
+  const int64_t src_ld = J.src_ld, dst_ld = J.dst_ld;
+  if (threadIdx.x < kTT) {
+    const int64_t j = jt + threadIdx.x;
     int32_t r = -1;
     if (j < ncols) {
       r = colrow ? colrow[j] : (j < nsrc ? (int32_t)j : -1);
@@ -237,34 +348,49 @@ transpose_kernel(const uint16_t* __restrict__ src, int64_t src_ld, int64_t src_b
     rows[threadIdx.x] = r;
   }
   __syncthreads();
-  // load: 64 source rows x 8 chunks of 8 columns
+  // load: 128 source rows x 16 chunks of 8 columns, all loads in flight
+  u32x4v v[kTT * kTC / kThreads];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < kTT * kTC / kThreads; ++u) {
     const int o = threadIdx.x + kThreads * u;
-    const int jj = o / 8, ch = o % 8;
+    const int jj = o / kTC, ch = o % kTC;
     const int32_t r = rows[jj];
     const int c = c0 + ch * 8;
-    u32x4v v = {0u, 0u, 0u, 0u};
-    if (r >= 0 && c < C) v = *reinterpret_cast<const u32x4v*>(S + (int64_t)r * src_ld + c);
-    *reinterpret_cast<u32x4v*>(&tile[jj * kTP + ch * 8]) = v;
+    // branch-free: out-of-range chunks load the problem's first chunk and
+    // are zeroed after
+    const bool in = r >= 0 && c < C;
+    v[u] = *reinterpret_cast<const u32x4v*>(S + (in ? (int64_t)r * src_ld + c : 0));
+    if (!in) v[u] = u32x4v{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int u = 0; u < kTT * kTC / kThreads; ++u) {
+    const int o = threadIdx.x + kThreads * u;
+    const int jj = o / kTC, ch = o % kTC;
+    tile[jj * kTC + (ch ^ ((jj / 8) % kTC))] = v[u];
   }
   __syncthreads();
-  // store: 64 destination rows (c) x 8 chunks of 8 columns (j)
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  // store: 128 destination rows (c) x 16 chunks of 8 columns (j)
+  const uint16_t* t16 = reinterpret_cast<const uint16_t*>(tile);
+#pragma unroll 2
+  for (int u = 0; u < kTT * kTC / kThreads; ++u) {
     const int o = threadIdx.x + kThreads * u;
-    const int cc = o / 8, jc = o % 8;
+    const int cc = o / kTC, jc = o % kTC;
     const int c = c0 + cc;
-    const int64_t j = j0 + jc * 8;
+    const int64_t j = jt + jc * 8;
     if (c >= C || j >= ncols) continue;
+    // rows jc * 8 + 0..7 all keep column cc in chunk (cc / 8) ^ jc
+    const int base = ((cc / 8) ^ jc) * 8 + cc % 8;
     uint32_t w[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      w[q] = (uint32_t)tile[(jc * 8 + 2 * q) * kTP + cc] |
-             ((uint32_t)tile[(jc * 8 + 2 * q + 1) * kTP + cc] << 16);
+      w[q] = (uint32_t)t16[(jc * 8 + 2 * q) * kTT + base] |
+             ((uint32_t)t16[(jc * 8 + 2 * q + 1) * kTT + base] << 16);
     *reinterpret_cast<u32x4v*>(D + (int64_t)c * dst_ld + j) = u32x4v{w[0], w[1], w[2], w[3]};
   }
 }
+
+// act_bwd_t's LDS tiles: 64 rows, pitch 72 elements (rows stay 16-byte aligned)
+constexpr int kTP = 72;
 
 // ---------------------------------------------------------------------------
 // activation backward fused with the transposes the weight gradients need.
@@ -386,187 +512,341 @@ seg_rowsum_kernel(const uint16_t* __restrict__ m, int64_t ld, int C, const int32
   if (lane == 0) out[(int64_t)g * out_ld + c] = acc;
 }
 
-// column sums of a float32 [T, E] matrix (router bias gradient): one
-// workgroup per column, fixed-order tree
-__global__ void __launch_bounds__(kThreads)
-colsum_f32_kernel(const float* __restrict__ m, int64_t T, int E, float* __restrict__ out) {
-  __shared__ float red[kThreads];
-  const int e = blockIdx.x;
-  float acc = 0.f;
-  for (int64_t t = threadIdx.x; t < T; t += kThreads) acc += m[t * E + e];
-  red[threadIdx.x] = acc;
-  __syncthreads();
-  for (int o = kThreads / 2; o > 0; o >>= 1) {
-    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) out[e] = red[0];
-}
-
 // ---------------------------------------------------------------------------
-// dx gather, token-major, 8 columns per thread:
-// dx_t = dx_router_t + sum_j kept dx_rows[row_tj] (+ shared_t) (+ dy_t)
+// router weight and bias gradients, float32 SIMT, split over tokens:
+//   out[s][e][i] = sum_{t in split s} dl[t, e] x[t, i]       (e < E, i < d)
+//   bout[s][e]   = sum_{t in split s} dl[t, e]               (first column tile)
+// 64 x 64 output tiles, 32 tokens per LDS round (the next round's loads in
+// registers while the current one is used), a 4 x 4 block of outputs per
+// thread (16-byte LDS reads and stores).
+// blockIdx.z = split s: tokens [s * kchunk, (s + 1) * kchunk), kchunk a
+// multiple of 32.
+
+constexpr int kRK = 32;
 
 __global__ void __launch_bounds__(kThreads)
-dx_gather_kernel(const uint16_t* __restrict__ dx_rows, const int32_t* __restrict__ inv_row,
-                 const uint16_t* __restrict__ shared, const float* __restrict__ dx_router,
-                 const uint16_t* __restrict__ residual, int64_t T, int d, int k,
-                 uint16_t* __restrict__ dx) {
-  const int nch = d / 8;
-  const int64_t o = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (o >= T * nch) return;
-  const int64_t t = o / nch;
-  const int c = (int)(o % nch) * 8;
-  float acc[8], v[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = dx_router[t * d + c + i];
-  for (int j = 0; j < k; ++j) {
-    const int32_t row = inv_row[t * k + j];
-    if (row < 0) continue;
-    unpack8(*reinterpret_cast<const u32x4v*>(dx_rows + (int64_t)row * d + c), v);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += v[i];
-  }
-  if (shared) {
-    unpack8(*reinterpret_cast<const u32x4v*>(shared + t * d + c), v);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += v[i];
-  }
-  if (residual) {
-    unpack8(*reinterpret_cast<const u32x4v*>(residual + t * d + c), v);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += v[i];
-  }
-  *reinterpret_cast<u32x4v*>(dx + t * d + c) = pack8(acc);
-}
-
-// ---------------------------------------------------------------------------
-// float32 SIMT GEMM for the router's gradients:
-//   C[m, n] = sum_{k in split} A(m, k) B(k, n),
-//   A(m, k) = a[m * sam + k * sak] (float32), B(k, n) = b[k * ldb + n] (bf16),
-// 64 x 64 tiles, K chunks of 16 through LDS (the next chunk's loads in
-// registers while the current one is used), 4 x 4 outputs per thread.
-// blockIdx.z = K split s: rows k in [s * kchunk, (s + 1) * kchunk) go to
-// c + s * c_split (partials summed afterwards in split order).
-
-__global__ void __launch_bounds__(kThreads)
-simt_gemm_kernel(const float* __restrict__ a, int64_t sam, int64_t sak,
-                 const uint16_t* __restrict__ b, int64_t ldb, int M, int N, int64_t K,
-                 int64_t kchunk, float* __restrict__ c, int64_t ldc, int64_t c_split) {
-  __shared__ float As[16][64 + 1];
-  __shared__ float Bs[16][64 + 1];
+router_wgrad_kernel(const float* __restrict__ dl, const uint16_t* __restrict__ x, int64_t T,
+                    int E, int d, int64_t kchunk, float* __restrict__ out, int64_t out_split,
+                    float* __restrict__ bout, int64_t bout_split) {
+  __shared__ __attribute__((aligned(16))) float As[kRK][64];
+  __shared__ __attribute__((aligned(16))) float Bs[kRK][64];
   const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
   const int64_t kb = (int64_t)blockIdx.z * kchunk;
-  const int64_t ke = kb + kchunk < K ? kb + kchunk : K;
-  const int tm = threadIdx.x / 16, tn = threadIdx.x % 16;
+  const int64_t ke = kb + kchunk < T ? kb + kchunk : T;
+  const int tid = threadIdx.x, tm = tid / 16, tn = tid % 16;
+  const bool bias = bout != nullptr && blockIdx.x == 0;
   float acc[4][4] = {};
-  float ra[4], rb[4];
+  float bacc = 0.f;
+  float ra[8];
+  u32x4v rb;
   auto load = [&](int64_t k0) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int o = threadIdx.x + kThreads * u, kk = o / 64, mm = o % 64;
+    for (int u = 0; u < 8; ++u) {
+      const int o = tid + kThreads * u, kk = o / 64, mm = o % 64;
       const int64_t kg = k0 + kk;
-      ra[u] = (kg < ke && m0 + mm < M) ? a[(int64_t)(m0 + mm) * sam + kg * sak] : 0.f;
-      rb[u] = (kg < ke && n0 + mm < N) ? bf(b[kg * ldb + n0 + mm]) : 0.f;
+      ra[u] = (kg < ke && m0 + mm < E) ? dl[kg * E + m0 + mm] : 0.f;
     }
+    const int kk = tid / 8, c = n0 + (tid % 8) * 8;
+    const int64_t kg = k0 + kk;
+    rb = u32x4v{0u, 0u, 0u, 0u};
+    if (kg < ke && c < d) rb = *reinterpret_cast<const u32x4v*>(x + kg * d + c);
   };
   if (kb < ke) load(kb);
-  for (int64_t k0 = kb; k0 < ke; k0 += 16) {
+  for (int64_t k0 = kb; k0 < ke; k0 += kRK) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int o = threadIdx.x + kThreads * u, kk = o / 64, mm = o % 64;
-      As[kk][mm] = ra[u];
-      Bs[kk][mm] = rb[u];
+    for (int u = 0; u < 8; ++u) {
+      const int o = tid + kThreads * u;
+      As[o / 64][o % 64] = ra[u];
+    }
+    {
+      float v[8];
+      unpack8(rb, v);
+      float4* dst = reinterpret_cast<float4*>(&Bs[tid / 8][(tid % 8) * 8]);
+      dst[0] = float4{v[0], v[1], v[2], v[3]};
+      dst[1] = float4{v[4], v[5], v[6], v[7]};
     }
     __syncthreads();
-    if (k0 + 16 < ke) load(k0 + 16);
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      float av[4], bv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) av[i] = As[kk][tm + 16 * i];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) bv[i] = Bs[kk][tn + 16 * i];
+    if (k0 + kRK < ke) load(k0 + kRK);
+#pragma unroll 8
+    for (int kk = 0; kk < kRK; ++kk) {
+      const float4 av = *reinterpret_cast<const float4*>(&As[kk][tm * 4]);
+      const float4 bv = *reinterpret_cast<const float4*>(&Bs[kk][tn * 4]);
+      const float a4[4] = {av.x, av.y, av.z, av.w}, b4[4] = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int jx = 0; jx < 4; ++jx) acc[i][jx] += av[i] * bv[jx];
+        for (int jx = 0; jx < 4; ++jx) acc[i][jx] += a4[i] * b4[jx];
+    }
+    if (bias && tid < 64)
+      for (int kk = 0; kk < kRK; ++kk) bacc += As[kk][tid];
+    __syncthreads();
+  }
+  float* O = out + (int64_t)blockIdx.z * out_split;
+  const int n = n0 + tn * 4;  // d is a multiple of 8: four columns all in or all out
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + tm * 4 + i;
+    if (m < E && n < d)
+      *reinterpret_cast<float4*>(O + (int64_t)m * d + n) =
+          float4{acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
+  }
+  if (bias && tid < 64 && m0 + tid < E) bout[(int64_t)blockIdx.z * bout_split + m0 + tid] = bacc;
+}
+
+// Sum of the splits (split s at part + s * ld), 64 outputs per workgroup:
+// the four waves take every fourth split each (eight loads in flight), then
+// wave 0 adds the four partial sums in order.  Outputs i < n_a go to out_a,
+// the rest (i < n) to out_b.
+__global__ void __launch_bounds__(kThreads)
+reduce_splits_kernel(const float* __restrict__ part, int nsplit, int64_t ld, int64_t n,
+                     int64_t n_a, float* __restrict__ out_a, float* __restrict__ out_b) {
+  constexpr int G = kThreads / kWave;
+  __shared__ float red[G][kWave];
+  const int g = threadIdx.x / kWave, li = threadIdx.x % kWave;
+  const int64_t i = (int64_t)blockIdx.x * kWave + li;
+  float acc = 0.f;
+  if (i < n) {
+    int s = g;
+    for (; s + 7 * G < nsplit; s += 8 * G) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = part[(int64_t)(s + u * G) * ld + i];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += v[u];
+    }
+    for (; s < nsplit; s += G) acc += part[(int64_t)s * ld + i];
+  }
+  red[g][li] = acc;
+  __syncthreads();
+  if (g == 0 && i < n) {
+    float r = red[0][li];
+#pragma unroll
+    for (int q = 1; q < G; ++q) r += red[q][li];
+    if (i < n_a) out_a[i] = r; else out_b[i - n_a] = r;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dx, 64 tokens x 64 columns per workgroup:
+//   dx_t = sum_j kept dx_rows[row_tj] (+ shared_t) (+ dy_t) + dl_t W_r
+// Each thread owns 8 consecutive columns of two tokens: it gathers their
+// rows first (four assignments' indices, then their rows, in flight at
+// once), so that those loads overlap the router product, which runs through
+// LDS in chunks of 32 experts (float32, a 4 x 4 block per thread) and comes
+// back through LDS to the same 8-column layout.
+
+__device__ __forceinline__ void add8(float* acc, const uint16_t* p) {
+  float v[8];
+  unpack8(*reinterpret_cast<const u32x4v*>(p), v);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] += v[i];
+}
+
+__global__ void __launch_bounds__(kThreads)
+dx_final_kernel(const float* __restrict__ dl, const uint16_t* __restrict__ w_router,
+                const uint16_t* __restrict__ dx_rows, const int32_t* __restrict__ inv_row,
+                const uint16_t* __restrict__ shared, const uint16_t* __restrict__ residual,
+                int64_t T, int d, int E, int k, uint16_t* __restrict__ dx) {
+  __shared__ __attribute__((aligned(16))) float As[kRK][64 + 4];
+  __shared__ __attribute__((aligned(16))) float Bs[kRK][64];
+  __shared__ __attribute__((aligned(16))) float O[64][64 + 4];
+  const int64_t t0 = (int64_t)blockIdx.y * 64;
+  const int c0 = blockIdx.x * 64;
+  const int tid = threadIdx.x, tm = tid / 16, tn = tid % 16;
+  float ra[8];
+  u32x4v rb;
+  auto load = [&](int e0) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int o = tid + kThreads * u, kk = o % kRK, mm = o / kRK;
+      const int e = e0 + kk;
+      const int64_t t = t0 + mm;
+      ra[u] = (e < E && t < T) ? dl[t * E + e] : 0.f;
+    }
+    const int e = e0 + tid / 8, c = c0 + (tid % 8) * 8;
+    rb = u32x4v{0u, 0u, 0u, 0u};
+    if (e < E && c < d) rb = *reinterpret_cast<const u32x4v*>(w_router + (int64_t)e * d + c);
+  };
+  load(0);
+
+  // the gathered rows of this thread's two (token, 8 columns) items
+  int64_t tt[2];
+  int cc[2];
+  bool ok[2];
+  float s8[2][8];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int o = tid + kThreads * u;
+    tt[u] = t0 + o / 8;
+    cc[u] = c0 + (o % 8) * 8;
+    ok[u] = tt[u] < T && cc[u] < d;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s8[u][i] = 0.f;
+  }
+  for (int j0 = 0; j0 < k; j0 += 4) {
+    int32_t row[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        row[u][q] = (ok[u] && j0 + q < k) ? inv_row[tt[u] * k + j0 + q] : -1;
+    // every load issued before the first use (a dropped row reads row 0)
+    u32x4v raw[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        raw[u][q] = u32x4v{0u, 0u, 0u, 0u};
+        if (ok[u] && j0 + q < k) {
+          const int64_t r = row[u][q] >= 0 ? row[u][q] : 0;
+          raw[u][q] = *reinterpret_cast<const u32x4v*>(dx_rows + r * d + cc[u]);
+        }
+      }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (row[u][q] >= 0) {
+          float v[8];
+          unpack8(raw[u][q], v);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) s8[u][i] += v[i];
+        }
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    if (!ok[u]) continue;
+    if (shared) add8(s8[u], shared + tt[u] * d + cc[u]);
+    if (residual) add8(s8[u], residual + tt[u] * d + cc[u]);
+  }
+
+  float acc[4][4] = {};
+  for (int e0 = 0; e0 < E; e0 += kRK) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int o = tid + kThreads * u;
+      As[o % kRK][o / kRK] = ra[u];
+    }
+    {
+      float v[8];
+      unpack8(rb, v);
+      float4* dst = reinterpret_cast<float4*>(&Bs[tid / 8][(tid % 8) * 8]);
+      dst[0] = float4{v[0], v[1], v[2], v[3]};
+      dst[1] = float4{v[4], v[5], v[6], v[7]};
+    }
+    __syncthreads();
+    if (e0 + kRK < E) load(e0 + kRK);
+#pragma unroll 8
+    for (int kk = 0; kk < kRK; ++kk) {
+      const float4 av = *reinterpret_cast<const float4*>(&As[kk][tm * 4]);
+      const float4 bv = *reinterpret_cast<const float4*>(&Bs[kk][tn * 4]);
+      const float a4[4] = {av.x, av.y, av.z, av.w}, b4[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jx = 0; jx < 4; ++jx) acc[i][jx] += a4[i] * b4[jx];
     }
     __syncthreads();
   }
-  float* C = c + (int64_t)blockIdx.z * c_split;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
+    *reinterpret_cast<float4*>(&O[tm * 4 + i][tn * 4]) =
+        float4{acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
+  __syncthreads();
 #pragma unroll
-    for (int jx = 0; jx < 4; ++jx) {
-      const int m = m0 + tm + 16 * i, n = n0 + tn + 16 * jx;
-      if (m < M && n < N) C[(int64_t)m * ldc + n] = acc[i][jx];
-    }
-}
-
-// out[i] = sum_s part[s * n + i], s in order (eight loads in flight)
-__global__ void __launch_bounds__(kThreads)
-sum_splits_kernel(const float* __restrict__ part, int nsplit, int64_t n, float* __restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= n) return;
-  float acc = 0.f;
-  int s = 0;
-  for (; s + 8 <= nsplit; s += 8) {
-    float v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = part[(int64_t)(s + u) * n + i];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) acc += v[u];
+  for (int u = 0; u < 2; ++u) {
+    if (!ok[u]) continue;
+    const int o = tid + kThreads * u, r = o / 8, ch = o % 8;
+    const float4 lo = *reinterpret_cast<const float4*>(&O[r][ch * 8]);
+    const float4 hi = *reinterpret_cast<const float4*>(&O[r][ch * 8 + 4]);
+    s8[u][0] += lo.x; s8[u][1] += lo.y; s8[u][2] += lo.z; s8[u][3] += lo.w;
+    s8[u][4] += hi.x; s8[u][5] += hi.y; s8[u][6] += hi.z; s8[u][7] += hi.w;
+    *reinterpret_cast<u32x4v*>(dx + tt[u] * d + cc[u]) = pack8(s8[u]);
   }
-  for (; s < nsplit; ++s) acc += part[(int64_t)s * n + i];
-  out[i] = acc;
 }
 
 unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
 
 }  // namespace
 
-hipError_t launch_combine_bwd(const moe_config& c, const void* dy, const void* y_perm,
-                              const int32_t* inv_row, const float* topk_w, void* d_yperm,
-                              float* d_topk_w, hipStream_t s) {
-  combine_bwd_kernel<<<blocks_for(c.n_tokens, kThreads / kWave), kThreads, 0, s>>>(
-      static_cast<const uint16_t*>(dy), static_cast<const uint16_t*>(y_perm), inv_row, topk_w,
-      c.n_tokens, c.d_model, c.top_k, static_cast<uint16_t*>(d_yperm), d_topk_w);
-  return hipGetLastError();
-}
-
-hipError_t launch_router_grad(const moe_config& c, const float* scores, const float* lse,
-                              const int32_t* topk_idx, const float* topk_w, const float* d_topk_w,
-                              const int32_t* counts, const moe_loss_weights& lw, float* aux_dp,
-                              float* dl, hipStream_t s) {
+hipError_t launch_aux_dp(const moe_config& c, const float* scores, const float* lse,
+                         const int32_t* counts, const moe_loss_weights& lw, float* aux_dp,
+                         hipStream_t s) {
   aux_dp_kernel<<<c.n_experts, kThreads, 0, s>>>(scores, lse, counts, c.n_tokens, c.n_experts,
                                                  c.top_k, lw.load_balance, lw.lb_squares,
                                                  lw.kl_uniform, aux_dp);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const float c_z = (float)(lw.z_loss * 2.0 / (double)c.n_tokens);
-  const float inv_tau = c.router_temperature == 0.f ? 1.f : 1.f / c.router_temperature;
-  router_grad_kernel<<<blocks_for(c.n_tokens, kThreads / kWave), kThreads, 0, s>>>(
-      scores, lse, topk_idx, topk_w, d_topk_w, aux_dp, c.n_tokens, c.n_experts, c.top_k, c_z,
-      inv_tau, dl);
   return hipGetLastError();
 }
 
-hipError_t launch_pad_offsets(const int32_t* offsets, int G, int pad, int64_t ncols, int32_t* poff,
-                              int32_t* colrow, hipStream_t s) {
-  pad_offsets_kernel<<<blocks_for(ncols, kThreads), kThreads, 0, s>>>(offsets, G, pad, ncols, poff,
-                                                                      colrow);
+hipError_t launch_combine_router_bwd(const moe_config& c, const moe_loss_weights& lw,
+                                     const CombineRouterBwd& b, hipStream_t s) {
+  CombineRouterArgs a;
+  a.dy = static_cast<const uint16_t*>(b.dy);
+  a.y_perm = static_cast<const uint16_t*>(b.y_perm);
+  a.inv_row = b.inv_row;
+  a.topk_w = b.topk_w;
+  a.d_yperm = static_cast<uint16_t*>(b.d_yperm);
+  a.scores = b.scores;
+  a.lse = b.lse;
+  a.topk_idx = b.topk_idx;
+  a.counts = b.counts;
+  a.aux_dp = b.aux_dp;
+  const double T = (double)c.n_tokens;
+  a.lb_coef = lw.load_balance * (double)c.n_experts / (T * (double)c.top_k) / T;
+  a.c_z = (float)(lw.z_loss * 2.0 / T);
+  a.inv_tau = c.router_temperature == 0.f ? 1.f : 1.f / c.router_temperature;
+  a.dl = b.dl;
+  a.T = c.n_tokens;
+  a.d = c.d_model;
+  a.E = c.n_experts;
+  a.k = c.top_k;
+  a.nb_tok = blocks_for(c.n_tokens, kThreads / kWave);
+  a.offsets = b.offsets;
+  a.pad = b.pad;
+  a.ncols = b.ncols;
+  a.poff = b.poff;
+  a.colrow = b.colrow;
+  const unsigned nb_pad = blocks_for(b.ncols > 0 ? b.ncols : 1, kThreads);
+  const unsigned grid = a.nb_tok + nb_pad;
+  if (c.n_experts <= kWave)
+    combine_router_bwd_kernel<1><<<grid, kThreads, 0, s>>>(a);
+  else if (c.n_experts <= 2 * kWave)
+    combine_router_bwd_kernel<2><<<grid, kThreads, 0, s>>>(a);
+  else if (c.n_experts <= 4 * kWave)
+    combine_router_bwd_kernel<4><<<grid, kThreads, 0, s>>>(a);
+  else
+    combine_router_bwd_kernel<kMaxPerLane><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
-hipError_t launch_transpose(const void* src, int64_t src_ld, int64_t src_batch,
-                            const int32_t* colrow, const int32_t* gather, int64_t nsrc,
-                            int64_t ncols, int C, void* dst, int64_t dst_ld, int64_t dst_batch,
-                            int batches, hipStream_t s) {
-  if (ncols <= 0 || C <= 0 || batches <= 0) return hipSuccess;
-  transpose_kernel<<<dim3(blocks_for(ncols, 64), blocks_for(C, 64), batches), kThreads, 0, s>>>(
-      static_cast<const uint16_t*>(src), src_ld, src_batch, colrow, gather, nsrc, ncols, C,
-      static_cast<uint16_t*>(dst), dst_ld, dst_batch);
+static TransposeJob job_of(const TransposeDesc& t) {
+  TransposeJob j;
+  j.src = static_cast<const uint16_t*>(t.src);
+  j.src_ld = t.src_ld;
+  j.src_batch = t.src_batch;
+  j.colrow = t.colrow;
+  j.gather = t.gather;
+  j.nsrc = t.nsrc;
+  j.ncols = t.ncols;
+  j.C = t.C;
+  j.dst = static_cast<uint16_t*>(t.dst);
+  j.dst_ld = t.dst_ld;
+  j.dst_batch = t.dst_batch;
+  j.tx = blocks_for(t.ncols, kTT);
+  j.ty = blocks_for(t.C, kTT);
+  return j;
+}
+
+hipError_t launch_transpose(const TransposeDesc& a, const TransposeDesc& b, hipStream_t s) {
+  const bool ua = a.ncols > 0 && a.C > 0 && a.batches > 0;
+  const bool ub = b.ncols > 0 && b.C > 0 && b.batches > 0;
+  if (!ua && !ub) return hipSuccess;
+  const TransposeJob j0 = job_of(ua ? a : b);  // a lone problem goes first
+  const TransposeJob j1 = ua && ub ? job_of(b) : j0;
+  const uint64_t n0 = (uint64_t)j0.tx * j0.ty * (uint64_t)(ua ? a.batches : b.batches);
+  const uint64_t n1 = ua && ub ? (uint64_t)j1.tx * j1.ty * (uint64_t)b.batches : 0;
+  if (n0 + n1 > 0xFFFFFFFFull) return hipErrorInvalidValue;
+  transpose_kernel<<<(unsigned)(n0 + n1), kThreads, 0, s>>>(j0, j1, (unsigned)n0);
   return hipGetLastError();
 }
 
@@ -589,54 +869,52 @@ hipError_t launch_seg_rowsum(const void* m, int64_t ld, int C, const int32_t* po
   return hipGetLastError();
 }
 
-hipError_t launch_colsum_f32(const float* m, int64_t T, int E, float* out, hipStream_t s) {
-  colsum_f32_kernel<<<E, kThreads, 0, s>>>(m, T, E, out);
-  return hipGetLastError();
-}
-
-hipError_t launch_dx_gather(const moe_config& c, const void* dx_rows, const int32_t* inv_row,
-                            const void* shared, const float* dx_router, const void* residual,
-                            void* dx, hipStream_t s) {
-  const int64_t n = c.n_tokens * (c.d_model / 8);
-  dx_gather_kernel<<<blocks_for(n, kThreads), kThreads, 0, s>>>(
-      static_cast<const uint16_t*>(dx_rows), inv_row, static_cast<const uint16_t*>(shared), dx_router,
-      static_cast<const uint16_t*>(residual), c.n_tokens, c.d_model, c.top_k,
-      static_cast<uint16_t*>(dx));
-  return hipGetLastError();
-}
-
-// Split count of a SIMT GEMM with long K: enough workgroups to cover the
-// chip several times over (each K chunk costs a memory round trip), each
-// with at least 64 rows of K.
-int simt_splits(int M, int N, int64_t K) {
-  const int64_t tiles = (int64_t)((M + 63) / 64) * ((N + 63) / 64);
-  int64_t want = (2048 + tiles - 1) / tiles;
-  const int64_t most = (K + 63) / 64;
+// Token splits of the router weight gradient: about 1024 workgroups (each
+// split costs a memory round trip per 32 tokens), at least 64 tokens each,
+// at most 256 splits.
+int router_wgrad_splits(int E, int d, int64_t T) {
+  const int64_t tiles = (int64_t)((E + 63) / 64) * ((d + 63) / 64);
+  int64_t want = (1024 + tiles - 1) / tiles;
+  const int64_t most = (T + 63) / 64;
   if (want > most) want = most;
-  if (want < 1) want = 1;
   if (want > 256) want = 256;
-  return (int)want;
+  if (want < 1) want = 1;
+  const int64_t kchunk = ((T + want - 1) / want + kRK - 1) / kRK * kRK;
+  return (int)((T + kchunk - 1) / kchunk);
 }
 
-hipError_t launch_simt_gemm(const float* a, int64_t sam, int64_t sak, const void* b, int64_t ldb,
-                            int M, int N, int64_t K, int nsplit, float* c, int64_t ldc,
-                            float* partial, hipStream_t s) {
-  if (M <= 0 || N <= 0) return hipSuccess;
-  const int64_t kchunk = ((K + nsplit - 1) / nsplit + 15) / 16 * 16;
-  const dim3 grid(blocks_for(N, 64), blocks_for(M, 64), nsplit);
-  if (nsplit == 1) {
-    simt_gemm_kernel<<<grid, kThreads, 0, s>>>(a, sam, sak, static_cast<const uint16_t*>(b), ldb, M,
-                                               N, K, kchunk, c, ldc, 0);
+int64_t router_wgrad_split_ld(int E, int d) { return ((int64_t)E * d + E + 3) / 4 * 4; }
+
+hipError_t launch_router_wgrad(const float* dl, const void* x, int64_t T, int E, int d, int nsplit,
+                               float* part, float* dw, float* db, hipStream_t s) {
+  if (nsplit < 1 || part == nullptr || ((uintptr_t)part & 15) != 0) return hipErrorInvalidValue;
+  const int64_t kchunk = ((T + nsplit - 1) / nsplit + kRK - 1) / kRK * kRK;
+  if ((T + kchunk - 1) / kchunk != nsplit) return hipErrorInvalidValue;
+  const dim3 grid(blocks_for(d, 64), blocks_for(E, 64), (unsigned)nsplit);
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  if (nsplit == 1 && ((uintptr_t)dw & 15) == 0) {  // 16-byte stores straight to dW_r
+    router_wgrad_kernel<<<grid, kThreads, 0, s>>>(dl, xb, T, E, d, kchunk, dw, 0, db, 0);
     return hipGetLastError();
   }
-  // partials [nsplit][M][N] (ldc = N), then the sum in split order
-  simt_gemm_kernel<<<grid, kThreads, 0, s>>>(a, sam, sak, static_cast<const uint16_t*>(b), ldb, M, N,
-                                             K, kchunk, partial, N, (int64_t)M * N);
+  // partials [nsplit][ld], ld = E * d + E rounded up to 16 bytes; the bias
+  // partials after the weight's
+  const int64_t nw = (int64_t)E * d, n = nw + (db ? E : 0), ld = router_wgrad_split_ld(E, d);
+  router_wgrad_kernel<<<grid, kThreads, 0, s>>>(dl, xb, T, E, d, kchunk, part, ld,
+                                                db ? part + nw : nullptr, ld);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (ldc != N) return hipErrorInvalidValue;
-  sum_splits_kernel<<<blocks_for((int64_t)M * N, kThreads), kThreads, 0, s>>>(partial, nsplit,
-                                                                              (int64_t)M * N, c);
+  reduce_splits_kernel<<<blocks_for(n, kWave), kThreads, 0, s>>>(part, nsplit, ld, n, nw, dw, db);
+  return hipGetLastError();
+}
+
+hipError_t launch_dx_final(const moe_config& c, const float* dl, const void* w_router,
+                           const void* dx_rows, const int32_t* inv_row, const void* shared,
+                           const void* residual, void* dx, hipStream_t s) {
+  const dim3 grid(blocks_for(c.d_model, 64), blocks_for(c.n_tokens, 64));
+  dx_final_kernel<<<grid, kThreads, 0, s>>>(
+      dl, static_cast<const uint16_t*>(w_router), static_cast<const uint16_t*>(dx_rows), inv_row,
+      static_cast<const uint16_t*>(shared), static_cast<const uint16_t*>(residual), c.n_tokens,
+      c.d_model, c.n_experts, c.top_k, static_cast<uint16_t*>(dx));
   return hipGetLastError();
 }
 

@@ -8,23 +8,23 @@
 //
 // dW2_e = d_o_e^T h_e and dW1_e = da_e^T x_e take their operands from the
 // transposed activations, so both operands are read along K like the
-// forward's grouped GEMMs: 128 x 128 x 64 tiles over 4 waves (64 x 64 each,
-// v_mfma_f32_32x32x16_bf16), global loads of K tile t+1 staged in registers
-// while tile t feeds the MFMAs from LDS, 16-byte LDS chunks XOR-swizzled so
-// the 16 lanes of a fragment read hit distinct bank groups.  Rows past M or
-// N are clamped on load and masked on store.
+// forward's grouped GEMMs: 128 x 128 x 64 tiles over 4 waves, or, for long K
+// and enough output tiles, 256 x 256 x 64 tiles over 8 waves (half the bytes
+// per flop); each wave holds 64 x 64 or 128 x 64 of the tile in
+// v_mfma_f32_32x32x16_bf16 accumulators.  Global loads of K tile t+1 are
+// staged in registers while tile t feeds the MFMAs from LDS; 16-byte LDS
+// chunks are XOR-swizzled so the 16 lanes of a fragment read hit distinct
+// bank groups.  Rows past M or N are clamped on load and masked on store.
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64, WM = 2, WN = 2;
-constexpr int kThreads = 64 * WM * WN;
-constexpr int TM = BM / WM, TN = BN / WN, MI = TM / 32, NI = TN / 32;
+constexpr int BK = 64;
 constexpr int CPR = BK / 8;               // 16-byte chunks per tile row
 constexpr int RPW = 256 / (BK * 2);       // tile rows per 256-byte bank window
-constexpr int A_LD = BM * CPR / kThreads;
-constexpr int B_LD = BN * CPR / kThreads;
 constexpr int KS = BK / 16;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -39,15 +39,27 @@ struct WgradArgs {
   int M, N;
   float* c;
   int64_t ldc, c_batch;
+  int nsplit;       // K splits per batch: blockIdx.z = batch * nsplit + split
+  int64_t c_split;  // output offset of split s: s * c_split
 };
 
-__global__ void __launch_bounds__(kThreads, 2) wgrad_kernel(WgradArgs p) {
+template <int BM, int BN, int WM, int WN>
+__global__ void __launch_bounds__(64 * WM * WN, BM * BN > 128 * 128 ? 1 : 2)
+wgrad_kernel(WgradArgs p) {
+  constexpr int kThreads = 64 * WM * WN;
+  constexpr int TM = BM / WM, TN = BN / WN, MI = TM / 32, NI = TN / 32;
+  constexpr int A_LD = BM * CPR / kThreads;
+  constexpr int B_LD = BN * CPR / kThreads;
   __shared__ __attribute__((aligned(16))) u32x4 sA[2][BM * CPR];
   __shared__ __attribute__((aligned(16))) u32x4 sB[2][BN * CPR];
-  const int bt = blockIdx.z;
+  const int bt = blockIdx.z / p.nsplit, sp = blockIdx.z % p.nsplit;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-  const int64_t k0 = p.kofs ? p.kofs[bt] : 0;
-  const int64_t k1 = p.kofs ? p.kofs[bt + 1] : p.K;
+  // this split's share of the batch's K range (whole K tiles)
+  const int64_t kb0 = p.kofs ? p.kofs[bt] : 0;
+  const int64_t kb1 = p.kofs ? p.kofs[bt + 1] : p.K;
+  const int64_t chunk = ((kb1 - kb0 + p.nsplit - 1) / p.nsplit + BK - 1) / BK * BK;
+  const int64_t k0 = kb0 + sp * chunk < kb1 ? kb0 + sp * chunk : kb1;
+  const int64_t k1 = k0 + chunk < kb1 ? k0 + chunk : kb1;
   const int nk = (int)((k1 - k0) / BK);
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int wm = wave / WN, wn = wave % WN;
@@ -130,7 +142,7 @@ __global__ void __launch_bounds__(kThreads, 2) wgrad_kernel(WgradArgs p) {
   }
 
   // 32x32 C layout: column lane%32, rows 8*(q/4) + 4*(lane/32) + q%4
-  float* C = p.c + (int64_t)bt * p.c_batch;
+  float* C = p.c + (int64_t)sp * p.c_split + (int64_t)bt * p.c_batch;
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -145,13 +157,70 @@ __global__ void __launch_bounds__(kThreads, 2) wgrad_kernel(WgradArgs p) {
     }
 }
 
+// out[i] = sum over the splits s of part[s * n + i], in split order
+__global__ void __launch_bounds__(256)
+wgrad_reduce_kernel(const float* __restrict__ part, int nsplit, int64_t n, float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float acc = part[i];
+  int s = 1;
+  for (; s + 4 <= nsplit; s += 4) {
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = part[(int64_t)(s + u) * n + i];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc += v[u];
+  }
+  for (; s < nsplit; ++s) acc += part[(int64_t)s * n + i];
+  out[i] = acc;
+}
+
 }  // namespace
+
+// Tile and K split of a weight-gradient product, from a cost model in units
+// of one K tile of a 128 x 128 tile pair on a CU: a round of resident
+// workgroups (256 tiles of 256 x 256, one per CU, or 512 of 128 x 128, two
+// per CU) costs its K tiles per split, times 1.5 for the large tile (it does
+// twice the work of a pair at the higher efficiency measured for it).
+// A split product also writes and reads back its float32 partials (one such
+// unit moves about 8.5 MB at HBM rate).  Splits keep at least 1024 (large
+// tile) or 512 K rows each, at most 64; the fewest splits win a tie.
+WgradPlan wgrad_plan(int M, int N, int batches, int64_t k_avg) {
+  WgradPlan best{128, 1};
+  if (M <= 0 || N <= 0 || batches <= 0 || k_avg <= 0) return best;
+  double best_cost = 1e300;
+  for (const int tile : {256, 128}) {
+    const int64_t t = (int64_t)((M + tile - 1) / tile) * ((N + tile - 1) / tile) * batches;
+    const int64_t slots = tile == 256 ? 256 : 512;
+    const int64_t min_rows = tile == 256 ? 1024 : 512;
+    if (tile == 256 && k_avg < min_rows) continue;
+    const int64_t ns_max = std::max<int64_t>(1, std::min<int64_t>(k_avg / min_rows, 64));
+    for (int64_t ns = 1; ns <= ns_max; ++ns) {
+      const int64_t rounds = (t * ns + slots - 1) / slots;
+      const int64_t ksteps = ((k_avg + ns - 1) / ns + BK - 1) / BK;
+      const double partial_bytes = ns > 1 ? 8.0 * (double)ns * batches * M * N : 0.0;
+      const double cost =
+          (double)rounds * (double)ksteps * (tile == 256 ? 1.5 : 1.0) + partial_bytes / 8.5e6;
+      if (cost < best_cost) {
+        best_cost = cost;
+        best = WgradPlan{tile, (int)ns};
+      }
+    }
+  }
+  return best;
+}
+
+size_t wgrad_partial_floats(const WgradPlan& w, int M, int N, int batches) {
+  return w.nsplit > 1 ? (size_t)w.nsplit * batches * M * N : 0;
+}
 
 hipError_t launch_wgrad(const void* a, int64_t lda, int64_t a_batch, const void* b, int64_t ldb,
                         int64_t b_batch, const int32_t* kofs, int64_t K, int M, int N, int batches,
-                        float* c, int64_t ldc, int64_t c_batch, hipStream_t s) {
+                        float* c, int64_t ldc, int64_t c_batch, float* partial, hipStream_t s) {
   if (M <= 0 || N <= 0 || batches <= 0) return hipSuccess;
-  if (lda % 8 != 0 || ldb % 8 != 0 || (!kofs && K % BK != 0)) return hipErrorInvalidValue;
+  if (lda % 8 != 0 || ldb % 8 != 0 || K < 0 || (!kofs && K % BK != 0))
+    return hipErrorInvalidValue;
+  const WgradPlan w = wgrad_plan(M, N, batches, kofs ? K / batches : K);
   WgradArgs p;
   p.a = static_cast<const uint16_t*>(a);
   p.lda = lda;
@@ -163,11 +232,32 @@ hipError_t launch_wgrad(const void* a, int64_t lda, int64_t a_batch, const void*
   p.K = K;
   p.M = M;
   p.N = N;
-  p.c = c;
-  p.ldc = ldc;
-  p.c_batch = c_batch;
-  const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM), (unsigned)batches);
-  wgrad_kernel<<<grid, kThreads, 0, s>>>(p);
+  p.nsplit = w.nsplit;
+  const int64_t n = (int64_t)batches * M * N;
+  if (w.nsplit > 1) {
+    // partials [nsplit][batches][M][N], summed into c (which must be dense)
+    if (partial == nullptr || ldc != N || c_batch != (int64_t)M * N) return hipErrorInvalidValue;
+    p.c = partial;
+    p.ldc = N;
+    p.c_batch = (int64_t)M * N;
+    p.c_split = n;
+  } else {
+    p.c = c;
+    p.ldc = ldc;
+    p.c_batch = c_batch;
+    p.c_split = 0;
+  }
+  const unsigned z = (unsigned)(batches * w.nsplit);
+  if (w.tile == 256) {
+    const dim3 grid((unsigned)((N + 255) / 256), (unsigned)((M + 255) / 256), z);
+    wgrad_kernel<256, 256, 2, 4><<<grid, 512, 0, s>>>(p);
+  } else {
+    const dim3 grid((unsigned)((N + 127) / 128), (unsigned)((M + 127) / 128), z);
+    wgrad_kernel<128, 128, 2, 2><<<grid, 256, 0, s>>>(p);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || w.nsplit == 1) return e;
+  wgrad_reduce_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(partial, w.nsplit, n, c);
   return hipGetLastError();
 }
 

@@ -2,6 +2,7 @@
 // workspace planning and the launch sequences of the entry points.
 // Nothing here allocates device memory or synchronises; every launch goes to
 // the caller's stream.
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 
@@ -535,22 +536,33 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
   constexpr int kPad = 64;  // K tile of the weight-gradient GEMM
   const int64_t Rp = (R + (int64_t)kPad * E + kPad - 1) / kPad * kPad;  // padded columns, bound
   const int64_t Tp = (T + kPad - 1) / kPad * kPad;
-  const int nsplit = simt_splits(E, d, T);
+  const int nsplit = router_wgrad_splits(E, d, T);
+  const bool p_terms = lw.lb_squares != 0.0 || lw.kl_uniform != 0.0;
+  // split weight-gradient products share one partial buffer (same stream)
+  size_t wg_part = 0;
+  auto wg_need = [&](int M, int N, int batches, int64_t K, bool grouped) {
+    const WgradPlan pl = wgrad_plan(M, N, batches, grouped ? K / batches : K);
+    wg_part = std::max(wg_part, wgrad_partial_floats(pl, M, N, batches));
+  };
+  wg_need(d, f, E, Rp, true);
+  wg_need(w1r, d, E, Rp, true);
+  if (S > 0) {
+    wg_need(d, f, S, Tp, false);
+    wg_need(w1r, d, S, Tp, false);
+  }
 
   struct Plan {
     void *dO, *W2t, *W1t, *dH, *dA, *dXr, *dOt, *Ht, *dAt, *Xt;
-    float *dw, *dl, *dxr, *wr_part, *aux_dp;
+    float *dl, *wr_part, *aux_dp, *wg_part;
     int32_t *poff, *colrow;
     void *Ws2t, *Ws1t, *dHs, *dAs, *dXs, *dyt, *Hst, *dAst, *xt;
   };
   auto plan = [&](void* base, Plan& p) {
     Carver cv(base);
     p.dO = cv.take<uint16_t>(R * d);
-    p.dw = cv.take<float>(R);
     p.dl = cv.take<float>(T * E);
-    p.aux_dp = cv.take<float>(E);
-    p.dxr = cv.take<float>(T * d);
-    p.wr_part = cv.take<float>(nsplit > 1 ? (size_t)nsplit * E * d : 0);
+    p.aux_dp = cv.take<float>(E);  // the size does not depend on the loss weights
+    p.wr_part = cv.take<float>((size_t)nsplit * router_wgrad_split_ld(E, d));
     p.W2t = cv.take<uint16_t>((size_t)E * f * d);
     p.W1t = cv.take<uint16_t>((size_t)E * d * w1r);
     p.dH = cv.take<uint16_t>(R * f);
@@ -562,6 +574,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
     p.Ht = cv.take<uint16_t>(f * Rp);
     p.dAt = cv.take<uint16_t>(w1r * Rp);
     p.Xt = cv.take<uint16_t>(d * Rp);
+    p.wg_part = cv.take<float>(wg_part);
     if (S > 0) {
       p.Ws2t = cv.take<uint16_t>((size_t)S * f * d);
       p.Ws1t = cv.take<uint16_t>((size_t)S * d * w1r);
@@ -595,27 +608,44 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
   if (st != MOE_OK || ws == nullptr) return st;
   plan(ws, p);
 
-  // combine and router
-  MOE_HIP_TRY(launch_combine_bwd(c, dy, sv->y_perm, sv->inv_row, sv->topk_w, p.dO, p.dw, stream));
-  MOE_HIP_TRY(launch_router_grad(c, sv->scores, sv->token_lse, sv->topk_idx, sv->topk_w, p.dw,
-                                 sv->expert_counts, lw, p.aux_dp, p.dl, stream));
-  MOE_HIP_TRY(launch_simt_gemm(p.dl, 1, E, x, d, E, d, T, nsplit, g->dw_router, d, p.wr_part,
-                               stream));
-  if (g->drouter_bias) MOE_HIP_TRY(launch_colsum_f32(p.dl, T, E, g->drouter_bias, stream));
-  MOE_HIP_TRY(launch_simt_gemm(p.dl, E, 1, w->w_router, d, (int)T, d, E, 1, p.dxr, d, nullptr,
-                               stream));
+  // combine and router backward (and the padded offsets of the
+  // weight-gradient columns), then the router's weight and bias gradients
+  if (p_terms)
+    MOE_HIP_TRY(launch_aux_dp(c, sv->scores, sv->token_lse, sv->expert_counts, lw, p.aux_dp,
+                              stream));
+  CombineRouterBwd cb;
+  cb.dy = dy;
+  cb.y_perm = sv->y_perm;
+  cb.inv_row = sv->inv_row;
+  cb.topk_w = sv->topk_w;
+  cb.d_yperm = p.dO;
+  cb.scores = sv->scores;
+  cb.lse = sv->token_lse;
+  cb.topk_idx = sv->topk_idx;
+  cb.counts = sv->expert_counts;
+  cb.aux_dp = p_terms ? p.aux_dp : nullptr;
+  cb.dl = p.dl;
+  cb.offsets = sv->expert_offsets;
+  cb.pad = kPad;
+  cb.ncols = Rp;
+  cb.poff = p.poff;
+  cb.colrow = p.colrow;
+  MOE_HIP_TRY(launch_combine_router_bwd(c, lw, cb, stream));
+  MOE_HIP_TRY(launch_router_wgrad(p.dl, x, T, E, d, nsplit, p.wr_part, g->dw_router,
+                                  g->drouter_bias, stream));
 
   // routed experts: transposed weights, dh, da / h (from the saved
   // pre-activations), dx rows
+  TransposeDesc t2{w->w2, f, (int64_t)d * f, nullptr, nullptr, d, d, f, p.W2t, d,
+                   (int64_t)f * d, E};
+  TransposeDesc t1{w->w1, d, (int64_t)w1r * d, nullptr, nullptr, w1r, w1r, d, p.W1t, w1r,
+                   (int64_t)d * w1r, E};
+  MOE_HIP_TRY(launch_transpose(t2, t1, stream));
   GemmDesc gd{};
   gd.group_off = sv->expert_offsets;
   gd.n_groups = E;
   gd.n_seg = 1;
   gd.rows_max = R;
-  MOE_HIP_TRY(launch_transpose(w->w2, f, (int64_t)d * f, nullptr, nullptr, d, d, f, p.W2t, d,
-                               (int64_t)f * d, E, stream));
-  MOE_HIP_TRY(launch_transpose(w->w1, d, (int64_t)w1r * d, nullptr, nullptr, w1r, w1r, d, p.W1t,
-                               w1r, (int64_t)d * w1r, E, stream));
   gd.a = p.dO;
   gd.a_rows = nullptr;
   gd.lda = d;
@@ -627,7 +657,6 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
   gd.ldo = f;
   MOE_HIP_TRY(launch_gemm(c, kGemmDown, gd, stream));
   // da (row-major) and the expert-padded da^T, h^T in one pass
-  MOE_HIP_TRY(launch_pad_offsets(sv->expert_offsets, E, kPad, Rp, p.poff, p.colrow, stream));
   MOE_HIP_TRY(launch_act_bwd_t(sv->preact, w1r, p.dH, f, p.colrow, 0, Rp, 1, f, c.act, p.dA, p.dAt,
                                p.Ht, Rp, stream));
   gd.a = p.dA;
@@ -639,13 +668,14 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
   gd.ldo = d;
   MOE_HIP_TRY(launch_gemm(c, kGemmDown, gd, stream));
 
-  // weight gradients from the expert-padded transposes
-  MOE_HIP_TRY(launch_transpose(p.dO, d, 0, p.colrow, nullptr, 0, Rp, d, p.dOt, Rp, 0, 1, stream));
-  MOE_HIP_TRY(launch_transpose(x, d, 0, p.colrow, sv->perm_token, 0, Rp, d, p.Xt, Rp, 0, 1, stream));
-  MOE_HIP_TRY(launch_wgrad(p.dOt, Rp, 0, p.Ht, Rp, 0, p.poff, 0, d, f, E, g->dw2, f,
-                           (int64_t)d * f, stream));
-  MOE_HIP_TRY(launch_wgrad(p.dAt, Rp, 0, p.Xt, Rp, 0, p.poff, 0, w1r, d, E, g->dw1, d,
-                           (int64_t)w1r * d, stream));
+  // weight gradients from the expert-padded transposes of d o and x
+  TransposeDesc to{p.dO, d, 0, p.colrow, nullptr, 0, Rp, d, p.dOt, Rp, 0, 1};
+  TransposeDesc tx{x, d, 0, p.colrow, sv->perm_token, 0, Rp, d, p.Xt, Rp, 0, 1};
+  MOE_HIP_TRY(launch_transpose(to, tx, stream));
+  MOE_HIP_TRY(launch_wgrad(p.dOt, Rp, 0, p.Ht, Rp, 0, p.poff, Rp, d, f, E, g->dw2, f,
+                           (int64_t)d * f, p.wg_part, stream));
+  MOE_HIP_TRY(launch_wgrad(p.dAt, Rp, 0, p.Xt, Rp, 0, p.poff, Rp, w1r, d, E, g->dw1, d,
+                           (int64_t)w1r * d, p.wg_part, stream));
   if (w->b2) MOE_HIP_TRY(launch_seg_rowsum(p.dOt, Rp, d, p.poff, Rp, E, g->db2, d, stream));
   if (w->b1) MOE_HIP_TRY(launch_seg_rowsum(p.dAt, Rp, w1r, p.poff, Rp, E, g->db1, w1r, stream));
 
@@ -656,10 +686,11 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
     sd.n_groups = 1;
     sd.n_seg = 1;
     sd.rows_max = T;
-    MOE_HIP_TRY(launch_transpose(w->shared_w2, f, (int64_t)d * f, nullptr, nullptr, d, d, f, p.Ws2t,
-                                 d, (int64_t)f * d, S, stream));
-    MOE_HIP_TRY(launch_transpose(w->shared_w1, d, (int64_t)w1r * d, nullptr, nullptr, w1r, w1r, d,
-                                 p.Ws1t, w1r, (int64_t)d * w1r, S, stream));
+    TransposeDesc s2{w->shared_w2, f, (int64_t)d * f, nullptr, nullptr, d, d, f, p.Ws2t, d,
+                     (int64_t)f * d, S};
+    TransposeDesc s1{w->shared_w1, d, (int64_t)w1r * d, nullptr, nullptr, w1r, w1r, d, p.Ws1t,
+                     w1r, (int64_t)d * w1r, S};
+    MOE_HIP_TRY(launch_transpose(s2, s1, stream));
     for (int s = 0; s < S; ++s) {
       sd.a = dy;
       sd.lda = d;
@@ -682,12 +713,13 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
     sd.out = p.dXs;
     sd.ldo = d;
     MOE_HIP_TRY(launch_gemm(c, kGemmDown, sd, stream));
-    MOE_HIP_TRY(launch_transpose(dy, d, 0, nullptr, nullptr, T, Tp, d, p.dyt, Tp, 0, 1, stream));
-    MOE_HIP_TRY(launch_transpose(x, d, 0, nullptr, nullptr, T, Tp, d, p.xt, Tp, 0, 1, stream));
+    TransposeDesc ty{dy, d, 0, nullptr, nullptr, T, Tp, d, p.dyt, Tp, 0, 1};
+    TransposeDesc txs{x, d, 0, nullptr, nullptr, T, Tp, d, p.xt, Tp, 0, 1};
+    MOE_HIP_TRY(launch_transpose(ty, txs, stream));
     MOE_HIP_TRY(launch_wgrad(p.dyt, Tp, 0, p.Hst, Tp, (int64_t)f * Tp, nullptr, Tp, d, f, S, g->dws2,
-                             f, (int64_t)d * f, stream));
+                             f, (int64_t)d * f, p.wg_part, stream));
     MOE_HIP_TRY(launch_wgrad(p.dAst, Tp, (int64_t)w1r * Tp, p.xt, Tp, 0, nullptr, Tp, w1r, d, S,
-                             g->dws1, d, (int64_t)w1r * d, stream));
+                             g->dws1, d, (int64_t)w1r * d, p.wg_part, stream));
     if (w->shared_b2)
       for (int s = 0; s < S; ++s)
         MOE_HIP_TRY(launch_seg_rowsum(p.dyt, Tp, d, nullptr, Tp, 1, g->dsb2 + (int64_t)s * d, d,
@@ -696,8 +728,9 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
       MOE_HIP_TRY(launch_seg_rowsum(p.dAst, Tp, S * w1r, nullptr, Tp, 1, g->dsb1, S * w1r, stream));
   }
 
-  MOE_HIP_TRY(launch_dx_gather(c, p.dXr, sv->inv_row, S > 0 ? p.dXs : nullptr, p.dxr,
-                               c.add_residual ? dy : nullptr, g->dx, stream));
+  // dx: router product, kept expert rows, shared experts, residual
+  MOE_HIP_TRY(launch_dx_final(c, p.dl, w->w_router, p.dXr, sv->inv_row, S > 0 ? p.dXs : nullptr,
+                              c.add_residual ? dy : nullptr, g->dx, stream));
   return MOE_OK;
 }
 

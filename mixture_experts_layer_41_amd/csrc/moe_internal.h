@@ -137,34 +137,79 @@ hipError_t launch_combine(const moe_config& c, const void* y_perm, const int32_t
 // ---------------------------------------------------------------------------
 // backward pass (backward.hip, gemm_wgrad.hip); bf16 operands
 
-hipError_t launch_combine_bwd(const moe_config& c, const void* dy, const void* y_perm,
-                              const int32_t* inv_row, const float* topk_w, void* d_yperm,
-                              float* d_topk_w, hipStream_t s);
-hipError_t launch_router_grad(const moe_config& c, const float* scores, const float* lse,
-                              const int32_t* topk_idx, const float* topk_w, const float* d_topk_w,
-                              const int32_t* counts, const moe_loss_weights& lw, float* aux_dp,
-                              float* dl, hipStream_t s);
-hipError_t launch_pad_offsets(const int32_t* offsets, int G, int pad, int64_t ncols, int32_t* poff,
-                              int32_t* colrow, hipStream_t s);
-hipError_t launch_transpose(const void* src, int64_t src_ld, int64_t src_batch,
-                            const int32_t* colrow, const int32_t* gather, int64_t nsrc,
-                            int64_t ncols, int C, void* dst, int64_t dst_ld, int64_t dst_batch,
-                            int batches, hipStream_t s);
+// per-expert load-balance part of dL/dp when a term needs the mean router
+// probability (lb_squares or kl_uniform weighted)
+hipError_t launch_aux_dp(const moe_config& c, const float* scores, const float* lse,
+                         const int32_t* counts, const moe_loss_weights& lw, float* aux_dp,
+                         hipStream_t s);
+
+// Combine and router backward in one launch; extra workgroups of the same
+// launch pad the group offsets to multiples of `pad` and map the padded
+// columns j < ncols to their source rows.
+struct CombineRouterBwd {
+  const void* dy;
+  const void* y_perm;
+  const int32_t* inv_row;
+  const float* topk_w;
+  void* d_yperm;          // [T k, d] bf16: d o rows (kept rows only)
+  const float* scores;
+  const float* lse;
+  const int32_t* topk_idx;
+  const int32_t* counts;
+  const float* aux_dp;    // from launch_aux_dp, or null
+  float* dl;              // [T, E] float32: dL/d logits
+  const int32_t* offsets; // [E + 1]
+  int pad;
+  int64_t ncols;
+  int32_t* poff;          // [E + 1]
+  int32_t* colrow;        // [ncols]
+};
+hipError_t launch_combine_router_bwd(const moe_config& c, const moe_loss_weights& lw,
+                                     const CombineRouterBwd& b, hipStream_t s);
+
+// dst[b][c][j] = src[b][row(j)][c], c < C, j < ncols, row(j) = colrow ?
+// colrow[j] : (j < nsrc ? j : -1), then through gather when given; negative
+// rows read as zero.  Two problems per launch (b.batches = 0: one).
+struct TransposeDesc {
+  const void* src;
+  int64_t src_ld, src_batch;
+  const int32_t* colrow;
+  const int32_t* gather;
+  int64_t nsrc, ncols;
+  int C;
+  void* dst;
+  int64_t dst_ld, dst_batch;
+  int batches;
+};
+hipError_t launch_transpose(const TransposeDesc& a, const TransposeDesc& b, hipStream_t s);
 hipError_t launch_act_bwd_t(const void* a, int64_t lda, const void* dh, int64_t ldh,
                             const int32_t* colrow, int64_t nsrc, int64_t ncols, int S, int f,
                             int act, void* da, void* dat, void* ht, int64_t ldt, hipStream_t s);
 hipError_t launch_seg_rowsum(const void* m, int64_t ld, int C, const int32_t* poff, int64_t ncols,
                              int G, float* out, int64_t out_ld, hipStream_t s);
-hipError_t launch_colsum_f32(const float* m, int64_t T, int E, float* out, hipStream_t s);
-hipError_t launch_dx_gather(const moe_config& c, const void* dx_rows, const int32_t* inv_row,
-                            const void* shared, const float* dx_router, const void* residual,
-                            void* dx, hipStream_t s);
-int simt_splits(int M, int N, int64_t K);
-hipError_t launch_simt_gemm(const float* a, int64_t sam, int64_t sak, const void* b, int64_t ldb,
-                            int M, int N, int64_t K, int nsplit, float* c, int64_t ldc,
-                            float* partial, hipStream_t s);
+// dW_r = dl^T x (float32 [E, d]) and, when db is given, db_r[e] = sum_t
+// dl[t, e]; nsplit from router_wgrad_splits, part (16-byte aligned) holding
+// nsplit * router_wgrad_split_ld(E, d) floats
+int router_wgrad_splits(int E, int d, int64_t T);
+int64_t router_wgrad_split_ld(int E, int d);
+hipError_t launch_router_wgrad(const float* dl, const void* x, int64_t T, int E, int d, int nsplit,
+                               float* part, float* dw, float* db, hipStream_t s);
+// dx_t = dl_t W_r + sum_j kept dx_rows[row_tj] (+ shared_t) (+ residual_t)
+hipError_t launch_dx_final(const moe_config& c, const float* dl, const void* w_router,
+                           const void* dx_rows, const int32_t* inv_row, const void* shared,
+                           const void* residual, void* dx, hipStream_t s);
+// Weight gradients C_b = A_b B_b^T (float32) over the K range of batch b:
+// kofs[b] .. kofs[b + 1] (K = their total) or 0 .. K.  The plan picks the
+// tile and a K split; a split product needs wgrad_partial_floats(...) floats
+// of `partial` and a dense C (ldc = N, c_batch = M N).
+struct WgradPlan {
+  int tile;    // 128 or 256
+  int nsplit;  // K splits per batch
+};
+WgradPlan wgrad_plan(int M, int N, int batches, int64_t k_avg);
+size_t wgrad_partial_floats(const WgradPlan& w, int M, int N, int batches);
 hipError_t launch_wgrad(const void* a, int64_t lda, int64_t a_batch, const void* b, int64_t ldb,
                         int64_t b_batch, const int32_t* kofs, int64_t K, int M, int N, int batches,
-                        float* c, int64_t ldc, int64_t c_batch, hipStream_t s);
+                        float* c, int64_t ldc, int64_t c_batch, float* partial, hipStream_t s);
 
 }  // namespace moe

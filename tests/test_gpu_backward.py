@@ -106,6 +106,11 @@ CASES = [
     ("k_eq_E", 64, 64, 8, 8, 64, 0, "swiglu", 0.0, "none", "none", False, 1.0, 0.0, 1.0),
     ("T1_E200", 1, 128, 200, 6, 64, 1, "swiglu", 0.0, "none", "none", False, 1.0, 0.0, 1.0),
     ("cap1", 40, 32, 4, 2, 32, 0, "swiglu", 0.25, "none", "none", True, 1.0, 0.0, 1.0),
+    # 65-128 and more than 256 experts (two and eight per router lane); more
+    # than 64 assignments per token (past one per lane)
+    ("E100_k3", 150, 64, 100, 3, 64, 0, "swiglu", 0.0, "none", "zipf", False, 1.0, 0.0, 1.0),
+    ("E300_k4", 70, 64, 300, 4, 32, 1, "gelu", 0.0, "none", "none", False, 1.2, 0.5, 1.0),
+    ("k70_E80", 20, 32, 80, 70, 32, 0, "swiglu", 0.0, "random", "none", True, 1.0, 0.0, 1.0),
 ]
 
 
@@ -140,3 +145,21 @@ def test_backward_load_balance_forms(name):
         cfg = get_config("c2")
     say(f"[case] {name}")
     run_case(cfg, 1.0, seed=951, loss_weights=LW)
+
+
+# Shapes that reach the weight-gradient product's other plans: 128 x 128
+# tiles with a K split (long K, few tiles: the shared expert's 2048 tokens
+# and two routed experts of ~1024 rows each), and 256 x 256 tiles with and
+# without a K split (16384 tokens; eight experts of ~4096 rows each)
+WGRAD_SHAPES = [
+    ("wgrad_split_128", 2048, 64, 2, 1, 64, 1),
+    ("wgrad_tile256_split", 16384, 1024, 8, 2, 1024, 1),
+]
+
+
+@pytest.mark.parametrize("row", WGRAD_SHAPES, ids=[r[0] for r in WGRAD_SHAPES])
+def test_backward_wgrad_plans(row):
+    name, T, d, E, k, f, S = row
+    cfg = LayerConfig(name, T=T, d=d, E=E, k=k, f=f, S=S, dtype="bf16", act="swiglu", seed=960)
+    say(f"[case] {name}")
+    run_case(cfg, 1.0, seed=961)
