@@ -389,95 +389,123 @@ transpose_kernel(TransposeJob j0, TransposeJob j1, unsigned n0) {
   }
 }
 
-// act_bwd_t's LDS tiles: 64 rows, pitch 72 elements (rows stay 16-byte aligned)
-constexpr int kTP = 72;
-
 // ---------------------------------------------------------------------------
 // activation backward fused with the transposes the weight gradients need.
-// Tile (64 destination columns j) x (64 columns n of one segment s): column j
-// takes source row r = colrow ? colrow[j] : (j < nsrc ? j : -1) (-1 and -2:
+// Tile (128 destination columns j) x (64 columns n of one segment s): column
+// j takes source row r = colrow ? colrow[j] : (j < nsrc ? j : -1) (-1 and -2:
 // zero padding).  SwiGLU: a holds [gate | up] per segment (2f columns),
 // h = silu(g) u, dg = dh u silu'(g), du = dh silu(g); GELU: h = gelu(a),
 // da = dh gelu'(a).  Writes da row-major (rows r >= 0 only, for the dx
 // product) and, through LDS, da^T [S * arow, ldt] and h^T [S * f, ldt] at
-// columns j (zeros for padding).
+// columns j (zeros for padding).  Every thread issues the loads of its four
+// (row, 8 columns) items before it computes; LDS rows keep their 8 chunks at
+// positions ch ^ (row / 8 % 8), so the column reads of the transposed side
+// are at most 2-way bank-conflicted; the transposed stores are 256 bytes
+// per destination row.
+
+constexpr int kAJ = 128;                    // destination columns j (source rows) per tile
+constexpr int kAN = 64;                     // columns n per tile
+constexpr int kACh = kAN / 8;               // 16-byte chunks per LDS row
+constexpr int kAI = kAJ * kACh / kThreads;  // (row, chunk) items per thread
 
 __global__ void __launch_bounds__(kThreads)
 act_bwd_t_kernel(const uint16_t* __restrict__ a, int64_t lda, const uint16_t* __restrict__ dh,
                  int64_t ldh, const int32_t* __restrict__ colrow, int64_t nsrc, int64_t ncols,
                  int f, int act, uint16_t* __restrict__ da, uint16_t* __restrict__ dat,
                  uint16_t* __restrict__ ht, int64_t ldt) {
-  __shared__ __attribute__((aligned(16))) uint16_t tg[64 * kTP];
-  __shared__ __attribute__((aligned(16))) uint16_t tu[64 * kTP];
-  __shared__ __attribute__((aligned(16))) uint16_t th[64 * kTP];
-  __shared__ int32_t rows[64];
-  const int64_t j0 = (int64_t)blockIdx.x * 64;
-  const int n0 = blockIdx.y * 64, s = blockIdx.z;
+  __shared__ __attribute__((aligned(16))) u32x4v tg[kAJ * kACh];
+  __shared__ __attribute__((aligned(16))) u32x4v tu[kAJ * kACh];
+  __shared__ __attribute__((aligned(16))) u32x4v th[kAJ * kACh];
+  __shared__ int32_t rows[kAJ];
+  const int64_t j0 = (int64_t)blockIdx.x * kAJ;
+  const int n0 = blockIdx.y * kAN, s = blockIdx.z;
   const bool swiglu = act == MOE_ACT_SWIGLU;
   const int arow = swiglu ? 2 * f : f;
-  if (threadIdx.x < 64) {
+  if (threadIdx.x < kAJ) {
     const int64_t j = j0 + threadIdx.x;
     int32_t r = -1;
     if (j < ncols) r = colrow ? colrow[j] : (j < nsrc ? (int32_t)j : -1);
     rows[threadIdx.x] = r;
   }
   __syncthreads();
+  // loads (branch-free: an item outside the problem reads element 0 and is
+  // zeroed)
+  u32x4v rg[kAI], ru[kAI], rd[kAI];
+  int64_t ab[kAI];
+  bool ok[kAI];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int o = threadIdx.x + kThreads * u;
-    const int jj = o / 8, ch = o % 8;
+  for (int i = 0; i < kAI; ++i) {
+    const int o = threadIdx.x + kThreads * i;
+    const int jj = o / kACh, ch = o % kACh;
     const int32_t r = rows[jj];
     const int n = n0 + ch * 8;
+    ok[i] = r >= 0 && n < f;
+    ab[i] = ok[i] ? (int64_t)r * lda + (int64_t)s * arow + n : 0;
+    const int64_t hb = ok[i] ? (int64_t)r * ldh + (int64_t)s * f + n : 0;
+    rg[i] = *reinterpret_cast<const u32x4v*>(a + ab[i]);
+    rd[i] = *reinterpret_cast<const u32x4v*>(dh + hb);
+    ru[i] = u32x4v{0u, 0u, 0u, 0u};
+    if (swiglu) ru[i] = *reinterpret_cast<const u32x4v*>(a + ab[i] + f);
+  }
+#pragma unroll
+  for (int i = 0; i < kAI; ++i) {
+    const int o = threadIdx.x + kThreads * i;
+    const int jj = o / kACh, ch = o % kACh;
     float gv[8], uv[8], dv[8], dg[8], du[8], hv[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dg[i] = du[i] = hv[i] = 0.f;
-    if (r >= 0 && n < f) {
-      const int64_t ab = (int64_t)r * lda + (int64_t)s * arow + n;
-      unpack8(*reinterpret_cast<const u32x4v*>(a + ab), gv);
-      unpack8(*reinterpret_cast<const u32x4v*>(dh + (int64_t)r * ldh + (int64_t)s * f + n), dv);
+    for (int e = 0; e < 8; ++e) dg[e] = du[e] = hv[e] = 0.f;
+    if (ok[i]) {
+      unpack8(rg[i], gv);
+      unpack8(rd[i], dv);
       if (swiglu) {
-        unpack8(*reinterpret_cast<const u32x4v*>(a + ab + f), uv);
+        unpack8(ru[i], uv);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float sg = 1.f / (1.f + __expf(-gv[i]));
-          const float si = gv[i] * sg;
-          hv[i] = si * uv[i];
-          dg[i] = dv[i] * uv[i] * sg * (1.f + gv[i] * (1.f - sg));
-          du[i] = dv[i] * si;
+        for (int e = 0; e < 8; ++e) {
+          const float sg = 1.f / (1.f + __expf(-gv[e]));
+          const float si = gv[e] * sg;
+          hv[e] = si * uv[e];
+          dg[e] = dv[e] * uv[e] * sg * (1.f + gv[e] * (1.f - sg));
+          du[e] = dv[e] * si;
         }
-        *reinterpret_cast<u32x4v*>(da + ab) = pack8(dg);
-        *reinterpret_cast<u32x4v*>(da + ab + f) = pack8(du);
+        *reinterpret_cast<u32x4v*>(da + ab[i]) = pack8(dg);
+        *reinterpret_cast<u32x4v*>(da + ab[i] + f) = pack8(du);
       } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float Phi = 0.5f * (1.f + erff(gv[i] * 0.70710678118654752f));
-          const float phi = 0.39894228040143268f * __expf(-0.5f * gv[i] * gv[i]);
-          hv[i] = gv[i] * Phi;
-          dg[i] = dv[i] * (Phi + gv[i] * phi);
+        for (int e = 0; e < 8; ++e) {
+          const float Phi = 0.5f * (1.f + erff(gv[e] * 0.70710678118654752f));
+          const float phi = 0.39894228040143268f * __expf(-0.5f * gv[e] * gv[e]);
+          hv[e] = gv[e] * Phi;
+          dg[e] = dv[e] * (Phi + gv[e] * phi);
         }
-        *reinterpret_cast<u32x4v*>(da + ab) = pack8(dg);
+        *reinterpret_cast<u32x4v*>(da + ab[i]) = pack8(dg);
       }
     }
     // the bf16 values written above, or zeros
-    *reinterpret_cast<u32x4v*>(&tg[jj * kTP + ch * 8]) = pack8(dg);
-    if (swiglu) *reinterpret_cast<u32x4v*>(&tu[jj * kTP + ch * 8]) = pack8(du);
-    *reinterpret_cast<u32x4v*>(&th[jj * kTP + ch * 8]) = pack8(hv);
+    const int pos = jj * kACh + (ch ^ ((jj / 8) % kACh));
+    tg[pos] = pack8(dg);
+    if (swiglu) tu[pos] = pack8(du);
+    th[pos] = pack8(hv);
   }
   __syncthreads();
+  const uint16_t* g16 = reinterpret_cast<const uint16_t*>(tg);
+  const uint16_t* u16 = reinterpret_cast<const uint16_t*>(tu);
+  const uint16_t* h16 = reinterpret_cast<const uint16_t*>(th);
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int o = threadIdx.x + kThreads * u;
-    const int cc = o / 8, jc = o % 8;
+  for (int i = 0; i < kAI; ++i) {
+    const int o = threadIdx.x + kThreads * i;
+    const int cc = o / (kAJ / 8), jc = o % (kAJ / 8);
     const int c = n0 + cc;
     const int64_t j = j0 + jc * 8;
     if (c >= f || j >= ncols) continue;
+    // rows jc * 8 + 0..7 keep column cc in chunk (cc / 8) ^ (jc % 8)
+    const int base = ((cc / 8) ^ (jc % kACh)) * 8 + cc % 8;
     uint32_t wg[4], wu[4], wh[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int r0 = (jc * 8 + 2 * q) * kTP + cc, r1 = r0 + kTP;
-      wg[q] = (uint32_t)tg[r0] | ((uint32_t)tg[r1] << 16);
-      wu[q] = swiglu ? ((uint32_t)tu[r0] | ((uint32_t)tu[r1] << 16)) : 0u;
-      wh[q] = (uint32_t)th[r0] | ((uint32_t)th[r1] << 16);
+      const int r0 = (jc * 8 + 2 * q) * kAN + base, r1 = r0 + kAN;
+      wg[q] = (uint32_t)g16[r0] | ((uint32_t)g16[r1] << 16);
+      wu[q] = swiglu ? ((uint32_t)u16[r0] | ((uint32_t)u16[r1] << 16)) : 0u;
+      wh[q] = (uint32_t)h16[r0] | ((uint32_t)h16[r1] << 16);
     }
     const int64_t crow = (int64_t)s * arow + c;
     *reinterpret_cast<u32x4v*>(dat + crow * ldt + j) = u32x4v{wg[0], wg[1], wg[2], wg[3]};
@@ -854,7 +882,7 @@ hipError_t launch_act_bwd_t(const void* a, int64_t lda, const void* dh, int64_t 
                             const int32_t* colrow, int64_t nsrc, int64_t ncols, int S, int f,
                             int act, void* da, void* dat, void* ht, int64_t ldt, hipStream_t s) {
   if (ncols <= 0 || S <= 0) return hipSuccess;
-  act_bwd_t_kernel<<<dim3(blocks_for(ncols, 64), blocks_for(f, 64), S), kThreads, 0, s>>>(
+  act_bwd_t_kernel<<<dim3(blocks_for(ncols, kAJ), blocks_for(f, kAN), S), kThreads, 0, s>>>(
       static_cast<const uint16_t*>(a), lda, static_cast<const uint16_t*>(dh), ldh, colrow, nsrc,
       ncols, f, act, static_cast<uint16_t*>(da), static_cast<uint16_t*>(dat),
       static_cast<uint16_t*>(ht), ldt);
