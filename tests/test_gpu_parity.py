@@ -249,6 +249,9 @@ SMALL_Q8 = [
     ("q8_gelu_bias_shared2", 150, 256, 6, 3, 128, 2, "gelu", 0.0, "random", "none", True),
     ("q8_cap_drop_shared", 300, 128, 16, 2, 256, 1, "swiglu", 1.0, "none", "zipf", False),
     ("q8_k10", 64, 128, 12, 10, 128, 0, "swiglu", 0.0, "none", "none", False),
+    # decode-shaped (12 rows per expert) with K = 512 and 256: the INT8
+    # weight stream's two-deep prefetch over several loop turns
+    ("q8_decode_k512", 96, 512, 32, 4, 256, 1, "swiglu", 0.0, "random", "none", False),
 ]
 
 
