@@ -183,8 +183,9 @@ wgrad_reduce_kernel(const float* __restrict__ part, int nsplit, int64_t n, float
 // per CU) costs its K tiles per split, times 1.5 for the large tile (it does
 // twice the work of a pair at the higher efficiency measured for it).
 // A split product also writes and reads back its float32 partials (one such
-// unit moves about 8.5 MB at HBM rate).  Splits keep at least 1024 (large
-// tile) or 512 K rows each, at most 64; the fewest splits win a tie.
+// unit moves about 8.5 MB at HBM rate).  The large tile needs batches of 512
+// K rows on average; splits keep at least 512 K rows each, at most 64; the
+// fewest splits win a tie.
 WgradPlan wgrad_plan(int M, int N, int batches, int64_t k_avg) {
   WgradPlan best{128, 1};
   if (M <= 0 || N <= 0 || batches <= 0 || k_avg <= 0) return best;
@@ -192,8 +193,8 @@ WgradPlan wgrad_plan(int M, int N, int batches, int64_t k_avg) {
   for (const int tile : {256, 128}) {
     const int64_t t = (int64_t)((M + tile - 1) / tile) * ((N + tile - 1) / tile) * batches;
     const int64_t slots = tile == 256 ? 256 : 512;
-    const int64_t min_rows = tile == 256 ? 1024 : 512;
-    if (tile == 256 && k_avg < min_rows) continue;
+    const int64_t min_rows = 512;
+    if (k_avg < min_rows && tile == 256) continue;
     const int64_t ns_max = std::max<int64_t>(1, std::min<int64_t>(k_avg / min_rows, 64));
     for (int64_t ns = 1; ns <= ns_max; ++ns) {
       const int64_t rounds = (t * ns + slots - 1) / slots;
