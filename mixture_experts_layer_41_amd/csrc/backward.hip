@@ -16,14 +16,16 @@
 //                   workgroups of the same launch pad the group offsets to
 //                   multiples of the K tile and map every padded column to
 //                   its source row (-1: zero padding)
-//   transpose       [rows, C] -> [C, columns], two problems per launch: the
+//   side            one launch of independent parts: [rows, C] -> [C,
+//                   columns] transposes, two problems per launch (the
 //                   weights, and d_o and the gathered x into the padded
-//                   columns
+//                   columns), with the router weight gradient's split
+//                   products or split sums as extra workgroups
 //   act_bwd_t       a, dh -> da (row-major) and da^T, h^T (padded columns)
 //   seg_rowsum      bias gradients: sums of each row of a transposed matrix
 //                   over each group's columns
 //   router_wgrad    dW_r = dl^T x and db_r = column sums of dl (float32,
-//                   split over tokens), reduce_splits sums the splits
+//                   split over tokens); reduce sums the splits
 //   dx_final        dx_t = dl_t W_r + sum_j dx_rows[row_tj] + shared +
 //                   residual
 // Every reduction runs in a fixed order: no atomics.
@@ -318,11 +320,10 @@ struct TransposeJob {
 constexpr int kTT = 128;
 constexpr int kTC = kTT / 8;  // 16-byte chunks per tile row
 
-__global__ void __launch_bounds__(kThreads)
-transpose_kernel(TransposeJob j0, TransposeJob j1, unsigned n0) {
-  __shared__ __attribute__((aligned(16))) u32x4v tile[kTT * kTC];
-  __shared__ int32_t rows[kTT];
-  unsigned b = blockIdx.x;
+// Workgroup b of a two-problem transpose launch (tile: kTT * kTC chunks of
+// LDS, rows: kTT ints).
+__device__ void transpose_part(const TransposeJob& j0, const TransposeJob& j1, unsigned n0,
+                               unsigned b, u32x4v* __restrict__ tile, int32_t* __restrict__ rows) {
   const bool second = b >= n0;
   const TransposeJob& J = second ? j1 : j0;
   if (second) b -= n0;
@@ -552,17 +553,33 @@ seg_rowsum_kernel(const uint16_t* __restrict__ m, int64_t ld, int C, const int32
 
 constexpr int kRK = 32;
 
-__global__ void __launch_bounds__(kThreads)
-router_wgrad_kernel(const float* __restrict__ dl, const uint16_t* __restrict__ x, int64_t T,
-                    int E, int d, int64_t kchunk, float* __restrict__ out, int64_t out_split,
-                    float* __restrict__ bout, int64_t bout_split) {
-  __shared__ __attribute__((aligned(16))) float As[kRK][64];
-  __shared__ __attribute__((aligned(16))) float Bs[kRK][64];
-  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
-  const int64_t kb = (int64_t)blockIdx.z * kchunk;
+struct RouterWgradArgs {
+  const float* dl;
+  const uint16_t* x;
+  int64_t T;
+  int E, d;
+  int64_t kchunk;
+  float* out;  // split s at out + s * out_split
+  int64_t out_split;
+  float* bout;  // split s at bout + s * bout_split, or null
+  int64_t bout_split;
+  unsigned tx, ty;  // column and row tiles; workgroup b = (split * ty + row tile) * tx + column tile
+};
+
+// Workgroup b of the router weight gradient (As, Bs: kRK x 64 floats of LDS
+// each).
+__device__ void router_wgrad_part(const RouterWgradArgs& w, unsigned b, float (*__restrict__ As)[64],
+                                  float (*__restrict__ Bs)[64]) {
+  const float* __restrict__ dl = w.dl;
+  const uint16_t* __restrict__ x = w.x;
+  const int64_t T = w.T, kchunk = w.kchunk;
+  const int E = w.E, d = w.d;
+  const unsigned bx = b % w.tx, by = (b / w.tx) % w.ty, bz = b / (w.tx * w.ty);
+  const int m0 = by * 64, n0 = bx * 64;
+  const int64_t kb = (int64_t)bz * kchunk;
   const int64_t ke = kb + kchunk < T ? kb + kchunk : T;
   const int tid = threadIdx.x, tm = tid / 16, tn = tid % 16;
-  const bool bias = bout != nullptr && blockIdx.x == 0;
+  const bool bias = w.bout != nullptr && bx == 0;
   float acc[4][4] = {};
   float bacc = 0.f;
   float ra[8];
@@ -609,7 +626,7 @@ router_wgrad_kernel(const float* __restrict__ dl, const uint16_t* __restrict__ x
       for (int kk = 0; kk < kRK; ++kk) bacc += As[kk][tid];
     __syncthreads();
   }
-  float* O = out + (int64_t)blockIdx.z * out_split;
+  float* O = w.out + (int64_t)bz * w.out_split;
   const int n = n0 + tn * 4;  // d is a multiple of 8: four columns all in or all out
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -618,20 +635,31 @@ router_wgrad_kernel(const float* __restrict__ dl, const uint16_t* __restrict__ x
       *reinterpret_cast<float4*>(O + (int64_t)m * d + n) =
           float4{acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
   }
-  if (bias && tid < 64 && m0 + tid < E) bout[(int64_t)blockIdx.z * bout_split + m0 + tid] = bacc;
+  if (bias && tid < 64 && m0 + tid < E) w.bout[(int64_t)bz * w.bout_split + m0 + tid] = bacc;
 }
 
 // Sum of the splits (split s at part + s * ld), 64 outputs per workgroup:
 // the four waves take every fourth split each (eight loads in flight), then
 // wave 0 adds the four partial sums in order.  Outputs i < n_a go to out_a,
 // the rest (i < n) to out_b.
-__global__ void __launch_bounds__(kThreads)
-reduce_splits_kernel(const float* __restrict__ part, int nsplit, int64_t ld, int64_t n,
-                     int64_t n_a, float* __restrict__ out_a, float* __restrict__ out_b) {
-  constexpr int G = kThreads / kWave;
-  __shared__ float red[G][kWave];
+struct ReduceArgs {
+  const float* part;
+  int nsplit;
+  int64_t ld, n, n_a;
+  float* out_a;
+  float* out_b;
+};
+
+constexpr int kRG = kThreads / kWave;  // split groups of the sum
+
+// Workgroup b of the sum (red: kRG x kWave floats of LDS).
+__device__ void reduce_part(const ReduceArgs& r, unsigned b, float (*__restrict__ red)[kWave]) {
+  constexpr int G = kRG;
+  const float* __restrict__ part = r.part;
+  const int nsplit = r.nsplit;
+  const int64_t ld = r.ld, n = r.n, n_a = r.n_a;
   const int g = threadIdx.x / kWave, li = threadIdx.x % kWave;
-  const int64_t i = (int64_t)blockIdx.x * kWave + li;
+  const int64_t i = (int64_t)b * kWave + li;
   float acc = 0.f;
   if (i < n) {
     int s = g;
@@ -647,11 +675,47 @@ reduce_splits_kernel(const float* __restrict__ part, int nsplit, int64_t ld, int
   red[g][li] = acc;
   __syncthreads();
   if (g == 0 && i < n) {
-    float r = red[0][li];
+    float sum = red[0][li];
 #pragma unroll
-    for (int q = 1; q < G; ++q) r += red[q][li];
-    if (i < n_a) out_a[i] = r; else out_b[i - n_a] = r;
+    for (int q = 1; q < G; ++q) sum += red[q][li];
+    if (i < n_a) r.out_a[i] = sum; else r.out_b[i - n_a] = sum;
   }
+}
+
+// ---------------------------------------------------------------------------
+// One launch for independent side work of the backward: the workgroups
+// [0, n_w) run the router weight gradient's split products, the next n_r
+// sum its splits, the rest transpose (two problems).  The latency-bound
+// router parts come first in dispatch order, so the bandwidth-bound
+// transposes fill the CUs around them.  The parts share one LDS buffer.
+
+struct SideArgs {
+  TransposeJob t0, t1;
+  unsigned n_t0;
+  RouterWgradArgs w;
+  unsigned n_w;
+  ReduceArgs r;
+  unsigned n_r;
+};
+
+__global__ void __launch_bounds__(kThreads) side_kernel(SideArgs a) {
+  __shared__ __attribute__((aligned(16))) u32x4v lds[kTT * kTC];
+  __shared__ int32_t rows[kTT];
+  static_assert(2 * kRK * 64 * sizeof(float) <= sizeof(lds), "router tiles fit the buffer");
+  static_assert(kRG * kWave * sizeof(float) <= sizeof(lds), "split sums fit the buffer");
+  unsigned b = blockIdx.x;
+  float* f = reinterpret_cast<float*>(lds);
+  if (b < a.n_w) {
+    router_wgrad_part(a.w, b, reinterpret_cast<float (*)[64]>(f),
+                      reinterpret_cast<float (*)[64]>(f + kRK * 64));
+    return;
+  }
+  b -= a.n_w;
+  if (b < a.n_r) {
+    reduce_part(a.r, b, reinterpret_cast<float (*)[kWave]>(f));
+    return;
+  }
+  transpose_part(a.t0, a.t1, a.n_t0, b - a.n_r, lds, rows);
 }
 
 // ---------------------------------------------------------------------------
@@ -865,17 +929,80 @@ static TransposeJob job_of(const TransposeDesc& t) {
   return j;
 }
 
-hipError_t launch_transpose(const TransposeDesc& a, const TransposeDesc& b, hipStream_t s) {
+// dW_r goes straight to the caller's buffer (16-byte stores) when there is
+// one split and the buffer allows it; otherwise through the split partials.
+static bool router_wgrad_direct(const RouterWgradDesc& r) {
+  return r.nsplit == 1 && ((uintptr_t)r.dw & 15) == 0;
+}
+
+hipError_t launch_side(const TransposeDesc& a, const TransposeDesc& b, const RouterWgradDesc* rp,
+                       const RouterWgradDesc* rs, hipStream_t s) {
+  SideArgs x{};
   const bool ua = a.ncols > 0 && a.C > 0 && a.batches > 0;
   const bool ub = b.ncols > 0 && b.C > 0 && b.batches > 0;
-  if (!ua && !ub) return hipSuccess;
-  const TransposeJob j0 = job_of(ua ? a : b);  // a lone problem goes first
-  const TransposeJob j1 = ua && ub ? job_of(b) : j0;
-  const uint64_t n0 = (uint64_t)j0.tx * j0.ty * (uint64_t)(ua ? a.batches : b.batches);
-  const uint64_t n1 = ua && ub ? (uint64_t)j1.tx * j1.ty * (uint64_t)b.batches : 0;
-  if (n0 + n1 > 0xFFFFFFFFull) return hipErrorInvalidValue;
-  transpose_kernel<<<(unsigned)(n0 + n1), kThreads, 0, s>>>(j0, j1, (unsigned)n0);
+  uint64_t n_t = 0, n_w = 0, n_r = 0;
+  if (ua || ub) {
+    x.t0 = job_of(ua ? a : b);  // a lone problem goes first
+    x.t1 = ua && ub ? job_of(b) : x.t0;
+    const uint64_t n0 = (uint64_t)x.t0.tx * x.t0.ty * (uint64_t)(ua ? a.batches : b.batches);
+    const uint64_t n1 = ua && ub ? (uint64_t)x.t1.tx * x.t1.ty * (uint64_t)b.batches : 0;
+    if (n0 > 0xFFFFFFFFull) return hipErrorInvalidValue;
+    x.n_t0 = (unsigned)n0;
+    n_t = n0 + n1;
+  }
+  if (rp != nullptr) {
+    const RouterWgradDesc& r = *rp;
+    if (r.nsplit < 1 || r.part == nullptr || ((uintptr_t)r.part & 15) != 0 || r.T < 1)
+      return hipErrorInvalidValue;
+    const int64_t kchunk = ((r.T + r.nsplit - 1) / r.nsplit + kRK - 1) / kRK * kRK;
+    if ((r.T + kchunk - 1) / kchunk != r.nsplit) return hipErrorInvalidValue;
+    x.w.dl = r.dl;
+    x.w.x = static_cast<const uint16_t*>(r.x);
+    x.w.T = r.T;
+    x.w.E = r.E;
+    x.w.d = r.d;
+    x.w.kchunk = kchunk;
+    if (router_wgrad_direct(r)) {
+      x.w.out = r.dw;
+      x.w.out_split = 0;
+      x.w.bout = r.db;
+      x.w.bout_split = 0;
+    } else {
+      // partials [nsplit][ld], the bias partials after the weight's
+      const int64_t ld = router_wgrad_split_ld(r.E, r.d);
+      x.w.out = r.part;
+      x.w.out_split = ld;
+      x.w.bout = r.db ? r.part + (int64_t)r.E * r.d : nullptr;
+      x.w.bout_split = ld;
+    }
+    x.w.tx = blocks_for(r.d, 64);
+    x.w.ty = blocks_for(r.E, 64);
+    n_w = (uint64_t)x.w.tx * x.w.ty * (uint64_t)r.nsplit;
+  }
+  if (rs != nullptr && !router_wgrad_direct(*rs)) {
+    const RouterWgradDesc& r = *rs;
+    if (r.part == nullptr) return hipErrorInvalidValue;
+    const int64_t nw = (int64_t)r.E * r.d;
+    x.r.part = r.part;
+    x.r.nsplit = r.nsplit;
+    x.r.ld = router_wgrad_split_ld(r.E, r.d);
+    x.r.n = nw + (r.db ? r.E : 0);
+    x.r.n_a = nw;
+    x.r.out_a = r.dw;
+    x.r.out_b = r.db;
+    n_r = blocks_for(x.r.n, kWave);
+  }
+  const uint64_t total = n_t + n_w + n_r;
+  if (total == 0) return hipSuccess;
+  if (total > 0xFFFFFFFFull) return hipErrorInvalidValue;
+  x.n_w = (unsigned)n_w;
+  x.n_r = (unsigned)n_r;
+  side_kernel<<<(unsigned)total, kThreads, 0, s>>>(x);
   return hipGetLastError();
+}
+
+hipError_t launch_transpose(const TransposeDesc& a, const TransposeDesc& b, hipStream_t s) {
+  return launch_side(a, b, nullptr, nullptr, s);
 }
 
 hipError_t launch_act_bwd_t(const void* a, int64_t lda, const void* dh, int64_t ldh,
@@ -912,28 +1039,6 @@ int router_wgrad_splits(int E, int d, int64_t T) {
 }
 
 int64_t router_wgrad_split_ld(int E, int d) { return ((int64_t)E * d + E + 3) / 4 * 4; }
-
-hipError_t launch_router_wgrad(const float* dl, const void* x, int64_t T, int E, int d, int nsplit,
-                               float* part, float* dw, float* db, hipStream_t s) {
-  if (nsplit < 1 || part == nullptr || ((uintptr_t)part & 15) != 0) return hipErrorInvalidValue;
-  const int64_t kchunk = ((T + nsplit - 1) / nsplit + kRK - 1) / kRK * kRK;
-  if ((T + kchunk - 1) / kchunk != nsplit) return hipErrorInvalidValue;
-  const dim3 grid(blocks_for(d, 64), blocks_for(E, 64), (unsigned)nsplit);
-  const uint16_t* xb = static_cast<const uint16_t*>(x);
-  if (nsplit == 1 && ((uintptr_t)dw & 15) == 0) {  // 16-byte stores straight to dW_r
-    router_wgrad_kernel<<<grid, kThreads, 0, s>>>(dl, xb, T, E, d, kchunk, dw, 0, db, 0);
-    return hipGetLastError();
-  }
-  // partials [nsplit][ld], ld = E * d + E rounded up to 16 bytes; the bias
-  // partials after the weight's
-  const int64_t nw = (int64_t)E * d, n = nw + (db ? E : 0), ld = router_wgrad_split_ld(E, d);
-  router_wgrad_kernel<<<grid, kThreads, 0, s>>>(dl, xb, T, E, d, kchunk, part, ld,
-                                                db ? part + nw : nullptr, ld);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  reduce_splits_kernel<<<blocks_for(n, kWave), kThreads, 0, s>>>(part, nsplit, ld, n, nw, dw, db);
-  return hipGetLastError();
-}
 
 hipError_t launch_dx_final(const moe_config& c, const float* dl, const void* w_router,
                            const void* dx_rows, const int32_t* inv_row, const void* shared,

@@ -631,16 +631,16 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
   cb.poff = p.poff;
   cb.colrow = p.colrow;
   MOE_HIP_TRY(launch_combine_router_bwd(c, lw, cb, stream));
-  MOE_HIP_TRY(launch_router_wgrad(p.dl, x, T, E, d, nsplit, p.wr_part, g->dw_router,
-                                  g->drouter_bias, stream));
+  const RouterWgradDesc rw{p.dl, x, T, E, d, nsplit, p.wr_part, g->dw_router, g->drouter_bias};
 
-  // routed experts: transposed weights, dh, da / h (from the saved
+  // routed experts: transposed weights (with the router weight gradient's
+  // split products in the same launch), dh, da / h (from the saved
   // pre-activations), dx rows
   TransposeDesc t2{w->w2, f, (int64_t)d * f, nullptr, nullptr, d, d, f, p.W2t, d,
                    (int64_t)f * d, E};
   TransposeDesc t1{w->w1, d, (int64_t)w1r * d, nullptr, nullptr, w1r, w1r, d, p.W1t, w1r,
                    (int64_t)d * w1r, E};
-  MOE_HIP_TRY(launch_transpose(t2, t1, stream));
+  MOE_HIP_TRY(launch_side(t2, t1, &rw, nullptr, stream));
   GemmDesc gd{};
   gd.group_off = sv->expert_offsets;
   gd.n_groups = E;
@@ -668,10 +668,11 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
   gd.ldo = d;
   MOE_HIP_TRY(launch_gemm(c, kGemmDown, gd, stream));
 
-  // weight gradients from the expert-padded transposes of d o and x
+  // weight gradients from the expert-padded transposes of d o and x (the
+  // router weight gradient's split sums in the same launch)
   TransposeDesc to{p.dO, d, 0, p.colrow, nullptr, 0, Rp, d, p.dOt, Rp, 0, 1};
   TransposeDesc tx{x, d, 0, p.colrow, sv->perm_token, 0, Rp, d, p.Xt, Rp, 0, 1};
-  MOE_HIP_TRY(launch_transpose(to, tx, stream));
+  MOE_HIP_TRY(launch_side(to, tx, nullptr, &rw, stream));
   MOE_HIP_TRY(launch_wgrad(p.dOt, Rp, 0, p.Ht, Rp, 0, p.poff, Rp, d, f, E, g->dw2, f,
                            (int64_t)d * f, p.wg_part, stream));
   MOE_HIP_TRY(launch_wgrad(p.dAt, Rp, 0, p.Xt, Rp, 0, p.poff, Rp, w1r, d, E, g->dw1, d,

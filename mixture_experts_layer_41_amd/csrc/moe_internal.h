@@ -182,18 +182,32 @@ struct TransposeDesc {
   int batches;
 };
 hipError_t launch_transpose(const TransposeDesc& a, const TransposeDesc& b, hipStream_t s);
+
+// dW_r = dl^T x (float32 [E, d]) and, when db is given, db_r[e] = sum_t
+// dl[t, e], split over tokens: nsplit from router_wgrad_splits, part
+// (16-byte aligned) holding nsplit * router_wgrad_split_ld(E, d) floats.
+struct RouterWgradDesc {
+  const float* dl;  // [T, E]
+  const void* x;    // [T, d] bf16
+  int64_t T;
+  int E, d, nsplit;
+  float* part;
+  float* dw;
+  float* db;
+};
+int router_wgrad_splits(int E, int d, int64_t T);
+int64_t router_wgrad_split_ld(int E, int d);
+// The transposes a and b (batches = 0: none) in one launch, with more
+// workgroups in the same launch for the router weight gradient: rp (if
+// given) runs its split products, rs (if given) sums the splits.  Launch
+// rs after rp, in a later launch.
+hipError_t launch_side(const TransposeDesc& a, const TransposeDesc& b, const RouterWgradDesc* rp,
+                       const RouterWgradDesc* rs, hipStream_t s);
 hipError_t launch_act_bwd_t(const void* a, int64_t lda, const void* dh, int64_t ldh,
                             const int32_t* colrow, int64_t nsrc, int64_t ncols, int S, int f,
                             int act, void* da, void* dat, void* ht, int64_t ldt, hipStream_t s);
 hipError_t launch_seg_rowsum(const void* m, int64_t ld, int C, const int32_t* poff, int64_t ncols,
                              int G, float* out, int64_t out_ld, hipStream_t s);
-// dW_r = dl^T x (float32 [E, d]) and, when db is given, db_r[e] = sum_t
-// dl[t, e]; nsplit from router_wgrad_splits, part (16-byte aligned) holding
-// nsplit * router_wgrad_split_ld(E, d) floats
-int router_wgrad_splits(int E, int d, int64_t T);
-int64_t router_wgrad_split_ld(int E, int d);
-hipError_t launch_router_wgrad(const float* dl, const void* x, int64_t T, int E, int d, int nsplit,
-                               float* part, float* dw, float* db, hipStream_t s);
 // dx_t = dl_t W_r + sum_j kept dx_rows[row_tj] (+ shared_t) (+ residual_t)
 hipError_t launch_dx_final(const moe_config& c, const float* dl, const void* w_router,
                            const void* dx_rows, const int32_t* inv_row, const void* shared,
