@@ -136,11 +136,14 @@ def test_backward_full_size(name):
 LW = {"load_balance": 0.5, "z_loss": 0.05, "lb_squares": 2.0, "kl_uniform": 3.0}
 
 
-@pytest.mark.parametrize("name", ["lb_forms_small", "lb_forms_c2"])
+@pytest.mark.parametrize("name", ["lb_forms_small", "lb_forms_E300", "lb_forms_c2"])
 def test_backward_load_balance_forms(name):
     if name == "lb_forms_small":
         cfg = LayerConfig(name, T=300, d=64, E=12, k=3, f=64, S=1, dtype="bf16", act="swiglu",
                           router_bias="zipf", router_temperature=1.3, router_noise_std=0.5, seed=950)
+    elif name == "lb_forms_E300":  # eight experts per router lane
+        cfg = LayerConfig(name, T=90, d=64, E=300, k=4, f=32, S=1, dtype="bf16", act="gelu",
+                          router_temperature=1.2, router_noise_std=0.5, seed=952)
     else:
         cfg = get_config("c2")
     say(f"[case] {name}")
