@@ -99,7 +99,7 @@ def traffic_entry(workload):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (this build runs on a single MI355X); "
+        print(f"bench.py measures one GPU only (the layer runs on a single MI355X); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
