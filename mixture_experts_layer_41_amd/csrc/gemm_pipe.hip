@@ -107,7 +107,11 @@ struct TileSrc {
   const uint16_t* b[B_IW];
 };
 
-template <int BM, int BN, int WM, int WN, int KIND, int ACT, bool BIAS, int NSt>
+// PAIRED (SwiGLU up GEMM that also stores the pre-activations): the
+// epilogue pairs lanes l and l ^ 32, which hold the two 4-column halves of
+// each 8-column run of a row, so that every store is 16 bytes.  A separate
+// instantiation, so the inference kernel keeps its registers.
+template <int BM, int BN, int WM, int WN, int KIND, int ACT, bool BIAS, int NSt, bool PAIRED>
 __global__ void __launch_bounds__(64 * WM * WN)
 gemm_pipe_kernel(GemmDesc p, int tiles_n) {
   constexpr int NS = NSt;  // LDS stages: 4, or 8 for the deep variant
@@ -406,7 +410,54 @@ gemm_pipe_kernel(GemmDesc p, int tiles_n) {
       const int r = wm * TM + i * 32 + fr;
       if (r < tc.rows) {
         const int64_t grow = tc.row0 + r;
-        if (kSwiglu) {
+        if constexpr (kSwiglu && PAIRED) {
+          // lane l keeps its own half of runs 0, 2 (lower 32 lanes) or 1, 3
+          // (upper), gives the partner its half of the other two runs and
+          // stores 16 bytes per run it keeps
+#pragma unroll
+          for (int j = 0; j < NI / 2; ++j) {
+            uint32_t hw[4][2], gw[4][2], uw[4][2];
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const int cidx = wn * (TN / 2) + j * 32 + 8 * g4 + 4 * half;
+              uint16_t h[4], pg[4], pu[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                float gv = acc[i][j][4 * g4 + e], uv = acc[i][j + NI / 2][4 * g4 + e];
+                if (BIAS) {
+                  const uint16_t* b = bias + ((int64_t)tc.group * S + tc.seg) * 2 * f;
+                  gv += bf16_to_f32(b[tc.n0 + cidx + e]);
+                  uv += bf16_to_f32(b[f + tc.n0 + cidx + e]);
+                }
+                h[e] = f32_to_bf16(silu_f(gv) * uv);
+                pg[e] = f32_to_bf16(gv);
+                pu[e] = f32_to_bf16(uv);
+              }
+              hw[g4][0] = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+              hw[g4][1] = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+              gw[g4][0] = (uint32_t)pg[0] | ((uint32_t)pg[1] << 16);
+              gw[g4][1] = (uint32_t)pg[2] | ((uint32_t)pg[3] << 16);
+              uw[g4][0] = (uint32_t)pu[0] | ((uint32_t)pu[1] << 16);
+              uw[g4][1] = (uint32_t)pu[2] | ((uint32_t)pu[3] << 16);
+            }
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr) {
+              const int gs = 2 * pr + (half ? 0 : 1), gk = 2 * pr + (half ? 1 : 0);
+              const int cidx = wn * (TN / 2) + j * 32 + 8 * gk;
+              // the partner's half of run gk arrives for this lane's half of run gs
+              auto run = [&](const uint32_t (*w)[2]) {
+                const uint32_t r0 = (uint32_t)__shfl_xor((int)w[gs][0], 32);
+                const uint32_t r1 = (uint32_t)__shfl_xor((int)w[gs][1], 32);
+                return half ? uint4{r0, r1, w[gk][0], w[gk][1]} : uint4{w[gk][0], w[gk][1], r0, r1};
+              };
+              *reinterpret_cast<uint4*>(out + grow * p.ldo + (int64_t)tc.seg * f + tc.n0 + cidx) = run(hw);
+              uint16_t* pa = static_cast<uint16_t*>(p.preact) + grow * p.ldp +
+                             (int64_t)tc.seg * 2 * f + tc.n0 + cidx;
+              *reinterpret_cast<uint4*>(pa) = run(gw);
+              *reinterpret_cast<uint4*>(pa + f) = run(uw);
+            }
+          }
+        } else if (kSwiglu) {
 #pragma unroll
           for (int j = 0; j < NI / 2; ++j) {
 #pragma unroll
@@ -518,7 +569,7 @@ int device_cus() {
   return n;
 }
 
-template <int BM, int BN, int WM, int WN, int KIND, int ACT, bool BIAS, int NSt>
+template <int BM, int BN, int WM, int WN, int KIND, int ACT, bool BIAS, int NSt, bool PAIRED>
 hipError_t run_pipe(const GemmDesc& g, int occ, hipStream_t s) {
   constexpr int NT = 64 * WM * WN;
   constexpr bool kSwiglu = (KIND == kGemmUp && ACT == MOE_ACT_SWIGLU);
@@ -528,18 +579,18 @@ hipError_t run_pipe(const GemmDesc& g, int occ, hipStream_t s) {
   if (upper <= 0 || g.rows_max <= 0) return hipSuccess;
   int64_t grid = std::min<int64_t>(upper, (int64_t)device_cus() * occ);
   grid = (grid + 7) / 8 * 8;  // a multiple of 8 (XCDs)
-  pipe::gemm_pipe_kernel<BM, BN, WM, WN, KIND, ACT, BIAS, NSt>
+  pipe::gemm_pipe_kernel<BM, BN, WM, WN, KIND, ACT, BIAS, NSt, PAIRED>
       <<<dim3((unsigned)grid), dim3(NT), 0, s>>>(g, tiles_n);
   return hipGetLastError();
 }
 
-template <int KIND, int ACT, bool BIAS>
+template <int KIND, int ACT, bool BIAS, bool PAIRED = false>
 hipError_t dispatch_pipe(const GemmDesc& g, int shape, int occ, hipStream_t s) {
   switch (shape) {
-    case 0: return run_pipe<256, 256, 2, 2, KIND, ACT, BIAS, 4>(g, occ, s);
-    case 1: return run_pipe<256, 128, 2, 2, KIND, ACT, BIAS, 4>(g, occ, s);
-    case 2: return run_pipe<128, 128, 2, 2, KIND, ACT, BIAS, 4>(g, occ, s);
-    default: return run_pipe<128, 128, 2, 2, KIND, ACT, BIAS, 8>(g, occ, s);
+    case 0: return run_pipe<256, 256, 2, 2, KIND, ACT, BIAS, 4, PAIRED>(g, occ, s);
+    case 1: return run_pipe<256, 128, 2, 2, KIND, ACT, BIAS, 4, PAIRED>(g, occ, s);
+    case 2: return run_pipe<128, 128, 2, 2, KIND, ACT, BIAS, 4, PAIRED>(g, occ, s);
+    default: return run_pipe<128, 128, 2, 2, KIND, ACT, BIAS, 8, PAIRED>(g, occ, s);
   }
 }
 
@@ -564,6 +615,9 @@ hipError_t launch_gemm_pipe(GemmKind kind, const GemmDesc& g, int shape, int occ
   if (kind == kGemmDown)
     return bias ? dispatch_pipe<kGemmDown, 0, true>(g, shape, occ, s)
                 : dispatch_pipe<kGemmDown, 0, false>(g, shape, occ, s);
+  if (g.act == MOE_ACT_SWIGLU && g.preact)  // training forward: 16-byte epilogue stores
+    return bias ? dispatch_pipe<kGemmUp, MOE_ACT_SWIGLU, true, true>(g, shape, occ, s)
+                : dispatch_pipe<kGemmUp, MOE_ACT_SWIGLU, false, true>(g, shape, occ, s);
   if (g.act == MOE_ACT_SWIGLU)
     return bias ? dispatch_pipe<kGemmUp, MOE_ACT_SWIGLU, true>(g, shape, occ, s)
                 : dispatch_pipe<kGemmUp, MOE_ACT_SWIGLU, false>(g, shape, occ, s);
