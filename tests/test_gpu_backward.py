@@ -111,6 +111,9 @@ CASES = [
     ("E100_k3", 150, 64, 100, 3, 64, 0, "swiglu", 0.0, "none", "zipf", False, 1.0, 0.0, 1.0),
     ("E300_k4", 70, 64, 300, 4, 32, 1, "gelu", 0.0, "none", "none", False, 1.2, 0.5, 1.0),
     ("k70_E80", 20, 32, 80, 70, 32, 0, "swiglu", 0.0, "random", "none", True, 1.0, 0.0, 1.0),
+    # the expert-count limit (512): 512 weight-gradient batches, most of them
+    # empty, and 64 padded columns per expert
+    ("E512_k16", 64, 512, 512, 16, 32, 1, "swiglu", 0.0, "none", "zipf", False, 1.0, 0.0, 1.0),
 ]
 
 
