@@ -211,10 +211,15 @@ def router_gap_ok(x, w_router, bias, k: int, dtype: str, gap: float = 1e-4,
                   temperature: float = 1.0, noise=None) -> np.ndarray:
     """Input acceptance rule: p_(k) - p_(k+1) >= gap for every token.
 
-    Evaluated in float64 on the stored (rounded) values, with the router's
-    temperature and noise rows (of the same tokens) applied.  With k == E
-    there is no (k+1)-th expert and every token is accepted.  Used by the
-    input generator through a callback, so that routing is unambiguous.
+    [P3 §3.1] and [P4 §3.1] route by a softmax over the router's scores and
+    keep the k largest probabilities; this rule keeps generated tokens away
+    from near-ties of the k-th and (k+1)-th probability, so that the chosen
+    set is unambiguous.  Evaluated in float64 on the stored (rounded)
+    values, with the router's bias, temperature and noise rows (of the same
+    tokens) applied.  With k == E there is no (k+1)-th expert and every
+    token is accepted.  Used by the input generator through a callback.
+    Pinned by closed-form tokens on both sides of the threshold (k = 1, 2,
+    E; temperature, noise and bias moving the gap).
     """
     xd = decode(x, dtype)
     wr = decode(w_router, dtype)

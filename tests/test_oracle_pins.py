@@ -869,3 +869,137 @@ def test_backward_matches_torch_autograd():
     for name, key in keys.items():
         ref = tt[name].grad.numpy()
         assert np.allclose(g[key], ref, rtol=1e-10, atol=1e-12), key
+
+
+# ---------------------------------------------------------------------------
+# the input acceptance rule (gap of at least 1e-4 between the k-th and the
+# (k+1)-th router probability of every token), pinned by closed forms.
+# [P3 §3.1] and [P4 §3.1] route by softmax and then take the k largest
+# probabilities; the rule only keeps that choice away from near-ties.  Each
+# token below has probabilities q chosen by hand: its logits are ln q (the
+# router is the identity map, float32), so p = q to float32 rounding
+# (absolute error < 1e-7, far inside the 2e-6 margins used here).
+
+def _gap_token(q, k, temperature=1.0, noise=None, bias=None):
+    """router_gap_ok on one token whose probabilities are q (identity router)."""
+    q = np.asarray(q, dtype=np.float64)
+    E = q.size
+    x = f32(np.log(q))[None, :]
+    w = f32(np.eye(E))
+    n = None if noise is None else f32(noise)[None, :]
+    b = None if bias is None else f32(bias)
+    return bool(oracle.router_gap_ok(x, w, b, k, "f32", temperature=temperature, noise=n)[0])
+
+
+def _q_k2(g):
+    """Five experts; the 2nd and 3rd probabilities differ by g (the 1st/2nd
+    and 3rd/4th gaps are about 0.1 and 0.15)."""
+    return [0.35, 0.25 + g / 2, 0.25 - g / 2, 0.1, 0.05]
+
+
+def _q_k1(g):
+    """Five experts; the 1st and 2nd probabilities differ by g."""
+    return [0.3 + g / 2, 0.3 - g / 2, 0.2, 0.15, 0.05]
+
+
+@pytest.mark.parametrize("below", [True, False])
+def test_gap_rule_threshold_k2(below):
+    """k = 2: the gap that matters is p_(2) - p_(3).  Just below 1e-4 the
+    token is rejected, just above it accepted.  A rule that compared the
+    3rd and 4th probabilities (an index off by one) would accept both; one
+    that took the gap on logits (ln(0.25 + g/2) - ln(0.25 - g/2) ~ 4 g)
+    would accept the first."""
+    g = 1e-4 - 2e-6 if below else 1e-4 + 2e-6
+    assert _gap_token(_q_k2(g), 2) is (not below)
+
+
+@pytest.mark.parametrize("below", [True, False])
+def test_gap_rule_threshold_k1(below):
+    """k = 1: the gap that matters is p_(1) - p_(2); the same token passes
+    with k = 2, whose gap (about 0.1) is far above the threshold."""
+    g = 1e-4 - 2e-6 if below else 1e-4 + 2e-6
+    assert _gap_token(_q_k1(g), 1) is (not below)
+    assert _gap_token(_q_k1(g), 2)
+
+
+def test_gap_rule_other_gaps_do_not_count():
+    """A near-tie away from the k-th / (k+1)-th pair does not reject: q with
+    p_(1) = p_(2) exactly passes at k = 2 (gap p_(2) - p_(3) = 0.1), and
+    fails at k = 1."""
+    q = [0.3, 0.3, 0.2, 0.15, 0.05]
+    assert _gap_token(q, 2)
+    assert not _gap_token(q, 1)
+    assert _gap_token(q, 3)          # p_(3) - p_(4) = 0.05
+
+
+def test_gap_rule_k_equals_E_always_accepts():
+    """k = E has no (k+1)-th expert: every token passes, a uniform one (all
+    gaps zero) included; the same uniform token fails for every k < E."""
+    E = 4
+    q = [0.25] * E
+    assert _gap_token(q, E)
+    for k in range(1, E):
+        assert not _gap_token(q, k)
+
+
+def test_gap_rule_sorts_the_probabilities():
+    """The rule ranks the probabilities, not the expert indices: the k = 2
+    token of the threshold test with its experts listed in reverse order is
+    judged the same way."""
+    for g, ok in ((1e-4 - 2e-6, False), (1e-4 + 2e-6, True)):
+        assert _gap_token(_q_k2(g)[::-1], 2) is ok
+
+
+def test_gap_rule_temperature_moves_the_gap():
+    """Temperature tau = 1/2 squares the unnormalised probabilities: with q
+    of the k = 2 token, the new gap is ((0.25 + g/2)^2 - (0.25 - g/2)^2) /
+    sum q^2 = 0.5 g / (0.26 + g^2 / 2), about 1.92 g.  g = 0.6e-4 fails at
+    tau = 1 and passes at tau = 1/2 (1.15e-4); g = 1.2e-4 passes at tau = 1
+    and fails at tau = 2, where the gap is (sqrt(q2) - sqrt(q3)) / sum sqrt(q),
+    about 0.56e-4."""
+    g = 0.6e-4
+    q = np.array(_q_k2(g))
+    sharp = 0.5 * g / float(np.sum(q ** 2))
+    assert sharp > 1.1e-4
+    assert not _gap_token(q, 2)
+    assert _gap_token(q, 2, temperature=0.5)
+    g = 1.2e-4
+    q = np.array(_q_k2(g))
+    flat = (math.sqrt(q[1]) - math.sqrt(q[2])) / float(np.sum(np.sqrt(q)))
+    assert flat < 0.9e-4
+    assert _gap_token(q, 2)
+    assert not _gap_token(q, 2, temperature=2.0)
+
+
+def test_gap_rule_noise_moves_the_gap():
+    """Noise n added to an expert's score multiplies its unnormalised
+    probability by e^n.  With q of the k = 2 token at g = 0.5e-4 (rejected)
+    and e^n = 1 + delta on the 2nd expert, delta = (2e-4 - g) / ((0.25 +
+    g/2)(1 - 2e-4)), the gap becomes exactly 2e-4 and the token passes.
+    Lifting the 3rd expert instead by 1 + delta3, delta3 = (g + 0.5e-4) /
+    (0.25 - g/2), makes it the 2nd largest, 0.5e-4 above the old 2nd before
+    normalisation (Z = 1 + g + 0.5e-4): still a near-tie, rejected."""
+    g = 0.5e-4
+    q = _q_k2(g)
+    delta = (2e-4 - g) / ((0.25 + g / 2) * (1 - 2e-4))
+    assert not _gap_token(q, 2)
+    assert _gap_token(q, 2, noise=[0.0, math.log1p(delta), 0.0, 0.0, 0.0])
+    delta3 = (g + 0.5e-4) / (0.25 - g / 2)
+    swapped = 0.5e-4 / (1 + g + 0.5e-4)
+    assert 0.4e-4 < swapped < 0.6e-4
+    assert not _gap_token(q, 2, noise=[0.0, 0.0, math.log1p(delta3), 0.0, 0.0])
+    # the same lift on the 4th expert leaves the 2nd / 3rd pair alone
+    assert not _gap_token(q, 2, noise=[0.0, 0.0, 0.0, math.log1p(delta3), 0.0])
+
+
+def test_gap_rule_bias_enters_before_the_softmax():
+    """A router bias is part of the logits: x = 0 with bias ln q gives the
+    same probabilities as x = ln q, so the threshold token is judged the
+    same way through the bias."""
+    for g, ok in ((1e-4 - 2e-6, False), (1e-4 + 2e-6, True)):
+        q = np.array(_q_k2(g))
+        E = q.size
+        x = f32(np.zeros((1, E)))
+        w = f32(np.eye(E))
+        got = bool(oracle.router_gap_ok(x, w, f32(np.log(q)), 2, "f32")[0])
+        assert got is ok
