@@ -151,7 +151,9 @@ const char* moe_status_string(moe_status s);
  *   s[t,e] = logits[t,e] / tau + router_noise[t,e]
  *   p = softmax_e(s), lse[t] = logsumexp_e(s[t,:])
  *   topk_idx[t,:] = the k experts of largest score (= largest p), sorted by
- *                   descending score, lower index first on exact ties
+ *                   descending score, lower index first on exact ties; a
+ *                   NaN score ranks below every number (the k indices stay
+ *                   distinct; a NaN pick gets weight 0)
  *   topk_w[t,j]   = p[t,idx] / sum_j' p[t,idx']
  * tau = cfg->router_temperature ([P2 §5.1]); router_noise [T,E] float32 or
  * NULL: a perturbation the caller draws, added before the top-k ([P2 §2.2]
@@ -178,8 +180,10 @@ moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
  *   (expert, token): expert_offsets[E+1] is the exclusive scan of the kept
  *   counts, perm_token[row] = t, perm_w[row] = topk_w[t,j],
  *   inv_row[t,j] = row or -1 if dropped, *n_dropped = dropped assignments.
- * topk_idx [T,k] int32 with values in [0,E) (checked on device: an invalid
- * index is counted as dropped and reported through n_dropped = -1);
+ * topk_idx [T,k] int32 with values in [0,E) and the k indices of a token
+ * distinct (checked on device: an index out of range, or a repeat of an
+ * expert the token already lists, is counted as dropped and reported through
+ * n_dropped = -1; the outputs are then those of the table without it);
  * topk_w [T,k] float32 (required iff perm_w != NULL); x [T,d] act-dtype
  * (required iff x_perm != NULL); outputs: expert_counts [E],
  * expert_offsets [E+1], perm_token [T*k] (first R entries valid),
@@ -242,8 +246,10 @@ moe_status moe_expert_ffn_int8(const moe_config* cfg, int32_t n_groups, int32_t 
  *   y[t,:] = shared_y[t,:] + sum_{j: inv_row[t,j] >= 0} topk_w[t,j] * y_perm[inv_row[t,j],:]
  *            (+ residual[t,:])
  * summed in float32 in the order shared, j = 0..k-1, residual.
- * y_perm [R,d], shared_y [T,d] or NULL, residual [T,d] or NULL, y [T,d]
- * act-dtype; inv_row [T,k] int32; topk_w [T,k] float32.
+ * y_perm [R,d] (required, also when every slot is dropped), shared_y [T,d]
+ * or NULL, residual [T,d] or NULL, y [T,d] act-dtype; inv_row [T,k] int32;
+ * topk_w [T,k] float32.  INVALID_ARG for a NULL y_perm, inv_row, topk_w or
+ * y, or a misaligned (16-byte) act-dtype pointer.
  */
 moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* inv_row,
                        const float* topk_w, const void* shared_y, const void* residual,

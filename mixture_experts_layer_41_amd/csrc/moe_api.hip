@@ -302,8 +302,8 @@ moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t*
                        void* y, hipStream_t stream) {
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
-  if (!inv_row || !topk_w || !y) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(y) || (y_perm && !aligned16(y_perm)) || (shared_y && !aligned16(shared_y)) ||
+  if (!y_perm || !inv_row || !topk_w || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(y) || !aligned16(y_perm) || (shared_y && !aligned16(shared_y)) ||
       (residual && !aligned16(residual)))
     return MOE_ERR_INVALID_ARG;
   MOE_HIP_TRY(launch_combine(*cfg, y_perm, inv_row, topk_w, shared_y, residual, y, stream));

@@ -38,19 +38,35 @@ constexpr int64_t kSmallTable = 8192;    // nb * E up to this: no colscan launch
 constexpr int kBatch = 16;               // independent loads issued together
 constexpr int kMaxKReg = 8;              // top-k indices of a token kept in registers
 
+// Per-block expert counts of a caller's routing table, with its input check:
+// an index outside [0, E) or an expert listed twice by one token is counted
+// in bad[] (moe_permute then reports n_dropped = -1) and not in the counts,
+// so the ranks of the scatter still cover every counted row.  Each thread
+// owns one token and a bit set of the experts it has listed (LDS words only
+// that thread touches).
 __global__ void __launch_bounds__(64)
 histogram_kernel(const int32_t* __restrict__ idx, int64_t T, int k, int E, int BT,
                  int32_t* __restrict__ cnt, int32_t* __restrict__ bad) {
+  constexpr int kSetWords = kMaxExperts / 32;
   __shared__ int32_t c[kMaxExperts];
+  __shared__ uint32_t seen[64][kSetWords + 1];
   __shared__ int32_t nbad;
   for (int e = threadIdx.x; e < E; e += 64) c[e] = 0;
   if (threadIdx.x == 0) nbad = 0;
+  uint32_t* mine = seen[threadIdx.x];
+  for (int w = 0; w < kSetWords; ++w) mine[w] = 0u;
   __syncthreads();
   const int64_t t = (int64_t)blockIdx.x * BT + threadIdx.x;
   if (threadIdx.x < BT && t < T) {
     for (int j = 0; j < k; ++j) {
       const int e = idx[t * k + j];
-      if (e >= 0 && e < E)
+      bool ok = e >= 0 && e < E;
+      if (ok) {
+        const uint32_t bit = 1u << (e & 31);
+        ok = (mine[e >> 5] & bit) == 0u;
+        mine[e >> 5] |= bit;
+      }
+      if (ok)
         atomicAdd(&c[e], 1);
       else
         atomicAdd(&nbad, 1);

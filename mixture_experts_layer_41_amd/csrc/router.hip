@@ -162,12 +162,15 @@ __device__ void logits_f32(const float* __restrict__ x, const float* __restrict_
 }
 
 // Order key of a logit: a larger logit has a larger key and -0 and +0 share
-// one; NaN gets 0, below every number (-inf has 0x007FFFFF).  No number has
-// key 0, so 0 also marks an expert that is absent or already picked.
+// one; NaN gets kNanKey = 1, below every number (-inf has 0x007FFFFF), so a
+// NaN score is still picked (last, lower index first, with weight 0) and the
+// k picks of a token stay distinct.  0 marks an expert that is absent or
+// already picked.
+constexpr uint32_t kNanKey = 1u;
 __device__ inline uint32_t order_key(float l) {
   const uint32_t u = l == 0.f ? 0u : __float_as_uint(l);
   const uint32_t key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return l != l ? 0u : key;
+  return l != l ? kNanKey : key;
 }
 __device__ inline float key_logit(uint32_t key) {
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
@@ -274,10 +277,10 @@ __device__ void select_and_stats_t(float* lg, int ep, int BT, int nvalid, int E,
     const bool mine = be == my_e && bi >= 0;
 #pragma unroll
     for (int i = 0; i < NPL; ++i) key[i] = (mine && i == bi) ? 0u : key[i];
-    // no number left (NaN logits, k above the count of numbers): keep the
-    // index in range, weight 0
+    // every expert holds a key (a number or kNanKey), so k <= E picks always
+    // find one; the guard only keeps the index in range
     if (be == kNone) be = j % E;
-    const float ex = bk != 0u ? expf(key_logit(bk) - m) : 0.f;
+    const float ex = bk > kNanKey ? expf(key_logit(bk) - m) : 0.f;
     wsum += ex;
     if (valid && sub == 0) {
       topk_idx[tok * k + j] = be;
@@ -289,7 +292,7 @@ __device__ void select_and_stats_t(float* lg, int ep, int BT, int nvalid, int E,
       if (q == j) exv[q] = ex;
   }
   if (valid && sub == 0) {
-    const float inv = 1.f / wsum;
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;  // only NaN picks: weights 0
 #pragma unroll
     for (int q = 0; q < kRegPicks; ++q)
       if (q < k) topk_w[tok * k + q] = exv[q] * inv;

@@ -173,6 +173,9 @@ def test_misaligned_pointers(L):
     assert L.moe_route(ctypes.byref(c), P, P, None, None, None, P, None, P, ctypes.byref(n), None) == INVALID
     assert L.moe_combine(ctypes.byref(c), P, P, P, None, None, P + 4, None) == INVALID
     assert L.moe_combine(ctypes.byref(c), P, None, P, None, None, P, None) == INVALID
+    # expert rows are required even when every slot could be dropped
+    assert L.moe_combine(ctypes.byref(c), None, P, P, None, None, P, None) == INVALID
+    assert L.moe_combine(ctypes.byref(c), P + 8, P, P, None, None, P, None) == INVALID
 
 
 def test_expert_ffn_argument_checks(L):
