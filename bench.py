@@ -2,15 +2,28 @@
 
 One step = one moe_forward call (router, permutation, routed and shared
 expert FFNs, combine, aux statistics) over one batch of synthetic tokens
-already resident in HBM.  Workload: the small "Flash" layer (T = 4096 tokens
-as 2 x 2048, d_model 512, 16 experts, top-2, SwiGLU d_ffn 1024, capacity
-factor 1.25), bf16 with float32 accumulation.
+already resident in HBM, bf16 with float32 accumulation.
 
-Prints ONE JSON line (rank 0).  Extra legs:
-  roofline      the grouped expert GEMMs (moe_expert_ffn on the routed rows:
-                gate/up GEMM + down GEMM) timed with HIP events on the stream
-                they run on, against the bf16 dense MFMA peak;
-  cpu_baseline  the float64 CPU oracle on the same inputs, timed on the host.
+Headline workload (default): the skewed-routing layer, the largest named
+layer that fits one GPU: T = 65536 tokens, d_model 2048, 64 routed experts
+top-6 plus 2 shared experts, SwiGLU d_ffn 1408, Zipf-like router bias
+b_i = 2 ln(1/(i+1)), no capacity limit.  The other named layers are timed as
+extra legs of the same run (Flash T = 4096, FLAME-shaped T = 16384, decode
+T = 128 with 22.5 GB of expert weights).
+
+Prints ONE JSON line (rank 0).  Per leg:
+  roofline      the grouped expert GEMMs (routed experts: gate/up GEMM with
+                the SwiGLU epilogue + down GEMM; shared experts: the same
+                pair over all tokens) timed with HIP events on the stream
+                they run on, against the bf16 dense MFMA peak, or, for the
+                weight-streaming decode layer, against the HBM peak;
+  flush         the forward timed once per iteration with a 512 MB device
+                write between iterations (cold L2 / Infinity Cache);
+  backward      moe_forward_train + moe_backward (headline and Flash legs).
+Headline only:
+  cpu_baseline  the float64 CPU oracle on a bounded token sample of the
+                headline workload, timed on the host;
+  clock         the GPU clock amd-smi reports while the GEMM leg runs.
 """
 
 from __future__ import annotations
@@ -20,7 +33,10 @@ import dataclasses
 import hashlib
 import json
 import os
+import platform
+import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -28,12 +44,14 @@ sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
-WORKLOAD = "c2"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_gemm_flash_T4096_traffic.json")
+HEADLINE = "c4"
+EXTRA_LEGS = "c2,c3,c5"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_gemm_traffic.json")
 # sources of the grouped GEMM kernels: the committed counter figures hold only
 # while these are unchanged
 GEMM_SRCS = [os.path.join(ROOT, "mixture_experts_layer_41_amd", "csrc", n)
              for n in ("gemm.hip", "gemm_mfma.hip", "gemm_pipe.hip", "gemm_common.h")]
+FLUSH_BYTES = 512 << 20
 
 
 def log(*a):
@@ -43,15 +61,20 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=WORKLOAD, help="named layer config (default: c2)")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE, help="headline layer config (default: c4)")
+    ap.add_argument("--legs", default=EXTRA_LEGS,
+                    help="comma-separated extra layer configs, or 'none' (default: c2,c3,c5)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--no-backward", action="store_true", help="skip the training (backward) leg")
+    ap.add_argument("--cpu-tokens", type=int, default=2048,
+                    help="tokens of the headline batch the CPU oracle leg runs on")
+    ap.add_argument("--no-backward", action="store_true", help="skip the training (backward) legs")
+    ap.add_argument("--no-flush", action="store_true", help="skip the cold-cache variant")
     ap.add_argument("--top-k", type=int, default=None,
-                    help="override the workload's k (e.g. top-1 against top-2 inference)")
+                    help="override the headline workload's k (e.g. top-1 against top-2 inference)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling HBM byte counters)")
     return ap.parse_args()
@@ -84,81 +107,136 @@ def copy_calibration(n_bytes=1 << 30, reps=5):
 
 
 def traffic_entry(workload):
-    """HBM traffic of the grouped GEMMs from the committed counter runs, if
-    they were taken on this workload and the current kernel source; else None."""
+    """HBM bytes of one grouped-GEMM launch (routed + shared) from the
+    committed counter runs, if they were taken on this workload and the
+    current kernel sources; else None."""
     try:
         with open(TRAFFIC_FILE) as fh:
             rec = json.load(fh)
-        if rec.get("kernel_sha256_16") != gemm_source_hash() or rec.get("workload") != workload:
+        if rec.get("kernel_sha256_16") != gemm_source_hash():
             return None
-        return rec["bytes_per_launch"]
-    except (OSError, KeyError, ValueError):
+        return rec["bytes_per_launch"].get(workload)
+    except (OSError, KeyError, ValueError, AttributeError):
         return None
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (the layer runs on a single MI355X); "
-              f"--gpus {args.gpus} is not supported", file=sys.stderr)
-        sys.exit(2)
-    if args.copy_calibration:
-        copy_calibration()
-        return
+def cpu_info():
+    model = platform.processor() or None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas, threads = None, None
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                blas = f"{i.get('internal_api')} {i.get('version')} ({i.get('threading_layer', '?')})"
+                threads = i.get("num_threads")
+                break
+    except Exception:
+        pass
+    if threads is None:
+        threads = len(os.sched_getaffinity(0))
+    return model, blas, int(threads)
 
+
+def gpu_clock_sample():
+    """One reading of amd-smi's clock metrics for GPU 0 (raw JSON trimmed to
+    the graphics clock entries), or an error string."""
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"], capture_output=True,
+                           text=True, timeout=20)
+        if r.returncode != 0:
+            return {"error": (r.stderr or r.stdout).strip()[-200:]}
+        data = json.loads(r.stdout)
+    except Exception as e:  # amd-smi missing or unparsable: report, never fail
+        return {"error": str(e)[-200:]}
+
+    found = {}
+
+    def walk(o, path):
+        if isinstance(o, dict):
+            for k2, v in o.items():
+                walk(v, path + [str(k2)])
+        elif isinstance(o, list):
+            for i, v in enumerate(o):
+                walk(v, path + [str(i)])
+        else:
+            key = "/".join(path).lower()
+            if "gfx" in key and ("clk" in key or "clock" in key):
+                found["/".join(path)] = o
+
+    walk(data, [])
+    return found or {"raw": json.dumps(data)[:600]}
+
+
+# ---------------------------------------------------------------------------
+
+
+def dev_tensor(a):
     import numpy as np
     import torch
+    from moe_inputs import Bank
+    if a is None:
+        return None
+    if isinstance(a, Bank):
+        from concurrent.futures import ThreadPoolExecutor
+        tdt = {np.uint16: torch.bfloat16, np.int8: torch.int8}.get(a.np_dtype, torch.float32)
+        out = torch.empty(a.full_shape, dtype=tdt, device="cuda")
+        with ThreadPoolExecutor(max_workers=16) as ex:
+            for e, arr in ex.map(lambda e: (e, a[e]), range(a.n)):
+                out[e].copy_(dev_tensor(arr))
+        return out
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.int8:          # 8-bit weight codes
+        return torch.from_numpy(a).cuda()
+    if a.dtype == np.uint16:        # bf16 bit patterns
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
 
-    from moe_inputs import Bank, get_config, make_inputs
+
+def layer_weights(t):
+    import torch
+    from mixture_experts_layer_41_amd import binding as B
+    rb = t["router_bias"]
+    return B.LayerWeights(
+        w_router=dev_tensor(t["w_router"]), w1=dev_tensor(t["w1"]), w2=dev_tensor(t["w2"]),
+        b1=dev_tensor(t["b1"]), b2=dev_tensor(t["b2"]), shared_w1=dev_tensor(t["ws1"]),
+        shared_w2=dev_tensor(t["ws2"]), shared_b1=dev_tensor(t["sb1"]),
+        shared_b2=dev_tensor(t["sb2"]), w1_scale=dev_tensor(t.get("w1_scale")),
+        w2_scale=dev_tensor(t.get("w2_scale")), shared_w1_scale=dev_tensor(t.get("ws1_scale")),
+        shared_w2_scale=dev_tensor(t.get("ws2_scale")),
+        router_bias=None if rb is None else torch.from_numpy(rb).cuda())
+
+
+def run_leg(cfg, args, headline, want_backward, want_host_inputs):
+    """Times one layer config; returns (leg dict, host inputs or None,
+    device handles for the parity check)."""
+    import torch
+    from moe_inputs import make_inputs
     from mixture_experts_layer_41_amd import binding as B
 
-    torch.cuda.set_device(0)
-    cfg = get_config(args.workload)
-    if args.top_k is not None:
-        cfg = dataclasses.replace(cfg, k=args.top_k, name=f"{cfg.name}_top{args.top_k}")
-    log(f"[bench] workload {cfg.name}")
+    stream = torch.cuda.current_stream()
+    q8 = cfg.weights == "int8"
+    log(f"[bench] leg {cfg.name}: generating inputs")
+    t0 = time.perf_counter()
     # raw seeded draws (no tie rejection: timing only); expert weight stacks
     # stay lazy (generated one expert at a time) unless the CPU leg needs them
-    big = cfg.E * cfg.w1_rows * cfg.d * 3 > (1 << 31)
-    t = make_inputs(cfg, materialize=not (args.no_cpu or big))
-    if big and not args.no_cpu:
-        log(f"[bench] {cfg.name}: weights too large for the CPU oracle leg; skipping it")
-        args.no_cpu = True
-
-    def dev(a):
-        if a is None:
-            return None
-        if isinstance(a, Bank):
-            from concurrent.futures import ThreadPoolExecutor
-            tdt = {np.uint16: torch.bfloat16, np.int8: torch.int8}.get(a.np_dtype, torch.float32)
-            out = torch.empty(a.full_shape, dtype=tdt, device="cuda")
-            with ThreadPoolExecutor(max_workers=16) as ex:
-                for e, arr in ex.map(lambda e: (e, a[e]), range(a.n)):
-                    out[e].copy_(dev(arr))
-            return out
-        a = np.ascontiguousarray(a)
-        if a.dtype == np.int8:          # 8-bit weight codes
-            return torch.from_numpy(a).cuda()
-        if a.dtype == np.uint16:        # bf16 bit patterns
-            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
-        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
-
-    rb = t["router_bias"]
-    W = B.LayerWeights(
-        w_router=dev(t["w_router"]), w1=dev(t["w1"]), w2=dev(t["w2"]), b1=dev(t["b1"]),
-        b2=dev(t["b2"]), shared_w1=dev(t["ws1"]), shared_w2=dev(t["ws2"]),
-        shared_b1=dev(t["sb1"]), shared_b2=dev(t["sb2"]),
-        w1_scale=dev(t.get("w1_scale")), w2_scale=dev(t.get("w2_scale")),
-        shared_w1_scale=dev(t.get("ws1_scale")), shared_w2_scale=dev(t.get("ws2_scale")),
-        router_bias=None if rb is None else torch.from_numpy(rb).cuda())
-    q8 = cfg.weights == "int8"
-    x = dev(t["x"])
-    noise = dev(t.get("router_noise"))   # [T, E] float32 or None
+    t = make_inputs(cfg, materialize=want_host_inputs)
+    W = layer_weights(t)
+    x = dev_tensor(t["x"])
+    noise = dev_tensor(t.get("router_noise"))
+    torch.cuda.synchronize()
+    log(f"[bench] leg {cfg.name}: inputs on the GPU in {time.perf_counter() - t0:.1f} s")
     c = B.config_of(cfg)
     fwd = B.Forward(c, W)
-    stream = torch.cuda.current_stream()
 
-    # ---- eager warm-up and (optionally) a captured graph of one step
+    # ---- eager warm-up, then eager and (optionally) graph timing
     for _ in range(max(args.warmup, 1)):
         fwd(x, noise)
     torch.cuda.synchronize()
@@ -175,108 +253,154 @@ def main():
             graph = g
         except Exception as e:  # capture not possible: time eager launches
             log(f"[bench] graph capture failed ({e}); timing eager launches")
-            graph = None
 
     def timed(step_fn, steps):
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
+        s0 = time.perf_counter()
         for _ in range(steps):
             step_fn()
         torch.cuda.synchronize()
-        return time.perf_counter() - t0
+        return time.perf_counter() - s0
 
     eager_s = timed(lambda: fwd(x, noise), args.steps)
     graph_s = timed(graph.replay, args.steps) if graph is not None else None
     best_s = min(s for s in (eager_s, graph_s) if s is not None)
     mode = "hip_graph" if (graph_s is not None and graph_s <= eager_s) else "eager"
-    log(f"[bench] eager {eager_s / args.steps * 1e6:.1f} us/step"
+    del graph
+    step_us = best_s / args.steps * 1e6
+    log(f"[bench] leg {cfg.name}: eager {eager_s / args.steps * 1e6:.1f} us/step"
         + (f", graph {graph_s / args.steps * 1e6:.1f} us/step" if graph_s else ""))
 
     # ---- routing statistics of this batch (for the algorithmic work counts)
     torch.cuda.synchronize()
     aux = B.aux_to_dict(fwd.aux)
     R = int(aux["n_kept"])
-    T, d, f, S, k = cfg.T, cfg.d, cfg.f, cfg.S, cfg.k
+    T, d, f, S, k, E = cfg.T, cfg.d, cfg.f, cfg.S, cfg.k, cfg.E
     per_row = (6 if cfg.act == "swiglu" else 4) * d * f        # flops per kept row (one expert)
     routed_flops = R * per_row
     shared_flops = T * S * per_row
-    router_flops = 2 * T * d * cfg.E
+    router_flops = 2 * T * d * E
     layer_flops = routed_flops + shared_flops + router_flops
 
-    # ---- roofline leg: the routed grouped GEMMs alone, HIP events on this stream
+    # ---- cold-cache variant: a 512 MB write between iterations, each
+    # forward bracketed by its own events
+    flush = None
+    if not args.no_flush:
+        junk = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        n_fl = max(5, min(args.steps, 20))
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n_fl)]
+        torch.cuda.synchronize()
+        for a, b in evs:
+            junk.fill_(1)
+            a.record(stream)
+            fwd(x, noise)
+            b.record(stream)
+        torch.cuda.synchronize()
+        fl_us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+        flush = {"us_per_step_median": round(fl_us[len(fl_us) // 2], 2),
+                 "tokens_per_s": round(T / (fl_us[len(fl_us) // 2] / 1e6), 1),
+                 "iterations": n_fl, "flush_bytes": FLUSH_BYTES}
+        del junk
+
+    # ---- roofline leg: the grouped expert GEMMs alone (routed + shared),
+    # HIP events on this stream
     pr = B.moe_permute(c, fwd.topk_idx)
     torch.cuda.synchronize()
-    y_perm = torch.empty(T * k, d, dtype=B.torch_dtype(c), device="cuda")
+    calls = []
     if q8:
-        ffn_call = B.moe_expert_ffn_int8
-        ffn_args = (c, cfg.E, 1, T * k, x, pr["perm_token"], pr["expert_offsets"], W.w1,
-                    W.w1_scale, W.b1, W.w2, W.w2_scale, W.b2, y_perm)
+        calls.append(B.ExpertFFN(c, E, 1, T * k, x, pr["perm_token"], pr["expert_offsets"], W.w1,
+                                 W.b1, W.w2, W.b2, w1_scale=W.w1_scale, w2_scale=W.w2_scale))
+        if S:
+            calls.append(B.ExpertFFN(c, 1, S, T, x, None, None, W.shared_w1, W.shared_b1,
+                                     W.shared_w2, W.shared_b2, w1_scale=W.shared_w1_scale,
+                                     w2_scale=W.shared_w2_scale))
     else:
-        ffn_call = B.moe_expert_ffn
-        ffn_args = (c, cfg.E, 1, T * k, x, pr["perm_token"], pr["expert_offsets"], W.w1, W.b1,
-                    W.w2, W.b2, y_perm)
-    for _ in range(10):
-        ffn_call(*ffn_args)
-    n_ffn = max(50, args.steps // 2)
+        calls.append(B.ExpertFFN(c, E, 1, T * k, x, pr["perm_token"], pr["expert_offsets"], W.w1,
+                                 W.b1, W.w2, W.b2))
+        if S:
+            calls.append(B.ExpertFFN(c, 1, S, T, x, None, None, W.shared_w1, W.shared_b1,
+                                     W.shared_w2, W.shared_b2))
+
+    def ffn_all():
+        for cl in calls:
+            cl()
+
+    for _ in range(5):
+        ffn_all()
+    n_ffn = max(20, args.steps)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record(stream)
     for _ in range(n_ffn):
-        ffn_call(*ffn_args)
+        ffn_all()
     ev1.record(stream)
     ev1.synchronize()
     ffn_s = ev0.elapsed_time(ev1) / 1e3 / n_ffn
-    gemm_tflops = routed_flops / ffn_s / 1e12
-    # algorithmic bytes of the same call: the weights of every expert that
-    # keeps a row (W1 [w1_rows, d] and W2 [d, f]; with 8-bit weights one byte
-    # per code plus a float32 scale per row), the gathered input rows, H
-    # written and read back, the output rows
-    counts = pr["expert_offsets"].cpu().numpy()
-    touched = int((counts[1:] - counts[:-1] > 0).sum())
+    gemm_flops = routed_flops + shared_flops
+    gemm_tflops = gemm_flops / ffn_s / 1e12
+
+    # sustained clock while the GEMMs run (headline only): enqueue about two
+    # seconds of GEMM launches, read amd-smi from the host meanwhile
+    clock = None
+    if headline:
+        n_busy = max(1, int(2.0 / max(ffn_s, 1e-6)))
+        box = {}
+        th = threading.Thread(target=lambda: (time.sleep(0.8), box.setdefault("c", gpu_clock_sample())))
+        for _ in range(min(n_busy, 4000)):
+            ffn_all()
+        th.start()
+        th.join()
+        torch.cuda.synchronize()
+        clock = box.get("c")
+
+    # algorithmic bytes of the same launches: the weights of every expert
+    # that keeps a row (W1 [w1_rows, d] and W2 [d, f]; with 8-bit weights one
+    # byte per code plus a float32 scale per row), the shared experts'
+    # weights, the input rows read, H written and read back, the output rows
+    offs = pr["expert_offsets"].cpu().numpy()
+    touched = int((offs[1:] - offs[:-1] > 0).sum())
     ab = 2 if cfg.dtype == "bf16" else 4
+    n_w = touched + S
     if q8:
-        weight_bytes = touched * ((cfg.w1_rows + f) * d + 4 * (cfg.w1_rows + d))
+        weight_bytes = n_w * ((cfg.w1_rows + f) * d + 4 * (cfg.w1_rows + d))
     else:
-        weight_bytes = ab * touched * (cfg.w1_rows + f) * d
-    routed_bytes = weight_bytes + ab * (R * d + 2 * R * f + R * d)
-    # MFMA-bound unless the weights alone give fewer flops per byte than the
-    # MFMA / HBM ridge (the weight-streaming decode shape)
-    if routed_flops / weight_bytes >= MFMA_BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3:
+        weight_bytes = ab * n_w * (cfg.w1_rows + f) * d
+    act_rows = R + T * S if S else R
+    gemm_bytes = weight_bytes + ab * (R * d + (T * d if S else 0) + 2 * act_rows * f + act_rows * d)
+    ridge = MFMA_BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3          # flop per byte
+    common = {"launch_us": round(ffn_s * 1e6, 2), "flops_per_launch": gemm_flops,
+              "bytes_per_launch": gemm_bytes, "touched_experts": touched,
+              "traffic": traffic_entry(cfg.name)}
+    if gemm_flops / weight_bytes >= ridge:
         roofline = {
-            "kernel": "grouped expert GEMMs (gate/up + activation epilogue, down) over the routed rows",
+            "kernel": "grouped expert GEMMs: routed (gate/up + SwiGLU epilogue, down) and "
+                      "shared (the same pair over all tokens)",
             "bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(gemm_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": traffic_entry(cfg.name), "launch_us": round(ffn_s * 1e6, 2),
-            "flops_per_launch": routed_flops, "bytes_per_launch": routed_bytes,
-        }
+            "unit": "TFLOP/s", "frac": round(gemm_tflops / MFMA_BF16_PEAK_TFLOPS, 4), **common}
     else:   # weight streaming: fewer flops per byte than the MFMA/HBM ridge
-        gbs = routed_bytes / ffn_s / 1e9
+        gbs = gemm_bytes / ffn_s / 1e9
         roofline = {
-            "kernel": "grouped expert GEMMs streaming the weights of the touched experts",
+            "kernel": "grouped expert GEMMs streaming the weights of the touched and shared experts",
             "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_entry(cfg.name),
-            "launch_us": round(ffn_s * 1e6, 2), "bytes_per_launch": routed_bytes,
-            "flops_per_launch": routed_flops, "touched_experts": touched,
-        }
-    log(f"[bench] grouped GEMMs {ffn_s * 1e6:.1f} us -> {gemm_tflops:.1f} TFLOP/s, "
-        f"{routed_bytes / ffn_s / 1e9:.0f} GB/s")
+            "frac": round(gbs / HBM_PEAK_GBS, 4), **common}
+    log(f"[bench] leg {cfg.name}: grouped GEMMs {ffn_s * 1e6:.1f} us -> {gemm_tflops:.1f} TFLOP/s, "
+        f"{gemm_bytes / ffn_s / 1e9:.0f} GB/s")
+    del calls
 
     # ---- training leg: moe_forward_train + moe_backward on the same batch
-    # (bf16 activations with bf16 expert weights), HIP events on this stream
     backward = None
-    if not args.no_backward and cfg.dtype == "bf16" and not q8:
+    if want_backward and cfg.dtype == "bf16" and not q8:
         tr = B.TrainStep(c, W)
-        g_dy = torch.randn(T, d, device="cuda", generator=torch.Generator(device="cuda").manual_seed(5))
-        g_dy = g_dy.to(torch.bfloat16)
-        for _ in range(5):
+        gen = torch.Generator(device="cuda").manual_seed(5)
+        g_dy = torch.randn(T, d, device="cuda", generator=gen).to(torch.bfloat16)
+        for _ in range(3):
             tr.forward(x, noise)
             tr.backward(g_dy)
-        n_tr = max(20, args.steps // 4)
+        n_tr = max(10, args.steps)
         e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
 
         def loop_ms(fn):
-            """n_tr back-to-back calls (steady state, as the inference leg),
-            bracketed by events on the stream."""
             torch.cuda.synchronize()
             e0.record(stream)
             for _ in range(n_tr):
@@ -286,14 +410,11 @@ def main():
             return e0.elapsed_time(e1)
 
         f_ms = loop_ms(lambda: tr.forward(x, noise))
-        # the backward repeated on the last forward's saved state
         b_ms = loop_ms(lambda: tr.backward(g_dy))
         s_ms = loop_ms(lambda: (tr.forward(x, noise), tr.backward(g_dy)))
         bwd_s = b_ms / 1e3 / n_tr
-        # algorithmic backward flops: twice the forward's expert products
-        # (d input and d weight of each), routed and shared, plus the router's
         w1r = 2 * f if cfg.act == "swiglu" else f
-        bflops = 2 * (R + T * S) * (2 * d * w1r + 2 * d * f) + 2 * 2 * T * d * cfg.E
+        bflops = 2 * (R + T * S) * (2 * d * w1r + 2 * d * f) + 2 * 2 * T * d * E
         bt = bflops / bwd_s / 1e12
         backward = {
             "what": "moe_backward (all gradients) after moe_forward_train, same batch; "
@@ -305,63 +426,131 @@ def main():
             "flops_per_step": bflops, "achieved_tflops": round(bt, 2),
             "frac_of_mfma_peak": round(bt / MFMA_BF16_PEAK_TFLOPS, 4),
         }
-        log(f"[bench] training step: forward {f_ms / n_tr * 1e3:.1f} us + backward "
+        log(f"[bench] leg {cfg.name}: training forward {f_ms / n_tr * 1e3:.1f} us + backward "
             f"{bwd_s * 1e6:.1f} us ({bt:.0f} TFLOP/s algorithmic); whole step "
             f"{s_ms / n_tr * 1e3:.1f} us")
+        del tr
 
-    # ---- CPU oracle leg (rank 0, N = 1 only)
-    cpu = None
+    leg = {
+        "workload": cfg.name, "tokens": T, "d_model": d, "experts": E, "top_k": k, "d_ffn": f,
+        "shared_experts": S, "capacity_factor": cfg.capacity_factor,
+        "router_temperature": cfg.router_temperature, "router_noise_std": cfg.router_noise_std,
+        "expert_weights": "int8 codes + f32 row scales" if q8 else
+        ("bf16" if cfg.dtype == "bf16" else "f32"),
+        "us_per_step": round(step_us, 2), "tokens_per_s": round(T / (step_us / 1e6), 1),
+        "launch": mode, "eager_us_per_step": round(eager_s / args.steps * 1e6, 2),
+        "graph_us_per_step": None if graph_s is None else round(graph_s / args.steps * 1e6, 2),
+        "layer_tflops": round(layer_flops / (step_us / 1e6) / 1e12, 2),
+        "kept_rows": R, "dropped": int(aux["n_dropped"]),
+        "roofline": roofline, "flush": flush, "backward": backward,
+    }
+    handles = {"fwd": fwd, "x": x, "noise": noise, "W": W}
+    return leg, t if want_host_inputs else None, handles, clock
+
+
+def cpu_baseline_leg(cfg, t, handles, args):
+    """The oracle (float64 numpy, as it stands) on the first n tokens of the
+    headline batch, as one batch of its own; and the GPU output of the same
+    tokens against it (per-token results do not depend on the batch without a
+    capacity limit)."""
+    import numpy as np
+    import torch
+    import oracle
+
+    n = min(args.cpu_tokens, cfg.T)
+    cs = dataclasses.replace(cfg, T=n)
+    ts = dict(t)
+    ts["x"] = t["x"][:n]
+    if t.get("router_noise") is not None:
+        ts["router_noise"] = t["router_noise"][:n]
+    model, blas, threads = cpu_info()
+    runs, t_cpu, ref = 0, 0.0, None
+    while t_cpu < args.cpu_seconds or runs == 0:
+        s0 = time.perf_counter()
+        ref = oracle.forward(cs, ts)
+        t_cpu += time.perf_counter() - s0
+        runs += 1
+    cpu = {"value": round(n * runs / t_cpu, 1), "unit": "tokens/s", "cores": threads,
+           "kind": "oracle",
+           "sample": f"the first {n} of the {cfg.T} tokens of this workload as one batch "
+                     f"(routing, permutation, routed and shared expert FFNs, combine, aux), "
+                     f"{runs} run(s) in {t_cpu:.1f} s, float64 numpy",
+           "cpu_model": model, "blas": blas}
+    log(f"[bench] oracle {t_cpu / runs:.2f} s per {n}-token batch on {threads} threads ({model}; {blas})")
     parity = None
-    if not args.no_cpu:
-        import oracle
-        try:
-            from threadpoolctl import threadpool_info
-            cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-        except Exception:
-            cores = os.cpu_count()
-        runs, t_cpu = 0, 0.0
-        ref = None
-        while t_cpu < args.cpu_seconds or runs == 0:
-            t0 = time.perf_counter()
-            ref = oracle.forward(cfg, t)
-            t_cpu += time.perf_counter() - t0
-            runs += 1
-        cpu = {"value": round(T * runs / t_cpu, 1), "unit": "tokens/s", "cores": int(cores),
-               "kind": "oracle",
-               "sample": f"full layer forward of this workload ({T} tokens), {runs} run(s), "
-                         f"{t_cpu:.1f} s, float64 numpy"}
-        y = fwd(x, noise)
+    if not (cfg.capacity_factor > 0 and n < cfg.T):
+        fwd = handles["fwd"]
+        y = fwd(handles["x"], handles["noise"])
         torch.cuda.synchronize()
-        yg = y.float().cpu().numpy().astype(np.float64)
+        yg = y[:n].float().cpu().numpy().astype(np.float64)
         err = float(np.max(np.abs(yg - ref["y"])) / np.max(np.abs(ref["y"])))
-        idx_mismatch = int((fwd.topk_idx.cpu().numpy() != ref["topk_idx"]).any(1).sum())
-        parity = {"y_normwise_err": err, "tokens_with_other_topk": idx_mismatch,
-                  "lb_rel_err": abs(aux["load_balance"] - ref["lb"]) / abs(ref["lb"])}
-        log(f"[bench] oracle {t_cpu / runs:.2f} s/forward on {cores} threads; parity {parity}")
+        other = int((fwd.topk_idx[:n].cpu().numpy() != ref["topk_idx"]).any(1).sum())
+        parity = {"tokens_compared": n, "y_normwise_err": err, "tokens_with_other_topk": other,
+                  "note": "raw draws without the tie-gap rule: a token with a near-tie may pick "
+                          "another expert"}
+        log(f"[bench] parity on {n} tokens: {parity}")
+    return cpu, parity
 
-    value = T * args.steps / best_s
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the layer runs on a single MI355X); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import torch
+    from moe_inputs import get_config
+
+    torch.cuda.set_device(0)
+    cfg = get_config(args.workload)
+    if args.top_k is not None:
+        cfg = dataclasses.replace(cfg, k=args.top_k, name=f"{cfg.name}_top{args.top_k}")
+    extra = [] if args.legs.strip().lower() in ("", "none") else \
+        [w.strip() for w in args.legs.split(",") if w.strip() and w.strip() != args.workload]
+
+    # ---- headline
+    want_cpu = not args.no_cpu
+    big = cfg.E * cfg.w1_rows * cfg.d * 3 > (1 << 32)
+    if want_cpu and big:
+        log(f"[bench] {cfg.name}: weights too large for the CPU oracle leg; skipping it")
+        want_cpu = False
+    head, t, handles, clock = run_leg(cfg, args, True, not args.no_backward, want_cpu)
+    cpu = parity = None
+    if want_cpu:
+        cpu, parity = cpu_baseline_leg(cfg, t, handles, args)
+    del t, handles
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    # ---- extra legs (other named layers), each freed before the next
+    legs = {}
+    for name in extra:
+        lc = get_config(name)
+        leg, _, h, _ = run_leg(lc, args, False, not args.no_backward and name == "c2", False)
+        legs[name] = leg
+        del h
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
     out = {
         "metric": "MoE-layer fwd tokens/s + grouped-GEMM % MFMA peak (1 MI355X)",
-        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(best_s / args.steps * 1e3, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16"
-        if cfg.dtype == "bf16" else "f32",
-        "data": "synthetic",
-        "config": {"workload": cfg.name, "tokens": T, "d_model": d, "experts": cfg.E,
-                   "top_k": k, "d_ffn": f, "shared_experts": S,
-                   "capacity_factor": cfg.capacity_factor,
-                   "router_temperature": cfg.router_temperature,
-                   "router_noise_std": cfg.router_noise_std, "expert_weights": "int8 codes + "
-                   "f32 row scales" if q8 else ("bf16" if cfg.dtype == "bf16" else "f32"),
-                   "launch": mode,
-                   "eager_us_per_step": round(eager_s / args.steps * 1e6, 2),
-                   "graph_us_per_step": None if graph_s is None else round(graph_s / args.steps * 1e6, 2),
-                   "layer_tflops": round(layer_flops / (best_s / args.steps) / 1e12, 2),
-                   "kept_rows": R, "dropped": int(aux["n_dropped"])},
-        "roofline": roofline,
-        "backward": backward,
+        "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(head["us_per_step"] / 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded draws of the layer's shapes and distributions)",
+        "config": {k2: v for k2, v in head.items() if k2 not in ("roofline", "flush", "backward")},
+        "roofline": head["roofline"],
+        "flush": head["flush"],
+        "backward": head["backward"],
         "cpu_baseline": cpu,
         "parity": parity,
+        "clock": clock,
+        "legs": legs,
     }
     print(json.dumps(out), flush=True)
 

@@ -150,6 +150,40 @@ def moe_expert_ffn_int8(cfg: MoeConfig, n_groups, n_seg, rows_max, a, a_rows, gr
     return out
 
 
+class ExpertFFN:
+    """A prepared moe_expert_ffn (or, with w1_scale / w2_scale, INT8
+    moe_expert_ffn_int8) call: workspace and output allocated once, so
+    repeated calls allocate nothing and cost one library call each."""
+
+    def __init__(self, cfg: MoeConfig, n_groups, n_seg, rows_max, a, a_rows, group_offsets, w1, b1,
+                 w2, b2, out=None, w1_scale=None, w2_scale=None):
+        self.cfg = cfg
+        self.q8 = w1_scale is not None
+        self.out = out if out is not None else torch.empty(
+            max(int(rows_max), 1), cfg.d_model, dtype=torch_dtype(cfg), device=_dev())
+        self._keep = (a, a_rows, group_offsets, w1, b1, w2, b2, w1_scale, w2_scale)
+        if self.q8:
+            self._head = (int(n_groups), int(n_seg), int(rows_max), _p(a), _p(a_rows),
+                          _p(group_offsets), _p(w1), _p(w1_scale), _p(b1), _p(w2), _p(w2_scale),
+                          _p(b2), _p(self.out))
+            self._fn = lib().moe_expert_ffn_int8
+        else:
+            self._head = (int(n_groups), int(n_seg), int(rows_max), _p(a), _p(a_rows),
+                          _p(group_offsets), _p(w1), _p(b1), _p(w2), _p(b2), _p(self.out))
+            self._fn = lib().moe_expert_ffn
+        n = ctypes.c_size_t(0)
+        check(self._fn.__name__, self._fn(ctypes.byref(cfg), *self._head, None, ctypes.byref(n), None))
+        self.ws = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=_dev())
+        self._n = ctypes.c_size_t(self.ws.numel())
+        self._ws = _p(self.ws)
+
+    def __call__(self):
+        self._n.value = self.ws.numel()
+        check(self._fn.__name__, self._fn(ctypes.byref(self.cfg), *self._head, self._ws,
+                                          ctypes.byref(self._n), _stream()))
+        return self.out
+
+
 def moe_combine(cfg: MoeConfig, y_perm, inv_row, topk_w, shared_y=None, residual=None, y=None):
     L = lib()
     if y is None:
