@@ -146,33 +146,24 @@ def cpu_info():
 
 
 def gpu_clock_sample():
-    """One reading of amd-smi's clock metrics for GPU 0 (raw JSON trimmed to
-    the graphics clock entries), or an error string."""
+    """One reading of amd-smi's graphics clocks of GPU 0 (one per XCD), or an
+    error string; never raises."""
     try:
         r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"], capture_output=True,
                            text=True, timeout=20)
         if r.returncode != 0:
             return {"error": (r.stderr or r.stdout).strip()[-200:]}
         data = json.loads(r.stdout)
-    except Exception as e:  # amd-smi missing or unparsable: report, never fail
+        gpu = data["gpu_data"][0] if isinstance(data, dict) else data[0]
+        clk = gpu["clock"]
+        cur = [clk[k]["clk"]["value"] for k in sorted(clk) if k.startswith("gfx_")]
+        mx = [clk[k]["max_clk"]["value"] for k in sorted(clk) if k.startswith("gfx_")]
+        cur = [float(v) for v in cur if isinstance(v, (int, float))]
+        return {"source": "amd-smi metric -g 0 -c", "gfx_clk_mhz": cur,
+                "mean_mhz": round(sum(cur) / len(cur), 1) if cur else None,
+                "max_clk_mhz": max(mx) if mx else None}
+    except Exception as e:  # amd-smi missing or its output unexpected: report, never fail
         return {"error": str(e)[-200:]}
-
-    found = {}
-
-    def walk(o, path):
-        if isinstance(o, dict):
-            for k2, v in o.items():
-                walk(v, path + [str(k2)])
-        elif isinstance(o, list):
-            for i, v in enumerate(o):
-                walk(v, path + [str(i)])
-        else:
-            key = "/".join(path).lower()
-            if "gfx" in key and ("clk" in key or "clock" in key):
-                found["/".join(path)] = o
-
-    walk(data, [])
-    return found or {"raw": json.dumps(data)[:600]}
 
 
 # ---------------------------------------------------------------------------

@@ -21,8 +21,6 @@
 // sub-tile of v_mfma_f32_32x32x16_bf16 (fp32 accumulation), A and B tiles
 // double-buffered through LDS with register prefetch of the next K tile.
 // f32 kernel: 64x64 tile, FMA on the vector ALUs (no reduced precision).
-#include <cstdlib>
-
 #include "moe_internal.h"
 #include "gemm_common.h"
 
@@ -410,19 +408,8 @@ int pick_tile_variant(const moe_config& c, GemmKind kind, const GemmDesc& g, int
 hipError_t launch_gemm_tiled(const moe_config& c, GemmKind kind, const GemmDesc& g, int variant,
                              hipStream_t s);
 
-// Tuning knob: MOE_TILE_UP / MOE_TILE_DOWN = index of a large-tile shape to
-// use when it covers the problem (read once; unset = model-based choice).
-static int forced_tile(GemmKind kind) {
-  static const int up = [] { const char* e = getenv("MOE_TILE_UP"); return e ? atoi(e) : -1; }();
-  static const int down = [] { const char* e = getenv("MOE_TILE_DOWN"); return e ? atoi(e) : -1; }();
-  return kind == kGemmUp ? up : down;
-}
-
 hipError_t launch_gemm(const moe_config& c, GemmKind kind, const GemmDesc& g, hipStream_t s) {
-  int variant = pick_tile_variant(c, kind, g, forced_tile(kind));
-  // INT8 weights run on the register-staged tiles only (a forced shape that
-  // cannot take them falls back to the model's choice)
-  if (variant < 0 && g.w_scale) variant = pick_tile_variant(c, kind, g, -1);
+  const int variant = pick_tile_variant(c, kind, g, -1);
   if (variant >= 0) return launch_gemm_tiled(c, kind, g, variant, s);
   if (g.w_scale) return hipErrorInvalidValue;  // shapes checked by the API never get here
   const bool bias = g.bias != nullptr;

@@ -1,0 +1,563 @@
+// Wide-tile persistent grouped GEMM for bf16 on gfx950, for groups of
+// thousands of rows (the FLAME-shaped and skewed layers, and the dense
+// shared-expert products).
+//
+// Same operation as the other grouped GEMM kernels (expert FFN up GEMM with
+// the SwiGLU / GELU epilogue; down GEMM summing the shared-expert segments
+// along K).  Design:
+//   * 256 x 256 output tiles, 4 waves (2 x 2), each wave a 128 x 128 block of
+//     4 x 4 v_mfma_f32_32x32x16_bf16 tiles: every 16-byte LDS fragment feeds
+//     four MFMAs, so LDS reads stay at 64 bytes per clock per CU at the MFMA
+//     rate (a 128 x 64 wave tile needs 96);
+//   * K advances 32 per stage through 4 LDS stages (32 KB each); global data
+//     goes straight into LDS (16-byte direct copies, no staging registers);
+//   * one barrier per stage, placed between the stage's two K steps: the
+//     first K step's MFMAs run on fragments read before the barrier, the
+//     second's on fragments read right after it, and the copies for stage
+//     s + 3 are issued at the top of stage s, so a copy has two and a half
+//     stages (about 2500 MFMA cycles) to land;
+//   * only two sets of MFMA operand registers (the two K steps), the
+//     accumulators in AGPRs: no register spills at one wave per SIMD;
+//   * persistent workgroups, one per CU, walk a contiguous run of their XCD's
+//     share of the tile list; the copies of the next tile's first stages are
+//     issued during the current tile's last stages, so the epilogue overlaps
+//     them;
+//   * LDS rows (64 bytes) are XOR-swizzled in 16-byte chunks on the global
+//     side of the copy: chunk' = chunk ^ ((row / 4) % 4), so the 16 lanes of
+//     a fragment read hit 16 distinct 16-byte bank groups;
+//   * the weight fragment is the MFMA's first operand: each lane ends up with
+//     4 consecutive output columns of one row (8-byte stores).
+// Requirements (checked by the host): K per segment a multiple of 32, the
+// K stages per tile a multiple of 4, output widths a multiple of the tile.
+#include <algorithm>
+
+#include "moe_internal.h"
+#include "gemm_common.h"
+
+namespace moe {
+namespace wide {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte chunk
+
+constexpr int BM = 256, BN = 256;   // output tile
+constexpr int BK = 32;              // K elements per stage
+constexpr int NS = 4;               // LDS stages
+constexpr int CPR = BK / 8;         // 16-byte chunks per LDS row
+constexpr int SCH = BM * CPR;       // u32x4 per operand stage
+static_assert(CPR == 4, "64-byte LDS rows");
+
+// Wave layout: WM x WN waves, each a (BM / WM) x (BN / WN) block of 32x32
+// MFMA tiles.
+template <int WM, int WN>
+struct Layout {
+  static constexpr int NW = WM * WN, NT = 64 * NW;
+  static constexpr int TM = BM / WM, TN = BN / WN;   // wave tile
+  static constexpr int MI = TM / 32, NI = TN / 32;
+  static constexpr int A_IW = BM / (16 * NW);        // 16-row copies per wave per stage (A)
+  static constexpr int B_IW = BN / (16 * NW);        // (B)
+  static constexpr int LPS = A_IW + B_IW;            // copies per lane per stage
+  static_assert(A_IW >= 1 && B_IW >= 1 && MI >= 1 && NI >= 2, "layout");
+};
+
+__device__ __forceinline__ void copy16(const void* g, u32x4* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+}
+
+// 4 bytes per lane into LDS; lane i lands at lds + 4 * i
+__device__ __forceinline__ void copy4(const void* g, int* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0);
+}
+
+// LDS read of a gather index, with its wait in the same asm block (the
+// callers order it after the copy of the index with explicit waits)
+__device__ __forceinline__ int lds_read_i32(const int* p, int i) {
+  int v;
+  const uint32_t addr = (uint32_t)(uintptr_t)(p + i);
+  __asm__ volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+
+// workgroup barrier without a memory fence; the empty asm statements keep the
+// compiler from moving memory accesses across it
+__device__ __forceinline__ void wg_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0)
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0070 | (N & 15) | ((N >> 4) << 14));
+}
+// s_waitcnt vmcnt(0)
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Buffer resource word 3 for raw (untyped, unswizzled) access.
+constexpr int kBufFlags = 0x00020000;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// 4 floats rounded to bf16 (nearest even), one 8-byte buffer store at byte
+// offset off (dropped by the range check when past the resource's end)
+__device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, int off, const float* v) {
+  const u32x2 w = {(uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
+                   (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16)};
+  __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, 0);
+}
+
+template <int WM, int WN, int KIND, int ACT, bool BIAS>
+__global__ void __launch_bounds__(64 * WM * WN, 1)
+gemm_wide_kernel(GemmDesc p, int tiles_n) {
+  constexpr bool kSwiglu = (KIND == kGemmUp && ACT == MOE_ACT_SWIGLU);
+  using Ly = Layout<WM, WN>;
+  constexpr int NT = Ly::NT, TM = Ly::TM, TN = Ly::TN, MI = Ly::MI, NI = Ly::NI;
+  constexpr int A_IW = Ly::A_IW, B_IW = Ly::B_IW, LPS = Ly::LPS;
+  constexpr int RW = 16 * A_IW;      // A rows copied by one wave (a contiguous block)
+  constexpr int BW = 16 * B_IW;      // B rows copied by one wave
+  // the group barriers below hand out one LDS read or copy after each MFMA
+  constexpr int MF = MI * NI;        // MFMAs per K step
+  constexpr int DSR = MI + NI;       // fragment reads per K step
+  static_assert(DSR <= MF && LPS <= MF, "interleave pattern");
+
+  __shared__ __attribute__((aligned(16))) u32x4 sA0[SCH];
+  __shared__ __attribute__((aligned(16))) u32x4 sA1[SCH];
+  __shared__ __attribute__((aligned(16))) u32x4 sA2[SCH];
+  __shared__ __attribute__((aligned(16))) u32x4 sA3[SCH];
+  __shared__ __attribute__((aligned(16))) u32x4 sB0[SCH];
+  __shared__ __attribute__((aligned(16))) u32x4 sB1[SCH];
+  __shared__ __attribute__((aligned(16))) u32x4 sB2[SCH];
+  __shared__ __attribute__((aligned(16))) u32x4 sB3[SCH];
+  __shared__ int s_off[kMaxExperts + 1];     // group row offsets
+  __shared__ int s_tstart[kMaxExperts + 1];  // first row tile of each group
+  __shared__ int s_scan[kMaxExperts + 1];
+  __shared__ int s_idx[3][BM];               // gather indices of three consecutive tiles
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+
+  // ---- row-tile table of the groups (exact, from the device offsets)
+  const int G = p.group_off ? p.n_groups : 1;
+  for (int g = tid; g <= G; g += NT)
+    s_off[g] = p.group_off ? p.group_off[g] : (g == 0 ? 0 : (int)p.rows_max);
+  __syncthreads();
+  for (int g = tid; g <= G; g += NT) {
+    const int rows = g < G ? min(s_off[g + 1], (int)p.rows_max) - min(s_off[g], (int)p.rows_max) : 0;
+    s_tstart[g] = rows > 0 ? (rows + BM - 1) / BM : 0;
+  }
+  __syncthreads();
+  for (int o = 1; o <= G; o <<= 1) {  // inclusive scan over g = 0..G
+    for (int g = tid; g <= G; g += NT) s_scan[g] = g >= o ? s_tstart[g - o] : 0;
+    __syncthreads();
+    for (int g = tid; g <= G; g += NT) s_tstart[g] += s_scan[g];
+    __syncthreads();
+  }
+  const int m_tiles = s_tstart[G - 1];
+  for (int g = tid; g <= G; g += NT) s_scan[g] = g == 0 ? 0 : s_tstart[g - 1];
+  __syncthreads();
+  for (int g = tid; g <= G; g += NT) s_tstart[g] = s_scan[g];
+  __syncthreads();
+
+  // ---- this workgroup's tiles: XCD x = blockIdx % 8 owns the x-th eighth of
+  // the tile list; its workgroups stride through it
+  const int total = m_tiles * tiles_n;
+  const int xcd = blockIdx.x % 8, per_xcd = gridDim.x / 8;
+  const int t_lo = (int)((int64_t)total * xcd / 8), t_hi = (int)((int64_t)total * (xcd + 1) / 8);
+  int L = t_lo + (int)(blockIdx.x / 8);
+  if (L >= t_hi) return;
+
+  const int S = p.n_seg, d = p.d, f = p.f;
+  const uint16_t* A = static_cast<const uint16_t*>(p.a);
+  const uint16_t* W = static_cast<const uint16_t*>(p.w);
+  const int kw = (KIND == kGemmUp) ? d : f;                // weight row length (one segment)
+  const int rows1 = (KIND == kGemmUp) ? (kSwiglu ? 2 * f : f) : d;  // weight rows per segment
+  const int nk_seg = kw / BK;                              // stages per FFN segment
+  const int nk = (KIND == kGemmUp) ? nk_seg : S * nk_seg;  // stages per tile
+
+  // copy geometry: copy i of wave w covers tile rows w*64 + i*16 + lane/4 at
+  // LDS chunk lane%4, which holds global chunk (lane%4) ^ ((row/4)%4) =
+  // (lane%4) ^ ((lane/16)%4)
+  const int lrow = lane / 4;
+  const int chk = ((lane % 4) ^ ((lane / 16) % 4)) * 8;
+
+  struct Tile {
+    int group, rows, seg, n0;
+    int64_t row0;
+  };
+  auto tile_of = [&](int l) {
+    Tile t;
+    const int mt = l / tiles_n, nt = l % tiles_n;
+    int glo = 0, ghi = G - 1;  // last g with s_tstart[g] <= mt
+    while (glo < ghi) {
+      const int mid = (glo + ghi + 1) / 2;
+      if (s_tstart[mid] <= mt) glo = mid; else ghi = mid - 1;
+    }
+    // the values are the same in every lane: keep them in scalar registers
+    t.group = __builtin_amdgcn_readfirstlane(glo);
+    const int r0 = __builtin_amdgcn_readfirstlane(s_off[glo] + (mt - s_tstart[glo]) * BM);
+    t.row0 = r0;
+    t.rows = __builtin_amdgcn_readfirstlane(min(BM, min(s_off[glo + 1], (int)p.rows_max) - r0));
+    if (KIND == kGemmUp) {
+      constexpr int bnh = kSwiglu ? BN / 2 : BN;
+      const int tpn = f / bnh;
+      t.seg = nt / tpn;
+      t.n0 = (nt % tpn) * bnh;
+    } else {
+      t.seg = 0;
+      t.n0 = nt * BN;
+    }
+    return t;
+  };
+
+  // per-lane copy sources of one tile at K = 0: A rows (gathered or direct)
+  // and the first B row (the wave's B rows are 16 apart per copy)
+  struct Src {
+    const uint16_t* a[A_IW];
+    const uint16_t* b;
+  };
+  const bool gather = p.a_rows != nullptr;
+  // gather indices of this wave's 64 rows of tile t_ -> s_idx[buf_] (one
+  // 4-byte copy per lane; rows past the tile end repeat its last row)
+#define MOE_WIDE_IDX(t_, buf_)                                                              \
+  do {                                                                                      \
+    if (lane < RW) {                                                                        \
+      const int r_ = wave * RW + lane;                                                      \
+      const int64_t gr_ = (t_).row0 + (r_ < (t_).rows ? r_ : (t_).rows - 1);               \
+      copy4(p.a_rows + gr_, &s_idx[buf_][wave * RW]);                                       \
+    }                                                                                       \
+  } while (0)
+  auto src_of = [&](const Tile& t, int buf) {
+    Src s;
+#pragma unroll
+    for (int i = 0; i < A_IW; ++i) {
+      const int rr = wave * RW + i * 16 + lrow;
+      const int64_t row = gather ? (int64_t)lds_read_i32(s_idx[buf], rr)
+                                 : t.row0 + (rr < t.rows ? rr : t.rows - 1);
+      s.a[i] = A + row * p.lda + chk;
+    }
+    const uint16_t* wb = W + ((int64_t)t.group * S + t.seg) * rows1 * (int64_t)kw;
+    // the wave's B rows (BW of them, never across the gate / up boundary at
+    // BN / 2 for SwiGLU)
+    const int rb = wave * BW + lrow;
+    int wr;
+    if (kSwiglu)
+      wr = (rb < BN / 2) ? t.n0 + rb : f + t.n0 + (rb - BN / 2);
+    else
+      wr = t.n0 + rb;
+    s.b = wb + (int64_t)wr * kw + chk;
+    return s;
+  };
+  // copies of K stage kt_ of the tile with sources src_ into LDS (sa_, sb_)
+#define MOE_WIDE_LOAD(src_, kt_, sa_, sb_)                                                  \
+  do {                                                                                      \
+    int64_t ao_, bo_;                                                                       \
+    if (KIND == kGemmUp) {                                                                  \
+      ao_ = (int64_t)(kt_) * BK;                                                            \
+      bo_ = ao_;                                                                            \
+    } else {                                                                                \
+      const int s_ = (kt_) / nk_seg, kk_ = ((kt_) - s_ * nk_seg) * BK;                      \
+      ao_ = (int64_t)s_ * f + kk_;                                                          \
+      bo_ = (int64_t)s_ * d * f + kk_;                                                      \
+    }                                                                                       \
+    _Pragma("unroll") for (int i_ = 0; i_ < A_IW; ++i_)                                    \
+        copy16((src_).a[i_] + ao_, (sa_) + (wave * A_IW + i_) * 64);                        \
+    _Pragma("unroll") for (int i_ = 0; i_ < B_IW; ++i_)                                    \
+        copy16((src_).b + (int64_t)i_ * 16 * kw + bo_, (sb_) + (wave * B_IW + i_) * 64);   \
+  } while (0)
+
+  // fragment rows of this wave (row bases are multiples of 32, so the
+  // swizzle key depends on the lane's row only)
+  const int wm = wave / WN, wn = wave % WN;  // wave position in the tile
+  const int fr = lane % 32, half = lane / 32;
+  int arow[MI], brow[NI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) arow[i] = (wm * TM + i * 32 + fr) * CPR;
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    int r;
+    if (kSwiglu)
+      r = (j < NI / 2) ? wn * (TN / 2) + j * 32 + fr : BN / 2 + wn * (TN / 2) + (j - NI / 2) * 32 + fr;
+    else
+      r = wn * TN + j * 32 + fr;
+    brow[j] = r * CPR;
+  }
+  const int sw = (fr / 4) % 4;
+
+  f32x16 acc[MI][NI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  // ---- prologue: gather indices of the first two tiles, their sources,
+  // stages 0..2 of the first tile
+  int ib = 0;  // s_idx buffer of the current tile; the next two follow cyclically
+  Tile tc = tile_of(L);
+  bool has_next = L + per_xcd < t_hi;
+  Tile tn = has_next ? tile_of(L + per_xcd) : tc;
+  if (gather) {
+    MOE_WIDE_IDX(tc, 0);
+    MOE_WIDE_IDX(tn, 1);
+    wait_vm0();
+  }
+  Src cur = src_of(tc, 0);
+  Src nxt = src_of(tn, 1);
+  MOE_WIDE_LOAD(cur, 0, sA0, sB0);
+  MOE_WIDE_LOAD(cur, 1, sA1, sB1);
+  MOE_WIDE_LOAD(cur, 2, sA2, sB2);
+  wait_vm_lgkm<2 * LPS>();  // stage 0 landed (this lane's copies)
+  wg_barrier();
+
+  bf16x8 F0a[MI], F0b[NI], F1a[MI], F1b[NI];
+#define MOE_WIDE_FRAGS(va_, vb_, sa_, sb_, ks_)                                             \
+  do {                                                                                      \
+    const int c_ = (half + 2 * (ks_)) ^ sw;                                                 \
+    _Pragma("unroll") for (int i_ = 0; i_ < MI; ++i_)                                      \
+        (va_)[i_] = __builtin_bit_cast(bf16x8, (sa_)[arow[i_] + c_]);                       \
+    _Pragma("unroll") for (int j_ = 0; j_ < NI; ++j_)                                      \
+        (vb_)[j_] = __builtin_bit_cast(bf16x8, (sb_)[brow[j_] + c_]);                       \
+  } while (0)
+#define MOE_WIDE_MFMA(va_, vb_)                                                             \
+  do {                                                                                      \
+    _Pragma("unroll") for (int i_ = 0; i_ < MI; ++i_)                                      \
+        _Pragma("unroll") for (int j_ = 0; j_ < NI; ++j_) acc[i_][j_] =                     \
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16((vb_)[j_], (va_)[i_], acc[i_][j_], 0, 0, 0); \
+  } while (0)
+  MOE_WIDE_FRAGS(F0a, F0b, sA0, sB0, 0);
+
+  uint16_t* out = static_cast<uint16_t*>(p.out);
+  const uint16_t* bias = static_cast<const uint16_t*>(p.bias);
+
+  for (;;) {
+    // gather indices of the tile after next (landed long before they are read)
+    const bool has_next2 = has_next && L + 2 * per_xcd < t_hi;
+    Tile tn2 = tn;
+    if (has_next2) {
+      tn2 = tile_of(L + 2 * per_xcd);
+      if (gather) MOE_WIDE_IDX(tn2, ib == 0 ? 2 : ib - 1);
+    }
+
+    // one stage, in two halves around one barrier.  On entry stage kk is in
+    // LDS and visible to every wave, its first K step is in F0, and stages
+    // kk+1, kk+2 may be in flight.
+    //   first half: refill the buffer of stage kk - 1 (free since the last
+    //   barrier) with stage kk + 3 (of this tile, of the next one, or past
+    //   the last tile a harmless repeat of stage 0, which keeps one copy
+    //   group per stage) and read the second K step (F1), both interleaved
+    //   with the MFMAs on F0;
+    //   wait until stage kk + 1 has landed and F1 is in registers; barrier;
+    //   second half: read stage kk + 1's first K step into F0, interleaved
+    //   with the MFMAs on F1.
+    // The group barriers place one LDS read or one copy after each MFMA, so
+    // the matrix pipe is fed while the memory instructions issue.
+#define MOE_WIDE_STAGE(kk_, sa_, sb_, na_, nb_, fa_, fb_)                                   \
+  do {                                                                                      \
+    {                                                                                       \
+      const int kn_ = (kk_) + NS - 1;                                                       \
+      const bool in_cur_ = kn_ < nk;                                                        \
+      const int kt_ = in_cur_ ? kn_ : (has_next ? kn_ - nk : 0);                            \
+      Src ls_;                                                                              \
+      _Pragma("unroll") for (int i_ = 0; i_ < A_IW; ++i_) ls_.a[i_] = in_cur_ ? cur.a[i_] : nxt.a[i_]; \
+      ls_.b = in_cur_ ? cur.b : nxt.b;                                                      \
+      MOE_WIDE_LOAD(ls_, kt_, fa_, fb_);                                                    \
+    }                                                                                       \
+    MOE_WIDE_FRAGS(F1a, F1b, sa_, sb_, 1);                                                  \
+    MOE_WIDE_MFMA(F0a, F0b);                                                                \
+    _Pragma("unroll") for (int g_ = 0; g_ < MF; ++g_) {                                    \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); /* MFMA */                         \
+      if (g_ < DSR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); /* LDS read */       \
+      if (g_ < LPS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); /* copy */           \
+    }                                                                                       \
+    wait_vm_lgkm<(NS - 2) * LPS>();                                                         \
+    wg_barrier();                                                                           \
+    MOE_WIDE_FRAGS(F0a, F0b, na_, nb_, 0);                                                  \
+    MOE_WIDE_MFMA(F1a, F1b);                                                                \
+    _Pragma("unroll") for (int g_ = 0; g_ < MF; ++g_) {                                    \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1); /* MFMA */                         \
+      if (g_ < DSR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1); /* LDS read */       \
+    }                                                                                       \
+    __builtin_amdgcn_sched_barrier(0);                                                      \
+  } while (0)
+
+    for (int kk = 0; kk < nk; kk += NS) {
+      MOE_WIDE_STAGE(kk + 0, sA0, sB0, sA1, sB1, sA3, sB3);
+      MOE_WIDE_STAGE(kk + 1, sA1, sB1, sA2, sB2, sA0, sB0);
+      MOE_WIDE_STAGE(kk + 2, sA2, sB2, sA3, sB3, sA1, sB1);
+      MOE_WIDE_STAGE(kk + 3, sA3, sB3, sA0, sB0, sA2, sB2);
+    }
+#undef MOE_WIDE_STAGE
+
+    // ---- epilogue.  acc[i][j] holds the transposed 32x32 block: lane l has
+    // tile row i*32 + l%32 and output columns j*32 + 8*(q/4) + 4*(l/32) + q%4.
+    // Stores go through buffer resources that span the tile's valid rows, so
+    // a row past the group's end is dropped by the range check (no branch:
+    // the epilogue stays one block, read one row block at a time).
+    {
+      const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+          out + tc.row0 * p.ldo, (short)0, (int)(tc.rows * p.ldo * 2), kBufFlags);
+      __amdgpu_buffer_rsrc_t rp = ro;
+      if (KIND == kGemmUp && p.preact)
+        rp = __builtin_amdgcn_make_buffer_rsrc(static_cast<uint16_t*>(p.preact) + tc.row0 * p.ldp,
+                                              (short)0, (int)(tc.rows * p.ldp * 2), kBufFlags);
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int r = wm * TM + i * 32 + fr;
+        const int orow = r * (int)p.ldo, prow = r * (int)p.ldp;
+        if (kSwiglu) {
+#pragma unroll
+          for (int j = 0; j < NI / 2; ++j) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const int cidx = wn * (TN / 2) + j * 32 + 8 * g4 + 4 * half;
+              float hv[4], gv[4], uv[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                gv[e] = acc[i][j][4 * g4 + e];
+                uv[e] = acc[i][j + NI / 2][4 * g4 + e];
+                if (BIAS) {
+                  const uint16_t* b = bias + ((int64_t)tc.group * S + tc.seg) * 2 * f;
+                  gv[e] += bf16_to_f32(b[tc.n0 + cidx + e]);
+                  uv[e] += bf16_to_f32(b[f + tc.n0 + cidx + e]);
+                }
+                hv[e] = silu_f(gv[e]) * uv[e];
+              }
+              const int col = tc.seg * f + tc.n0 + cidx;
+              store4(ro, (orow + col) * 2, hv);
+              if (p.preact) {
+                const int pc = tc.seg * 2 * f + tc.n0 + cidx;
+                store4(rp, (prow + pc) * 2, gv);
+                store4(rp, (prow + pc + f) * 2, uv);
+              }
+            }
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < NI; ++j) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const int cidx = wn * TN + j * 32 + 8 * g4 + 4 * half;
+              float hv[4], pv[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                float v = acc[i][j][4 * g4 + e];
+                if (KIND == kGemmUp) {
+                  if (BIAS) v += bf16_to_f32(bias[((int64_t)tc.group * S + tc.seg) * f + tc.n0 + cidx + e]);
+                  pv[e] = v;
+                  hv[e] = gelu_f(v);
+                } else {
+                  if (BIAS)
+                    for (int s = 0; s < S; ++s)
+                      v += bf16_to_f32(bias[((int64_t)tc.group * S + s) * d + tc.n0 + cidx + e]);
+                  hv[e] = v;
+                }
+              }
+              const int col = (KIND == kGemmUp) ? tc.seg * f + tc.n0 + cidx : tc.n0 + cidx;
+              store4(ro, (orow + col) * 2, hv);
+              if (KIND == kGemmUp && p.preact) store4(rp, (prow + col) * 2, pv);
+            }
+          }
+        }
+      }
+    }
+    if (!has_next) {
+      wait_vm0();  // no copy may still target LDS when the workgroup ends
+      break;
+    }
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+    // advance: next becomes current; the tile after next becomes next (its
+    // indices were copied at the start of this tile, many stages ago, and
+    // the stage waits since then have seen them land)
+    L += per_xcd;
+    tc = tn;
+    cur = nxt;
+    ib = ib == 2 ? 0 : ib + 1;
+    has_next = has_next2;
+    if (has_next) {
+      tn = tn2;
+      nxt = src_of(tn, ib == 2 ? 0 : ib + 1);
+    }
+  }
+#undef MOE_WIDE_FRAGS
+#undef MOE_WIDE_MFMA
+#undef MOE_WIDE_LOAD
+#undef MOE_WIDE_IDX
+}
+
+}  // namespace wide
+
+namespace {
+
+int wide_cus() {
+  static int n = [] {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    return v;
+  }();
+  return n;
+}
+
+template <int WM, int WN, int KIND, int ACT, bool BIAS>
+hipError_t run_wide(const GemmDesc& g, hipStream_t s) {
+  constexpr bool kSwiglu = (KIND == kGemmUp && ACT == MOE_ACT_SWIGLU);
+  const int tiles_n = KIND == kGemmUp ? g.n_seg * (g.f / (kSwiglu ? wide::BN / 2 : wide::BN))
+                                      : g.d / wide::BN;
+  const int64_t tiles_m = (g.rows_max + wide::BM - 1) / wide::BM + (g.group_off ? g.n_groups : 0);
+  const int64_t upper = tiles_m * tiles_n;
+  if (upper <= 0 || g.rows_max <= 0) return hipSuccess;
+  int64_t grid = std::min<int64_t>(upper, (int64_t)wide_cus());
+  grid = (grid + 7) / 8 * 8;  // a multiple of 8 (XCDs)
+  wide::gemm_wide_kernel<WM, WN, KIND, ACT, BIAS>
+      <<<dim3((unsigned)grid), dim3(64 * WM * WN), 0, s>>>(g, tiles_n);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Whether the wide kernel covers the problem: bf16 weights (no INT8 codes),
+// K per segment a multiple of 32 with a multiple of 4 stages per tile, and
+// output widths that fill whole tiles.
+bool wide_fits(GemmKind kind, const GemmDesc& g) {
+  if (g.w_scale) return false;
+  // the epilogue's 32-bit buffer offsets: 256 rows of output (and
+  // pre-activations) stay below 2 GiB
+  if (g.ldo >= ((int64_t)1 << 22) || (g.preact && g.ldp >= ((int64_t)1 << 22))) return false;
+  const bool swiglu = kind == kGemmUp && g.act == MOE_ACT_SWIGLU;
+  const int K = kind == kGemmUp ? g.d : g.f;
+  if (K % wide::BK != 0) return false;
+  const int nk = (kind == kGemmUp ? 1 : g.n_seg) * (K / wide::BK);
+  if (nk % wide::NS != 0) return false;
+  const int ncol = kind == kGemmUp ? (swiglu ? wide::BN / 2 : wide::BN) : wide::BN;
+  const int width = kind == kGemmUp ? g.f : g.d;
+  return width % ncol == 0;
+}
+
+template <int WM, int WN>
+hipError_t launch_wide_t(GemmKind kind, const GemmDesc& g, hipStream_t s) {
+  const bool bias = g.bias != nullptr;
+  if (kind == kGemmDown)
+    return bias ? run_wide<WM, WN, kGemmDown, 0, true>(g, s) : run_wide<WM, WN, kGemmDown, 0, false>(g, s);
+  if (g.act == MOE_ACT_SWIGLU)
+    return bias ? run_wide<WM, WN, kGemmUp, MOE_ACT_SWIGLU, true>(g, s)
+                : run_wide<WM, WN, kGemmUp, MOE_ACT_SWIGLU, false>(g, s);
+  return bias ? run_wide<WM, WN, kGemmUp, MOE_ACT_GELU, true>(g, s)
+              : run_wide<WM, WN, kGemmUp, MOE_ACT_GELU, false>(g, s);
+}
+
+// waves8: 8 waves (2 x 4, wave tile 128 x 64, two waves per SIMD), else 4
+// waves (2 x 2, wave tile 128 x 128)
+hipError_t launch_gemm_wide(GemmKind kind, const GemmDesc& g, bool waves8, hipStream_t s) {
+  return waves8 ? launch_wide_t<2, 4>(kind, g, s) : launch_wide_t<2, 2>(kind, g, s);
+}
+
+}  // namespace moe

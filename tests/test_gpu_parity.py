@@ -114,6 +114,12 @@ SMALL = [
     # k above 8: picks past the register-held ones, generic combine and scatter paths
     ("bf16_k12_cap", 300, 64, 16, 12, 64, 1, "bf16", "swiglu", 1.0, "none", "none", True),
     ("f32_k10", 100, 32, 12, 10, 32, 0, "f32", "gelu", 0.0, "random", "none", False),
+    # more than 1024 rows per group: the wide-tile grouped GEMM, ragged group
+    # ends inside a 256-row tile, shared experts summed along K, GELU with
+    # biases, capacity drops
+    ("bf16_wide_swiglu_shared2", 3000, 512, 2, 1, 384, 2, "bf16", "swiglu", 0.0, "none", "none", False),
+    ("bf16_wide_gelu_bias", 2600, 256, 2, 1, 512, 1, "bf16", "gelu", 0.0, "random", "none", True),
+    ("bf16_wide_cap_zipf", 4100, 256, 4, 2, 256, 0, "bf16", "swiglu", 1.0, "none", "zipf", False),
 ]
 
 
