@@ -441,7 +441,7 @@ gemm_tile_persistent(GemmDesc p, int tiles_n) {
 bool pipe_shape_fits(GemmKind kind, const GemmDesc& g, int bm, int bn, int stages);
 hipError_t launch_gemm_pipe(GemmKind kind, const GemmDesc& g, int shape, int occ, hipStream_t s);
 bool wide_fits(GemmKind kind, const GemmDesc& g);
-hipError_t launch_gemm_wide(GemmKind kind, const GemmDesc& g, bool waves8, hipStream_t s);
+hipError_t launch_gemm_wide(GemmKind kind, const GemmDesc& g, hipStream_t s);
 
 namespace {
 using namespace tiled;
@@ -451,9 +451,9 @@ struct TileCfg {
   double eff;           // relative MFMA efficiency of the shape
 };
 
-constexpr int kVariants = 10;
+constexpr int kVariants = 9;
 constexpr int kFirstPipe = 4;  // variants 4..7 are the pipelined kernel (gemm_pipe.hip)
-constexpr int kWide = 8;       // 8, 9: the wide-tile kernel (gemm_wide.hip), 4 or 8 waves
+constexpr int kWide = 8;       // the wide-tile kernel (gemm_wide.hip)
 constexpr TileCfg kTiles[kVariants] = {
     {256, 256, 64, 1, 1.0},   // 8 waves, wave tile 128 x 64
     {256, 128, 64, 1, 0.85},  // 8 waves, wave tile 64 x 64
@@ -463,7 +463,6 @@ constexpr TileCfg kTiles[kVariants] = {
     {256, 128, 32, 1, 1.1},   // pipelined, 4 waves, wave tile 128 x 64
     {128, 128, 32, 2, 1.1},   // pipelined, 4 waves, wave tile 64 x 64
     {128, 128, 32, 1, 1.0},   // pipelined, 8 stages (long K, few tiles)
-    {256, 256, 32, 1, 1.5},   // wide: 4 waves, wave tile 128 x 128, 4 stages
     {256, 256, 32, 1, 1.6},   // wide: 8 waves, wave tile 128 x 64, 4 stages
 };
 
@@ -543,7 +542,7 @@ int cu_count() {
 const int* preferred_variants(GemmKind kind, double rows_per_group) {
   static const int up_decode[] = {3, 6, 2, -1}, dn_decode[] = {6, 3, 2, -1};
   static const int up_small[] = {6, 2, 5, -1}, dn_small[] = {2, 1, 6, -1};
-  static const int up_large[] = {9, 5, 0, 4, -1}, dn_large[] = {9, 0, 2, 5, -1};
+  static const int up_large[] = {8, 5, 0, 4, -1}, dn_large[] = {8, 0, 2, 5, -1};
   if (rows_per_group < 64) return kind == kGemmUp ? up_decode : dn_decode;
   if (rows_per_group < 1024) return kind == kGemmUp ? up_small : dn_small;
   return kind == kGemmUp ? up_large : dn_large;
@@ -565,7 +564,7 @@ int pick_tile_variant(const moe_config& c, GemmKind kind, const GemmDesc& g, int
   auto fits = [&](int v) {
     const TileCfg& tc = kTiles[v];
     if (g.w_scale && v >= kFirstPipe) return false;  // INT8 weights: register-staged tiles only
-    if (v >= kWide) return wide_fits(kind, g);
+    if (v == kWide) return wide_fits(kind, g);
     if (K % tc.bk != 0) return false;
     const int ncol = kind == kGemmUp ? (swiglu ? tc.bn / 2 : tc.bn) : tc.bn;
     const int nwidth = kind == kGemmUp ? g.f : g.d;
@@ -598,7 +597,7 @@ int pick_tile_variant(const moe_config& c, GemmKind kind, const GemmDesc& g, int
 
 hipError_t launch_gemm_tiled(const moe_config& c, GemmKind kind, const GemmDesc& g, int variant,
                              hipStream_t s) {
-  if (variant >= kWide) return launch_gemm_wide(kind, g, variant == kWide + 1, s);
+  if (variant == kWide) return launch_gemm_wide(kind, g, s);
   if (variant >= kFirstPipe)
     return launch_gemm_pipe(kind, g, variant - kFirstPipe, kTiles[variant].occ, s);
   const bool bias = g.bias != nullptr;

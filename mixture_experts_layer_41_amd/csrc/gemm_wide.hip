@@ -5,19 +5,23 @@
 // Same operation as the other grouped GEMM kernels (expert FFN up GEMM with
 // the SwiGLU / GELU epilogue; down GEMM summing the shared-expert segments
 // along K).  Design:
-//   * 256 x 256 output tiles, 4 waves (2 x 2), each wave a 128 x 128 block of
-//     4 x 4 v_mfma_f32_32x32x16_bf16 tiles: every 16-byte LDS fragment feeds
-//     four MFMAs, so LDS reads stay at 64 bytes per clock per CU at the MFMA
-//     rate (a 128 x 64 wave tile needs 96);
+//   * 256 x 256 output tiles (the largest whose float32 accumulators fit the
+//     register file: 256 per lane of a CU), 8 waves as 2 x 4, each wave a
+//     128 x 64 block of 4 x 2 v_mfma_f32_32x32x16_bf16 tiles, two waves per
+//     SIMD.  With one wave per SIMD the in-order issue of the LDS reads and
+//     copies stalls that SIMD's matrix pipe (a loop of 16-byte LDS reads and
+//     MFMAs measured 1.3 PFLOP/s at one wave per SIMD and 1.9 at two); with
+//     two, one wave's memory instructions issue while the other's MFMAs run;
 //   * K advances 32 per stage through 4 LDS stages (32 KB each); global data
 //     goes straight into LDS (16-byte direct copies, no staging registers);
 //   * one barrier per stage, placed between the stage's two K steps: the
 //     first K step's MFMAs run on fragments read before the barrier, the
 //     second's on fragments read right after it, and the copies for stage
 //     s + 3 are issued at the top of stage s, so a copy has two and a half
-//     stages (about 2500 MFMA cycles) to land;
-//   * only two sets of MFMA operand registers (the two K steps), the
-//     accumulators in AGPRs: no register spills at one wave per SIMD;
+//     stages to land; group barriers place one LDS read or copy after each
+//     MFMA;
+//   * two sets of MFMA operand registers (the two K steps), 128 accumulators
+//     per lane: no spills in the K loop;
 //   * persistent workgroups, one per CU, walk a contiguous run of their XCD's
 //     share of the tile list; the copies of the next tile's first stages are
 //     issued during the current tile's last stages, so the epilogue overlaps
@@ -26,7 +30,11 @@
 //     side of the copy: chunk' = chunk ^ ((row / 4) % 4), so the 16 lanes of
 //     a fragment read hit 16 distinct 16-byte bank groups;
 //   * the weight fragment is the MFMA's first operand: each lane ends up with
-//     4 consecutive output columns of one row (8-byte stores).
+//     4 consecutive output columns of one row (8-byte stores through buffer
+//     resources whose range check drops rows past the group's end).
+// What bounds it: the global -> LDS copies.  With the MFMAs removed the
+// copies and LDS reads alone take as long as the whole kernel; with every
+// tile reading the same (L2-resident) data the kernel gains only about 15 %.
 // Requirements (checked by the host): K per segment a multiple of 32, the
 // K stages per tile a multiple of 4, output widths a multiple of the tile.
 #include <algorithm>
@@ -492,6 +500,7 @@ gemm_wide_kernel(GemmDesc p, int tiles_n) {
 #undef MOE_WIDE_IDX
 }
 
+
 }  // namespace wide
 
 namespace {
@@ -542,8 +551,9 @@ bool wide_fits(GemmKind kind, const GemmDesc& g) {
   return width % ncol == 0;
 }
 
-template <int WM, int WN>
-hipError_t launch_wide_t(GemmKind kind, const GemmDesc& g, hipStream_t s) {
+// 8 waves (2 x 4, wave tile 128 x 64, two waves per SIMD)
+hipError_t launch_gemm_wide(GemmKind kind, const GemmDesc& g, hipStream_t s) {
+  constexpr int WM = 2, WN = 4;
   const bool bias = g.bias != nullptr;
   if (kind == kGemmDown)
     return bias ? run_wide<WM, WN, kGemmDown, 0, true>(g, s) : run_wide<WM, WN, kGemmDown, 0, false>(g, s);
@@ -552,12 +562,6 @@ hipError_t launch_wide_t(GemmKind kind, const GemmDesc& g, hipStream_t s) {
                 : run_wide<WM, WN, kGemmUp, MOE_ACT_SWIGLU, false>(g, s);
   return bias ? run_wide<WM, WN, kGemmUp, MOE_ACT_GELU, true>(g, s)
               : run_wide<WM, WN, kGemmUp, MOE_ACT_GELU, false>(g, s);
-}
-
-// waves8: 8 waves (2 x 4, wave tile 128 x 64, two waves per SIMD), else 4
-// waves (2 x 2, wave tile 128 x 128)
-hipError_t launch_gemm_wide(GemmKind kind, const GemmDesc& g, bool waves8, hipStream_t s) {
-  return waves8 ? launch_wide_t<2, 4>(kind, g, s) : launch_wide_t<2, 2>(kind, g, s);
 }
 
 }  // namespace moe
