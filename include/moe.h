@@ -282,6 +282,27 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
                        int32_t* expert_counts, moe_aux* aux, void* ws, size_t* ws_bytes,
                        hipStream_t stream);
 
+/*
+ * moe_forward_static - moe_forward for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  The same layer and arguments as moe_forward, without
+ * the workspace: the scratch memory is a static device array of
+ * MOE_STATIC_SCRATCH_BYTES inside the library, one copy per GPU, held from
+ * the first call on that GPU until the process ends (that first call looks
+ * up the array's device address; no call allocates or frees anything).
+ * Layers whose scratch need (moe_forward's workspace query) exceeds the
+ * array are rejected with MOE_ERR_WORKSPACE before anything is launched;
+ * 64 MiB covers, for example, 4096 tokens of a 512-wide, 16-expert top-2
+ * layer with d_ffn 1024, or 128 decode tokens of a 7168-wide, 256-expert
+ * top-8 layer.  Every call on one GPU uses the same array and leaves its
+ * contents behind: calls that overlap in time on one GPU (other streams,
+ * other threads) race, and the caller must order them.
+ */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_forward_static(const moe_config* cfg, const moe_weights* w, const void* x,
+                              const float* router_noise, void* y, int32_t* topk_idx, float* topk_w,
+                              int32_t* expert_counts, moe_aux* aux, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * Training: the forward with the state the backward needs, and the backward
  * ([P3 §4.2] trains on loss = task loss + auxiliary loss and back-propagates

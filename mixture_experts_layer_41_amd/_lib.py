@@ -20,7 +20,8 @@ MOE_WEIGHTS_ACT, MOE_WEIGHTS_INT8 = 0, 1
 # every symbol include/moe.h declares
 EXPORTS = ("moe_status_string", "moe_route", "moe_permute", "moe_expert_ffn",
            "moe_expert_ffn_int8", "moe_combine", "moe_aux_stats", "moe_forward",
-           "moe_forward_train", "moe_backward")
+           "moe_forward_static", "moe_forward_train", "moe_backward")
+MOE_STATIC_SCRATCH_BYTES = 64 << 20
 
 
 class MoeConfig(ctypes.Structure):
@@ -107,6 +108,7 @@ def lib():
         "moe_combine": [cfgp, vp, vp, vp, vp, vp, vp, vp],
         "moe_aux_stats": [cfgp, vp, vp, vp, ctypes.c_size_t, vp, vp],
         "moe_forward": [cfgp, ctypes.POINTER(MoeWeights), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "moe_forward_static": [cfgp, ctypes.POINTER(MoeWeights), vp, vp, vp, vp, vp, vp, vp, vp],
         "moe_forward_train": [cfgp, ctypes.POINTER(MoeWeights), vp, vp, vp, ctypes.POINTER(MoeSaved),
                               vp, vp, sz, vp],
         "moe_backward": [cfgp, ctypes.POINTER(MoeWeights), vp, ctypes.POINTER(MoeSaved), vp,

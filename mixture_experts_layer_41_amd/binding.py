@@ -267,6 +267,24 @@ class Forward:
         return self.y
 
 
+def moe_forward_static(cfg: MoeConfig, weights: LayerWeights, x, router_noise=None, y=None,
+                       topk_idx=None, topk_w=None, expert_counts=None, aux=None):
+    """moe_forward without a workspace (the library's static scratch array).
+    Output tensors may be passed in (then nothing is allocated here either);
+    returns (y, topk_idx, topk_w, expert_counts, aux)."""
+    T, k, E = cfg.n_tokens, cfg.top_k, cfg.n_experts
+    y = torch.empty(T, cfg.d_model, dtype=torch_dtype(cfg), device=_dev()) if y is None else y
+    topk_idx = _i32(T, k) if topk_idx is None else topk_idx
+    topk_w = _f32(T, k) if topk_w is None else topk_w
+    expert_counts = _i32(E) if expert_counts is None else expert_counts
+    aux = new_aux() if aux is None else aux
+    w = weights.c_struct()
+    check("moe_forward_static", lib().moe_forward_static(
+        ctypes.byref(cfg), ctypes.byref(w), _p(x), _p(router_noise), _p(y), _p(topk_idx),
+        _p(topk_w), _p(expert_counts), _p(aux), _stream()))
+    return y, topk_idx, topk_w, expert_counts, aux
+
+
 def moe_forward(cfg: MoeConfig, weights: LayerWeights, x, router_noise=None):
     """One-shot forward: returns (y, extras dict with topk_idx, topk_w,
     expert_counts, aux (decoded after a synchronise))."""

@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "moe_internal.h"
 
@@ -488,6 +489,56 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
                        hipStream_t stream) {
   return forward_impl(cfg, w, x, router_noise, y, topk_idx, topk_w, expert_counts, aux, nullptr, ws,
                       ws_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// moe_forward_static: the scratch memory of moe_forward in a static device
+// array.  Each GPU the library runs on holds its own copy (the code object's
+// variable) from the first call on that device until the process ends.  In
+// host code the array's name is only a host-side stand-in: its device
+// address is looked up once per device with hipGetSymbolAddress (with that
+// device current) and only that address is ever handed to kernels.
+
+static __device__ __align__(256) unsigned char scratch[MOE_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+
+moe_status static_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward_static(const moe_config* cfg, const moe_weights* w, const void* x,
+                              const float* router_noise, void* y, int32_t* topk_idx, float* topk_w,
+                              int32_t* expert_counts, moe_aux* aux, hipStream_t stream) {
+  void* ws = nullptr;
+  const moe_status st = static_scratch(&ws);
+  if (st != MOE_OK) return st;
+  // the workspace check of the forward rejects a layer whose scratch need
+  // exceeds the array (MOE_ERR_WORKSPACE) before anything is launched; no
+  // kernel of the forward needs its scratch memory cleared
+  size_t n = MOE_STATIC_SCRATCH_BYTES;
+  return forward_impl(cfg, w, x, router_noise, y, topk_idx, topk_w, expert_counts, aux, nullptr, ws,
+                      &n, stream);
 }
 
 // Training needs bf16 activations and activation-dtype expert weights.
