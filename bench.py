@@ -50,7 +50,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_gemm_traffic.json")
 # sources of the grouped GEMM kernels: the committed counter figures hold only
 # while these are unchanged
 GEMM_SRCS = [os.path.join(ROOT, "mixture_experts_layer_41_amd", "csrc", n)
-             for n in ("gemm.hip", "gemm_mfma.hip", "gemm_pipe.hip", "gemm_common.h")]
+             for n in ("gemm.hip", "gemm_mfma.hip", "gemm_pipe.hip", "gemm_common.h", "gemm_wide.hip")]
 FLUSH_BYTES = 512 << 20
 
 
@@ -73,6 +73,8 @@ def parse():
                     help="tokens of the headline batch the CPU oracle leg runs on")
     ap.add_argument("--no-backward", action="store_true", help="skip the training (backward) legs")
     ap.add_argument("--no-flush", action="store_true", help="skip the cold-cache variant")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the amd-smi clock reading (and the GEMM launches it runs under)")
     ap.add_argument("--top-k", type=int, default=None,
                     help="override the headline workload's k (e.g. top-1 against top-2 inference)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -334,7 +336,7 @@ def run_leg(cfg, args, headline, want_backward, want_host_inputs):
     # sustained clock while the GEMMs run (headline only): enqueue about two
     # seconds of GEMM launches, read amd-smi from the host meanwhile
     clock = None
-    if headline:
+    if headline and not args.no_clock:
         n_busy = max(1, int(2.0 / max(ffn_s, 1e-6)))
         box = {}
         th = threading.Thread(target=lambda: (time.sleep(0.8), box.setdefault("c", gpu_clock_sample())))
