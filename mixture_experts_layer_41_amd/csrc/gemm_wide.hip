@@ -30,8 +30,13 @@
 //     side of the copy: chunk' = chunk ^ ((row / 4) % 4), so the 16 lanes of
 //     a fragment read hit 16 distinct 16-byte bank groups;
 //   * the weight fragment is the MFMA's first operand: each lane ends up with
-//     4 consecutive output columns of one row (8-byte stores through buffer
-//     resources whose range check drops rows past the group's end).
+//     4 consecutive output columns of one row;
+//   * the output tile leaves through LDS, a band of rows at a time, as
+//     16-byte stores of whole rows (full 128-byte lines) through buffer
+//     resources whose range check drops rows past the group's end.  Storing
+//     straight from the accumulators wrote 16 bytes per row per instruction,
+//     eight times the L2 write requests; those stores, which the next tile's
+//     first stage has to wait for, cost 10-20 % of the kernel's time.
 // What bounds it: the global -> LDS copies.  With the MFMAs removed the
 // copies and LDS reads alone take as long as the whole kernel; with every
 // tile reading the same (L2-resident) data the kernel gains only about 15 %.
@@ -89,6 +94,15 @@ __device__ __forceinline__ int lds_read_i32(const int* p, int i) {
 // compiler from moving memory accesses across it
 __device__ __forceinline__ void wg_barrier() {
   __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+// LDS accesses of this wave done, then a workgroup barrier (outstanding
+// global copies and stores are not waited for)
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
   __asm__ volatile("" ::: "memory");
 }
@@ -400,9 +414,14 @@ gemm_wide_kernel(GemmDesc p, int tiles_n) {
 
     // ---- epilogue.  acc[i][j] holds the transposed 32x32 block: lane l has
     // tile row i*32 + l%32 and output columns j*32 + 8*(q/4) + 4*(l/32) + q%4.
-    // Stores go through buffer resources that span the tile's valid rows, so
-    // a row past the group's end is dropped by the range check (no branch:
-    // the epilogue stays one block, read one row block at a time).
+    // The output tile leaves through LDS (stage buffer 3, free from the last
+    // stage's barrier until the next tile's first stage refills it): in each
+    // pass every wave writes its accumulators of IPP row blocks (bf16, 8
+    // bytes per lane, 16-byte chunks XOR-swizzled by row), then every lane
+    // stores 16-byte chunks of whole rows, so a wave's store covers full
+    // 128-byte lines.  Stores go through buffer resources that span the
+    // tile's valid rows: a row past the group's end is dropped by the range
+    // check.  Pre-activations (training) are stored from the registers.
     {
       const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
           out + tc.row0 * p.ldo, (short)0, (int)(tc.rows * p.ldo * 2), kBufFlags);
@@ -410,65 +429,98 @@ gemm_wide_kernel(GemmDesc p, int tiles_n) {
       if (KIND == kGemmUp && p.preact)
         rp = __builtin_amdgcn_make_buffer_rsrc(static_cast<uint16_t*>(p.preact) + tc.row0 * p.ldp,
                                               (short)0, (int)(tc.rows * p.ldp * 2), kBufFlags);
+      constexpr int OC = kSwiglu ? BN / 2 : BN;   // output columns of the tile
+      constexpr int NCH = OC / 8;                 // 16-byte chunks per output row
+      constexpr int IPP = (SCH * 16) / (32 * OC * 2);  // row blocks per pass (16 KB per wave row)
+      constexpr int NP = MI / IPP;                // passes
+      constexpr int RCH = SCH;                    // chunks per half band (16 KB)
+      static_assert(IPP >= 1 && MI % IPP == 0 && (2 * RCH) % NT == 0, "epilogue band");
+      const int col0 = (KIND == kGemmUp) ? tc.seg * f + tc.n0 : tc.n0;
+      char* band = reinterpret_cast<char*>(wm == 0 ? sA3 : sB3);  // this wave's half
+      // 4 values of output column oc (a multiple of 4) of band row lr
+      auto put = [&](int lr, int oc, const float* v) {
+        const u32x2 w = {(uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
+                         (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16)};
+        const int ch = (oc / 8) ^ (lr & (NCH - 1));
+        *reinterpret_cast<u32x2*>(band + lr * (OC * 2) + ch * 16 + (oc % 8) * 2) = w;
+      };
 #pragma unroll
-      for (int i = 0; i < MI; ++i) {
+      for (int q = 0; q < NP; ++q) {
         __builtin_amdgcn_sched_barrier(0);
-        const int r = wm * TM + i * 32 + fr;
-        const int orow = r * (int)p.ldo, prow = r * (int)p.ldp;
-        if (kSwiglu) {
 #pragma unroll
-          for (int j = 0; j < NI / 2; ++j) {
+        for (int ii = 0; ii < IPP; ++ii) {
+          const int i = q * IPP + ii;
+          const int lr = ii * 32 + fr;
+          const int r = wm * TM + i * 32 + fr;
+          const int prow = r * (int)p.ldp;
+          if (kSwiglu) {
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-              const int cidx = wn * (TN / 2) + j * 32 + 8 * g4 + 4 * half;
-              float hv[4], gv[4], uv[4];
+            for (int j = 0; j < NI / 2; ++j) {
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                gv[e] = acc[i][j][4 * g4 + e];
-                uv[e] = acc[i][j + NI / 2][4 * g4 + e];
-                if (BIAS) {
-                  const uint16_t* b = bias + ((int64_t)tc.group * S + tc.seg) * 2 * f;
-                  gv[e] += bf16_to_f32(b[tc.n0 + cidx + e]);
-                  uv[e] += bf16_to_f32(b[f + tc.n0 + cidx + e]);
+              for (int g4 = 0; g4 < 4; ++g4) {
+                const int cidx = wn * (TN / 2) + j * 32 + 8 * g4 + 4 * half;
+                float hv[4], gv[4], uv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  gv[e] = acc[i][j][4 * g4 + e];
+                  uv[e] = acc[i][j + NI / 2][4 * g4 + e];
+                  if (BIAS) {
+                    const uint16_t* b = bias + ((int64_t)tc.group * S + tc.seg) * 2 * f;
+                    gv[e] += bf16_to_f32(b[tc.n0 + cidx + e]);
+                    uv[e] += bf16_to_f32(b[f + tc.n0 + cidx + e]);
+                  }
+                  hv[e] = silu_f(gv[e]) * uv[e];
                 }
-                hv[e] = silu_f(gv[e]) * uv[e];
-              }
-              const int col = tc.seg * f + tc.n0 + cidx;
-              store4(ro, (orow + col) * 2, hv);
-              if (p.preact) {
-                const int pc = tc.seg * 2 * f + tc.n0 + cidx;
-                store4(rp, (prow + pc) * 2, gv);
-                store4(rp, (prow + pc + f) * 2, uv);
+                put(lr, cidx, hv);
+                if (p.preact) {
+                  const int pc = tc.seg * 2 * f + tc.n0 + cidx;
+                  store4(rp, (prow + pc) * 2, gv);
+                  store4(rp, (prow + pc + f) * 2, uv);
+                }
               }
             }
-          }
-        } else {
+          } else {
 #pragma unroll
-          for (int j = 0; j < NI; ++j) {
+            for (int j = 0; j < NI; ++j) {
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-              const int cidx = wn * TN + j * 32 + 8 * g4 + 4 * half;
-              float hv[4], pv[4];
+              for (int g4 = 0; g4 < 4; ++g4) {
+                const int cidx = wn * TN + j * 32 + 8 * g4 + 4 * half;
+                float hv[4], pv[4];
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                float v = acc[i][j][4 * g4 + e];
-                if (KIND == kGemmUp) {
-                  if (BIAS) v += bf16_to_f32(bias[((int64_t)tc.group * S + tc.seg) * f + tc.n0 + cidx + e]);
-                  pv[e] = v;
-                  hv[e] = gelu_f(v);
-                } else {
-                  if (BIAS)
-                    for (int s = 0; s < S; ++s)
-                      v += bf16_to_f32(bias[((int64_t)tc.group * S + s) * d + tc.n0 + cidx + e]);
-                  hv[e] = v;
+                for (int e = 0; e < 4; ++e) {
+                  float v = acc[i][j][4 * g4 + e];
+                  if (KIND == kGemmUp) {
+                    if (BIAS) v += bf16_to_f32(bias[((int64_t)tc.group * S + tc.seg) * f + tc.n0 + cidx + e]);
+                    pv[e] = v;
+                    hv[e] = gelu_f(v);
+                  } else {
+                    if (BIAS)
+                      for (int s = 0; s < S; ++s)
+                        v += bf16_to_f32(bias[((int64_t)tc.group * S + s) * d + tc.n0 + cidx + e]);
+                    hv[e] = v;
+                  }
                 }
+                put(lr, cidx, hv);
+                if (KIND == kGemmUp && p.preact) store4(rp, (prow + col0 + cidx) * 2, pv);
               }
-              const int col = (KIND == kGemmUp) ? tc.seg * f + tc.n0 + cidx : tc.n0 + cidx;
-              store4(ro, (orow + col) * 2, hv);
-              if (KIND == kGemmUp && p.preact) store4(rp, (prow + col) * 2, pv);
             }
           }
         }
+        lds_barrier();
+        // whole rows out: chunk c of the band (two halves of RCH chunks: the
+        // rows of wm = 0, then wm = 1)
+#pragma unroll
+        for (int u = 0; u < 2 * RCH / NT; ++u) {
+          const int c = tid + u * NT;
+          const int hb = c / RCH, lc = c % RCH;
+          const int lr = lc / NCH, cc = lc % NCH;
+          const char* src = reinterpret_cast<const char*>(hb == 0 ? sA3 : sB3) + lr * (OC * 2) +
+                            ((cc ^ (lr & (NCH - 1))) * 16);
+          const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+          const int trow = hb * TM + q * IPP * 32 + lr;
+          __builtin_amdgcn_raw_buffer_store_b128(v, ro, (trow * (int)p.ldo + col0 + cc * 8) * 2, 0, 0);
+        }
+        lds_barrier();
       }
     }
     if (!has_next) {
