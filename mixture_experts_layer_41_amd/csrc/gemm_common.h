@@ -94,7 +94,10 @@ __device__ inline int count_row_tiles(const int32_t* __restrict__ off, int n_gro
   return total;
 }
 
-__device__ __forceinline__ float silu_f(float g) { return g / (1.f + __expf(-g)); }
+// silu(g) = g sigmoid(g), the reciprocal from the hardware (1 ulp; the
+// quotient's full-precision division costs several times more in the
+// epilogues); 1 + e^-g >= 1 or +inf, so the reciprocal is finite or 0
+__device__ __forceinline__ float silu_f(float g) { return g * __builtin_amdgcn_rcpf(1.f + __expf(-g)); }
 
 // INT8 weight codes: 16 codes (one 16-byte load, code i in byte i) times the
 // row scale s, each product rounded to bfloat16 (nearest even), as two

@@ -290,57 +290,145 @@ __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo
 #undef MOE_TILE_STORE
 #undef MOE_TILE_COMPUTE
 
-  // epilogue (32x32 C layout: column lane%32, rows 8*(q/4) + 4*(lane/32) + q%4)
-  uint16_t* out = static_cast<uint16_t*>(p.out);
-  const uint16_t* bias = static_cast<const uint16_t*>(p.bias);
+  // epilogue.  The bf16 SwiGLU up GEMM and the down GEMMs stage the output
+  // tile through LDS; the GELU and INT8-scaled up GEMMs, whose epilogues
+  // would spill with the band addressing, store from the registers.
+  constexpr bool kStage = !(KIND == kGemmUp && (Q8 == 1 || !kSwiglu));
+  if constexpr (kStage) {
+    // 32x32 C layout: column lane%32, rows 8*(q/4) + 4*(lane/32) + q%4.
+    // The output tile goes through LDS (free since the K loop's last barrier):
+    // each lane writes its values (bf16) into a [BM][OC] band, output columns
+    // [0, 128) in sA's bytes and [128, 256) in sB's, 256-byte rows whose
+    // 16-byte chunks are XOR-swizzled by row; then every lane stores 16-byte
+    // chunks of whole rows (a 2-byte store per value would write 64 bytes of
+    // two rows per instruction).  Pre-activations are stored from the registers.
+    static_assert(BK == 64, "256-byte band rows in the LDS stages");
+    constexpr int OC = kSwiglu ? BN / 2 : BN;  // output columns of the tile
+    constexpr int NCH = OC / 8;                // 16-byte chunks per output row
+    static_assert(OC % 8 == 0 && OC <= 256 && (OC <= 128 || BN >= BM), "epilogue band");
+    static_assert((BM * NCH) % kTileThreads == 0, "epilogue band");
+    uint16_t* out = static_cast<uint16_t*>(p.out);
+    const uint16_t* bias = static_cast<const uint16_t*>(p.bias);
+    char* const bandA = reinterpret_cast<char*>(&sA[0][0]);
+    char* const bandB = reinterpret_cast<char*>(&sB[0][0]);
+    auto band_at = [&](int r, int c) -> char* {
+      const int cc = c % 128;
+      return (c < 128 ? bandA : bandB) + r * 256 + (((cc / 8) ^ (r & 15)) * 16) + (cc % 8) * 2;
+    };
 #pragma unroll
-  for (int i = 0; i < MI; ++i) {
+    for (int i = 0; i < MI; ++i) {
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int r = wm * TM + i * 32 + 8 * (q / 4) + 4 * half + (q % 4);
-      if (r >= tile.rows) continue;
-      const int64_t grow = tile.row0 + r;
-      if (kSwiglu) {
+      for (int q = 0; q < 16; ++q) {
+        const int r = wm * TM + i * 32 + 8 * (q / 4) + 4 * half + (q % 4);
+        const bool live = r < tile.rows;
+        const int64_t grow = tile.row0 + r;
+        if (kSwiglu) {
 #pragma unroll
-        for (int j = 0; j < NI / 2; ++j) {
-          const int cidx = wn * (TN / 2) + j * 32 + fr;
-          float g = acc[i][j][q], u = acc[i][j + NI / 2][q];
-          if constexpr (Q8 == 1) {
-            g *= esc[j];
-            u *= esc[j + NI / 2];
+          for (int j = 0; j < NI / 2; ++j) {
+            const int cidx = wn * (TN / 2) + j * 32 + fr;
+            float g = acc[i][j][q], u = acc[i][j + NI / 2][q];
+            if constexpr (Q8 == 1) {
+              g *= esc[j];
+              u *= esc[j + NI / 2];
+            }
+            if (BIAS) {
+              const uint16_t* b = bias + ((int64_t)tile.group * S + seg) * 2 * f;
+              g += bf16_to_f32(b[n0 + cidx]);
+              u += bf16_to_f32(b[f + n0 + cidx]);
+            }
+            *reinterpret_cast<uint16_t*>(band_at(r, cidx)) = f32_to_bf16(silu_f(g) * u);
+            if (p.preact && live) {
+              uint16_t* pa = static_cast<uint16_t*>(p.preact) + grow * p.ldp + (int64_t)seg * 2 * f + n0 + cidx;
+              pa[0] = f32_to_bf16(g);
+              pa[f] = f32_to_bf16(u);
+            }
           }
-          if (BIAS) {
-            const uint16_t* b = bias + ((int64_t)tile.group * S + seg) * 2 * f;
-            g += bf16_to_f32(b[n0 + cidx]);
-            u += bf16_to_f32(b[f + n0 + cidx]);
-          }
-          out[grow * p.ldo + (int64_t)seg * f + n0 + cidx] = f32_to_bf16(silu_f(g) * u);
-          if (p.preact) {
-            uint16_t* pa = static_cast<uint16_t*>(p.preact) + grow * p.ldp + (int64_t)seg * 2 * f + n0 + cidx;
-            pa[0] = f32_to_bf16(g);
-            pa[f] = f32_to_bf16(u);
-          }
-        }
-      } else {
+        } else {
 #pragma unroll
-        for (int j = 0; j < NI; ++j) {
-          const int cidx = wn * TN + j * 32 + fr;
-          float v = acc[i][j][q];
-          if constexpr (Q8 == 1) v *= esc[j];
-          if (KIND == kGemmUp) {
-            if (BIAS) v += bf16_to_f32(bias[((int64_t)tile.group * S + seg) * f + n0 + cidx]);
-            if (p.preact)
-              static_cast<uint16_t*>(p.preact)[grow * p.ldp + (int64_t)seg * f + n0 + cidx] = f32_to_bf16(v);
-            out[grow * p.ldo + (int64_t)seg * f + n0 + cidx] = f32_to_bf16(gelu_f(v));
-          } else {
-            if (BIAS)
-              for (int s = 0; s < S; ++s)
-                v += bf16_to_f32(bias[((int64_t)tile.group * S + s) * d + n0 + cidx]);
-            out[grow * p.ldo + n0 + cidx] = f32_to_bf16(v);
+          for (int j = 0; j < NI; ++j) {
+            const int cidx = wn * TN + j * 32 + fr;
+            float v = acc[i][j][q];
+            if constexpr (Q8 == 1) v *= esc[j];
+            if (KIND == kGemmUp) {
+              if (BIAS) v += bf16_to_f32(bias[((int64_t)tile.group * S + seg) * f + n0 + cidx]);
+              if (p.preact && live)
+                static_cast<uint16_t*>(p.preact)[grow * p.ldp + (int64_t)seg * f + n0 + cidx] = f32_to_bf16(v);
+              *reinterpret_cast<uint16_t*>(band_at(r, cidx)) = f32_to_bf16(gelu_f(v));
+            } else {
+              if (BIAS)
+                for (int s = 0; s < S; ++s)
+                  v += bf16_to_f32(bias[((int64_t)tile.group * S + s) * d + n0 + cidx]);
+              *reinterpret_cast<uint16_t*>(band_at(r, cidx)) = f32_to_bf16(v);
+            }
           }
         }
       }
     }
+    __syncthreads();
+    const int64_t col0 = (KIND == kGemmUp) ? (int64_t)seg * f + n0 : n0;
+#pragma unroll
+    for (int u = 0; u < BM * NCH / kTileThreads; ++u) {
+      const int c = tid + u * kTileThreads;
+      const int r = c / NCH, cc = c % NCH;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(band_at(r, cc * 8));
+      if (r < tile.rows) *reinterpret_cast<u32x4*>(out + (tile.row0 + r) * p.ldo + col0 + cc * 8) = v;
+    }
+    __syncthreads();  // the band is read before the next tile's loads land in LDS
+
+  } else {
+    // epilogue (32x32 C layout: column lane%32, rows 8*(q/4) + 4*(lane/32) + q%4)
+    uint16_t* out = static_cast<uint16_t*>(p.out);
+    const uint16_t* bias = static_cast<const uint16_t*>(p.bias);
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int r = wm * TM + i * 32 + 8 * (q / 4) + 4 * half + (q % 4);
+        if (r >= tile.rows) continue;
+        const int64_t grow = tile.row0 + r;
+        if (kSwiglu) {
+#pragma unroll
+          for (int j = 0; j < NI / 2; ++j) {
+            const int cidx = wn * (TN / 2) + j * 32 + fr;
+            float g = acc[i][j][q], u = acc[i][j + NI / 2][q];
+            if constexpr (Q8 == 1) {
+              g *= esc[j];
+              u *= esc[j + NI / 2];
+            }
+            if (BIAS) {
+              const uint16_t* b = bias + ((int64_t)tile.group * S + seg) * 2 * f;
+              g += bf16_to_f32(b[n0 + cidx]);
+              u += bf16_to_f32(b[f + n0 + cidx]);
+            }
+            out[grow * p.ldo + (int64_t)seg * f + n0 + cidx] = f32_to_bf16(silu_f(g) * u);
+            if (p.preact) {
+              uint16_t* pa = static_cast<uint16_t*>(p.preact) + grow * p.ldp + (int64_t)seg * 2 * f + n0 + cidx;
+              pa[0] = f32_to_bf16(g);
+              pa[f] = f32_to_bf16(u);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < NI; ++j) {
+            const int cidx = wn * TN + j * 32 + fr;
+            float v = acc[i][j][q];
+            if constexpr (Q8 == 1) v *= esc[j];
+            if (KIND == kGemmUp) {
+              if (BIAS) v += bf16_to_f32(bias[((int64_t)tile.group * S + seg) * f + n0 + cidx]);
+              if (p.preact)
+                static_cast<uint16_t*>(p.preact)[grow * p.ldp + (int64_t)seg * f + n0 + cidx] = f32_to_bf16(v);
+              out[grow * p.ldo + (int64_t)seg * f + n0 + cidx] = f32_to_bf16(gelu_f(v));
+            } else {
+              if (BIAS)
+                for (int s = 0; s < S; ++s)
+                  v += bf16_to_f32(bias[((int64_t)tile.group * S + s) * d + n0 + cidx]);
+              out[grow * p.ldo + n0 + cidx] = f32_to_bf16(v);
+            }
+          }
+        }
+      }
+    }
+
   }
 }
 
@@ -564,6 +652,8 @@ int pick_tile_variant(const moe_config& c, GemmKind kind, const GemmDesc& g, int
   auto fits = [&](int v) {
     const TileCfg& tc = kTiles[v];
     if (g.w_scale && v >= kFirstPipe) return false;  // INT8 weights: register-staged tiles only
+    // 16-byte output stores
+    if (g.ldo % 8 != 0 || reinterpret_cast<uintptr_t>(g.out) % 16 != 0) return false;
     if (v == kWide) return wide_fits(kind, g);
     if (K % tc.bk != 0) return false;
     const int ncol = kind == kGemmUp ? (swiglu ? tc.bn / 2 : tc.bn) : tc.bn;

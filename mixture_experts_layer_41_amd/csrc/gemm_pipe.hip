@@ -15,7 +15,9 @@
 //     of its next tile are issued while the current tile finishes, so the
 //     epilogue and the next tile's first loads overlap;
 //   * the MFMA takes the weight fragment as its first operand, so each lane
-//     ends up with 4 consecutive output columns of one row (8-byte stores);
+//     ends up with 4 consecutive output columns of one row; the output tile
+//     then leaves through LDS as 16-byte stores of whole rows (the training
+//     forward's SwiGLU variant stores from the registers, lane pairs joined);
 //   * LDS rows (64 bytes) are XOR-swizzled in 16-byte chunks on the global
 //     side of the copy: chunk' = chunk ^ ((row / 4) % 4).  A fragment read
 //     (16 lanes, 16 consecutive rows, one chunk each) then touches 16
@@ -65,6 +67,15 @@ __device__ __forceinline__ int lds_read_i32(const int* p, int i) {
 // from moving memory accesses across it.
 __device__ __forceinline__ void wg_barrier() {
   __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+// this wave's LDS accesses done, then a workgroup barrier (global copies and
+// stores in flight are not waited for)
+__device__ __forceinline__ void wait_lgkm_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
   __asm__ volatile("" ::: "memory");
 }
@@ -405,12 +416,14 @@ gemm_pipe_kernel(GemmDesc p, int tiles_n) {
 
     // ---- epilogue.  acc[i][j] holds the transposed 32x32 block: lane l has
     // tile row i*32 + l%32 and output columns j*32 + 8*(q/4) + 4*(l/32) + q%4.
+    if constexpr (kSwiglu && PAIRED) {
+      // training forward (pre-activations too): 16-byte stores from the
+      // registers, lane pairs l, l ^ 32 joining their 4-column halves
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      const int r = wm * TM + i * 32 + fr;
-      if (r < tc.rows) {
-        const int64_t grow = tc.row0 + r;
-        if constexpr (kSwiglu && PAIRED) {
+      for (int i = 0; i < MI; ++i) {
+        const int r = wm * TM + i * 32 + fr;
+        if (r < tc.rows) {
+          const int64_t grow = tc.row0 + r;
           // lane l keeps its own half of runs 0, 2 (lower 32 lanes) or 1, 3
           // (upper), gives the partner its half of the other two runs and
           // stores 16 bytes per run it keeps
@@ -457,71 +470,124 @@ gemm_pipe_kernel(GemmDesc p, int tiles_n) {
               *reinterpret_cast<uint4*>(pa + f) = run(uw);
             }
           }
-        } else if (kSwiglu) {
+        }
+      }
+    } else {
+      // The output tile leaves through LDS (the last stage's buffers, free
+      // until the next tile's first step refills them): each pass, every
+      // wave writes IPP of its row blocks (bf16, 8 bytes per lane, 16-byte
+      // chunks XOR-swizzled by row), then the workgroup stores 16-byte chunks
+      // of whole rows, so a wave's store covers full 128-byte lines (storing
+      // from the accumulators writes 16 bytes of 32 rows per instruction).
+      static_assert(WM == 2, "two half bands");
+      constexpr int OC = kSwiglu ? BN / 2 : BN;  // output columns of the tile
+      constexpr int NCH = OC / 8;                // 16-byte chunks per output row
+      constexpr int HB = (BM < BN ? BM : BN) * CPR * 16;  // bytes per half band
+      constexpr int IPP0 = HB / (32 * OC * 2);
+      constexpr int IPP = IPP0 > MI ? MI : IPP0;  // row blocks per pass
+      constexpr int NP = MI / IPP;                // passes
+      constexpr int RCH = IPP * 32 * NCH;         // chunks per half band
+      // swizzle key: rows sharing a 256-byte bank window get distinct keys
+      constexpr int RPWIN = OC * 2 >= 256 ? 1 : 256 / (OC * 2);
+      static_assert(IPP >= 1 && MI % IPP == 0 && (2 * RCH) % NT == 0, "epilogue band");
+      char* hb0;
+      char* hb1;
+      if constexpr (NS == 4) {
+        hb0 = reinterpret_cast<char*>(sA3);
+        hb1 = reinterpret_cast<char*>(sB3);
+      } else {
+        hb0 = reinterpret_cast<char*>(sA7);
+        hb1 = reinterpret_cast<char*>(sB7);
+      }
+      char* band = wm == 0 ? hb0 : hb1;
+      const int64_t col0 = (KIND == kGemmUp) ? (int64_t)tc.seg * f + tc.n0 : tc.n0;
+      auto put = [&](int lr, int oc, const uint16_t* h) {
+        const uint2 w = {(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+        const int ch = (oc / 8) ^ ((lr / RPWIN) & (NCH - 1));
+        *reinterpret_cast<uint2*>(band + lr * (OC * 2) + ch * 16 + (oc % 8) * 2) = w;
+      };
 #pragma unroll
-          for (int j = 0; j < NI / 2; ++j) {
+      for (int q = 0; q < NP; ++q) {
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-              const int cidx = wn * (TN / 2) + j * 32 + 8 * g4 + 4 * half;
-              uint16_t h[4], pg[4], pu[4];
+        for (int ii = 0; ii < IPP; ++ii) {
+          const int i = q * IPP + ii;
+          const int lr = ii * 32 + fr;
+          const int r = wm * TM + i * 32 + fr;
+          const int64_t grow = tc.row0 + r;
+          const bool live = r < tc.rows;
+          if (kSwiglu) {
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                float gv = acc[i][j][4 * g4 + e], uv = acc[i][j + NI / 2][4 * g4 + e];
-                if (BIAS) {
-                  const uint16_t* b = bias + ((int64_t)tc.group * S + tc.seg) * 2 * f;
-                  gv += bf16_to_f32(b[tc.n0 + cidx + e]);
-                  uv += bf16_to_f32(b[f + tc.n0 + cidx + e]);
+            for (int j = 0; j < NI / 2; ++j) {
+#pragma unroll
+              for (int g4 = 0; g4 < 4; ++g4) {
+                const int cidx = wn * (TN / 2) + j * 32 + 8 * g4 + 4 * half;
+                uint16_t h[4], pg[4], pu[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  float gv = acc[i][j][4 * g4 + e], uv = acc[i][j + NI / 2][4 * g4 + e];
+                  if (BIAS) {
+                    const uint16_t* b = bias + ((int64_t)tc.group * S + tc.seg) * 2 * f;
+                    gv += bf16_to_f32(b[tc.n0 + cidx + e]);
+                    uv += bf16_to_f32(b[f + tc.n0 + cidx + e]);
+                  }
+                  h[e] = f32_to_bf16(silu_f(gv) * uv);
+                  pg[e] = f32_to_bf16(gv);
+                  pu[e] = f32_to_bf16(uv);
                 }
-                h[e] = f32_to_bf16(silu_f(gv) * uv);
-                pg[e] = f32_to_bf16(gv);
-                pu[e] = f32_to_bf16(uv);
-              }
-              uint2 v;
-              v.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
-              v.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
-              *reinterpret_cast<uint2*>(out + grow * p.ldo + (int64_t)tc.seg * f + tc.n0 + cidx) = v;
-              if (p.preact) {
-                uint16_t* pa = static_cast<uint16_t*>(p.preact) + grow * p.ldp +
-                               (int64_t)tc.seg * 2 * f + tc.n0 + cidx;
-                *reinterpret_cast<uint2*>(pa) =
-                    uint2{(uint32_t)pg[0] | ((uint32_t)pg[1] << 16), (uint32_t)pg[2] | ((uint32_t)pg[3] << 16)};
-                *reinterpret_cast<uint2*>(pa + f) =
-                    uint2{(uint32_t)pu[0] | ((uint32_t)pu[1] << 16), (uint32_t)pu[2] | ((uint32_t)pu[3] << 16)};
+                put(lr, cidx, h);
+                if (p.preact && live) {
+                  uint16_t* pa = static_cast<uint16_t*>(p.preact) + grow * p.ldp +
+                                 (int64_t)tc.seg * 2 * f + tc.n0 + cidx;
+                  *reinterpret_cast<uint2*>(pa) =
+                      uint2{(uint32_t)pg[0] | ((uint32_t)pg[1] << 16), (uint32_t)pg[2] | ((uint32_t)pg[3] << 16)};
+                  *reinterpret_cast<uint2*>(pa + f) =
+                      uint2{(uint32_t)pu[0] | ((uint32_t)pu[1] << 16), (uint32_t)pu[2] | ((uint32_t)pu[3] << 16)};
+                }
               }
             }
-          }
-        } else {
+          } else {
 #pragma unroll
-          for (int j = 0; j < NI; ++j) {
+            for (int j = 0; j < NI; ++j) {
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-              const int cidx = wn * TN + j * 32 + 8 * g4 + 4 * half;
-              uint16_t h[4], pv[4];
+              for (int g4 = 0; g4 < 4; ++g4) {
+                const int cidx = wn * TN + j * 32 + 8 * g4 + 4 * half;
+                uint16_t h[4], pv[4];
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                float v = acc[i][j][4 * g4 + e];
-                if (KIND == kGemmUp) {
-                  if (BIAS) v += bf16_to_f32(bias[((int64_t)tc.group * S + tc.seg) * f + tc.n0 + cidx + e]);
-                  pv[e] = f32_to_bf16(v);
-                  h[e] = f32_to_bf16(gelu_f(v));
-                } else {
-                  if (BIAS)
-                    for (int s = 0; s < S; ++s)
-                      v += bf16_to_f32(bias[((int64_t)tc.group * S + s) * d + tc.n0 + cidx + e]);
-                  h[e] = f32_to_bf16(v);
+                for (int e = 0; e < 4; ++e) {
+                  float v = acc[i][j][4 * g4 + e];
+                  if (KIND == kGemmUp) {
+                    if (BIAS) v += bf16_to_f32(bias[((int64_t)tc.group * S + tc.seg) * f + tc.n0 + cidx + e]);
+                    pv[e] = f32_to_bf16(v);
+                    h[e] = f32_to_bf16(gelu_f(v));
+                  } else {
+                    if (BIAS)
+                      for (int s = 0; s < S; ++s)
+                        v += bf16_to_f32(bias[((int64_t)tc.group * S + s) * d + tc.n0 + cidx + e]);
+                    h[e] = f32_to_bf16(v);
+                  }
                 }
+                put(lr, cidx, h);
+                if (KIND == kGemmUp && p.preact && live)
+                  *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.preact) + grow * p.ldp + col0 + cidx) =
+                      uint2{(uint32_t)pv[0] | ((uint32_t)pv[1] << 16), (uint32_t)pv[2] | ((uint32_t)pv[3] << 16)};
               }
-              uint2 v;
-              v.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
-              v.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
-              const int64_t col = (KIND == kGemmUp) ? (int64_t)tc.seg * f + tc.n0 + cidx : tc.n0 + cidx;
-              *reinterpret_cast<uint2*>(out + grow * p.ldo + col) = v;
-              if (KIND == kGemmUp && p.preact)
-                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.preact) + grow * p.ldp + col) =
-                    uint2{(uint32_t)pv[0] | ((uint32_t)pv[1] << 16), (uint32_t)pv[2] | ((uint32_t)pv[3] << 16)};
             }
           }
         }
+        wait_lgkm_barrier();
+        // whole rows out: chunk c of the band (the rows of wm = 0, then wm = 1)
+#pragma unroll
+        for (int u = 0; u < 2 * RCH / NT; ++u) {
+          const int c = tid + u * NT;
+          const int hb = c / RCH, lc = c % RCH;
+          const int lr = lc / NCH, cc = lc % NCH;
+          const u32x4 v = *reinterpret_cast<const u32x4*>((hb == 0 ? hb0 : hb1) + lr * (OC * 2) +
+                                                          ((cc ^ ((lr / RPWIN) & (NCH - 1))) * 16));
+          const int trow = hb * TM + q * IPP * 32 + lr;
+          if (trow < tc.rows)
+            *reinterpret_cast<u32x4*>(out + (tc.row0 + trow) * p.ldo + col0 + cc * 8) = v;
+        }
+        wait_lgkm_barrier();
       }
     }
     if (!has_next) {
@@ -607,6 +673,8 @@ bool pipe_shape_fits(GemmKind kind, const GemmDesc& g, int bm, int bn, int stage
   if (nk % stages != 0) return false;
   const int ncol = kind == kGemmUp ? (swiglu ? bn / 2 : bn) : bn;
   const int width = kind == kGemmUp ? g.f : g.d;
+  // 16-byte output stores
+  if (g.ldo % 8 != 0 || reinterpret_cast<uintptr_t>(g.out) % 16 != 0) return false;
   return width % ncol == 0;
 }
 

@@ -435,6 +435,7 @@ gemm_wide_kernel(GemmDesc p, int tiles_n) {
       constexpr int NP = MI / IPP;                // passes
       constexpr int RCH = SCH;                    // chunks per half band (16 KB)
       static_assert(IPP >= 1 && MI % IPP == 0 && (2 * RCH) % NT == 0, "epilogue band");
+      static_assert(OC * 2 >= 256, "a row per 256-byte bank window at least (swizzle key = row)");
       const int col0 = (KIND == kGemmUp) ? tc.seg * f + tc.n0 : tc.n0;
       char* band = reinterpret_cast<char*>(wm == 0 ? sA3 : sB3);  // this wave's half
       // 4 values of output column oc (a multiple of 4) of band row lr
@@ -593,6 +594,8 @@ bool wide_fits(GemmKind kind, const GemmDesc& g) {
   // the epilogue's 32-bit buffer offsets: 256 rows of output (and
   // pre-activations) stay below 2 GiB
   if (g.ldo >= ((int64_t)1 << 22) || (g.preact && g.ldp >= ((int64_t)1 << 22))) return false;
+  // 16-byte output stores
+  if (g.ldo % 8 != 0 || reinterpret_cast<uintptr_t>(g.out) % 16 != 0) return false;
   const bool swiglu = kind == kGemmUp && g.act == MOE_ACT_SWIGLU;
   const int K = kind == kGemmUp ? g.d : g.f;
   if (K % wide::BK != 0) return false;
