@@ -71,15 +71,6 @@ __device__ __forceinline__ void wg_barrier() {
   __asm__ volatile("" ::: "memory");
 }
 
-// this wave's LDS accesses done, then a workgroup barrier (global copies and
-// stores in flight are not waited for)
-__device__ __forceinline__ void wait_lgkm_barrier() {
-  __asm__ volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  __asm__ volatile("" ::: "memory");
-}
-
 // s_waitcnt vmcnt(N) (expcnt and lgkmcnt left at their maxima).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -574,7 +565,7 @@ gemm_pipe_kernel(GemmDesc p, int tiles_n) {
             }
           }
         }
-        wait_lgkm_barrier();
+        lds_barrier();
         // whole rows out: chunk c of the band (the rows of wm = 0, then wm = 1)
 #pragma unroll
         for (int u = 0; u < 2 * RCH / NT; ++u) {
@@ -587,7 +578,7 @@ gemm_pipe_kernel(GemmDesc p, int tiles_n) {
           if (trow < tc.rows)
             *reinterpret_cast<u32x4*>(out + (tc.row0 + trow) * p.ldo + col0 + cc * 8) = v;
         }
-        wait_lgkm_barrier();
+        lds_barrier();
       }
     }
     if (!has_next) {

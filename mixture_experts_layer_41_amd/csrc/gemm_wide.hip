@@ -98,15 +98,6 @@ __device__ __forceinline__ void wg_barrier() {
   __asm__ volatile("" ::: "memory");
 }
 
-// LDS accesses of this wave done, then a workgroup barrier (outstanding
-// global copies and stores are not waited for)
-__device__ __forceinline__ void lds_barrier() {
-  __asm__ volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  __asm__ volatile("" ::: "memory");
-}
-
 // s_waitcnt vmcnt(N) lgkmcnt(0)
 template <int N>
 __device__ __forceinline__ void wait_vm_lgkm() {

@@ -21,6 +21,8 @@
 //  * selection: 256 / BT lanes per token, each holding its share of the
 //    token's logits as order keys in registers; max, sum of exponentials
 //    and each of the k picks end in DPP reductions inside that lane group.
+//  * barriers order LDS data only (lds_barrier): no workgroup reads back
+//    global memory it has written, so no barrier waits for stores;
 //  * scores: everything after the logits GEMM sees
 //    s = (logit + bias) / tau + noise ([P2 §5.1] temperature scaling,
 //    [P2 §2.2] noise added before the top-k); with tau = 1 and no noise these
@@ -302,7 +304,7 @@ __device__ void select_and_stats_t(float* lg, int ep, int BT, int nvalid, int E,
   const float iz = 1.f / z;
   if (valid)
     for (int e = sub; e < E; e += G) row[e] = expf(row[e] - m) * iz;
-  __syncthreads();
+  lds_barrier();
 
   for (int e = threadIdx.x; e < E; e += kThreads) {
     float acc = 0.f;
@@ -364,7 +366,7 @@ router_kernel(const void* __restrict__ x, const void* __restrict__ wr,
                      s, part);
   else
     logits_f32(static_cast<const float*>(x), static_cast<const float*>(wr), T, d, E, t0, s, part);
-  __syncthreads();
+  lds_barrier();
   // sum the K slices in a fixed order and add the bias
   for (int o = threadIdx.x; o < BT * E; o += kThreads) {
     const int r = o / E, e = o % E;
@@ -374,7 +376,7 @@ router_kernel(const void* __restrict__ x, const void* __restrict__ wr,
     lg[r * (ep + 1) + e] = sc;
     if (mod.scores_out && t0 + r < T) mod.scores_out[(t0 + r) * E + e] = sc;
   }
-  __syncthreads();
+  lds_barrier();
 
   if (DT == MOE_DTYPE_BF16)
     select_and_stats_t<(4 * TPW < 64 ? 4 * TPW : 64)>(lg, ep, BT, nvalid, E, k, t0, blk, topk_idx,
@@ -513,7 +515,7 @@ router_bf16_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
     MOE_ROUTER_LOAD(c0);
     MOE_ROUTER_STORE(stage0);
   }
-  __syncthreads();
+  lds_barrier();
   for (int c = c0; c < c1; ++c) {
     u32x4* cur = ((c - c0) & 1) ? stage1 : stage0;
     u32x4* nxt = ((c - c0) & 1) ? stage0 : stage1;
@@ -534,7 +536,7 @@ router_bf16_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
       }
     }
     if (c + 1 < c1) MOE_ROUTER_STORE(nxt);
-    __syncthreads();
+    lds_barrier();
   }
 
 #undef MOE_ROUTER_LOAD
@@ -551,7 +553,7 @@ router_bf16_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
       pk[(tb * 16 + 4 * (lane / 16) + r) * (ep + 1) + eb * 16 + (lane % 16)] = acc[i][r];
   }
   for (int e = tid; e < ep; e += kThreads) cnt[e] = 0;
-  __syncthreads();
+  lds_barrier();
   float* lg = part;  // wave-split slice 0 receives the sum
   if (s.ks > 1) {
     // K split over workgroups: this split's partial logits go out, in
@@ -572,7 +574,7 @@ router_bf16_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
     lg[r * (ep + 1) + e] = sc;
     if (mod.scores_out && t0 + r < T) mod.scores_out[(t0 + r) * E + e] = sc;
   }
-  __syncthreads();
+  lds_barrier();
   select_and_stats_t<(4 * TPW < 64 ? 4 * TPW : 64)>(lg, ep, BT, nvalid, E, k, t0, blk, topk_idx,
                                                     topk_w, token_lse, st_cnt, st_psum, st_zsum,
                                                     cnt, lse2);
@@ -627,7 +629,7 @@ router_select_kernel(const float* __restrict__ part_in, int nsplit, const Router
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
   select_and_stats_any(lg, ep, BT, nvalid, E, k, t0, blk, topk_idx, topk_w, token_lse, st_cnt,
                        st_psum, st_zsum, cnt, lse2);
 }
