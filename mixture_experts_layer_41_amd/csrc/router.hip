@@ -216,7 +216,7 @@ __device__ inline void sum_step(float& z) {
 // then a group arg-max in the order (logit descending, index ascending); the
 // winner's key is then cleared in its owner lane.
 template <int NPL>
-__device__ void select_and_stats_t(float* lg, int ep, int BT, int nvalid, int E, int k, int64_t t0,
+__device__ __forceinline__ void select_and_stats_t(float* lg, int ep, int BT, int nvalid, int E, int k, int64_t t0,
                                    int64_t blk, int32_t* __restrict__ topk_idx,
                                    float* __restrict__ topk_w, float* __restrict__ token_lse,
                                    int32_t* __restrict__ st_cnt, float* __restrict__ st_psum,
@@ -385,6 +385,180 @@ router_kernel(const void* __restrict__ x, const void* __restrict__ wr,
   else
     select_and_stats_any(lg, ep, BT, nvalid, E, k, t0, blk, topk_idx, topk_w, token_lse, st_cnt,
                          st_psum, st_zsum, cnt, lse2);
+}
+
+// ---------------------------------------------------------------------------
+// bfloat16 router for batches that fill the chip, logits through a deep LDS
+// pipeline.  Same workgroup, tiles and selection as router_kernel, but the
+// x rows and the W_r rows of each 64-wide K chunk are copied straight into
+// an LDS stage (16-byte direct copies, 8 lanes per 128-byte row: every copy
+// covers 8 whole lines), kStagedNS stages deep, and the MFMA fragments are
+// read from LDS: W_r is fetched once per workgroup instead of once per wave,
+// and each wave keeps two chunks of copies in flight under the MFMAs.
+// Stage rows: the BT token rows, then the ep expert rows (padding experts
+// repeat expert 0; their logits are never read).  16-byte chunk c of row r
+// sits at chunk c ^ ((r / 2) % 8): a fragment read (16 consecutive rows, one
+// chunk) then hits 16 distinct 16-byte bank groups.
+constexpr int kStagedNS = 3;
+
+__host__ __device__ inline bool router_staged_fits(const RouterShape& s, int d) {
+  return s.nks == 1 && d % 64 == 0 && (s.BT + s.ep) % 32 == 0 && s.ep <= 128;
+}
+__host__ __device__ inline int router_staged_smem_bytes(const RouterShape& s) {
+  return kStagedNS * (s.BT + s.ep) * 128 + s.BT * (s.ep + 1) * 4 + s.ep * 4 + s.BT * 4;
+}
+
+// s_waitcnt vmcnt(n) lgkmcnt(0) for a wave-uniform n in [0, 15]
+__device__ __forceinline__ void wait_vm_lgkm_dyn(int n) {
+  __asm__ volatile("" ::: "memory");
+  switch (n) {
+#define MOE_W(N) case N: __builtin_amdgcn_s_waitcnt(0x0070 | N); break;
+    MOE_W(0) MOE_W(1) MOE_W(2) MOE_W(3) MOE_W(4) MOE_W(5) MOE_W(6) MOE_W(7)
+    MOE_W(8) MOE_W(9) MOE_W(10) MOE_W(11) MOE_W(12) MOE_W(13) MOE_W(14)
+#undef MOE_W
+    default: __builtin_amdgcn_s_waitcnt(0x0070 | 15); break;
+  }
+  __asm__ volatile("" ::: "memory");
+}
+
+template <int TPW>
+__global__ void __launch_bounds__(kThreads, 2)
+router_staged_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+                     const RouterMod mod, int64_t T, int d, int E, int k,
+                     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+                     float* __restrict__ token_lse, int32_t* __restrict__ st_cnt,
+                     float* __restrict__ st_psum, float* __restrict__ st_zsum) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const RouterShape s = router_shape(T, E, true);
+  const int BT = s.BT, ep = s.ep;
+  const int rows = BT + ep;                 // rows per stage (128 bytes each)
+  const int64_t blk = blockIdx.x;
+  const int64_t t0 = blk * BT;
+  const int nvalid = (int)((T - t0) < BT ? (T - t0) : BT);
+  u32x4* stages = reinterpret_cast<u32x4*>(smem);
+  float* part = reinterpret_cast<float*>(smem + kStagedNS * rows * 128);
+  int32_t* cnt = reinterpret_cast<int32_t*>(part + BT * (ep + 1));
+  float* lse2 = reinterpret_cast<float*>(cnt + ep);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+  const int nch = d / 64;
+
+  // copies: instruction q covers stage rows 8q .. 8q + 7; wave w issues
+  // q = w, w + 4, ... (lpw per wave); lane i -> row 8q + i / 8, LDS chunk
+  // i % 8, global chunk (i % 8) ^ ((row / 2) % 8)
+  const int lpw = rows / 32;
+  constexpr int kMaxLpw = 6;                // rows <= 64 + 128
+  const uint16_t* src[kMaxLpw];
+#pragma unroll
+  for (int i = 0; i < kMaxLpw; ++i) {
+    const int q = wave + 4 * i;
+    const int r = 8 * q + lane / 8;
+    const int gc = (lane % 8) ^ ((r / 2) % 8);
+    const uint16_t* rowp;
+    if (r < BT) {
+      int64_t tok = t0 + r;
+      if (tok >= T) tok = T - 1;
+      rowp = x + tok * (int64_t)d;
+    } else {
+      const int e = r - BT;
+      rowp = wr + (int64_t)(e < E ? e : 0) * d;
+    }
+    src[i] = rowp + gc * 8;
+  }
+  auto issue = [&](int c) {
+    u32x4* st = stages + (c % kStagedNS) * rows * 8;
+#pragma unroll
+    for (int i = 0; i < kMaxLpw; ++i)
+      if (i < lpw)
+        __builtin_amdgcn_global_load_lds(src[i] + (int64_t)c * 64, st + (wave + 4 * i) * 64, 16, 0, 0);
+  };
+
+  // tiles of this wave (as in logits_bf16): t = wave + 4 i, token block
+  // t % n_tb (the same for all of the wave's tiles), expert block t / n_tb
+  const int tb = wave % s.n_tb;
+  const int ra = tb * 16 + lane % 16;       // A fragment row (stage row)
+  const int ka = ((ra / 2) % 8);
+  int rb[TPW], kb[TPW];
+  bool tok_ok[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int t = wave + 4 * i;
+    tok_ok[i] = t < s.n_tiles;
+    rb[i] = BT + (tok_ok[i] ? t / s.n_tb : 0) * 16 + lane % 16;
+    kb[i] = (rb[i] / 2) % 8;
+  }
+  f32x4 acc[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int e = threadIdx.x; e < ep; e += kThreads) cnt[e] = 0;
+  // prologue: chunks 0 .. NS-2 in flight, chunk 0 landed
+  for (int c = 0; c < kStagedNS - 1; ++c)
+    if (c < nch) issue(c);
+  wait_vm_lgkm_dyn(nch > 1 ? lpw : 0);
+  lds_barrier();
+  for (int c = 0; c < nch; ++c) {
+    if (c + kStagedNS - 1 < nch) issue(c + kStagedNS - 1);
+    const u32x4* st = stages + (c % kStagedNS) * rows * 8;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      // 16-byte chunk of this lane in the 32-wide K step: 4 ks + lane / 16
+      const int ch = 4 * ks + lane / 16;
+      const u32x4 a = st[ra * 8 + (ch ^ ka)];
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        if (!tok_ok[i]) continue;
+        const u32x4 b = st[rb[i] * 8 + (ch ^ kb[i])];
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                         __builtin_bit_cast(bf16x8, b), acc[i], 0, 0, 0);
+      }
+    }
+    // chunk c + 1 landed (the copies of chunk c + 2 may stay in flight);
+    // every wave done with chunk c's stage before the next step refills it
+    const int after = c + kStagedNS - 1 < nch ? lpw : 0;
+    wait_vm_lgkm_dyn(c + 1 < nch ? after : 0);
+    lds_barrier();
+  }
+  // 16x16 C layout: lane holds token rows 4*(lane/16) + r, expert column lane%16
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    if (!tok_ok[i]) continue;
+    const int eb = (wave + 4 * i) / s.n_tb;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      part[(tb * 16 + 4 * (lane / 16) + r) * (ep + 1) + eb * 16 + (lane % 16)] = acc[i][r];
+  }
+  lds_barrier();
+  float* lg = part;
+  for (int o = threadIdx.x; o < BT * E; o += kThreads) {
+    const int r = o / E, e = o % E;
+    const float sc = router_score(lg[r * (ep + 1) + e], mod, t0 + r, T, E, e);
+    lg[r * (ep + 1) + e] = sc;
+    if (mod.scores_out && t0 + r < T) mod.scores_out[(t0 + r) * E + e] = sc;
+  }
+  lds_barrier();
+  select_and_stats_t<(4 * TPW < 64 ? 4 * TPW : 64)>(lg, ep, BT, nvalid, E, k, t0, blk, topk_idx,
+                                                    topk_w, token_lse, st_cnt, st_psum, st_zsum,
+                                                    cnt, lse2);
+}
+
+template <int TPW>
+hipError_t router_staged_launch(const moe_config& c, const void* x, const void* w_router,
+                                const RouterMod& mod, int32_t* topk_idx, float* topk_w,
+                                float* token_lse, const RouteStats& st, hipStream_t s) {
+  const RouterShape sh = router_shape(c.n_tokens, c.n_experts, true);
+  const int64_t nb = (c.n_tokens + sh.BT - 1) / sh.BT;
+  const int smem = router_staged_smem_bytes(sh);
+  auto fn = router_staged_kernel<TPW>;
+  if (smem > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    if (e != hipSuccess) return e;
+  }
+  fn<<<dim3((unsigned)nb), dim3(kThreads), smem, s>>>(
+      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router), mod, c.n_tokens,
+      c.d_model, c.n_experts, c.top_k, topk_idx, topk_w, token_lse, st.cnt, st.psum, st.zsum);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -708,7 +882,15 @@ hipError_t launch_router(const moe_config& c, const void* x, const void* w_route
 #undef MOE_ROUTER2_CASE
     return hipErrorInvalidConfiguration;
   }
-  const int tpw = router_shape(c.n_tokens, c.n_experts, true).tiles_per_wave;
+  const RouterShape rs = router_shape(c.n_tokens, c.n_experts, true);
+  const int tpw = rs.tiles_per_wave;
+  if (router_staged_fits(rs, c.d_model)) {
+    // batches that fill the chip with at least 4 tiles per workgroup
+    if (tpw <= 1) return router_staged_launch<1>(c, x, w_router, mod, topk_idx, topk_w, token_lse, st, s);
+    if (tpw <= 2) return router_staged_launch<2>(c, x, w_router, mod, topk_idx, topk_w, token_lse, st, s);
+    if (tpw <= 4) return router_staged_launch<4>(c, x, w_router, mod, topk_idx, topk_w, token_lse, st, s);
+    if (tpw <= 8) return router_staged_launch<8>(c, x, w_router, mod, topk_idx, topk_w, token_lse, st, s);
+  }
 #define MOE_ROUTER_CASE(N) \
   if (tpw <= N)            \
     return router_launch_t<MOE_DTYPE_BF16, N>(c, x, w_router, mod, topk_idx, topk_w, token_lse, st, s);

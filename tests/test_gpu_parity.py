@@ -343,6 +343,11 @@ VARIANTS = [
     ("bf16_tau1.5_noise_E64", 1200, 256, 64, 6, 64, 2, "bf16", 1.5, 1.0, "zipf", 0.0),
     # decode-sized: the router's K split and separate selection kernel
     ("bf16_decode_tau_noise", 64, 2048, 128, 8, 128, 1, "bf16", 1.5, 1.0, "none", 0.0),
+    # batches that fill the chip: the router's LDS-staged logits pipeline
+    # (32- and 64-token blocks, ragged last block, 1 and 3 K chunks, 64 and
+    # 128 experts)
+    ("bf16_staged_tau_noise_E64", 16400, 192, 64, 6, 64, 1, "bf16", 1.5, 1.0, "zipf", 0.0),
+    ("bf16_staged_E128_cap", 32800, 64, 128, 8, 32, 0, "bf16", 0.7, 0.5, "none", 1.0),
 ]
 
 
