@@ -37,7 +37,7 @@ struct Vec8<MOE_DTYPE_BF16> {
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      w[i] = (uint32_t)f32_to_bf16(v[2 * i]) | ((uint32_t)f32_to_bf16(v[2 * i + 1]) << 16);
+      w[i] = pack2_bf16(v[2 * i], v[2 * i + 1]);
     *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + off) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 };

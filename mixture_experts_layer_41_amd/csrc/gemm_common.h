@@ -103,12 +103,7 @@ __device__ __forceinline__ float silu_f(float g) { return g * __builtin_amdgcn_r
 // row scale s, each product rounded to bfloat16 (nearest even), as two
 // 16-byte chunks of 8 bf16 (codes 0..7 and 8..15).  codes16_to_bf16 below
 // widens the codes alone (no scale) in the same layout.
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  const bf16x2_t v = {(__bf16)a, (__bf16)b};
-  return __builtin_bit_cast(uint32_t, v);
-}
 __device__ __forceinline__ void dequant16(const u32x4_t q, float s, u32x4_t& lo, u32x4_t& hi) {
   const uint32_t w[4] = {q.x, q.y, q.z, q.w};
   uint32_t o[8];
@@ -117,8 +112,8 @@ __device__ __forceinline__ void dequant16(const u32x4_t q, float s, u32x4_t& lo,
     float v[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) v[b] = (float)(int8_t)(w[i] >> (8 * b)) * s;
-    o[2 * i] = pack_bf16x2(v[0], v[1]);
-    o[2 * i + 1] = pack_bf16x2(v[2], v[3]);
+    o[2 * i] = pack2_bf16(v[0], v[1]);
+    o[2 * i + 1] = pack2_bf16(v[2], v[3]);
   }
   lo = u32x4_t{o[0], o[1], o[2], o[3]};
   hi = u32x4_t{o[4], o[5], o[6], o[7]};
@@ -132,8 +127,8 @@ __device__ __forceinline__ void codes16_to_bf16(const u32x4_t q, u32x4_t& lo, u3
     float v[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) v[b] = (float)(int8_t)(w[i] >> (8 * b));
-    o[2 * i] = pack_bf16x2(v[0], v[1]);
-    o[2 * i + 1] = pack_bf16x2(v[2], v[3]);
+    o[2 * i] = pack2_bf16(v[0], v[1]);
+    o[2 * i + 1] = pack2_bf16(v[2], v[3]);
   }
   lo = u32x4_t{o[0], o[1], o[2], o[3]};
   hi = u32x4_t{o[4], o[5], o[6], o[7]};

@@ -118,8 +118,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // 4 floats rounded to bf16 (nearest even), one 8-byte buffer store at byte
 // offset off (dropped by the range check when past the resource's end)
 __device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, int off, const float* v) {
-  const u32x2 w = {(uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
-                   (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16)};
+  const u32x2 w = {pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3])};
   __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, 0);
 }
 
@@ -441,8 +440,7 @@ gemm_wide_kernel(GemmDesc p, int tiles_n) {
       char* band = reinterpret_cast<char*>(wm == 0 ? sA3 : sB3);  // this wave's half
       // 4 values of output column oc (a multiple of 4) of band row lr
       auto put = [&](int lr, int oc, const float* v) {
-        const u32x2 w = {(uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
-                         (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16)};
+        const u32x2 w = {pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3])};
         const int ch = (oc / 8) ^ (lr & (NCH - 1));
         *reinterpret_cast<u32x2*>(band + lr * (OC * 2) + ch * 16 + (oc % 8) * 2) = w;
       };
