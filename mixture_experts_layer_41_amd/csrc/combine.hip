@@ -19,13 +19,29 @@
 namespace moe {
 namespace {
 
-template <int DT>
+typedef uint32_t u32x4c __attribute__((ext_vector_type(4)));
+
+// 16 bytes, with the streaming (nontemporal) hint when NT
+template <bool NT>
+__device__ __forceinline__ u32x4c ld16(const void* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(static_cast<const u32x4c*>(p));
+  return *static_cast<const u32x4c*>(p);
+}
+template <bool NT>
+__device__ __forceinline__ void st16(void* p, u32x4c v) {
+  if constexpr (NT)
+    __builtin_nontemporal_store(v, static_cast<u32x4c*>(p));
+  else
+    *static_cast<u32x4c*>(p) = v;
+}
+
+template <int DT, bool NT = false>
 struct Vec8;
 
-template <>
-struct Vec8<MOE_DTYPE_BF16> {
+template <bool NT>
+struct Vec8<MOE_DTYPE_BF16, NT> {
   static __device__ __forceinline__ void load(const void* base, int64_t off, float v[8]) {
-    const uint4 q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+    const u32x4c q = ld16<NT>(static_cast<const uint16_t*>(base) + off);
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -34,31 +50,37 @@ struct Vec8<MOE_DTYPE_BF16> {
     }
   }
   static __device__ __forceinline__ void store(void* base, int64_t off, const float v[8]) {
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = pack2_bf16(v[2 * i], v[2 * i + 1]);
-    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + off) = make_uint4(w[0], w[1], w[2], w[3]);
+    u32x4c w;
+    w.x = pack2_bf16(v[0], v[1]);
+    w.y = pack2_bf16(v[2], v[3]);
+    w.z = pack2_bf16(v[4], v[5]);
+    w.w = pack2_bf16(v[6], v[7]);
+    st16<NT>(static_cast<uint16_t*>(base) + off, w);
   }
 };
 
-template <>
-struct Vec8<MOE_DTYPE_F32> {
+template <bool NT>
+struct Vec8<MOE_DTYPE_F32, NT> {
   static __device__ __forceinline__ void load(const void* base, int64_t off, float v[8]) {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
-    const float4 a = p[0], b = p[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    const float* p = static_cast<const float*>(base) + off;
+    const u32x4c a = ld16<NT>(p), b = ld16<NT>(p + 4);
+    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
+    v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+    v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
+    v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
   }
   static __device__ __forceinline__ void store(void* base, int64_t off, const float v[8]) {
-    float4* p = reinterpret_cast<float4*>(static_cast<float*>(base) + off);
-    p[0] = make_float4(v[0], v[1], v[2], v[3]);
-    p[1] = make_float4(v[4], v[5], v[6], v[7]);
+    float* p = static_cast<float*>(base) + off;
+    st16<NT>(p, u32x4c{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])});
+    st16<NT>(p + 4, u32x4c{__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7])});
   }
 };
 
 // k = K (compile time, 1..8): indices, weights and rows held in registers.
-template <int DT, int K>
+// NT: streaming loads and stores, for expert outputs larger than the
+// Infinity Cache (the rows are read once; the hint keeps them from evicting
+// lines that are reused).
+template <int DT, int K, bool NT>
 __global__ void __launch_bounds__(256)
 combine_small_k_kernel(const void* __restrict__ y_perm, const int32_t* __restrict__ inv_row,
                        const float* __restrict__ topk_w, const void* __restrict__ shared_y,
@@ -81,12 +103,12 @@ combine_small_k_kernel(const void* __restrict__ y_perm, const int32_t* __restric
     float v[K][8];
 #pragma unroll
     for (int j = 0; j < K; ++j)
-      Vec8<DT>::load(y_perm, (int64_t)(rows[j] >= 0 ? rows[j] : 0) * d + c, v[j]);
+      Vec8<DT, NT>::load(y_perm, (int64_t)(rows[j] >= 0 ? rows[j] : 0) * d + c, v[j]);
     // the shared output and the residual are loaded with the rows (from
     // y_perm's first row when absent, then unused), not after a branch
     float sv[8], rv[8];
-    Vec8<DT>::load(shared_y ? shared_y : y_perm, shared_y ? t * d + c : c, sv);
-    Vec8<DT>::load(residual ? residual : y_perm, residual ? t * d + c : c, rv);
+    Vec8<DT, NT>::load(shared_y ? shared_y : y_perm, shared_y ? t * d + c : c, sv);
+    Vec8<DT, NT>::load(residual ? residual : y_perm, residual ? t * d + c : c, rv);
     float acc[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[q] = shared_y ? sv[q] : 0.f;
@@ -98,7 +120,7 @@ combine_small_k_kernel(const void* __restrict__ y_perm, const int32_t* __restric
     }
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[q] = residual ? acc[q] + rv[q] : acc[q];
-    Vec8<DT>::store(y, t * d + c, acc);
+    Vec8<DT, NT>::store(y, t * d + c, acc);
   }
 }
 
@@ -147,10 +169,18 @@ hipError_t launch_combine(const moe_config& c, const void* y_perm, const int32_t
   const int64_t total = c.n_tokens * (c.d_model / 8);
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
+  // streaming hints once the expert outputs outgrow the 256 MB Infinity
+  // Cache (measured: 18 % faster at 1.6 GB of rows, 11 % slower at 200 MB)
+  const int64_t elt = c.dtype == MOE_DTYPE_BF16 ? 2 : 4;
+  const bool nt = c.n_tokens * c.top_k * c.d_model * elt > ((int64_t)256 << 20);
 #define MOE_COMBINE(K_, DT_)                                                                \
   case K_:                                                                                  \
-    combine_small_k_kernel<DT_, K_><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(            \
-        y_perm, inv_row, topk_w, shared_y, residual, y, c.n_tokens, c.d_model);              \
+    if (nt)                                                                                 \
+      combine_small_k_kernel<DT_, K_, true><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(    \
+          y_perm, inv_row, topk_w, shared_y, residual, y, c.n_tokens, c.d_model);            \
+    else                                                                                    \
+      combine_small_k_kernel<DT_, K_, false><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(   \
+          y_perm, inv_row, topk_w, shared_y, residual, y, c.n_tokens, c.d_model);            \
     break;
 #define MOE_COMBINE_ALL(DT_)                                                                \
   switch (c.top_k) {                                                                        \

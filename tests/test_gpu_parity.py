@@ -120,6 +120,9 @@ SMALL = [
     ("bf16_wide_swiglu_shared2", 3000, 512, 2, 1, 384, 2, "bf16", "swiglu", 0.0, "none", "none", False),
     ("bf16_wide_gelu_bias", 2600, 256, 2, 1, 512, 1, "bf16", "gelu", 0.0, "random", "none", True),
     ("bf16_wide_cap_zipf", 4100, 256, 4, 2, 256, 0, "bf16", "swiglu", 1.0, "none", "zipf", False),
+    # 8 column tiles on both products: the wide kernel's grouped tile order
+    # (groups of 8 row tiles, the last group ragged: 10 row tiles)
+    ("bf16_wide_grouped_order", 2050, 2048, 2, 1, 1024, 0, "bf16", "swiglu", 0.0, "none", "none", False),
 ]
 
 
