@@ -113,6 +113,8 @@ __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70);
 
 // Buffer resource word 3 for raw (untyped, unswizzled) access.
 constexpr int kBufFlags = 0x00020000;
+// cache-policy operand of a buffer store: the nontemporal (nt) bit
+constexpr int kStoreNT = 2;
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // 4 floats rounded to bf16 (nearest even), one 8-byte buffer store at byte
@@ -518,7 +520,9 @@ gemm_wide_kernel(GemmDesc p, int tiles_n) {
                             ((cc ^ (lr & (NCH - 1))) * 16);
           const u32x4 v = *reinterpret_cast<const u32x4*>(src);
           const int trow = hb * TM + q * IPP * 32 + lr;
-          __builtin_amdgcn_raw_buffer_store_b128(v, ro, (trow * (int)p.ldo + col0 + cc * 8) * 2, 0, 0);
+          // streaming store (nt): the output is read back only by the next
+          // kernel, so it need not displace this kernel's operand lines in L2
+          __builtin_amdgcn_raw_buffer_store_b128(v, ro, (trow * (int)p.ldo + col0 + cc * 8) * 2, 0, kStoreNT);
         }
         lds_barrier();
       }
