@@ -44,7 +44,9 @@
 // copies and LDS reads alone take as long as the whole kernel; with every
 // tile reading the same (L2-resident) data the kernel gains only about 15 %.
 // Requirements (checked by the host): K per segment a multiple of 32, the
-// K stages per tile a multiple of 4, output widths a multiple of the tile.
+// K stages per tile a multiple of 4, output widths a multiple of the tile
+// (of half a tile for the down kind: a last half tile clamps its weight rows
+// to the width and stores only its first half).
 #include <algorithm>
 
 #include "moe_internal.h"
@@ -268,7 +270,7 @@ gemm_wide_kernel(GemmDesc p, int tiles_n) {
     if (kSwiglu)
       wr = (rb < BN / 2) ? t.n0 + rb : f + t.n0 + (rb - BN / 2);
     else
-      wr = t.n0 + rb;
+      wr = min(t.n0 + rb, rows1 - 1);  // a last column tile may be half outside the width
     s.b = wb + (int64_t)wr * kw + chk;
     return s;
   };
@@ -498,7 +500,7 @@ gemm_wide_kernel(GemmDesc p, int tiles_n) {
                   } else {
                     if (BIAS)
                       for (int s = 0; s < S; ++s)
-                        v += bf16_to_f32(bias[((int64_t)tc.group * S + s) * d + tc.n0 + cidx + e]);
+                        v += bf16_to_f32(bias[((int64_t)tc.group * S + s) * d + min(tc.n0 + cidx + e, d - 1)]);
                     hv[e] = v;
                   }
                 }
@@ -522,7 +524,8 @@ gemm_wide_kernel(GemmDesc p, int tiles_n) {
           const int trow = hb * TM + q * IPP * 32 + lr;
           // streaming store (nt): the output is read back only by the next
           // kernel, so it need not displace this kernel's operand lines in L2
-          __builtin_amdgcn_raw_buffer_store_b128(v, ro, (trow * (int)p.ldo + col0 + cc * 8) * 2, 0, kStoreNT);
+          if (KIND == kGemmUp || tc.n0 + cc * 8 < d)  // columns past the width (down: half tiles)
+            __builtin_amdgcn_raw_buffer_store_b128(v, ro, (trow * (int)p.ldo + col0 + cc * 8) * 2, 0, kStoreNT);
         }
         lds_barrier();
       }
@@ -575,8 +578,9 @@ int wide_cus() {
 template <int WM, int WN, int KIND, int ACT, bool BIAS>
 hipError_t run_wide(const GemmDesc& g, hipStream_t s) {
   constexpr bool kSwiglu = (KIND == kGemmUp && ACT == MOE_ACT_SWIGLU);
+  // down: the last column tile may cover half a tile (widths multiple of 128)
   const int tiles_n = KIND == kGemmUp ? g.n_seg * (g.f / (kSwiglu ? wide::BN / 2 : wide::BN))
-                                      : g.d / wide::BN;
+                                      : (g.d + wide::BN - 1) / wide::BN;
   const int64_t tiles_m = (g.rows_max + wide::BM - 1) / wide::BM + (g.group_off ? g.n_groups : 0);
   const int64_t upper = tiles_m * tiles_n;
   if (upper <= 0 || g.rows_max <= 0) return hipSuccess;
@@ -604,7 +608,9 @@ bool wide_fits(GemmKind kind, const GemmDesc& g) {
   if (K % wide::BK != 0) return false;
   const int nk = (kind == kGemmUp ? 1 : g.n_seg) * (K / wide::BK);
   if (nk % wide::NS != 0) return false;
-  const int ncol = kind == kGemmUp ? (swiglu ? wide::BN / 2 : wide::BN) : wide::BN;
+  // output widths in whole tiles; the down kind also takes a last half tile
+  // (the backward's dh product: width f = 1408 on the skewed layer)
+  const int ncol = kind == kGemmUp ? (swiglu ? wide::BN / 2 : wide::BN) : wide::BN / 2;
   const int width = kind == kGemmUp ? g.f : g.d;
   return width % ncol == 0;
 }

@@ -156,10 +156,14 @@ def test_backward_load_balance_forms(name):
 # Shapes that reach the weight-gradient product's other plans: 128 x 128
 # tiles with a K split (long K, few tiles: the shared expert's 2048 tokens
 # and two routed experts of ~1024 rows each), and 256 x 256 tiles with and
-# without a K split (16384 tokens; eight experts of ~4096 rows each)
+# without a K split (16384 tokens; eight experts of ~4096 rows each); and
+# one that reaches the wide kernel's half column tile
 WGRAD_SHAPES = [
     ("wgrad_split_128", 2048, 64, 2, 1, 64, 1),
     ("wgrad_tile256_split", 16384, 1024, 8, 2, 1024, 1),
+    # thousands of rows per expert and f = 384: the dh products (width f) go
+    # to the wide-tile kernel with a last half column tile
+    ("dh_wide_half_tile", 4200, 256, 2, 1, 384, 1),
 ]
 
 

@@ -123,6 +123,8 @@ SMALL = [
     # 8 column tiles on both products: the wide kernel's grouped tile order
     # (groups of 8 row tiles, the last group ragged: 10 row tiles)
     ("bf16_wide_grouped_order", 2050, 2048, 2, 1, 1024, 0, "bf16", "swiglu", 0.0, "none", "none", False),
+    # d = 384: the down product's last column tile is half a tile
+    ("bf16_wide_half_tile", 2300, 384, 2, 1, 256, 1, "bf16", "swiglu", 0.0, "none", "none", True),
 ]
 
 
