@@ -143,11 +143,15 @@ gemm_wide_kernel(GemmDesc p, int tiles_n) {
   __shared__ __attribute__((aligned(16))) u32x4 sA0[SCH];
   __shared__ __attribute__((aligned(16))) u32x4 sA1[SCH];
   __shared__ __attribute__((aligned(16))) u32x4 sA2[SCH];
-  __shared__ __attribute__((aligned(16))) u32x4 sA3[SCH];
   __shared__ __attribute__((aligned(16))) u32x4 sB0[SCH];
   __shared__ __attribute__((aligned(16))) u32x4 sB1[SCH];
   __shared__ __attribute__((aligned(16))) u32x4 sB2[SCH];
-  __shared__ __attribute__((aligned(16))) u32x4 sB3[SCH];
+  // stage 3 is one array holding both operands: the epilogue's band (either
+  // half of it) is then one LDS object, which the compiler knows the copies
+  // in flight to stages 0-2 do not write
+  __shared__ __attribute__((aligned(16))) u32x4 s3[2 * SCH];
+  u32x4* const sA3 = s3;
+  u32x4* const sB3 = s3 + SCH;
   __shared__ int s_off[kMaxExperts + 1];     // group row offsets
   __shared__ int s_tstart[kMaxExperts + 1];  // first row tile of each group
   __shared__ int s_scan[kMaxExperts + 1];
@@ -441,12 +445,16 @@ gemm_wide_kernel(GemmDesc p, int tiles_n) {
       static_assert(IPP >= 1 && MI % IPP == 0 && (2 * RCH) % NT == 0, "epilogue band");
       static_assert(OC * 2 >= 256, "a row per 256-byte bank window at least (swizzle key = row)");
       const int col0 = (KIND == kGemmUp) ? tc.seg * f + tc.n0 : tc.n0;
-      char* band = reinterpret_cast<char*>(wm == 0 ? sA3 : sB3);  // this wave's half
-      // 4 values of output column oc (a multiple of 4) of band row lr
+      u32x2* const band = reinterpret_cast<u32x2*>(s3) + wm * (2 * SCH);  // this wave's half
+      // 4 values of output column oc (a multiple of 4) of band row lr.  The
+      // write is an asm statement: the compiler would otherwise wait for
+      // every copy in flight (the next tile's stages 1 and 2, which target
+      // other buffers) before the first write.
       auto put = [&](int lr, int oc, const float* v) {
         const u32x2 w = {pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3])};
         const int ch = (oc / 8) ^ (lr & (NCH - 1));
-        *reinterpret_cast<u32x2*>(band + lr * (OC * 2) + ch * 16 + (oc % 8) * 2) = w;
+        const uint32_t a = (uint32_t)(uintptr_t)(band + lr * (OC / 4) + ch * 2 + (oc % 8) / 4);
+        __asm__ volatile("ds_write_b64 %0, %1" ::"v"(a), "v"(w) : "memory");
       };
 #pragma unroll
       for (int q = 0; q < NP; ++q) {
@@ -518,9 +526,7 @@ gemm_wide_kernel(GemmDesc p, int tiles_n) {
           const int c = tid + u * NT;
           const int hb = c / RCH, lc = c % RCH;
           const int lr = lc / NCH, cc = lc % NCH;
-          const char* src = reinterpret_cast<const char*>(hb == 0 ? sA3 : sB3) + lr * (OC * 2) +
-                            ((cc ^ (lr & (NCH - 1))) * 16);
-          const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+          const u32x4 v = s3[hb * SCH + lr * NCH + (cc ^ (lr & (NCH - 1)))];
           const int trow = hb * TM + q * IPP * 32 + lr;
           // streaming store (nt): the output is read back only by the next
           // kernel, so it need not displace this kernel's operand lines in L2
