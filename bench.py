@@ -20,9 +20,12 @@ Prints ONE JSON line (rank 0).  Per leg:
   flush         the forward timed once per iteration with a 512 MB device
                 write between iterations (cold L2 / Infinity Cache);
   backward      moe_forward_train + moe_backward (headline and Flash legs).
+  cpu_baseline  the float64 CPU oracle timed on the host on a bounded
+                sample of the leg's workload (the first tokens as a batch of
+                their own; for the decode layer a few tokens of the full
+                batch, with only their experts' weights), and the GPU output
+                of the same tokens against it (parity).
 Headline only:
-  cpu_baseline  the float64 CPU oracle on a bounded token sample of the
-                headline workload, timed on the host;
   clock         the GPU clock amd-smi reports while the GEMM leg runs.
 """
 
@@ -68,9 +71,14 @@ def parse():
                     help="comma-separated extra layer configs, or 'none' (default: c2,c3,c5)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU time the oracle is run for on the headline workload")
+    ap.add_argument("--cpu-leg-seconds", type=float, default=4.0,
+                    help="CPU time the oracle is run for on each extra leg")
     ap.add_argument("--cpu-tokens", type=int, default=2048,
-                    help="tokens of the headline batch the CPU oracle leg runs on")
+                    help="tokens of a batch the CPU oracle leg runs on (a whole batch if smaller)")
+    ap.add_argument("--cpu-decode-tokens", type=int, default=2,
+                    help="tokens of the decode layer's batch the CPU oracle evaluates")
     ap.add_argument("--no-backward", action="store_true", help="skip the training (backward) legs")
     ap.add_argument("--no-flush", action="store_true", help="skip the cold-cache variant")
     ap.add_argument("--no-clock", action="store_true",
@@ -207,6 +215,24 @@ def layer_weights(t):
         router_bias=None if rb is None else torch.from_numpy(rb).cuda())
 
 
+def oracle_lazy(cfg):
+    """Whether the CPU oracle leg keeps the expert weights lazy (generated
+    one expert at a time) and evaluates a few tokens of the full batch: the
+    weight stacks of the decode layer (22.5 GB) are too large to hold."""
+    return cfg.E * cfg.w1_rows * cfg.d * 3 > (1 << 32)
+
+
+def cpu_sample_tokens(cfg, args):
+    """Tokens the CPU oracle leg evaluates: a few of the decode batch; the
+    whole batch when a capacity limit makes the drops depend on it (if it
+    is not much larger than the sample); else the first --cpu-tokens."""
+    if oracle_lazy(cfg):
+        return args.cpu_decode_tokens
+    if cfg.capacity_factor > 0 and cfg.T <= 4 * args.cpu_tokens:
+        return cfg.T
+    return args.cpu_tokens
+
+
 def run_leg(cfg, args, headline, want_backward, want_host_inputs):
     """Times one layer config; returns (leg dict, host inputs or None,
     device handles for the parity check)."""
@@ -220,7 +246,7 @@ def run_leg(cfg, args, headline, want_backward, want_host_inputs):
     t0 = time.perf_counter()
     # raw seeded draws (no tie rejection: timing only); expert weight stacks
     # stay lazy (generated one expert at a time) unless the CPU leg needs them
-    t = make_inputs(cfg, materialize=want_host_inputs)
+    t = make_inputs(cfg, materialize=want_host_inputs and not oracle_lazy(cfg))
     W = layer_weights(t)
     x = dev_tensor(t["x"])
     noise = dev_tensor(t.get("router_noise"))
@@ -441,47 +467,85 @@ def run_leg(cfg, args, headline, want_backward, want_host_inputs):
     return leg, t if want_host_inputs else None, handles, clock
 
 
-def cpu_baseline_leg(cfg, t, handles, args):
-    """The oracle (float64 numpy, as it stands) on the first n tokens of the
-    headline batch, as one batch of its own; and the GPU output of the same
-    tokens against it (per-token results do not depend on the batch without a
-    capacity limit)."""
+class _ExpertCache(dict):
+    """Weights of some experts of a lazy stack, generated before the timed
+    region; an expert not in it is generated on first use."""
+
+    def __init__(self, bank, experts):
+        from concurrent.futures import ThreadPoolExecutor
+        experts = [int(e) for e in experts]
+        with ThreadPoolExecutor(max_workers=16) as ex:
+            super().__init__(zip(experts, ex.map(lambda e: bank[e], experts)))
+        self.bank = bank
+
+    def __missing__(self, e):
+        v = self[e] = self.bank[e]
+        return v
+
+
+def cpu_baseline_leg(cfg, t, handles, n_tokens, seconds):
+    """The oracle (float64 numpy, as it stands) timed on the host, and the
+    GPU output of the same tokens against it.
+
+    Stacked weights: the first n tokens of the batch as a batch of their own
+    (per-token results do not depend on the batch without a capacity limit;
+    with one, n is the whole batch or parity is skipped).  Lazy weights (the
+    decode layer): routing over the full batch and the expert FFNs of its
+    first n tokens only, with those tokens' experts generated beforehand (the
+    generation is not timed)."""
     import numpy as np
     import torch
     import oracle
 
-    n = min(args.cpu_tokens, cfg.T)
-    cs = dataclasses.replace(cfg, T=n)
-    ts = dict(t)
-    ts["x"] = t["x"][:n]
-    if t.get("router_noise") is not None:
-        ts["router_noise"] = t["router_noise"][:n]
+    fwd = handles["fwd"]
+    y = fwd(handles["x"], handles["noise"])
+    torch.cuda.synchronize()
     model, blas, threads = cpu_info()
+    lazy = oracle_lazy(cfg)
+    if lazy:
+        n = min(n_tokens, cfg.T)
+        rows = list(range(n))
+        touched = sorted(set(fwd.topk_idx[:n].cpu().numpy().reshape(-1).tolist()))
+        cs, ts = cfg, dict(t)
+        for name in ("w1", "w2", "w1_scale", "w2_scale"):
+            if ts.get(name) is not None:
+                ts[name] = _ExpertCache(ts[name], touched)
+        for name in ("ws1", "ws2", "ws1_scale", "ws2_scale"):
+            if ts.get(name) is not None:
+                ts[name] = _ExpertCache(ts[name], range(cfg.S))
+        what = (f"tokens 0..{n - 1} of the {cfg.T}-token batch: routing of all {cfg.T} tokens, the "
+                f"routed ({len(touched)} experts) and shared expert FFNs and the combine of those {n}")
+    else:
+        n = min(n_tokens, cfg.T)
+        rows = None
+        cs = dataclasses.replace(cfg, T=n)
+        ts = dict(t)
+        ts["x"] = t["x"][:n]
+        if t.get("router_noise") is not None:
+            ts["router_noise"] = t["router_noise"][:n]
+        what = (f"the first {n} of the {cfg.T} tokens of this workload as one batch "
+                f"(routing, permutation, routed and shared expert FFNs, combine, aux)")
     runs, t_cpu, ref = 0, 0.0, None
-    while t_cpu < args.cpu_seconds or runs == 0:
+    while t_cpu < seconds or runs == 0:
         s0 = time.perf_counter()
-        ref = oracle.forward(cs, ts)
+        ref = oracle.forward(cs, ts, rows=rows)
         t_cpu += time.perf_counter() - s0
         runs += 1
-    cpu = {"value": round(n * runs / t_cpu, 1), "unit": "tokens/s", "cores": threads,
+    cpu = {"value": round(n * runs / t_cpu, 2), "unit": "tokens/s", "cores": threads,
            "kind": "oracle",
-           "sample": f"the first {n} of the {cfg.T} tokens of this workload as one batch "
-                     f"(routing, permutation, routed and shared expert FFNs, combine, aux), "
-                     f"{runs} run(s) in {t_cpu:.1f} s, float64 numpy",
+           "sample": f"{what}, {runs} run(s) in {t_cpu:.1f} s, float64 numpy",
            "cpu_model": model, "blas": blas}
-    log(f"[bench] oracle {t_cpu / runs:.2f} s per {n}-token batch on {threads} threads ({model}; {blas})")
+    log(f"[bench] {cfg.name}: oracle {t_cpu / runs:.2f} s per run of {n} tokens on {threads} threads "
+        f"({model}; {blas})")
     parity = None
-    if not (cfg.capacity_factor > 0 and n < cfg.T):
-        fwd = handles["fwd"]
-        y = fwd(handles["x"], handles["noise"])
-        torch.cuda.synchronize()
+    if lazy or not (cfg.capacity_factor > 0 and n < cfg.T):
         yg = y[:n].float().cpu().numpy().astype(np.float64)
         err = float(np.max(np.abs(yg - ref["y"])) / np.max(np.abs(ref["y"])))
-        other = int((fwd.topk_idx[:n].cpu().numpy() != ref["topk_idx"]).any(1).sum())
+        other = int((fwd.topk_idx[:n].cpu().numpy() != ref["topk_idx"][:n]).any(1).sum())
         parity = {"tokens_compared": n, "y_normwise_err": err, "tokens_with_other_topk": other,
                   "note": "raw draws without the tie-gap rule: a token with a near-tie may pick "
                           "another expert"}
-        log(f"[bench] parity on {n} tokens: {parity}")
+        log(f"[bench] {cfg.name}: parity on {n} tokens: {parity}")
     return cpu, parity
 
 
@@ -507,14 +571,10 @@ def main():
 
     # ---- headline
     want_cpu = not args.no_cpu
-    big = cfg.E * cfg.w1_rows * cfg.d * 3 > (1 << 32)
-    if want_cpu and big:
-        log(f"[bench] {cfg.name}: weights too large for the CPU oracle leg; skipping it")
-        want_cpu = False
     head, t, handles, clock = run_leg(cfg, args, True, not args.no_backward, want_cpu)
     cpu = parity = None
     if want_cpu:
-        cpu, parity = cpu_baseline_leg(cfg, t, handles, args)
+        cpu, parity = cpu_baseline_leg(cfg, t, handles, cpu_sample_tokens(cfg, args), args.cpu_seconds)
     del t, handles
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -523,9 +583,12 @@ def main():
     legs = {}
     for name in extra:
         lc = get_config(name)
-        leg, _, h, _ = run_leg(lc, args, False, not args.no_backward and name == "c2", False)
+        leg, tl, h, _ = run_leg(lc, args, False, not args.no_backward and name == "c2", want_cpu)
+        if want_cpu:
+            leg["cpu_baseline"], leg["parity"] = cpu_baseline_leg(lc, tl, h, cpu_sample_tokens(lc, args),
+                                                                  args.cpu_leg_seconds)
         legs[name] = leg
-        del h
+        del h, tl
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
 
