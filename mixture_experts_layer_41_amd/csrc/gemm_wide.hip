@@ -156,6 +156,7 @@ gemm_wide_kernel(GemmDesc p, int tiles_n) {
   __shared__ int s_tstart[kMaxExperts + 1];  // first row tile of each group
   __shared__ int s_scan[kMaxExperts + 1];
   __shared__ int s_idx[3][BM];               // gather indices of three consecutive tiles
+  __shared__ float s_bias[BIAS ? BN : 1];    // bias of the current tile's output columns
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
@@ -445,6 +446,25 @@ gemm_wide_kernel(GemmDesc p, int tiles_n) {
       static_assert(IPP >= 1 && MI % IPP == 0 && (2 * RCH) % NT == 0, "epilogue band");
       static_assert(OC * 2 >= 256, "a row per 256-byte bank window at least (swizzle key = row)");
       const int col0 = (KIND == kGemmUp) ? tc.seg * f + tc.n0 : tc.n0;
+      // bias of the tile's columns as float32, once per tile (the down kind:
+      // the segments' biases summed in segment order): one round of loads
+      // instead of a load and its wait for every accumulator
+      if (BIAS) {
+        for (int c = tid; c < BN; c += NT) {
+          float b = 0.f;
+          if (kSwiglu) {
+            const uint16_t* bb = bias + ((int64_t)tc.group * S + tc.seg) * 2 * f;
+            b = bf16_to_f32(bb[c < BN / 2 ? tc.n0 + c : f + tc.n0 + (c - BN / 2)]);
+          } else if (KIND == kGemmUp) {
+            b = bf16_to_f32(bias[((int64_t)tc.group * S + tc.seg) * f + tc.n0 + c]);
+          } else {
+            for (int sg = 0; sg < S; ++sg)
+              b += bf16_to_f32(bias[((int64_t)tc.group * S + sg) * d + min(tc.n0 + c, d - 1)]);
+          }
+          s_bias[c] = b;
+        }
+        lds_barrier();
+      }
       u32x2* const band = reinterpret_cast<u32x2*>(s3) + wm * (2 * SCH);  // this wave's half
       // 4 values of output column oc (a multiple of 4) of band row lr.  The
       // write is an asm statement: the compiler would otherwise wait for
@@ -477,9 +497,8 @@ gemm_wide_kernel(GemmDesc p, int tiles_n) {
                   gv[e] = acc[i][j][4 * g4 + e];
                   uv[e] = acc[i][j + NI / 2][4 * g4 + e];
                   if (BIAS) {
-                    const uint16_t* b = bias + ((int64_t)tc.group * S + tc.seg) * 2 * f;
-                    gv[e] += bf16_to_f32(b[tc.n0 + cidx + e]);
-                    uv[e] += bf16_to_f32(b[f + tc.n0 + cidx + e]);
+                    gv[e] += s_bias[cidx + e];
+                    uv[e] += s_bias[BN / 2 + cidx + e];
                   }
                   hv[e] = silu_f(gv[e]) * uv[e];
                 }
@@ -502,13 +521,11 @@ gemm_wide_kernel(GemmDesc p, int tiles_n) {
                 for (int e = 0; e < 4; ++e) {
                   float v = acc[i][j][4 * g4 + e];
                   if (KIND == kGemmUp) {
-                    if (BIAS) v += bf16_to_f32(bias[((int64_t)tc.group * S + tc.seg) * f + tc.n0 + cidx + e]);
+                    if (BIAS) v += s_bias[cidx + e];
                     pv[e] = v;
                     hv[e] = gelu_f(v);
                   } else {
-                    if (BIAS)
-                      for (int s = 0; s < S; ++s)
-                        v += bf16_to_f32(bias[((int64_t)tc.group * S + s) * d + min(tc.n0 + cidx + e, d - 1)]);
+                    if (BIAS) v += s_bias[cidx + e];
                     hv[e] = v;
                   }
                 }

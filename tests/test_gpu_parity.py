@@ -125,6 +125,10 @@ SMALL = [
     ("bf16_wide_grouped_order", 2050, 2048, 2, 1, 1024, 0, "bf16", "swiglu", 0.0, "none", "none", False),
     # d = 384: the down product's last column tile is half a tile
     ("bf16_wide_half_tile", 2300, 384, 2, 1, 256, 1, "bf16", "swiglu", 0.0, "none", "none", True),
+    # SwiGLU with expert biases on the wide tiles (gate and up halves of the
+    # bias slice; the shared pair's two down biases summed), with the half
+    # column tile: the bias of its columns past d clamped
+    ("bf16_wide_swiglu_bias", 2400, 384, 2, 1, 256, 2, "bf16", "swiglu", 0.0, "random", "none", False),
 ]
 
 
