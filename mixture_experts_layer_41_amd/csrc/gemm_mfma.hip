@@ -294,6 +294,32 @@ __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo
   // tile through LDS; the GELU and INT8-scaled up GEMMs, whose epilogues
   // would spill with the band addressing, store from the registers.
   constexpr bool kStage = !(KIND == kGemmUp && (Q8 == 1 || !kSwiglu));
+  // bias of this lane's output columns (one per j; SwiGLU: gate and up),
+  // float32, loaded once instead of once per accumulator (the down kind: the
+  // segments' biases summed in segment order)
+  float bsa[NI], bsb[NI];
+  if (BIAS) {
+    const uint16_t* bias = static_cast<const uint16_t*>(p.bias);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      bsa[j] = bsb[j] = 0.f;
+      if (kSwiglu) {
+        if (j < NI / 2) {
+          const int cidx = wn * (TN / 2) + j * 32 + fr;
+          const uint16_t* b = bias + ((int64_t)tile.group * S + seg) * 2 * f;
+          bsa[j] = bf16_to_f32(b[n0 + cidx]);
+          bsb[j] = bf16_to_f32(b[f + n0 + cidx]);
+        }
+      } else {
+        const int cidx = wn * TN + j * 32 + fr;
+        if (KIND == kGemmUp) {
+          bsa[j] = bf16_to_f32(bias[((int64_t)tile.group * S + seg) * f + n0 + cidx]);
+        } else {
+          for (int sg = 0; sg < S; ++sg) bsa[j] += bf16_to_f32(bias[((int64_t)tile.group * S + sg) * d + n0 + cidx]);
+        }
+      }
+    }
+  }
   if constexpr (kStage) {
     // 32x32 C layout: column lane%32, rows 8*(q/4) + 4*(lane/32) + q%4.
     // The output tile goes through LDS (free since the K loop's last barrier):
@@ -308,7 +334,6 @@ __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo
     static_assert(OC % 8 == 0 && OC <= 256 && (OC <= 128 || BN >= BM), "epilogue band");
     static_assert((BM * NCH) % kTileThreads == 0, "epilogue band");
     uint16_t* out = static_cast<uint16_t*>(p.out);
-    const uint16_t* bias = static_cast<const uint16_t*>(p.bias);
     char* const bandA = reinterpret_cast<char*>(&sA[0][0]);
     char* const bandB = reinterpret_cast<char*>(&sB[0][0]);
     auto band_at = [&](int r, int c) -> char* {
@@ -332,9 +357,8 @@ __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo
               u *= esc[j + NI / 2];
             }
             if (BIAS) {
-              const uint16_t* b = bias + ((int64_t)tile.group * S + seg) * 2 * f;
-              g += bf16_to_f32(b[n0 + cidx]);
-              u += bf16_to_f32(b[f + n0 + cidx]);
+              g += bsa[j];
+              u += bsb[j];
             }
             *reinterpret_cast<uint16_t*>(band_at(r, cidx)) = f32_to_bf16(silu_f(g) * u);
             if (p.preact && live) {
@@ -350,14 +374,12 @@ __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo
             float v = acc[i][j][q];
             if constexpr (Q8 == 1) v *= esc[j];
             if (KIND == kGemmUp) {
-              if (BIAS) v += bf16_to_f32(bias[((int64_t)tile.group * S + seg) * f + n0 + cidx]);
+              if (BIAS) v += bsa[j];
               if (p.preact && live)
                 static_cast<uint16_t*>(p.preact)[grow * p.ldp + (int64_t)seg * f + n0 + cidx] = f32_to_bf16(v);
               *reinterpret_cast<uint16_t*>(band_at(r, cidx)) = f32_to_bf16(gelu_f(v));
             } else {
-              if (BIAS)
-                for (int s = 0; s < S; ++s)
-                  v += bf16_to_f32(bias[((int64_t)tile.group * S + s) * d + n0 + cidx]);
+              if (BIAS) v += bsa[j];
               *reinterpret_cast<uint16_t*>(band_at(r, cidx)) = f32_to_bf16(v);
             }
           }
@@ -378,7 +400,6 @@ __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo
   } else {
     // epilogue (32x32 C layout: column lane%32, rows 8*(q/4) + 4*(lane/32) + q%4)
     uint16_t* out = static_cast<uint16_t*>(p.out);
-    const uint16_t* bias = static_cast<const uint16_t*>(p.bias);
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
 #pragma unroll
@@ -396,9 +417,8 @@ __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo
               u *= esc[j + NI / 2];
             }
             if (BIAS) {
-              const uint16_t* b = bias + ((int64_t)tile.group * S + seg) * 2 * f;
-              g += bf16_to_f32(b[n0 + cidx]);
-              u += bf16_to_f32(b[f + n0 + cidx]);
+              g += bsa[j];
+              u += bsb[j];
             }
             out[grow * p.ldo + (int64_t)seg * f + n0 + cidx] = f32_to_bf16(silu_f(g) * u);
             if (p.preact) {
@@ -414,14 +434,12 @@ __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo
             float v = acc[i][j][q];
             if constexpr (Q8 == 1) v *= esc[j];
             if (KIND == kGemmUp) {
-              if (BIAS) v += bf16_to_f32(bias[((int64_t)tile.group * S + seg) * f + n0 + cidx]);
+              if (BIAS) v += bsa[j];
               if (p.preact)
                 static_cast<uint16_t*>(p.preact)[grow * p.ldp + (int64_t)seg * f + n0 + cidx] = f32_to_bf16(v);
               out[grow * p.ldo + (int64_t)seg * f + n0 + cidx] = f32_to_bf16(gelu_f(v));
             } else {
-              if (BIAS)
-                for (int s = 0; s < S; ++s)
-                  v += bf16_to_f32(bias[((int64_t)tile.group * S + s) * d + n0 + cidx]);
+              if (BIAS) v += bsa[j];
               out[grow * p.ldo + n0 + cidx] = f32_to_bf16(v);
             }
           }

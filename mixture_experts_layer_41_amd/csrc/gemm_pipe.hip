@@ -137,6 +137,7 @@ gemm_pipe_kernel(GemmDesc p, int tiles_n) {
   __shared__ __attribute__((aligned(16))) u32x4 sB2[BN * CPR];
   __shared__ __attribute__((aligned(16))) u32x4 sB3[BN * CPR];
   __shared__ __attribute__((aligned(16))) u32x4 sA4[XS * BM * CPR + 1], sA5[XS * BM * CPR + 1];
+  __shared__ float s_bias[BIAS ? BN : 1];   // bias of the current tile's output columns
   __shared__ __attribute__((aligned(16))) u32x4 sA6[XS * BM * CPR + 1], sA7[XS * BM * CPR + 1];
   __shared__ __attribute__((aligned(16))) u32x4 sB4[XS * BN * CPR + 1], sB5[XS * BN * CPR + 1];
   __shared__ __attribute__((aligned(16))) u32x4 sB6[XS * BN * CPR + 1], sB7[XS * BN * CPR + 1];
@@ -407,6 +408,24 @@ gemm_pipe_kernel(GemmDesc p, int tiles_n) {
 
     // ---- epilogue.  acc[i][j] holds the transposed 32x32 block: lane l has
     // tile row i*32 + l%32 and output columns j*32 + 8*(q/4) + 4*(l/32) + q%4.
+    // The bias of the tile's columns goes to LDS as float32 once per tile
+    // (the down kind: the segments' biases summed in segment order): one
+    // round of loads instead of a load and its wait for every accumulator.
+    if (BIAS) {
+      for (int c = tid; c < BN; c += NT) {
+        float b = 0.f;
+        if (kSwiglu) {
+          const uint16_t* bb = bias + ((int64_t)tc.group * S + tc.seg) * 2 * f;
+          b = bf16_to_f32(bb[c < BN / 2 ? tc.n0 + c : f + tc.n0 + (c - BN / 2)]);
+        } else if (KIND == kGemmUp) {
+          b = bf16_to_f32(bias[((int64_t)tc.group * S + tc.seg) * f + tc.n0 + c]);
+        } else {
+          for (int sg = 0; sg < S; ++sg) b += bf16_to_f32(bias[((int64_t)tc.group * S + sg) * d + tc.n0 + c]);
+        }
+        s_bias[c] = b;
+      }
+      lds_barrier();
+    }
     if constexpr (kSwiglu && PAIRED) {
       // training forward (pre-activations too): 16-byte stores from the
       // registers, lane pairs l, l ^ 32 joining their 4-column halves
@@ -429,9 +448,8 @@ gemm_pipe_kernel(GemmDesc p, int tiles_n) {
               for (int e = 0; e < 4; ++e) {
                 float gv = acc[i][j][4 * g4 + e], uv = acc[i][j + NI / 2][4 * g4 + e];
                 if (BIAS) {
-                  const uint16_t* b = bias + ((int64_t)tc.group * S + tc.seg) * 2 * f;
-                  gv += bf16_to_f32(b[tc.n0 + cidx + e]);
-                  uv += bf16_to_f32(b[f + tc.n0 + cidx + e]);
+                  gv += s_bias[cidx + e];
+                  uv += s_bias[BN / 2 + cidx + e];
                 }
                 h[e] = f32_to_bf16(silu_f(gv) * uv);
                 pg[e] = f32_to_bf16(gv);
@@ -517,9 +535,8 @@ gemm_pipe_kernel(GemmDesc p, int tiles_n) {
                 for (int e = 0; e < 4; ++e) {
                   float gv = acc[i][j][4 * g4 + e], uv = acc[i][j + NI / 2][4 * g4 + e];
                   if (BIAS) {
-                    const uint16_t* b = bias + ((int64_t)tc.group * S + tc.seg) * 2 * f;
-                    gv += bf16_to_f32(b[tc.n0 + cidx + e]);
-                    uv += bf16_to_f32(b[f + tc.n0 + cidx + e]);
+                    gv += s_bias[cidx + e];
+                    uv += s_bias[BN / 2 + cidx + e];
                   }
                   h[e] = f32_to_bf16(silu_f(gv) * uv);
                   pg[e] = f32_to_bf16(gv);
@@ -547,13 +564,11 @@ gemm_pipe_kernel(GemmDesc p, int tiles_n) {
                 for (int e = 0; e < 4; ++e) {
                   float v = acc[i][j][4 * g4 + e];
                   if (KIND == kGemmUp) {
-                    if (BIAS) v += bf16_to_f32(bias[((int64_t)tc.group * S + tc.seg) * f + tc.n0 + cidx + e]);
+                    if (BIAS) v += s_bias[cidx + e];
                     pv[e] = f32_to_bf16(v);
                     h[e] = f32_to_bf16(gelu_f(v));
                   } else {
-                    if (BIAS)
-                      for (int s = 0; s < S; ++s)
-                        v += bf16_to_f32(bias[((int64_t)tc.group * S + s) * d + tc.n0 + cidx + e]);
+                    if (BIAS) v += s_bias[cidx + e];
                     h[e] = f32_to_bf16(v);
                   }
                 }
