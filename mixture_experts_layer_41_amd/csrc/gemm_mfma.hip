@@ -640,17 +640,19 @@ int cu_count() {
 }  // namespace
 
 // Shape preference by expected rows per group, from kernel-time sweeps of
-// every shape on MI355X: weight streaming (few rows per group) is fastest
-// with the 32-row decode tile on both GEMMs (on the decode layer the down
-// GEMM 1 % faster than with the pipelined 128x128 tile); a few hundred rows
-// per group with the pipelined 128x128
+// every shape on MI355X: weight streaming (up to 128 rows per group) is
+// fastest with the 32-row decode tile on both GEMMs (on the decode layer the
+// routed down GEMM 1 % faster than with the pipelined 128x128 tile, and the
+// shared expert's 128 rows take twice the tiles, so twice the CUs stream its
+// weights: the step 0.9 % faster); a few hundred rows per group with the
+// pipelined 128x128
 // (up) and the 128x128 persistent tile (down); thousands of rows with the
 // pipelined 256x128 (up) and the 8-wave 256x256 (down).
 const int* preferred_variants(GemmKind kind, double rows_per_group) {
   static const int up_decode[] = {3, 6, 2, -1}, dn_decode[] = {3, 6, 2, -1};
   static const int up_small[] = {6, 2, 5, -1}, dn_small[] = {2, 1, 6, -1};
   static const int up_large[] = {8, 5, 0, 4, -1}, dn_large[] = {8, 0, 2, 5, -1};
-  if (rows_per_group < 64) return kind == kGemmUp ? up_decode : dn_decode;
+  if (rows_per_group <= 128) return kind == kGemmUp ? up_decode : dn_decode;
   if (rows_per_group < 1024) return kind == kGemmUp ? up_small : dn_small;
   return kind == kGemmUp ? up_large : dn_large;
 }
