@@ -770,36 +770,75 @@ router_select_kernel(const float* __restrict__ part_in, int nsplit, const Router
   int32_t* cnt = reinterpret_cast<int32_t*>(lg + BT * (ep + 1));
   float* lse2 = reinterpret_cast<float*>(cnt + ep);
   for (int e = threadIdx.x; e < ep; e += kThreads) cnt[e] = 0;
-  // each thread adds up to kPer elements' splits in split order; the loads
-  // of four splits are in flight together
-  constexpr int kPer = 32;
+  // the splits of each element added in split order.  Loads are
+  // unconditional, from clamped addresses (a load under a per-lane condition
+  // is waited for before the next one is issued), and the splits' loads are
+  // in flight together in batches.
   const int n = nvalid * E;
-  for (int o0 = 0; o0 < n; o0 += kThreads * kPer) {
-    float v[kPer];
+  auto put_score = [&](int o, float v) {
+    const int r = o / E, e = o % E;
+    const float sc = router_score(v, mod, t0 + r, T, E, e);
+    lg[r * (ep + 1) + e] = sc;
+    if (mod.scores_out) mod.scores_out[(t0 + r) * E + e] = sc;
+  };
+  if (E % 4 == 0 && (reinterpret_cast<uintptr_t>(part_in) & 15u) == 0) {
+    // 4 consecutive elements (16 bytes) per load, kV of them per thread,
+    // kQ splits per batch
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    constexpr int kV = 2, kQ = 14;
+    const int n4 = n / 4;
+    for (int o0 = 0; o0 < n4; o0 += kThreads * kV) {
+      f4 v[kV];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) v[i] = 0.f;
-    for (int q0 = 0; q0 < nsplit; q0 += 4) {
-      float w[4][kPer];
+      for (int i = 0; i < kV; ++i) v[i] = f4{0.f, 0.f, 0.f, 0.f};
+      for (int q0 = 0; q0 < nsplit; q0 += kQ) {
+        f4 w[kQ][kV];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < kQ; ++u) {
+          const int q = min(q0 + u, nsplit - 1);
+          const f4* src = reinterpret_cast<const f4*>(part_in + ((int64_t)q * T + t0) * E);
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-          const int o = o0 + threadIdx.x + i * kThreads;
-          w[u][i] = (q0 + u < nsplit && o < n) ? part_in[((int64_t)(q0 + u) * T + t0) * E + o] : 0.f;
+          for (int i = 0; i < kV; ++i) w[u][i] = src[min(o0 + (int)threadIdx.x + i * kThreads, n4 - 1)];
         }
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < kQ; ++u)
+          if (q0 + u < nsplit)
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) v[i] += w[u][i];
+            for (int i = 0; i < kV; ++i) v[i] += w[u][i];
+      }
+#pragma unroll
+      for (int i = 0; i < kV; ++i) {
+        const int o = o0 + threadIdx.x + i * kThreads;
+        if (o < n4)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) put_score(4 * o + c, v[i][c]);
+      }
     }
+  } else {
+    constexpr int kPer = 16, kQ = 4;
+    for (int o0 = 0; o0 < n; o0 += kThreads * kPer) {
+      float v[kPer];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int o = o0 + threadIdx.x + i * kThreads;
-      if (o < n) {
-        const int r = o / E, e = o % E;
-        const float sc = router_score(v[i], mod, t0 + r, T, E, e);
-        lg[r * (ep + 1) + e] = sc;
-        if (mod.scores_out) mod.scores_out[(t0 + r) * E + e] = sc;
+      for (int i = 0; i < kPer; ++i) v[i] = 0.f;
+      for (int q0 = 0; q0 < nsplit; q0 += kQ) {
+        float w[kQ][kPer];
+#pragma unroll
+        for (int u = 0; u < kQ; ++u) {
+          const int q = min(q0 + u, nsplit - 1);
+#pragma unroll
+          for (int i = 0; i < kPer; ++i)
+            w[u][i] = part_in[((int64_t)q * T + t0) * E + min(o0 + (int)threadIdx.x + i * kThreads, n - 1)];
+        }
+#pragma unroll
+        for (int u = 0; u < kQ; ++u)
+          if (q0 + u < nsplit)
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) v[i] += w[u][i];
+      }
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int o = o0 + threadIdx.x + i * kThreads;
+        if (o < n) put_score(o, v[i]);
       }
     }
   }
