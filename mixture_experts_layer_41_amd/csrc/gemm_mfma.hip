@@ -613,6 +613,13 @@ hipError_t dispatch(const GemmDesc& g, int variant, hipStream_t s) {
     case 1: return run<256, 128, 64, 4, 2, true, KIND, ACT, BIAS, Q8, PD>(g, kTiles[1].occ, s);
     case 2: return run<128, 128, 64, 2, 2, true, KIND, ACT, BIAS, Q8, PD>(g, kTiles[2].occ, s);
     default:
+      // one group (a shared expert over a decode batch): half-width column
+      // tiles over 2 waves, up to 4 per CU, so that twice the CUs stream
+      // its weights (many groups already give every CU tiles)
+      if (!g.group_off || g.n_groups == 1) {
+        if (even_k_tiles) return run<32, 128, 64, 1, 2, true, KIND, ACT, BIAS, Q8, 2>(g, 4, s);
+        return run<32, 128, 64, 1, 2, true, KIND, ACT, BIAS, Q8, PD>(g, 4, s);
+      }
       if (even_k_tiles) return run<32, 256, 64, 1, 4, true, KIND, ACT, BIAS, Q8, 2>(g, kTiles[3].occ, s);
       return run<32, 256, 64, 1, 4, true, KIND, ACT, BIAS, Q8, PD>(g, kTiles[3].occ, s);
   }
