@@ -129,6 +129,10 @@ SMALL = [
     # bias slice; the shared pair's two down biases summed), with the half
     # column tile: the bias of its columns past d clamped
     ("bf16_wide_swiglu_bias", 2400, 384, 2, 1, 256, 2, "bf16", "swiglu", 0.0, "random", "none", False),
+    # decode-sized groups with expert biases: the 32-row decode tiles (many
+    # groups: 32 x 256; the one shared group of 100 rows: 32 x 128)
+    ("bf16_decode_tiles_bias", 100, 256, 16, 2, 128, 1, "bf16", "swiglu", 0.0, "random", "none", False),
+    ("bf16_decode_tiles_gelu", 120, 512, 8, 1, 256, 2, "bf16", "gelu", 0.0, "random", "none", True),
 ]
 
 
