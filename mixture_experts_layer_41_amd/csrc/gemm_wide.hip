@@ -126,7 +126,9 @@ __device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, int off, const 
   __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, 0);
 }
 
-template <int WM, int WN, int KIND, int ACT, bool BIAS>
+// ONE_SEG (down kind): every group has one FFN segment, so stage kt reads
+// K chunk kt with no segment arithmetic in the K loop
+template <int WM, int WN, int KIND, int ACT, bool BIAS, bool ONE_SEG>
 __global__ void __launch_bounds__(64 * WM * WN, 1)
 gemm_wide_kernel(GemmDesc p, int tiles_n) {
   constexpr bool kSwiglu = (KIND == kGemmUp && ACT == MOE_ACT_SWIGLU);
@@ -198,6 +200,12 @@ gemm_wide_kernel(GemmDesc p, int tiles_n) {
   const int rows1 = (KIND == kGemmUp) ? (kSwiglu ? 2 * f : f) : d;  // weight rows per segment
   const int nk_seg = kw / BK;                              // stages per FFN segment
   const int nk = (KIND == kGemmUp) ? nk_seg : S * nk_seg;  // stages per tile
+  // stage kt of the down kind reads chunk kt % nk_seg of FFN segment
+  // kt / nk_seg; the quotient as a multiply-high by ceil(2^32 / nk_seg),
+  // exact while kt and nk_seg stay below 2^16 (the host checks nk, and
+  // nk_seg >= 2 for the down kind)
+  const uint32_t seg_mul = (uint32_t)((0x100000000ull + nk_seg - 1) / nk_seg);
+  const int64_t seg_w = (int64_t)d * f;                    // weight elements per segment
 
   // copy geometry: copy i of wave w covers tile rows w*64 + i*16 + lane/4 at
   // LDS chunk lane%4, which holds global chunk (lane%4) ^ ((row/4)%4) =
@@ -287,9 +295,10 @@ gemm_wide_kernel(GemmDesc p, int tiles_n) {
       ao_ = (int64_t)(kt_) * BK;                                                            \
       bo_ = ao_;                                                                            \
     } else {                                                                                \
-      const int s_ = (kt_) / nk_seg, kk_ = ((kt_) - s_ * nk_seg) * BK;                      \
+      const int s_ = ONE_SEG ? 0 : (int)__umulhi((uint32_t)(kt_), seg_mul);               \
+      const int kk_ = ((kt_) - s_ * nk_seg) * BK;                                           \
       ao_ = (int64_t)s_ * f + kk_;                                                          \
-      bo_ = (int64_t)s_ * d * f + kk_;                                                      \
+      bo_ = s_ * seg_w + kk_;                                                               \
     }                                                                                       \
     _Pragma("unroll") for (int i_ = 0; i_ < A_IW; ++i_)                                    \
         copy16((src_).a[i_] + ao_, (sa_) + (wave * A_IW + i_) * 64);                        \
@@ -598,7 +607,7 @@ int wide_cus() {
   return n;
 }
 
-template <int WM, int WN, int KIND, int ACT, bool BIAS>
+template <int WM, int WN, int KIND, int ACT, bool BIAS, bool ONE_SEG = false>
 hipError_t run_wide(const GemmDesc& g, hipStream_t s) {
   constexpr bool kSwiglu = (KIND == kGemmUp && ACT == MOE_ACT_SWIGLU);
   // down: the last column tile may cover half a tile (widths multiple of 128)
@@ -609,7 +618,7 @@ hipError_t run_wide(const GemmDesc& g, hipStream_t s) {
   if (upper <= 0 || g.rows_max <= 0) return hipSuccess;
   int64_t grid = std::min<int64_t>(upper, (int64_t)wide_cus());
   grid = (grid + 7) / 8 * 8;  // a multiple of 8 (XCDs)
-  wide::gemm_wide_kernel<WM, WN, KIND, ACT, BIAS>
+  wide::gemm_wide_kernel<WM, WN, KIND, ACT, BIAS, ONE_SEG>
       <<<dim3((unsigned)grid), dim3(64 * WM * WN), 0, s>>>(g, tiles_n);
   return hipGetLastError();
 }
@@ -630,7 +639,8 @@ bool wide_fits(GemmKind kind, const GemmDesc& g) {
   const int K = kind == kGemmUp ? g.d : g.f;
   if (K % wide::BK != 0) return false;
   const int nk = (kind == kGemmUp ? 1 : g.n_seg) * (K / wide::BK);
-  if (nk % wide::NS != 0) return false;
+  // the down kind's segment quotient: nk below 2^16, two stages per segment at least
+  if (nk % wide::NS != 0 || nk >= (1 << 16) || (kind == kGemmDown && K / wide::BK < 2)) return false;
   // output widths in whole tiles; the down kind also takes a last half tile
   // (the backward's dh product: width f = 1408 on the skewed layer)
   const int ncol = kind == kGemmUp ? (swiglu ? wide::BN / 2 : wide::BN) : wide::BN / 2;
@@ -642,8 +652,12 @@ bool wide_fits(GemmKind kind, const GemmDesc& g) {
 hipError_t launch_gemm_wide(GemmKind kind, const GemmDesc& g, hipStream_t s) {
   constexpr int WM = 2, WN = 4;
   const bool bias = g.bias != nullptr;
-  if (kind == kGemmDown)
+  if (kind == kGemmDown) {
+    if (g.n_seg == 1)
+      return bias ? run_wide<WM, WN, kGemmDown, 0, true, true>(g, s)
+                  : run_wide<WM, WN, kGemmDown, 0, false, true>(g, s);
     return bias ? run_wide<WM, WN, kGemmDown, 0, true>(g, s) : run_wide<WM, WN, kGemmDown, 0, false>(g, s);
+  }
   if (g.act == MOE_ACT_SWIGLU)
     return bias ? run_wide<WM, WN, kGemmUp, MOE_ACT_SWIGLU, true>(g, s)
                 : run_wide<WM, WN, kGemmUp, MOE_ACT_SWIGLU, false>(g, s);
