@@ -156,7 +156,6 @@ gemm_wide_kernel(GemmDesc p, int tiles_n) {
   u32x4* const sB3 = s3 + SCH;
   __shared__ int s_off[kMaxExperts + 1];     // group row offsets
   __shared__ int s_tstart[kMaxExperts + 1];  // first row tile of each group
-  __shared__ int s_scan[kMaxExperts + 1];
   __shared__ int s_idx[3][BM];               // gather indices of three consecutive tiles
   __shared__ float s_bias[BIAS ? BN : 1];    // bias of the current tile's output columns
 
@@ -168,22 +167,33 @@ gemm_wide_kernel(GemmDesc p, int tiles_n) {
   for (int g = tid; g <= G; g += NT)
     s_off[g] = p.group_off ? p.group_off[g] : (g == 0 ? 0 : (int)p.rows_max);
   __syncthreads();
-  for (int g = tid; g <= G; g += NT) {
-    const int rows = g < G ? min(s_off[g + 1], (int)p.rows_max) - min(s_off[g], (int)p.rows_max) : 0;
-    s_tstart[g] = rows > 0 ? (rows + BM - 1) / BM : 0;
+  // first row tile of each group (s_tstart[G] = all row tiles): one wave,
+  // each lane owning a run of consecutive groups, the runs' totals scanned
+  // across the lanes
+  if (wave == 0) {
+    const int per = (G + kWave - 1) / kWave;
+    const int g0 = min(lane * per, G), g1 = min(g0 + per, G);
+    auto row_tiles = [&](int g) {
+      const int rows = min(s_off[g + 1], (int)p.rows_max) - min(s_off[g], (int)p.rows_max);
+      return rows > 0 ? (rows + BM - 1) / BM : 0;
+    };
+    int own = 0;
+    for (int g = g0; g < g1; ++g) own += row_tiles(g);
+    int incl = own;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
+    }
+    int run = incl - own;
+    for (int g = g0; g < g1; ++g) {
+      s_tstart[g] = run;
+      run += row_tiles(g);
+    }
+    if (lane == kWave - 1) s_tstart[G] = incl;
   }
   __syncthreads();
-  for (int o = 1; o <= G; o <<= 1) {  // inclusive scan over g = 0..G
-    for (int g = tid; g <= G; g += NT) s_scan[g] = g >= o ? s_tstart[g - o] : 0;
-    __syncthreads();
-    for (int g = tid; g <= G; g += NT) s_tstart[g] += s_scan[g];
-    __syncthreads();
-  }
-  const int m_tiles = s_tstart[G - 1];
-  for (int g = tid; g <= G; g += NT) s_scan[g] = g == 0 ? 0 : s_tstart[g - 1];
-  __syncthreads();
-  for (int g = tid; g <= G; g += NT) s_tstart[g] = s_scan[g];
-  __syncthreads();
+  const int m_tiles = s_tstart[G];
 
   // ---- this workgroup's tiles: XCD x = blockIdx % 8 owns the x-th eighth of
   // the tile list; its workgroups stride through it
