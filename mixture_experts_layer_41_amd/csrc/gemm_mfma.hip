@@ -42,8 +42,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte chun
 // One output tile: K loop over the group's rows and the tile's weight rows,
 // then the epilogue.  sA / sB are the two LDS stages.  PD = K tiles whose
 // global loads are in flight at once (1, or 2 with two register sets; PD = 2
-// needs an even number of K tiles).
-template <int BM, int BN, int BK, int WM, int WN, int KIND, int ACT, bool BIAS, int Q8, int PD>
+// needs an even number of K tiles).  STREAM_W: the tile is its group's only
+// row tile, so it reads each weight byte once (bf16 weight loads then carry
+// the nontemporal hint).
+template <int BM, int BN, int BK, int WM, int WN, int KIND, int ACT, bool BIAS, int Q8, int PD,
+          bool STREAM_W = false>
 __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo& tile, int nt,
                                                u32x4 (*sA)[BM * (BK / 8)],
                                                u32x4 (*sB)[BN * (BK / 8)]) {
@@ -136,16 +139,16 @@ __device__ __forceinline__ void gemm_tile_body(const GemmDesc& p, const TileInfo
     }
   }
 
-  // bf16 weight loads of the decode-shaped tiles (32 rows) carry the
-  // nontemporal hint: a group of at most 32 rows reads each weight byte
-  // once, and a K tile is one whole 128-byte line of each weight row, so the
-  // lines need not stay in the caches (a plain streaming read of HBM runs
-  // 7-10 % faster with the hint).  Not for INT8 codes: their K tile is half
-  // a line, whose other half the next K tile reads (with the hint that half
-  // came from HBM again: 40 % slower).  Larger tiles keep their weight
-  // panels cached for the group's other row tiles.
+  // bf16 weight loads of a tile that is its group's only row tile (decode
+  // batches: groups of at most 32 rows) carry the nontemporal hint: each
+  // weight byte is read once, and a K tile is one whole 128-byte line of
+  // each weight row, so the lines need not stay in the caches (a plain
+  // streaming read of HBM runs 7-10 % faster with the hint).  Not for INT8
+  // codes: their K tile is half a line, whose other half the next K tile
+  // reads (with the hint that half came from HBM again: 40 % slower).  A
+  // group of several row tiles keeps its weight panels cached for the others.
   auto ld_w = [](const u32x4* q) -> u32x4 {
-    if constexpr (BM <= 32) return __builtin_nontemporal_load(q);
+    if constexpr (STREAM_W) return __builtin_nontemporal_load(q);
     return *q;
   };
   u32x4 ra[PD][A_LD], rb[PD][B_LD];  // staging registers of the next K tile(s)
@@ -494,6 +497,14 @@ gemm_tile_kernel(GemmDesc p, int tiles_n) {
   const TileInfo tile = s_tile;
   const int nt = s_nt;
   if (tile.group < 0) return;
+  if constexpr (BM <= 32 && !Q8) {
+    const int64_t grows = p.group_off ? (int64_t)p.group_off[tile.group + 1] - p.group_off[tile.group]
+                                      : p.rows_max;
+    if (grows <= BM) {
+      gemm_tile_body<BM, BN, BK, WM, WN, KIND, ACT, BIAS, Q8, PD, true>(p, tile, nt, sA, sB);
+      return;
+    }
+  }
   gemm_tile_body<BM, BN, BK, WM, WN, KIND, ACT, BIAS, Q8, PD>(p, tile, nt, sA, sB);
 }
 
@@ -550,6 +561,12 @@ gemm_tile_persistent(GemmDesc p, int tiles_n) {
     tile.group = glo;
     tile.row0 = (int64_t)s_off[glo] + (int64_t)(mt - s_tstart[glo]) * BM;
     tile.rows = min(BM, min(s_off[glo + 1], (int)p.rows_max) - (int)tile.row0);
+    if constexpr (BM <= 32 && !Q8) {
+      if (min(s_off[glo + 1], (int)p.rows_max) - s_off[glo] <= BM) {
+        gemm_tile_body<BM, BN, BK, WM, WN, KIND, ACT, BIAS, Q8, PD, true>(p, tile, nt, sA, sB);
+        continue;
+      }
+    }
     gemm_tile_body<BM, BN, BK, WM, WN, KIND, ACT, BIAS, Q8, PD>(p, tile, nt, sA, sB);
   }
 }
