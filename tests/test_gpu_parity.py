@@ -133,6 +133,10 @@ SMALL = [
     # groups: 32 x 256; the one shared group of 100 rows: 32 x 128)
     ("bf16_decode_tiles_bias", 100, 256, 16, 2, 128, 1, "bf16", "swiglu", 0.0, "random", "none", False),
     ("bf16_decode_tiles_gelu", 120, 512, 8, 1, 256, 2, "bf16", "gelu", 0.0, "random", "none", True),
+    # decode tiles over groups of 23-41 rows: groups of at most 32 rows are
+    # one row tile (weights streamed with the nontemporal hint), larger ones
+    # two (weights cached), in one launch
+    ("bf16_decode_mixed_rows", 256, 256, 16, 2, 128, 1, "bf16", "swiglu", 0.0, "none", "none", False),
 ]
 
 
