@@ -55,6 +55,11 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_gemm_traffic.json")
 GEMM_SRCS = [os.path.join(ROOT, "mixture_experts_layer_41_amd", "csrc", n)
              for n in ("gemm.hip", "gemm_mfma.hip", "gemm_pipe.hip", "gemm_common.h", "gemm_wide.hip")]
 FLUSH_BYTES = 512 << 20
+# Timed work per measurement of an extra leg (and of every grouped-GEMM
+# leg), at least: a short layer timed over 20 steps (1.5 ms on the Flash
+# layer) reads several percent slow against its steady state.
+MIN_TIMED_SECONDS = 0.05
+MAX_TIMED_ITERS = 2000
 
 
 def log(*a):
@@ -273,6 +278,17 @@ def run_leg(cfg, args, headline, want_backward, want_host_inputs):
         except Exception as e:  # capture not possible: time eager launches
             log(f"[bench] graph capture failed ({e}); timing eager launches")
 
+    def iters_for(fn, base):
+        """At least `base` iterations, and enough for MIN_TIMED_SECONDS of
+        work (estimated from 3 untimed calls)."""
+        torch.cuda.synchronize()
+        s0 = time.perf_counter()
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        est = (time.perf_counter() - s0) / 3
+        return int(min(MAX_TIMED_ITERS, max(base, -(-MIN_TIMED_SECONDS // max(est, 1e-6)))))
+
     def timed(step_fn, steps):
         torch.cuda.synchronize()
         s0 = time.perf_counter()
@@ -281,14 +297,18 @@ def run_leg(cfg, args, headline, want_backward, want_host_inputs):
         torch.cuda.synchronize()
         return time.perf_counter() - s0
 
-    eager_s = timed(lambda: fwd(x, noise), args.steps)
-    graph_s = timed(graph.replay, args.steps) if graph is not None else None
+    # the headline leg times exactly --steps steps; an extra leg at least that
+    # many and at least MIN_TIMED_SECONDS of them
+    n_steps = args.steps if headline else iters_for(lambda: fwd(x, noise), args.steps)
+    eager_s = timed(lambda: fwd(x, noise), n_steps)
+    graph_s = timed(graph.replay, n_steps) if graph is not None else None
     best_s = min(s for s in (eager_s, graph_s) if s is not None)
     mode = "hip_graph" if (graph_s is not None and graph_s <= eager_s) else "eager"
     del graph
-    step_us = best_s / args.steps * 1e6
-    log(f"[bench] leg {cfg.name}: eager {eager_s / args.steps * 1e6:.1f} us/step"
-        + (f", graph {graph_s / args.steps * 1e6:.1f} us/step" if graph_s else ""))
+    step_us = best_s / n_steps * 1e6
+    log(f"[bench] leg {cfg.name}: eager {eager_s / n_steps * 1e6:.1f} us/step"
+        + (f", graph {graph_s / n_steps * 1e6:.1f} us/step" if graph_s else "")
+        + f" ({n_steps} steps)")
 
     # ---- routing statistics of this batch (for the algorithmic work counts)
     torch.cuda.synchronize()
@@ -347,7 +367,7 @@ def run_leg(cfg, args, headline, want_backward, want_host_inputs):
 
     for _ in range(5):
         ffn_all()
-    n_ffn = max(20, args.steps)
+    n_ffn = iters_for(ffn_all, max(20, args.steps))
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record(stream)
@@ -388,7 +408,7 @@ def run_leg(cfg, args, headline, want_backward, want_host_inputs):
     act_rows = R + T * S if S else R
     gemm_bytes = weight_bytes + ab * (R * d + (T * d if S else 0) + 2 * act_rows * f + act_rows * d)
     ridge = MFMA_BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3          # flop per byte
-    common = {"launch_us": round(ffn_s * 1e6, 2), "flops_per_launch": gemm_flops,
+    common = {"launch_us": round(ffn_s * 1e6, 2), "calls_timed": n_ffn, "flops_per_launch": gemm_flops,
               "bytes_per_launch": gemm_bytes, "touched_experts": touched,
               "traffic": traffic_entry(cfg.name)}
     if gemm_flops / weight_bytes >= ridge:
@@ -416,7 +436,7 @@ def run_leg(cfg, args, headline, want_backward, want_host_inputs):
         for _ in range(3):
             tr.forward(x, noise)
             tr.backward(g_dy)
-        n_tr = max(10, args.steps)
+        n_tr = iters_for(lambda: (tr.forward(x, noise), tr.backward(g_dy)), max(10, args.steps))
         e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
 
         def loop_ms(fn):
@@ -438,7 +458,7 @@ def run_leg(cfg, args, headline, want_backward, want_host_inputs):
         backward = {
             "what": "moe_backward (all gradients) after moe_forward_train, same batch; "
                     "each figure from back-to-back calls",
-            "us_per_step": round(bwd_s * 1e6, 2),
+            "us_per_step": round(bwd_s * 1e6, 2), "calls_timed": n_tr,
             "train_forward_us": round(f_ms / n_tr * 1e3, 2),
             "train_step_us": round(s_ms / n_tr * 1e3, 2),
             "tokens_per_s_train": round(T / (s_ms / n_tr / 1e3), 1),
@@ -457,8 +477,8 @@ def run_leg(cfg, args, headline, want_backward, want_host_inputs):
         "expert_weights": "int8 codes + f32 row scales" if q8 else
         ("bf16" if cfg.dtype == "bf16" else "f32"),
         "us_per_step": round(step_us, 2), "tokens_per_s": round(T / (step_us / 1e6), 1),
-        "launch": mode, "eager_us_per_step": round(eager_s / args.steps * 1e6, 2),
-        "graph_us_per_step": None if graph_s is None else round(graph_s / args.steps * 1e6, 2),
+        "launch": mode, "timed_steps": n_steps, "eager_us_per_step": round(eager_s / n_steps * 1e6, 2),
+        "graph_us_per_step": None if graph_s is None else round(graph_s / n_steps * 1e6, 2),
         "layer_tflops": round(layer_flops / (step_us / 1e6) / 1e12, 2),
         "kept_rows": R, "dropped": int(aux["n_dropped"]),
         "roofline": roofline, "flush": flush, "backward": backward,
